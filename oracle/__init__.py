@@ -1,0 +1,204 @@
+"""CPU oracle of the DSA lightning indexer forward pass -- TEST INFRASTRUCTURE.
+
+Only ``tests/``, ``__graft_entry__.smoke()`` and the CPU-baseline leg of
+``bench.py`` may import this package.  The library path never does, and it
+shares no code with the HIP implementation.
+
+The arithmetic lives in ``oracle.c`` (plain C, fp64, OpenMP over rows); this
+module only marshals numpy arrays into it.  What it follows, from the
+archdiff.com compare pages on Kimi K3.1 Pro (component tables):
+  * sparse-attention row: q = c_q W_q (1,536 -> 4,096 = 32 heads x 128),
+    k = LayerNorm(x W_k) (7,168 -> 128, one key shared by all heads),
+    w = x W_w (7,168 -> 32), I = sum_h w_h ReLU(q_h . k), top 2,048 per query;
+  * QK-norm row: the LayerNorm is on the indexer key;
+  * RoPE row (K3.1 vs Gemma 4 page): no rotary step in the indexer;
+  * long-context row (same page): the whole prefix is scored.
+"""
+import ctypes
+import os
+import subprocess
+
+import numpy as np
+
+_HERE = os.path.dirname(os.path.abspath(__file__))
+_SO = os.path.join(_HERE, "liboracle.so")
+_SRC = os.path.join(_HERE, "oracle.c")
+
+H, D, QLAT, QOUT, HIDDEN, TOPK = 32, 128, 1536, 4096, 7168, 2048
+
+
+def build(force=False):
+    if force or not os.path.exists(_SO) or os.path.getmtime(_SO) < os.path.getmtime(_SRC):
+        subprocess.check_call(["gcc", "-O2", "-std=c11", "-ffp-contract=off", "-fopenmp",
+                               "-fPIC", "-shared", _SRC, "-o", _SO + ".tmp", "-lm"])
+        os.replace(_SO + ".tmp", _SO)
+
+
+_lib = None
+
+
+def lib():
+    global _lib
+    if _lib is None:
+        if not os.path.exists(_SO):
+            build()
+        L = ctypes.CDLL(_SO)
+        vp, i64, i32, f64 = ctypes.c_void_p, ctypes.c_int64, ctypes.c_int, ctypes.c_double
+        L.oracle_param_count.restype = i64
+        L.oracle_param_count.argtypes = []
+        L.oracle_dims.restype = i32
+        L.oracle_dims.argtypes = [vp]
+        L.oracle_bf16_to_f64.restype = f64
+        L.oracle_bf16_to_f64.argtypes = [ctypes.c_uint16]
+        L.oracle_f64_to_bf16.restype = ctypes.c_uint16
+        L.oracle_f64_to_bf16.argtypes = [f64]
+        L.oracle_f64_to_bf16_array.restype = None
+        L.oracle_f64_to_bf16_array.argtypes = [vp, i64, vp]
+        L.oracle_linear_f64.restype = None
+        L.oracle_linear_f64.argtypes = [vp, i64, vp, i64, i64, i64, vp]
+        L.oracle_layernorm_f64.restype = None
+        L.oracle_layernorm_f64.argtypes = [vp, i64, vp, vp, f64, vp]
+        L.oracle_project.restype = None
+        L.oracle_project.argtypes = [vp, i64, vp, i64, vp, vp, vp, vp, vp, f64, i64, vp, vp, vp]
+        L.oracle_scores.restype = None
+        L.oracle_scores.argtypes = [vp, vp, vp, i64, i32, i32, vp]
+        L.oracle_topk.restype = None
+        L.oracle_topk.argtypes = [vp, i64, i32, vp, vp, vp, vp]
+        L.oracle_rows.restype = None
+        L.oracle_rows.argtypes = [vp, vp, vp, vp, vp, i64, i32, i32, i32, vp, vp, vp, vp, vp, vp]
+        _lib = L
+    return _lib
+
+
+def _p(a):
+    return None if a is None else a.ctypes.data
+
+
+def _c(a, dt):
+    return np.ascontiguousarray(a, dtype=dt)
+
+
+# ---------------------------------------------------------------- numbers
+def bf16_to_f64(b):
+    b = np.asarray(b, dtype=np.uint16)
+    return (b.astype(np.uint32) << 16).view(np.float32).astype(np.float64)
+
+
+def f64_to_bf16(x):
+    x = _c(x, np.float64)
+    out = np.empty(x.shape, dtype=np.uint16)
+    lib().oracle_f64_to_bf16_array(_p(x), x.size, _p(out))
+    return out
+
+
+def param_count():
+    return int(lib().oracle_param_count())
+
+
+def dims():
+    d = np.zeros(6, dtype=np.int32)
+    lib().oracle_dims(_p(d))
+    return dict(zip(("heads", "dim", "qlat", "qout", "hidden", "topk"), d.tolist()))
+
+
+# ---------------------------------------------------------------- projections
+def linear_f64(A, W):
+    A = _c(A, np.uint16)
+    W = _c(W, np.uint16)
+    rows, n_in = A.shape
+    n_out = W.shape[1]
+    out = np.empty((rows, n_out), dtype=np.float64)
+    lib().oracle_linear_f64(_p(A), n_in, _p(W), n_in, n_out, rows, _p(out))
+    return out
+
+
+def layernorm_f64(a, gamma, beta, eps):
+    a = _c(a, np.float64)
+    g = _c(gamma, np.uint16)
+    b = _c(beta, np.uint16)
+    out = np.empty_like(a)
+    for r in range(a.shape[0]):
+        lib().oracle_layernorm_f64(a[r].ctypes.data, a.shape[1], _p(g), _p(b), float(eps),
+                                   out[r].ctypes.data)
+    return out
+
+
+def project(x, c_q, Wt, want=("q", "k", "w")):
+    """q [T,32,128], k [T,128], w [T,32] (bf16 patterns) of one indexer layer."""
+    T = (x if x is not None else c_q).shape[0]
+    x = None if x is None else _c(x, np.uint16)
+    c_q = None if c_q is None else _c(c_q, np.uint16)
+    q = np.empty((T, H, D), np.uint16) if "q" in want else None
+    k = np.empty((T, D), np.uint16) if "k" in want else None
+    w = np.empty((T, H), np.uint16) if "w" in want else None
+    lib().oracle_project(_p(x), HIDDEN, _p(c_q), QLAT, _p(_c(Wt["W_q"], np.uint16)),
+                         _p(_c(Wt["W_k"], np.uint16)), _p(_c(Wt["W_w"], np.uint16)),
+                         _p(_c(Wt["gamma"], np.uint16)), _p(_c(Wt["beta"], np.uint16)),
+                         float(Wt["eps"]), T, _p(q), _p(k), _p(w))
+    return q, k, w
+
+
+# ---------------------------------------------------------------- scores and top-k
+def scores(q_row, w_row, k, n=None):
+    """I[s] for s < n of one query row; q_row [H,D], w_row [H], k [>=n, D] (bf16 patterns)."""
+    q_row = _c(q_row, np.uint16)
+    w_row = _c(w_row, np.uint16)
+    k = _c(k, np.uint16)
+    Hh, Dd = q_row.shape
+    n = k.shape[0] if n is None else n
+    out = np.empty(n, dtype=np.float64)
+    lib().oracle_scores(_p(q_row), _p(w_row), _p(k), n, Hh, Dd, _p(out))
+    return out
+
+
+def topk(I, k=TOPK):
+    I = _c(I, np.float64)
+    idx = np.empty(k, dtype=np.int32)
+    sc = np.empty(k, dtype=np.float64)
+    tau = np.zeros(1)
+    m = np.zeros(1)
+    lib().oracle_topk(_p(I), I.size, k, _p(idx), _p(sc), _p(tau), _p(m))
+    return idx, sc, float(tau[0]), float(m[0])
+
+
+def rows(q_rows, w_rows, k, k_off, t, topk=TOPK, full=False):
+    """Score and select a batch of query rows.
+
+    q_rows [R,H,D], w_rows [R,H]; row r scores keys k[k_off[r] : k_off[r] + t[r] + 1].
+    Rows are handed to OpenMP longest first.  Returns dict(idx [R,topk] int32,
+    score [R,topk] f64, tau [R], maxabs [R], full (list of per-row score vectors or None)).
+    """
+    q_rows = _c(q_rows, np.uint16)
+    w_rows = _c(w_rows, np.uint16)
+    k = _c(k, np.uint16)
+    k_off = _c(k_off, np.int64)
+    t = _c(t, np.int64)
+    R = t.size
+    Hh, Dd = q_rows.shape[1], q_rows.shape[2]
+    order = np.argsort(-t, kind="stable")
+    qo, wo, ko, to = (_c(q_rows[order], np.uint16), _c(w_rows[order], np.uint16),
+                      _c(k_off[order], np.int64), _c(t[order], np.int64))
+    idx = np.empty((R, topk), np.int32)
+    sc = np.empty((R, topk), np.float64)
+    tau = np.empty(R)
+    m = np.empty(R)
+    fbuf = foff = None
+    if full:
+        foff = np.zeros(R, dtype=np.int64)
+        foff[1:] = np.cumsum(to + 1)[:-1]
+        fbuf = np.empty(int((to + 1).sum()), dtype=np.float64)
+    lib().oracle_rows(_p(qo), _p(wo), _p(k), _p(ko), _p(to), R, Hh, Dd, topk, _p(idx), _p(sc),
+                      _p(tau), _p(m), _p(fbuf), _p(foff))
+    inv = np.empty(R, dtype=np.int64)
+    inv[order] = np.arange(R)
+    out = dict(idx=idx[inv], score=sc[inv], tau=tau[inv], maxabs=m[inv], full=None)
+    if full:
+        vec = [fbuf[foff[j]:foff[j] + to[j] + 1] for j in range(R)]
+        out["full"] = [vec[inv[r]] for r in range(R)]
+    return out
+
+
+def prefill_rows(q, k, w, row_ids, topk=TOPK, full=False):
+    """Rows of one causal sequence: q [T,H,D], k [T,D], w [T,H]."""
+    row_ids = np.asarray(row_ids, dtype=np.int64)
+    return rows(q[row_ids], w[row_ids], k, np.zeros_like(row_ids), row_ids, topk, full)

@@ -1,0 +1,264 @@
+/*
+ * CPU ORACLE for the DSA lightning indexer forward pass -- test
+ * infrastructure only.  Only the tests, the smoke check and the benchmark's
+ * CPU-baseline leg may load this library; the product path never does.
+ *
+ * It is a plain, slow, obviously-correct restatement of the method, written
+ * from the archdiff.com compare pages for Kimi K3.1 Pro (page "Qwen3.5 vs
+ * Kimi K3.1 Pro", component table):
+ *   - sparse/compressed-attention row: a DSA lightning indexer per MLA layer,
+ *     32 heads x 128 dims, queries projected 1,536 -> 4,096 from the query
+ *     latent, one shared 128-dim key from the hidden state with a LayerNorm,
+ *     per-head weights from a 7,168 -> 32 projection, scores
+ *     I = sum_h w_h * ReLU(q_h . k), top 2,048 tokens kept per query;
+ *   - QK-norm row: the LayerNorm sits on the indexer key;
+ *   - RoPE row of the "Kimi K3.1 Pro vs Gemma 4" page: the indexer uses no
+ *     rotary embedding (index_rope_dim = 0);
+ *   - long-context row of that page: the indexer scores the whole prefix.
+ *
+ * Arithmetic: inputs are bf16 bit patterns widened exactly to double; every
+ * sum runs in double in a fixed ascending order; the projected q, k, w are
+ * rounded once, from double, to bf16 with round-to-nearest-even (own bit
+ * level routine, no trip through float).  Top-k is a full sort of the row by
+ * (score descending, index ascending) -- ties go to the lower token index --
+ * after which the kept indices are listed in ascending order.
+ *
+ * Readings where the pages are silent (each is listed in the design notes):
+ * causal boundary s <= t (a query scores itself); short rows keep all t+1
+ * tokens and pad with -1 / -inf; no score scale; no projection biases; the
+ * LayerNorm is mean-centred with biased variance over the 128 key dims,
+ * applied to the unrounded projection, with gain and bias; w has no
+ * activation and may be negative; head h of q is columns [128h, 128h+128).
+ *
+ * Shares no code, header or table with the HIP implementation.
+ */
+#include <math.h>
+#include <stdint.h>
+#include <stdlib.h>
+#include <string.h>
+
+/* ---- shapes of one indexer layer (sparse-attention row of the table) ---- */
+enum {
+    OR_HEADS = 32,     /* "32 heads" */
+    OR_DIM = 128,      /* "x 128 dims" */
+    OR_QLAT = 1536,    /* query latent width */
+    OR_QOUT = 4096,    /* 1,536 -> 4,096 = 32 x 128 */
+    OR_HIDDEN = 7168,  /* hidden width, 7,168 -> 32 for the head weights */
+    OR_TOPK = 2048     /* "top 2,048 tokens per query" */
+};
+
+/* Number of weight elements one indexer layer holds under the readings above
+ * (W_q, W_k, W_w, LayerNorm gain and bias; no projection biases). */
+int64_t oracle_param_count(void) {
+    return (int64_t)OR_QLAT * OR_QOUT      /* W_q */
+         + (int64_t)OR_HIDDEN * OR_DIM     /* W_k */
+         + (int64_t)OR_HIDDEN * OR_HEADS   /* W_w */
+         + 2 * (int64_t)OR_DIM;            /* LayerNorm gain and bias */
+}
+
+int oracle_dims(int32_t *out6) {
+    out6[0] = OR_HEADS; out6[1] = OR_DIM; out6[2] = OR_QLAT;
+    out6[3] = OR_QOUT; out6[4] = OR_HIDDEN; out6[5] = OR_TOPK;
+    return 6;
+}
+
+/* ---------------- bf16 <-> double ---------------- */
+
+/* Exact widening: a bf16 pattern is the top half of an IEEE binary32. */
+double oracle_bf16_to_f64(uint16_t b) {
+    uint32_t u = (uint32_t)b << 16;
+    float f;
+    memcpy(&f, &u, 4);
+    return (double)f;
+}
+
+/* Round a double to the nearest bf16 (8 significant bits, binary32 exponent
+ * range, subnormals included), ties to even, in one step from the double.
+ * Overflow goes to infinity.  NaN maps to the canonical quiet NaN. */
+uint16_t oracle_f64_to_bf16(double x) {
+    if (isnan(x)) return 0x7FC0;
+    uint16_t sign = signbit(x) ? 0x8000 : 0;
+    double a = fabs(x);
+    if (a == 0.0) return sign;
+    if (isinf(a)) return sign | 0x7F80;
+    int e;
+    frexp(a, &e);                          /* a = m * 2^e, 0.5 <= m < 1 */
+    int qexp = e - 8;                      /* 8 significant bits -> quantum 2^(e-8) */
+    if (qexp < -133) qexp = -133;          /* bf16 subnormal quantum is 2^-133 */
+    double scaled = ldexp(a, -qexp);       /* exact: power-of-two scaling */
+    double r = floor(scaled);
+    double frac = scaled - r;              /* exact */
+    if (frac > 0.5 || (frac == 0.5 && fmod(r, 2.0) != 0.0)) r += 1.0;
+    double v = ldexp(r, qexp);             /* exactly representable in bf16 (or 2^128) */
+    if (v >= 0x1p128) return sign | 0x7F80;
+    float f = (float)v;                    /* exact */
+    uint32_t u;
+    memcpy(&u, &f, 4);
+    return (uint16_t)(sign | ((u >> 16) & 0x7FFF));
+}
+
+void oracle_f64_to_bf16_array(const double *x, int64_t n, uint16_t *out) {
+    for (int64_t i = 0; i < n; ++i) out[i] = oracle_f64_to_bf16(x[i]);
+}
+
+/* ---------------- projections ---------------- */
+
+/* out[r][j] = sum_{i < n_in, ascending} A[r][i] * W[i][j]  in double,
+ * for r < rows.  A is bf16 [rows][lda], W is bf16 [n_in][n_out] row-major. */
+void oracle_linear_f64(const uint16_t *A, int64_t lda, const uint16_t *W, int64_t n_in,
+                       int64_t n_out, int64_t rows, double *out) {
+    double *Wd = (double *)malloc(sizeof(double) * (size_t)(n_in * n_out));
+    for (int64_t e = 0; e < n_in * n_out; ++e) Wd[e] = oracle_bf16_to_f64(W[e]);
+#pragma omp parallel for schedule(dynamic, 1)
+    for (int64_t r = 0; r < rows; ++r) {
+        double *o = out + r * n_out;
+        for (int64_t j = 0; j < n_out; ++j) o[j] = 0.0;
+        for (int64_t i = 0; i < n_in; ++i) {
+            double a = oracle_bf16_to_f64(A[r * lda + i]);
+            const double *wr = Wd + i * n_out;
+            for (int64_t j = 0; j < n_out; ++j) o[j] += a * wr[j];
+        }
+    }
+    free(Wd);
+}
+
+/* LayerNorm over n values (the QK-norm row: a LayerNorm on the indexer key).
+ * mu = mean(a), var = mean((a - mu)^2) (biased), out = (a - mu)/sqrt(var + eps)*g + b. */
+void oracle_layernorm_f64(const double *a, int64_t n, const uint16_t *gamma,
+                          const uint16_t *beta, double eps, double *out) {
+    double mu = 0.0;
+    for (int64_t j = 0; j < n; ++j) mu += a[j];
+    mu /= (double)n;
+    double var = 0.0;
+    for (int64_t j = 0; j < n; ++j) var += (a[j] - mu) * (a[j] - mu);
+    var /= (double)n;
+    double inv = 1.0 / sqrt(var + eps);
+    for (int64_t j = 0; j < n; ++j)
+        out[j] = (a[j] - mu) * inv * oracle_bf16_to_f64(gamma[j]) + oracle_bf16_to_f64(beta[j]);
+}
+
+/* One indexer layer's projections for rows [0, rows):
+ *   q[r]  = bf16( c_q[r] . W_q )                       [rows][4096]
+ *   k[r]  = bf16( LayerNorm( x[r] . W_k ) )            [rows][128]
+ *   w[r]  = bf16( x[r] . W_w )                         [rows][32]
+ * Any of q/k/w may be NULL to skip it (c_q / x may then be NULL too). */
+void oracle_project(const uint16_t *x, int64_t ldx, const uint16_t *c_q, int64_t ldc,
+                    const uint16_t *Wq, const uint16_t *Wk, const uint16_t *Ww,
+                    const uint16_t *gamma, const uint16_t *beta, double eps, int64_t rows,
+                    uint16_t *q, uint16_t *k, uint16_t *w) {
+    const int64_t chunk = 256;
+    double *buf = (double *)malloc(sizeof(double) * (size_t)chunk * OR_QOUT);
+    for (int64_t r0 = 0; r0 < rows; r0 += chunk) {
+        int64_t n = rows - r0 < chunk ? rows - r0 : chunk;
+        if (q) {
+            oracle_linear_f64(c_q + r0 * ldc, ldc, Wq, OR_QLAT, OR_QOUT, n, buf);
+            oracle_f64_to_bf16_array(buf, n * OR_QOUT, q + r0 * OR_QOUT);
+        }
+        if (k) {
+            oracle_linear_f64(x + r0 * ldx, ldx, Wk, OR_HIDDEN, OR_DIM, n, buf);
+#pragma omp parallel for schedule(static)
+            for (int64_t r = 0; r < n; ++r) {
+                double ln[OR_DIM];
+                oracle_layernorm_f64(buf + r * OR_DIM, OR_DIM, gamma, beta, eps, ln);
+                oracle_f64_to_bf16_array(ln, OR_DIM, k + (r0 + r) * OR_DIM);
+            }
+        }
+        if (w) {
+            oracle_linear_f64(x + r0 * ldx, ldx, Ww, OR_HIDDEN, OR_HEADS, n, buf);
+            oracle_f64_to_bf16_array(buf, n * OR_HEADS, w + r0 * OR_HEADS);
+        }
+    }
+    free(buf);
+}
+
+/* ---------------- scores ---------------- */
+
+/* I[s] = sum_{h < H} w[h] * max(0, sum_{d < D} q[h][d] * k[s][d]),  s in [0, n).
+ * q is bf16 [H][D] (head-major), w bf16 [H], k bf16 [n][D]; sums in double,
+ * h and d ascending.  No rotary step (index_rope_dim = 0), no scale. */
+void oracle_scores(const uint16_t *q, const uint16_t *w, const uint16_t *k, int64_t n,
+                   int H, int D, double *I) {
+    double *qd = (double *)malloc(sizeof(double) * (size_t)H * D);
+    double *wd = (double *)malloc(sizeof(double) * (size_t)H);
+    double *kd = (double *)malloc(sizeof(double) * (size_t)D);
+    for (int i = 0; i < H * D; ++i) qd[i] = oracle_bf16_to_f64(q[i]);
+    for (int h = 0; h < H; ++h) wd[h] = oracle_bf16_to_f64(w[h]);
+    for (int64_t s = 0; s < n; ++s) {
+        for (int d = 0; d < D; ++d) kd[d] = oracle_bf16_to_f64(k[s * D + d]);
+        double acc = 0.0;
+        for (int h = 0; h < H; ++h) {
+            double dot = 0.0;
+            for (int d = 0; d < D; ++d) dot += qd[h * D + d] * kd[d];
+            acc += wd[h] * (dot > 0.0 ? dot : 0.0);
+        }
+        I[s] = acc;
+    }
+    free(qd); free(wd); free(kd);
+}
+
+/* ---------------- selection ---------------- */
+
+typedef struct { double v; int64_t i; } or_item;
+
+/* Score descending, then index ascending: a strict total order, so the sort
+ * result is the unique "stable" order the method's tie rule asks for.
+ * -0.0 and +0.0 compare equal here (IEEE ==), so they tie. */
+static int or_cmp_desc(const void *a, const void *b) {
+    const or_item *x = (const or_item *)a, *y = (const or_item *)b;
+    if (x->v > y->v) return -1;
+    if (x->v < y->v) return 1;
+    return x->i < y->i ? -1 : (x->i > y->i ? 1 : 0);
+}
+
+static int or_cmp_idx(const void *a, const void *b) {
+    const or_item *x = (const or_item *)a, *y = (const or_item *)b;
+    return x->i < y->i ? -1 : (x->i > y->i ? 1 : 0);
+}
+
+/* Top-k of I[0..n): keep the first min(topk, n) items of the full sort by
+ * (score desc, index asc); list them by ascending index into idx/score,
+ * padding with -1 / -inf up to topk.  tau = score of the topk-th item when
+ * n > topk (else -inf); maxabs = max |I|. */
+void oracle_topk(const double *I, int64_t n, int topk, int32_t *idx, double *score,
+                 double *tau, double *maxabs) {
+    or_item *it = (or_item *)malloc(sizeof(or_item) * (size_t)(n > 0 ? n : 1));
+    double m = 0.0;
+    for (int64_t s = 0; s < n; ++s) {
+        it[s].v = I[s];
+        it[s].i = s;
+        if (fabs(I[s]) > m) m = fabs(I[s]);
+    }
+    qsort(it, (size_t)n, sizeof(or_item), or_cmp_desc);
+    int64_t keep = n < topk ? n : topk;
+    if (tau) *tau = n > topk ? it[topk - 1].v : -INFINITY;
+    if (maxabs) *maxabs = m;
+    qsort(it, (size_t)keep, sizeof(or_item), or_cmp_idx);
+    for (int64_t j = 0; j < topk; ++j) {
+        idx[j] = j < keep ? (int32_t)it[j].i : -1;
+        score[j] = j < keep ? it[j].v : -INFINITY;
+    }
+    free(it);
+}
+
+/* ---------------- rows ---------------- */
+
+/* For each listed row r (OpenMP over rows, caller orders them longest first):
+ * query q_rows[r] ([H][D] bf16), weights w_rows[r] ([H] bf16), keys
+ * k_base + k_off[r]*D .. (t[r] + 1 keys: the whole causal prefix, self
+ * included).  Writes idx/score [nrows][topk], tau/maxabs [nrows], and, when
+ * full is not NULL, the row's full score vector at full + full_off[r]. */
+void oracle_rows(const uint16_t *q_rows, const uint16_t *w_rows, const uint16_t *k_base,
+                 const int64_t *k_off, const int64_t *t, int64_t nrows, int H, int D, int topk,
+                 int32_t *idx, double *score, double *tau, double *maxabs, double *full,
+                 const int64_t *full_off) {
+#pragma omp parallel for schedule(dynamic, 1)
+    for (int64_t r = 0; r < nrows; ++r) {
+        int64_t n = t[r] + 1;
+        double *I = full ? full + full_off[r] : (double *)malloc(sizeof(double) * (size_t)n);
+        oracle_scores(q_rows + r * (int64_t)H * D, w_rows + r * (int64_t)H, k_base + k_off[r] * D,
+                      n, H, D, I);
+        oracle_topk(I, n, topk, idx + r * (int64_t)topk, score + r * (int64_t)topk, tau + r,
+                    maxabs + r);
+        if (!full) free(I);
+    }
+}
