@@ -1,0 +1,160 @@
+/*
+ * libdsaidx -- forward pass of a DSA lightning indexer on AMD MI355X (gfx950).
+ *
+ * The operation is the one fixed on the archdiff.com compare page "Qwen3.5-397B-A17B vs
+ * Kimi K3.1 Pro" (component table, sparse/compressed-attention row, Kimi K3.1 Pro cell):
+ * every MLA layer owns an indexer with 32 heads of 128 dims whose queries are projected
+ * from the 1,536-dim query latent (1,536 -> 4,096), one 128-dim key shared by all heads
+ * taken from the hidden state through a LayerNorm, and per-head weights from a
+ * 7,168 -> 32 projection; the score of key token s for query token t is
+ *
+ *         I[t,s] = sum_h w[t,h] * ReLU( q[t,h,:] . k[s,:] ),
+ *
+ * and each query keeps the 2,048 tokens with the largest scores, which become the only
+ * keys its MLA attends (gated-MLA row of the same table).  The key LayerNorm is named in
+ * the QK-norm row; the indexer applies no rotary embedding ("Kimi K3.1 Pro vs Gemma 4"
+ * page, RoPE row) and scores the whole prefix (same page, long-context row).  Serving
+ * engines cache the indexer keys across decode steps ("Kimi K3.1 Pro vs GLM-5" page,
+ * low-precision row); dsa_idx_decode scores against such a cache.
+ *
+ * Readings taken where the pages say nothing (fixed here, identical in the oracle):
+ *   - causal prefix s <= t: a query scores itself;
+ *   - a query with fewer than topk causal tokens keeps all t+1 of them; unused output
+ *     slots hold index -1 and score -inf;
+ *   - equal scores are broken toward the lower token index (-0 and +0 are equal);
+ *   - selected indices are listed in ascending order;
+ *   - no score scale, no projection biases, w has no activation (may be negative);
+ *   - LayerNorm = mean-centred, biased variance over the 128 key dims, eps from the
+ *     caller, gain and bias, applied before rounding k to bf16;
+ *   - q, k and w are stored as bf16 (round to nearest even from the fp32 accumulators);
+ *     scores are computed in fp32;
+ *   - q is head-major: head h is columns [128h, 128h + 128) of the 4,096.
+ *
+ * Conventions of every entry point:
+ *   - Tensor pointers are DEVICE pointers unless stated; bf16 is passed as uint16_t bit
+ *     patterns.  Rows are contiguous (row-major) unless a leading dimension is given.
+ *   - `stream` is a hipStream_t (NULL = the default stream).  Calls are asynchronous:
+ *     they enqueue kernels and return; they never synchronize.  The caller keeps every
+ *     buffer alive until the stream work completes.
+ *   - The library allocates no device memory and keeps no pointer after returning.
+ *     Scratch memory is the caller's workspace `ws` of `ws_bytes` bytes, sized with
+ *     dsa_idx_workspace_size(); it must not be shared by calls that may overlap.
+ *   - Status: DSA_IDX_OK (0) or a negative code below; on error nothing is launched and
+ *     outputs are untouched, and dsa_idx_last_error() returns a message (thread-local).
+ *   - Identical inputs give bitwise-identical outputs (no floating-point atomics).
+ *   - The device must be gfx950 (checked once per device).
+ */
+#ifndef DSAIDX_H
+#define DSAIDX_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+#define DSA_IDX_HEADS 32     /* indexer heads */
+#define DSA_IDX_DIM 128      /* dims per head, and the shared key width */
+#define DSA_IDX_QLAT 1536    /* query latent width (input of the q projection) */
+#define DSA_IDX_QOUT 4096    /* 32 x 128 */
+#define DSA_IDX_HIDDEN 7168  /* hidden width (input of the key and weight projections) */
+#define DSA_IDX_MAX_TOPK 2048
+
+/* status codes */
+#define DSA_IDX_OK 0
+#define DSA_IDX_EINVAL (-1)      /* null pointer, negative size, misalignment, ld too small */
+#define DSA_IDX_EUNSUPPORTED (-2)/* topk outside [1, 2048], device not gfx950, size too large */
+#define DSA_IDX_EWORKSPACE (-3)  /* ws_bytes below dsa_idx_workspace_size() */
+#define DSA_IDX_EHIP (-4)        /* a HIP runtime call failed (message names it) */
+
+/* operations for dsa_idx_workspace_size */
+#define DSA_IDX_OP_PROJECT 0
+#define DSA_IDX_OP_SCORE_TOPK 1
+#define DSA_IDX_OP_SCORE_TOPK_VARLEN 2
+#define DSA_IDX_OP_DECODE 3
+
+typedef uint16_t dsa_idx_bf16;
+
+/* One layer's indexer weights (device pointers, borrowed for the call).  Each of the 24
+ * MLA layers owns its own set (sparse/compressed-attention row: no index sharing). */
+typedef struct {
+    const dsa_idx_bf16 *W_q;      /* [1536][4096] row-major: q = c_q . W_q            */
+    const dsa_idx_bf16 *W_k;      /* [7168][128]  row-major: k = LN(x . W_k)           */
+    const dsa_idx_bf16 *W_w;      /* [7168][32]   row-major: w = x . W_w               */
+    const dsa_idx_bf16 *ln_gamma; /* [128] LayerNorm gain on the key                   */
+    const dsa_idx_bf16 *ln_beta;  /* [128] LayerNorm bias on the key                   */
+    float ln_eps;                 /* LayerNorm epsilon (> 0)                           */
+} dsa_idx_weights;
+
+/* Library version string (static storage). */
+const char *dsa_idx_version(void);
+
+/* Message of the last non-OK status returned on the calling thread ("" if none). */
+const char *dsa_idx_last_error(void);
+
+/* Bytes of workspace an operation needs (host-only, no device access).
+ *   op               one of DSA_IDX_OP_*
+ *   total_tokens     T for PROJECT and SCORE_TOPK; the packed token count for VARLEN
+ *   B                number of sequences (VARLEN, DECODE); ignored otherwise
+ *   max_seqlen       longest sequence (VARLEN, DECODE), keys of the longest cache for DECODE
+ *   topk             tokens kept per query, 1..2048
+ * Writes *bytes (0 is a valid answer).  Returns a status. */
+int dsa_idx_workspace_size(int op, int64_t total_tokens, int B, int max_seqlen, int topk,
+                           size_t *bytes);
+
+/* Projections of one indexer layer for T tokens (sparse-attention row; key LayerNorm
+ * from the QK-norm row):
+ *   q[t]  = bf16( c_q[t] . W_q )                   q    [T][4096]  (= [T][32][128])
+ *   k     = bf16( LayerNorm( x[t] . W_k ) )        row k_slot[t] (or t when k_slot is
+ *                                                  NULL) of k_base, rows of 128
+ *   w[t]  = bf16( x[t] . W_w )                     w    [T][32]
+ * x is [T][ldx] (ldx >= 7168), c_q is [T][ldc] (ldc >= 1536); ldx and ldc are in
+ * elements and must be multiples of 8; x, c_q, q, k_base, w must be 16-byte aligned.
+ * k_slot (device, int64 [T], may be NULL) scatters the keys into a cache (decode).
+ * Needs dsa_idx_workspace_size(DSA_IDX_OP_PROJECT, T, ...) bytes of workspace. */
+int dsa_idx_project(const dsa_idx_weights *weights, const dsa_idx_bf16 *x, int64_t ldx,
+                    const dsa_idx_bf16 *c_q, int64_t ldc, int64_t T, dsa_idx_bf16 *q,
+                    dsa_idx_bf16 *k_base, const int64_t *k_slot, dsa_idx_bf16 *w, void *ws,
+                    size_t ws_bytes, void *stream);
+
+/* Causal scores and top-k of one sequence of T tokens (sparse-attention row: score
+ * formula and top-2,048; long-context row: whole prefix scored):
+ *   q [T][32][128], k [T][128], w [T][32]   bf16, 16-byte aligned
+ *   idx    [T][topk] int32  selected key positions s <= t, ascending, -1 padded
+ *   scores [T][topk] fp32   I[t, idx] (may be NULL), -inf padded
+ * The T x T score matrix is never stored; the workspace holds per-row candidates. */
+int dsa_idx_score_topk(const dsa_idx_bf16 *q, const dsa_idx_bf16 *k, const dsa_idx_bf16 *w,
+                       int64_t T, int topk, int32_t *idx, float *scores, void *ws,
+                       size_t ws_bytes, void *stream);
+
+/* Ragged (varlen) form: B sequences packed back to back.  cu_seqlens (device, int32
+ * [B+1], non-decreasing, cu_seqlens[0] = 0, cu_seqlens[B] = total) delimits them;
+ * max_seqlen bounds every length.  Scoring is causal inside each sequence and never
+ * crosses sequences; returned indices are relative to the sequence start.  q, k, w,
+ * idx and scores are the packed [total][...] arrays of dsa_idx_score_topk. */
+int dsa_idx_score_topk_varlen(const dsa_idx_bf16 *q, const dsa_idx_bf16 *k,
+                              const dsa_idx_bf16 *w, const int32_t *cu_seqlens, int B,
+                              int max_seqlen, int64_t total, int topk, int32_t *idx,
+                              float *scores, void *ws, size_t ws_bytes, void *stream);
+
+/* Decode: one new query per sequence against that sequence's cached keys.
+ *   q [B][32][128], w [B][32]      the new tokens' projections (from dsa_idx_project)
+ *   k_cache [*][128]               cache rows; sequence b owns rows
+ *                                  [start[b], start[b] + seqlens[b]), whose last row is
+ *                                  the new token's own key (written by dsa_idx_project
+ *                                  through k_slot)
+ *   start   (device, int64 [B]), seqlens (device, int32 [B], 1 <= seqlens[b] <= max_seqlen)
+ *   idx [B][topk], scores [B][topk] (may be NULL): as for prefill row seqlens[b] - 1,
+ *   indices relative to start[b].
+ * The cached keys are the per-layer indexer keys that serving engines keep across steps. */
+int dsa_idx_decode(const dsa_idx_bf16 *q, const dsa_idx_bf16 *w, const dsa_idx_bf16 *k_cache,
+                   const int64_t *start, const int32_t *seqlens, int B, int max_seqlen,
+                   int topk, int32_t *idx, float *scores, void *ws, size_t ws_bytes,
+                   void *stream);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* DSAIDX_H */

@@ -1,0 +1,225 @@
+"""Python binding of libdsaidx, the MI355X (gfx950) DSA lightning indexer forward pass.
+
+Every function here is argument marshalling only: it checks dtypes and shapes, allocates
+outputs and workspace with torch (torch supplies device memory and the current stream),
+and calls the C-ABI entry point of the same name in ``libdsaidx.so``.  All computation
+runs in the library's HIP kernels; there is no CPU or PyTorch fallback, and importing
+fails loudly when the library has not been built.
+
+bf16 tensors are ``torch.bfloat16``; index outputs are int32 and scores float32.
+"""
+import ctypes
+import os
+
+import torch
+
+__all__ = ["version", "workspace_size", "project", "score_topk", "score_topk_varlen", "decode",
+           "HEADS", "DIM", "QLAT", "QOUT", "HIDDEN", "MAX_TOPK", "OP_PROJECT", "OP_SCORE_TOPK",
+           "OP_SCORE_TOPK_VARLEN", "OP_DECODE", "DsaIdxError", "lib"]
+
+HEADS, DIM, QLAT, QOUT, HIDDEN, MAX_TOPK = 32, 128, 1536, 4096, 7168, 2048
+OP_PROJECT, OP_SCORE_TOPK, OP_SCORE_TOPK_VARLEN, OP_DECODE = 0, 1, 2, 3
+
+_HERE = os.path.dirname(os.path.abspath(__file__))
+LIB_PATH = os.path.join(_HERE, "libdsaidx.so")
+
+
+class DsaIdxError(RuntimeError):
+    def __init__(self, fn, code, msg):
+        super().__init__(f"{fn} failed with status {code}: {msg}")
+        self.code = code
+
+
+class _Weights(ctypes.Structure):
+    _fields_ = [("W_q", ctypes.c_void_p), ("W_k", ctypes.c_void_p), ("W_w", ctypes.c_void_p),
+                ("ln_gamma", ctypes.c_void_p), ("ln_beta", ctypes.c_void_p),
+                ("ln_eps", ctypes.c_float)]
+
+
+_lib = None
+
+
+def lib():
+    """The loaded libdsaidx (raises if it was not built)."""
+    global _lib
+    if _lib is None:
+        if not os.path.exists(LIB_PATH):
+            raise ImportError(f"{LIB_PATH} is missing: build it with __graft_entry__.build() "
+                              "(hipcc --offload-arch=gfx950); there is no fallback path")
+        L = ctypes.CDLL(LIB_PATH)
+        vp, i64, i32, sz = ctypes.c_void_p, ctypes.c_int64, ctypes.c_int, ctypes.c_size_t
+        L.dsa_idx_version.restype = ctypes.c_char_p
+        L.dsa_idx_version.argtypes = []
+        L.dsa_idx_last_error.restype = ctypes.c_char_p
+        L.dsa_idx_last_error.argtypes = []
+        L.dsa_idx_workspace_size.restype = i32
+        L.dsa_idx_workspace_size.argtypes = [i32, i64, i32, i32, i32, ctypes.POINTER(sz)]
+        L.dsa_idx_project.restype = i32
+        L.dsa_idx_project.argtypes = [ctypes.POINTER(_Weights), vp, i64, vp, i64, i64, vp, vp, vp,
+                                      vp, vp, sz, vp]
+        L.dsa_idx_score_topk.restype = i32
+        L.dsa_idx_score_topk.argtypes = [vp, vp, vp, i64, i32, vp, vp, vp, sz, vp]
+        L.dsa_idx_score_topk_varlen.restype = i32
+        L.dsa_idx_score_topk_varlen.argtypes = [vp, vp, vp, vp, i32, i32, i64, i32, vp, vp, vp,
+                                                sz, vp]
+        L.dsa_idx_decode.restype = i32
+        L.dsa_idx_decode.argtypes = [vp, vp, vp, vp, vp, i32, i32, i32, vp, vp, vp, sz, vp]
+        _lib = L
+    return _lib
+
+
+def version():
+    return lib().dsa_idx_version().decode()
+
+
+def _check(fn, code):
+    if code != 0:
+        raise DsaIdxError(fn, code, lib().dsa_idx_last_error().decode())
+
+
+def workspace_size(op, total_tokens=0, B=0, max_seqlen=0, topk=MAX_TOPK):
+    n = ctypes.c_size_t(0)
+    _check("dsa_idx_workspace_size",
+           lib().dsa_idx_workspace_size(op, int(total_tokens), int(B), int(max_seqlen), int(topk),
+                                        ctypes.byref(n)))
+    return n.value
+
+
+def _ptr(t):
+    return None if t is None else t.data_ptr()
+
+
+def _stream(stream):
+    s = torch.cuda.current_stream() if stream is None else stream
+    return s.cuda_stream
+
+
+def _need(t, name, dtype, shape=None, contiguous=True):
+    if not isinstance(t, torch.Tensor) or not t.is_cuda:
+        raise TypeError(f"{name} must be a CUDA (HIP) tensor")
+    if t.dtype != dtype:
+        raise TypeError(f"{name} must be {dtype}, got {t.dtype}")
+    if shape is not None and tuple(t.shape) != tuple(shape):
+        raise ValueError(f"{name} must have shape {tuple(shape)}, got {tuple(t.shape)}")
+    if contiguous and not t.is_contiguous():
+        raise ValueError(f"{name} must be contiguous")
+
+
+def _workspace(nbytes, device, ws):
+    if nbytes == 0:
+        return None
+    if ws is not None:
+        if ws.numel() * ws.element_size() < nbytes:
+            raise ValueError(f"workspace of {ws.numel() * ws.element_size()} bytes < {nbytes}")
+        return ws
+    return torch.empty(nbytes, dtype=torch.uint8, device=device)
+
+
+def project(x, c_q, weights, q=None, k_out=None, k_slot=None, w=None, stream=None):
+    """q [T,32,128], k [T,128] (or rows k_slot of k_out), w [T,32] of one indexer layer.
+
+    x [T,>=7168] and c_q [T,>=1536] are bf16 with unit stride along the row;
+    weights = dict(W_q, W_k, W_w, gamma, beta, eps).  Returns (q, k_out, w).
+    """
+    T = x.shape[0]
+    dev = x.device
+    _need(x, "x", torch.bfloat16, contiguous=False)
+    _need(c_q, "c_q", torch.bfloat16, contiguous=False)
+    if x.stride(1) != 1 or c_q.stride(1) != 1 or c_q.shape[0] != T:
+        raise ValueError("x and c_q need unit column stride and equal row counts")
+    W = weights
+    _need(W["W_q"], "W_q", torch.bfloat16, (QLAT, QOUT))
+    _need(W["W_k"], "W_k", torch.bfloat16, (HIDDEN, DIM))
+    _need(W["W_w"], "W_w", torch.bfloat16, (HIDDEN, HEADS))
+    _need(W["gamma"], "gamma", torch.bfloat16, (DIM,))
+    _need(W["beta"], "beta", torch.bfloat16, (DIM,))
+    q = torch.empty((T, HEADS, DIM), dtype=torch.bfloat16, device=dev) if q is None else q
+    w = torch.empty((T, HEADS), dtype=torch.bfloat16, device=dev) if w is None else w
+    if k_out is None:
+        k_out = torch.empty((T, DIM), dtype=torch.bfloat16, device=dev)
+    _need(q, "q", torch.bfloat16, (T, HEADS, DIM))
+    _need(w, "w", torch.bfloat16, (T, HEADS))
+    _need(k_out, "k_out", torch.bfloat16)
+    if k_out.dim() != 2 or k_out.shape[1] != DIM:
+        raise ValueError("k_out must be [rows, 128]")
+    if k_slot is not None:
+        _need(k_slot, "k_slot", torch.int64, (T,))
+    elif k_out.shape[0] < T:
+        raise ValueError("k_out has fewer than T rows")
+    wt = _Weights(_ptr(W["W_q"]), _ptr(W["W_k"]), _ptr(W["W_w"]), _ptr(W["gamma"]),
+                  _ptr(W["beta"]), float(W["eps"]))
+    nbytes = workspace_size(OP_PROJECT, T)
+    ws = _workspace(nbytes, dev, None)
+    _check("dsa_idx_project",
+           lib().dsa_idx_project(ctypes.byref(wt), _ptr(x), x.stride(0), _ptr(c_q), c_q.stride(0),
+                                 T, _ptr(q), _ptr(k_out), _ptr(k_slot), _ptr(w), _ptr(ws), nbytes,
+                                 _stream(stream)))
+    return q, k_out, w
+
+
+def score_topk(q, k, w, topk=MAX_TOPK, with_scores=True, ws=None, out=None, stream=None):
+    """Causal top-k of one sequence: q [T,32,128], k [T,128], w [T,32] -> idx [T,topk] int32,
+    scores [T,topk] float32 (or None)."""
+    T = q.shape[0]
+    _need(q, "q", torch.bfloat16, (T, HEADS, DIM))
+    _need(k, "k", torch.bfloat16, (T, DIM))
+    _need(w, "w", torch.bfloat16, (T, HEADS))
+    if out is None:
+        idx = torch.empty((T, topk), dtype=torch.int32, device=q.device)
+        sc = torch.empty((T, topk), dtype=torch.float32, device=q.device) if with_scores else None
+    else:
+        idx, sc = out
+    nbytes = workspace_size(OP_SCORE_TOPK, T, topk=topk)
+    ws = _workspace(nbytes, q.device, ws)
+    _check("dsa_idx_score_topk",
+           lib().dsa_idx_score_topk(_ptr(q), _ptr(k), _ptr(w), T, topk, _ptr(idx), _ptr(sc),
+                                    _ptr(ws), nbytes, _stream(stream)))
+    return idx, sc
+
+
+def score_topk_varlen(q, k, w, cu_seqlens, max_seqlen, topk=MAX_TOPK, with_scores=True, ws=None,
+                      out=None, stream=None):
+    """Packed sequences delimited by cu_seqlens (int32 [B+1] on the device); indices are
+    relative to each sequence's start."""
+    total = q.shape[0]
+    _need(q, "q", torch.bfloat16, (total, HEADS, DIM))
+    _need(k, "k", torch.bfloat16, (total, DIM))
+    _need(w, "w", torch.bfloat16, (total, HEADS))
+    _need(cu_seqlens, "cu_seqlens", torch.int32)
+    B = cu_seqlens.numel() - 1
+    if out is None:
+        idx = torch.empty((total, topk), dtype=torch.int32, device=q.device)
+        sc = torch.empty((total, topk), dtype=torch.float32, device=q.device) if with_scores else None
+    else:
+        idx, sc = out
+    nbytes = workspace_size(OP_SCORE_TOPK_VARLEN, total, B, max_seqlen, topk)
+    ws = _workspace(nbytes, q.device, ws)
+    _check("dsa_idx_score_topk_varlen",
+           lib().dsa_idx_score_topk_varlen(_ptr(q), _ptr(k), _ptr(w), _ptr(cu_seqlens), B,
+                                           int(max_seqlen), total, topk, _ptr(idx), _ptr(sc),
+                                           _ptr(ws), nbytes, _stream(stream)))
+    return idx, sc
+
+
+def decode(q, w, k_cache, start, seqlens, max_seqlen, topk=MAX_TOPK, with_scores=True, ws=None,
+           out=None, stream=None):
+    """One query per sequence against its cached keys: q [B,32,128], w [B,32],
+    k_cache [*,128], start int64 [B], seqlens int32 [B] (own key included)."""
+    B = q.shape[0]
+    _need(q, "q", torch.bfloat16, (B, HEADS, DIM))
+    _need(w, "w", torch.bfloat16, (B, HEADS))
+    _need(k_cache, "k_cache", torch.bfloat16)
+    _need(start, "start", torch.int64, (B,))
+    _need(seqlens, "seqlens", torch.int32, (B,))
+    if out is None:
+        idx = torch.empty((B, topk), dtype=torch.int32, device=q.device)
+        sc = torch.empty((B, topk), dtype=torch.float32, device=q.device) if with_scores else None
+    else:
+        idx, sc = out
+    nbytes = workspace_size(OP_DECODE, 0, B, max_seqlen, topk)
+    ws = _workspace(nbytes, q.device, ws)
+    _check("dsa_idx_decode",
+           lib().dsa_idx_decode(_ptr(q), _ptr(w), _ptr(k_cache), _ptr(start), _ptr(seqlens), B,
+                                int(max_seqlen), topk, _ptr(idx), _ptr(sc), _ptr(ws), nbytes,
+                                _stream(stream)))
+    return idx, sc

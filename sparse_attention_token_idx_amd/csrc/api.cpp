@@ -1,0 +1,219 @@
+// C-ABI of libdsaidx: argument validation, workspace sizing, device check, error state and
+// dispatch to the HIP kernels.  The contract of every entry point is documented in
+// include/dsaidx.h.  Validation runs entirely on the host before any HIP call, so a
+// rejected call touches neither the device nor the outputs.
+#include "../../include/dsaidx.h"
+
+#include <hip/hip_runtime.h>
+
+#include <cstdarg>
+#include <cstdio>
+#include <cstring>
+#include <mutex>
+
+#include "launch.hpp"
+
+namespace {
+
+thread_local char g_err[512] = "";
+
+int fail(int code, const char *fmt, ...) {
+    va_list ap;
+    va_start(ap, fmt);
+    vsnprintf(g_err, sizeof(g_err), fmt, ap);
+    va_end(ap);
+    return code;
+}
+
+int ok() { return DSA_IDX_OK; }
+
+bool aligned16(const void *p) { return (reinterpret_cast<uintptr_t>(p) & 15u) == 0; }
+
+int hip_fail(const char *what, hipError_t e) {
+    return fail(DSA_IDX_EHIP, "%s: %s", what, hipGetErrorString(e));
+}
+
+// gfx950 check, cached per device.
+int check_device() {
+    int dev = 0;
+    hipError_t e = hipGetDevice(&dev);
+    if (e != hipSuccess) return hip_fail("hipGetDevice", e);
+    static std::mutex mu;
+    static int state[64] = {0};   // 0 unknown, 1 ok, 2 unsupported
+    if (dev < 0 || dev >= 64) return fail(DSA_IDX_EUNSUPPORTED, "device ordinal %d out of range", dev);
+    std::lock_guard<std::mutex> lk(mu);
+    if (state[dev] == 0) {
+        hipDeviceProp_t p;
+        e = hipGetDeviceProperties(&p, dev);
+        if (e != hipSuccess) return hip_fail("hipGetDeviceProperties", e);
+        state[dev] = strncmp(p.gcnArchName, "gfx950", 6) == 0 ? 1 : 2;
+        if (state[dev] == 2)
+            return fail(DSA_IDX_EUNSUPPORTED, "device %d is %s; libdsaidx runs on gfx950 only", dev,
+                        p.gcnArchName);
+    }
+    if (state[dev] == 2) return fail(DSA_IDX_EUNSUPPORTED, "device %d is not gfx950", dev);
+    return ok();
+}
+
+int check_topk(int topk) {
+    if (topk < 1 || topk > DSA_IDX_MAX_TOPK)
+        return fail(DSA_IDX_EUNSUPPORTED, "topk=%d outside [1, %d]", topk, DSA_IDX_MAX_TOPK);
+    return ok();
+}
+
+// Longest sequence the prefill grid can address (row blocks of 32 on grid.y).
+constexpr int64_t kMaxSeq = 65535LL * 32;
+
+size_t ws_score_topk(int64_t total, int topk) {
+    const int cap = dsaidx::candidate_capacity(topk);
+    return (size_t)total * (size_t)cap * 8u;
+}
+
+size_t ws_decode(int B, int max_seqlen) { return (size_t)B * (size_t)max_seqlen * 4u; }
+
+}  // namespace
+
+extern "C" {
+
+const char *dsa_idx_version(void) { return "libdsaidx 0.1.0 (gfx950)"; }
+
+const char *dsa_idx_last_error(void) { return g_err; }
+
+int dsa_idx_workspace_size(int op, int64_t total_tokens, int B, int max_seqlen, int topk,
+                           size_t *bytes) {
+    if (!bytes) return fail(DSA_IDX_EINVAL, "bytes is NULL");
+    switch (op) {
+        case DSA_IDX_OP_PROJECT:
+            if (total_tokens < 0) return fail(DSA_IDX_EINVAL, "T=%lld < 0", (long long)total_tokens);
+            *bytes = 0;
+            return ok();
+        case DSA_IDX_OP_SCORE_TOPK:
+        case DSA_IDX_OP_SCORE_TOPK_VARLEN: {
+            if (total_tokens < 0) return fail(DSA_IDX_EINVAL, "total=%lld < 0", (long long)total_tokens);
+            int r = check_topk(topk);
+            if (r) return r;
+            *bytes = ws_score_topk(total_tokens, topk);
+            return ok();
+        }
+        case DSA_IDX_OP_DECODE: {
+            if (B < 0 || max_seqlen < 0) return fail(DSA_IDX_EINVAL, "B=%d max_seqlen=%d", B, max_seqlen);
+            int r = check_topk(topk);
+            if (r) return r;
+            *bytes = ws_decode(B, max_seqlen);
+            return ok();
+        }
+        default:
+            return fail(DSA_IDX_EINVAL, "unknown op %d", op);
+    }
+}
+
+int dsa_idx_project(const dsa_idx_weights *wt, const dsa_idx_bf16 *x, int64_t ldx,
+                    const dsa_idx_bf16 *c_q, int64_t ldc, int64_t T, dsa_idx_bf16 *q,
+                    dsa_idx_bf16 *k_base, const int64_t *k_slot, dsa_idx_bf16 *w, void *ws,
+                    size_t ws_bytes, void *stream) {
+    (void)ws;
+    (void)ws_bytes;
+    if (!wt) return fail(DSA_IDX_EINVAL, "weights is NULL");
+    if (T < 0) return fail(DSA_IDX_EINVAL, "T=%lld < 0", (long long)T);
+    if (T == 0) return ok();
+    if (!wt->W_q || !wt->W_k || !wt->W_w || !wt->ln_gamma || !wt->ln_beta)
+        return fail(DSA_IDX_EINVAL, "a weight pointer is NULL");
+    if (!x || !c_q || !q || !k_base || !w) return fail(DSA_IDX_EINVAL, "a tensor pointer is NULL");
+    if (ldx < DSA_IDX_HIDDEN || ldx % 8) return fail(DSA_IDX_EINVAL, "ldx=%lld must be >= 7168 and a multiple of 8", (long long)ldx);
+    if (ldc < DSA_IDX_QLAT || ldc % 8) return fail(DSA_IDX_EINVAL, "ldc=%lld must be >= 1536 and a multiple of 8", (long long)ldc);
+    if (!(wt->ln_eps > 0.f)) return fail(DSA_IDX_EINVAL, "ln_eps must be > 0");
+    const void *ptrs[] = {x, c_q, q, k_base, w, wt->W_q, wt->W_k, wt->W_w};
+    for (const void *p : ptrs)
+        if (!aligned16(p)) return fail(DSA_IDX_EINVAL, "tensor pointer %p is not 16-byte aligned", p);
+    if (T > (int64_t)INT32_MAX * 128) return fail(DSA_IDX_EUNSUPPORTED, "T=%lld too large", (long long)T);
+    int r = check_device();
+    if (r) return r;
+    hipError_t e = dsaidx::launch_project(x, ldx, c_q, ldc, T, wt->W_q, wt->W_k, wt->W_w, wt->ln_gamma,
+                                          wt->ln_beta, wt->ln_eps, q, k_base, k_slot, w,
+                                          reinterpret_cast<hipStream_t>(stream));
+    if (e != hipSuccess) return hip_fail("project launch", e);
+    return ok();
+}
+
+static int score_common(const dsa_idx_bf16 *q, const dsa_idx_bf16 *k, const dsa_idx_bf16 *w,
+                        int32_t *idx, int topk, int64_t total, void *ws, size_t ws_bytes) {
+    int r = check_topk(topk);
+    if (r) return r;
+    if (total == 0) return ok();
+    if (!q || !k || !w || !idx) return fail(DSA_IDX_EINVAL, "a tensor pointer is NULL");
+    if (!aligned16(q) || !aligned16(k) || !aligned16(w))
+        return fail(DSA_IDX_EINVAL, "q, k and w must be 16-byte aligned");
+    const size_t need = ws_score_topk(total, topk);
+    if (!ws || ws_bytes < need)
+        return fail(DSA_IDX_EWORKSPACE, "workspace %zu bytes < %zu needed", ws ? ws_bytes : (size_t)0, need);
+    if (!aligned16(ws)) return fail(DSA_IDX_EINVAL, "workspace must be 16-byte aligned");
+    return ok();
+}
+
+int dsa_idx_score_topk(const dsa_idx_bf16 *q, const dsa_idx_bf16 *k, const dsa_idx_bf16 *w,
+                       int64_t T, int topk, int32_t *idx, float *scores, void *ws,
+                       size_t ws_bytes, void *stream) {
+    if (T < 0) return fail(DSA_IDX_EINVAL, "T=%lld < 0", (long long)T);
+    int r = score_common(q, k, w, idx, topk, T, ws, ws_bytes);
+    if (r || T == 0) return r;
+    if (T > kMaxSeq) return fail(DSA_IDX_EUNSUPPORTED, "T=%lld above %lld", (long long)T, (long long)kMaxSeq);
+    r = check_device();
+    if (r) return r;
+    const int cap = dsaidx::candidate_capacity(topk);
+    uint32_t *ck = static_cast<uint32_t *>(ws);
+    int32_t *ci = reinterpret_cast<int32_t *>(ck + (size_t)T * cap);
+    hipError_t e = dsaidx::launch_score_topk(q, k, w, nullptr, 1, T, T, topk, cap, ck, ci, idx, scores,
+                                             reinterpret_cast<hipStream_t>(stream));
+    if (e != hipSuccess) return hip_fail("score_topk launch", e);
+    return ok();
+}
+
+int dsa_idx_score_topk_varlen(const dsa_idx_bf16 *q, const dsa_idx_bf16 *k,
+                              const dsa_idx_bf16 *w, const int32_t *cu_seqlens, int B,
+                              int max_seqlen, int64_t total, int topk, int32_t *idx,
+                              float *scores, void *ws, size_t ws_bytes, void *stream) {
+    if (B < 0 || max_seqlen < 0 || total < 0)
+        return fail(DSA_IDX_EINVAL, "B=%d max_seqlen=%d total=%lld must be >= 0", B, max_seqlen, (long long)total);
+    if (B > 0 && !cu_seqlens) return fail(DSA_IDX_EINVAL, "cu_seqlens is NULL");
+    if (B > 65535) return fail(DSA_IDX_EUNSUPPORTED, "B=%d above 65535", B);
+    int r = score_common(q, k, w, idx, topk, total, ws, ws_bytes);
+    if (r || total == 0 || B == 0 || max_seqlen == 0) return r;
+    if (max_seqlen > kMaxSeq) return fail(DSA_IDX_EUNSUPPORTED, "max_seqlen=%d above %lld", max_seqlen, (long long)kMaxSeq);
+    r = check_device();
+    if (r) return r;
+    const int cap = dsaidx::candidate_capacity(topk);
+    uint32_t *ck = static_cast<uint32_t *>(ws);
+    int32_t *ci = reinterpret_cast<int32_t *>(ck + (size_t)total * cap);
+    hipError_t e = dsaidx::launch_score_topk(q, k, w, cu_seqlens, B, max_seqlen, total, topk, cap, ck, ci,
+                                             idx, scores, reinterpret_cast<hipStream_t>(stream));
+    if (e != hipSuccess) return hip_fail("score_topk_varlen launch", e);
+    return ok();
+}
+
+int dsa_idx_decode(const dsa_idx_bf16 *q, const dsa_idx_bf16 *w, const dsa_idx_bf16 *k_cache,
+                   const int64_t *start, const int32_t *seqlens, int B, int max_seqlen,
+                   int topk, int32_t *idx, float *scores, void *ws, size_t ws_bytes,
+                   void *stream) {
+    if (B < 0 || max_seqlen < 0) return fail(DSA_IDX_EINVAL, "B=%d max_seqlen=%d must be >= 0", B, max_seqlen);
+    int r = check_topk(topk);
+    if (r) return r;
+    if (B == 0) return ok();
+    if (max_seqlen < 1) return fail(DSA_IDX_EINVAL, "max_seqlen must be >= 1");
+    if (!q || !w || !k_cache || !start || !seqlens || !idx) return fail(DSA_IDX_EINVAL, "a tensor pointer is NULL");
+    if (!aligned16(q) || !aligned16(w) || !aligned16(k_cache))
+        return fail(DSA_IDX_EINVAL, "q, w and k_cache must be 16-byte aligned");
+    if (B > 65535) return fail(DSA_IDX_EUNSUPPORTED, "B=%d above 65535", B);
+    const size_t need = ws_decode(B, max_seqlen);
+    if (!ws || ws_bytes < need)
+        return fail(DSA_IDX_EWORKSPACE, "workspace %zu bytes < %zu needed", ws ? ws_bytes : (size_t)0, need);
+    if (!aligned16(ws)) return fail(DSA_IDX_EINVAL, "workspace must be 16-byte aligned");
+    r = check_device();
+    if (r) return r;
+    hipError_t e = dsaidx::launch_decode(q, w, k_cache, start, seqlens, B, max_seqlen, topk,
+                                         static_cast<float *>(ws), idx, scores,
+                                         reinterpret_cast<hipStream_t>(stream));
+    if (e != hipSuccess) return hip_fail("decode launch", e);
+    return ok();
+}
+
+}  // extern "C"

@@ -1,0 +1,94 @@
+// Device-side building blocks shared by the libdsaidx kernels (gfx950 / CDNA4 only).
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+namespace dsaidx {
+
+constexpr int kHeads = 32;
+constexpr int kDim = 128;
+constexpr int kQLat = 1536;
+constexpr int kQOut = 4096;
+constexpr int kHidden = 7168;
+constexpr int kMaxTopk = 2048;
+
+typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
+typedef float f32x4 __attribute__((ext_vector_type(4)));
+typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
+typedef uint32_t u32x2 __attribute__((ext_vector_type(2)));
+
+// ---------------------------------------------------------------- bf16
+__device__ __forceinline__ float bf16_to_f32(uint32_t bits16) {
+    return __uint_as_float(bits16 << 16);
+}
+
+// fp32 -> bf16, round to nearest even (finite inputs; NaN stays a quiet NaN).
+__device__ __forceinline__ uint32_t f32_to_bf16(float f) {
+    uint32_t u = __float_as_uint(f);
+    if ((u & 0x7F800000u) == 0x7F800000u) return (u >> 16) | ((u & 0xFFFFu) ? 0x40u : 0u);
+    u += 0x7FFFu + ((u >> 16) & 1u);
+    return u >> 16;
+}
+
+__device__ __forceinline__ uint32_t pack_bf16x2(float lo, float hi) {
+    return f32_to_bf16(lo) | (f32_to_bf16(hi) << 16);
+}
+
+// ---------------------------------------------------------------- MFMA
+// D(16x16) += A(16x32) * B(32x16), bf16 inputs, fp32 accumulate.  Lane l supplies
+// A[l % 16][kk] and B[kk][l % 16] for the 8 values kk of its k-slot (any assignment of
+// the 32 k values to (lane / 16, element) works as long as A and B use the same one),
+// and receives D[4 * (l / 16) + r][l % 16] in element r.
+__device__ __forceinline__ f32x4 mfma16x16x32(u32x4 a, u32x4 b, f32x4 c) {
+    return __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8, a),
+                                                  __builtin_bit_cast(bf16x8, b), c, 0, 0, 0);
+}
+
+// ---------------------------------------------------------------- ordering keys
+// Monotone map fp32 -> uint32 (larger score -> larger key); -0 is mapped as +0 so the two
+// zeros tie.  NaN is outside the contract.
+__device__ __forceinline__ uint32_t score_key(float v) {
+    uint32_t u = __float_as_uint(v);
+    if (u == 0x80000000u) u = 0u;
+    return (u & 0x80000000u) ? ~u : (u | 0x80000000u);
+}
+
+__device__ __forceinline__ float key_score(uint32_t k) {
+    uint32_t u = (k & 0x80000000u) ? (k & 0x7FFFFFFFu) : ~k;
+    return __uint_as_float(u);
+}
+
+// ---------------------------------------------------------------- wave64 helpers
+__device__ __forceinline__ int lane_id() { return __lane_id(); }
+
+// Number of set bits of `mask` in lanes strictly below the calling lane.
+__device__ __forceinline__ uint32_t bits_below(uint64_t mask) {
+    return __builtin_amdgcn_mbcnt_hi((uint32_t)(mask >> 32),
+                                     __builtin_amdgcn_mbcnt_lo((uint32_t)mask, 0u));
+}
+
+__device__ __forceinline__ uint64_t ballot(bool p) { return __ballot(p); }
+
+__device__ __forceinline__ int readlane(int v, int lane) {
+    return __builtin_amdgcn_readlane(v, lane);
+}
+
+// Inclusive prefix sum across the 64 lanes.
+__device__ __forceinline__ int wave_inclusive_sum(int v) {
+    const int l = lane_id();
+#pragma unroll
+    for (int d = 1; d < 64; d <<= 1) {
+        int o = __shfl_up(v, d, 64);
+        if (l >= d) v += o;
+    }
+    return v;
+}
+
+__device__ __forceinline__ int wave_sum(int v) {
+#pragma unroll
+    for (int d = 32; d >= 1; d >>= 1) v += __shfl_xor(v, d, 64);
+    return v;
+}
+
+}  // namespace dsaidx

@@ -1,0 +1,324 @@
+// Indexer projections: q = c_q W_q (1,536 -> 4,096), k = LayerNorm(x W_k) (7,168 -> 128),
+// w = x W_w (7,168 -> 32), as listed for the Kimi K3.1 Pro indexer on the
+// "Qwen3.5-397B-A17B vs Kimi K3.1 Pro" compare page (sparse/compressed-attention row; the
+// LayerNorm on the key is the QK-norm row).  bf16 in, fp32 accumulation on
+// v_mfma_f32_16x16x32_bf16, bf16 (round to nearest even) out.
+//
+// One tiled GEMM serves both products.  The weights arrive [K][N] (N contiguous) while the
+// MFMA wants 8 consecutive k per lane for both operands, so each B tile is transposed on
+// its way into LDS: a thread loads an 8(k) x 8(n) block with 16-byte loads, transposes it
+// in registers and writes 8 k-contiguous 16-byte chunks.  Both LDS tiles are stored as
+// 128-byte rows of eight 16-byte chunks, chunk c of row r at slot c ^ (r & 7), which keeps
+// the 16-byte MFMA operand reads and the transposed writes free of bank conflicts.
+// The k/w product (N = 160) keeps whole rows in one wave, so the LayerNorm over the 128
+// key columns runs in the epilogue on the fp32 accumulators before rounding.
+#include "common.hpp"
+#include "launch.hpp"
+
+namespace dsaidx {
+namespace {
+
+constexpr int kBK = 64;  // k per LDS tile (8 chunks of 8)
+
+__device__ __forceinline__ int swz(int row, int chunk) { return row * 64 + 8 * (chunk ^ (row & 7)); }
+
+template <int BM, int BN>
+struct GemmSmem {
+    uint16_t a[2][BM * kBK];
+    uint16_t b[2][BN * kBK];
+};
+
+// C tile = A[m0:m0+BM, :] x B[:, n0:n0+BN]; wave (wm, wn) of a WM x WN grid owns a
+// (BM/WM) x (BN/WN) sub-tile as SM x SN MFMA tiles of 16 x 16.
+template <int BM, int BN, int WM, int WN>
+struct GemmCore {
+    static constexpr int SM = BM / WM / 16;
+    static constexpr int SN = BN / WN / 16;
+    static constexpr int A_CHUNKS = BM * 8 / 256;   // 16-byte A chunks per thread per tile
+
+    __device__ static void run(const uint16_t *__restrict__ A, int64_t lda, int64_t M, int64_t m0,
+                               const uint16_t *__restrict__ B, int N, int n0, int K,
+                               GemmSmem<BM, BN> &sm, f32x4 (&acc)[SM][SN]) {
+        const int tid = threadIdx.x;
+        const int wave = tid >> 6, lane = tid & 63;
+        const int wm = wave / WN, wn = wave % WN;
+        const int l16 = lane & 15, lg = lane >> 4;
+#pragma unroll
+        for (int i = 0; i < SM; ++i)
+#pragma unroll
+            for (int j = 0; j < SN; ++j) acc[i][j] = f32x4{0.f, 0.f, 0.f, 0.f};
+
+        u32x4 ra[A_CHUNKS];
+        u32x4 rb[8];
+        const bool b_thread = tid < BN;
+        const int bkb = tid & 7, bnb = tid >> 3;   // B block: k rows 8*bkb.., n cols 8*bnb..
+        auto load = [&](int kt) {
+            const int k0 = kt * kBK;
+#pragma unroll
+            for (int i = 0; i < A_CHUNKS; ++i) {
+                const int c = tid + 256 * i;
+                const int row = c >> 3, kc = c & 7;
+                const int64_t gm = m0 + row;
+                ra[i] = gm < M ? *reinterpret_cast<const u32x4 *>(A + gm * lda + k0 + 8 * kc)
+                               : u32x4{0u, 0u, 0u, 0u};
+            }
+            if (b_thread) {
+#pragma unroll
+                for (int i = 0; i < 8; ++i)
+                    rb[i] = *reinterpret_cast<const u32x4 *>(B + (int64_t)(k0 + 8 * bkb + i) * N + n0 + 8 * bnb);
+            }
+        };
+        auto store = [&](int buf) {
+#pragma unroll
+            for (int i = 0; i < A_CHUNKS; ++i) {
+                const int c = tid + 256 * i;
+                *reinterpret_cast<u32x4 *>(&sm.a[buf][swz(c >> 3, c & 7)]) = ra[i];
+            }
+            if (b_thread) {
+#pragma unroll
+                for (int j = 0; j < 8; ++j) {
+                    // column j of the 8x8 block: element i = row i's bf16 j
+                    const int sh = 16 * (j & 1), dw = j >> 1;
+                    u32x4 o;
+#pragma unroll
+                    for (int m = 0; m < 4; ++m) {
+                        const uint32_t lo = (rb[2 * m][dw] >> sh) & 0xFFFFu;
+                        const uint32_t hi = (rb[2 * m + 1][dw] >> sh) & 0xFFFFu;
+                        o[m] = lo | (hi << 16);
+                    }
+                    *reinterpret_cast<u32x4 *>(&sm.b[buf][swz(8 * bnb + j, bkb)]) = o;
+                }
+            }
+        };
+
+        const int nk = K / kBK;
+        load(0);
+        store(0);
+        __syncthreads();
+        for (int kt = 0; kt < nk; ++kt) {
+            const int buf = kt & 1;
+            if (kt + 1 < nk) load(kt + 1);
+#pragma unroll
+            for (int ks = 0; ks < 2; ++ks) {
+                const int kc = 4 * ks + lg;
+                u32x4 af[SM], bf[SN];
+#pragma unroll
+                for (int i = 0; i < SM; ++i)
+                    af[i] = *reinterpret_cast<const u32x4 *>(&sm.a[buf][swz(wm * (BM / WM) + 16 * i + l16, kc)]);
+#pragma unroll
+                for (int j = 0; j < SN; ++j)
+                    bf[j] = *reinterpret_cast<const u32x4 *>(&sm.b[buf][swz(wn * (BN / WN) + 16 * j + l16, kc)]);
+#pragma unroll
+                for (int i = 0; i < SM; ++i)
+#pragma unroll
+                    for (int j = 0; j < SN; ++j) acc[i][j] = mfma16x16x32(af[i], bf[j], acc[i][j]);
+            }
+            if (kt + 1 < nk) store(buf ^ 1);
+            __syncthreads();
+        }
+    }
+};
+
+// q = bf16(c_q . W_q): 128 x 128 tiles, 2 x 2 waves of 64 x 64.
+__global__ __launch_bounds__(256) void proj_q_kernel(const uint16_t *__restrict__ cq, int64_t ldc,
+                                                     int64_t T, const uint16_t *__restrict__ Wq,
+                                                     uint16_t *__restrict__ q) {
+    using Core = GemmCore<128, 128, 2, 2>;
+    extern __shared__ __align__(16) unsigned char smem_raw[];
+    auto &sm = *reinterpret_cast<GemmSmem<128, 128> *>(smem_raw);
+    const int ntn = kQOut / 128;
+    const int64_t m0 = (int64_t)(blockIdx.x / ntn) * 128;
+    const int n0 = (blockIdx.x % ntn) * 128;
+    f32x4 acc[Core::SM][Core::SN];
+    Core::run(cq, ldc, T, m0, Wq, kQOut, n0, kQLat, sm, acc);
+
+    const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63;
+    const int wm = wave / 2, wn = wave % 2;
+    const int l16 = lane & 15, lg = lane >> 4;
+#pragma unroll
+    for (int i = 0; i < Core::SM; ++i)
+#pragma unroll
+        for (int r = 0; r < 4; ++r) {
+            const int64_t row = m0 + wm * 64 + 16 * i + 4 * lg + r;
+            if (row >= T) continue;
+#pragma unroll
+            for (int j = 0; j < Core::SN; ++j)
+                q[row * kQOut + n0 + wn * 64 + 16 * j + l16] = (uint16_t)f32_to_bf16(acc[i][j][r]);
+        }
+}
+
+// [k | w] = x . [W_k | W_w] (N = 128 + 32), LayerNorm on the k part: 128-row tiles, each
+// of the 4 waves owns 32 full rows.  The two weight matrices are read as one [7168][160]
+// operand whose first 16 column-chunks come from W_k and the last 4 from W_w.
+struct KWArgs {
+    const uint16_t *x;
+    int64_t ldx;
+    int64_t T;
+    const uint16_t *Wk;
+    const uint16_t *Ww;
+    const uint16_t *gamma;
+    const uint16_t *beta;
+    float eps;
+    uint16_t *k_base;
+    const int64_t *k_slot;
+    uint16_t *w;
+};
+
+__global__ __launch_bounds__(256) void proj_kw_kernel(KWArgs a) {
+    constexpr int BM = 128, BN = 160, SM = 2, SN = 10;
+    extern __shared__ __align__(16) unsigned char smem_raw[];
+    auto &sm = *reinterpret_cast<GemmSmem<BM, BN> *>(smem_raw);
+    const int64_t m0 = (int64_t)blockIdx.x * BM;
+    const int tid = threadIdx.x;
+    const int wave = tid >> 6, lane = tid & 63;
+    const int l16 = lane & 15, lg = lane >> 4;
+
+    f32x4 acc[SM][SN];
+#pragma unroll
+    for (int i = 0; i < SM; ++i)
+#pragma unroll
+        for (int j = 0; j < SN; ++j) acc[i][j] = f32x4{0.f, 0.f, 0.f, 0.f};
+
+    constexpr int A_CHUNKS = BM * 8 / 256;
+    u32x4 ra[A_CHUNKS];
+    u32x4 rb[8];
+    const bool b_thread = tid < BN;
+    const int bkb = tid & 7, bnb = tid >> 3;   // bnb in 0..19: 0..15 -> W_k, 16..19 -> W_w
+    auto load = [&](int kt) {
+        const int k0 = kt * kBK;
+#pragma unroll
+        for (int i = 0; i < A_CHUNKS; ++i) {
+            const int c = tid + 256 * i;
+            const int row = c >> 3, kc = c & 7;
+            const int64_t gm = m0 + row;
+            ra[i] = gm < a.T ? *reinterpret_cast<const u32x4 *>(a.x + gm * a.ldx + k0 + 8 * kc)
+                             : u32x4{0u, 0u, 0u, 0u};
+        }
+        if (b_thread) {
+            const uint16_t *src = bnb < 16 ? a.Wk + 8 * bnb : a.Ww + 8 * (bnb - 16);
+            const int ld = bnb < 16 ? kDim : kHeads;
+#pragma unroll
+            for (int i = 0; i < 8; ++i)
+                rb[i] = *reinterpret_cast<const u32x4 *>(src + (int64_t)(k0 + 8 * bkb + i) * ld);
+        }
+    };
+    auto store = [&](int buf) {
+#pragma unroll
+        for (int i = 0; i < A_CHUNKS; ++i) {
+            const int c = tid + 256 * i;
+            *reinterpret_cast<u32x4 *>(&sm.a[buf][swz(c >> 3, c & 7)]) = ra[i];
+        }
+        if (b_thread) {
+#pragma unroll
+            for (int j = 0; j < 8; ++j) {
+                const int sh = 16 * (j & 1), dw = j >> 1;
+                u32x4 o;
+#pragma unroll
+                for (int m = 0; m < 4; ++m) {
+                    const uint32_t lo = (rb[2 * m][dw] >> sh) & 0xFFFFu;
+                    const uint32_t hi = (rb[2 * m + 1][dw] >> sh) & 0xFFFFu;
+                    o[m] = lo | (hi << 16);
+                }
+                *reinterpret_cast<u32x4 *>(&sm.b[buf][swz(8 * bnb + j, bkb)]) = o;
+            }
+        }
+    };
+
+    const int nk = kHidden / kBK;
+    load(0);
+    store(0);
+    __syncthreads();
+    for (int kt = 0; kt < nk; ++kt) {
+        const int buf = kt & 1;
+        if (kt + 1 < nk) load(kt + 1);
+#pragma unroll
+        for (int ks = 0; ks < 2; ++ks) {
+            const int kc = 4 * ks + lg;
+            u32x4 af[SM], bf[SN];
+#pragma unroll
+            for (int i = 0; i < SM; ++i)
+                af[i] = *reinterpret_cast<const u32x4 *>(&sm.a[buf][swz(wave * 32 + 16 * i + l16, kc)]);
+#pragma unroll
+            for (int j = 0; j < SN; ++j)
+                bf[j] = *reinterpret_cast<const u32x4 *>(&sm.b[buf][swz(16 * j + l16, kc)]);
+#pragma unroll
+            for (int i = 0; i < SM; ++i)
+#pragma unroll
+                for (int j = 0; j < SN; ++j) acc[i][j] = mfma16x16x32(af[i], bf[j], acc[i][j]);
+        }
+        if (kt + 1 < nk) store(buf ^ 1);
+        __syncthreads();
+    }
+
+    // ---- epilogue: LayerNorm over the 128 key columns (mean-centred, biased variance)
+    float g[8], b[8];
+#pragma unroll
+    for (int j = 0; j < 8; ++j) {
+        g[j] = bf16_to_f32(a.gamma[16 * j + l16]);
+        b[j] = bf16_to_f32(a.beta[16 * j + l16]);
+    }
+#pragma unroll
+    for (int i = 0; i < SM; ++i)
+#pragma unroll
+        for (int r = 0; r < 4; ++r) {
+            const int64_t row = m0 + wave * 32 + 16 * i + 4 * lg + r;
+            float s = 0.f;
+#pragma unroll
+            for (int j = 0; j < 8; ++j) s += acc[i][j][r];
+#pragma unroll
+            for (int d = 1; d < 16; d <<= 1) s += __shfl_xor(s, d, 64);
+            const float mu = s * (1.0f / kDim);
+            float v = 0.f;
+#pragma unroll
+            for (int j = 0; j < 8; ++j) {
+                const float c = acc[i][j][r] - mu;
+                v = fmaf(c, c, v);
+            }
+#pragma unroll
+            for (int d = 1; d < 16; d <<= 1) v += __shfl_xor(v, d, 64);
+            const float inv = 1.0f / sqrtf(v * (1.0f / kDim) + a.eps);
+            if (row >= a.T) continue;
+            const int64_t slot = a.k_slot ? a.k_slot[row] : row;
+            uint16_t *kr = a.k_base + slot * kDim;
+#pragma unroll
+            for (int j = 0; j < 8; ++j)
+                kr[16 * j + l16] = (uint16_t)f32_to_bf16(fmaf((acc[i][j][r] - mu) * inv, g[j], b[j]));
+#pragma unroll
+            for (int j = 0; j < 2; ++j)
+                a.w[row * kHeads + 16 * j + l16] = (uint16_t)f32_to_bf16(acc[i][8 + j][r]);
+        }
+}
+
+}  // namespace
+
+hipError_t launch_project(const uint16_t *x, int64_t ldx, const uint16_t *c_q, int64_t ldc,
+                          int64_t T, const uint16_t *W_q, const uint16_t *W_k,
+                          const uint16_t *W_w, const uint16_t *gamma, const uint16_t *beta,
+                          float eps, uint16_t *q, uint16_t *k_base, const int64_t *k_slot,
+                          uint16_t *w, hipStream_t stream) {
+    if (T == 0) return hipSuccess;
+    static bool attr_done = false;
+    const size_t smem_q = sizeof(GemmSmem<128, 128>);
+    const size_t smem_kw = sizeof(GemmSmem<128, 160>);
+    if (!attr_done) {
+        hipError_t e = hipFuncSetAttribute(reinterpret_cast<const void *>(proj_q_kernel),
+                                           hipFuncAttributeMaxDynamicSharedMemorySize, (int)smem_q);
+        if (e != hipSuccess) return e;
+        e = hipFuncSetAttribute(reinterpret_cast<const void *>(proj_kw_kernel),
+                                hipFuncAttributeMaxDynamicSharedMemorySize, (int)smem_kw);
+        if (e != hipSuccess) return e;
+        attr_done = true;
+    }
+    const int64_t mt = (T + 127) / 128;
+    if (q) {
+        hipLaunchKernelGGL(proj_q_kernel, dim3((unsigned)(mt * (kQOut / 128))), dim3(256), smem_q,
+                           stream, c_q, ldc, T, W_q, q);
+        hipError_t e = hipGetLastError();
+        if (e != hipSuccess) return e;
+    }
+    KWArgs a{x, ldx, T, W_k, W_w, gamma, beta, eps, k_base, k_slot, w};
+    hipLaunchKernelGGL(proj_kw_kernel, dim3((unsigned)mt), dim3(256), smem_kw, stream, a);
+    return hipGetLastError();
+}
+
+}  // namespace dsaidx

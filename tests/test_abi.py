@@ -1,0 +1,110 @@
+"""The C-ABI library without a GPU: it loads, exports every declared symbol, sizes
+workspaces, and rejects bad arguments before touching any device."""
+import ctypes
+import os
+import re
+
+import pytest
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+HEADER = os.path.join(ROOT, "include", "dsaidx.h")
+
+
+@pytest.fixture(scope="module")
+def dsa():
+    import sparse_attention_token_idx_amd as m
+    if not os.path.exists(m.LIB_PATH):
+        from sparse_attention_token_idx_amd import build
+        build.build()
+    return m
+
+
+def declared_functions():
+    text = open(HEADER).read()
+    return sorted(set(re.findall(r"\b(dsa_idx_[a-z_]+)\s*\(", text)))
+
+
+def test_exports_every_declared_symbol(dsa):
+    L = dsa.lib()
+    names = declared_functions()
+    assert set(names) == {"dsa_idx_version", "dsa_idx_last_error", "dsa_idx_workspace_size",
+                          "dsa_idx_project", "dsa_idx_score_topk", "dsa_idx_score_topk_varlen",
+                          "dsa_idx_decode"}
+    for n in names:
+        assert getattr(L, n) is not None
+
+
+def test_version(dsa):
+    assert "gfx950" in dsa.version()
+
+
+def test_workspace_sizes(dsa):
+    assert dsa.workspace_size(dsa.OP_PROJECT, 100) == 0
+    # candidate lists: (2*topk rounded to 64) + 64 slots of 8 bytes per row
+    assert dsa.workspace_size(dsa.OP_SCORE_TOPK, 1000, topk=2048) == 1000 * 4160 * 8
+    assert dsa.workspace_size(dsa.OP_SCORE_TOPK_VARLEN, 10, 2, 8, topk=5) == 10 * 128 * 8
+    assert dsa.workspace_size(dsa.OP_DECODE, 0, 64, 131072, 2048) == 64 * 131072 * 4
+    with pytest.raises(dsa.DsaIdxError) as e:
+        dsa.workspace_size(dsa.OP_SCORE_TOPK, 10, topk=0)
+    assert e.value.code == -2
+    with pytest.raises(dsa.DsaIdxError) as e:
+        dsa.workspace_size(99, 10)
+    assert e.value.code == -1
+
+
+def _vp(x):
+    return ctypes.c_void_p(x)
+
+
+def test_rejections_before_device(dsa):
+    L = dsa.lib()
+    A = 0x10000   # a fake, aligned "device" address: never dereferenced on these paths
+    # topk out of range
+    assert L.dsa_idx_score_topk(_vp(A), _vp(A), _vp(A), 10, 0, _vp(A), None, _vp(A), 1 << 30, None) == -2
+    assert b"topk" in L.dsa_idx_last_error()
+    assert L.dsa_idx_score_topk(_vp(A), _vp(A), _vp(A), 10, 2049, _vp(A), None, _vp(A), 1 << 30, None) == -2
+    # negative T, null pointers, misalignment, small workspace
+    assert L.dsa_idx_score_topk(_vp(A), _vp(A), _vp(A), -1, 8, _vp(A), None, _vp(A), 1 << 30, None) == -1
+    assert L.dsa_idx_score_topk(None, _vp(A), _vp(A), 10, 8, _vp(A), None, _vp(A), 1 << 30, None) == -1
+    assert L.dsa_idx_score_topk(_vp(A + 2), _vp(A), _vp(A), 10, 8, _vp(A), None, _vp(A), 1 << 30, None) == -1
+    assert L.dsa_idx_score_topk(_vp(A), _vp(A), _vp(A), 10, 8, _vp(A), None, _vp(A), 10, None) == -3
+    assert b"workspace" in L.dsa_idx_last_error()
+    # T = 0 is a no-op that succeeds without a device
+    assert L.dsa_idx_score_topk(None, None, None, 0, 8, None, None, None, 0, None) == 0
+    # varlen
+    assert L.dsa_idx_score_topk_varlen(_vp(A), _vp(A), _vp(A), None, 2, 8, 10, 8, _vp(A), None,
+                                       _vp(A), 1 << 30, None) == -1
+    assert L.dsa_idx_score_topk_varlen(_vp(A), _vp(A), _vp(A), _vp(A), -1, 8, 10, 8, _vp(A), None,
+                                       _vp(A), 1 << 30, None) == -1
+    # decode
+    assert L.dsa_idx_decode(_vp(A), _vp(A), _vp(A), _vp(A), _vp(A), 4, 100, 0, _vp(A), None, _vp(A),
+                            1 << 30, None) == -2
+    assert L.dsa_idx_decode(_vp(A), _vp(A), _vp(A), None, _vp(A), 4, 100, 8, _vp(A), None, _vp(A),
+                            1 << 30, None) == -1
+    assert L.dsa_idx_decode(_vp(A), _vp(A), _vp(A), _vp(A), _vp(A), 4, 100, 8, _vp(A), None, _vp(A),
+                            16, None) == -3
+    assert L.dsa_idx_decode(None, None, None, None, None, 0, 0, 8, None, None, None, 0, None) == 0
+
+
+def test_project_rejections(dsa):
+    L = dsa.lib()
+    A = 0x10000
+    W = dsa._Weights(A, A, A, A, A, 1e-6)
+    args = lambda **kw: dict(dict(x=_vp(A), ldx=7168, c_q=_vp(A), ldc=1536, T=4, q=_vp(A),
+                                  k=_vp(A), slot=None, w=_vp(A)), **kw)
+
+    def call(wt=W, **kw):
+        a = args(**kw)
+        return L.dsa_idx_project(ctypes.byref(wt) if wt is not None else None, a["x"], a["ldx"],
+                                 a["c_q"], a["ldc"], a["T"], a["q"], a["k"], a["slot"], a["w"],
+                                 None, 0, None)
+    assert call(wt=None) == -1
+    assert call(T=-1) == -1
+    assert call(ldx=7000) == -1
+    assert call(ldx=7172) == -1          # not a multiple of 8
+    assert call(ldc=1535) == -1
+    assert call(q=None) == -1
+    assert call(x=_vp(A + 8)) == -1       # misaligned
+    W0 = dsa._Weights(A, A, A, A, A, 0.0)
+    assert call(wt=W0) == -1             # eps must be positive
+    assert call(T=0) == 0

@@ -1,0 +1,175 @@
+"""GPU parity of the fused causal score + top-k kernel against the CPU oracle."""
+import numpy as np
+import pytest
+import torch
+
+import oracle
+from oracle import D, H
+import synth
+from synth import workloads as wl
+from tests.helpers import check_row, to_dev, to_host
+
+pytestmark = pytest.mark.gpu
+
+
+def _bf(x):
+    return oracle.f64_to_bf16(np.asarray(x, dtype=np.float64))
+
+
+@pytest.fixture(scope="module")
+def dsa():
+    import sparse_attention_token_idx_amd as m
+    assert torch.cuda.is_available()
+    return m
+
+
+def _run(dsa, q, k, w, topk):
+    idx, sc = dsa.score_topk(to_dev(q), to_dev(k), to_dev(w), topk=topk)
+    torch.cuda.synchronize()
+    return idx.cpu().numpy(), sc.cpu().numpy()
+
+
+def test_hand_example_padded_exact(dsa, golden_hand):
+    gh = golden_hand
+    T = gh["T"]
+    q = np.zeros((T, H, D), np.uint16)
+    k = np.zeros((T, D), np.uint16)
+    w = np.zeros((T, H), np.uint16)
+    q[:, :2, :2] = _bf(gh["q"])
+    k[:, :2] = _bf(gh["k"])
+    w[:, :2] = _bf(gh["w"])
+    for name, kk in (("topk2", 2), ("topk1", 1)):
+        gi, gs = _run(dsa, q, k, w, kk)
+        for t in range(T):
+            sel = [int(i) for i in gi[t] if i >= 0]
+            assert sel == gh["expected_selection"][name][t]
+            assert gs[t][:len(sel)].tolist() == [gh["expected_scores"][t][s] for s in sel]
+    # default topk: every row keeps its whole prefix
+    gi, gs = _run(dsa, q, k, w, 2048)
+    for t in range(T):
+        assert gi[t][:t + 1].tolist() == list(range(t + 1))
+        assert gs[t][:t + 1].tolist() == gh["expected_scores"][t]
+    nv = gh["negative_w_variant"]
+    w2 = w.copy()
+    w2[nv["row"], :2] = _bf(nv["w"])
+    for name, kk in (("topk2", 2), ("topk1", 1)):
+        gi, gs = _run(dsa, q, k, w2, kk)
+        assert [int(i) for i in gi[2] if i >= 0] == nv["expected_selection"][name]
+
+
+@pytest.mark.parametrize("topk", [1, 7, 64])
+def test_integer_ties_exact(dsa, topk):
+    # small integers: every score is exact in fp32 and fp64, and ties are frequent, so the
+    # selection (ties -> lower index) must match the oracle bit for bit
+    rng = np.random.default_rng(topk)
+    T = 200
+    q = _bf(rng.integers(-2, 3, (T, H, D)))
+    k = _bf(rng.integers(-1, 2, (T, D)))
+    w = _bf(rng.integers(-2, 3, (T, H)) * 0.5)
+    gi, gs = _run(dsa, q, k, w, topk)
+    ref = oracle.prefill_rows(q, k, w, np.arange(T), topk=topk, full=True)
+    for t in range(T):
+        check_row(t, gi[t], gs[t], ref, t, topk, exact=True)
+
+
+@pytest.mark.parametrize("T", [1, 2, 63, 65, 97, 2047, 2048, 2049, 2113])
+def test_edge_lengths(dsa, T):
+    s = wl.score_inputs(T, seed=T)
+    gi, gs = _run(dsa, s["q"], s["k"], s["w"], 2048)
+    rows = sorted(set([0, 1, T // 2, T - 2, T - 1, 2046, 2047, 2048]) & set(range(T)))
+    ref = oracle.prefill_rows(s["q"], s["k"], s["w"], rows, topk=2048, full=True)
+    for r, t in enumerate(rows):
+        check_row(t, gi[t], gs[t], ref, r, 2048)
+
+
+def test_config1_all_rows(dsa):
+    """Score + top-k only, one causal sequence T=2560, q,k ~N(0,1), w ~N(0,0.1), seed 0."""
+    s = wl.score_inputs(2560, seed=0)
+    gi, gs = _run(dsa, s["q"], s["k"], s["w"], 2048)
+    rows = np.arange(2560)
+    ref = oracle.prefill_rows(s["q"], s["k"], s["w"], rows, topk=2048, full=True)
+    excused = sum(check_row(t, gi[t], gs[t], ref, t, 2048) for t in rows)
+    print(f"config 1: 2560 rows, {excused} band-excused index differences", flush=True)
+
+
+def test_small_topk_streaming(dsa):
+    # topk far below T forces many in-kernel compactions per row
+    s = wl.score_inputs(3000, seed=21)
+    for topk in (16, 300):
+        gi, gs = _run(dsa, s["q"], s["k"], s["w"], topk)
+        rows = [0, 15, 16, 17, 299, 300, 1000, 2999]
+        ref = oracle.prefill_rows(s["q"], s["k"], s["w"], rows, topk=topk, full=True)
+        for r, t in enumerate(rows):
+            check_row(t, gi[t], gs[t], ref, r, topk)
+
+
+def test_power_of_two_invariance_bitwise(dsa):
+    s = wl.score_inputs(2300, seed=4)
+    gi, gs = _run(dsa, s["q"], s["k"], s["w"], 2048)
+    w8 = oracle.f64_to_bf16(oracle.bf16_to_f64(s["w"]) * 8.0)
+    gi2, gs2 = _run(dsa, s["q"], s["k"], w8, 2048)
+    assert np.array_equal(gi, gi2)
+    assert np.array_equal(gs * 8.0, gs2)
+    kq = oracle.f64_to_bf16(oracle.bf16_to_f64(s["k"]) * 0.25)
+    gi3, gs3 = _run(dsa, s["q"], kq, s["w"], 2048)
+    assert np.array_equal(gi, gi3)
+    assert np.array_equal(gs * 0.25, gs3)
+
+
+def test_head_permutation(dsa):
+    s = wl.score_inputs(2200, seed=9)
+    perm = np.random.default_rng(1).permutation(H)
+    gi, gs = _run(dsa, s["q"], s["k"], s["w"], 2048)
+    gi2, gs2 = _run(dsa, np.ascontiguousarray(s["q"][:, perm]), s["k"],
+                    np.ascontiguousarray(s["w"][:, perm]), 2048)
+    rows = [2100, 2199]
+    ref = oracle.prefill_rows(s["q"], s["k"], s["w"], rows, topk=2048, full=True)
+    for r, t in enumerate(rows):
+        check_row(t, gi[t], gs[t], ref, r, 2048)
+        check_row(t, gi2[t], gs2[t], ref, r, 2048)
+
+
+def test_deterministic(dsa):
+    s = wl.score_inputs(2500, seed=3)
+    a = _run(dsa, s["q"], s["k"], s["w"], 2048)
+    b = _run(dsa, s["q"], s["k"], s["w"], 2048)
+    assert np.array_equal(a[0], b[0]) and np.array_equal(a[1], b[1])
+
+
+def test_causality(dsa):
+    s = wl.score_inputs(2300, seed=8)
+    k2 = s["k"].copy()
+    k2[2200:] = synth.normal_bf16(k2[2200:].shape, 0.0, 1.0, synth.K, 77)
+    a = _run(dsa, s["q"], s["k"], s["w"], 2048)
+    b = _run(dsa, s["q"], k2, s["w"], 2048)
+    assert np.array_equal(a[0][:2200], b[0][:2200]) and np.array_equal(a[1][:2200], b[1][:2200])
+
+
+def test_without_scores(dsa):
+    s = wl.score_inputs(700, seed=2)
+    idx, sc = dsa.score_topk(to_dev(s["q"]), to_dev(s["k"]), to_dev(s["w"]), topk=100,
+                             with_scores=False)
+    torch.cuda.synchronize()
+    assert sc is None
+    gi, _ = _run(dsa, s["q"], s["k"], s["w"], 100)
+    assert np.array_equal(idx.cpu().numpy(), gi)
+
+
+def test_varlen_equals_per_sequence(dsa):
+    lens = [1, 33, 100, 2100, 70, 2049]
+    total = sum(lens)
+    s = wl.score_inputs(total, seed=6)
+    cu = wl.cu_seqlens(lens)
+    idx, sc = dsa.score_topk_varlen(to_dev(s["q"]), to_dev(s["k"]), to_dev(s["w"]),
+                                    torch.from_numpy(cu).cuda(), max(lens), topk=2048)
+    torch.cuda.synchronize()
+    gi, gs = idx.cpu().numpy(), sc.cpu().numpy()
+    for b, L in enumerate(lens):
+        a, e = cu[b], cu[b + 1]
+        di, ds = _run(dsa, s["q"][a:e], s["k"][a:e], s["w"][a:e], 2048)
+        assert np.array_equal(gi[a:e], di)
+        assert np.array_equal(gs[a:e], ds)
+        rows = sorted(set([0, L // 2, L - 1]))
+        ref = oracle.prefill_rows(s["q"][a:e], s["k"][a:e], s["w"][a:e], rows, topk=2048, full=True)
+        for r, t in enumerate(rows):
+            check_row(t, gi[a + t], gs[a + t], ref, r, 2048)
