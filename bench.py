@@ -1,0 +1,272 @@
+#!/usr/bin/env python3
+"""Throughput of the DSA lightning indexer forward pass on one MI355X.
+
+Default workload (the headline): one full indexer layer over one causal sequence of
+T = 65,536 tokens -- q/k/w projections from x [T,7168] and c_q [T,1536], then causal scores
+I = sum_h w_h ReLU(q_h . k) over the whole prefix and the top 2,048 keys per query.  One
+step = dsa_idx_project + dsa_idx_score_topk on resident inputs.  `value` is queries/s.
+
+Also reported on the same line:
+  * roofline of the dominant kernel (the fused score + top-k kernel) against the bf16 MFMA
+    peak, its average duration measured with HIP events on the stream it runs on;
+  * the decode leg: 64 sequences with cached bf16 keys of U[32768, 131072] tokens, one
+    new query each (project + decode), as HBM GB/s of the decode kernels;
+  * cpu_baseline: the fp64 CPU oracle on a bounded sample of the same workload, with the
+    extrapolation to the full layer.
+
+Inputs are seeded synthetic tensors with the shapes and distributions of the workload
+(x, c_q ~ N(0,1); W_q ~ N(0,1/1536); W_k, W_w ~ N(0,1/7168); LayerNorm gain 1 + N(0,0.02),
+bias N(0,0.02), eps 1e-6; all bf16).
+"""
+import argparse
+import json
+import os
+import sys
+import time
+
+import numpy as np
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+PEAK_BF16_TFLOPS = 2516.6     # MI355X dense bf16 MFMA (published)
+PEAK_HBM_GBPS = 8000.0        # MI355X HBM3E (published)
+H, D, QLAT, HIDDEN = 32, 128, 1536, 7168
+PROJ_FLOP_PER_TOKEN = 2 * (QLAT * 4096 + HIDDEN * D + HIDDEN * H)   # 14,876,672
+SCORE_FLOP_PER_PAIR = 2 * H * D                                     # 8,192
+
+
+def log(*a):
+    print(*a, file=sys.stderr, flush=True)
+
+
+def parse():
+    p = argparse.ArgumentParser()
+    p.add_argument("--gpus", type=int, default=1)
+    p.add_argument("--steps", type=int, default=10)
+    p.add_argument("--warmup", type=int, default=3)
+    p.add_argument("--T", type=int, default=65536)
+    p.add_argument("--topk", type=int, default=2048)
+    p.add_argument("--no-decode", action="store_true")
+    p.add_argument("--no-cpu-baseline", action="store_true")
+    p.add_argument("--decode-batch", type=int, default=64)
+    p.add_argument("--calibrate-copy", action="store_true",
+                   help="also run a plain 1 GiB device copy (reference for HBM byte counters)")
+    return p.parse_args()
+
+
+def dev_bf16(a):
+    import torch
+    return torch.from_numpy(a.view(np.int16)).view(torch.bfloat16).cuda()
+
+
+def bench_prefill(dsa, args):
+    import torch
+    from synth import workloads as wl
+    T, topk = args.T, args.topk
+    t0 = time.time()
+    Wt = wl.layer_weights(layer=0, seed=0)
+    act = wl.layer_activations(T, seed=0)
+    log(f"prefill: generated inputs T={T} in {time.time() - t0:.1f}s")
+    W = {k: dev_bf16(v) for k, v in Wt.items() if k != "eps"}
+    W["eps"] = Wt["eps"]
+    x, cq = dev_bf16(act["x"]), dev_bf16(act["c_q"])
+    del act
+    q = torch.empty((T, H, D), dtype=torch.bfloat16, device="cuda")
+    k = torch.empty((T, D), dtype=torch.bfloat16, device="cuda")
+    w = torch.empty((T, H), dtype=torch.bfloat16, device="cuda")
+    idx = torch.empty((T, topk), dtype=torch.int32, device="cuda")
+    sc = torch.empty((T, topk), dtype=torch.float32, device="cuda")
+    ws = torch.empty(dsa.workspace_size(dsa.OP_SCORE_TOPK, T, topk=topk), dtype=torch.uint8,
+                     device="cuda")
+    stream = torch.cuda.current_stream()
+
+    def step(ev=None):
+        if ev is not None:
+            ev[0].record(stream)
+        dsa.project(x, cq, W, q=q, k_out=k, w=w)
+        if ev is not None:
+            ev[1].record(stream)
+        dsa.score_topk(q, k, w, topk=topk, ws=ws, out=(idx, sc))
+        if ev is not None:
+            ev[2].record(stream)
+
+    for i in range(args.warmup):
+        step()
+        torch.cuda.synchronize()
+        log(f"prefill: warmup step {i + 1}/{args.warmup} done")
+    evs = [[torch.cuda.Event(enable_timing=True) for _ in range(3)] for _ in range(args.steps)]
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    for i in range(args.steps):
+        step(evs[i])
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - t0
+    proj_ms = [e[0].elapsed_time(e[1]) for e in evs]
+    score_ms = [e[1].elapsed_time(e[2]) for e in evs]
+    log(f"prefill: {args.steps} steps in {wall:.3f}s; project {np.mean(proj_ms):.3f} ms, "
+        f"score_topk {np.mean(score_ms):.3f} ms")
+    pairs = T * (T + 1) // 2
+    return dict(wall=wall, proj_ms=float(np.mean(proj_ms)), score_ms=float(np.mean(score_ms)),
+                score_ms_min=float(np.min(score_ms)), pairs=pairs,
+                score_flop=pairs * SCORE_FLOP_PER_PAIR, proj_flop=T * PROJ_FLOP_PER_TOKEN)
+
+
+def bench_decode(dsa, args):
+    import torch
+    from synth import workloads as wl
+    B, topk = args.decode_batch, args.topk
+    lens = wl.decode_lengths(B, seed=0)
+    t0 = time.time()
+    cache, start = wl.decode_cache(lens, seed=0)
+    Wt = wl.layer_weights(layer=0, seed=1)
+    act = wl.layer_activations(B, seed=1)
+    log(f"decode: generated {cache.shape[0]} cached keys in {time.time() - t0:.1f}s")
+    W = {k: dev_bf16(v) for k, v in Wt.items() if k != "eps"}
+    W["eps"] = Wt["eps"]
+    cache_d = dev_bf16(cache)
+    del cache
+    x, cq = dev_bf16(act["x"]), dev_bf16(act["c_q"])
+    start_d = torch.from_numpy(start).cuda()
+    lens_d = torch.from_numpy(lens.astype(np.int32)).cuda()
+    slots = torch.from_numpy((start + lens - 1).astype(np.int64)).cuda()
+    maxL = int(lens.max())
+    q = torch.empty((B, H, D), dtype=torch.bfloat16, device="cuda")
+    w = torch.empty((B, H), dtype=torch.bfloat16, device="cuda")
+    idx = torch.empty((B, topk), dtype=torch.int32, device="cuda")
+    sc = torch.empty((B, topk), dtype=torch.float32, device="cuda")
+    ws = torch.empty(dsa.workspace_size(dsa.OP_DECODE, 0, B, maxL, topk), dtype=torch.uint8,
+                     device="cuda")
+    stream = torch.cuda.current_stream()
+
+    def step(ev=None):
+        if ev is not None:
+            ev[0].record(stream)
+        dsa.project(x, cq, W, q=q, k_out=cache_d, k_slot=slots, w=w)
+        if ev is not None:
+            ev[1].record(stream)
+        dsa.decode(q, w, cache_d, start_d, lens_d, maxL, topk=topk, ws=ws, out=(idx, sc))
+        if ev is not None:
+            ev[2].record(stream)
+
+    for _ in range(max(args.warmup, 1)):
+        step()
+    torch.cuda.synchronize()
+    n = max(args.steps, 10)
+    evs = [[torch.cuda.Event(enable_timing=True) for _ in range(3)] for _ in range(n)]
+    for i in range(n):
+        step(evs[i])
+    torch.cuda.synchronize()
+    proj_ms = float(np.mean([e[0].elapsed_time(e[1]) for e in evs]))
+    dec_ms = float(np.mean([e[1].elapsed_time(e[2]) for e in evs]))
+    sumL = int(lens.sum())
+    # algorithmic bytes of the decode kernels: every cached key once, q and w of the new
+    # tokens, the selected indices and scores
+    dec_bytes = 256 * sumL + B * (H * D * 2 + H * 2) + B * topk * 8
+    proj_bytes = 2 * (QLAT * 4096 + HIDDEN * D + HIDDEN * H + 2 * D) + B * 2 * (HIDDEN + QLAT) \
+        + B * 2 * (H * D + D + H)
+    gbps = dec_bytes / (dec_ms * 1e-3) / 1e9
+    log(f"decode: B={B} sum L={sumL}: project {proj_ms:.3f} ms, decode {dec_ms:.3f} ms "
+        f"({gbps:.0f} GB/s)")
+    return dict(batch=B, sum_keys=sumL, project_ms=proj_ms, decode_ms=dec_ms,
+                decode_bytes=dec_bytes, decode_GBps=gbps, decode_hbm_frac=gbps / PEAK_HBM_GBPS,
+                step_GBps=(dec_bytes + proj_bytes) / ((dec_ms + proj_ms) * 1e-3) / 1e9)
+
+
+def cpu_baseline(args):
+    """The oracle on a bounded sample of the T-token layer, extrapolated per its cost model."""
+    import oracle
+    from synth import workloads as wl
+    T, topk = args.T, args.topk
+    cores = oracle.num_threads()
+    rng = np.random.default_rng(0)
+    rows = np.unique(np.concatenate([[0, T - 1], rng.integers(0, T, 62)]))
+    Wt = wl.layer_weights(layer=0, seed=0)
+    act = wl.layer_activations(T, seed=0)
+    kmax = int(rows.max()) + 1
+    t0 = time.perf_counter()
+    _, k_all, _ = oracle.project(act["x"][:kmax], None, Wt, want=("k",))   # every key needed
+    t_k = time.perf_counter() - t0
+    t0 = time.perf_counter()
+    q_s, _, w_s = oracle.project(act["x"][rows], act["c_q"][rows], Wt, want=("q", "w"))
+    t_qw = time.perf_counter() - t0
+    t0 = time.perf_counter()
+    oracle.rows(q_s, w_s, k_all, np.zeros(len(rows), np.int64), rows, topk=topk)
+    t_rows = time.perf_counter() - t0
+    total = (t_k * T / kmax + t_qw * T / len(rows)
+             + t_rows * (T * (T + 1) / 2) / float((rows + 1).sum()))
+    return dict(value=round(T / total, 2), unit="queries/s", cores=cores, kind="oracle",
+                sample=(f"fp64 oracle, OpenMP over {cores} host threads: keys projected for all "
+                        f"{kmax} tokens, q and w for {len(rows)} sampled rows, those rows scored "
+                        f"over their whole causal prefix and fully sorted; extrapolated to all "
+                        f"{T} rows by tokens (projections) and causal pairs (scores)"),
+                measured_s=round(t_k + t_qw + t_rows, 2), extrapolated_s=round(total, 1))
+
+
+def main():
+    args = parse()
+    if args.gpus != 1:
+        print(f"bench.py runs on one GPU only (asked for --gpus {args.gpus}); the multi-GPU "
+              "sharding of this path is described in the design notes but not built.",
+              file=sys.stderr, flush=True)
+        sys.exit(2)
+    import torch
+    import sparse_attention_token_idx_amd as dsa
+    assert torch.cuda.is_available(), "no GPU visible"
+    log(f"{dsa.version()} on {torch.cuda.get_device_name(0)}")
+    if args.calibrate_copy:
+        src = torch.empty(1 << 30, dtype=torch.uint8, device="cuda")
+        dst = torch.empty_like(src)
+        dst.copy_(src)
+        torch.cuda.synchronize()
+        log("calibration: copied 1073741824 bytes device to device")
+        del src, dst
+    pre = bench_prefill(dsa, args)
+    dec = None if args.no_decode else bench_decode(dsa, args)
+    ms_step = pre["proj_ms"] + pre["score_ms"]
+    ms_wall = pre["wall"] * 1e3 / args.steps
+    qps = args.T / (ms_wall * 1e-3)
+    tflops = (pre["score_flop"] + pre["proj_flop"]) / (ms_wall * 1e-3) / 1e12
+    achieved = pre["score_flop"] / (pre["score_ms"] * 1e-3) / 1e12
+    cpu = None
+    if not args.no_cpu_baseline:
+        log("cpu baseline: running the oracle on a bounded sample")
+        cpu = cpu_baseline(args)
+        log(f"cpu baseline: {cpu['value']:.1f} queries/s ({cpu['measured_s']} s measured)")
+    line = {
+        "metric": "DSA indexer queries/s + TFLOP/s (T=64K prefill, top-2048); decode HBM GB/s",
+        "value": round(qps, 1),
+        "unit": "queries/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": round(ms_wall, 3),
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "bf16",
+        "data": "synthetic",
+        "config": {"workload": f"one indexer layer, causal prefill T={args.T}, top-{args.topk}: "
+                               "project + score_topk", "seq_len": args.T, "topk": args.topk,
+                   "heads": H, "head_dim": D, "parallelism": "single GPU"},
+        "tflops": round(tflops, 1),
+        "split_ms": {"project": round(pre["proj_ms"], 3), "score_topk": round(pre["score_ms"], 3),
+                     "sum_of_events": round(ms_step, 3)},
+        "roofline": {"kernel": "score_topk_kernel", "bound": "mfma",
+                     "achieved": round(achieved, 1), "peak": PEAK_BF16_TFLOPS, "unit": "TFLOP/s",
+                     "frac": round(achieved / PEAK_BF16_TFLOPS, 4), "traffic": None,
+                     "algorithmic_flop_per_launch": pre["score_flop"]},
+        "decode": None if dec is None else {
+            "workload": f"{dec['batch']} sequences, one new query each, cached bf16 keys "
+                        f"U[32768,131072] (sum {dec['sum_keys']}), top-{args.topk}",
+            "decode_ms": round(dec["decode_ms"], 4), "project_ms": round(dec["project_ms"], 4),
+            "GBps": round(dec["decode_GBps"], 1), "hbm_frac": round(dec["decode_hbm_frac"], 4),
+            "step_GBps_incl_project": round(dec["step_GBps"], 1),
+            "algorithmic_bytes": dec["decode_bytes"]},
+        "cpu_baseline": cpu,
+    }
+    print(json.dumps(line), flush=True)
+
+
+if __name__ == "__main__":
+    main()

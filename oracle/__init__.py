@@ -46,6 +46,8 @@ def lib():
         vp, i64, i32, f64 = ctypes.c_void_p, ctypes.c_int64, ctypes.c_int, ctypes.c_double
         L.oracle_param_count.restype = i64
         L.oracle_param_count.argtypes = []
+        L.oracle_num_threads.restype = i32
+        L.oracle_num_threads.argtypes = []
         L.oracle_dims.restype = i32
         L.oracle_dims.argtypes = [vp]
         L.oracle_bf16_to_f64.restype = f64
@@ -93,6 +95,10 @@ def f64_to_bf16(x):
 
 def param_count():
     return int(lib().oracle_param_count())
+
+
+def num_threads():
+    return int(lib().oracle_num_threads())
 
 
 def dims():

@@ -33,6 +33,7 @@
  * Shares no code, header or table with the HIP implementation.
  */
 #include <math.h>
+#include <omp.h>
 #include <stdint.h>
 #include <stdlib.h>
 #include <string.h>
@@ -55,6 +56,9 @@ int64_t oracle_param_count(void) {
          + (int64_t)OR_HIDDEN * OR_HEADS   /* W_w */
          + 2 * (int64_t)OR_DIM;            /* LayerNorm gain and bias */
 }
+
+/* Threads the OpenMP loops of this library use. */
+int oracle_num_threads(void) { return omp_get_max_threads(); }
 
 int oracle_dims(int32_t *out6) {
     out6[0] = OR_HEADS; out6[1] = OR_DIM; out6[2] = OR_QLAT;
