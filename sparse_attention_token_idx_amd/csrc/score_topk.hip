@@ -12,13 +12,17 @@
 //     runs q.k for each head on v_mfma_f32_16x16x32_bf16 with the key tile (A operand, read
 //     from LDS), then applies ReLU and the w-weighted sum over its 8 heads in registers;
 //   * the four head groups' partial sums meet in LDS and are added in a fixed order;
-//   * each wave then owns 4 rows: keys above the row's running threshold are appended,
-//     in ascending s, to the row's candidate list in the workspace.  When a list nears its
-//     capacity the owning wave runs an exact radix select over it, keeps exactly topk
-//     entries (stable) and raises the threshold to the topk-th key.  Later keys have
-//     larger s and so lose every tie against kept entries, hence the strict ">" rule is
-//     exact.
-//   * at the end each row's list is selected once more and written out in ascending s.
+//   * each wave then owns 4 rows.  A key whose score beats the row's emit threshold is
+//     appended, in ascending s, to the row's candidate list in the workspace, and counted
+//     in the row's LDS histogram: 512 bins of 1/32 binade over the orderable key, placed
+//     just below the row's largest score.  As soon as the bins above the threshold's bin
+//     hold topk candidates the threshold moves up to the next bin edge.  Later keys have
+//     larger s and so lose every tie against candidates already kept, hence the strict
+//     ">" emission rule never drops a winner.  Nothing is re-read while streaming, except
+//     in the rare case that a list fills up (it is then compacted).
+//   * at the end only the threshold bin needs an exact decision: its few candidates are
+//     gathered, the exact boundary key and its tie count are found with a bitwise search,
+//     and one ordered pass over the list writes the topk winners in ascending s.
 #include "common.hpp"
 #include "launch.hpp"
 
@@ -31,11 +35,26 @@ constexpr int kWaves = 8;
 constexpr int kThreads = 64 * kWaves;
 constexpr int kKStride = kDim + 8;    // bf16 per key row in LDS (272 B: conflict-free reads)
 constexpr int kRStride = kBK + 4;     // floats per row of the partial-score tile (272 B)
+constexpr int kNB = 512;              // histogram bins per row
+constexpr int kBinShift = 18;         // a bin is a 14-bit key prefix: 1/32 binade
+constexpr int kGather = 1024;         // per-wave buffer for the threshold bin's keys
 
 struct ScoreSmem {
     uint16_t k[2][kBK][kKStride];      // double-buffered key tile
-    float red[4][kBQ][kRStride];       // per head-group partial scores [hg][query][key]
-    uint32_t hist[kWaves][4][256];     // radix-select histograms, 4 copies per wave
+    float red[2][4][kBQ][kRStride];    // double-buffered partial scores [buf][hg][query][key]
+    uint32_t hist[kBQ / 2][kNB];       // candidate histograms, 16-bit counts, two rows a word
+};
+// the final phase reuses k and red as per-wave gather buffers
+static_assert(kWaves * kGather * 4 <= sizeof(uint16_t) * 2 * kBK * kKStride + sizeof(float) * 8 * kBQ * kRStride,
+              "gather buffers must fit in the key and partial-score tiles");
+
+// One row's 16-bit histogram counters (the low or high halves of a shared word array).
+// Both rows of a word belong to the same wave, so plain read-modify-writes are safe.
+struct RowHist {
+    uint32_t *w;
+    int sh;
+    __device__ int get(int b) const { return (int)((w[b] >> sh) & 0xFFFFu); }
+    __device__ void inc(int b) const { atomicAdd(&w[b], 1u << sh); }
 };
 
 struct ScoreArgs {
@@ -58,35 +77,128 @@ __device__ __forceinline__ void wave_sync_lds() {
     __builtin_amdgcn_wave_barrier();
 }
 
-// Exact selection over one candidate list, run by one whole wave.
-// keys/ids[0..n) hold (orderable score key, token index) in ascending index order, n > topk.
-// Finds theta = the topk-th largest key, then compacts the list in place (stable) to the
-// topk entries that win under (key desc, index asc): every key > theta plus the first
-// topk - #(key > theta) entries equal to theta.  Returns theta.
-__device__ uint32_t wave_select(uint32_t *keys, int32_t *ids, int n, int topk, uint32_t *hist) {
+// ---------------------------------------------------------------- histogram window
+// Bins are consecutive 14-bit prefixes of the orderable key, bin 0 taking everything below
+// the window and bin kNB-1 everything above.  The window ends one binade above the row's
+// largest key seen when it was placed.
+__device__ __forceinline__ int window_base(uint32_t kmax) {
+    int top = (int)(kmax >> kBinShift) + 32;
+    if (top > (1 << (32 - kBinShift)) - 1) top = (1 << (32 - kBinShift)) - 1;
+    const int base = top - (kNB - 1);
+    return base < 0 ? 0 : base;
+}
+__device__ __forceinline__ int bin_of(uint32_t key, int pbase) {
+    const int b = (int)(key >> kBinShift) - pbase;
+    return b < 0 ? 0 : (b >= kNB ? kNB - 1 : b);
+}
+// Smallest key of bin b (b >= 1).
+__device__ __forceinline__ uint32_t bin_edge(int b, int pbase) {
+    return (uint32_t)(pbase + b) << kBinShift;
+}
+
+__device__ __forceinline__ uint32_t group16_max(uint32_t v) {
+#pragma unroll
+    for (int d = 1; d < 16; d <<= 1) {
+        const uint32_t o = (uint32_t)__shfl_xor((int)v, d, 64);
+        v = o > v ? o : v;
+    }
+    return v;
+}
+
+// ---------------------------------------------------------------- whole-wave list passes
+// Histogram of keys[0..n) into hist[kNB] (zeroed first).  Entries are read in batches of B
+// per lane so that many loads are in flight.
+template <int B>
+__device__ void wave_fill_hist(const uint32_t *keys, int n, RowHist hist, int pbase) {
+    const int lane = lane_id();
+#pragma unroll
+    for (int i = 0; i < kNB / 64; ++i) hist.w[lane + 64 * i] &= ~(0xFFFFu << hist.sh);
+    wave_sync_lds();
+    for (int base = 0; base < n; base += 64 * B) {
+        uint32_t kv[B];
+#pragma unroll
+        for (int j = 0; j < B; ++j) {
+            const int i = base + 64 * j + lane;
+            kv[j] = i < n ? keys[i] : 0u;
+        }
+#pragma unroll
+        for (int j = 0; j < B; ++j)
+            if (base + 64 * j + lane < n) hist.inc(bin_of(kv[j], pbase));
+    }
+    wave_sync_lds();
+}
+
+// Stable in-place compaction keeping keys >= min_key; returns the new length.  A batch is
+// loaded before any of its slots is written and writes never pass the batch being read.
+template <int B>
+__device__ int wave_keep_at_least(uint32_t *keys, int32_t *ids, int n, uint32_t min_key) {
+    const int lane = lane_id();
+    int out = 0;
+    for (int base = 0; base < n; base += 64 * B) {
+        uint32_t kv[B];
+        int32_t iv[B];
+#pragma unroll
+        for (int j = 0; j < B; ++j) {
+            const int i = base + 64 * j + lane;
+            kv[j] = i < n ? keys[i] : 0u;
+            iv[j] = i < n ? ids[i] : 0;
+        }
+#pragma unroll
+        for (int j = 0; j < B; ++j) {
+            const bool keep = base + 64 * j + lane < n && kv[j] >= min_key;
+            const uint64_t km = ballot(keep);
+            if (keep) {
+                const int pos = out + (int)bits_below(km);
+                keys[pos] = kv[j];
+                ids[pos] = iv[j];
+            }
+            out += __popcll(km);
+        }
+    }
+    __threadfence();
+    return out;
+}
+
+// Exact selection over a whole list (the rare path): an MSD radix select on 8-bit digits
+// finds theta, the topk-th largest key, and how many entries equal to theta win the tie
+// (the lowest indices, i.e. the earliest list positions); the list is then compacted in
+// place (stable) to exactly those topk entries.  s0 and s1 are two scratch histograms of
+// 256 words each (lanes alternate between them).  Returns theta.
+template <int B>
+__device__ uint32_t wave_exact_select(uint32_t *keys, int32_t *ids, int n, int topk, uint32_t *s0,
+                                      uint32_t *s1) {
     const int lane = lane_id();
     uint32_t prefix = 0, pmask = 0;
     int need = topk;
     for (int shift = 24; shift >= 0; shift -= 8) {
 #pragma unroll
-        for (int i = 0; i < 16; ++i) hist[lane + 64 * i] = 0u;
+        for (int i = 0; i < 4; ++i) {
+            s0[lane + 64 * i] = 0u;
+            s1[lane + 64 * i] = 0u;
+        }
         wave_sync_lds();
-        uint32_t *h = hist + 256 * (lane & 3);
-        for (int i = lane; i < n; i += 64) {
-            const uint32_t kv = keys[i];
-            if ((kv & pmask) == prefix) atomicAdd(&h[(kv >> shift) & 255u], 1u);
+        uint32_t *h = (lane & 1) ? s1 : s0;
+        for (int base = 0; base < n; base += 64 * B) {
+            uint32_t kv[B];
+#pragma unroll
+            for (int j = 0; j < B; ++j) {
+                const int i = base + 64 * j + lane;
+                kv[j] = i < n ? keys[i] : 0u;
+            }
+#pragma unroll
+            for (int j = 0; j < B; ++j)
+                if (base + 64 * j + lane < n && (kv[j] & pmask) == prefix)
+                    atomicAdd(&h[(kv[j] >> shift) & 255u], 1u);
         }
         wave_sync_lds();
         int c[4];
 #pragma unroll
         for (int j = 0; j < 4; ++j) {
             const int b = 4 * lane + j;
-            c[j] = (int)(hist[b] + hist[256 + b] + hist[512 + b] + hist[768 + b]);
+            c[j] = (int)(s0[b] + s1[b]);
         }
-        const int s = c[0] + c[1] + c[2] + c[3];
-        const int incl = wave_inclusive_sum(s);
-        const int total = readlane(incl, 63);
-        int above = total - incl;   // entries in bins above 4*lane+3
+        const int incl = wave_inclusive_sum(c[0] + c[1] + c[2] + c[3]);
+        int above = readlane(incl, 63) - incl;   // entries in digits above 4*lane+3
         int found = -1, found_above = 0;
 #pragma unroll
         for (int j = 3; j >= 0; --j) {
@@ -96,38 +208,55 @@ __device__ uint32_t wave_select(uint32_t *keys, int32_t *ids, int n, int topk, u
             }
             above += c[j];
         }
-        const uint64_t bm = ballot(found >= 0);
-        const int src = (int)__builtin_ctzll(bm);
-        const int d = readlane(found, src);
+        const int src = (int)__builtin_ctzll(ballot(found >= 0));
         need -= readlane(found_above, src);
-        prefix |= (uint32_t)d << shift;
+        prefix |= (uint32_t)readlane(found, src) << shift;
         pmask |= 255u << shift;
         wave_sync_lds();
     }
-    // stable in-place compaction: each chunk is read before any of its slots is written,
-    // and writes never reach beyond the chunk being read
     const uint32_t theta = prefix;
     int out = 0, ties = 0;
-    for (int base = 0; base < n; base += 64) {
-        const int i = base + lane;
-        const bool in = i < n;
-        const uint32_t kv = in ? keys[i] : 0u;
-        const int32_t iv = in ? ids[i] : 0;
-        const bool gt = in && kv > theta;
-        const bool eq = in && kv == theta;
-        const uint64_t em = ballot(eq);
-        const bool keep = gt || (eq && ties + (int)bits_below(em) < need);
-        const uint64_t km = ballot(keep);
-        if (keep) {
-            const int pos = out + (int)bits_below(km);
-            keys[pos] = kv;
-            ids[pos] = iv;
+    for (int base = 0; base < n; base += 64 * B) {
+        uint32_t kv[B];
+        int32_t iv[B];
+#pragma unroll
+        for (int j = 0; j < B; ++j) {
+            const int i = base + 64 * j + lane;
+            kv[j] = i < n ? keys[i] : 0u;
+            iv[j] = i < n ? ids[i] : 0;
         }
-        out += __popcll(km);
-        ties += __popcll(em);
+#pragma unroll
+        for (int j = 0; j < B; ++j) {
+            const bool in = base + 64 * j + lane < n;
+            const bool eq = in && kv[j] == theta;
+            const uint64_t em = ballot(eq);
+            const bool keep = (in && kv[j] > theta) || (eq && ties + (int)bits_below(em) < need);
+            const uint64_t km = ballot(keep);
+            if (keep) {
+                const int pos = out + (int)bits_below(km);
+                keys[pos] = kv[j];
+                ids[pos] = iv[j];
+            }
+            out += __popcll(km);
+            ties += __popcll(em);
+        }
     }
     __threadfence();
     return theta;
+}
+
+// Largest v such that at least `need` of the m keys in g (m <= 1024, zero padded) are >= v:
+// the need-th largest key.  Bitwise search, counts reduced over the wave.
+__device__ uint32_t wave_kth_largest(const uint32_t (&g)[kGather / 64], int need) {
+    uint32_t v = 0;
+    for (int bit = 31; bit >= 0; --bit) {
+        const uint32_t c = v | (1u << bit);
+        int cnt = 0;
+#pragma unroll
+        for (int j = 0; j < kGather / 64; ++j) cnt += g[j] >= c ? 1 : 0;
+        if (wave_sum(cnt) >= need) v = c;
+    }
+    return v;
 }
 
 __global__ __launch_bounds__(kThreads, 1) void score_topk_kernel(ScoreArgs a) {
@@ -146,6 +275,7 @@ __global__ __launch_bounds__(kThreads, 1) void score_topk_kernel(ScoreArgs a) {
     const int rows_here = (int)(L - r0 < kBQ ? L - r0 : kBQ);
     const int64_t r_last = r0 + rows_here - 1;
     const int nkt = (int)(r_last / kBK) + 1;
+    const int topk = a.topk, cap = a.cap;
 
     const int tid = threadIdx.x;
     const int wave = tid >> 6, lane = tid & 63;
@@ -190,124 +320,284 @@ __global__ __launch_bounds__(kThreads, 1) void score_topk_kernel(ScoreArgs a) {
         *reinterpret_cast<u32x4 *>(p + 8) = kv1;
     };
 
-    // ---- row state for the 4 rows this wave emits (row 4*wave + lg, uniform per 16 lanes)
+    // ---- state of the row this lane's 16-lane group emits for (row 4*wave + lg);
+    // every value except kmax is uniform within the group
     const int er = 4 * wave + lg;
     const bool erow_ok = er < rows_here;
-    const int64_t et = r0 + er;                          // its position in the sequence
+    const int et32 = (int)(r0 + er);                     // its position in the sequence
     const int64_t egrow = seq_start + r0 + (erow_ok ? er : 0);
-    uint32_t *ck = a.cand_key + egrow * a.cap;
-    int32_t *ci = a.cand_idx + egrow * a.cap;
-    uint32_t theta = 0u;   // emit key > theta; 0 is below every finite score's key
-    int n = 0;
-    uint32_t *whist = &sm.hist[wave][0][0];
+    uint32_t *ck = a.cand_key + egrow * cap;
+    int32_t *ci = a.cand_idx + egrow * cap;
+    uint32_t theta = 0u;   // emit key > theta (0 is below every finite score's key)
+    int n = 0;             // list length
+    bool hv = false;       // histogram placed
+    int pbase = 0;         // histogram window
+    int bth = 0;           // bin of the threshold: bins >= bth hold the live candidates
+    int cum = 0;           // number of list entries in bins >= bth
+    uint32_t kmax = 0u;    // largest key this lane emitted
     const uint64_t gmask = 0xFFFFull << (16 * lg);
     const int64_t wave_last_row = r0 + 16 * qg + 15;
 
+    // Move the threshold up while the bins above bth alone hold topk candidates.
+    auto advance = [&](const RowHist &hist) {
+        for (;;) {
+            const int h = hist.get(bth);
+            if (bth < kNB - 1 && cum - h >= topk) {
+                cum -= h;
+                ++bth;
+                const uint32_t e = bin_edge(bth, pbase);
+                theta = e > theta ? e : theta;
+            } else {
+                break;
+            }
+        }
+    };
+
+    // ---- one tile of q.k on the matrix cores: 16 keys (subtile st) x 16 queries x 8 heads
+    auto mfma_subtile = [&](int kt, int st, f32x4 &acc) {
+        acc = f32x4{0.f, 0.f, 0.f, 0.f};
+        if ((int64_t)kt * kBK + 16 * st > wave_last_row) return;   // wave-uniform causal skip
+        const int buf = kt & 1;
+        u32x4 af[4];
+#pragma unroll
+        for (int ks = 0; ks < 4; ++ks)
+            af[ks] = *reinterpret_cast<const u32x4 *>(&sm.k[buf][16 * st + l16][32 * ks + 8 * lg]);
+#pragma unroll
+        for (int h = 0; h < 8; ++h) {
+            f32x4 sc = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+            for (int ks = 0; ks < 4; ++ks) sc = mfma16x16x32(af[ks], qf[h][ks], sc);
+#pragma unroll
+            for (int r = 0; r < 4; ++r) acc[r] = fmaf(wv[h], fmaxf(sc[r], 0.f), acc[r]);
+        }
+    };
+
+    // ---- candidates of tile ke for row er: this lane covers keys 4*l16 .. 4*l16+3
+    auto emit = [&](int ke) {
+        const int rb2 = ke & 1;
+        f32x4 v = *reinterpret_cast<const f32x4 *>(&sm.red[rb2][0][er][4 * l16]);
+#pragma unroll
+        for (int g = 1; g < 4; ++g) v += *reinterpret_cast<const f32x4 *>(&sm.red[rb2][g][er][4 * l16]);
+        const int s0 = ke * kBK + 4 * l16;
+        uint32_t kk[4];
+        bool e[4];
+        int before = 0, total = 0;
+#pragma unroll
+        for (int j = 0; j < 4; ++j) {
+            kk[j] = score_key(v[j]);
+            e[j] = erow_ok && (s0 + j <= et32) && (kk[j] > theta);
+            const uint64_t b = ballot(e[j]) & gmask;
+            before += (int)bits_below(b);
+            total += __popcll(b);
+        }
+        int pos = n + before;
+        const RowHist rh{sm.hist[er >> 1], 16 * (er & 1)};
+#pragma unroll
+        for (int j = 0; j < 4; ++j) {
+            if (e[j]) {
+                ck[pos] = kk[j];
+                ci[pos] = s0 + j;
+                ++pos;
+                kmax = kk[j] > kmax ? kk[j] : kmax;
+                if (hv) rh.inc(bin_of(kk[j], pbase));
+            }
+        }
+        n += total;
+        if (hv) {
+            cum += total;
+            wave_sync_lds();
+            advance(rh);
+        }
+
+        // rare per-row work, done by the whole wave one row at a time: place the histogram
+        // once a row holds more than topk candidates; compact a full list
+        const uint64_t want = ballot((!hv && n > topk) || n > cap - kBK);
+        if (want) {
+            const uint32_t gkmax = group16_max(kmax);
+#pragma unroll 1
+            for (int g = 0; g < 4; ++g) {
+                if (!((want >> (16 * g)) & 1ull)) continue;
+                const int row = 4 * wave + g;
+                const int64_t grow = seq_start + r0 + row;
+                uint32_t *rk = a.cand_key + grow * cap;
+                int32_t *ri = a.cand_idx + grow * cap;
+                const RowHist hist{sm.hist[row >> 1], 16 * (row & 1)};
+                int ng = readlane(n, 16 * g);
+                const uint32_t km = (uint32_t)readlane((int)gkmax, 16 * g);
+                uint32_t th = (uint32_t)readlane((int)theta, 16 * g);
+                bool hvg = readlane(hv ? 1 : 0, 16 * g) != 0;
+                int pb = readlane(pbase, 16 * g), bt = readlane(bth, 16 * g), cm = readlane(cum, 16 * g);
+                __threadfence();
+                if (!hvg) {
+                    pb = window_base(km);
+                    wave_fill_hist<8>(rk, ng, hist, pb);
+                    hvg = true;
+                    bt = 0;
+                    cm = ng;
+                }
+                if (ng > cap - kBK) {
+                    if (bt > 0 && cm <= cap / 2) {
+                        ng = wave_keep_at_least<8>(rk, ri, ng, bin_edge(bt, pb));
+                        cm = ng;
+                    } else {
+                        // scratch: this wave's rows of the partial tile it has just consumed
+                        th = wave_exact_select<8>(rk, ri, ng, topk,
+                                                  reinterpret_cast<uint32_t *>(&sm.red[rb2][0][4 * wave][0]),
+                                                  reinterpret_cast<uint32_t *>(&sm.red[rb2][1][4 * wave][0]));
+                        ng = topk;
+                        pb = window_base(km);
+                        wave_fill_hist<8>(rk, ng, hist, pb);
+                        bt = 0;
+                        cm = ng;
+                    }
+                }
+                for (;;) {
+                    const int h = hist.get(bt);
+                    if (bt < kNB - 1 && cm - h >= topk) {
+                        cm -= h;
+                        ++bt;
+                        const uint32_t ed = bin_edge(bt, pb);
+                        th = ed > th ? ed : th;
+                    } else {
+                        break;
+                    }
+                }
+                if (lg == g) {
+                    n = ng;
+                    theta = th;
+                    hv = hvg;
+                    pbase = pb;
+                    bth = bt;
+                    cum = cm;
+                }
+            }
+        }
+    };
+
+    // ---- the stream: tile kt's products run while tile kt-1's candidates are emitted;
+    // one barrier per tile
     load_k(0);
     store_k(0);
     __syncthreads();
-
-    for (int kt = 0; kt < nkt; ++kt) {
-        const int buf = kt & 1;
+    for (int kt = 0; kt <= nkt; ++kt) {
+        const bool have = kt < nkt;
         const bool more = kt + 1 < nkt;
         if (more) load_k(kt + 1);
-
-        f32x4 acc[4];
-#pragma unroll
-        for (int st = 0; st < 4; ++st) {
-            acc[st] = f32x4{0.f, 0.f, 0.f, 0.f};
-            if ((int64_t)kt * kBK + 16 * st <= wave_last_row) {
-                u32x4 af[4];
-#pragma unroll
-                for (int ks = 0; ks < 4; ++ks)
-                    af[ks] = *reinterpret_cast<const u32x4 *>(&sm.k[buf][16 * st + l16][32 * ks + 8 * lg]);
-#pragma unroll
-                for (int h = 0; h < 8; ++h) {
-                    f32x4 s = {0.f, 0.f, 0.f, 0.f};
-#pragma unroll
-                    for (int ks = 0; ks < 4; ++ks) s = mfma16x16x32(af[ks], qf[h][ks], s);
-#pragma unroll
-                    for (int r = 0; r < 4; ++r) acc[st][r] = fmaf(wv[h], fmaxf(s[r], 0.f), acc[st][r]);
-                }
-            }
+        f32x4 acc0, acc1, acc2, acc3;
+        if (have) {
+            mfma_subtile(kt, 0, acc0);
+            mfma_subtile(kt, 1, acc1);
         }
-#pragma unroll
-        for (int st = 0; st < 4; ++st)
-            *reinterpret_cast<f32x4 *>(&sm.red[hg][16 * qg + l16][16 * st + 4 * lg]) = acc[st];
-        if (more) store_k(buf ^ 1);
-        __syncthreads();
-
-        // ---- emission: this lane covers keys 4*l16 .. 4*l16+3 of the tile for row er
-        {
-            f32x4 v = *reinterpret_cast<const f32x4 *>(&sm.red[0][er][4 * l16]);
-#pragma unroll
-            for (int g = 1; g < 4; ++g) v += *reinterpret_cast<const f32x4 *>(&sm.red[g][er][4 * l16]);
-            const int64_t s0 = (int64_t)kt * kBK + 4 * l16;
-            uint32_t kk[4];
-            bool e[4];
-            int before = 0, total = 0;
-#pragma unroll
-            for (int j = 0; j < 4; ++j) {
-                kk[j] = score_key(v[j]);
-                e[j] = erow_ok && (s0 + j <= et) && (kk[j] > theta);
-                const uint64_t b = ballot(e[j]) & gmask;
-                before += (int)bits_below(b);
-                total += __popcll(b);
-            }
-            int pos = n + before;
-#pragma unroll
-            for (int j = 0; j < 4; ++j) {
-                if (e[j]) {
-                    ck[pos] = kk[j];
-                    ci[pos] = (int32_t)(s0 + j);
-                    ++pos;
-                }
-            }
-            n += total;
+        if (kt > 0) emit(kt - 1);
+        if (have) {
+            mfma_subtile(kt, 2, acc2);
+            mfma_subtile(kt, 3, acc3);
+            float *dst = &sm.red[kt & 1][hg][16 * qg + l16][4 * lg];
+            *reinterpret_cast<f32x4 *>(dst) = acc0;
+            *reinterpret_cast<f32x4 *>(dst + 16) = acc1;
+            *reinterpret_cast<f32x4 *>(dst + 32) = acc2;
+            *reinterpret_cast<f32x4 *>(dst + 48) = acc3;
         }
-        // ---- compaction of rows whose list could overflow on the next tile
-        {
-            const uint64_t full = ballot(n > a.cap - kBK);
-            if (full) {
-#pragma unroll 1
-                for (int g = 0; g < 4; ++g) {
-                    if (!((full >> (16 * g)) & 1ull)) continue;
-                    const int row = 4 * wave + g;
-                    const int64_t grow = seq_start + r0 + row;
-                    const int ng = readlane(n, 16 * g);
-                    __threadfence();
-                    const uint32_t th = wave_select(a.cand_key + grow * a.cap,
-                                                    a.cand_idx + grow * a.cap, ng, a.topk, whist);
-                    if (lg == g) {
-                        theta = th;
-                        n = a.topk;
-                    }
-                }
-            }
-        }
+        if (more) store_k((kt + 1) & 1);
         __syncthreads();
     }
 
     // ---- final selection and output, one row at a time per wave
+    uint32_t *G = reinterpret_cast<uint32_t *>(smem_raw) + wave * kGather;
     __threadfence();
 #pragma unroll 1
     for (int g = 0; g < 4; ++g) {
         const int row = 4 * wave + g;
         if (row >= rows_here) break;
         const int64_t grow = seq_start + r0 + row;
-        int ng = readlane(n, 16 * g);
-        uint32_t *rk = a.cand_key + grow * a.cap;
-        int32_t *ri = a.cand_idx + grow * a.cap;
-        if (ng > a.topk) {
-            wave_select(rk, ri, ng, a.topk, whist);
-            ng = a.topk;
+        uint32_t *rk = a.cand_key + grow * cap;
+        int32_t *ri = a.cand_idx + grow * cap;
+        int32_t *oi = a.out_idx + grow * topk;
+        float *os = a.out_score ? a.out_score + grow * topk : nullptr;
+        const int ng = readlane(n, 16 * g);
+        if (ng <= topk) {
+            // short row: the list is the whole causal prefix
+            for (int i = lane; i < topk; i += 64) {
+                const bool in = i < ng;
+                oi[i] = in ? ri[i] : -1;
+                if (os) os[i] = in ? key_score(rk[i]) : -INFINITY;
+            }
+            continue;
         }
-        int32_t *oi = a.out_idx + grow * a.topk;
-        float *os = a.out_score ? a.out_score + grow * a.topk : nullptr;
-        for (int i = lane; i < a.topk; i += 64) {
-            const bool in = i < ng;
-            oi[i] = in ? ri[i] : -1;
-            if (os) os[i] = in ? key_score(rk[i]) : -INFINITY;
+        const int pb = readlane(pbase, 16 * g), bt = readlane(bth, 16 * g), cm = readlane(cum, 16 * g);
+        const bool hvg = readlane(hv ? 1 : 0, 16 * g) != 0;
+        const int m = hvg ? RowHist{sm.hist[row >> 1], 16 * (row & 1)}.get(bt) : 0;   // in the threshold bin
+        const int need = topk - (cm - m);                // how many of them win
+        if (!hvg || m > kGather) {
+            // rare: too many candidates share the threshold bin -- exact select of the list
+            wave_exact_select<8>(rk, ri, ng, topk, G, G + 256);
+            for (int i = lane; i < topk; i += 64) {
+                oi[i] = ri[i];
+                if (os) os[i] = key_score(rk[i]);
+            }
+            continue;
+        }
+        // gather the threshold bin's keys
+        int gpos = 0;
+        for (int base = 0; base < ng; base += 64 * 16) {
+            uint32_t kv[16];
+#pragma unroll
+            for (int j = 0; j < 16; ++j) {
+                const int i = base + 64 * j + lane;
+                kv[j] = i < ng ? rk[i] : 0u;
+            }
+#pragma unroll
+            for (int j = 0; j < 16; ++j) {
+                const bool sel = base + 64 * j + lane < ng && bin_of(kv[j], pb) == bt;
+                const uint64_t mk = ballot(sel);
+                const int p = gpos + (int)bits_below(mk);
+                if (sel && p < kGather) G[p] = kv[j];
+                gpos += __popcll(mk);
+            }
+        }
+        wave_sync_lds();
+        uint32_t gk[kGather / 64];
+#pragma unroll
+        for (int j = 0; j < kGather / 64; ++j) {
+            const int i = lane + 64 * j;
+            gk[j] = i < gpos ? G[i] : 0u;
+        }
+        wave_sync_lds();
+        const uint32_t v = wave_kth_largest(gk, need);
+        int gt = 0;
+#pragma unroll
+        for (int j = 0; j < kGather / 64; ++j) gt += gk[j] > v ? 1 : 0;
+        const int ties_need = need - wave_sum(gt);
+        // one ordered pass writes the winners in ascending index order
+        int out = 0, ties = 0;
+        for (int base = 0; base < ng; base += 64 * 8) {
+            uint32_t kv[8];
+            int32_t iv[8];
+#pragma unroll
+            for (int j = 0; j < 8; ++j) {
+                const int i = base + 64 * j + lane;
+                kv[j] = i < ng ? rk[i] : 0u;
+                iv[j] = i < ng ? ri[i] : 0;
+            }
+#pragma unroll
+            for (int j = 0; j < 8; ++j) {
+                const bool in = base + 64 * j + lane < ng;
+                const int b = bin_of(kv[j], pb);
+                const bool eq = in && b == bt && kv[j] == v;
+                const uint64_t em = ballot(eq);
+                const bool keep = in && (b > bt || (b == bt && kv[j] > v) ||
+                                         (eq && ties + (int)bits_below(em) < ties_need));
+                const uint64_t km = ballot(keep);
+                if (keep) {
+                    const int pos = out + (int)bits_below(km);
+                    if (pos < topk) {
+                        oi[pos] = iv[j];
+                        if (os) os[pos] = key_score(kv[j]);
+                    }
+                }
+                out += __popcll(km);
+                ties += __popcll(em);
+            }
         }
     }
 }
@@ -315,8 +605,9 @@ __global__ __launch_bounds__(kThreads, 1) void score_topk_kernel(ScoreArgs a) {
 }  // namespace
 
 int candidate_capacity(int topk) {
-    // room for topk survivors plus at least topk fresh emissions and one tile of slack
-    return ((2 * topk + kBK - 1) / kBK) * kBK + kBK;
+    // room for about four times topk candidates before a list has to be compacted
+    const int c = ((4 * topk + kBK - 1) / kBK) * kBK;
+    return c < 256 ? 256 : c;
 }
 
 hipError_t launch_score_topk(const uint16_t *q, const uint16_t *k, const uint16_t *w,

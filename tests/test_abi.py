@@ -40,9 +40,9 @@ def test_version(dsa):
 
 def test_workspace_sizes(dsa):
     assert dsa.workspace_size(dsa.OP_PROJECT, 100) == 0
-    # candidate lists: (2*topk rounded to 64) + 64 slots of 8 bytes per row
-    assert dsa.workspace_size(dsa.OP_SCORE_TOPK, 1000, topk=2048) == 1000 * 4160 * 8
-    assert dsa.workspace_size(dsa.OP_SCORE_TOPK_VARLEN, 10, 2, 8, topk=5) == 10 * 128 * 8
+    # candidate lists: 4*topk rounded up to 64 (at least 256) slots of 8 bytes per row
+    assert dsa.workspace_size(dsa.OP_SCORE_TOPK, 1000, topk=2048) == 1000 * 8192 * 8
+    assert dsa.workspace_size(dsa.OP_SCORE_TOPK_VARLEN, 10, 2, 8, topk=5) == 10 * 256 * 8
     assert dsa.workspace_size(dsa.OP_DECODE, 0, 64, 131072, 2048) == 64 * 131072 * 4
     with pytest.raises(dsa.DsaIdxError) as e:
         dsa.workspace_size(dsa.OP_SCORE_TOPK, 10, topk=0)

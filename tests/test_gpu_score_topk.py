@@ -173,3 +173,46 @@ def test_varlen_equals_per_sequence(dsa):
         ref = oracle.prefill_rows(s["q"][a:e], s["k"][a:e], s["w"][a:e], rows, topk=2048, full=True)
         for r, t in enumerate(rows):
             check_row(t, gi[a + t], gs[a + t], ref, r, 2048)
+
+
+# ---------------------------------------------------------------- adversarial score patterns
+def test_all_equal_scores(dsa):
+    # w = 0 makes every score exactly 0: every row keeps its lowest topk indices
+    T = 5000
+    s = wl.score_inputs(T, seed=12)
+    w = np.zeros_like(s["w"])
+    for topk in (2048, 100):
+        gi, gs = _run(dsa, s["q"], s["k"], w, topk)
+        for t in (0, 99, 100, 2047, 2048, 4999):
+            n = min(topk, t + 1)
+            assert gi[t][:n].tolist() == list(range(n))
+            assert np.all(gi[t][n:] == -1)
+            assert np.all(gs[t][:n] == 0.0)
+
+
+def test_increasing_scores(dsa):
+    # I[t, s] = k[s, 0] strictly increasing in s: every key beats every earlier one, so the
+    # candidate lists fill at full rate and must be compacted; row t keeps its last topk keys
+    T = 3000
+    q = np.zeros((T, H, D), np.uint16)
+    q[:, 0, 0] = 0x3F80                      # 1.0
+    k = np.zeros((T, D), np.uint16)
+    k[:, 0] = (0x3F80 + np.arange(T)).astype(np.uint16)   # increasing positive bf16 values
+    w = np.zeros((T, H), np.uint16)
+    w[:, 0] = 0x3F80
+    for topk in (2048, 100, 7):
+        gi, gs = _run(dsa, q, k, w, topk)
+        for t in (0, 50, 2047, 2048, 2999):
+            n = min(topk, t + 1)
+            assert gi[t][:n].tolist() == list(range(t + 1 - n, t + 1)), (topk, t)
+            assert np.array_equal(gs[t][:n], oracle.bf16_to_f64(k[t + 1 - n:t + 1, 0]).astype(np.float32))
+
+
+def test_negative_weights(dsa):
+    s = wl.score_inputs(2600, seed=13)
+    w = oracle.f64_to_bf16(-np.abs(oracle.bf16_to_f64(s["w"])))
+    gi, gs = _run(dsa, s["q"], s["k"], w, 2048)
+    rows = [2047, 2048, 2300, 2599]
+    ref = oracle.prefill_rows(s["q"], s["k"], w, rows, topk=2048, full=True)
+    for r, t in enumerate(rows):
+        check_row(t, gi[t], gs[t], ref, r, 2048)
