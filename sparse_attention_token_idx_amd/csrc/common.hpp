@@ -17,6 +17,8 @@ typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
 typedef float f32x4 __attribute__((ext_vector_type(4)));
 typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
 typedef uint32_t u32x2 __attribute__((ext_vector_type(2)));
+// 16-byte vector with 4-byte alignment, for global stores at any dword offset
+typedef uint32_t u32x4a4 __attribute__((ext_vector_type(4), aligned(4)));
 
 // ---------------------------------------------------------------- bf16
 __device__ __forceinline__ float bf16_to_f32(uint32_t bits16) {

@@ -35,7 +35,8 @@ constexpr int kWaves = 8;
 constexpr int kThreads = 64 * kWaves;
 constexpr int kKStride = kDim + 8;    // bf16 per key row in LDS (272 B: conflict-free reads)
 constexpr int kRStride = kBK + 4;     // floats per row of the partial-score tile (272 B)
-constexpr int kNB = 512;              // histogram bins per row
+constexpr int kNB = 256;              // histogram bins per row (8 binades)
+constexpr int kRing = 128;            // per-row LDS staging ring of pending candidates
 constexpr int kBinShift = 18;         // a bin is a 14-bit key prefix: 1/32 binade
 constexpr int kGather = 1024;         // per-wave buffer for the threshold bin's keys
 
@@ -43,6 +44,7 @@ struct ScoreSmem {
     uint16_t k[2][kBK][kKStride];      // double-buffered key tile
     float red[2][4][kBQ][kRStride];    // double-buffered partial scores [buf][hg][query][key]
     uint32_t hist[kBQ / 2][kNB];       // candidate histograms, 16-bit counts, two rows a word
+    uint64_t ring[kBQ][kRing];         // pending candidates (key | index << 32) per row
 };
 // the final phase reuses k and red as per-wave gather buffers
 static_assert(kWaves * kGather * 4 <= sizeof(uint16_t) * 2 * kBK * kKStride + sizeof(float) * 8 * kBQ * kRStride,
@@ -328,20 +330,24 @@ __global__ __launch_bounds__(kThreads, 1) void score_topk_kernel(ScoreArgs a) {
     const int64_t egrow = seq_start + r0 + (erow_ok ? er : 0);
     uint32_t *ck = a.cand_key + egrow * cap;
     int32_t *ci = a.cand_idx + egrow * cap;
+    uint64_t *ring = sm.ring[er];
+    const RowHist rh{sm.hist[er >> 1], 16 * (er & 1)};
     uint32_t theta = 0u;   // emit key > theta (0 is below every finite score's key)
-    int n = 0;             // list length
+    int n = 0;             // candidates already in the list in memory
+    int p = 0;             // candidates pending in the LDS ring, starting at slot head
+    int head = 0;
     bool hv = false;       // histogram placed
     int pbase = 0;         // histogram window
     int bth = 0;           // bin of the threshold: bins >= bth hold the live candidates
-    int cum = 0;           // number of list entries in bins >= bth
+    int cum = 0;           // number of candidates in bins >= bth
     uint32_t kmax = 0u;    // largest key this lane emitted
     const uint64_t gmask = 0xFFFFull << (16 * lg);
     const int64_t wave_last_row = r0 + 16 * qg + 15;
 
     // Move the threshold up while the bins above bth alone hold topk candidates.
-    auto advance = [&](const RowHist &hist) {
+    auto advance = [&]() {
         for (;;) {
-            const int h = hist.get(bth);
+            const int h = rh.get(bth);
             if (bth < kNB - 1 && cum - h >= topk) {
                 cum -= h;
                 ++bth;
@@ -351,6 +357,30 @@ __global__ __launch_bounds__(kThreads, 1) void score_topk_kernel(ScoreArgs a) {
                 break;
             }
         }
+    };
+    // Write 64 pending candidates of the ring to the list with 16-byte stores (group-wide).
+    auto flush64 = [&]() {
+        const uint64_t *src = ring + head + 4 * l16;
+        const u32x4 lo = *reinterpret_cast<const u32x4 *>(src);
+        const u32x4 hi = *reinterpret_cast<const u32x4 *>(src + 2);
+        const u32x4a4 kv = {lo[0], lo[2], hi[0], hi[2]};
+        const u32x4a4 iv = {lo[1], lo[3], hi[1], hi[3]};
+        *reinterpret_cast<u32x4a4 *>(ck + n + 4 * l16) = kv;
+        *reinterpret_cast<u32x4a4 *>(ci + n + 4 * l16) = iv;
+        n += 64;
+        p -= 64;
+        head ^= 64;
+    };
+    // Write every pending candidate of the ring to the list (group-wide, any count).
+    auto flush_all = [&]() {
+        for (int i = l16; i < p; i += 16) {
+            const uint64_t e = ring[(head + i) & (kRing - 1)];
+            ck[n + i] = (uint32_t)e;
+            ci[n + i] = (int32_t)(e >> 32);
+        }
+        n += p;
+        p = 0;
+        head = 0;
     };
 
     // ---- one tile of q.k on the matrix cores: 16 keys (subtile st) x 16 queries x 8 heads
@@ -372,9 +402,12 @@ __global__ __launch_bounds__(kThreads, 1) void score_topk_kernel(ScoreArgs a) {
         }
     };
 
-    // ---- candidates of tile ke for row er: this lane covers keys 4*l16 .. 4*l16+3
+    // ---- candidates of tile ke for row er: this lane covers keys 4*l16 .. 4*l16+3.
+    // Only LDS is touched here (the ring, the histogram and the partial tile).
     auto emit = [&](int ke) {
         const int rb2 = ke & 1;
+        // the previous tile's histogram updates are complete (a barrier has passed)
+        if (hv) advance();
         f32x4 v = *reinterpret_cast<const f32x4 *>(&sm.red[rb2][0][er][4 * l16]);
 #pragma unroll
         for (int g = 1; g < 4; ++g) v += *reinterpret_cast<const f32x4 *>(&sm.red[rb2][g][er][4 * l16]);
@@ -390,67 +423,51 @@ __global__ __launch_bounds__(kThreads, 1) void score_topk_kernel(ScoreArgs a) {
             before += (int)bits_below(b);
             total += __popcll(b);
         }
-        int pos = n + before;
-        const RowHist rh{sm.hist[er >> 1], 16 * (er & 1)};
+        int slot = head + p + before;
 #pragma unroll
         for (int j = 0; j < 4; ++j) {
             if (e[j]) {
-                ck[pos] = kk[j];
-                ci[pos] = s0 + j;
-                ++pos;
+                ring[slot & (kRing - 1)] = (uint64_t)kk[j] | ((uint64_t)(uint32_t)(s0 + j) << 32);
+                ++slot;
                 kmax = kk[j] > kmax ? kk[j] : kmax;
                 if (hv) rh.inc(bin_of(kk[j], pbase));
             }
         }
-        n += total;
-        if (hv) {
-            cum += total;
-            wave_sync_lds();
-            advance(rh);
-        }
+        p += total;
+        if (hv) cum += total;
+    };
 
-        // rare per-row work, done by the whole wave one row at a time: place the histogram
-        // once a row holds more than topk candidates; compact a full list
-        const uint64_t want = ballot((!hv && n > topk) || n > cap - kBK);
-        if (want) {
-            const uint32_t gkmax = group16_max(kmax);
+    // ---- rare per-row work, done by the whole wave one row at a time: place the histogram
+    // once a row holds more than topk candidates; compact a full list.  scratch: two
+    // 256-word areas only this wave uses right now.
+    auto rare = [&](uint32_t *scr0, uint32_t *scr1) {
+        const uint64_t want = ballot((!hv && n + p > topk) || n + p > cap - 2 * kBK);
+        if (!want) return;
+        const uint32_t gkmax = group16_max(kmax);
 #pragma unroll 1
-            for (int g = 0; g < 4; ++g) {
-                if (!((want >> (16 * g)) & 1ull)) continue;
-                const int row = 4 * wave + g;
-                const int64_t grow = seq_start + r0 + row;
-                uint32_t *rk = a.cand_key + grow * cap;
-                int32_t *ri = a.cand_idx + grow * cap;
-                const RowHist hist{sm.hist[row >> 1], 16 * (row & 1)};
-                int ng = readlane(n, 16 * g);
-                const uint32_t km = (uint32_t)readlane((int)gkmax, 16 * g);
-                uint32_t th = (uint32_t)readlane((int)theta, 16 * g);
-                bool hvg = readlane(hv ? 1 : 0, 16 * g) != 0;
-                int pb = readlane(pbase, 16 * g), bt = readlane(bth, 16 * g), cm = readlane(cum, 16 * g);
-                __threadfence();
-                if (!hvg) {
-                    pb = window_base(km);
-                    wave_fill_hist<8>(rk, ng, hist, pb);
-                    hvg = true;
-                    bt = 0;
-                    cm = ng;
-                }
-                if (ng > cap - kBK) {
-                    if (bt > 0 && cm <= cap / 2) {
-                        ng = wave_keep_at_least<8>(rk, ri, ng, bin_edge(bt, pb));
-                        cm = ng;
-                    } else {
-                        // scratch: this wave's rows of the partial tile it has just consumed
-                        th = wave_exact_select<8>(rk, ri, ng, topk,
-                                                  reinterpret_cast<uint32_t *>(&sm.red[rb2][0][4 * wave][0]),
-                                                  reinterpret_cast<uint32_t *>(&sm.red[rb2][1][4 * wave][0]));
-                        ng = topk;
-                        pb = window_base(km);
-                        wave_fill_hist<8>(rk, ng, hist, pb);
-                        bt = 0;
-                        cm = ng;
-                    }
-                }
+        for (int g = 0; g < 4; ++g) {
+            if (!((want >> (16 * g)) & 1ull)) continue;
+            if (lg == g) flush_all();
+            const int row = 4 * wave + g;
+            const int64_t grow = seq_start + r0 + row;
+            uint32_t *rk = a.cand_key + grow * cap;
+            int32_t *ri = a.cand_idx + grow * cap;
+            const RowHist hist{sm.hist[row >> 1], 16 * (row & 1)};
+            int ng = readlane(n, 16 * g);
+            const uint32_t km = (uint32_t)readlane((int)gkmax, 16 * g);
+            uint32_t th = (uint32_t)readlane((int)theta, 16 * g);
+            bool hvg = readlane(hv ? 1 : 0, 16 * g) != 0;
+            int pb = readlane(pbase, 16 * g), bt = readlane(bth, 16 * g), cm = readlane(cum, 16 * g);
+            __threadfence();
+            if (!hvg) {
+                pb = window_base(km);
+                wave_fill_hist<8>(rk, ng, hist, pb);
+                hvg = true;
+                bt = 0;
+                cm = ng;
+            }
+            if (ng > cap - 2 * kBK) {
+                // pending advance first, so that bt is as high as the counts allow
                 for (;;) {
                     const int h = hist.get(bt);
                     if (bt < kNB - 1 && cm - h >= topk) {
@@ -462,14 +479,25 @@ __global__ __launch_bounds__(kThreads, 1) void score_topk_kernel(ScoreArgs a) {
                         break;
                     }
                 }
-                if (lg == g) {
-                    n = ng;
-                    theta = th;
-                    hv = hvg;
-                    pbase = pb;
-                    bth = bt;
-                    cum = cm;
+                if (bt > 0 && cm <= cap / 2) {
+                    ng = wave_keep_at_least<8>(rk, ri, ng, bin_edge(bt, pb));
+                    cm = ng;
+                } else {
+                    th = wave_exact_select<8>(rk, ri, ng, topk, scr0, scr1);
+                    ng = topk;
+                    pb = window_base(km);
+                    wave_fill_hist<8>(rk, ng, hist, pb);
+                    bt = 0;
+                    cm = ng;
                 }
+            }
+            if (lg == g) {
+                n = ng;
+                theta = th;
+                hv = hvg;
+                pbase = pb;
+                bth = bt;
+                cum = cm;
             }
         }
     };
@@ -499,10 +527,20 @@ __global__ __launch_bounds__(kThreads, 1) void score_topk_kernel(ScoreArgs a) {
             *reinterpret_cast<f32x4 *>(dst + 48) = acc3;
         }
         if (more) store_k((kt + 1) & 1);
+        if (kt > 0) {
+            // global stores go after the tile load has been consumed, so that waiting for
+            // the next tile does not also wait for them
+            if (p >= 64) flush64();
+            const int rb2 = (kt - 1) & 1;
+            rare(reinterpret_cast<uint32_t *>(&sm.red[rb2][0][4 * wave][0]),
+                 reinterpret_cast<uint32_t *>(&sm.red[rb2][1][4 * wave][0]));
+        }
         __syncthreads();
     }
 
     // ---- final selection and output, one row at a time per wave
+    flush_all();
+    if (hv) advance();
     uint32_t *G = reinterpret_cast<uint32_t *>(smem_raw) + wave * kGather;
     __threadfence();
 #pragma unroll 1
@@ -550,8 +588,8 @@ __global__ __launch_bounds__(kThreads, 1) void score_topk_kernel(ScoreArgs a) {
             for (int j = 0; j < 16; ++j) {
                 const bool sel = base + 64 * j + lane < ng && bin_of(kv[j], pb) == bt;
                 const uint64_t mk = ballot(sel);
-                const int p = gpos + (int)bits_below(mk);
-                if (sel && p < kGather) G[p] = kv[j];
+                const int q = gpos + (int)bits_below(mk);
+                if (sel && q < kGather) G[q] = kv[j];
                 gpos += __popcll(mk);
             }
         }
