@@ -47,6 +47,14 @@ __device__ __forceinline__ f32x4 mfma16x16x32(u32x4 a, u32x4 b, f32x4 c) {
                                                   __builtin_bit_cast(bf16x8, b), c, 0, 0, 0);
 }
 
+// max(x, 0) as one integer max on the bit pattern: non-negative floats order like their
+// bits read as int32, and every negative float (-0 included) is a negative int32, which the
+// max turns into +0.  A float max would first canonicalize x, costing a second instruction.
+__device__ __forceinline__ float relu(float x) {
+    const int b = __float_as_int(x);
+    return __int_as_float(b > 0 ? b : 0);
+}
+
 // ---------------------------------------------------------------- ordering keys
 // Monotone map fp32 -> uint32 (larger score -> larger key); -0 is mapped as +0 so the two
 // zeros tie.  NaN is outside the contract.
@@ -86,6 +94,19 @@ __device__ __forceinline__ int wave_inclusive_sum(int v) {
     }
     return v;
 }
+
+// Inclusive prefix sum within each 16-lane row of the wave (DPP row shifts).
+__device__ __forceinline__ int row16_inclusive_sum(int x) {
+    x += __builtin_amdgcn_update_dpp(0, x, 0x111, 0xF, 0xF, true);   // row_shr:1
+    x += __builtin_amdgcn_update_dpp(0, x, 0x112, 0xF, 0xF, true);   // row_shr:2
+    x += __builtin_amdgcn_update_dpp(0, x, 0x114, 0xF, 0xF, true);   // row_shr:4
+    x += __builtin_amdgcn_update_dpp(0, x, 0x118, 0xF, 0xF, true);   // row_shr:8
+    return x;
+}
+
+// Value of the last lane (15) of the calling lane's 16-lane row (ds_swizzle bit mode:
+// and_mask 0x10, or_mask 0x0F).
+__device__ __forceinline__ int row16_last(int x) { return __builtin_amdgcn_ds_swizzle(x, 0x1F0); }
 
 __device__ __forceinline__ int wave_sum(int v) {
 #pragma unroll

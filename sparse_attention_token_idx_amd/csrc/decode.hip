@@ -76,9 +76,9 @@ __global__ __launch_bounds__(256) void decode_score_kernel(DecArgs a) {
             }
             float p = 0.f;
 #pragma unroll
-            for (int r = 0; r < 4; ++r) p = fmaf(wv[0][r], fmaxf(s_lo[r], 0.f), p);
+            for (int r = 0; r < 4; ++r) p = fmaf(wv[0][r], relu(s_lo[r]), p);
 #pragma unroll
-            for (int r = 0; r < 4; ++r) p = fmaf(wv[1][r], fmaxf(s_hi[r], 0.f), p);
+            for (int r = 0; r < 4; ++r) p = fmaf(wv[1][r], relu(s_hi[r]), p);
             p += __shfl_xor(p, 16, 64);
             p += __shfl_xor(p, 32, 64);
             const int key = s0 + 16 * u + l16;

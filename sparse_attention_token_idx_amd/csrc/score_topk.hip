@@ -45,6 +45,7 @@ struct ScoreSmem {
     float red[2][4][kBQ][kRStride];    // double-buffered partial scores [buf][hg][query][key]
     uint32_t hist[kBQ / 2][kNB];       // candidate histograms, 16-bit counts, two rows a word
     uint64_t ring[kBQ][kRing];         // pending candidates (key | index << 32) per row
+    uint64_t trash[kWaves][64];        // write target of lanes with nothing to emit
 };
 // the final phase reuses k and red as per-wave gather buffers
 static_assert(kWaves * kGather * 4 <= sizeof(uint16_t) * 2 * kBK * kKStride + sizeof(float) * 8 * kBQ * kRStride,
@@ -98,6 +99,19 @@ __device__ __forceinline__ uint32_t bin_edge(int b, int pbase) {
     return (uint32_t)(pbase + b) << kBinShift;
 }
 
+// Maximum over each 16-lane row (DPP row-shift max scan, then the row's last lane).
+__device__ __forceinline__ uint32_t row16_max(uint32_t v) {
+    int x = (int)v;
+#define DSA_ROWMAX_STEP(ctrl)                                                         \
+    {                                                                                 \
+        const uint32_t o = (uint32_t)__builtin_amdgcn_update_dpp(0, x, ctrl, 0xF, 0xF, true); \
+        x = (int)(o > (uint32_t)x ? o : (uint32_t)x);                                 \
+    }
+    DSA_ROWMAX_STEP(0x111) DSA_ROWMAX_STEP(0x112) DSA_ROWMAX_STEP(0x114) DSA_ROWMAX_STEP(0x118)
+#undef DSA_ROWMAX_STEP
+    return (uint32_t)row16_last(x);
+}
+
 __device__ __forceinline__ uint32_t group16_max(uint32_t v) {
 #pragma unroll
     for (int d = 1; d < 16; d <<= 1) {
@@ -121,7 +135,7 @@ __device__ void wave_fill_hist(const uint32_t *keys, int n, RowHist hist, int pb
 #pragma unroll
         for (int j = 0; j < B; ++j) {
             const int i = base + 64 * j + lane;
-            kv[j] = i < n ? keys[i] : 0u;
+            kv[j] = keys[i < n ? i : n - 1];
         }
 #pragma unroll
         for (int j = 0; j < B; ++j)
@@ -142,8 +156,8 @@ __device__ int wave_keep_at_least(uint32_t *keys, int32_t *ids, int n, uint32_t 
 #pragma unroll
         for (int j = 0; j < B; ++j) {
             const int i = base + 64 * j + lane;
-            kv[j] = i < n ? keys[i] : 0u;
-            iv[j] = i < n ? ids[i] : 0;
+            kv[j] = keys[i < n ? i : n - 1];
+            iv[j] = ids[i < n ? i : n - 1];
         }
 #pragma unroll
         for (int j = 0; j < B; ++j) {
@@ -185,7 +199,7 @@ __device__ uint32_t wave_exact_select(uint32_t *keys, int32_t *ids, int n, int t
 #pragma unroll
             for (int j = 0; j < B; ++j) {
                 const int i = base + 64 * j + lane;
-                kv[j] = i < n ? keys[i] : 0u;
+                kv[j] = keys[i < n ? i : n - 1];
             }
 #pragma unroll
             for (int j = 0; j < B; ++j)
@@ -224,8 +238,8 @@ __device__ uint32_t wave_exact_select(uint32_t *keys, int32_t *ids, int n, int t
 #pragma unroll
         for (int j = 0; j < B; ++j) {
             const int i = base + 64 * j + lane;
-            kv[j] = i < n ? keys[i] : 0u;
-            iv[j] = i < n ? ids[i] : 0;
+            kv[j] = keys[i < n ? i : n - 1];
+            iv[j] = ids[i < n ? i : n - 1];
         }
 #pragma unroll
         for (int j = 0; j < B; ++j) {
@@ -295,26 +309,30 @@ __global__ __launch_bounds__(kThreads, 1) void score_topk_kernel(ScoreArgs a) {
 #pragma unroll
         for (int h = 0; h < 8; ++h) {
 #pragma unroll
-            for (int ks = 0; ks < 4; ++ks)
-                qf[h][ks] = ok ? *reinterpret_cast<const u32x4 *>(qrow + h * kDim + 32 * ks)
-                               : u32x4{0u, 0u, 0u, 0u};
-            wv[h] = ok ? bf16_to_f32(a.w[g * kHeads + 8 * hg + h]) : 0.f;
+            for (int ks = 0; ks < 4; ++ks) qf[h][ks] = *reinterpret_cast<const u32x4 *>(qrow + h * kDim + 32 * ks);
+            wv[h] = bf16_to_f32(a.w[g * kHeads + 8 * hg + h]);
+        }
+        if (!ok) {   // rows past the end: zero queries (row 0's data was loaded in their place)
+#pragma unroll
+            for (int h = 0; h < 8; ++h) {
+#pragma unroll
+                for (int ks = 0; ks < 4; ++ks) qf[h][ks] = u32x4{0u, 0u, 0u, 0u};
+                wv[h] = 0.f;
+            }
         }
     }
 
     // ---- key tile staging: thread -> key tid/8, 32 bytes at dim 16*(tid%8)
     const int st_key = tid >> 3, st_dim = 16 * (tid & 7);
     u32x4 kv0, kv1;
+    // Keys past the sequence end are loaded from its last row instead (never a branch, so
+    // the load never waits for earlier stores); the causal mask discards their scores.
     auto load_k = [&](int kt) {
-        const int64_t s = (int64_t)kt * kBK + st_key;
-        if (s < L) {
-            const uint16_t *p = a.k + (seq_start + s) * kDim + st_dim;
-            kv0 = *reinterpret_cast<const u32x4 *>(p);
-            kv1 = *reinterpret_cast<const u32x4 *>(p + 8);
-        } else {
-            kv0 = u32x4{0u, 0u, 0u, 0u};
-            kv1 = kv0;
-        }
+        int64_t s = (int64_t)kt * kBK + st_key;
+        s = s < L ? s : L - 1;
+        const uint16_t *p = a.k + (seq_start + s) * kDim + st_dim;
+        kv0 = *reinterpret_cast<const u32x4 *>(p);
+        kv1 = *reinterpret_cast<const u32x4 *>(p + 8);
     };
     auto store_k = [&](int buf) {
         uint16_t *p = &sm.k[buf][st_key][st_dim];
@@ -332,7 +350,8 @@ __global__ __launch_bounds__(kThreads, 1) void score_topk_kernel(ScoreArgs a) {
     int32_t *ci = a.cand_idx + egrow * cap;
     uint64_t *ring = sm.ring[er];
     const RowHist rh{sm.hist[er >> 1], 16 * (er & 1)};
-    uint32_t theta = 0u;   // emit key > theta (0 is below every finite score's key)
+    // emit key > theta (0 is below every finite score's key; rows past the end never emit)
+    uint32_t theta = erow_ok ? 0u : 0xFFFFFFFFu;
     int n = 0;             // candidates already in the list in memory
     int p = 0;             // candidates pending in the LDS ring, starting at slot head
     int head = 0;
@@ -340,9 +359,12 @@ __global__ __launch_bounds__(kThreads, 1) void score_topk_kernel(ScoreArgs a) {
     int pbase = 0;         // histogram window
     int bth = 0;           // bin of the threshold: bins >= bth hold the live candidates
     int cum = 0;           // number of candidates in bins >= bth
-    uint32_t kmax = 0u;    // largest key this lane emitted
-    const uint64_t gmask = 0xFFFFull << (16 * lg);
+    uint32_t kmax = 0u;    // largest key this lane has written to the list
     const int64_t wave_last_row = r0 + 16 * qg + 15;
+    uint64_t *const trash = &sm.trash[wave][lane];
+
+    int live_pend = 0;     // flushed candidates in bins >= bth not yet added to cum (per lane)
+    bool dirty = false;    // flushed since the last advance
 
     // Move the threshold up while the bins above bth alone hold topk candidates.
     auto advance = [&]() {
@@ -358,7 +380,28 @@ __global__ __launch_bounds__(kThreads, 1) void score_topk_kernel(ScoreArgs a) {
             }
         }
     };
-    // Write 64 pending candidates of the ring to the list with 16-byte stores (group-wide).
+    // Fold the flushed candidates into cum and advance (row-wide).
+    auto settle = [&]() {
+        cum += row16_last(row16_inclusive_sum(live_pend));
+        live_pend = 0;
+        dirty = false;
+        advance();
+    };
+    // Place the histogram window for a row whose largest candidate so far is m.
+    auto place = [&](uint32_t m) {
+        pbase = window_base(m);
+        hv = true;
+        bth = 0;
+        cum = 0;
+    };
+    auto account = [&](uint32_t key) {
+        kmax = key > kmax ? key : kmax;
+        const int b = bin_of(key, pbase);
+        rh.inc(b);
+        live_pend += b >= bth ? 1 : 0;
+    };
+    // Write 64 pending candidates of the ring to the list with 16-byte stores (row-wide).
+    // The first flush of a row places its histogram window from these 64 keys.
     auto flush64 = [&]() {
         const uint64_t *src = ring + head + 4 * l16;
         const u32x4 lo = *reinterpret_cast<const u32x4 *>(src);
@@ -367,20 +410,43 @@ __global__ __launch_bounds__(kThreads, 1) void score_topk_kernel(ScoreArgs a) {
         const u32x4a4 iv = {lo[1], lo[3], hi[1], hi[3]};
         *reinterpret_cast<u32x4a4 *>(ck + n + 4 * l16) = kv;
         *reinterpret_cast<u32x4a4 *>(ci + n + 4 * l16) = iv;
+        if (!hv) {
+            uint32_t m = kv[0] > kv[1] ? kv[0] : kv[1];
+            const uint32_t m2 = kv[2] > kv[3] ? kv[2] : kv[3];
+            place(row16_max(m > m2 ? m : m2));
+        }
+#pragma unroll
+        for (int i = 0; i < 4; ++i) account(kv[i]);
         n += 64;
         p -= 64;
         head ^= 64;
+        dirty = true;
     };
-    // Write every pending candidate of the ring to the list (group-wide, any count).
+    // Write every pending candidate of the ring to the list and settle (row-wide).
     auto flush_all = [&]() {
+        if (!hv && n + p > topk) {
+            uint32_t m = kmax;
+            for (int i = l16; i < p; i += 16) {
+                const uint32_t k = (uint32_t)ring[(head + i) & (kRing - 1)];
+                m = k > m ? k : m;
+            }
+            place(row16_max(m));
+            // candidates already in the list were written before the window existed
+            for (int i = l16; i < n; i += 16) account(ck[i]);
+        }
         for (int i = l16; i < p; i += 16) {
             const uint64_t e = ring[(head + i) & (kRing - 1)];
             ck[n + i] = (uint32_t)e;
             ci[n + i] = (int32_t)(e >> 32);
+            if (hv) account((uint32_t)e);
         }
         n += p;
         p = 0;
         head = 0;
+        if (hv) {
+            wave_sync_lds();
+            settle();
+        }
     };
 
     // ---- one tile of q.k on the matrix cores: 16 keys (subtile st) x 16 queries x 8 heads
@@ -403,51 +469,47 @@ __global__ __launch_bounds__(kThreads, 1) void score_topk_kernel(ScoreArgs a) {
     };
 
     // ---- candidates of tile ke for row er: this lane covers keys 4*l16 .. 4*l16+3.
-    // Only LDS is touched here (the ring, the histogram and the partial tile).
+    // Only LDS is touched: every lane writes all four slots, the losers to its trash slot,
+    // and positions come from a prefix sum over the row's 16 lanes.
     auto emit = [&](int ke) {
         const int rb2 = ke & 1;
-        // the previous tile's histogram updates are complete (a barrier has passed)
-        if (hv) advance();
+        // fold in the last flush (its histogram updates completed before the barrier)
+        if (dirty) settle();
         f32x4 v = *reinterpret_cast<const f32x4 *>(&sm.red[rb2][0][er][4 * l16]);
 #pragma unroll
         for (int g = 1; g < 4; ++g) v += *reinterpret_cast<const f32x4 *>(&sm.red[rb2][g][er][4 * l16]);
         const int s0 = ke * kBK + 4 * l16;
         uint32_t kk[4];
         bool e[4];
-        int before = 0, total = 0;
+        int c = 0;
 #pragma unroll
         for (int j = 0; j < 4; ++j) {
             kk[j] = score_key(v[j]);
-            e[j] = erow_ok && (s0 + j <= et32) && (kk[j] > theta);
-            const uint64_t b = ballot(e[j]) & gmask;
-            before += (int)bits_below(b);
-            total += __popcll(b);
+            e[j] = kk[j] > theta && s0 + j <= et32;
+            c += e[j] ? 1 : 0;
         }
-        int slot = head + p + before;
+        const int incl = row16_inclusive_sum(c);
+        int pos = head + p + incl - c;
 #pragma unroll
         for (int j = 0; j < 4; ++j) {
-            if (e[j]) {
-                ring[slot & (kRing - 1)] = (uint64_t)kk[j] | ((uint64_t)(uint32_t)(s0 + j) << 32);
-                ++slot;
-                kmax = kk[j] > kmax ? kk[j] : kmax;
-                if (hv) rh.inc(bin_of(kk[j], pbase));
-            }
+            uint64_t *dst = e[j] ? ring + (pos & (kRing - 1)) : trash;
+            *dst = (uint64_t)kk[j] | ((uint64_t)(uint32_t)(s0 + j) << 32);
+            pos += e[j] ? 1 : 0;
         }
-        p += total;
-        if (hv) cum += total;
+        p += row16_last(incl);
     };
 
     // ---- rare per-row work, done by the whole wave one row at a time: place the histogram
     // once a row holds more than topk candidates; compact a full list.  scratch: two
     // 256-word areas only this wave uses right now.
     auto rare = [&](uint32_t *scr0, uint32_t *scr1) {
-        const uint64_t want = ballot((!hv && n + p > topk) || n + p > cap - 2 * kBK);
+        const uint64_t want = ballot(n + p > cap - 2 * kBK);
         if (!want) return;
+        if ((want >> (16 * lg)) & 1ull) flush_all();
         const uint32_t gkmax = group16_max(kmax);
 #pragma unroll 1
         for (int g = 0; g < 4; ++g) {
             if (!((want >> (16 * g)) & 1ull)) continue;
-            if (lg == g) flush_all();
             const int row = 4 * wave + g;
             const int64_t grow = seq_start + r0 + row;
             uint32_t *rk = a.cand_key + grow * cap;
@@ -456,18 +518,20 @@ __global__ __launch_bounds__(kThreads, 1) void score_topk_kernel(ScoreArgs a) {
             int ng = readlane(n, 16 * g);
             const uint32_t km = (uint32_t)readlane((int)gkmax, 16 * g);
             uint32_t th = (uint32_t)readlane((int)theta, 16 * g);
-            bool hvg = readlane(hv ? 1 : 0, 16 * g) != 0;
             int pb = readlane(pbase, 16 * g), bt = readlane(bth, 16 * g), cm = readlane(cum, 16 * g);
             __threadfence();
-            if (!hvg) {
+            if (bt > 0 && cm <= cap / 2) {
+                // drop the dead candidates (bins below the threshold bin)
+                ng = wave_keep_at_least<8>(rk, ri, ng, bin_edge(bt, pb));
+                cm = ng;
+            } else {
+                // too many live candidates: exact select, then re-place the window
+                th = wave_exact_select<8>(rk, ri, ng, topk, scr0, scr1);
+                ng = topk;
                 pb = window_base(km);
                 wave_fill_hist<8>(rk, ng, hist, pb);
-                hvg = true;
                 bt = 0;
                 cm = ng;
-            }
-            if (ng > cap - 2 * kBK) {
-                // pending advance first, so that bt is as high as the counts allow
                 for (;;) {
                     const int h = hist.get(bt);
                     if (bt < kNB - 1 && cm - h >= topk) {
@@ -479,22 +543,10 @@ __global__ __launch_bounds__(kThreads, 1) void score_topk_kernel(ScoreArgs a) {
                         break;
                     }
                 }
-                if (bt > 0 && cm <= cap / 2) {
-                    ng = wave_keep_at_least<8>(rk, ri, ng, bin_edge(bt, pb));
-                    cm = ng;
-                } else {
-                    th = wave_exact_select<8>(rk, ri, ng, topk, scr0, scr1);
-                    ng = topk;
-                    pb = window_base(km);
-                    wave_fill_hist<8>(rk, ng, hist, pb);
-                    bt = 0;
-                    cm = ng;
-                }
             }
             if (lg == g) {
                 n = ng;
                 theta = th;
-                hv = hvg;
                 pbase = pb;
                 bth = bt;
                 cum = cm;
@@ -504,13 +556,16 @@ __global__ __launch_bounds__(kThreads, 1) void score_topk_kernel(ScoreArgs a) {
 
     // ---- the stream: tile kt's products run while tile kt-1's candidates are emitted;
     // one barrier per tile
+    for (int i = tid; i < (kBQ / 2) * kNB; i += kThreads) (&sm.hist[0][0])[i] = 0u;
     load_k(0);
     store_k(0);
     __syncthreads();
     for (int kt = 0; kt <= nkt; ++kt) {
         const bool have = kt < nkt;
-        const bool more = kt + 1 < nkt;
-        if (more) load_k(kt + 1);
+        // always fetch a tile (the last one again past the end) and always stage it: with no
+        // conditional load the compiler never waits at the top of the loop, and a wait there
+        // would also wait for the candidate stores (vmcnt counts loads and stores in order)
+        load_k(kt + 1 < nkt ? kt + 1 : nkt - 1);
         f32x4 acc0, acc1, acc2, acc3;
         if (have) {
             mfma_subtile(kt, 0, acc0);
@@ -526,7 +581,7 @@ __global__ __launch_bounds__(kThreads, 1) void score_topk_kernel(ScoreArgs a) {
             *reinterpret_cast<f32x4 *>(dst + 32) = acc2;
             *reinterpret_cast<f32x4 *>(dst + 48) = acc3;
         }
-        if (more) store_k((kt + 1) & 1);
+        store_k((kt + 1) & 1);
         if (kt > 0) {
             // global stores go after the tile load has been consumed, so that waiting for
             // the next tile does not also wait for them
@@ -540,7 +595,6 @@ __global__ __launch_bounds__(kThreads, 1) void score_topk_kernel(ScoreArgs a) {
 
     // ---- final selection and output, one row at a time per wave
     flush_all();
-    if (hv) advance();
     uint32_t *G = reinterpret_cast<uint32_t *>(smem_raw) + wave * kGather;
     __threadfence();
 #pragma unroll 1
@@ -582,7 +636,7 @@ __global__ __launch_bounds__(kThreads, 1) void score_topk_kernel(ScoreArgs a) {
 #pragma unroll
             for (int j = 0; j < 16; ++j) {
                 const int i = base + 64 * j + lane;
-                kv[j] = i < ng ? rk[i] : 0u;
+                kv[j] = rk[i < ng ? i : ng - 1];
             }
 #pragma unroll
             for (int j = 0; j < 16; ++j) {
@@ -614,8 +668,8 @@ __global__ __launch_bounds__(kThreads, 1) void score_topk_kernel(ScoreArgs a) {
 #pragma unroll
             for (int j = 0; j < 8; ++j) {
                 const int i = base + 64 * j + lane;
-                kv[j] = i < ng ? rk[i] : 0u;
-                iv[j] = i < ng ? ri[i] : 0;
+                kv[j] = rk[i < ng ? i : ng - 1];
+                iv[j] = ri[i < ng ? i : ng - 1];
             }
 #pragma unroll
             for (int j = 0; j < 8; ++j) {
