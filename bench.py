@@ -30,6 +30,10 @@ ROOT = os.path.dirname(os.path.abspath(__file__))
 sys.path.insert(0, ROOT)
 
 PEAK_BF16_TFLOPS = 2516.6     # MI355X dense bf16 MFMA (published)
+# HBM bytes per launch of score_topk_kernel at T=65536, topk 2048, from rocprofv3
+# FETCH_SIZE and WRITE_SIZE scaled by a 1 GiB device-copy calibration; reported only while
+# the kernel source is the one the counters were taken on
+TRAFFIC_SCORE_T65536 = {"source_sha256_prefix": "e9ca51a27e6fd079", "bytes": 7.990e9 + 6.432e9}
 PEAK_HBM_GBPS = 8000.0        # MI355X HBM3E (published)
 H, D, QLAT, HIDDEN = 32, 128, 1536, 7168
 PROJ_FLOP_PER_TOKEN = 2 * (QLAT * 4096 + HIDDEN * D + HIDDEN * H)   # 14,876,672
@@ -58,6 +62,15 @@ def parse():
 def dev_bf16(a):
     import torch
     return torch.from_numpy(a.view(np.int16)).view(torch.bfloat16).cuda()
+
+
+def score_traffic(args):
+    import hashlib
+    src = os.path.join(ROOT, "sparse_attention_token_idx_amd", "csrc", "score_topk.hip")
+    h = hashlib.sha256(open(src, "rb").read()).hexdigest()[:16]
+    if args.T == 65536 and args.topk == 2048 and h == TRAFFIC_SCORE_T65536["source_sha256_prefix"]:
+        return TRAFFIC_SCORE_T65536["bytes"]
+    return None
 
 
 def bench_prefill(dsa, args):
@@ -254,7 +267,7 @@ def main():
                      "sum_of_events": round(ms_step, 3)},
         "roofline": {"kernel": "score_topk_kernel", "bound": "mfma",
                      "achieved": round(achieved, 1), "peak": PEAK_BF16_TFLOPS, "unit": "TFLOP/s",
-                     "frac": round(achieved / PEAK_BF16_TFLOPS, 4), "traffic": None,
+                     "frac": round(achieved / PEAK_BF16_TFLOPS, 4), "traffic": score_traffic(args),
                      "algorithmic_flop_per_launch": pre["score_flop"]},
         "decode": None if dec is None else {
             "workload": f"{dec['batch']} sequences, one new query each, cached bf16 keys "

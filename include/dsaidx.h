@@ -12,7 +12,7 @@
  *
  * and each query keeps the 2,048 tokens with the largest scores, which become the only
  * keys its MLA attends (gated-MLA row of the same table).  The key LayerNorm is named in
- * the QK-norm row; the indexer applies no rotary embedding ("Kimi K3.1 Pro vs Gemma 4"
+ * the QK-norm row; the indexer applies no rotary embedding ("Kimi K3.1 Pro vs Gemma 4 31B"
  * page, RoPE row) and scores the whole prefix (same page, long-context row).  Serving
  * engines cache the indexer keys across decode steps ("Kimi K3.1 Pro vs GLM-5" page,
  * low-precision row); dsa_idx_decode scores against such a cache.

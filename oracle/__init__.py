@@ -11,7 +11,7 @@ archdiff.com compare pages on Kimi K3.1 Pro (component tables):
     k = LayerNorm(x W_k) (7,168 -> 128, one key shared by all heads),
     w = x W_w (7,168 -> 32), I = sum_h w_h ReLU(q_h . k), top 2,048 per query;
   * QK-norm row: the LayerNorm is on the indexer key;
-  * RoPE row (K3.1 vs Gemma 4 page): no rotary step in the indexer;
+  * RoPE row ("Kimi K3.1 Pro vs Gemma 4 31B" page): no rotary step in the indexer;
   * long-context row (same page): the whole prefix is scored.
 """
 import ctypes

@@ -12,7 +12,7 @@
  *     per-head weights from a 7,168 -> 32 projection, scores
  *     I = sum_h w_h * ReLU(q_h . k), top 2,048 tokens kept per query;
  *   - QK-norm row: the LayerNorm sits on the indexer key;
- *   - RoPE row of the "Kimi K3.1 Pro vs Gemma 4" page: the indexer uses no
+ *   - RoPE row of the "Kimi K3.1 Pro vs Gemma 4 31B" page: the indexer uses no
  *     rotary embedding (index_rope_dim = 0);
  *   - long-context row of that page: the indexer scores the whole prefix.
  *

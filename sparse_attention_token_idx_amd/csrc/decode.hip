@@ -2,7 +2,7 @@
 // (serving engines cache the indexer keys: "Kimi K3.1 Pro vs GLM-5" compare page,
 // low-precision row), then the top-k of the whole prefix (sparse/compressed-attention
 // row of the "Qwen3.5-397B-A17B vs Kimi K3.1 Pro" page; long-context row of the
-// "Kimi K3.1 Pro vs Gemma 4" page).
+// "Kimi K3.1 Pro vs Gemma 4 31B" page).
 //
 // Pass 1 streams the key cache once (256 bytes per key, the bandwidth-bound part): each
 // 16-key slice is one pair of v_mfma_f32_16x16x32_bf16 chains with the 32 heads as the M

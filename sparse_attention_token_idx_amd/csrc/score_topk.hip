@@ -4,7 +4,7 @@
 // over its whole causal prefix s <= t and keeps the topk largest (ties -> lower s), as
 // fixed on the "Qwen3.5-397B-A17B vs Kimi K3.1 Pro" compare page (component table,
 // sparse/compressed-attention row) with the whole prefix scored (long-context row of the
-// "Kimi K3.1 Pro vs Gemma 4" page).  The T x T score matrix never reaches memory.
+// "Kimi K3.1 Pro vs Gemma 4 31B" page).  The T x T score matrix never reaches memory.
 //
 // One workgroup (8 waves) owns 32 query rows and streams the keys of their prefix in
 // tiles of 64:
