@@ -64,6 +64,13 @@ __device__ __forceinline__ uint32_t score_key(float v) {
     return (u & 0x80000000u) ? ~u : (u | 0x80000000u);
 }
 
+// score_key for a value known not to be -0 (the two zeros would get different keys): one
+// arithmetic shift and two bitwise ops.
+__device__ __forceinline__ uint32_t score_key_nz(float v) {
+    const uint32_t u = __float_as_uint(v);
+    return u ^ ((uint32_t)((int32_t)u >> 31) | 0x80000000u);
+}
+
 __device__ __forceinline__ float key_score(uint32_t k) {
     uint32_t u = (k & 0x80000000u) ? (k & 0x7FFFFFFFu) : ~k;
     return __uint_as_float(u);

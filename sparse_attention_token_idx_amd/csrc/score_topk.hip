@@ -360,7 +360,6 @@ __global__ __launch_bounds__(kThreads, 1) void score_topk_kernel(ScoreArgs a) {
     int bth = 0;           // bin of the threshold: bins >= bth hold the live candidates
     int cum = 0;           // number of candidates in bins >= bth
     uint32_t kmax = 0u;    // largest key this lane has written to the list
-    const int64_t wave_last_row = r0 + 16 * qg + 15;
     uint64_t *const trash = &sm.trash[wave][lane];
 
     int live_pend = 0;     // flushed candidates in bins >= bth not yet added to cum (per lane)
@@ -449,32 +448,14 @@ __global__ __launch_bounds__(kThreads, 1) void score_topk_kernel(ScoreArgs a) {
         }
     };
 
-    // ---- one tile of q.k on the matrix cores: 16 keys (subtile st) x 16 queries x 8 heads
-    auto mfma_subtile = [&](int kt, int st, f32x4 &acc) {
-        acc = f32x4{0.f, 0.f, 0.f, 0.f};
-        if ((int64_t)kt * kBK + 16 * st > wave_last_row) return;   // wave-uniform causal skip
-        const int buf = kt & 1;
-        u32x4 af[4];
-#pragma unroll
-        for (int ks = 0; ks < 4; ++ks)
-            af[ks] = *reinterpret_cast<const u32x4 *>(&sm.k[buf][16 * st + l16][32 * ks + 8 * lg]);
-#pragma unroll
-        for (int h = 0; h < 8; ++h) {
-            f32x4 sc = {0.f, 0.f, 0.f, 0.f};
-#pragma unroll
-            for (int ks = 0; ks < 4; ++ks) sc = mfma16x16x32(af[ks], qf[h][ks], sc);
-#pragma unroll
-            for (int r = 0; r < 4; ++r) acc[r] = fmaf(wv[h], fmaxf(sc[r], 0.f), acc[r]);
-        }
-    };
-
     // ---- candidates of tile ke for row er: this lane covers keys 4*l16 .. 4*l16+3.
     // Only LDS is touched: every lane writes all four slots, the losers to its trash slot,
-    // and positions come from a prefix sum over the row's 16 lanes.
-    auto emit = [&](int ke) {
+    // and positions come from a prefix sum over the row's 16 lanes.  Straight-line code (en
+    // false: nothing is emitted), so that it can be interleaved with the matrix products.
+    // A summed score is never -0 (every partial sum starts from +0, and in round-to-nearest
+    // an exact zero of nonzero terms is +0), so the shorter key map applies.
+    auto emit_core = [&](int ke, bool en) {
         const int rb2 = ke & 1;
-        // fold in the last flush (its histogram updates completed before the barrier)
-        if (dirty) settle();
         f32x4 v = *reinterpret_cast<const f32x4 *>(&sm.red[rb2][0][er][4 * l16]);
 #pragma unroll
         for (int g = 1; g < 4; ++g) v += *reinterpret_cast<const f32x4 *>(&sm.red[rb2][g][er][4 * l16]);
@@ -484,8 +465,8 @@ __global__ __launch_bounds__(kThreads, 1) void score_topk_kernel(ScoreArgs a) {
         int c = 0;
 #pragma unroll
         for (int j = 0; j < 4; ++j) {
-            kk[j] = score_key(v[j]);
-            e[j] = kk[j] > theta && s0 + j <= et32;
+            kk[j] = score_key_nz(v[j]);
+            e[j] = en && kk[j] > theta && s0 + j <= et32;
             c += e[j] ? 1 : 0;
         }
         const int incl = row16_inclusive_sum(c);
@@ -497,6 +478,70 @@ __global__ __launch_bounds__(kThreads, 1) void score_topk_kernel(ScoreArgs a) {
             pos += e[j] ? 1 : 0;
         }
         p += row16_last(incl);
+    };
+
+    // ---- one key tile on the matrix cores, software pipelined.  A unit is 16 keys (one
+    // subtile) x 16 queries x 4 heads: four independent MFMA chains over the 128 dims.  The
+    // ReLU / w epilogue of each unit runs under the products of the next one, and the
+    // candidates of the previous tile (emit_core) are interleaved as well; the scheduling
+    // groups at the end of every unit ask for one MFMA followed by up to three VALU ops.
+    // Keys past the causal end are computed like the others and masked when emitted.
+    auto tile_block = [&](int kt) {
+        const int buf = kt & 1;
+        const uint16_t *kb = &sm.k[buf][l16][8 * lg];
+        u32x4 a[4];
+#pragma unroll
+        for (int ks = 0; ks < 4; ++ks) a[ks] = *reinterpret_cast<const u32x4 *>(kb + 32 * ks);
+        emit_core(kt - 1, kt > 0);
+        float *dst = &sm.red[buf][hg][16 * qg + l16][4 * lg];
+        f32x4 prev[4];
+        f32x4 acc = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+        for (int st = 0; st < 4; ++st) {
+#pragma unroll
+            for (int u = 0; u < 2; ++u) {
+                f32x4 cur[4];
+#pragma unroll
+                for (int h = 0; h < 4; ++h) cur[h] = mfma16x16x32(a[0], qf[4 * u + h][0], f32x4{0.f, 0.f, 0.f, 0.f});
+#pragma unroll
+                for (int ks = 1; ks < 4; ++ks)
+#pragma unroll
+                    for (int h = 0; h < 4; ++h) cur[h] = mfma16x16x32(a[ks], qf[4 * u + h][ks], cur[h]);
+                if (u == 1 && st < 3) {
+#pragma unroll
+                    for (int ks = 0; ks < 4; ++ks)
+                        a[ks] = *reinterpret_cast<const u32x4 *>(kb + (16 * (st + 1)) * kKStride + 32 * ks);
+                }
+                if (st > 0 || u > 0) {
+                    // epilogue of the previous unit (heads 4*(1-u) .. of subtile st-(u==0))
+                    const int pu = 1 - u;
+#pragma unroll
+                    for (int h = 0; h < 4; ++h)
+#pragma unroll
+                        for (int r = 0; r < 4; ++r) acc[r] = fmaf(wv[4 * pu + h], relu(prev[h][r]), acc[r]);
+                    if (u == 0) {
+                        *reinterpret_cast<f32x4 *>(dst + 16 * (st - 1)) = acc;
+                        acc = f32x4{0.f, 0.f, 0.f, 0.f};
+                    }
+                }
+                if (u == 1 && st < 3) {
+#pragma unroll
+                    for (int i = 0; i < 4; ++i) __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);
+                }
+#pragma unroll
+                for (int i = 0; i < 16; ++i) {
+                    __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);   // MFMA
+                    __builtin_amdgcn_sched_group_barrier(0x002, 3, 0);   // VALU
+                }
+#pragma unroll
+                for (int h = 0; h < 4; ++h) prev[h] = cur[h];
+            }
+        }
+#pragma unroll
+        for (int h = 0; h < 4; ++h)
+#pragma unroll
+            for (int r = 0; r < 4; ++r) acc[r] = fmaf(wv[4 + h], relu(prev[h][r]), acc[r]);
+        *reinterpret_cast<f32x4 *>(dst + 48) = acc;
     };
 
     // ---- rare per-row work, done by the whole wave one row at a time: place the histogram
@@ -560,27 +605,14 @@ __global__ __launch_bounds__(kThreads, 1) void score_topk_kernel(ScoreArgs a) {
     load_k(0);
     store_k(0);
     __syncthreads();
-    for (int kt = 0; kt <= nkt; ++kt) {
-        const bool have = kt < nkt;
-        // always fetch a tile (the last one again past the end) and always stage it: with no
+    for (int kt = 0; kt < nkt; ++kt) {
+        // always fetch a tile (the last one again at the end) and always stage it: with no
         // conditional load the compiler never waits at the top of the loop, and a wait there
         // would also wait for the candidate stores (vmcnt counts loads and stores in order)
         load_k(kt + 1 < nkt ? kt + 1 : nkt - 1);
-        f32x4 acc0, acc1, acc2, acc3;
-        if (have) {
-            mfma_subtile(kt, 0, acc0);
-            mfma_subtile(kt, 1, acc1);
-        }
-        if (kt > 0) emit(kt - 1);
-        if (have) {
-            mfma_subtile(kt, 2, acc2);
-            mfma_subtile(kt, 3, acc3);
-            float *dst = &sm.red[kt & 1][hg][16 * qg + l16][4 * lg];
-            *reinterpret_cast<f32x4 *>(dst) = acc0;
-            *reinterpret_cast<f32x4 *>(dst + 16) = acc1;
-            *reinterpret_cast<f32x4 *>(dst + 32) = acc2;
-            *reinterpret_cast<f32x4 *>(dst + 48) = acc3;
-        }
+        // fold in the last flush (its histogram updates completed before the barrier)
+        if (dirty) settle();
+        tile_block(kt);
         store_k((kt + 1) & 1);
         if (kt > 0) {
             // global stores go after the tile load has been consumed, so that waiting for
@@ -592,6 +624,16 @@ __global__ __launch_bounds__(kThreads, 1) void score_topk_kernel(ScoreArgs a) {
         }
         __syncthreads();
     }
+    // candidates of the last tile
+    if (dirty) settle();
+    emit_core(nkt - 1, true);
+    if (p >= 64) flush64();
+    {
+        const int rb2 = (nkt - 1) & 1;
+        rare(reinterpret_cast<uint32_t *>(&sm.red[rb2][0][4 * wave][0]),
+             reinterpret_cast<uint32_t *>(&sm.red[rb2][1][4 * wave][0]));
+    }
+    __syncthreads();
 
     // ---- final selection and output, one row at a time per wave
     flush_all();
