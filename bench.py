@@ -30,10 +30,10 @@ ROOT = os.path.dirname(os.path.abspath(__file__))
 sys.path.insert(0, ROOT)
 
 PEAK_BF16_TFLOPS = 2516.6     # MI355X dense bf16 MFMA (published)
-# HBM bytes per launch of score_topk_kernel at T=65536, topk 2048, from rocprofv3
-# FETCH_SIZE and WRITE_SIZE scaled by a 1 GiB device-copy calibration; reported only while
-# the kernel source is the one the counters were taken on
-TRAFFIC_SCORE_T65536 = {"source_sha256_prefix": "e9ca51a27e6fd079", "bytes": 7.990e9 + 6.432e9}
+# HBM bytes per launch of the scoring kernel at T=65536, from rocprofv3 FETCH_SIZE and
+# WRITE_SIZE scaled by a 1 GiB device-copy calibration; reported only while the kernel
+# source is the one the counters were taken on (None: not measured for this source)
+TRAFFIC_SCORE_T65536 = {"source_sha256_prefix": None, "bytes": None}
 PEAK_HBM_GBPS = 8000.0        # MI355X HBM3E (published)
 H, D, QLAT, HIDDEN = 32, 128, 1536, 7168
 PROJ_FLOP_PER_TOKEN = 2 * (QLAT * 4096 + HIDDEN * D + HIDDEN * H)   # 14,876,672
@@ -66,7 +66,7 @@ def dev_bf16(a):
 
 def score_traffic(args):
     import hashlib
-    src = os.path.join(ROOT, "sparse_attention_token_idx_amd", "csrc", "score_topk.hip")
+    src = os.path.join(ROOT, "sparse_attention_token_idx_amd", "csrc", "scores.hip")
     h = hashlib.sha256(open(src, "rb").read()).hexdigest()[:16]
     if args.T == 65536 and args.topk == 2048 and h == TRAFFIC_SCORE_T65536["source_sha256_prefix"]:
         return TRAFFIC_SCORE_T65536["bytes"]

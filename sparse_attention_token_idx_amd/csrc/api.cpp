@@ -64,9 +64,31 @@ int check_topk(int topk) {
 // Longest sequence the prefill grid can address (row blocks of 32 on grid.y).
 constexpr int64_t kMaxSeq = 65535LL * 32;
 
-size_t ws_score_topk(int64_t total, int topk) {
-    const int cap = dsaidx::candidate_capacity(topk);
-    return (size_t)total * (size_t)cap * 8u;
+// Prefill workspace: [sequence bases: int64 x (B + 1)] [dummy row] [triangular score rows],
+// each part a multiple of 256 bytes.
+size_t round256(size_t b) { return (b + 255u) & ~(size_t)255u; }
+size_t ws_hdr(int B) { return round256(8u * (size_t)(B + 1)); }
+size_t ws_dummy(int64_t max_len) { return round256(4u * (size_t)(((max_len + 63) / 64) * 64)); }
+
+// Score floats of a ragged batch: sequence i needs tri_row_offset(L_i) <= (L_i + 64)^2 / 2
+// floats, and with sum L_i = total, L_i <= max_len and at most B sequences that sum of
+// squares is largest when as many sequences as possible have max_len.
+int64_t varlen_score_floats(int64_t total, int B, int64_t max_len) {
+    if (total == 0 || B == 0 || max_len == 0) return 0;
+    int64_t k = total / max_len;
+    if (k > B) k = B;
+    const int64_t rem = total - k * max_len;
+    const int64_t u = max_len + 64;
+    int64_t sq = k * u * u;
+    if (k < B) sq += (rem + 64) * (rem + 64) + (int64_t)(B - k - 1) * 64 * 64;
+    return ((sq / 2 + 63) / 64) * 64;
+}
+
+size_t ws_score_topk(int64_t T) {
+    return ws_hdr(1) + ws_dummy(T) + 4u * (size_t)dsaidx::tri_row_offset(T);
+}
+size_t ws_score_topk_varlen(int64_t total, int B, int max_seqlen) {
+    return ws_hdr(B) + ws_dummy(max_seqlen) + 4u * (size_t)varlen_score_floats(total, B, max_seqlen);
 }
 
 size_t ws_decode(int B, int max_seqlen) { return (size_t)B * (size_t)max_seqlen * 4u; }
@@ -87,12 +109,20 @@ int dsa_idx_workspace_size(int op, int64_t total_tokens, int B, int max_seqlen, 
             if (total_tokens < 0) return fail(DSA_IDX_EINVAL, "T=%lld < 0", (long long)total_tokens);
             *bytes = 0;
             return ok();
-        case DSA_IDX_OP_SCORE_TOPK:
-        case DSA_IDX_OP_SCORE_TOPK_VARLEN: {
-            if (total_tokens < 0) return fail(DSA_IDX_EINVAL, "total=%lld < 0", (long long)total_tokens);
+        case DSA_IDX_OP_SCORE_TOPK: {
+            if (total_tokens < 0) return fail(DSA_IDX_EINVAL, "T=%lld < 0", (long long)total_tokens);
             int r = check_topk(topk);
             if (r) return r;
-            *bytes = ws_score_topk(total_tokens, topk);
+            *bytes = ws_score_topk(total_tokens);
+            return ok();
+        }
+        case DSA_IDX_OP_SCORE_TOPK_VARLEN: {
+            if (total_tokens < 0 || B < 0 || max_seqlen < 0)
+                return fail(DSA_IDX_EINVAL, "total=%lld B=%d max_seqlen=%d must be >= 0",
+                            (long long)total_tokens, B, max_seqlen);
+            int r = check_topk(topk);
+            if (r) return r;
+            *bytes = ws_score_topk_varlen(total_tokens, B, max_seqlen);
             return ok();
         }
         case DSA_IDX_OP_DECODE: {
@@ -136,14 +166,14 @@ int dsa_idx_project(const dsa_idx_weights *wt, const dsa_idx_bf16 *x, int64_t ld
 }
 
 static int score_common(const dsa_idx_bf16 *q, const dsa_idx_bf16 *k, const dsa_idx_bf16 *w,
-                        int32_t *idx, int topk, int64_t total, void *ws, size_t ws_bytes) {
+                        int32_t *idx, int topk, int64_t total, size_t need, void *ws,
+                        size_t ws_bytes) {
     int r = check_topk(topk);
     if (r) return r;
     if (total == 0) return ok();
     if (!q || !k || !w || !idx) return fail(DSA_IDX_EINVAL, "a tensor pointer is NULL");
     if (!aligned16(q) || !aligned16(k) || !aligned16(w))
         return fail(DSA_IDX_EINVAL, "q, k and w must be 16-byte aligned");
-    const size_t need = ws_score_topk(total, topk);
     if (!ws || ws_bytes < need)
         return fail(DSA_IDX_EWORKSPACE, "workspace %zu bytes < %zu needed", ws ? ws_bytes : (size_t)0, need);
     if (!aligned16(ws)) return fail(DSA_IDX_EINVAL, "workspace must be 16-byte aligned");
@@ -154,17 +184,20 @@ int dsa_idx_score_topk(const dsa_idx_bf16 *q, const dsa_idx_bf16 *k, const dsa_i
                        int64_t T, int topk, int32_t *idx, float *scores, void *ws,
                        size_t ws_bytes, void *stream) {
     if (T < 0) return fail(DSA_IDX_EINVAL, "T=%lld < 0", (long long)T);
-    int r = score_common(q, k, w, idx, topk, T, ws, ws_bytes);
-    if (r || T == 0) return r;
     if (T > kMaxSeq) return fail(DSA_IDX_EUNSUPPORTED, "T=%lld above %lld", (long long)T, (long long)kMaxSeq);
+    int r = score_common(q, k, w, idx, topk, T, ws_score_topk(T), ws, ws_bytes);
+    if (r || T == 0) return r;
     r = check_device();
     if (r) return r;
-    const int cap = dsaidx::candidate_capacity(topk);
-    uint32_t *ck = static_cast<uint32_t *>(ws);
-    int32_t *ci = reinterpret_cast<int32_t *>(ck + (size_t)T * cap);
-    hipError_t e = dsaidx::launch_score_topk(q, k, w, nullptr, 1, T, T, topk, cap, ck, ci, idx, scores,
-                                             reinterpret_cast<hipStream_t>(stream));
-    if (e != hipSuccess) return hip_fail("score_topk launch", e);
+    char *p = static_cast<char *>(ws);
+    int64_t *base = reinterpret_cast<int64_t *>(p);
+    float *dummy = reinterpret_cast<float *>(p + ws_hdr(1));
+    float *rows = reinterpret_cast<float *>(p + ws_hdr(1) + ws_dummy(T));
+    const hipStream_t st = reinterpret_cast<hipStream_t>(stream);
+    hipError_t e = dsaidx::launch_scores(q, k, w, nullptr, 1, T, T, base, rows, dummy, st);
+    if (e != hipSuccess) return hip_fail("scores launch", e);
+    e = dsaidx::launch_row_topk_prefill(rows, nullptr, base, 1, T, T, topk, idx, scores, st);
+    if (e != hipSuccess) return hip_fail("row top-k launch", e);
     return ok();
 }
 
@@ -176,17 +209,22 @@ int dsa_idx_score_topk_varlen(const dsa_idx_bf16 *q, const dsa_idx_bf16 *k,
         return fail(DSA_IDX_EINVAL, "B=%d max_seqlen=%d total=%lld must be >= 0", B, max_seqlen, (long long)total);
     if (B > 0 && !cu_seqlens) return fail(DSA_IDX_EINVAL, "cu_seqlens is NULL");
     if (B > 65535) return fail(DSA_IDX_EUNSUPPORTED, "B=%d above 65535", B);
-    int r = score_common(q, k, w, idx, topk, total, ws, ws_bytes);
-    if (r || total == 0 || B == 0 || max_seqlen == 0) return r;
     if (max_seqlen > kMaxSeq) return fail(DSA_IDX_EUNSUPPORTED, "max_seqlen=%d above %lld", max_seqlen, (long long)kMaxSeq);
+    if (total > (int64_t)B * max_seqlen)
+        return fail(DSA_IDX_EINVAL, "total=%lld above B * max_seqlen", (long long)total);
+    int r = score_common(q, k, w, idx, topk, total, ws_score_topk_varlen(total, B, max_seqlen), ws, ws_bytes);
+    if (r || total == 0 || B == 0 || max_seqlen == 0) return r;
     r = check_device();
     if (r) return r;
-    const int cap = dsaidx::candidate_capacity(topk);
-    uint32_t *ck = static_cast<uint32_t *>(ws);
-    int32_t *ci = reinterpret_cast<int32_t *>(ck + (size_t)total * cap);
-    hipError_t e = dsaidx::launch_score_topk(q, k, w, cu_seqlens, B, max_seqlen, total, topk, cap, ck, ci,
-                                             idx, scores, reinterpret_cast<hipStream_t>(stream));
-    if (e != hipSuccess) return hip_fail("score_topk_varlen launch", e);
+    char *p = static_cast<char *>(ws);
+    int64_t *base = reinterpret_cast<int64_t *>(p);
+    float *dummy = reinterpret_cast<float *>(p + ws_hdr(B));
+    float *rows = reinterpret_cast<float *>(p + ws_hdr(B) + ws_dummy(max_seqlen));
+    const hipStream_t st = reinterpret_cast<hipStream_t>(stream);
+    hipError_t e = dsaidx::launch_scores(q, k, w, cu_seqlens, B, max_seqlen, total, base, rows, dummy, st);
+    if (e != hipSuccess) return hip_fail("scores launch", e);
+    e = dsaidx::launch_row_topk_prefill(rows, cu_seqlens, base, B, total, total, topk, idx, scores, st);
+    if (e != hipSuccess) return hip_fail("row top-k launch", e);
     return ok();
 }
 

@@ -111,9 +111,14 @@ __device__ __forceinline__ int row16_inclusive_sum(int x) {
     return x;
 }
 
-// Value of the last lane (15) of the calling lane's 16-lane row (ds_swizzle bit mode:
-// and_mask 0x10, or_mask 0x0F).
-__device__ __forceinline__ int row16_last(int x) { return __builtin_amdgcn_ds_swizzle(x, 0x1F0); }
+// Value of the last lane (15) of the calling lane's 16-lane row: four lane reads and a
+// select, all on the VALU (no LDS round trip on a latency-bound path).
+__device__ __forceinline__ int row16_last(int x) {
+    const int r0 = __builtin_amdgcn_readlane(x, 15), r1 = __builtin_amdgcn_readlane(x, 31);
+    const int r2 = __builtin_amdgcn_readlane(x, 47), r3 = __builtin_amdgcn_readlane(x, 63);
+    const int g = __lane_id() >> 4;
+    return g == 0 ? r0 : (g == 1 ? r1 : (g == 2 ? r2 : r3));
+}
 
 __device__ __forceinline__ int wave_sum(int v) {
 #pragma unroll

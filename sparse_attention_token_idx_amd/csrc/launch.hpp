@@ -7,8 +7,13 @@
 
 namespace dsaidx {
 
-// Rows of the per-row candidate buffer used by the fused score + top-k kernel.
-int candidate_capacity(int topk);
+// Offset (in floats) of score row t in a sequence's triangular block of the prefill score
+// workspace: row t holds 64 * (t / 64 + 1) scores, rows packed back to back.  The size of a
+// sequence of L rows is tri_row_offset(L).
+__host__ __device__ inline int64_t tri_row_offset(int64_t t) {
+    const int64_t q = t >> 6, r = t & 63;
+    return 2048 * q * (q + 1) + 64 * r * (q + 1);
+}
 
 // ---- projections (project.hip)
 hipError_t launch_project(const uint16_t *x, int64_t ldx, const uint16_t *c_q, int64_t ldc,
@@ -17,14 +22,23 @@ hipError_t launch_project(const uint16_t *x, int64_t ldx, const uint16_t *c_q, i
                           float eps, uint16_t *q, uint16_t *k_base, const int64_t *k_slot,
                           uint16_t *w, hipStream_t stream);
 
-// ---- fused causal score + top-k (score_topk.hip).  cu_seqlens == nullptr -> one
-// sequence of length T.  cand holds total * cap (key, index) pairs.
-hipError_t launch_score_topk(const uint16_t *q, const uint16_t *k, const uint16_t *w,
-                             const int32_t *cu_seqlens, int B, int64_t max_len, int64_t T,
-                             int topk, int cap, uint32_t *cand_key, int32_t *cand_idx,
-                             int32_t *idx, float *scores, hipStream_t stream);
+// ---- prefill scores (scores.hip).  cu_seqlens == nullptr -> one sequence of length T.
+// seq_base: B + 1 int64 (written here for varlen), out: triangular rows, dummy: a row of
+// 64 * ceil(max_len / 64) floats that absorbs the stores of rows past a sequence end.
+hipError_t launch_scores(const uint16_t *q, const uint16_t *k, const uint16_t *w,
+                         const int32_t *cu_seqlens, int B, int64_t max_len, int64_t T,
+                         int64_t *seq_base, float *out, float *dummy, hipStream_t stream);
 
-// ---- decode (decode.hip).  score_buf holds B * max_seqlen floats.
+// ---- row top-k (topk.hip).  Prefill: rows = T (dense) or the packed total (varlen), scores
+// in the triangular layout.  Decode: B rows of stride ld (a multiple of 64), row b holding
+// seqlens[b] scores.
+hipError_t launch_row_topk_prefill(const float *scores, const int32_t *cu_seqlens,
+                                   const int64_t *seq_base, int B, int64_t T, int64_t rows,
+                                   int topk, int32_t *idx, float *out_scores, hipStream_t stream);
+hipError_t launch_row_topk_decode(const float *scores, const int32_t *seqlens, int B, int64_t ld,
+                                  int topk, int32_t *idx, float *out_scores, hipStream_t stream);
+
+// ---- decode (decode.hip).  score_buf holds B rows of ld = 64 * ceil(max_seqlen / 64) floats.
 hipError_t launch_decode(const uint16_t *q, const uint16_t *w, const uint16_t *k_cache,
                          const int64_t *start, const int32_t *seqlens, int B, int max_seqlen,
                          int topk, float *score_buf, int32_t *idx, float *scores,

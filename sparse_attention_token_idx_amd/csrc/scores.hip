@@ -1,0 +1,298 @@
+// Causal indexer scores for prefill (dense and varlen), the matrix-core half of the prefill
+// path.  For every query row t of a sequence and every key s <= t it computes
+//
+//         I[t,s] = sum_h w[t,h] * ReLU( q[t,h,:] . k[s,:] )
+//
+// ("Qwen3.5-397B-A17B vs Kimi K3.1 Pro" compare page, component table, sparse/compressed-
+// attention row; whole prefix scored: long-context row of the "Kimi K3.1 Pro vs Gemma 4 31B"
+// page) and writes the fp32 scores to the workspace, one row per query in a triangular
+// layout (row t holds keys 0 .. 64*(t/64) + 63; the tail past t is never read).  The row
+// top-k (topk.hip) consumes them.
+//
+// One workgroup owns 32 query rows; its 8 waves (2 per SIMD) are symmetric.  Wave w owns rows
+// 4w .. 4w+3 completely: its q (4 queries x 32 heads, bf16) stays in registers as the A
+// operand of v_mfma_f32_16x16x32_bf16.  The 16 output rows of one product are 4 queries x 4
+// heads and the 16 columns are 16 keys (B operand, read from LDS), so each lane gets one
+// query's four head dot products for one key; ReLU and the w-weighted sum over the 32 heads
+// stay in that lane's registers (no exchange between waves), and a 64-key tile's four 16-key
+// slices give each lane the scores of four consecutive keys, stored with one 16-byte write.
+// The keys stream through a ring of LDS tiles that every wave stages one eighth of; progress
+// counters in LDS, not workgroup barriers, order the ring, so waves may drift two tiles apart.
+#include "common.hpp"
+#include "launch.hpp"
+
+namespace dsaidx {
+namespace {
+
+constexpr int kBQ = 32;               // query rows per workgroup
+constexpr int kBK = 64;               // keys per tile
+constexpr int kWaves = 8;             // 4 rows each
+constexpr int kThreads = 64 * kWaves;
+constexpr int kKR = 4;                // key tiles in the LDS ring
+constexpr int kKStride = kDim + 8;    // bf16 per key row in LDS (272 B: conflict-free reads)
+
+struct ScoreSmem {
+    // key ring; key 4n + st of a tile sits in row 16 st + n, so that the 16-key slice st
+    // holds every fourth key and a lane's four slice results are four consecutive keys
+    uint16_t k[kKR][kBK][kKStride];
+    uint32_t k_staged[kWaves];         // key tiles whose eighth wave w has staged
+    uint32_t k_used[kWaves];           // key tiles whose products wave w has finished
+};
+
+struct ScoreArgs {
+    const uint16_t *q;
+    const uint16_t *k;
+    const uint16_t *w;
+    const int32_t *cu_seqlens;  // nullptr: one sequence of length T
+    const int64_t *seq_base;    // start of each sequence's rows in `out` (varlen)
+    int64_t T;
+    int nrb;                    // grid.y: row blocks of the longest sequence
+    float *out;                 // triangular score rows
+    float *dummy;               // write target of rows past a sequence end
+};
+
+// Polls `ctr` (the smallest of kWaves counters) until it reaches `target`.  Every target is
+// reachable (a wave waits only for tiles that slower waves can finish without waiting for
+// it), but as a guard against a broken invariant the polls of one wave share a budget of
+// about a second in total: once it is spent, waits return at once and the kernel ends.
+__device__ __forceinline__ void wait_min_geq(const uint32_t *ctr, uint32_t target, int &budget) {
+    for (; budget > 0; --budget) {
+        uint32_t m = 0xFFFFFFFFu;
+#pragma unroll
+        for (int i = 0; i < kWaves; ++i) {
+            const uint32_t v = __hip_atomic_load(ctr + i, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_WORKGROUP);
+            m = v < m ? v : m;
+        }
+        if (m >= target) break;
+        __builtin_amdgcn_s_sleep(1);
+    }
+    asm volatile("" ::: "memory");
+}
+
+// Publishes this wave's LDS accesses so far (they are performed in order) and bumps `ctr`
+// by one (lane 0 adds 1, the others 0: no branch, which would split the scheduling region).
+__device__ __forceinline__ void signal(uint32_t *ctr) {
+    asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory");
+    __hip_atomic_fetch_add(ctr, __lane_id() == 0 ? 1u : 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_WORKGROUP);
+}
+
+__global__ __launch_bounds__(kThreads, 1) void score_rows_kernel(ScoreArgs a) {
+    extern __shared__ __align__(16) unsigned char smem_raw[];
+    ScoreSmem &sm = *reinterpret_cast<ScoreSmem *>(smem_raw);
+
+    const int seq = blockIdx.x;
+    const int rb = a.nrb - 1 - (int)blockIdx.y;   // longest rows first
+    int64_t seq_start = 0, L = a.T, base = 0;
+    if (a.cu_seqlens) {
+        seq_start = a.cu_seqlens[seq];
+        L = (int64_t)a.cu_seqlens[seq + 1] - seq_start;
+        base = a.seq_base[seq];
+    }
+    const int64_t r0 = (int64_t)rb * kBQ;
+    if (r0 >= L) return;
+    const int rows_here = (int)(L - r0 < kBQ ? L - r0 : kBQ);
+    const int nkt = (int)(r0 / kBK) + 1;          // every row of the block: keys < 64 * nkt
+
+    const int tid = threadIdx.x;
+    const int wave = tid >> 6, lane = tid & 63;
+    const int l16 = lane & 15, lg = lane >> 4;
+
+    if (tid < 2 * kWaves) (&sm.k_staged[0])[tid] = 0u;
+    __syncthreads();
+    int spin = 1 << 22;
+
+    // ---- q fragments: product g covers heads 4g .. 4g+3; A row m = 4 * (query) + (head -
+    // 4g); lane l supplies row l % 16 and the 8 dims 32 ks + 8 (l / 16) .. +7 of k-step ks
+    // (the key fragments use the same dims).  Output element r of lane l is then query
+    // l / 16, head 4g + r, key l % 16 of the slice.
+    u32x4 qa[8][4];
+    f32x4 wv[8];   // head weights of this lane's output query: w[4g + r] of products g
+    {
+        const int qrow = 4 * wave + (l16 >> 2);
+        const bool qok = qrow < rows_here;
+        const int64_t gq = seq_start + r0 + (qok ? qrow : 0);
+        const uint16_t *qp = a.q + gq * kQOut + (l16 & 3) * kDim + 8 * lg;
+#pragma unroll
+        for (int g = 0; g < 8; ++g)
+#pragma unroll
+            for (int ks = 0; ks < 4; ++ks) {
+                const u32x4 v = *reinterpret_cast<const u32x4 *>(qp + (4 * g) * kDim + 32 * ks);
+                qa[g][ks] = qok ? v : u32x4{0u, 0u, 0u, 0u};   // rows past the end: zero
+            }
+        const int wrow = 4 * wave + lg;
+        const bool wok = wrow < rows_here;
+        const int64_t gw = seq_start + r0 + (wok ? wrow : 0);
+#pragma unroll
+        for (int g = 0; g < 8; ++g) {
+            const uint2 w4 = *reinterpret_cast<const uint2 *>(a.w + gw * kHeads + 4 * g);
+            wv[g] = wok ? f32x4{bf16_to_f32(w4.x & 0xFFFFu), bf16_to_f32(w4.x >> 16),
+                                bf16_to_f32(w4.y & 0xFFFFu), bf16_to_f32(w4.y >> 16)}
+                        : f32x4{0.f, 0.f, 0.f, 0.f};
+        }
+    }
+    // this lane's output row; rows past the end write to the dummy row, so that every store
+    // is issued (a conditional store would make each later wait on a load wait for it too)
+    float *orow;
+    {
+        const int row = 4 * wave + lg;
+        orow = row < rows_here ? a.out + base + tri_row_offset(r0 + row) : a.dummy;
+        orow += 4 * l16;
+    }
+
+    // ---- key staging: wave w stages keys 8w .. 8w + 7 of every tile, lane -> key
+    // 8w + lane/8, 32 bytes at dim 16*(lane%8).  Keys past the sequence end are loaded from
+    // its last row; their scores are never read.
+    const int sk = 8 * wave + (lane >> 3), sd = 16 * (lane & 7);
+    u32x4 kv0, kv1;
+    auto load_k = [&](int kt) {
+        int64_t s = (int64_t)kt * kBK + sk;
+        s = s < L ? s : L - 1;
+        const uint16_t *src = a.k + (seq_start + s) * kDim + sd;
+        kv0 = *reinterpret_cast<const u32x4 *>(src);
+        kv1 = *reinterpret_cast<const u32x4 *>(src + 8);
+    };
+    auto store_k = [&](int slot) {
+        uint16_t *dst = &sm.k[slot][16 * (sk & 3) + (sk >> 2)][sd];
+        *reinterpret_cast<u32x4 *>(dst) = kv0;
+        *reinterpret_cast<u32x4 *>(dst + 8) = kv1;
+    };
+    // the first kKR - 2 tiles go to fresh slots
+    for (int u = 0; u < kKR - 2; ++u) {
+        load_k(u < nkt ? u : nkt - 1);
+        store_k(u);
+        signal(&sm.k_staged[wave]);
+    }
+    load_k(kKR - 2 < nkt ? kKR - 2 : nkt - 1);
+
+    // ---- the stream.  Software pipeline inside a tile: a unit is kUG products g (4 heads
+    // each) of one 16-key slice, kUG independent MFMA chains over the 128 dims.  The ReLU / w
+    // epilogue of each unit runs under the next unit's products, the next slice's key
+    // fragments are read under the last unit of the current slice (each as soon as its
+    // register is free), and the scheduling groups ask for one MFMA followed by up to two
+    // VALU ops.
+    constexpr int kUG = 2;
+    constexpr int kUnits = 8 / kUG;
+    f32x4 prev[kUG];
+    f32x4 acc = {0.f, 0.f, 0.f, 0.f};    // per-head-slot sums of the open slice
+    f32x4 sc;                            // scores of the tile, by slice
+    auto epilogue = [&](int g0) {
+#pragma unroll
+        for (int i = 0; i < kUG; ++i)
+#pragma unroll
+            for (int r = 0; r < 4; ++r) acc[r] = fmaf(wv[g0 + i][r], relu(prev[i][r]), acc[r]);
+    };
+    auto close_slice = [&]() {
+        const float v = (acc[0] + acc[1]) + (acc[2] + acc[3]);
+        acc = f32x4{0.f, 0.f, 0.f, 0.f};
+        return v;
+    };
+#pragma unroll 1
+    for (int t = 0; t < nkt; ++t) {
+        wait_min_geq(sm.k_staged, (uint32_t)(t + 1), spin);   // tile t staged by every wave
+        const uint16_t *kb = &sm.k[t % kKR][l16][8 * lg];
+        u32x4 b[4];
+#pragma unroll
+        for (int ks = 0; ks < 4; ++ks) b[ks] = *reinterpret_cast<const u32x4 *>(kb + 32 * ks);
+#pragma unroll
+        for (int st = 0; st < 4; ++st) {
+#pragma unroll
+            for (int u = 0; u < kUnits; ++u) {
+                f32x4 cur[kUG];
+#pragma unroll
+                for (int ks = 0; ks < 4; ++ks) {
+#pragma unroll
+                    for (int i = 0; i < kUG; ++i)
+                        cur[i] = mfma16x16x32(qa[kUG * u + i][ks], b[ks],
+                                              ks ? cur[i] : f32x4{0.f, 0.f, 0.f, 0.f});
+                    if (u == kUnits - 1 && st < 3)
+                        b[ks] = *reinterpret_cast<const u32x4 *>(kb + (16 * (st + 1)) * kKStride + 32 * ks);
+                }
+                if (st > 0 || u > 0) {
+                    epilogue(kUG * ((u + kUnits - 1) % kUnits));
+                    if (u == 0) sc[st - 1] = close_slice();
+                }
+#pragma unroll
+                for (int i = 0; i < 4 * kUG; ++i) {
+                    __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);   // MFMA
+                    __builtin_amdgcn_sched_group_barrier(0x002, 2, 0);   // VALU
+                }
+#pragma unroll
+                for (int i = 0; i < kUG; ++i) prev[i] = cur[i];
+            }
+        }
+        epilogue(8 - kUG);
+        sc[3] = close_slice();
+        signal(&sm.k_used[wave]);             // every read of key slot t % kKR is done
+        // one store and one load per tile, unconditionally and in this order, so that the
+        // wait for the load in the next tile never has to include a store
+        *reinterpret_cast<f32x4 *>(orow + (int64_t)t * kBK) = sc;
+        // stage tile t + kKR - 2 into the slot of tile t - 2 once every wave is done with it
+        // (so waves may drift up to two tiles apart); its loads were issued a tile earlier
+        const int u = t + kKR - 2;
+        if (u < nkt) {
+            wait_min_geq(sm.k_used, (uint32_t)(t - 1 > 0 ? t - 1 : 0), spin);
+            store_k(u % kKR);
+            signal(&sm.k_staged[wave]);
+        }
+        load_k(u + 1 < nkt ? u + 1 : nkt - 1);
+    }
+}
+
+// seq_base[i] = sum over sequences j < i of tri_row_offset(L_j), i = 0 .. B (one workgroup).
+__global__ __launch_bounds__(1024) void seq_base_kernel(const int32_t *cu_seqlens, int B, int64_t *seq_base) {
+    __shared__ int64_t part[1024];
+    const int tid = threadIdx.x;
+    const int per = (B + 1023) / 1024;
+    const int i0 = tid * per, i1 = min(B, i0 + per);
+    int64_t s = 0;
+    for (int i = i0; i < i1; ++i) s += tri_row_offset((int64_t)cu_seqlens[i + 1] - cu_seqlens[i]);
+    part[tid] = s;
+    __syncthreads();
+    for (int d = 1; d < 1024; d <<= 1) {   // inclusive scan of the partial sums
+        const int64_t o = tid >= d ? part[tid - d] : 0;
+        __syncthreads();
+        part[tid] += o;
+        __syncthreads();
+    }
+    int64_t run = tid ? part[tid - 1] : 0;
+    for (int i = i0; i < i1; ++i) {
+        seq_base[i] = run;
+        run += tri_row_offset((int64_t)cu_seqlens[i + 1] - cu_seqlens[i]);
+    }
+    if (tid == 1023) seq_base[B] = part[1023];
+}
+
+}  // namespace
+
+hipError_t launch_scores(const uint16_t *q, const uint16_t *k, const uint16_t *w,
+                         const int32_t *cu_seqlens, int B, int64_t max_len, int64_t T,
+                         int64_t *seq_base, float *out, float *dummy, hipStream_t stream) {
+    static bool attr_done = false;
+    const size_t smem = sizeof(ScoreSmem);
+    if (!attr_done) {
+        hipError_t e = hipFuncSetAttribute(reinterpret_cast<const void *>(score_rows_kernel),
+                                           hipFuncAttributeMaxDynamicSharedMemorySize, (int)smem);
+        if (e != hipSuccess) return e;
+        attr_done = true;
+    }
+    if (B == 0 || max_len == 0) return hipSuccess;
+    if (cu_seqlens) {
+        hipLaunchKernelGGL(seq_base_kernel, dim3(1), dim3(1024), 0, stream, cu_seqlens, B, seq_base);
+        hipError_t e = hipGetLastError();
+        if (e != hipSuccess) return e;
+    }
+    ScoreArgs a;
+    a.q = q;
+    a.k = k;
+    a.w = w;
+    a.cu_seqlens = cu_seqlens;
+    a.seq_base = seq_base;
+    a.T = T;
+    a.nrb = (int)((max_len + kBQ - 1) / kBQ);
+    a.out = out;
+    a.dummy = dummy;
+    hipLaunchKernelGGL(score_rows_kernel, dim3(B, a.nrb), dim3(kThreads), smem, stream, a);
+    return hipGetLastError();
+}
+
+}  // namespace dsaidx
