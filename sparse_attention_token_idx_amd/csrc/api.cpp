@@ -68,20 +68,24 @@ constexpr int64_t kMaxSeq = 65535LL * 32;
 // each part a multiple of 256 bytes.
 size_t round256(size_t b) { return (b + 255u) & ~(size_t)255u; }
 size_t ws_hdr(int B) { return round256(8u * (size_t)(B + 1)); }
-size_t ws_dummy(int64_t max_len) { return round256(4u * (size_t)(((max_len + 63) / 64) * 64)); }
+size_t ws_dummy(int64_t max_len) {
+    const int64_t q = dsaidx::kRowQuant;
+    return round256(4u * (size_t)(((max_len + q - 1) / q) * q));
+}
 
-// Score floats of a ragged batch: sequence i needs tri_row_offset(L_i) <= (L_i + 64)^2 / 2
-// floats, and with sum L_i = total, L_i <= max_len and at most B sequences that sum of
-// squares is largest when as many sequences as possible have max_len.
+// Score floats of a ragged batch: sequence i needs tri_row_offset(L_i) <= (L_i + Q)^2 / 2
+// floats (Q = kRowQuant), and with sum L_i = total, L_i <= max_len and at most B sequences
+// that sum of squares is largest when as many sequences as possible have max_len.
 int64_t varlen_score_floats(int64_t total, int B, int64_t max_len) {
     if (total == 0 || B == 0 || max_len == 0) return 0;
     int64_t k = total / max_len;
     if (k > B) k = B;
     const int64_t rem = total - k * max_len;
-    const int64_t u = max_len + 64;
+    const int64_t Q = dsaidx::kRowQuant;
+    const int64_t u = max_len + Q;
     int64_t sq = k * u * u;
-    if (k < B) sq += (rem + 64) * (rem + 64) + (int64_t)(B - k - 1) * 64 * 64;
-    return ((sq / 2 + 63) / 64) * 64;
+    if (k < B) sq += (rem + Q) * (rem + Q) + (int64_t)(B - k - 1) * Q * Q;
+    return ((sq / 2 + Q - 1) / Q) * Q;
 }
 
 size_t ws_score_topk(int64_t T) {

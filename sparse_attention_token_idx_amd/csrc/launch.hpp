@@ -8,11 +8,12 @@
 namespace dsaidx {
 
 // Offset (in floats) of score row t in a sequence's triangular block of the prefill score
-// workspace: row t holds 64 * (t / 64 + 1) scores, rows packed back to back.  The size of a
-// sequence of L rows is tri_row_offset(L).
+// workspace: row t holds kRowQuant * (t / kRowQuant + 1) scores (whole key tiles of the
+// scoring kernel), rows packed back to back.  A sequence of L rows takes tri_row_offset(L).
+constexpr int64_t kRowQuant = 128;
 __host__ __device__ inline int64_t tri_row_offset(int64_t t) {
-    const int64_t q = t >> 6, r = t & 63;
-    return 2048 * q * (q + 1) + 64 * r * (q + 1);
+    const int64_t q = t / kRowQuant, r = t % kRowQuant;
+    return kRowQuant * kRowQuant / 2 * q * (q + 1) + kRowQuant * r * (q + 1);
 }
 
 // ---- projections (project.hip)
@@ -24,13 +25,14 @@ hipError_t launch_project(const uint16_t *x, int64_t ldx, const uint16_t *c_q, i
 
 // ---- prefill scores (scores.hip).  cu_seqlens == nullptr -> one sequence of length T.
 // seq_base: B + 1 int64 (written here for varlen), out: triangular rows, dummy: a row of
-// 64 * ceil(max_len / 64) floats that absorbs the stores of rows past a sequence end.
+// kRowQuant * ceil(max_len / kRowQuant) floats that absorbs the stores of rows past a
+// sequence end.
 hipError_t launch_scores(const uint16_t *q, const uint16_t *k, const uint16_t *w,
                          const int32_t *cu_seqlens, int B, int64_t max_len, int64_t T,
                          int64_t *seq_base, float *out, float *dummy, hipStream_t stream);
 
 // ---- row top-k (topk.hip).  Prefill: rows = T (dense) or the packed total (varlen), scores
-// in the triangular layout.  Decode: B rows of stride ld (a multiple of 64), row b holding
+// in the triangular layout.  Decode: B rows of stride ld (a multiple of 4), row b holding
 // seqlens[b] scores.
 hipError_t launch_row_topk_prefill(const float *scores, const int32_t *cu_seqlens,
                                    const int64_t *seq_base, int B, int64_t T, int64_t rows,

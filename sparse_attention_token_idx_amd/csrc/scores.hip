@@ -6,7 +6,7 @@
 // ("Qwen3.5-397B-A17B vs Kimi K3.1 Pro" compare page, component table, sparse/compressed-
 // attention row; whole prefix scored: long-context row of the "Kimi K3.1 Pro vs Gemma 4 31B"
 // page) and writes the fp32 scores to the workspace, one row per query in a triangular
-// layout (row t holds keys 0 .. 64*(t/64) + 63; the tail past t is never read).  The row
+// layout (row t holds keys 0 .. 128*(t/128) + 127; the tail past t is never read).  The row
 // top-k (topk.hip) consumes them.
 //
 // One workgroup owns 32 query rows; its 8 waves (2 per SIMD) are symmetric.  Wave w owns rows
@@ -14,8 +14,8 @@
 // operand of v_mfma_f32_16x16x32_bf16.  The 16 output rows of one product are 4 queries x 4
 // heads and the 16 columns are 16 keys (B operand, read from LDS), so each lane gets one
 // query's four head dot products for one key; ReLU and the w-weighted sum over the 32 heads
-// stay in that lane's registers (no exchange between waves), and a 64-key tile's four 16-key
-// slices give each lane the scores of four consecutive keys, stored with one 16-byte write.
+// stay in that lane's registers (no exchange between waves), and a 128-key tile's eight
+// 16-key slices give each lane the scores of eight consecutive keys, stored as 32 bytes.
 // The keys stream through a ring of LDS tiles that every wave stages one eighth of; progress
 // counters in LDS, not workgroup barriers, order the ring, so waves may drift two tiles apart.
 #include "common.hpp"
@@ -25,19 +25,22 @@ namespace dsaidx {
 namespace {
 
 constexpr int kBQ = 32;               // query rows per workgroup
-constexpr int kBK = 64;               // keys per tile
+constexpr int kBK = 128;              // keys per tile (= kRowQuant)
+constexpr int kSlices = kBK / 16;
 constexpr int kWaves = 8;             // 4 rows each
 constexpr int kThreads = 64 * kWaves;
 constexpr int kKR = 4;                // key tiles in the LDS ring
 constexpr int kKStride = kDim + 8;    // bf16 per key row in LDS (272 B: conflict-free reads)
 
 struct ScoreSmem {
-    // key ring; key 4n + st of a tile sits in row 16 st + n, so that the 16-key slice st
-    // holds every fourth key and a lane's four slice results are four consecutive keys
+    // key ring; key 8n + st of a tile sits in row 16 st + n, so that the 16-key slice st
+    // holds every eighth key and a lane's eight slice results are eight consecutive keys
     uint16_t k[kKR][kBK][kKStride];
     uint32_t k_staged[kWaves];         // key tiles whose eighth wave w has staged
     uint32_t k_used[kWaves];           // key tiles whose products wave w has finished
 };
+
+static_assert(kBK == kRowQuant, "a tile is one row quantum of the score layout");
 
 struct ScoreArgs {
     const uint16_t *q;
@@ -91,7 +94,7 @@ __global__ __launch_bounds__(kThreads, 1) void score_rows_kernel(ScoreArgs a) {
     const int64_t r0 = (int64_t)rb * kBQ;
     if (r0 >= L) return;
     const int rows_here = (int)(L - r0 < kBQ ? L - r0 : kBQ);
-    const int nkt = (int)(r0 / kBK) + 1;          // every row of the block: keys < 64 * nkt
+    const int nkt = (int)(r0 / kBK) + 1;          // every row of the block: keys < kBK * nkt
 
     const int tid = threadIdx.x;
     const int wave = tid >> 6, lane = tid & 63;
@@ -136,25 +139,25 @@ __global__ __launch_bounds__(kThreads, 1) void score_rows_kernel(ScoreArgs a) {
     {
         const int row = 4 * wave + lg;
         orow = row < rows_here ? a.out + base + tri_row_offset(r0 + row) : a.dummy;
-        orow += 4 * l16;
+        orow += 8 * l16;
     }
 
-    // ---- key staging: wave w stages keys 8w .. 8w + 7 of every tile, lane -> key
-    // 8w + lane/8, 32 bytes at dim 16*(lane%8).  Keys past the sequence end are loaded from
+    // ---- key staging: wave w stages keys 16w .. 16w + 15 of every tile, lane -> key
+    // 16w + lane/4, 64 bytes at dim 32*(lane%4).  Keys past the sequence end are loaded from
     // its last row; their scores are never read.
-    const int sk = 8 * wave + (lane >> 3), sd = 16 * (lane & 7);
-    u32x4 kv0, kv1;
+    const int sk = 16 * wave + (lane >> 2), sd = 32 * (lane & 3);
+    u32x4 kv[4];
     auto load_k = [&](int kt) {
         int64_t s = (int64_t)kt * kBK + sk;
         s = s < L ? s : L - 1;
         const uint16_t *src = a.k + (seq_start + s) * kDim + sd;
-        kv0 = *reinterpret_cast<const u32x4 *>(src);
-        kv1 = *reinterpret_cast<const u32x4 *>(src + 8);
+#pragma unroll
+        for (int j = 0; j < 4; ++j) kv[j] = *reinterpret_cast<const u32x4 *>(src + 8 * j);
     };
     auto store_k = [&](int slot) {
-        uint16_t *dst = &sm.k[slot][16 * (sk & 3) + (sk >> 2)][sd];
-        *reinterpret_cast<u32x4 *>(dst) = kv0;
-        *reinterpret_cast<u32x4 *>(dst + 8) = kv1;
+        uint16_t *dst = &sm.k[slot][16 * (sk & 7) + (sk >> 3)][sd];
+#pragma unroll
+        for (int j = 0; j < 4; ++j) *reinterpret_cast<u32x4 *>(dst + 8 * j) = kv[j];
     };
     // the first kKR - 2 tiles go to fresh slots
     for (int u = 0; u < kKR - 2; ++u) {
@@ -167,14 +170,13 @@ __global__ __launch_bounds__(kThreads, 1) void score_rows_kernel(ScoreArgs a) {
     // ---- the stream.  Software pipeline inside a tile: a unit is kUG products g (4 heads
     // each) of one 16-key slice, kUG independent MFMA chains over the 128 dims.  The ReLU / w
     // epilogue of each unit runs under the next unit's products, the next slice's key
-    // fragments are read under the last unit of the current slice (each as soon as its
-    // register is free), and the scheduling groups ask for one MFMA followed by up to two
-    // VALU ops.
+    // fragments are read a whole slice ahead, and the scheduling groups ask for one MFMA
+    // followed by up to two VALU ops.
     constexpr int kUG = 2;
     constexpr int kUnits = 8 / kUG;
     f32x4 prev[kUG];
     f32x4 acc = {0.f, 0.f, 0.f, 0.f};    // per-head-slot sums of the open slice
-    f32x4 sc;                            // scores of the tile, by slice
+    float sc[kSlices];                   // scores of the tile, by slice
     auto epilogue = [&](int g0) {
 #pragma unroll
         for (int i = 0; i < kUG; ++i)
@@ -194,7 +196,14 @@ __global__ __launch_bounds__(kThreads, 1) void score_rows_kernel(ScoreArgs a) {
 #pragma unroll
         for (int ks = 0; ks < 4; ++ks) b[ks] = *reinterpret_cast<const u32x4 *>(kb + 32 * ks);
 #pragma unroll
-        for (int st = 0; st < 4; ++st) {
+        for (int st = 0; st < kSlices; ++st) {
+            // the next slice's key fragments, a whole slice ahead of their use
+            u32x4 bn[4];
+            if (st < kSlices - 1) {
+#pragma unroll
+                for (int ks = 0; ks < 4; ++ks)
+                    bn[ks] = *reinterpret_cast<const u32x4 *>(kb + (16 * (st + 1)) * kKStride + 32 * ks);
+            }
 #pragma unroll
             for (int u = 0; u < kUnits; ++u) {
                 f32x4 cur[kUG];
@@ -204,8 +213,6 @@ __global__ __launch_bounds__(kThreads, 1) void score_rows_kernel(ScoreArgs a) {
                     for (int i = 0; i < kUG; ++i)
                         cur[i] = mfma16x16x32(qa[kUG * u + i][ks], b[ks],
                                               ks ? cur[i] : f32x4{0.f, 0.f, 0.f, 0.f});
-                    if (u == kUnits - 1 && st < 3)
-                        b[ks] = *reinterpret_cast<const u32x4 *>(kb + (16 * (st + 1)) * kKStride + 32 * ks);
                 }
                 if (st > 0 || u > 0) {
                     epilogue(kUG * ((u + kUnits - 1) % kUnits));
@@ -219,13 +226,18 @@ __global__ __launch_bounds__(kThreads, 1) void score_rows_kernel(ScoreArgs a) {
 #pragma unroll
                 for (int i = 0; i < kUG; ++i) prev[i] = cur[i];
             }
+            if (st < kSlices - 1) {
+#pragma unroll
+                for (int ks = 0; ks < 4; ++ks) b[ks] = bn[ks];
+            }
         }
         epilogue(8 - kUG);
-        sc[3] = close_slice();
+        sc[kSlices - 1] = close_slice();
         signal(&sm.k_used[wave]);             // every read of key slot t % kKR is done
         // one store and one load per tile, unconditionally and in this order, so that the
         // wait for the load in the next tile never has to include a store
-        *reinterpret_cast<f32x4 *>(orow + (int64_t)t * kBK) = sc;
+        *reinterpret_cast<f32x4 *>(orow + (int64_t)t * kBK) = f32x4{sc[0], sc[1], sc[2], sc[3]};
+        *reinterpret_cast<f32x4 *>(orow + (int64_t)t * kBK + 4) = f32x4{sc[4], sc[5], sc[6], sc[7]};
         // stage tile t + kKR - 2 into the slot of tile t - 2 once every wave is done with it
         // (so waves may drift up to two tiles apart); its loads were issued a tile earlier
         const int u = t + kKR - 2;

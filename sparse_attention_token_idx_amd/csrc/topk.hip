@@ -9,12 +9,15 @@
 // chunk (four 16-byte loads), so index order is thread order.
 //   * Rows of at most 4,096 scores are held in registers and selected exactly.
 //   * Longer rows: a threshold theta0 is placed from a sample of 4,096 scores (64 blocks of
-//     64 consecutive scores spread over the row): the sample's r-th largest key, r chosen so
-//     that about 1.4 topk keys of the row are expected to reach it.  One streaming pass
-//     compacts the keys >= theta0 into LDS in index order; when there are between topk and
-//     4,096 of them (the normal case) the exact select runs over those candidates only.
-//     Otherwise an exact select streams the whole row (three digit passes) and a last pass
-//     writes the result.
+//     64 consecutive scores spread over the row) so that about 1.4 topk keys of the row are
+//     expected to reach it: one histogram pass over fine bins counted down from the sample's
+//     largest key (2^13 key units per bin, which keeps the LDS atomics spread out) finds
+//     the bin that holds the r-th largest sample key, and theta0 is that bin's lower edge.
+//     One streaming pass compacts the keys >= theta0 into LDS in index order; when there are
+//     between topk and 4,096 of them (the normal case) the exact select runs over those
+//     candidates only, on their keys relative to theta0, with only as many 11-bit digit
+//     passes as the candidates' key range needs.  Otherwise an exact select streams the
+//     whole row (three digit passes) and a last pass writes the result.
 // The exact select is a most-significant-digit radix select over the orderable key (11 + 11
 // + 10 bits, an LDS histogram per digit): theta = the topk-th largest key, and how many keys
 // equal to theta are kept (the lowest-index ones).
@@ -36,6 +39,7 @@ struct TopkSmem {
     int32_t cand_idx[kCand];
     uint32_t hist[kBins];
     int32_t wsum[kTkWaves];
+    uint32_t wmax[kTkWaves];
     int32_t bcast[2];
 };
 
@@ -123,6 +127,51 @@ __device__ uint32_t select_regs(const uint32_t (&key)[kPer], int &need, TopkSmem
         pmask |= dmask << shift;
     }
     return prefix;
+}
+
+// Largest of one key per thread over the workgroup.
+__device__ uint32_t block_max(uint32_t v, TopkSmem &sm) {
+    const int lane = __lane_id(), wave = threadIdx.x >> 6;
+#pragma unroll
+    for (int d = 32; d >= 1; d >>= 1) {
+        const uint32_t o = (uint32_t)__shfl_xor((int)v, d, 64);
+        v = o > v ? o : v;
+    }
+    if (lane == 0) sm.wmax[wave] = v;
+    __syncthreads();
+    uint32_t m = 0;
+#pragma unroll
+    for (int i = 0; i < kTkWaves; ++i) m = sm.wmax[i] > m ? sm.wmax[i] : m;
+    __syncthreads();
+    return m;
+}
+
+// Exact select over keys >= base held in registers (0 = no key), digits taken from the
+// relative key (key - base) < 2^nbits, 11 bits at a time from the top: returns theta, the
+// need-th largest key; on return need = how many keys equal to theta are among the need
+// largest.
+__device__ uint32_t select_rel(const uint32_t (&key)[kPer], uint32_t base, int nbits, int &need,
+                               TopkSmem &sm) {
+    uint32_t prefix = 0, pmask = 0;
+    int hi = nbits;
+#pragma unroll 1
+    while (hi > 0) {
+        const int w = hi < 11 ? hi : 11;
+        const int shift = hi - w;
+        const uint32_t dmask = (1u << w) - 1u;
+        for (int i = threadIdx.x; i < kBins; i += kTkThreads) sm.hist[i] = 0u;
+        __syncthreads();
+#pragma unroll
+        for (int i = 0; i < kPer; ++i) {
+            const uint32_t rel = key[i] - base;
+            if (key[i] != 0u && (rel & pmask) == prefix) atomicAdd(&sm.hist[(rel >> shift) & dmask], 1u);
+        }
+        __syncthreads();
+        prefix |= pick_digit(need, sm) << shift;
+        pmask |= dmask << shift;
+        hi = shift;
+    }
+    return base + prefix;
 }
 
 // Writes, in index order, the keys above theta and the first `need` keys equal to theta among
@@ -236,11 +285,58 @@ __global__ __launch_bounds__(kTkThreads) void row_topk_kernel(TopkArgs a) {
     // r such that about 1.4 topk keys of the row reach the r-th largest of the sample
     int r = (int)(((int64_t)topk * 7 * kChunk + (int64_t)5 * n - 1) / ((int64_t)5 * n)) + 8;
     if (r > kChunk) r = kChunk;
-    const uint32_t theta0 = select_regs(key, r, sm);
+    uint32_t theta0;
+    {
+        uint32_t m = 0;
+#pragma unroll
+        for (int i = 0; i < kPer; ++i) m = key[i] > m ? key[i] : m;
+        const uint32_t top = block_max(m, sm);
+        // bins of 2^sb key units counted down from the largest sample key; a second try with
+        // bins wide enough to hold every key if the first window holds fewer than r samples
+        int sb = 13;
+        for (;;) {
+            for (int i = tid; i < kBins; i += kTkThreads) sm.hist[i] = 0u;
+            __syncthreads();
+#pragma unroll
+            for (int i = 0; i < kPer; ++i) {
+                const uint32_t d = (top - key[i]) >> sb;
+                if (key[i] != 0u && d < (uint32_t)kBins) atomicAdd(&sm.hist[d], 1u);
+            }
+            __syncthreads();
+            // bins in descending key order are ascending d: the first bin where the running
+            // count reaches r (thread t owns bins 8t .. 8t+7)
+            int cnt[8], sum = 0;
+#pragma unroll
+            for (int j = 0; j < 8; ++j) {
+                cnt[j] = (int)sm.hist[8 * tid + j];
+                sum += cnt[j];
+            }
+            int total;
+            int run = block_inclusive_sum(sum, total, sm) - sum;
+            if (total >= r) {
+#pragma unroll
+                for (int j = 0; j < 8; ++j) {
+                    if (run < r && r <= run + cnt[j]) sm.bcast[0] = 8 * tid + j;
+                    run += cnt[j];
+                }
+            }
+            __syncthreads();
+            if (total >= r || sb >= 21) {
+                const int64_t b = total >= r ? sm.bcast[0] : kBins - 1;
+                const int64_t lo = (int64_t)top - ((b + 1) << sb) + 1;   // lowest key of bin b
+                theta0 = lo < 1 ? 1u : (uint32_t)lo;
+                __syncthreads();
+                break;
+            }
+            __syncthreads();
+            sb = 21;
+        }
+    }
 
     // ---- one streaming pass: compact the keys >= theta0 into LDS, in index order
     const int64_t nchunk = (n + kChunk - 1) / kChunk;
     int count = 0;
+    uint32_t cmax = 0;
     uint32_t nxt[kPer];
     load16(kPer * tid, nxt);
 #pragma unroll 1
@@ -250,7 +346,11 @@ __global__ __launch_bounds__(kTkThreads) void row_topk_kernel(TopkArgs a) {
         if (c + 1 < nchunk) load16((c + 1) * kChunk + kPer * tid, nxt);
         int f = 0;
 #pragma unroll
-        for (int i = 0; i < kPer; ++i) f += (key[i] != 0u && key[i] >= theta0) ? 1 : 0;
+        for (int i = 0; i < kPer; ++i) {
+            const bool in = key[i] != 0u && key[i] >= theta0;
+            f += in ? 1 : 0;
+            cmax = in && key[i] > cmax ? key[i] : cmax;
+        }
         int total;
         int pos = count + block_inclusive_sum(f, total, sm) - f;
         if (count + total <= kCand) {
@@ -277,7 +377,9 @@ __global__ __launch_bounds__(kTkThreads) void row_topk_kernel(TopkArgs a) {
             key[i] = ci < count ? sm.cand_key[ci] : 0u;
             kidx[i] = ci < count ? sm.cand_idx[ci] : 0;
         }
-        const uint32_t theta = select_regs(key, need, sm);
+        const uint32_t range = block_max(cmax, sm) - theta0;   // relative keys <= range
+        const int nbits = range ? 32 - __builtin_clz(range) : 1;
+        const uint32_t theta = select_rel(key, theta0, nbits, need, sm);
         int eq_base = 0;
         emit_ordered(key, kidx, theta, need, 0, eq_base, oi, os, sm);
         return;

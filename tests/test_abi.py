@@ -40,17 +40,17 @@ def test_version(dsa):
 
 def test_workspace_sizes(dsa):
     assert dsa.workspace_size(dsa.OP_PROJECT, 100) == 0
-    # prefill: 256-byte header of sequence bases, a dummy row of 64*ceil(max/64) floats, and the
-    # triangular score rows (row t holds 64*(t//64 + 1) floats)
+    # prefill: 256-byte header of sequence bases, a dummy row of 128*ceil(max/128) floats, and
+    # the triangular score rows (row t holds 128*(t//128 + 1) floats)
     def tri(t):
-        q, r = divmod(t, 64)
-        return 2048 * q * (q + 1) + 64 * r * (q + 1)
-    assert tri(1000) == sum(64 * (t // 64 + 1) for t in range(1000))
+        q, r = divmod(t, 128)
+        return 8192 * q * (q + 1) + 128 * r * (q + 1)
+    assert tri(1000) == sum(128 * (t // 128 + 1) for t in range(1000))
     r256 = lambda b: (b + 255) // 256 * 256
     assert dsa.workspace_size(dsa.OP_SCORE_TOPK, 1000, topk=2048) == 256 + r256(4 * 1024) + 4 * tri(1000)
-    # ragged: bound from sequences of max length (here 2 of length 8 -> (8+64)^2/2 floats each)
-    vb = ((2 * 72 * 72 // 2 + 63) // 64) * 64
-    assert dsa.workspace_size(dsa.OP_SCORE_TOPK_VARLEN, 16, 2, 8, topk=5) == 256 + 256 + 4 * vb
+    # ragged: bound from sequences of max length (here 2 of length 8 -> (8+128)^2/2 floats each)
+    vb = ((2 * 136 * 136 // 2 + 127) // 128) * 128
+    assert dsa.workspace_size(dsa.OP_SCORE_TOPK_VARLEN, 16, 2, 8, topk=5) == 256 + 512 + 4 * vb
     assert dsa.workspace_size(dsa.OP_DECODE, 0, 64, 131072, 2048) == 64 * 131072 * 4
     with pytest.raises(dsa.DsaIdxError) as e:
         dsa.workspace_size(dsa.OP_SCORE_TOPK, 10, topk=0)
