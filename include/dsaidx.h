@@ -123,7 +123,8 @@ int dsa_idx_project(const dsa_idx_weights *weights, const dsa_idx_bf16 *x, int64
  *   q [T][32][128], k [T][128], w [T][32]   bf16, 16-byte aligned
  *   idx    [T][topk] int32  selected key positions s <= t, ascending, -1 padded
  *   scores [T][topk] fp32   I[t, idx] (may be NULL), -inf padded
- * The T x T score matrix is never stored; the workspace holds per-row candidates. */
+ * Runs dsa_idx_prefill_scores then dsa_idx_prefill_select (below) on the same workspace, which
+ * holds the causal fp32 scores of every row (about 2 T^2 bytes). */
 int dsa_idx_score_topk(const dsa_idx_bf16 *q, const dsa_idx_bf16 *k, const dsa_idx_bf16 *w,
                        int64_t T, int topk, int32_t *idx, float *scores, void *ws,
                        size_t ws_bytes, void *stream);
@@ -137,6 +138,27 @@ int dsa_idx_score_topk_varlen(const dsa_idx_bf16 *q, const dsa_idx_bf16 *k,
                               const dsa_idx_bf16 *w, const int32_t *cu_seqlens, int B,
                               int max_seqlen, int64_t total, int topk, int32_t *idx,
                               float *scores, void *ws, size_t ws_bytes, void *stream);
+
+/* The two halves of dsa_idx_score_topk (cu_seqlens == NULL: one sequence of `total` tokens,
+ * B and max_seqlen ignored) and of dsa_idx_score_topk_varlen (cu_seqlens given), for callers
+ * that want the causal scores themselves or time the halves separately.  Both take the
+ * workspace of the matching dsa_idx_workspace_size op.
+ *
+ * dsa_idx_prefill_scores writes the scores I[t, s], s <= t, into ws: a header of
+ * H = 256 * ceil(8 (B' + 1) / 256) bytes (B' = 1 without cu_seqlens, else B) whose first
+ * B' + 1 int64 are the sequences' float offsets into the row area; a scratch row of
+ * 4 * 128 * ceil(max_len / 128) bytes (rounded up to 256; max_len = total or max_seqlen);
+ * then the row area: row t of sequence i starts at float offset
+ *     base[i] + 8192 q (q + 1) + 128 r (q + 1),   q = t / 128, r = t % 128,
+ * and holds 128 (q + 1) floats, of which the first t + 1 are the scores (the rest are
+ * unspecified).
+ * dsa_idx_prefill_select reads those rows and writes idx and scores as dsa_idx_score_topk. */
+int dsa_idx_prefill_scores(const dsa_idx_bf16 *q, const dsa_idx_bf16 *k, const dsa_idx_bf16 *w,
+                           const int32_t *cu_seqlens, int B, int max_seqlen, int64_t total,
+                           void *ws, size_t ws_bytes, void *stream);
+int dsa_idx_prefill_select(const int32_t *cu_seqlens, int B, int max_seqlen, int64_t total,
+                           int topk, int32_t *idx, float *scores, void *ws, size_t ws_bytes,
+                           void *stream);
 
 /* Decode: one new query per sequence against that sequence's cached keys.
  *   q [B][32][128], w [B][32]      the new tokens' projections (from dsa_idx_project)

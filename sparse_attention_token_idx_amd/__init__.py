@@ -14,6 +14,7 @@ import os
 import torch
 
 __all__ = ["version", "workspace_size", "project", "score_topk", "score_topk_varlen", "decode",
+           "prefill_scores", "prefill_select", "score_row",
            "HEADS", "DIM", "QLAT", "QOUT", "HIDDEN", "MAX_TOPK", "OP_PROJECT", "OP_SCORE_TOPK",
            "OP_SCORE_TOPK_VARLEN", "OP_DECODE", "DsaIdxError", "lib"]
 
@@ -62,6 +63,10 @@ def lib():
         L.dsa_idx_score_topk_varlen.restype = i32
         L.dsa_idx_score_topk_varlen.argtypes = [vp, vp, vp, vp, i32, i32, i64, i32, vp, vp, vp,
                                                 sz, vp]
+        L.dsa_idx_prefill_scores.restype = i32
+        L.dsa_idx_prefill_scores.argtypes = [vp, vp, vp, vp, i32, i32, i64, vp, sz, vp]
+        L.dsa_idx_prefill_select.restype = i32
+        L.dsa_idx_prefill_select.argtypes = [vp, i32, i32, i64, i32, vp, vp, vp, sz, vp]
         L.dsa_idx_decode.restype = i32
         L.dsa_idx_decode.argtypes = [vp, vp, vp, vp, vp, i32, i32, i32, vp, vp, vp, sz, vp]
         _lib = L
@@ -199,6 +204,48 @@ def score_topk_varlen(q, k, w, cu_seqlens, max_seqlen, topk=MAX_TOPK, with_score
                                            int(max_seqlen), total, topk, _ptr(idx), _ptr(sc),
                                            _ptr(ws), nbytes, _stream(stream)))
     return idx, sc
+
+
+def prefill_scores(q, k, w, ws, cu_seqlens=None, max_seqlen=0, stream=None):
+    """First half of score_topk / score_topk_varlen: causal fp32 scores into the workspace
+    `ws` (a uint8 tensor of workspace_size(...) bytes; see score_row for the layout)."""
+    total = q.shape[0]
+    _need(q, "q", torch.bfloat16, (total, HEADS, DIM))
+    _need(k, "k", torch.bfloat16, (total, DIM))
+    _need(w, "w", torch.bfloat16, (total, HEADS))
+    B = 1 if cu_seqlens is None else cu_seqlens.numel() - 1
+    nb = ws.numel() * ws.element_size()
+    _check("dsa_idx_prefill_scores",
+           lib().dsa_idx_prefill_scores(_ptr(q), _ptr(k), _ptr(w), _ptr(cu_seqlens), B,
+                                        int(max_seqlen), total, _ptr(ws), nb, _stream(stream)))
+
+
+def prefill_select(total, ws, topk=MAX_TOPK, with_scores=True, cu_seqlens=None, max_seqlen=0,
+                   out=None, stream=None):
+    """Second half: the top-k of the score rows that prefill_scores left in `ws`."""
+    B = 1 if cu_seqlens is None else cu_seqlens.numel() - 1
+    if out is None:
+        idx = torch.empty((total, topk), dtype=torch.int32, device=ws.device)
+        sc = torch.empty((total, topk), dtype=torch.float32, device=ws.device) if with_scores else None
+    else:
+        idx, sc = out
+    nb = ws.numel() * ws.element_size()
+    _check("dsa_idx_prefill_select",
+           lib().dsa_idx_prefill_select(_ptr(cu_seqlens), B, int(max_seqlen), total, topk,
+                                        _ptr(idx), _ptr(sc), _ptr(ws), nb, _stream(stream)))
+    return idx, sc
+
+
+def score_row(ws, t, max_len, B=1, seq_base=0):
+    """View of the t+1 causal scores of row t (of a sequence whose rows start at float offset
+    seq_base of the row area) inside a prefill workspace; max_len is the T or max_seqlen of the
+    call, B its sequence count (1 for the dense call)."""
+    hdr = (8 * (B + 1) + 255) // 256 * 256
+    dummy = (4 * ((max_len + 127) // 128) * 128 + 255) // 256 * 256
+    q, r = divmod(t, 128)
+    off = seq_base + 8192 * q * (q + 1) + 128 * r * (q + 1)
+    rows = ws[hdr + dummy:].view(torch.float32)
+    return rows[off:off + t + 1]
 
 
 def decode(q, w, k_cache, start, seqlens, max_seqlen, topk=MAX_TOPK, with_scores=True, ws=None,

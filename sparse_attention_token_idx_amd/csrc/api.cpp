@@ -169,18 +169,90 @@ int dsa_idx_project(const dsa_idx_weights *wt, const dsa_idx_bf16 *x, int64_t ld
     return ok();
 }
 
-static int score_common(const dsa_idx_bf16 *q, const dsa_idx_bf16 *k, const dsa_idx_bf16 *w,
-                        int32_t *idx, int topk, int64_t total, size_t need, void *ws,
-                        size_t ws_bytes) {
-    int r = check_topk(topk);
-    if (r) return r;
-    if (total == 0) return ok();
-    if (!q || !k || !w || !idx) return fail(DSA_IDX_EINVAL, "a tensor pointer is NULL");
-    if (!aligned16(q) || !aligned16(k) || !aligned16(w))
-        return fail(DSA_IDX_EINVAL, "q, k and w must be 16-byte aligned");
+
+// Workspace parts of a prefill call.  cu == nullptr: one sequence of `total` tokens.
+struct PrefillWs {
+    int64_t *base;
+    float *dummy;
+    float *rows;
+};
+
+static int64_t prefill_max_len(const int32_t *cu, int max_seqlen, int64_t total) {
+    return cu ? (int64_t)max_seqlen : total;
+}
+
+static int prefill_check(const int32_t *cu, int B, int max_seqlen, int64_t total, void *ws,
+                         size_t ws_bytes, size_t &need) {
+    if (total < 0) return fail(DSA_IDX_EINVAL, "total=%lld < 0", (long long)total);
+    if (cu) {
+        if (B < 0 || max_seqlen < 0)
+            return fail(DSA_IDX_EINVAL, "B=%d max_seqlen=%d must be >= 0", B, max_seqlen);
+        if (B > 65535) return fail(DSA_IDX_EUNSUPPORTED, "B=%d above 65535", B);
+        if (max_seqlen > kMaxSeq)
+            return fail(DSA_IDX_EUNSUPPORTED, "max_seqlen=%d above %lld", max_seqlen, (long long)kMaxSeq);
+        if (total > (int64_t)B * max_seqlen)
+            return fail(DSA_IDX_EINVAL, "total=%lld above B * max_seqlen", (long long)total);
+        need = ws_score_topk_varlen(total, B, max_seqlen);
+    } else {
+        if (total > kMaxSeq) return fail(DSA_IDX_EUNSUPPORTED, "T=%lld above %lld", (long long)total, (long long)kMaxSeq);
+        need = ws_score_topk(total);
+    }
+    if (total == 0 || (cu && (B == 0 || max_seqlen == 0))) return ok();
     if (!ws || ws_bytes < need)
         return fail(DSA_IDX_EWORKSPACE, "workspace %zu bytes < %zu needed", ws ? ws_bytes : (size_t)0, need);
     if (!aligned16(ws)) return fail(DSA_IDX_EINVAL, "workspace must be 16-byte aligned");
+    return ok();
+}
+
+static PrefillWs prefill_ws(const int32_t *cu, int B, int max_seqlen, int64_t total, void *ws) {
+    const int Bh = cu ? B : 1;
+    char *p = static_cast<char *>(ws);
+    PrefillWs r;
+    r.base = reinterpret_cast<int64_t *>(p);
+    r.dummy = reinterpret_cast<float *>(p + ws_hdr(Bh));
+    r.rows = reinterpret_cast<float *>(p + ws_hdr(Bh) + ws_dummy(prefill_max_len(cu, max_seqlen, total)));
+    return r;
+}
+
+static bool prefill_empty(const int32_t *cu, int B, int max_seqlen, int64_t total) {
+    return total == 0 || (cu && (B == 0 || max_seqlen == 0));
+}
+
+int dsa_idx_prefill_scores(const dsa_idx_bf16 *q, const dsa_idx_bf16 *k, const dsa_idx_bf16 *w,
+                           const int32_t *cu_seqlens, int B, int max_seqlen, int64_t total,
+                           void *ws, size_t ws_bytes, void *stream) {
+    size_t need = 0;
+    int r = prefill_check(cu_seqlens, B, max_seqlen, total, ws, ws_bytes, need);
+    if (r || prefill_empty(cu_seqlens, B, max_seqlen, total)) return r;
+    if (!q || !k || !w) return fail(DSA_IDX_EINVAL, "a tensor pointer is NULL");
+    if (!aligned16(q) || !aligned16(k) || !aligned16(w))
+        return fail(DSA_IDX_EINVAL, "q, k and w must be 16-byte aligned");
+    r = check_device();
+    if (r) return r;
+    const PrefillWs p = prefill_ws(cu_seqlens, B, max_seqlen, total, ws);
+    hipError_t e = dsaidx::launch_scores(q, k, w, cu_seqlens, cu_seqlens ? B : 1,
+                                         prefill_max_len(cu_seqlens, max_seqlen, total), total, p.base,
+                                         p.rows, p.dummy, reinterpret_cast<hipStream_t>(stream));
+    if (e != hipSuccess) return hip_fail("scores launch", e);
+    return ok();
+}
+
+int dsa_idx_prefill_select(const int32_t *cu_seqlens, int B, int max_seqlen, int64_t total,
+                           int topk, int32_t *idx, float *scores, void *ws, size_t ws_bytes,
+                           void *stream) {
+    int r = check_topk(topk);
+    if (r) return r;
+    size_t need = 0;
+    r = prefill_check(cu_seqlens, B, max_seqlen, total, ws, ws_bytes, need);
+    if (r || prefill_empty(cu_seqlens, B, max_seqlen, total)) return r;
+    if (!idx) return fail(DSA_IDX_EINVAL, "idx is NULL");
+    r = check_device();
+    if (r) return r;
+    const PrefillWs p = prefill_ws(cu_seqlens, B, max_seqlen, total, ws);
+    hipError_t e = dsaidx::launch_row_topk_prefill(p.rows, cu_seqlens, p.base, cu_seqlens ? B : 1, total,
+                                                   total, topk, idx, scores,
+                                                   reinterpret_cast<hipStream_t>(stream));
+    if (e != hipSuccess) return hip_fail("row top-k launch", e);
     return ok();
 }
 
@@ -188,21 +260,15 @@ int dsa_idx_score_topk(const dsa_idx_bf16 *q, const dsa_idx_bf16 *k, const dsa_i
                        int64_t T, int topk, int32_t *idx, float *scores, void *ws,
                        size_t ws_bytes, void *stream) {
     if (T < 0) return fail(DSA_IDX_EINVAL, "T=%lld < 0", (long long)T);
-    if (T > kMaxSeq) return fail(DSA_IDX_EUNSUPPORTED, "T=%lld above %lld", (long long)T, (long long)kMaxSeq);
-    int r = score_common(q, k, w, idx, topk, T, ws_score_topk(T), ws, ws_bytes);
-    if (r || T == 0) return r;
-    r = check_device();
+    int r = check_topk(topk);
     if (r) return r;
-    char *p = static_cast<char *>(ws);
-    int64_t *base = reinterpret_cast<int64_t *>(p);
-    float *dummy = reinterpret_cast<float *>(p + ws_hdr(1));
-    float *rows = reinterpret_cast<float *>(p + ws_hdr(1) + ws_dummy(T));
-    const hipStream_t st = reinterpret_cast<hipStream_t>(stream);
-    hipError_t e = dsaidx::launch_scores(q, k, w, nullptr, 1, T, T, base, rows, dummy, st);
-    if (e != hipSuccess) return hip_fail("scores launch", e);
-    e = dsaidx::launch_row_topk_prefill(rows, nullptr, base, 1, T, T, topk, idx, scores, st);
-    if (e != hipSuccess) return hip_fail("row top-k launch", e);
-    return ok();
+    if (T > 0 && (!q || !k || !w || !idx)) return fail(DSA_IDX_EINVAL, "a tensor pointer is NULL");
+    size_t need = 0;
+    r = prefill_check(nullptr, 1, 0, T, ws, ws_bytes, need);
+    if (r || T == 0) return r;
+    r = dsa_idx_prefill_scores(q, k, w, nullptr, 1, 0, T, ws, ws_bytes, stream);
+    if (r) return r;
+    return dsa_idx_prefill_select(nullptr, 1, 0, T, topk, idx, scores, ws, ws_bytes, stream);
 }
 
 int dsa_idx_score_topk_varlen(const dsa_idx_bf16 *q, const dsa_idx_bf16 *k,
@@ -212,24 +278,17 @@ int dsa_idx_score_topk_varlen(const dsa_idx_bf16 *q, const dsa_idx_bf16 *k,
     if (B < 0 || max_seqlen < 0 || total < 0)
         return fail(DSA_IDX_EINVAL, "B=%d max_seqlen=%d total=%lld must be >= 0", B, max_seqlen, (long long)total);
     if (B > 0 && !cu_seqlens) return fail(DSA_IDX_EINVAL, "cu_seqlens is NULL");
-    if (B > 65535) return fail(DSA_IDX_EUNSUPPORTED, "B=%d above 65535", B);
-    if (max_seqlen > kMaxSeq) return fail(DSA_IDX_EUNSUPPORTED, "max_seqlen=%d above %lld", max_seqlen, (long long)kMaxSeq);
-    if (total > (int64_t)B * max_seqlen)
-        return fail(DSA_IDX_EINVAL, "total=%lld above B * max_seqlen", (long long)total);
-    int r = score_common(q, k, w, idx, topk, total, ws_score_topk_varlen(total, B, max_seqlen), ws, ws_bytes);
-    if (r || total == 0 || B == 0 || max_seqlen == 0) return r;
-    r = check_device();
+    int r = check_topk(topk);
     if (r) return r;
-    char *p = static_cast<char *>(ws);
-    int64_t *base = reinterpret_cast<int64_t *>(p);
-    float *dummy = reinterpret_cast<float *>(p + ws_hdr(B));
-    float *rows = reinterpret_cast<float *>(p + ws_hdr(B) + ws_dummy(max_seqlen));
-    const hipStream_t st = reinterpret_cast<hipStream_t>(stream);
-    hipError_t e = dsaidx::launch_scores(q, k, w, cu_seqlens, B, max_seqlen, total, base, rows, dummy, st);
-    if (e != hipSuccess) return hip_fail("scores launch", e);
-    e = dsaidx::launch_row_topk_prefill(rows, cu_seqlens, base, B, total, total, topk, idx, scores, st);
-    if (e != hipSuccess) return hip_fail("row top-k launch", e);
-    return ok();
+    if (total > 0 && (!q || !k || !w || !idx)) return fail(DSA_IDX_EINVAL, "a tensor pointer is NULL");
+    if (B == 0) return total == 0 ? ok() : fail(DSA_IDX_EINVAL, "total=%lld with B=0", (long long)total);
+    size_t need = 0;
+    r = prefill_check(cu_seqlens, B, max_seqlen, total, ws, ws_bytes, need);
+    if (r || prefill_empty(cu_seqlens, B, max_seqlen, total)) return r;
+    r = dsa_idx_prefill_scores(q, k, w, cu_seqlens, B, max_seqlen, total, ws, ws_bytes, stream);
+    if (r) return r;
+    return dsa_idx_prefill_select(cu_seqlens, B, max_seqlen, total, topk, idx, scores, ws, ws_bytes,
+                                  stream);
 }
 
 int dsa_idx_decode(const dsa_idx_bf16 *q, const dsa_idx_bf16 *w, const dsa_idx_bf16 *k_cache,

@@ -29,7 +29,7 @@ def test_exports_every_declared_symbol(dsa):
     names = declared_functions()
     assert set(names) == {"dsa_idx_version", "dsa_idx_last_error", "dsa_idx_workspace_size",
                           "dsa_idx_project", "dsa_idx_score_topk", "dsa_idx_score_topk_varlen",
-                          "dsa_idx_decode"}
+                          "dsa_idx_prefill_scores", "dsa_idx_prefill_select", "dsa_idx_decode"}
     for n in names:
         assert getattr(L, n) is not None
 
@@ -84,6 +84,15 @@ def test_rejections_before_device(dsa):
                                        _vp(A), 1 << 30, None) == -1
     assert L.dsa_idx_score_topk_varlen(_vp(A), _vp(A), _vp(A), _vp(A), -1, 8, 10, 8, _vp(A), None,
                                        _vp(A), 1 << 30, None) == -1
+    # the two prefill halves
+    assert L.dsa_idx_prefill_scores(_vp(A), _vp(A), _vp(A), None, 1, 0, 10, _vp(A), 10, None) == -3
+    assert L.dsa_idx_prefill_scores(None, _vp(A), _vp(A), None, 1, 0, 10, _vp(A), 1 << 30, None) == -1
+    assert L.dsa_idx_prefill_scores(_vp(A), _vp(A), _vp(A), None, 1, 0, -5, _vp(A), 1 << 30, None) == -1
+    assert L.dsa_idx_prefill_select(None, 1, 0, 10, 0, _vp(A), None, _vp(A), 1 << 30, None) == -2
+    assert L.dsa_idx_prefill_select(None, 1, 0, 10, 8, None, None, _vp(A), 1 << 30, None) == -1
+    assert L.dsa_idx_prefill_select(_vp(A), 2, 4, 10, 8, _vp(A), None, _vp(A), 1 << 30, None) == -1
+    assert b"B * max_seqlen" in L.dsa_idx_last_error()
+    assert L.dsa_idx_prefill_select(None, 1, 0, 0, 8, None, None, None, 0, None) == 0
     # decode
     assert L.dsa_idx_decode(_vp(A), _vp(A), _vp(A), _vp(A), _vp(A), 4, 100, 0, _vp(A), None, _vp(A),
                             1 << 30, None) == -2

@@ -216,3 +216,26 @@ def test_negative_weights(dsa):
     ref = oracle.prefill_rows(s["q"], s["k"], w, rows, topk=2048, full=True)
     for r, t in enumerate(rows):
         check_row(t, gi[t], gs[t], ref, r, 2048)
+
+
+def test_prefill_halves_and_score_rows(dsa):
+    """The two C-ABI halves give score_topk's result, and the workspace rows hold the causal
+    scores of the oracle (fp32 tolerance of check_row) for every key s <= t."""
+    T = 2300
+    s = wl.score_inputs(T, seed=17)
+    q, k, w = to_dev(s["q"]), to_dev(s["k"]), to_dev(s["w"])
+    ws = torch.empty(dsa.workspace_size(dsa.OP_SCORE_TOPK, T, topk=2048), dtype=torch.uint8,
+                     device="cuda")
+    dsa.prefill_scores(q, k, w, ws)
+    idx, sc = dsa.prefill_select(T, ws, topk=2048)
+    torch.cuda.synchronize()
+    gi, gs = _run(dsa, s["q"], s["k"], s["w"], 2048)
+    assert np.array_equal(idx.cpu().numpy(), gi) and np.array_equal(sc.cpu().numpy(), gs)
+    rows = [0, 1, 127, 128, 129, 1000, 2047, 2048, 2299]
+    ref = oracle.prefill_rows(s["q"], s["k"], s["w"], rows, topk=2048, full=True)
+    for r, t in enumerate(rows):
+        row = dsa.score_row(ws, t, T).cpu().numpy().astype(np.float64)
+        I = ref["full"][r]
+        assert row.shape == I.shape
+        tol = 1e-3 * ref["maxabs"][r] + 1e-5
+        assert np.abs(row - I).max() <= tol, (t, np.abs(row - I).max(), tol)
