@@ -4,11 +4,12 @@
 Default workload (the headline): one full indexer layer over one causal sequence of
 T = 65,536 tokens -- q/k/w projections from x [T,7168] and c_q [T,1536], then causal scores
 I = sum_h w_h ReLU(q_h . k) over the whole prefix and the top 2,048 keys per query.  One
-step = dsa_idx_project + dsa_idx_score_topk on resident inputs.  `value` is queries/s.
+step = dsa_idx_project + dsa_idx_score_topk (run as its two halves, dsa_idx_prefill_scores
+and dsa_idx_prefill_select) on resident inputs.  `value` is queries/s.
 
 Also reported on the same line:
-  * roofline of the dominant kernel (the fused score + top-k kernel) against the bf16 MFMA
-    peak, its average duration measured with HIP events on the stream it runs on;
+  * roofline of the dominant kernel (score_rows_kernel, the causal scores) against the bf16
+    MFMA peak, its average duration measured with HIP events on the stream it runs on;
   * the decode leg: 64 sequences with cached bf16 keys of U[32768, 131072] tokens, one
     new query each (project + decode), as HBM GB/s of the decode kernels;
   * cpu_baseline: the fp64 CPU oracle on a bounded sample of the same workload, with the
@@ -33,7 +34,7 @@ PEAK_BF16_TFLOPS = 2516.6     # MI355X dense bf16 MFMA (published)
 # HBM bytes per launch of the scoring kernel at T=65536, from rocprofv3 FETCH_SIZE and
 # WRITE_SIZE scaled by a 1 GiB device-copy calibration; reported only while the kernel
 # source is the one the counters were taken on (None: not measured for this source)
-TRAFFIC_SCORE_T65536 = {"source_sha256_prefix": None, "bytes": None}
+TRAFFIC_SCORE_T65536 = {"source_sha256_prefix": "ac6e30b80565b5da", "bytes": 10879542492}
 PEAK_HBM_GBPS = 8000.0        # MI355X HBM3E (published)
 H, D, QLAT, HIDDEN = 32, 128, 1536, 7168
 PROJ_FLOP_PER_TOKEN = 2 * (QLAT * 4096 + HIDDEN * D + HIDDEN * H)   # 14,876,672

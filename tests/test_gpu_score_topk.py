@@ -1,4 +1,4 @@
-"""GPU parity of the fused causal score + top-k kernel against the CPU oracle."""
+"""GPU parity of the prefill path (causal scores, then the row top-k) against the CPU oracle."""
 import numpy as np
 import pytest
 import torch
@@ -239,3 +239,80 @@ def test_prefill_halves_and_score_rows(dsa):
         assert row.shape == I.shape
         tol = 1e-3 * ref["maxabs"][r] + 1e-5
         assert np.abs(row - I).max() <= tol, (t, np.abs(row - I).max(), tol)
+
+
+# ------------------------------------------------- long rows: every branch of the row top-k
+def test_long_rows_small_and_full_topk(dsa):
+    # rows longer than 4,096 scores take the sampled-threshold path; small topk makes the
+    # threshold sit far out in the tail of the sample
+    T = 9000
+    s = wl.score_inputs(T, seed=31)
+    rows = [4095, 4096, 4097, 6000, 8191, 8999]
+    for topk in (16, 100, 2048):
+        gi, gs = _run(dsa, s["q"], s["k"], s["w"], topk)
+        ref = oracle.prefill_rows(s["q"], s["k"], s["w"], rows, topk=topk, full=True)
+        for r, t in enumerate(rows):
+            check_row(t, gi[t], gs[t], ref, r, topk)
+
+
+def test_long_rows_negative_weights(dsa):
+    # all-negative scores: their order keys are spread over many binades near zero, which
+    # widens the threshold window
+    T = 7000
+    s = wl.score_inputs(T, seed=32)
+    w = oracle.f64_to_bf16(-np.abs(oracle.bf16_to_f64(s["w"])))
+    gi, gs = _run(dsa, s["q"], s["k"], w, 2048)
+    rows = [4500, 6999]
+    ref = oracle.prefill_rows(s["q"], s["k"], w, rows, topk=2048, full=True)
+    for r, t in enumerate(rows):
+        check_row(t, gi[t], gs[t], ref, r, 2048)
+
+
+def _key_scores(vals):
+    """Inputs whose scores are I[t, s] = vals[s] (bf16 codes) exactly, for every row t."""
+    T = len(vals)
+    q = np.zeros((T, H, D), np.uint16)
+    q[:, 0, 0] = 0x3F80
+    k = np.zeros((T, D), np.uint16)
+    k[:, 0] = vals
+    w = np.zeros((T, H), np.uint16)
+    w[:, 0] = 0x3F80
+    return q, k, w
+
+
+def test_long_rows_skewed_sample(dsa):
+    # Row 8191 (8,192 scores): the 64 blocks of 64 scores that a spread sample of that row
+    # reads get 4,096 distinct large values, every other score is 1.0.  A threshold placed
+    # from such a sample admits fewer than topk keys, so the exact whole-row select must
+    # take over; other rows see ordinary and many-tie rows.  The expected result holds
+    # whatever the sample.
+    T = 8192
+    n = T
+    vals = np.full(T, 0x3F80, np.uint16)
+    pos = np.concatenate([((b * (n - 64)) // 63 & ~3) + np.arange(64) for b in range(64)])
+    assert len(np.unique(pos)) == 4096 and pos.max() < n
+    vals[np.sort(pos)] = 0x4000 + np.arange(4096)            # 2.0 upwards, strictly increasing
+    q, k, w = _key_scores(vals)
+    for topk in (2048, 300):
+        gi, gs = _run(dsa, q, k, w, topk)
+        rows = [4200, 6000, 8191]
+        ref = oracle.prefill_rows(q, k, w, rows, topk=topk, full=True)
+        for r, t in enumerate(rows):
+            check_row(t, gi[t], gs[t], ref, r, topk, exact=True)
+        # row 8191 keeps the topk largest spikes, which are the last topk sampled positions
+        assert gi[8191][:topk].tolist() == np.sort(pos)[-topk:].tolist()
+
+
+def test_long_rows_many_ties(dsa):
+    # 6,000 keys in 3 value levels: the threshold bin holds thousands of equal keys and the
+    # lowest-index ones among them must be kept
+    T = 6000
+    rng = np.random.default_rng(5)
+    vals = np.array([0x3F80, 0x4000, 0x4040], np.uint16)[rng.integers(0, 3, T)]
+    q, k, w = _key_scores(vals)
+    for topk in (2048, 5):
+        gi, gs = _run(dsa, q, k, w, topk)
+        rows = [4096, 5000, 5999]
+        ref = oracle.prefill_rows(q, k, w, rows, topk=topk, full=True)
+        for r, t in enumerate(rows):
+            check_row(t, gi[t], gs[t], ref, r, topk, exact=True)
