@@ -4,23 +4,29 @@
 // tokens).  Rows come from the prefill score workspace (triangular rows of scores.hip) or
 // from the decode score buffer (one row per sequence).
 //
-// One workgroup of 4 waves per row, several workgroups per CU so that one row's selection
-// overlaps other rows' loads.  Thread t handles 16 consecutive scores of each 4,096-score
-// chunk (four 16-byte loads), so index order is thread order.
-//   * Rows of at most 4,096 scores are held in registers and selected exactly.
+// One workgroup of 4 waves per row, four workgroups per CU, so that one row's selection
+// overlaps other rows' loads.  Scores become order-preserving uint32 keys (0 = no score).
+//   * Rows of at most 4,096 scores are held in registers (16 consecutive per thread) and
+//     selected exactly.
 //   * Longer rows: a threshold theta0 is placed from a sample of 4,096 scores (64 blocks of
 //     64 consecutive scores spread over the row) so that about 1.4 topk keys of the row are
-//     expected to reach it: one histogram pass over fine bins counted down from the sample's
-//     largest key (2^13 key units per bin, which keeps the LDS atomics spread out) finds
-//     the bin that holds the r-th largest sample key, and theta0 is that bin's lower edge.
-//     One streaming pass compacts the keys >= theta0 into LDS in index order; when there are
-//     between topk and 4,096 of them (the normal case) the exact select runs over those
-//     candidates only, on their keys relative to theta0, with only as many 11-bit digit
-//     passes as the candidates' key range needs.  Otherwise an exact select streams the
-//     whole row (three digit passes) and a last pass writes the result.
-// The exact select is a most-significant-digit radix select over the orderable key (11 + 11
-// + 10 bits, an LDS histogram per digit): theta = the topk-th largest key, and how many keys
-// equal to theta are kept (the lowest-index ones).
+//     expected to reach it (a histogram of the sample in 1,024 bins over its own key range
+//     finds the bin that holds the r-th largest sample key; theta0 is that bin's lower
+//     edge).  Then one streaming pass in which every wave works alone: wave w takes
+//     the 1,024-key chunks w, w + 4, ... (16 consecutive keys per lane), keeps the keys >=
+//     theta0, reserves room for them in an LDS candidate list with one LDS atomic and writes
+//     them there in index order, recording where each chunk's run starts, and counts them in
+//     a histogram of 1,024 bins above theta0 (sized from the sample's range).  No workgroup
+//     barrier is crossed while the row streams, and each wave keeps two chunks of loads in
+//     flight.  When between topk and 4,096 keys reach theta0 (the normal case), one scan of
+//     that histogram finds the bin that holds the topk-th largest key; the few keys of that
+//     bin are ranked against each other exactly (key, then lower index first), and every
+//     candidate above the bin or ranked in wins.  The winners are placed in index order from
+//     counts per chunk run and written from LDS with 16-byte stores.  A crowded bin is first
+//     narrowed by an exact radix select; rows where the threshold misses (too few, too many
+//     candidates) take an exact select that streams the whole row.
+// The exact select is a most-significant-digit radix select: theta = the topk-th largest
+// key, and how many keys equal to theta are kept (the lowest-index ones).
 #include "common.hpp"
 #include "launch.hpp"
 
@@ -29,19 +35,50 @@ namespace {
 
 constexpr int kTkWaves = 4;
 constexpr int kTkThreads = 64 * kTkWaves;
-constexpr int kPer = 16;                        // scores per thread per chunk
-constexpr int kChunk = kTkThreads * kPer;       // 4,096
-constexpr int kCand = 4096;                     // candidates kept in LDS
-constexpr int kBins = 2048;
+constexpr int kPer = 16;                        // keys per thread per chunk
+constexpr int kChunk = kTkThreads * kPer;       // 4,096: the register path, the full-row passes
+constexpr int kWChunk = 64 * kPer;              // 1,024: one wave's chunk in the streaming pass
+constexpr int kCand = 4096;                     // candidate list capacity
+constexpr int kBins = 1024;                     // 10-bit digits
+constexpr int kDigit = 10;
+constexpr int kBinsPer = kBins / kTkThreads;    // bins owned by a thread in a scan
+constexpr int kMaxRun = 512;                    // chunk runs: rows of up to 512K keys
+constexpr int kPrefetch = 2;                    // wave chunks in flight ahead of the current
+constexpr int kRankMax = 256;                   // keys of the threshold bin ranked directly
+
+static_assert(kBins % kTkThreads == 0 && kMaxRun == 2 * kTkThreads, "thread ownership");
 
 struct TopkSmem {
-    uint32_t cand_key[kCand];
-    int32_t cand_idx[kCand];
-    uint32_t hist[kBins];
+    union {
+        struct {
+            uint32_t key[kCand];
+            int32_t idx[kCand];
+        } cand;
+        struct {                                // emission: list prefix counts, staged output
+            uint32_t pre[kCand];
+            int32_t out_idx[kMaxTopk];
+            float out_score[kMaxTopk];
+        } emit;
+    } u;
+    union {
+        uint32_t hist[kBins];      // digit histograms; per run: winners in earlier chunks
+        struct {                   // the keys of the threshold bin: (key, index), list slot
+            uint32_t key[kRankMax];
+            int32_t idx[kRankMax];
+            uint16_t slot[kRankMax];
+        } bin;
+    };
+    uint32_t run[kMaxRun];         // start | count << 16 of each chunk's run in the list
+    uint32_t win[kCand / 32];      // ranked-in keys of the threshold bin, by list slot
+    uint32_t count;                // candidates reserved so far
+    uint32_t nbin;                 // keys gathered from the threshold bin
     int32_t wsum[kTkWaves];
     uint32_t wmax[kTkWaves];
-    int32_t bcast[2];
+    int32_t bcast[3];
 };
+
+static_assert(sizeof(TopkSmem) <= 40 * 1024, "four workgroups per CU");
+static_assert(kMaxRun <= kBins, "per-run emission data lives in hist");
 
 struct TopkArgs {
     const float *scores;
@@ -56,9 +93,11 @@ struct TopkArgs {
     float *out_score;              // may be nullptr
 };
 
+
 // Inclusive sum over the workgroup of one int per thread (the sum of all in `total`).
 __device__ int block_inclusive_sum(int v, int &total, TopkSmem &sm) {
-    const int lane = __lane_id(), wave = threadIdx.x >> 6;
+    const int tid = (int)threadIdx.x;
+    const int lane = tid & 63, wave = tid >> 6;
     const int incl = wave_inclusive_sum(v);
     if (lane == 63) sm.wsum[wave] = incl;
     __syncthreads();
@@ -74,64 +113,53 @@ __device__ int block_inclusive_sum(int v, int &total, TopkSmem &sm) {
     return before + incl;
 }
 
+// Exclusive prefix over the wave of one int per lane, and the wave's total.
+__device__ __forceinline__ int wave_exclusive_sum(int v, int &total) {
+    const int incl = row16_inclusive_sum(v);
+    const int r0 = __builtin_amdgcn_readlane(incl, 15), r1 = __builtin_amdgcn_readlane(incl, 31);
+    const int r2 = __builtin_amdgcn_readlane(incl, 47), r3 = __builtin_amdgcn_readlane(incl, 63);
+    const int g = ((int)threadIdx.x & 63) >> 4;
+    const int below = (g > 0 ? r0 : 0) + (g > 1 ? r1 : 0) + (g > 2 ? r2 : 0);
+    total = r0 + r1 + r2 + r3;
+    return below + incl - v;
+}
+
 // One digit of the radix select: given the histogram of the keys that match the digits
 // found so far, return the digit of the need-th largest and subtract from need the keys in
-// higher digits.  Thread t owns bins 8t .. 8t+7.
-__device__ uint32_t pick_digit(int &need, TopkSmem &sm) {
-    const int tid = threadIdx.x;
-    int cnt[8], sum = 0;
+// higher digits; in_bin = the keys in the returned digit's bin.  Thread t owns bins
+// kBinsPer t .. kBinsPer t + kBinsPer - 1.
+__device__ uint32_t pick_digit(int &need, TopkSmem &sm, int *in_bin = nullptr) {
+    const int tid = (int)threadIdx.x;
+    int cnt[kBinsPer], sum = 0;
 #pragma unroll
-    for (int j = 0; j < 8; ++j) {
-        cnt[j] = (int)sm.hist[8 * tid + j];
+    for (int j = 0; j < kBinsPer; ++j) {
+        cnt[j] = (int)sm.hist[kBinsPer * tid + j];
         sum += cnt[j];
     }
     int total;
     const int incl = block_inclusive_sum(sum, total, sm);
-    int above = total - incl;   // keys in bins above 8t+7
+    int above = total - incl;   // keys in bins above this thread's
 #pragma unroll
-    for (int j = 7; j >= 0; --j) {
+    for (int j = kBinsPer - 1; j >= 0; --j) {
         if (above < need && need <= above + cnt[j]) {
-            sm.bcast[0] = 8 * tid + j;
+            sm.bcast[0] = kBinsPer * tid + j;
             sm.bcast[1] = above;
+            sm.bcast[2] = cnt[j];
         }
         above += cnt[j];
     }
     __syncthreads();
     const uint32_t d = (uint32_t)sm.bcast[0];
     need -= sm.bcast[1];
+    if (in_bin) *in_bin = sm.bcast[2];
     __syncthreads();
     return d;
 }
 
-constexpr int kShift[3] = {21, 10, 0};
-constexpr int kWidth[3] = {11, 11, 10};
-
-// Exact select over keys held in registers (kPer per thread, 0 = no key): returns theta, the
-// need-th largest key; on return need = how many keys equal to theta are among the need
-// largest.
-__device__ uint32_t select_regs(const uint32_t (&key)[kPer], int &need, TopkSmem &sm) {
-    uint32_t prefix = 0, pmask = 0;
-#pragma unroll 1
-    for (int p = 0; p < 3; ++p) {
-        const int shift = kShift[p];
-        const uint32_t dmask = (1u << kWidth[p]) - 1u;
-        for (int i = threadIdx.x; i < kBins; i += kTkThreads) sm.hist[i] = 0u;
-        __syncthreads();
-#pragma unroll
-        for (int i = 0; i < kPer; ++i) {
-            const uint32_t kv = key[i];
-            if (kv != 0u && (kv & pmask) == prefix) atomicAdd(&sm.hist[(kv >> shift) & dmask], 1u);
-        }
-        __syncthreads();
-        prefix |= pick_digit(need, sm) << shift;
-        pmask |= dmask << shift;
-    }
-    return prefix;
-}
-
 // Largest of one key per thread over the workgroup.
 __device__ uint32_t block_max(uint32_t v, TopkSmem &sm) {
-    const int lane = __lane_id(), wave = threadIdx.x >> 6;
+    const int tid = (int)threadIdx.x;
+    const int lane = tid & 63, wave = tid >> 6;
 #pragma unroll
     for (int d = 32; d >= 1; d >>= 1) {
         const uint32_t o = (uint32_t)__shfl_xor((int)v, d, 64);
@@ -147,8 +175,8 @@ __device__ uint32_t block_max(uint32_t v, TopkSmem &sm) {
 }
 
 // Exact select over keys >= base held in registers (0 = no key), digits taken from the
-// relative key (key - base) < 2^nbits, 11 bits at a time from the top: returns theta, the
-// need-th largest key; on return need = how many keys equal to theta are among the need
+// relative key (key - base) < 2^nbits, kDigit bits at a time from the top: returns theta,
+// the need-th largest key; on return need = how many keys equal to theta are among the need
 // largest.
 __device__ uint32_t select_rel(const uint32_t (&key)[kPer], uint32_t base, int nbits, int &need,
                                TopkSmem &sm) {
@@ -156,10 +184,10 @@ __device__ uint32_t select_rel(const uint32_t (&key)[kPer], uint32_t base, int n
     int hi = nbits;
 #pragma unroll 1
     while (hi > 0) {
-        const int w = hi < 11 ? hi : 11;
+        const int w = hi < kDigit ? hi : kDigit;
         const int shift = hi - w;
         const uint32_t dmask = (1u << w) - 1u;
-        for (int i = threadIdx.x; i < kBins; i += kTkThreads) sm.hist[i] = 0u;
+        for (int i = (int)threadIdx.x; i < kBins; i += kTkThreads) sm.hist[i] = 0u;
         __syncthreads();
 #pragma unroll
         for (int i = 0; i < kPer; ++i) {
@@ -174,11 +202,14 @@ __device__ uint32_t select_rel(const uint32_t (&key)[kPer], uint32_t base, int n
     return base + prefix;
 }
 
+// Number of significant bits of x (0 for x = 0).
+__device__ __forceinline__ int bit_width(uint32_t x) { return x ? 32 - __builtin_clz(x) : 0; }
+
 // Writes, in index order, the keys above theta and the first `need` keys equal to theta among
-// this thread's kPer keys (indices idx[i], increasing with thread and i); out_base = outputs
+// this thread's kPer keys (indices idx0 + i, increasing with thread and i); out_base = outputs
 // already written and eq_base = keys equal to theta already seen (both block-uniform).
 // Returns the number written by the whole workgroup; eq_base advances by the ties seen.
-__device__ int emit_ordered(const uint32_t (&key)[kPer], const int32_t (&idx)[kPer], uint32_t theta,
+__device__ int emit_ordered(const uint32_t (&key)[kPer], int32_t idx0, uint32_t theta,
                             int need, int out_base, int &eq_base, int32_t *oi, float *os,
                             TopkSmem &sm) {
     int eqc = 0;
@@ -200,7 +231,7 @@ __device__ int emit_ordered(const uint32_t (&key)[kPer], const int32_t (&idx)[kP
 #pragma unroll
     for (int i = 0; i < kPer; ++i) {
         if (keep[i]) {
-            oi[pos] = idx[i];
+            oi[pos] = idx0 + i;
             if (os) os[pos] = key_score(key[i]);
             ++pos;
         }
@@ -209,15 +240,75 @@ __device__ int emit_ordered(const uint32_t (&key)[kPer], const int32_t (&idx)[kP
     return keep_total;
 }
 
-__global__ __launch_bounds__(kTkThreads) void row_topk_kernel(TopkArgs a) {
-    __shared__ TopkSmem sm;
-    const int64_t g = blockIdx.x;
-    const int tid = threadIdx.x;
-    const int topk = a.topk;
+// Emission from the candidate list.  The list holds `count` candidates in runs, one run per
+// wave chunk of kWChunk keys (sm.run[c] = start | length << 16), each run in index order; the
+// runs themselves are in no particular order.  Thread t holds list entries kPer t .. kPer t +
+// kPer - 1 and bit i of `win` says whether entry i is kept (exactly topk are).  A winner's output
+// slot = winners in earlier chunks + winners before it in its run, both counted from prefix
+// sums over the list.  The output row is staged in LDS and written with 16-byte stores.
+__device__ void emit_winners(const uint32_t (&key)[kPer], const int32_t (&idx)[kPer],
+                             uint32_t win, int count, int nrun, int topk, int32_t *oi,
+                             float *os, TopkSmem &sm) {
+    const int tid = (int)threadIdx.x;
+    const int tsum = __builtin_popcount(win);
+    int all;
+    const int ex0 = block_inclusive_sum(tsum, all, sm) - tsum;   // winners before this thread
+#pragma unroll
+    for (int i = 0; i < kPer; ++i) {
+        const int ex = ex0 + __builtin_popcount(win & ((2u << i) - 1u));
+        if (kPer * tid + i < count) sm.u.emit.pre[kPer * tid + i] = (uint32_t)ex;   // inclusive
+    }
+    __syncthreads();
+    // per run, in chunk order (thread t: chunks 2t, 2t+1): winners W, and winners before it
+    // in the list (lo)
+    uint32_t lo[2], W[2];
+#pragma unroll
+    for (int j = 0; j < 2; ++j) {
+        const int c = 2 * tid + j;
+        const uint32_t r = c < nrun ? sm.run[c] : 0u;
+        const uint32_t s = r & 0xFFFFu, m = r >> 16;
+        lo[j] = s > 0 ? sm.u.emit.pre[s - 1] : 0u;
+        W[j] = (m > 0 ? sm.u.emit.pre[s + m - 1] : lo[j]) - lo[j];
+    }
+    int tot;
+    const int wb = block_inclusive_sum((int)(W[0] + W[1]), tot, sm) - (int)(W[0] + W[1]);
+#pragma unroll
+    for (int j = 0; j < 2; ++j) {
+        const int c = 2 * tid + j;
+        if (c < nrun) {
+            sm.hist[c] = (uint32_t)(wb + (j ? (int)W[0] : 0));
+            sm.run[c] = lo[j];
+        }
+    }
+    __syncthreads();   // (also: every read of pre is done before the staged output overwrites it)
+#pragma unroll
+    for (int i = 0; i < kPer; ++i) {
+        if (kPer * tid + i < count && ((win >> i) & 1u)) {
+            const int c = idx[i] / kWChunk;
+            const int exi = ex0 + __builtin_popcount(win & ((1u << i) - 1u));   // winners before
+            const int pos = (int)sm.hist[c] + exi - (int)sm.run[c];
+            sm.u.emit.out_idx[pos] = idx[i];
+            sm.u.emit.out_score[pos] = key_score(key[i]);
+        }
+    }
+    __syncthreads();
+    // copy-out: 16-byte stores where the output rows allow them
+    const uintptr_t align = reinterpret_cast<uintptr_t>(oi) | reinterpret_cast<uintptr_t>(os);
+    if ((topk & 3) == 0 && (align & 15) == 0) {
+        for (int p = 4 * tid; p < topk; p += 4 * kTkThreads) {
+            *reinterpret_cast<u32x4 *>(oi + p) = *reinterpret_cast<const u32x4 *>(&sm.u.emit.out_idx[p]);
+            if (os) *reinterpret_cast<u32x4 *>(os + p) = *reinterpret_cast<const u32x4 *>(&sm.u.emit.out_score[p]);
+        }
+    } else {
+        for (int p = tid; p < topk; p += kTkThreads) {
+            oi[p] = sm.u.emit.out_idx[p];
+            if (os) os[p] = sm.u.emit.out_score[p];
+        }
+    }
+}
 
-    // ---- locate the row
-    const float *row;
-    int64_t n;
+// Row g's scores and their number.
+__device__ __forceinline__ void locate_row(const TopkArgs &a, int64_t g, const float *&row, int64_t &n) {
     if (a.mode == 0) {
         int64_t t = g, base = 0;
         if (a.cu_seqlens) {
@@ -237,6 +328,41 @@ __global__ __launch_bounds__(kTkThreads) void row_topk_kernel(TopkArgs a) {
         n = L < 0 ? 0 : (L > a.ld ? a.ld : L);
         row = a.scores + g * a.ld;
     }
+}
+
+// 16 keys of a row of n scores from element e0 (4-aligned; rows are padded to a multiple of
+// 64 scores, so a 16-byte group that starts below n lies inside the row); 0 past the end.
+__device__ __forceinline__ void load16(const float *row, int64_t n, int64_t e0, uint32_t (&key)[kPer]) {
+#pragma unroll
+    for (int q = 0; q < 4; ++q) {
+        const int64_t e = e0 + 4 * q;
+        f32x4 v = {0.f, 0.f, 0.f, 0.f};
+        if (e < n) v = *reinterpret_cast<const f32x4 *>(row + e);
+#pragma unroll
+        for (int j = 0; j < 4; ++j) key[4 * q + j] = e + j < n ? score_key(v[j]) : 0u;
+    }
+}
+
+// The sample of a long row: 64 blocks of 64 consecutive scores spread over the row; thread t
+// reads quarter t % 4 of block t / 4.
+__device__ __forceinline__ void load_sample(const float *row, int64_t n, uint32_t (&key)[kPer]) {
+    const int tid = (int)threadIdx.x;
+    const int64_t start = ((int64_t)(tid >> 2) * (n - 64) / 63) & ~(int64_t)3;
+    load16(row, n, start + 16 * (tid & 3), key);
+}
+
+// One workgroup per row.
+__global__ __launch_bounds__(kTkThreads, 4) void row_topk_kernel(TopkArgs a) {
+    __shared__ TopkSmem sm;
+    const int64_t g = blockIdx.x;
+    const int topk = a.topk;
+    const int tid = (int)threadIdx.x;
+    const int lane = tid & 63, wave = tid >> 6;
+    uint32_t key[kPer];
+    int32_t kidx[kPer];
+    const float *row;
+    int64_t n;
+    locate_row(a, g, row, n);
     int32_t *oi = a.out_idx + g * topk;
     float *os = a.out_score ? a.out_score + g * topk : nullptr;
     if (n <= topk) {
@@ -248,154 +374,244 @@ __global__ __launch_bounds__(kTkThreads) void row_topk_kernel(TopkArgs a) {
         return;
     }
 
-    // 16 keys from element e0 (4-aligned; rows are padded to a multiple of 64 scores, so a
-    // 16-byte group that starts below n lies inside the row)
-    auto load16 = [&](int64_t e0, uint32_t (&key)[kPer]) {
-#pragma unroll
-        for (int q = 0; q < 4; ++q) {
-            const int64_t e = e0 + 4 * q;
-            f32x4 v = {0.f, 0.f, 0.f, 0.f};
-            if (e < n) v = *reinterpret_cast<const f32x4 *>(row + e);
-#pragma unroll
-            for (int j = 0; j < 4; ++j) key[4 * q + j] = e + j < n ? score_key(v[j]) : 0u;   // 0: no key
-        }
-    };
-
-    uint32_t key[kPer];
-    int32_t kidx[kPer];
     if (n <= kChunk) {
         // ---- short row: all of it in registers
-        load16(kPer * tid, key);
+        load16(row, n, kPer * tid, key);
+        uint32_t m = 0, mn = 0xFFFFFFFFu;
 #pragma unroll
-        for (int i = 0; i < kPer; ++i) kidx[i] = kPer * tid + i;
+        for (int i = 0; i < kPer; ++i) {
+            m = key[i] > m ? key[i] : m;
+            mn = key[i] != 0u && key[i] < mn ? key[i] : mn;
+        }
+        const uint32_t top = block_max(m, sm);
+        const uint32_t bot = ~block_max(~mn, sm);
         int need = topk;
-        const uint32_t theta = select_regs(key, need, sm);
+        const uint32_t theta = select_rel(key, bot, bit_width(top - bot), need, sm);
         int eq_base = 0;
-        emit_ordered(key, kidx, theta, need, 0, eq_base, oi, os, sm);
+        emit_ordered(key, kPer * tid, theta, need, 0, eq_base, oi, os, sm);
         return;
     }
 
-    // ---- sample: 64 blocks of 64 consecutive scores spread over the row; thread t reads
-    // quarter t % 4 of block t / 4
-    {
-        const int b = tid >> 2;
-        const int64_t start = ((int64_t)b * (n - 64) / 63) & ~(int64_t)3;
-        load16(start + 16 * (tid & 3), key);
+    // ---- sample; the wave's first chunks of the streaming pass are requested right behind
+    // it, so they arrive while theta0 is placed.
+#pragma unroll
+    for (int j = 0; j < kBinsPer; ++j) sm.hist[kBinsPer * tid + j] = 0u;
+    if (tid < kCand / 32) sm.win[tid] = 0u;
+    if (tid == 0) {
+        sm.count = 0u;
+        sm.nbin = 0u;
     }
+    load_sample(row, n, key);
+    const int64_t nwc = (n + kWChunk - 1) / kWChunk;   // wave chunks
+    uint32_t buf[kPrefetch][kPer];
+#pragma unroll
+    for (int p = 0; p < kPrefetch; ++p) load16(row, n, (int64_t)(wave + kTkWaves * p) * kWChunk + kPer * lane, buf[p]);
+
     // r such that about 1.4 topk keys of the row reach the r-th largest of the sample
     int r = (int)(((int64_t)topk * 7 * kChunk + (int64_t)5 * n - 1) / ((int64_t)5 * n)) + 8;
     if (r > kChunk) r = kChunk;
-    uint32_t theta0;
+    uint32_t theta0, top;
     {
         uint32_t m = 0;
 #pragma unroll
         for (int i = 0; i < kPer; ++i) m = key[i] > m ? key[i] : m;
-        const uint32_t top = block_max(m, sm);
-        // bins of 2^sb key units counted down from the largest sample key; a second try with
-        // bins wide enough to hold every key if the first window holds fewer than r samples
-        int sb = 13;
+#pragma unroll
+        for (int d = 32; d >= 1; d >>= 1) {
+            const uint32_t o = (uint32_t)__shfl_xor((int)m, d, 64);
+            m = o > m ? o : m;
+        }
+        if (lane == 0) sm.wmax[wave] = m;
+        __syncthreads();
+        top = 0;
+#pragma unroll
+        for (int i = 0; i < kTkWaves; ++i) top = sm.wmax[i] > top ? sm.wmax[i] : top;
+        // The r-th largest sample key, to 2^14 key units (1/512 of a binade): 1,024 bins of
+        // 2^sb units counted down from wtop.  First the window of two binades below the top;
+        // if it holds fewer than r sample keys, the whole key range in bins of 2^22 units,
+        // then the bin found there in bins of 2^12.  Each thread clears the bins it has read,
+        // so the histogram is zero again for the next pass and for the streaming pass.
+        int64_t wtop = top;
+        int sb = 14, rr = r;
+#pragma unroll 1
         for (;;) {
-            for (int i = tid; i < kBins; i += kTkThreads) sm.hist[i] = 0u;
-            __syncthreads();
 #pragma unroll
             for (int i = 0; i < kPer; ++i) {
-                const uint32_t d = (top - key[i]) >> sb;
-                if (key[i] != 0u && d < (uint32_t)kBins) atomicAdd(&sm.hist[d], 1u);
+                const int64_t d = (wtop - (int64_t)key[i]) >> sb;
+                if (key[i] != 0u && d >= 0 && d < kBins) atomicAdd(&sm.hist[d], 1u);
             }
             __syncthreads();
             // bins in descending key order are ascending d: the first bin where the running
-            // count reaches r (thread t owns bins 8t .. 8t+7)
-            int cnt[8], sum = 0;
+            // count reaches rr
+            int cnt[kBinsPer], sum = 0;
 #pragma unroll
-            for (int j = 0; j < 8; ++j) {
-                cnt[j] = (int)sm.hist[8 * tid + j];
+            for (int j = 0; j < kBinsPer; ++j) {
+                cnt[j] = (int)sm.hist[kBinsPer * tid + j];
                 sum += cnt[j];
             }
             int total;
             int run = block_inclusive_sum(sum, total, sm) - sum;
-            if (total >= r) {
 #pragma unroll
-                for (int j = 0; j < 8; ++j) {
-                    if (run < r && r <= run + cnt[j]) sm.bcast[0] = 8 * tid + j;
-                    run += cnt[j];
+            for (int j = 0; j < kBinsPer; ++j) {
+                if (run < rr && rr <= run + cnt[j]) {
+                    sm.bcast[0] = kBinsPer * tid + j;
+                    sm.bcast[1] = run;
                 }
+                run += cnt[j];
+                sm.hist[kBinsPer * tid + j] = 0u;
             }
             __syncthreads();
-            if (total >= r || sb >= 21) {
-                const int64_t b = total >= r ? sm.bcast[0] : kBins - 1;
-                const int64_t lo = (int64_t)top - ((b + 1) << sb) + 1;   // lowest key of bin b
-                theta0 = lo < 1 ? 1u : (uint32_t)lo;
-                __syncthreads();
+            if (total >= rr) {
+                const int64_t bb = sm.bcast[0];
+                if (sb <= 14) {
+                    const int64_t lo = wtop - ((bb + 1) << sb) + 1;   // lowest key of bin bb
+                    theta0 = lo < 1 ? 1u : (uint32_t)lo;
+                    break;
+                }
+                wtop -= bb << sb;   // the top of bin bb, split next in bins 2^10 times finer
+                rr -= sm.bcast[1];
+                sb -= 10;
+            } else if (sb < 22) {
+                sb = 22;            // the whole key range
+            } else {
+                theta0 = 1u;        // (not reached: the sample holds at least r keys)
                 break;
             }
-            __syncthreads();
-            sb = 21;
+            __syncthreads();        // bcast is read before the next pass writes it
         }
     }
+    // bins of the streaming histogram: 2^sh key units above theta0, so that the sample's
+    // range takes at most half of them; keys further up share the last bin
+    const int sh = bit_width((top - theta0) >> 9);
 
-    // ---- one streaming pass: compact the keys >= theta0 into LDS, in index order
-    const int64_t nchunk = (n + kChunk - 1) / kChunk;
-    int count = 0;
+
+    // ---- streaming pass, every wave on its own: compact the keys >= theta0 of wave chunk c
+    // into a run of the candidate list, in index order (no workgroup barrier until the end)
+    const bool runs_fit = nwc <= kMaxRun;
     uint32_t cmax = 0;
-    uint32_t nxt[kPer];
-    load16(kPer * tid, nxt);
 #pragma unroll 1
-    for (int64_t c = 0; c < nchunk; ++c) {
+    for (int64_t c = wave; c < nwc; c += kTkWaves) {
 #pragma unroll
-        for (int i = 0; i < kPer; ++i) key[i] = nxt[i];
-        if (c + 1 < nchunk) load16((c + 1) * kChunk + kPer * tid, nxt);
+        for (int i = 0; i < kPer; ++i) key[i] = buf[0][i];
+#pragma unroll
+        for (int p = 0; p + 1 < kPrefetch; ++p)
+#pragma unroll
+            for (int i = 0; i < kPer; ++i) buf[p][i] = buf[p + 1][i];
+        const int64_t cn = c + kTkWaves * kPrefetch;
+        if (cn < nwc) load16(row, n, cn * kWChunk + kPer * lane, buf[kPrefetch - 1]);
         int f = 0;
 #pragma unroll
         for (int i = 0; i < kPer; ++i) {
-            const bool in = key[i] != 0u && key[i] >= theta0;
+            const bool in = key[i] >= theta0;   // theta0 >= 1: never a missing key
             f += in ? 1 : 0;
             cmax = in && key[i] > cmax ? key[i] : cmax;
         }
         int total;
-        int pos = count + block_inclusive_sum(f, total, sm) - f;
-        if (count + total <= kCand) {
+        int pos = wave_exclusive_sum(f, total);
+        uint32_t start = 0;
+        if (lane == 0) start = atomicAdd(&sm.count, (uint32_t)total);
+        start = (uint32_t)__builtin_amdgcn_readfirstlane((int)start);
+        if (start + (uint32_t)total > (uint32_t)kCand || !runs_fit) break;   // wave-uniform
+        if (lane == 0) sm.run[c] = start | ((uint32_t)total << 16);
+        pos += (int)start;
 #pragma unroll
-            for (int i = 0; i < kPer; ++i) {
-                if (key[i] != 0u && key[i] >= theta0) {
-                    sm.cand_key[pos] = key[i];
-                    sm.cand_idx[pos] = (int32_t)(c * kChunk + kPer * tid + i);
-                    ++pos;
-                }
+        for (int i = 0; i < kPer; ++i) {
+            if (key[i] >= theta0) {
+                const uint32_t d = (key[i] - theta0) >> sh;
+                atomicAdd(&sm.hist[d < (uint32_t)kBins ? d : kBins - 1], 1u);
+                sm.u.cand.key[pos] = key[i];
+                sm.u.cand.idx[pos] = (int32_t)(c * kWChunk + kPer * lane + i);
+                ++pos;
             }
         }
-        count += total;
-        if (count > kCand) break;   // uniform: too many candidates
     }
     __syncthreads();
+    const int count = (int)sm.count;
 
     int need = topk;
-    if (count >= topk && count <= kCand) {
-        // ---- exact select among the candidates: thread t holds candidates 16t .. 16t+15
+    if (runs_fit && count >= topk && count <= kCand) {
+        // ---- select among the candidates: thread t holds list entries 16t .. 16t+15
 #pragma unroll
         for (int i = 0; i < kPer; ++i) {
             const int ci = kPer * tid + i;
-            key[i] = ci < count ? sm.cand_key[ci] : 0u;
-            kidx[i] = ci < count ? sm.cand_idx[ci] : 0;
+            key[i] = ci < count ? sm.u.cand.key[ci] : 0u;
+            kidx[i] = ci < count ? sm.u.cand.idx[ci] : 0;
         }
-        const uint32_t range = block_max(cmax, sm) - theta0;   // relative keys <= range
-        const int nbits = range ? 32 - __builtin_clz(range) : 1;
-        const uint32_t theta = select_rel(key, theta0, nbits, need, sm);
-        int eq_base = 0;
-        emit_ordered(key, kidx, theta, need, 0, eq_base, oi, os, sm);
-        return;
+        // the bin [blo, bhi] that holds the topk-th largest key; need = its keys that win
+        int in_bin;
+        const uint32_t d = pick_digit(need, sm, &in_bin);
+        const uint64_t lo64 = (uint64_t)theta0 + ((uint64_t)d << sh);   // a key lies above it
+        const uint64_t hi64 = lo64 + (1ull << sh) - 1ull;
+        uint32_t blo = (uint32_t)lo64;
+        uint32_t bhi = d == kBins - 1 || hi64 > 0xFFFFFFFFull ? 0xFFFFFFFFu : (uint32_t)hi64;
+        if (in_bin > kRankMax) {
+            // a crowded bin: narrow it to one key value by an exact select over its keys
+            uint32_t kb[kPer];
+            uint32_t bmax = 0;
+#pragma unroll
+            for (int i = 0; i < kPer; ++i) {
+                kb[i] = key[i] >= blo && key[i] <= bhi ? key[i] : 0u;
+                bmax = kb[i] > bmax ? kb[i] : bmax;
+            }
+            const uint32_t theta = select_rel(kb, blo, bit_width(block_max(bmax, sm) - blo), need, sm);
+            int e = 0;
+#pragma unroll
+            for (int i = 0; i < kPer; ++i) e += key[i] == theta ? 1 : 0;
+            block_inclusive_sum(e, in_bin, sm);
+            blo = bhi = theta;
+        }
+        if (in_bin <= kRankMax) {
+            // rank the bin's keys exactly: by key, then lower index first; the need best win
+#pragma unroll
+            for (int i = 0; i < kPer; ++i) {
+                if (key[i] >= blo && key[i] <= bhi) {
+                    const uint32_t j = atomicAdd(&sm.nbin, 1u);
+                    sm.bin.key[j] = key[i];
+                    sm.bin.idx[j] = kidx[i];
+                    sm.bin.slot[j] = (uint16_t)(kPer * tid + i);
+                }
+            }
+            __syncthreads();
+            if (tid < in_bin) {
+                const uint32_t mk = sm.bin.key[tid];
+                const int32_t mi = sm.bin.idx[tid];
+                int rank = 0;
+                for (int j = 0; j < in_bin; ++j) {
+                    const uint32_t ok = sm.bin.key[j];
+                    rank += (ok > mk || (ok == mk && sm.bin.idx[j] < mi)) ? 1 : 0;
+                }
+                if (rank < need) {
+                    const int sl = sm.bin.slot[tid];
+                    atomicOr(&sm.win[sl >> 5], 1u << (sl & 31));
+                }
+            }
+            __syncthreads();
+            uint32_t win = 0;
+#pragma unroll
+            for (int i = 0; i < kPer; ++i) {
+                const int sl = kPer * tid + i;
+                const bool w = key[i] > bhi || (key[i] >= blo && ((sm.win[sl >> 5] >> (sl & 31)) & 1u));
+                win |= w ? 1u << i : 0u;
+            }
+            emit_winners(key, kidx, win, count, (int)nwc, topk, oi, os, sm);
+            return;
+        }
+        need = topk;   // more than kRankMax equal keys at the threshold: the general path
     }
 
-    // ---- general path: exact select streaming the whole row
+    // ---- general path: exact select streaming the whole row, absolute 10-bit digits from
+    // the top (the last of the four has 2 bits)
+    const int64_t nchunk = (n + kChunk - 1) / kChunk;
     uint32_t prefix = 0, pmask = 0;
 #pragma unroll 1
-    for (int p = 0; p < 3; ++p) {
-        const int shift = kShift[p];
-        const uint32_t dmask = (1u << kWidth[p]) - 1u;
+    for (int hi = 32; hi > 0;) {
+        const int w = hi < kDigit ? hi : kDigit;
+        const int shift = hi - w;
+        const uint32_t dmask = (1u << w) - 1u;
         for (int i = tid; i < kBins; i += kTkThreads) sm.hist[i] = 0u;
         __syncthreads();
 #pragma unroll 1
         for (int64_t c = 0; c < nchunk; ++c) {
-            load16(c * kChunk + kPer * tid, key);
+            load16(row, n, c * kChunk + kPer * tid, key);
 #pragma unroll
             for (int i = 0; i < kPer; ++i) {
                 const uint32_t kv = key[i];
@@ -405,15 +621,14 @@ __global__ __launch_bounds__(kTkThreads) void row_topk_kernel(TopkArgs a) {
         __syncthreads();
         prefix |= pick_digit(need, sm) << shift;
         pmask |= dmask << shift;
+        hi = shift;
     }
     const uint32_t theta = prefix;
     int out = 0, eq_base = 0;
 #pragma unroll 1
     for (int64_t c = 0; c < nchunk; ++c) {
-        load16(c * kChunk + kPer * tid, key);
-#pragma unroll
-        for (int i = 0; i < kPer; ++i) kidx[i] = (int32_t)(c * kChunk + kPer * tid + i);
-        out += emit_ordered(key, kidx, theta, need, out, eq_base, oi, os, sm);
+        load16(row, n, c * kChunk + kPer * tid, key);
+        out += emit_ordered(key, (int32_t)(c * kChunk + kPer * tid), theta, need, out, eq_base, oi, os, sm);
     }
 }
 
