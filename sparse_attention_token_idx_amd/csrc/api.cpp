@@ -95,7 +95,10 @@ size_t ws_score_topk_varlen(int64_t total, int B, int max_seqlen) {
     return ws_hdr(B) + ws_dummy(max_seqlen) + 4u * (size_t)varlen_score_floats(total, B, max_seqlen);
 }
 
-size_t ws_decode(int B, int max_seqlen) { return (size_t)B * (size_t)max_seqlen * 4u; }
+// decode: B + 1 cache offsets, then B score rows of decode_row_stride(max_seqlen) floats
+size_t ws_decode(int B, int max_seqlen) {
+    return ws_hdr(B) + (size_t)B * (size_t)dsaidx::decode_row_stride(max_seqlen) * 4u;
+}
 
 }  // namespace
 
@@ -310,8 +313,10 @@ int dsa_idx_decode(const dsa_idx_bf16 *q, const dsa_idx_bf16 *w, const dsa_idx_b
     if (!aligned16(ws)) return fail(DSA_IDX_EINVAL, "workspace must be 16-byte aligned");
     r = check_device();
     if (r) return r;
+    char *wsb = static_cast<char *>(ws);
     hipError_t e = dsaidx::launch_decode(q, w, k_cache, start, seqlens, B, max_seqlen, topk,
-                                         static_cast<float *>(ws), idx, scores,
+                                         reinterpret_cast<int64_t *>(wsb),
+                                         reinterpret_cast<float *>(wsb + ws_hdr(B)), idx, scores,
                                          reinterpret_cast<hipStream_t>(stream));
     if (e != hipSuccess) return hip_fail("decode launch", e);
     return ok();

@@ -38,12 +38,17 @@ hipError_t launch_row_topk_prefill(const float *scores, const int32_t *cu_seqlen
                                    const int64_t *seq_base, int B, int64_t T, int64_t rows,
                                    int topk, int32_t *idx, float *out_scores, hipStream_t stream);
 hipError_t launch_row_topk_decode(const float *scores, const int32_t *seqlens, int B, int64_t ld,
-                                  int topk, int32_t *idx, float *out_scores, hipStream_t stream);
+                                  int64_t nmax, int topk, int32_t *idx, float *out_scores,
+                                  hipStream_t stream);
 
-// ---- decode (decode.hip).  score_buf holds B rows of ld = 64 * ceil(max_seqlen / 64) floats.
+// ---- decode (decode.hip).  Workspace: cu (B + 1 int64), then score_buf of B rows of
+// decode_row_stride(max_seqlen) floats.
+__host__ __device__ inline int64_t decode_row_stride(int64_t max_seqlen) {
+    return (max_seqlen + 63) / 64 * 64;
+}
 hipError_t launch_decode(const uint16_t *q, const uint16_t *w, const uint16_t *k_cache,
                          const int64_t *start, const int32_t *seqlens, int B, int max_seqlen,
-                         int topk, float *score_buf, int32_t *idx, float *scores,
+                         int topk, int64_t *cu, float *score_buf, int32_t *idx, float *scores,
                          hipStream_t stream);
 
 }  // namespace dsaidx

@@ -33,22 +33,24 @@
 namespace dsaidx {
 namespace {
 
-constexpr int kTkWaves = 4;
-constexpr int kTkThreads = 64 * kTkWaves;
+// W = waves per workgroup (4 for the many rows of prefill, 16 for the few long rows of
+// decode).  Per workgroup: 64 W threads; kPer keys per thread per block chunk of 64 W kPer keys
+// (the register path and the full-row passes).
 constexpr int kPer = 16;                        // keys per thread per chunk
-constexpr int kChunk = kTkThreads * kPer;       // 4,096: the register path, the full-row passes
 constexpr int kWChunk = 64 * kPer;              // 1,024: one wave's chunk in the streaming pass
+constexpr int kSample = 4096;                   // sampled keys of a long row (first 256 threads)
 constexpr int kCand = 4096;                     // candidate list capacity
 constexpr int kBins = 1024;                     // 10-bit digits
 constexpr int kDigit = 10;
-constexpr int kBinsPer = kBins / kTkThreads;    // bins owned by a thread in a scan
 constexpr int kMaxRun = 512;                    // chunk runs: rows of up to 512K keys
 constexpr int kPrefetch = 2;                    // wave chunks in flight ahead of the current
 constexpr int kRankMax = 256;                   // keys of the threshold bin ranked directly
 
-static_assert(kBins % kTkThreads == 0 && kMaxRun == 2 * kTkThreads, "thread ownership");
+// bins owned by a thread in a histogram scan
+template <int W> constexpr int kBinsPer = kBins / (64 * W);
+static_assert(kBinsPer<16> >= 1 && kMaxRun <= 2 * 64 * 4, "thread ownership of bins and runs");
 
-struct TopkSmem {
+template <int W> struct TopkSmem {
     union {
         struct {
             uint32_t key[kCand];
@@ -72,12 +74,12 @@ struct TopkSmem {
     uint32_t win[kCand / 32];      // ranked-in keys of the threshold bin, by list slot
     uint32_t count;                // candidates reserved so far
     uint32_t nbin;                 // keys gathered from the threshold bin
-    int32_t wsum[kTkWaves];
-    uint32_t wmax[kTkWaves];
+    int32_t wsum[W];
+    uint32_t wmax[W];
     int32_t bcast[3];
 };
 
-static_assert(sizeof(TopkSmem) <= 40 * 1024, "four workgroups per CU");
+static_assert(sizeof(TopkSmem<4>) <= 40 * 1024, "four workgroups of 4 waves per CU");
 static_assert(kMaxRun <= kBins, "per-run emission data lives in hist");
 
 struct TopkArgs {
@@ -86,8 +88,9 @@ struct TopkArgs {
     const int32_t *cu_seqlens;     // prefill varlen (nullptr: one sequence of length T)
     const int64_t *seq_base;
     int B;
-    const int32_t *seqlens;        // decode: row b holds seqlens[b] (clamped to ld) scores
-    int64_t ld;                    // decode: row stride
+    const int32_t *seqlens;        // decode: row b holds seqlens[b] (clamped to nmax) scores
+    int64_t ld;                    // decode: row stride (a multiple of 4)
+    int64_t nmax;                  // decode: longest row
     int topk;
     int32_t *out_idx;
     float *out_score;              // may be nullptr
@@ -95,7 +98,8 @@ struct TopkArgs {
 
 
 // Inclusive sum over the workgroup of one int per thread (the sum of all in `total`).
-__device__ int block_inclusive_sum(int v, int &total, TopkSmem &sm) {
+template <int W>
+__device__ int block_inclusive_sum(int v, int &total, TopkSmem<W> &sm) {
     const int tid = (int)threadIdx.x;
     const int lane = tid & 63, wave = tid >> 6;
     const int incl = wave_inclusive_sum(v);
@@ -103,7 +107,7 @@ __device__ int block_inclusive_sum(int v, int &total, TopkSmem &sm) {
     __syncthreads();
     int before = 0, all = 0;
 #pragma unroll
-    for (int i = 0; i < kTkWaves; ++i) {
+    for (int i = 0; i < W; ++i) {
         const int s = sm.wsum[i];
         before += i < wave ? s : 0;
         all += s;
@@ -128,21 +132,22 @@ __device__ __forceinline__ int wave_exclusive_sum(int v, int &total) {
 // found so far, return the digit of the need-th largest and subtract from need the keys in
 // higher digits; in_bin = the keys in the returned digit's bin.  Thread t owns bins
 // kBinsPer t .. kBinsPer t + kBinsPer - 1.
-__device__ uint32_t pick_digit(int &need, TopkSmem &sm, int *in_bin = nullptr) {
+template <int W>
+__device__ uint32_t pick_digit(int &need, TopkSmem<W> &sm, int *in_bin = nullptr) {
     const int tid = (int)threadIdx.x;
-    int cnt[kBinsPer], sum = 0;
+    int cnt[kBinsPer<W>], sum = 0;
 #pragma unroll
-    for (int j = 0; j < kBinsPer; ++j) {
-        cnt[j] = (int)sm.hist[kBinsPer * tid + j];
+    for (int j = 0; j < kBinsPer<W>; ++j) {
+        cnt[j] = (int)sm.hist[kBinsPer<W> * tid + j];
         sum += cnt[j];
     }
     int total;
     const int incl = block_inclusive_sum(sum, total, sm);
     int above = total - incl;   // keys in bins above this thread's
 #pragma unroll
-    for (int j = kBinsPer - 1; j >= 0; --j) {
+    for (int j = kBinsPer<W> - 1; j >= 0; --j) {
         if (above < need && need <= above + cnt[j]) {
-            sm.bcast[0] = kBinsPer * tid + j;
+            sm.bcast[0] = kBinsPer<W> * tid + j;
             sm.bcast[1] = above;
             sm.bcast[2] = cnt[j];
         }
@@ -157,7 +162,8 @@ __device__ uint32_t pick_digit(int &need, TopkSmem &sm, int *in_bin = nullptr) {
 }
 
 // Largest of one key per thread over the workgroup.
-__device__ uint32_t block_max(uint32_t v, TopkSmem &sm) {
+template <int W>
+__device__ uint32_t block_max(uint32_t v, TopkSmem<W> &sm) {
     const int tid = (int)threadIdx.x;
     const int lane = tid & 63, wave = tid >> 6;
 #pragma unroll
@@ -169,7 +175,7 @@ __device__ uint32_t block_max(uint32_t v, TopkSmem &sm) {
     __syncthreads();
     uint32_t m = 0;
 #pragma unroll
-    for (int i = 0; i < kTkWaves; ++i) m = sm.wmax[i] > m ? sm.wmax[i] : m;
+    for (int i = 0; i < W; ++i) m = sm.wmax[i] > m ? sm.wmax[i] : m;
     __syncthreads();
     return m;
 }
@@ -178,8 +184,9 @@ __device__ uint32_t block_max(uint32_t v, TopkSmem &sm) {
 // relative key (key - base) < 2^nbits, kDigit bits at a time from the top: returns theta,
 // the need-th largest key; on return need = how many keys equal to theta are among the need
 // largest.
+template <int W>
 __device__ uint32_t select_rel(const uint32_t (&key)[kPer], uint32_t base, int nbits, int &need,
-                               TopkSmem &sm) {
+                               TopkSmem<W> &sm) {
     uint32_t prefix = 0, pmask = 0;
     int hi = nbits;
 #pragma unroll 1
@@ -187,7 +194,7 @@ __device__ uint32_t select_rel(const uint32_t (&key)[kPer], uint32_t base, int n
         const int w = hi < kDigit ? hi : kDigit;
         const int shift = hi - w;
         const uint32_t dmask = (1u << w) - 1u;
-        for (int i = (int)threadIdx.x; i < kBins; i += kTkThreads) sm.hist[i] = 0u;
+        for (int i = (int)threadIdx.x; i < kBins; i += (64 * W)) sm.hist[i] = 0u;
         __syncthreads();
 #pragma unroll
         for (int i = 0; i < kPer; ++i) {
@@ -209,9 +216,10 @@ __device__ __forceinline__ int bit_width(uint32_t x) { return x ? 32 - __builtin
 // this thread's kPer keys (indices idx0 + i, increasing with thread and i); out_base = outputs
 // already written and eq_base = keys equal to theta already seen (both block-uniform).
 // Returns the number written by the whole workgroup; eq_base advances by the ties seen.
+template <int W>
 __device__ int emit_ordered(const uint32_t (&key)[kPer], int32_t idx0, uint32_t theta,
                             int need, int out_base, int &eq_base, int32_t *oi, float *os,
-                            TopkSmem &sm) {
+                            TopkSmem<W> &sm) {
     int eqc = 0;
 #pragma unroll
     for (int i = 0; i < kPer; ++i) eqc += key[i] == theta ? 1 : 0;
@@ -246,9 +254,10 @@ __device__ int emit_ordered(const uint32_t (&key)[kPer], int32_t idx0, uint32_t 
 // kPer - 1 and bit i of `win` says whether entry i is kept (exactly topk are).  A winner's output
 // slot = winners in earlier chunks + winners before it in its run, both counted from prefix
 // sums over the list.  The output row is staged in LDS and written with 16-byte stores.
+template <int W>
 __device__ void emit_winners(const uint32_t (&key)[kPer], const int32_t (&idx)[kPer],
                              uint32_t win, int count, int nrun, int topk, int32_t *oi,
-                             float *os, TopkSmem &sm) {
+                             float *os, TopkSmem<W> &sm) {
     const int tid = (int)threadIdx.x;
     const int tsum = __builtin_popcount(win);
     int all;
@@ -259,24 +268,24 @@ __device__ void emit_winners(const uint32_t (&key)[kPer], const int32_t (&idx)[k
         if (kPer * tid + i < count) sm.u.emit.pre[kPer * tid + i] = (uint32_t)ex;   // inclusive
     }
     __syncthreads();
-    // per run, in chunk order (thread t: chunks 2t, 2t+1): winners W, and winners before it
+    // per run, in chunk order (thread t: chunks 2t, 2t+1): winners nw, and winners before it
     // in the list (lo)
-    uint32_t lo[2], W[2];
+    uint32_t lo[2], nw[2];
 #pragma unroll
     for (int j = 0; j < 2; ++j) {
         const int c = 2 * tid + j;
         const uint32_t r = c < nrun ? sm.run[c] : 0u;
         const uint32_t s = r & 0xFFFFu, m = r >> 16;
         lo[j] = s > 0 ? sm.u.emit.pre[s - 1] : 0u;
-        W[j] = (m > 0 ? sm.u.emit.pre[s + m - 1] : lo[j]) - lo[j];
+        nw[j] = (m > 0 ? sm.u.emit.pre[s + m - 1] : lo[j]) - lo[j];
     }
     int tot;
-    const int wb = block_inclusive_sum((int)(W[0] + W[1]), tot, sm) - (int)(W[0] + W[1]);
+    const int wb = block_inclusive_sum((int)(nw[0] + nw[1]), tot, sm) - (int)(nw[0] + nw[1]);
 #pragma unroll
     for (int j = 0; j < 2; ++j) {
         const int c = 2 * tid + j;
         if (c < nrun) {
-            sm.hist[c] = (uint32_t)(wb + (j ? (int)W[0] : 0));
+            sm.hist[c] = (uint32_t)(wb + (j ? (int)nw[0] : 0));
             sm.run[c] = lo[j];
         }
     }
@@ -295,12 +304,12 @@ __device__ void emit_winners(const uint32_t (&key)[kPer], const int32_t (&idx)[k
     // copy-out: 16-byte stores where the output rows allow them
     const uintptr_t align = reinterpret_cast<uintptr_t>(oi) | reinterpret_cast<uintptr_t>(os);
     if ((topk & 3) == 0 && (align & 15) == 0) {
-        for (int p = 4 * tid; p < topk; p += 4 * kTkThreads) {
+        for (int p = 4 * tid; p < topk; p += 4 * (64 * W)) {
             *reinterpret_cast<u32x4 *>(oi + p) = *reinterpret_cast<const u32x4 *>(&sm.u.emit.out_idx[p]);
             if (os) *reinterpret_cast<u32x4 *>(os + p) = *reinterpret_cast<const u32x4 *>(&sm.u.emit.out_score[p]);
         }
     } else {
-        for (int p = tid; p < topk; p += kTkThreads) {
+        for (int p = tid; p < topk; p += (64 * W)) {
             oi[p] = sm.u.emit.out_idx[p];
             if (os) os[p] = sm.u.emit.out_score[p];
         }
@@ -325,7 +334,7 @@ __device__ __forceinline__ void locate_row(const TopkArgs &a, int64_t g, const f
         n = t + 1;
     } else {
         const int64_t L = a.seqlens[g];
-        n = L < 0 ? 0 : (L > a.ld ? a.ld : L);
+        n = L < 0 ? 0 : (L > a.nmax ? a.nmax : L);
         row = a.scores + g * a.ld;
     }
 }
@@ -347,13 +356,20 @@ __device__ __forceinline__ void load16(const float *row, int64_t n, int64_t e0, 
 // reads quarter t % 4 of block t / 4.
 __device__ __forceinline__ void load_sample(const float *row, int64_t n, uint32_t (&key)[kPer]) {
     const int tid = (int)threadIdx.x;
+    if (tid >= kSample / kPer) {
+#pragma unroll
+        for (int i = 0; i < kPer; ++i) key[i] = 0u;
+        return;
+    }
     const int64_t start = ((int64_t)(tid >> 2) * (n - 64) / 63) & ~(int64_t)3;
     load16(row, n, start + 16 * (tid & 3), key);
 }
 
 // One workgroup per row.
-__global__ __launch_bounds__(kTkThreads, 4) void row_topk_kernel(TopkArgs a) {
-    __shared__ TopkSmem sm;
+template <int W>
+__global__ __launch_bounds__(64 * W, 16 / W) void row_topk_kernel(TopkArgs a) {
+    constexpr int kChunk = 64 * W * kPer;   // keys of the register path / one full-row pass step
+    __shared__ TopkSmem<W> sm;
     const int64_t g = blockIdx.x;
     const int topk = a.topk;
     const int tid = (int)threadIdx.x;
@@ -366,7 +382,7 @@ __global__ __launch_bounds__(kTkThreads, 4) void row_topk_kernel(TopkArgs a) {
     int32_t *oi = a.out_idx + g * topk;
     float *os = a.out_score ? a.out_score + g * topk : nullptr;
     if (n <= topk) {
-        for (int i = tid; i < topk; i += kTkThreads) {
+        for (int i = tid; i < topk; i += (64 * W)) {
             const bool in = i < n;
             oi[i] = in ? i : -1;
             if (os) os[i] = in ? row[i] : -INFINITY;
@@ -395,7 +411,7 @@ __global__ __launch_bounds__(kTkThreads, 4) void row_topk_kernel(TopkArgs a) {
     // ---- sample; the wave's first chunks of the streaming pass are requested right behind
     // it, so they arrive while theta0 is placed.
 #pragma unroll
-    for (int j = 0; j < kBinsPer; ++j) sm.hist[kBinsPer * tid + j] = 0u;
+    for (int j = 0; j < kBinsPer<W>; ++j) sm.hist[kBinsPer<W> * tid + j] = 0u;
     if (tid < kCand / 32) sm.win[tid] = 0u;
     if (tid == 0) {
         sm.count = 0u;
@@ -405,11 +421,11 @@ __global__ __launch_bounds__(kTkThreads, 4) void row_topk_kernel(TopkArgs a) {
     const int64_t nwc = (n + kWChunk - 1) / kWChunk;   // wave chunks
     uint32_t buf[kPrefetch][kPer];
 #pragma unroll
-    for (int p = 0; p < kPrefetch; ++p) load16(row, n, (int64_t)(wave + kTkWaves * p) * kWChunk + kPer * lane, buf[p]);
+    for (int p = 0; p < kPrefetch; ++p) load16(row, n, (int64_t)(wave + W * p) * kWChunk + kPer * lane, buf[p]);
 
     // r such that about 1.4 topk keys of the row reach the r-th largest of the sample
-    int r = (int)(((int64_t)topk * 7 * kChunk + (int64_t)5 * n - 1) / ((int64_t)5 * n)) + 8;
-    if (r > kChunk) r = kChunk;
+    int r = (int)(((int64_t)topk * 7 * kSample + (int64_t)5 * n - 1) / ((int64_t)5 * n)) + 8;
+    if (r > kSample) r = kSample;
     uint32_t theta0, top;
     {
         uint32_t m = 0;
@@ -424,7 +440,7 @@ __global__ __launch_bounds__(kTkThreads, 4) void row_topk_kernel(TopkArgs a) {
         __syncthreads();
         top = 0;
 #pragma unroll
-        for (int i = 0; i < kTkWaves; ++i) top = sm.wmax[i] > top ? sm.wmax[i] : top;
+        for (int i = 0; i < W; ++i) top = sm.wmax[i] > top ? sm.wmax[i] : top;
         // The r-th largest sample key, to 2^14 key units (1/512 of a binade): 1,024 bins of
         // 2^sb units counted down from wtop.  First the window of two binades below the top;
         // if it holds fewer than r sample keys, the whole key range in bins of 2^22 units,
@@ -442,22 +458,22 @@ __global__ __launch_bounds__(kTkThreads, 4) void row_topk_kernel(TopkArgs a) {
             __syncthreads();
             // bins in descending key order are ascending d: the first bin where the running
             // count reaches rr
-            int cnt[kBinsPer], sum = 0;
+            int cnt[kBinsPer<W>], sum = 0;
 #pragma unroll
-            for (int j = 0; j < kBinsPer; ++j) {
-                cnt[j] = (int)sm.hist[kBinsPer * tid + j];
+            for (int j = 0; j < kBinsPer<W>; ++j) {
+                cnt[j] = (int)sm.hist[kBinsPer<W> * tid + j];
                 sum += cnt[j];
             }
             int total;
             int run = block_inclusive_sum(sum, total, sm) - sum;
 #pragma unroll
-            for (int j = 0; j < kBinsPer; ++j) {
+            for (int j = 0; j < kBinsPer<W>; ++j) {
                 if (run < rr && rr <= run + cnt[j]) {
-                    sm.bcast[0] = kBinsPer * tid + j;
+                    sm.bcast[0] = kBinsPer<W> * tid + j;
                     sm.bcast[1] = run;
                 }
                 run += cnt[j];
-                sm.hist[kBinsPer * tid + j] = 0u;
+                sm.hist[kBinsPer<W> * tid + j] = 0u;
             }
             __syncthreads();
             if (total >= rr) {
@@ -489,14 +505,14 @@ __global__ __launch_bounds__(kTkThreads, 4) void row_topk_kernel(TopkArgs a) {
     const bool runs_fit = nwc <= kMaxRun;
     uint32_t cmax = 0;
 #pragma unroll 1
-    for (int64_t c = wave; c < nwc; c += kTkWaves) {
+    for (int64_t c = wave; c < nwc; c += W) {
 #pragma unroll
         for (int i = 0; i < kPer; ++i) key[i] = buf[0][i];
 #pragma unroll
         for (int p = 0; p + 1 < kPrefetch; ++p)
 #pragma unroll
             for (int i = 0; i < kPer; ++i) buf[p][i] = buf[p + 1][i];
-        const int64_t cn = c + kTkWaves * kPrefetch;
+        const int64_t cn = c + W * kPrefetch;
         if (cn < nwc) load16(row, n, cn * kWChunk + kPer * lane, buf[kPrefetch - 1]);
         int f = 0;
 #pragma unroll
@@ -607,7 +623,7 @@ __global__ __launch_bounds__(kTkThreads, 4) void row_topk_kernel(TopkArgs a) {
         const int w = hi < kDigit ? hi : kDigit;
         const int shift = hi - w;
         const uint32_t dmask = (1u << w) - 1u;
-        for (int i = tid; i < kBins; i += kTkThreads) sm.hist[i] = 0u;
+        for (int i = tid; i < kBins; i += (64 * W)) sm.hist[i] = 0u;
         __syncthreads();
 #pragma unroll 1
         for (int64_t c = 0; c < nchunk; ++c) {
@@ -648,23 +664,25 @@ hipError_t launch_row_topk_prefill(const float *scores, const int32_t *cu_seqlen
     a.topk = topk;
     a.out_idx = idx;
     a.out_score = out_scores;
-    hipLaunchKernelGGL(row_topk_kernel, dim3((unsigned)rows), dim3(kTkThreads), 0, stream, a);
+    hipLaunchKernelGGL(row_topk_kernel<4>, dim3((unsigned)rows), dim3(256), 0, stream, a);
     return hipGetLastError();
 }
 
 hipError_t launch_row_topk_decode(const float *scores, const int32_t *seqlens, int B, int64_t ld,
-                                  int topk, int32_t *idx, float *out_scores, hipStream_t stream) {
+                                  int64_t nmax, int topk, int32_t *idx, float *out_scores,
+                                  hipStream_t stream) {
     if (B == 0) return hipSuccess;
     TopkArgs a{};
     a.scores = scores;
     a.mode = 1;
     a.seqlens = seqlens;
     a.ld = ld;
+    a.nmax = nmax;
     a.B = B;
     a.topk = topk;
     a.out_idx = idx;
     a.out_score = out_scores;
-    hipLaunchKernelGGL(row_topk_kernel, dim3((unsigned)B), dim3(kTkThreads), 0, stream, a);
+    hipLaunchKernelGGL(row_topk_kernel<16>, dim3((unsigned)B), dim3(1024), 0, stream, a);
     return hipGetLastError();
 }
 

@@ -51,7 +51,10 @@ def test_workspace_sizes(dsa):
     # ragged: bound from sequences of max length (here 2 of length 8 -> (8+128)^2/2 floats each)
     vb = ((2 * 136 * 136 // 2 + 127) // 128) * 128
     assert dsa.workspace_size(dsa.OP_SCORE_TOPK_VARLEN, 16, 2, 8, topk=5) == 256 + 512 + 4 * vb
-    assert dsa.workspace_size(dsa.OP_DECODE, 0, 64, 131072, 2048) == 64 * 131072 * 4
+    # decode: 256-byte-aligned header of B + 1 cache offsets, then score rows padded to a
+    # multiple of 64 floats
+    assert dsa.workspace_size(dsa.OP_DECODE, 0, 64, 131072, 2048) == 768 + 64 * 131072 * 4
+    assert dsa.workspace_size(dsa.OP_DECODE, 0, 3, 100, 8) == 256 + 3 * 128 * 4
     with pytest.raises(dsa.DsaIdxError) as e:
         dsa.workspace_size(dsa.OP_SCORE_TOPK, 10, topk=0)
     assert e.value.code == -2

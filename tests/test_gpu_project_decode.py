@@ -121,3 +121,15 @@ def test_decode_small_topk(dsa, topk):
                       full=True)
     for b, L in enumerate(lens):
         check_row(L - 1, r["idx"][b], r["sc"][b], ref, b, topk)
+
+
+@pytest.mark.parametrize("topk", [2048, 64])
+def test_decode_long_rows(dsa, topk):
+    # caches longer than one register-held chunk of the decode select (16,384 scores) take its
+    # sampled-threshold path; the longest length is not a multiple of 64 (padded row stride)
+    lens = [16385, 20001, 33333]
+    r = _decode_case(dsa, lens, seed=40 + topk, topk=topk)
+    ref = oracle.rows(r["q"], r["w"], r["cache"], r["start"], np.asarray(lens) - 1, topk=topk,
+                      full=True)
+    for b, L in enumerate(lens):
+        check_row(L - 1, r["idx"][b], r["sc"][b], ref, b, topk)
