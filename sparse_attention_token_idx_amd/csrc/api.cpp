@@ -114,7 +114,7 @@ int dsa_idx_workspace_size(int op, int64_t total_tokens, int B, int max_seqlen, 
     switch (op) {
         case DSA_IDX_OP_PROJECT:
             if (total_tokens < 0) return fail(DSA_IDX_EINVAL, "T=%lld < 0", (long long)total_tokens);
-            *bytes = 0;
+            *bytes = dsaidx::project_workspace(total_tokens);
             return ok();
         case DSA_IDX_OP_SCORE_TOPK: {
             if (total_tokens < 0) return fail(DSA_IDX_EINVAL, "T=%lld < 0", (long long)total_tokens);
@@ -148,8 +148,6 @@ int dsa_idx_project(const dsa_idx_weights *wt, const dsa_idx_bf16 *x, int64_t ld
                     const dsa_idx_bf16 *c_q, int64_t ldc, int64_t T, dsa_idx_bf16 *q,
                     dsa_idx_bf16 *k_base, const int64_t *k_slot, dsa_idx_bf16 *w, void *ws,
                     size_t ws_bytes, void *stream) {
-    (void)ws;
-    (void)ws_bytes;
     if (!wt) return fail(DSA_IDX_EINVAL, "weights is NULL");
     if (T < 0) return fail(DSA_IDX_EINVAL, "T=%lld < 0", (long long)T);
     if (T == 0) return ok();
@@ -163,11 +161,15 @@ int dsa_idx_project(const dsa_idx_weights *wt, const dsa_idx_bf16 *x, int64_t ld
     for (const void *p : ptrs)
         if (!aligned16(p)) return fail(DSA_IDX_EINVAL, "tensor pointer %p is not 16-byte aligned", p);
     if (T > (int64_t)INT32_MAX * 128) return fail(DSA_IDX_EUNSUPPORTED, "T=%lld too large", (long long)T);
+    const size_t need = dsaidx::project_workspace(T);
+    if (need && (!ws || ws_bytes < need))
+        return fail(DSA_IDX_EWORKSPACE, "workspace %zu bytes < %zu needed", ws ? ws_bytes : (size_t)0, need);
+    if (need && !aligned16(ws)) return fail(DSA_IDX_EINVAL, "workspace must be 16-byte aligned");
     int r = check_device();
     if (r) return r;
     hipError_t e = dsaidx::launch_project(x, ldx, c_q, ldc, T, wt->W_q, wt->W_k, wt->W_w, wt->ln_gamma,
                                           wt->ln_beta, wt->ln_eps, q, k_base, k_slot, w,
-                                          reinterpret_cast<hipStream_t>(stream));
+                                          static_cast<float *>(ws), reinterpret_cast<hipStream_t>(stream));
     if (e != hipSuccess) return hip_fail("project launch", e);
     return ok();
 }

@@ -16,12 +16,15 @@ __host__ __device__ inline int64_t tri_row_offset(int64_t t) {
     return kRowQuant * kRowQuant / 2 * q * (q + 1) + kRowQuant * r * (q + 1);
 }
 
-// ---- projections (project.hip)
+// ---- projections (project.hip).  T <= kSkinnyT takes the split-K path, whose fp32 partial
+// sums need project_workspace(T) bytes at ws (16-byte aligned); larger T needs none.
+constexpr int64_t kSkinnyT = 64;
+size_t project_workspace(int64_t T);
 hipError_t launch_project(const uint16_t *x, int64_t ldx, const uint16_t *c_q, int64_t ldc,
                           int64_t T, const uint16_t *W_q, const uint16_t *W_k,
                           const uint16_t *W_w, const uint16_t *gamma, const uint16_t *beta,
                           float eps, uint16_t *q, uint16_t *k_base, const int64_t *k_slot,
-                          uint16_t *w, hipStream_t stream);
+                          uint16_t *w, float *ws, hipStream_t stream);
 
 // ---- prefill scores (scores.hip).  cu_seqlens == nullptr -> one sequence of length T.
 // seq_base: B + 1 int64 (written here for varlen), out: triangular rows, dummy: a row of

@@ -12,6 +12,13 @@
 // the 16-byte MFMA operand reads and the transposed writes free of bank conflicts.
 // The k/w product (N = 160) keeps whole rows in one wave, so the LayerNorm over the 128
 // key columns runs in the epilogue on the fp32 accumulators before rounding.
+//
+// A handful of tokens (a decode step: T <= kSkinnyT) would give the tiled GEMM a handful
+// of workgroups, each streaming whole weight matrices.  There the work is tiny and the
+// weights are the bytes that matter, so K is split over many workgroups instead: each one
+// runs the same tiled core on one 64-row tile and its K-slice and writes fp32 partial sums
+// to the workspace; a second kernel adds the slices in order (deterministic), then
+// rounds, with the LayerNorm for k.
 #include "common.hpp"
 #include "launch.hpp"
 
@@ -36,9 +43,12 @@ struct GemmCore {
     static constexpr int SN = BN / WN / 16;
     static constexpr int A_CHUNKS = BM * 8 / 256;   // 16-byte A chunks per thread per tile
 
+    // Columns n < nsplit of B come from B0 ([K][ld0]), the others from B1 ([K][ld1], column
+    // n - nsplit).
     __device__ static void run(const uint16_t *__restrict__ A, int64_t lda, int64_t M, int64_t m0,
-                               const uint16_t *__restrict__ B, int N, int n0, int K,
-                               GemmSmem<BM, BN> &sm, f32x4 (&acc)[SM][SN]) {
+                               const uint16_t *__restrict__ B0, int ld0, const uint16_t *__restrict__ B1,
+                               int ld1, int nsplit, int n0, int K, GemmSmem<BM, BN> &sm,
+                               f32x4 (&acc)[SM][SN]) {
         const int tid = threadIdx.x;
         const int wave = tid >> 6, lane = tid & 63;
         const int wm = wave / WN, wn = wave % WN;
@@ -52,6 +62,9 @@ struct GemmCore {
         u32x4 rb[8];
         const bool b_thread = tid < BN;
         const int bkb = tid & 7, bnb = tid >> 3;   // B block: k rows 8*bkb.., n cols 8*bnb..
+        const int bn = n0 + 8 * bnb;
+        const uint16_t *bsrc = bn < nsplit ? B0 + bn : B1 + (bn - nsplit);
+        const int ldb = bn < nsplit ? ld0 : ld1;
         auto load = [&](int kt) {
             const int k0 = kt * kBK;
 #pragma unroll
@@ -65,7 +78,7 @@ struct GemmCore {
             if (b_thread) {
 #pragma unroll
                 for (int i = 0; i < 8; ++i)
-                    rb[i] = *reinterpret_cast<const u32x4 *>(B + (int64_t)(k0 + 8 * bkb + i) * N + n0 + 8 * bnb);
+                    rb[i] = *reinterpret_cast<const u32x4 *>(bsrc + (int64_t)(k0 + 8 * bkb + i) * ldb);
             }
         };
         auto store = [&](int buf) {
@@ -130,7 +143,7 @@ __global__ __launch_bounds__(256) void proj_q_kernel(const uint16_t *__restrict_
     const int64_t m0 = (int64_t)(blockIdx.x / ntn) * 128;
     const int n0 = (blockIdx.x % ntn) * 128;
     f32x4 acc[Core::SM][Core::SN];
-    Core::run(cq, ldc, T, m0, Wq, kQOut, n0, kQLat, sm, acc);
+    Core::run(cq, ldc, T, m0, Wq, kQOut, Wq, kQOut, kQOut, n0, kQLat, sm, acc);
 
     const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63;
     const int wm = wave / 2, wn = wave % 2;
@@ -289,14 +302,139 @@ __global__ __launch_bounds__(256) void proj_kw_kernel(KWArgs a) {
         }
 }
 
+// ---------------------------------------------------------------- small T (split K)
+// part[s][t][n] for one 64-row tile (all T <= 64 rows) and one BN-column tile n0 = BN x:
+// the product of A[:, k0:k0+KS] and B[k0:k0+KS, n0:n0+BN], k0 = KS s, on the tiled core.
+template <int BN, int WM, int WN, int KS>
+__global__ __launch_bounds__(256) void skinny_partial_kernel(const uint16_t *__restrict__ A, int64_t lda,
+                                                             int T, const uint16_t *__restrict__ B0, int ld0,
+                                                             const uint16_t *__restrict__ B1, int ld1,
+                                                             int nsplit, int N, float *__restrict__ part) {
+    using Core = GemmCore<64, BN, WM, WN>;
+    extern __shared__ __align__(16) unsigned char smem_raw[];
+    auto &sm = *reinterpret_cast<GemmSmem<64, BN> *>(smem_raw);
+    const int n0 = BN * blockIdx.x;
+    const int s = blockIdx.y;
+    const int k0 = KS * s;
+    f32x4 acc[Core::SM][Core::SN];
+    Core::run(A + k0, lda, T, 0, B0 + (int64_t)k0 * ld0, ld0, B1 + (int64_t)k0 * ld1, ld1, nsplit, n0, KS,
+              sm, acc);
+    const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63;
+    const int wm = wave / WN, wn = wave % WN;
+    const int l16 = lane & 15, lg = lane >> 4;
+#pragma unroll
+    for (int i = 0; i < Core::SM; ++i)
+#pragma unroll
+        for (int r = 0; r < 4; ++r) {
+            const int row = wm * (64 / WM) + 16 * i + 4 * lg + r;
+            if (row >= T) continue;
+            float *pr = part + ((int64_t)s * T + row) * N + n0 + wn * (BN / WN) + l16;
+#pragma unroll
+            for (int j = 0; j < Core::SN; ++j) pr[16 * j] = acc[i][j][r];
+        }
+}
+
+// q[t][n] = bf16(sum over the S slices of part[s][t][n]); thread: 4 consecutive n.
+__global__ __launch_bounds__(256) void skinny_reduce_q_kernel(const float *__restrict__ part, int S, int T,
+                                                              uint16_t *__restrict__ q) {
+    const int64_t e = 4 * ((int64_t)blockIdx.x * 256 + threadIdx.x);
+    if (e >= (int64_t)T * kQOut) return;
+    f32x4 v = *reinterpret_cast<const f32x4 *>(part + e);
+    for (int s = 1; s < S; ++s) {
+        const f32x4 p = *reinterpret_cast<const f32x4 *>(part + (int64_t)s * T * kQOut + e);
+        v = f32x4{v[0] + p[0], v[1] + p[1], v[2] + p[2], v[3] + p[3]};
+    }
+    *reinterpret_cast<u32x2 *>(q + e) = u32x2{pack_bf16x2(v[0], v[1]), pack_bf16x2(v[2], v[3])};
+}
+
+// One workgroup per token: wave j adds the slices s = j, j + 4, ... of the 160 columns of
+// [k | w] (lane: columns lane, 64 + lane, and 128 + lane for lane < 32); the four wave sums
+// are added in a fixed order, then wave 0 applies the LayerNorm over the 128 key columns
+// (as in the tiled kernel's epilogue), rounds to bf16 and writes k to its slot.
+__global__ __launch_bounds__(256) void skinny_reduce_kw_kernel(const float *__restrict__ part, int S, KWArgs a) {
+    constexpr int N = kDim + kHeads;
+    __shared__ float red[4][3][64];
+    const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+    const int64_t t = blockIdx.x;
+    const int64_t ss = (int64_t)a.T * N;  // slice stride
+    const float *p = part + t * N;
+    float v0 = 0.f, v1 = 0.f, vw = 0.f;
+#pragma unroll 4
+    for (int s = wave; s < S; s += 4) {
+        v0 += p[s * ss + lane];
+        v1 += p[s * ss + 64 + lane];
+        vw += lane < kHeads ? p[s * ss + kDim + lane] : 0.f;
+    }
+    red[wave][0][lane] = v0;
+    red[wave][1][lane] = v1;
+    red[wave][2][lane] = vw;
+    __syncthreads();
+    if (wave) return;
+    v0 = ((red[0][0][lane] + red[1][0][lane]) + red[2][0][lane]) + red[3][0][lane];
+    v1 = ((red[0][1][lane] + red[1][1][lane]) + red[2][1][lane]) + red[3][1][lane];
+    vw = ((red[0][2][lane] + red[1][2][lane]) + red[2][2][lane]) + red[3][2][lane];
+    float sum = v0 + v1;
+#pragma unroll
+    for (int d = 1; d < 64; d <<= 1) sum += __shfl_xor(sum, d, 64);
+    const float mu = sum * (1.0f / kDim);
+    const float c0 = v0 - mu, c1 = v1 - mu;
+    float var = fmaf(c0, c0, c1 * c1);
+#pragma unroll
+    for (int d = 1; d < 64; d <<= 1) var += __shfl_xor(var, d, 64);
+    const float inv = 1.0f / sqrtf(var * (1.0f / kDim) + a.eps);
+    const int64_t slot = a.k_slot ? a.k_slot[t] : t;
+    uint16_t *kr = a.k_base + slot * kDim;
+    kr[lane] = (uint16_t)f32_to_bf16(fmaf(c0 * inv, bf16_to_f32(a.gamma[lane]), bf16_to_f32(a.beta[lane])));
+    kr[64 + lane] = (uint16_t)f32_to_bf16(fmaf(c1 * inv, bf16_to_f32(a.gamma[64 + lane]), bf16_to_f32(a.beta[64 + lane])));
+    if (lane < kHeads) a.w[t * kHeads + lane] = (uint16_t)f32_to_bf16(vw);
+}
+
+constexpr int kSkQSlice = 256;    // q: K = 1,536 in 6 slices x 32 column tiles
+constexpr int kSkKWSlice = 128;   // k/w: K = 7,168 in 56 slices
+
 }  // namespace
+
+size_t project_workspace(int64_t T) {
+    if (T > kSkinnyT || T <= 0) return 0;
+    return 4u * (size_t)T * ((size_t)(kQLat / kSkQSlice) * kQOut + (size_t)(kHidden / kSkKWSlice) * (kDim + kHeads));
+}
 
 hipError_t launch_project(const uint16_t *x, int64_t ldx, const uint16_t *c_q, int64_t ldc,
                           int64_t T, const uint16_t *W_q, const uint16_t *W_k,
                           const uint16_t *W_w, const uint16_t *gamma, const uint16_t *beta,
                           float eps, uint16_t *q, uint16_t *k_base, const int64_t *k_slot,
-                          uint16_t *w, hipStream_t stream) {
+                          uint16_t *w, float *ws, hipStream_t stream) {
     if (T == 0) return hipSuccess;
+    if (T <= kSkinnyT) {
+        const int t = (int)T;
+        float *part_q = ws;
+        float *part_kw = ws + (size_t)(kQLat / kSkQSlice) * T * kQOut;
+        static bool sk_attr_done = false;
+        if (!sk_attr_done) {
+            hipError_t e = hipFuncSetAttribute(
+                reinterpret_cast<const void *>(skinny_partial_kernel<128, 1, 4, kSkQSlice>),
+                hipFuncAttributeMaxDynamicSharedMemorySize, (int)sizeof(GemmSmem<64, 128>));
+            if (e != hipSuccess) return e;
+            e = hipFuncSetAttribute(reinterpret_cast<const void *>(skinny_partial_kernel<160, 2, 2, kSkKWSlice>),
+                                    hipFuncAttributeMaxDynamicSharedMemorySize, (int)sizeof(GemmSmem<64, 160>));
+            if (e != hipSuccess) return e;
+            sk_attr_done = true;
+        }
+        if (q) {
+            hipLaunchKernelGGL((skinny_partial_kernel<128, 1, 4, kSkQSlice>), dim3(kQOut / 128, kQLat / kSkQSlice),
+                               dim3(256), sizeof(GemmSmem<64, 128>), stream, c_q, ldc, t, W_q, kQOut, W_q, kQOut,
+                               kQOut, kQOut, part_q);
+            hipLaunchKernelGGL(skinny_reduce_q_kernel, dim3((unsigned)((T * kQOut / 4 + 255) / 256)), dim3(256),
+                               0, stream, part_q, kQLat / kSkQSlice, t, q);
+        }
+        hipLaunchKernelGGL((skinny_partial_kernel<160, 2, 2, kSkKWSlice>), dim3(1, kHidden / kSkKWSlice), dim3(256),
+                           sizeof(GemmSmem<64, 160>), stream, x, ldx, t, W_k, kDim, W_w, kHeads, kDim, kDim + kHeads,
+                           part_kw);
+        KWArgs a{x, ldx, T, W_k, W_w, gamma, beta, eps, k_base, k_slot, w};
+        hipLaunchKernelGGL(skinny_reduce_kw_kernel, dim3((unsigned)T), dim3(256), 0, stream, part_kw,
+                           kHidden / kSkKWSlice, a);
+        return hipGetLastError();
+    }
     static bool attr_done = false;
     const size_t smem_q = sizeof(GemmSmem<128, 128>);
     const size_t smem_kw = sizeof(GemmSmem<128, 160>);

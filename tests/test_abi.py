@@ -40,6 +40,9 @@ def test_version(dsa):
 
 def test_workspace_sizes(dsa):
     assert dsa.workspace_size(dsa.OP_PROJECT, 100) == 0
+    # a few tokens (at most 64) split K: fp32 partial sums, 6 slices of q and 56 of [k | w]
+    assert dsa.workspace_size(dsa.OP_PROJECT, 64) == 4 * 64 * (6 * 4096 + 56 * 160)
+    assert dsa.workspace_size(dsa.OP_PROJECT, 1) == 4 * (6 * 4096 + 56 * 160)
     # prefill: 256-byte header of sequence bases, a dummy row of 128*ceil(max/128) floats, and
     # the triangular score rows (row t holds 128*(t//128 + 1) floats)
     def tri(t):
@@ -128,3 +131,7 @@ def test_project_rejections(dsa):
     W0 = dsa._Weights(A, A, A, A, A, 0.0)
     assert call(wt=W0) == -1             # eps must be positive
     assert call(T=0) == 0
+    # T <= 64 needs the split-K workspace
+    a = args(T=4)
+    assert L.dsa_idx_project(ctypes.byref(W), a["x"], a["ldx"], a["c_q"], a["ldc"], 4, a["q"], a["k"],
+                             None, a["w"], None, 0, None) == -3
