@@ -40,47 +40,51 @@ constexpr int kPer = 16;                        // keys per thread per chunk
 constexpr int kWChunk = 64 * kPer;              // 1,024: one wave's chunk in the streaming pass
 constexpr int kSample = 4096;                   // sampled keys of a long row (first 256 threads)
 constexpr int kCand = 4096;                     // candidate list capacity
-constexpr int kBins = 1024;                     // 10-bit digits
-constexpr int kDigit = 10;
 constexpr int kMaxRun = 512;                    // chunk runs: rows of up to 512K keys
 constexpr int kPrefetch = 2;                    // wave chunks in flight ahead of the current
-constexpr int kRankMax = 256;                   // keys of the threshold bin ranked directly
+constexpr int kRankMax = 128;                   // keys of the threshold bin ranked directly
 
+// Histogram bins (digits of kDigit<W> bits): 512 for the 4-wave prefill workgroups, whose
+// LDS footprint sets how many rows a CU holds, 1,024 for the 16-wave decode ones.
+template <int W> constexpr int kDigit = W <= 4 ? 9 : 10;
+template <int W> constexpr int kBins = 1 << kDigit<W>;
 // bins owned by a thread in a histogram scan
-template <int W> constexpr int kBinsPer = kBins / (64 * W);
-static_assert(kBinsPer<16> >= 1 && kMaxRun <= 2 * 64 * 4, "thread ownership of bins and runs");
+template <int W> constexpr int kBinsPer = kBins<W> / (64 * W);
+static_assert(kBinsPer<4> >= 1 && kBinsPer<16> >= 1 && kMaxRun <= 2 * 64 * 4,
+              "thread ownership of bins and runs");
 
 template <int W> struct TopkSmem {
     union {
-        struct {
+        struct {                   // a candidate: its key and its offset in its chunk
             uint32_t key[kCand];
-            int32_t idx[kCand];
+            uint16_t off[kCand];
         } cand;
-        struct {                                // emission: list prefix counts, staged output
-            uint32_t pre[kCand];
+        struct {                   // emission: list prefix counts, staged output
+            uint16_t pre[kCand];
             int32_t out_idx[kMaxTopk];
             float out_score[kMaxTopk];
         } emit;
     } u;
     union {
-        uint32_t hist[kBins];      // digit histograms; per run: winners in earlier chunks
+        uint32_t hist[kBins<W>];   // digit histograms; per run: winners in earlier chunks
         struct {                   // the keys of the threshold bin: (key, index), list slot
             uint32_t key[kRankMax];
             int32_t idx[kRankMax];
             uint16_t slot[kRankMax];
         } bin;
     };
-    uint32_t run[kMaxRun];         // start | count << 16 of each chunk's run in the list
+    uint32_t run[kMaxRun];         // start | length << 16 of each chunk's run in the list
+    uint32_t rlog[kMaxRun];        // chunk | start << 16 of each run, in list order
     uint32_t win[kCand / 32];      // ranked-in keys of the threshold bin, by list slot
-    uint32_t count;                // candidates reserved so far
+    uint32_t count;                // candidates reserved so far | runs reserved << 16
     uint32_t nbin;                 // keys gathered from the threshold bin
     int32_t wsum[W];
     uint32_t wmax[W];
     int32_t bcast[3];
 };
 
-static_assert(sizeof(TopkSmem<4>) <= 40 * 1024, "four workgroups of 4 waves per CU");
-static_assert(kMaxRun <= kBins, "per-run emission data lives in hist");
+static_assert(sizeof(TopkSmem<4>) <= 32 * 1024, "five workgroups of 4 waves per CU");
+static_assert(kMaxRun <= kBins<4> && kMaxRun <= kBins<16>, "per-run emission data lives in hist");
 
 struct TopkArgs {
     const float *scores;
@@ -181,7 +185,7 @@ __device__ uint32_t block_max(uint32_t v, TopkSmem<W> &sm) {
 }
 
 // Exact select over keys >= base held in registers (0 = no key), digits taken from the
-// relative key (key - base) < 2^nbits, kDigit bits at a time from the top: returns theta,
+// relative key (key - base) < 2^nbits, kDigit<W> bits at a time from the top: returns theta,
 // the need-th largest key; on return need = how many keys equal to theta are among the need
 // largest.
 template <int W>
@@ -191,10 +195,10 @@ __device__ uint32_t select_rel(const uint32_t (&key)[kPer], uint32_t base, int n
     int hi = nbits;
 #pragma unroll 1
     while (hi > 0) {
-        const int w = hi < kDigit ? hi : kDigit;
+        const int w = hi < kDigit<W> ? hi : kDigit<W>;
         const int shift = hi - w;
         const uint32_t dmask = (1u << w) - 1u;
-        for (int i = (int)threadIdx.x; i < kBins; i += (64 * W)) sm.hist[i] = 0u;
+        for (int i = (int)threadIdx.x; i < kBins<W>; i += (64 * W)) sm.hist[i] = 0u;
         __syncthreads();
 #pragma unroll
         for (int i = 0; i < kPer; ++i) {
@@ -265,7 +269,7 @@ __device__ void emit_winners(const uint32_t (&key)[kPer], const int32_t (&idx)[k
 #pragma unroll
     for (int i = 0; i < kPer; ++i) {
         const int ex = ex0 + __builtin_popcount(win & ((2u << i) - 1u));
-        if (kPer * tid + i < count) sm.u.emit.pre[kPer * tid + i] = (uint32_t)ex;   // inclusive
+        if (kPer * tid + i < count) sm.u.emit.pre[kPer * tid + i] = (uint16_t)ex;   // inclusive
     }
     __syncthreads();
     // per run, in chunk order (thread t: chunks 2t, 2t+1): winners nw, and winners before it
@@ -361,13 +365,14 @@ __device__ __forceinline__ void load_sample(const float *row, int64_t n, uint32_
         for (int i = 0; i < kPer; ++i) key[i] = 0u;
         return;
     }
-    const int64_t start = ((int64_t)(tid >> 2) * (n - 64) / 63) & ~(int64_t)3;
+    constexpr int kBlocks = kSample / 64;
+    const int64_t start = ((int64_t)(tid >> 2) * (n - 64) / (kBlocks - 1)) & ~(int64_t)3;
     load16(row, n, start + 16 * (tid & 3), key);
 }
 
 // One workgroup per row.
 template <int W>
-__global__ __launch_bounds__(64 * W, 16 / W) void row_topk_kernel(TopkArgs a) {
+__global__ __launch_bounds__(64 * W, W == 4 ? 5 : 16 / W) void row_topk_kernel(TopkArgs a) {
     constexpr int kChunk = 64 * W * kPer;   // keys of the register path / one full-row pass step
     __shared__ TopkSmem<W> sm;
     const int64_t g = blockIdx.x;
@@ -441,19 +446,21 @@ __global__ __launch_bounds__(64 * W, 16 / W) void row_topk_kernel(TopkArgs a) {
         top = 0;
 #pragma unroll
         for (int i = 0; i < W; ++i) top = sm.wmax[i] > top ? sm.wmax[i] : top;
-        // The r-th largest sample key, to 2^14 key units (1/512 of a binade): 1,024 bins of
-        // 2^sb units counted down from wtop.  First the window of two binades below the top;
-        // if it holds fewer than r sample keys, the whole key range in bins of 2^22 units,
-        // then the bin found there in bins of 2^12.  Each thread clears the bins it has read,
-        // so the histogram is zero again for the next pass and for the streaming pass.
+        // The r-th largest sample key, to 2^(24 - D) key units: kBins = 2^D bins of 2^sb
+        // units counted down from wtop.  First the window of two binades (2^24 units) below
+        // the top; if it holds fewer than r sample keys, the whole key range in bins of
+        // 2^(32 - D) units, then the bin found there in bins of 2^(32 - 2D).  Each thread
+        // clears the bins it has read, so the histogram is zero again for the next pass and
+        // for the streaming pass.
+        constexpr int kD = kDigit<W>;
         int64_t wtop = top;
-        int sb = 14, rr = r;
+        int sb = 24 - kD, rr = r;
 #pragma unroll 1
         for (;;) {
 #pragma unroll
             for (int i = 0; i < kPer; ++i) {
                 const int64_t d = (wtop - (int64_t)key[i]) >> sb;
-                if (key[i] != 0u && d >= 0 && d < kBins) atomicAdd(&sm.hist[d], 1u);
+                if (key[i] != 0u && d >= 0 && d < kBins<W>) atomicAdd(&sm.hist[d], 1u);
             }
             __syncthreads();
             // bins in descending key order are ascending d: the first bin where the running
@@ -478,16 +485,16 @@ __global__ __launch_bounds__(64 * W, 16 / W) void row_topk_kernel(TopkArgs a) {
             __syncthreads();
             if (total >= rr) {
                 const int64_t bb = sm.bcast[0];
-                if (sb <= 14) {
+                if (sb <= 24 - kD) {
                     const int64_t lo = wtop - ((bb + 1) << sb) + 1;   // lowest key of bin bb
                     theta0 = lo < 1 ? 1u : (uint32_t)lo;
                     break;
                 }
-                wtop -= bb << sb;   // the top of bin bb, split next in bins 2^10 times finer
+                wtop -= bb << sb;   // the top of bin bb, split next in bins 2^D times finer
                 rr -= sm.bcast[1];
-                sb -= 10;
-            } else if (sb < 22) {
-                sb = 22;            // the whole key range
+                sb -= kD;
+            } else if (sb < 32 - kD) {
+                sb = 32 - kD;       // the whole key range
             } else {
                 theta0 = 1u;        // (not reached: the sample holds at least r keys)
                 break;
@@ -497,7 +504,7 @@ __global__ __launch_bounds__(64 * W, 16 / W) void row_topk_kernel(TopkArgs a) {
     }
     // bins of the streaming histogram: 2^sh key units above theta0, so that the sample's
     // range takes at most half of them; keys further up share the last bin
-    const int sh = bit_width((top - theta0) >> 9);
+    const int sh = bit_width((top - theta0) >> (kDigit<W> - 1));
 
 
     // ---- streaming pass, every wave on its own: compact the keys >= theta0 of wave chunk c
@@ -523,34 +530,54 @@ __global__ __launch_bounds__(64 * W, 16 / W) void row_topk_kernel(TopkArgs a) {
         }
         int total;
         int pos = wave_exclusive_sum(f, total);
-        uint32_t start = 0;
-        if (lane == 0) start = atomicAdd(&sm.count, (uint32_t)total);
-        start = (uint32_t)__builtin_amdgcn_readfirstlane((int)start);
+        // one LDS atomic reserves the run: list start in the low half, run number in the
+        // high half (the low half stays below 2^16: reservations stop past kCand)
+        uint32_t res = 0;
+        if (lane == 0) res = atomicAdd(&sm.count, (uint32_t)total | 0x10000u);
+        res = (uint32_t)__builtin_amdgcn_readfirstlane((int)res);
+        const uint32_t start = res & 0xFFFFu;
         if (start + (uint32_t)total > (uint32_t)kCand || !runs_fit) break;   // wave-uniform
-        if (lane == 0) sm.run[c] = start | ((uint32_t)total << 16);
+        if (lane == 0) {
+            sm.run[c] = start | ((uint32_t)total << 16);
+            sm.rlog[res >> 16] = (uint32_t)c | (start << 16);
+        }
         pos += (int)start;
 #pragma unroll
         for (int i = 0; i < kPer; ++i) {
             if (key[i] >= theta0) {
                 const uint32_t d = (key[i] - theta0) >> sh;
-                atomicAdd(&sm.hist[d < (uint32_t)kBins ? d : kBins - 1], 1u);
+                atomicAdd(&sm.hist[d < (uint32_t)kBins<W> ? d : kBins<W> - 1], 1u);
                 sm.u.cand.key[pos] = key[i];
-                sm.u.cand.idx[pos] = (int32_t)(c * kWChunk + kPer * lane + i);
+                sm.u.cand.off[pos] = (uint16_t)(kPer * lane + i);
                 ++pos;
             }
         }
     }
     __syncthreads();
-    const int count = (int)sm.count;
+    const int count = (int)(sm.count & 0xFFFFu);
+    const int nres = (int)(sm.count >> 16);
 
     int need = topk;
     if (runs_fit && count >= topk && count <= kCand) {
         // ---- select among the candidates: thread t holds list entries 16t .. 16t+15
+        // the run (and so the chunk) of list entry 16t: the last run starting at or below it
+        // (runs are logged in list order; an empty run starts where the next one does)
+        int rr0 = 0;
+        {
+            int lo = 0, hi = nres - 1;
+            while (lo < hi) {
+                const int mid = (lo + hi + 1) >> 1;
+                if ((int)(sm.rlog[mid] >> 16) <= kPer * tid) lo = mid;
+                else hi = mid - 1;
+            }
+            rr0 = lo;
+        }
 #pragma unroll
         for (int i = 0; i < kPer; ++i) {
             const int ci = kPer * tid + i;
+            while (rr0 + 1 < nres && (int)(sm.rlog[rr0 + 1] >> 16) <= ci) ++rr0;
             key[i] = ci < count ? sm.u.cand.key[ci] : 0u;
-            kidx[i] = ci < count ? sm.u.cand.idx[ci] : 0;
+            kidx[i] = ci < count ? (int32_t)((sm.rlog[rr0] & 0xFFFFu) * kWChunk + sm.u.cand.off[ci]) : 0;
         }
         // the bin [blo, bhi] that holds the topk-th largest key; need = its keys that win
         int in_bin;
@@ -558,7 +585,7 @@ __global__ __launch_bounds__(64 * W, 16 / W) void row_topk_kernel(TopkArgs a) {
         const uint64_t lo64 = (uint64_t)theta0 + ((uint64_t)d << sh);   // a key lies above it
         const uint64_t hi64 = lo64 + (1ull << sh) - 1ull;
         uint32_t blo = (uint32_t)lo64;
-        uint32_t bhi = d == kBins - 1 || hi64 > 0xFFFFFFFFull ? 0xFFFFFFFFu : (uint32_t)hi64;
+        uint32_t bhi = d == kBins<W> - 1 || hi64 > 0xFFFFFFFFull ? 0xFFFFFFFFu : (uint32_t)hi64;
         if (in_bin > kRankMax) {
             // a crowded bin: narrow it to one key value by an exact select over its keys
             uint32_t kb[kPer];
@@ -620,10 +647,10 @@ __global__ __launch_bounds__(64 * W, 16 / W) void row_topk_kernel(TopkArgs a) {
     uint32_t prefix = 0, pmask = 0;
 #pragma unroll 1
     for (int hi = 32; hi > 0;) {
-        const int w = hi < kDigit ? hi : kDigit;
+        const int w = hi < kDigit<W> ? hi : kDigit<W>;
         const int shift = hi - w;
         const uint32_t dmask = (1u << w) - 1u;
-        for (int i = tid; i < kBins; i += (64 * W)) sm.hist[i] = 0u;
+        for (int i = tid; i < kBins<W>; i += (64 * W)) sm.hist[i] = 0u;
         __syncthreads();
 #pragma unroll 1
         for (int64_t c = 0; c < nchunk; ++c) {
