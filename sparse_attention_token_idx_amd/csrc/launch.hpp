@@ -16,8 +16,8 @@ __host__ __device__ inline int64_t tri_row_offset(int64_t t) {
     return kRowQuant * kRowQuant / 2 * q * (q + 1) + kRowQuant * r * (q + 1);
 }
 
-// ---- projections (project.hip).  T <= kSkinnyT takes the split-K path, whose fp32 partial
-// sums need project_workspace(T) bytes at ws (16-byte aligned); larger T needs none.
+// ---- projections (project.hip).  ws (16-byte aligned) holds project_workspace(T) bytes:
+// for T <= kSkinnyT the split-K path's fp32 partial sums, for larger T W_q transposed.
 constexpr int64_t kSkinnyT = 64;
 size_t project_workspace(int64_t T);
 hipError_t launch_project(const uint16_t *x, int64_t ldx, const uint16_t *c_q, int64_t ldc,

@@ -132,33 +132,134 @@ struct GemmCore {
     }
 };
 
-// q = bf16(c_q . W_q): 128 x 128 tiles, 2 x 2 waves of 64 x 64.
-__global__ __launch_bounds__(256) void proj_q_kernel(const uint16_t *__restrict__ cq, int64_t ldc,
-                                                     int64_t T, const uint16_t *__restrict__ Wq,
-                                                     uint16_t *__restrict__ q) {
-    using Core = GemmCore<128, 128, 2, 2>;
-    extern __shared__ __align__(16) unsigned char smem_raw[];
-    auto &sm = *reinterpret_cast<GemmSmem<128, 128> *>(smem_raw);
-    const int ntn = kQOut / 128;
-    const int64_t m0 = (int64_t)(blockIdx.x / ntn) * 128;
-    const int n0 = (blockIdx.x % ntn) * 128;
-    f32x4 acc[Core::SM][Core::SN];
-    Core::run(cq, ldc, T, m0, Wq, kQOut, Wq, kQOut, kQOut, n0, kQLat, sm, acc);
+// ---------------------------------------------------------------- q for many tokens
+// q = bf16(c_q . W_q) with W_q first transposed into the workspace (W_qT [4096][1536], a
+// few microseconds), so that both operands are k-contiguous and every tile can be copied
+// from global memory into LDS by the direct global->LDS loads (16 bytes per lane, no
+// registers, no VALU transpose).  256 x 256 block tiles, 4 waves of 128 x 128 (the 64
+// accumulator tiles live in AGPRs), K-steps of 32 through a ring of kQStages LDS stages
+// refilled kQStages steps ahead; the next step's MFMA fragments are read while the current
+// step's MFMAs run.  One wave instruction fills 1 KB = 16 rows of 64 bytes, so each MFMA
+// fragment read is one contiguous 1 KB (no bank conflicts, no swizzle).
+typedef __attribute__((address_space(3))) void lds_void;
+constexpr int kQBM = 256, kQBN = 256, kQKB = 32, kQStages = 3;
+constexpr int kQStage = (kQBM + kQBN) * kQKB;   // bf16 per stage
 
-    const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63;
-    const int wm = wave / 2, wn = wave % 2;
-    const int l16 = lane & 15, lg = lane >> 4;
+// W_qT[n][k] = W_q[k][n], 64 x 64 tiles through LDS.
+__global__ __launch_bounds__(256) void transpose_wq_kernel(const uint16_t *__restrict__ Wq, uint16_t *__restrict__ WqT) {
+    __shared__ uint16_t t[64][72];
+    const int n0 = 64 * blockIdx.x, k0 = 64 * blockIdx.y;
+    const int r = threadIdx.x >> 2, c = 16 * (threadIdx.x & 3);
+    const u32x4 v0 = *reinterpret_cast<const u32x4 *>(Wq + (int64_t)(k0 + r) * kQOut + n0 + c);
+    const u32x4 v1 = *reinterpret_cast<const u32x4 *>(Wq + (int64_t)(k0 + r) * kQOut + n0 + c + 8);
 #pragma unroll
-    for (int i = 0; i < Core::SM; ++i)
+    for (int j = 0; j < 4; ++j) {
+        t[r][c + 2 * j] = (uint16_t)(v0[j] & 0xFFFFu);
+        t[r][c + 2 * j + 1] = (uint16_t)(v0[j] >> 16);
+        t[r][c + 8 + 2 * j] = (uint16_t)(v1[j] & 0xFFFFu);
+        t[r][c + 8 + 2 * j + 1] = (uint16_t)(v1[j] >> 16);
+    }
+    __syncthreads();
+    u32x4 o0, o1;   // row n0 + r of W_qT, k = k0 + c .. k0 + c + 15
+#pragma unroll
+    for (int j = 0; j < 4; ++j) {
+        o0[j] = (uint32_t)t[c + 2 * j][r] | ((uint32_t)t[c + 2 * j + 1][r] << 16);
+        o1[j] = (uint32_t)t[c + 8 + 2 * j][r] | ((uint32_t)t[c + 8 + 2 * j + 1][r] << 16);
+    }
+    *reinterpret_cast<u32x4 *>(WqT + (int64_t)(n0 + r) * kQLat + k0 + c) = o0;
+    *reinterpret_cast<u32x4 *>(WqT + (int64_t)(n0 + r) * kQLat + k0 + c + 8) = o1;
+}
+
+__global__ __launch_bounds__(256, 1) void proj_q_kernel(const uint16_t *__restrict__ cq, int64_t ldc,
+                                                        int64_t T, const uint16_t *__restrict__ WqT,
+                                                        uint16_t *__restrict__ q) {
+    constexpr int SM = 8, SN = 8, S = kQStages, KB = kQKB;
+    extern __shared__ __align__(16) uint16_t qsm[];
+    const int ntn = kQOut / kQBN;
+    const int64_t m0 = (int64_t)(blockIdx.x / ntn) * kQBM;
+    const int n0 = (blockIdx.x % ntn) * kQBN;
+    const int tid = threadIdx.x, wave = tid >> 6, lane = tid & 63;
+    const int wm = wave >> 1, wn = wave & 1, l16 = lane & 15, lg = lane >> 4;
+    f32x4 acc[SM][SN];
+#pragma unroll
+    for (int i = 0; i < SM; ++i)
+#pragma unroll
+        for (int j = 0; j < SN; ++j) acc[i][j] = f32x4{0.f, 0.f, 0.f, 0.f};
+
+    // stage of K-step kt: A rows 0..255 then B rows 0..255, 32 bf16 each; wave w fills rows
+    // 64w .. 64w+63 of both, 8 load instructions per wave (rows past T repeat row T - 1)
+    auto issue = [&](int kt) {
+        uint16_t *st = qsm + (kt % S) * kQStage;
+        const int k0 = kt * KB;
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+            const int row = 64 * wave + 16 * i + (lane >> 2);
+            const int kc = 8 * (lane & 3);
+            const int64_t ga = m0 + row < T ? m0 + row : T - 1;
+            __builtin_amdgcn_global_load_lds(static_cast<const void *>(cq + ga * ldc + k0 + kc),
+                                             (lds_void *)(st + (64 * wave + 16 * i) * KB), 16, 0, 0);
+            __builtin_amdgcn_global_load_lds(static_cast<const void *>(WqT + (int64_t)(n0 + row) * kQLat + k0 + kc),
+                                             (lds_void *)(st + kQBM * KB + (64 * wave + 16 * i) * KB),
+                                             16, 0, 0);
+        }
+    };
+    // Until this wave's loads of stage kt are done (8 per later stage may stay in flight),
+    // then this wave's fragment reads of older stages (before anyone refills them), then a
+    // barrier without the fence of __syncthreads (which would wait for every load in flight).
+    const int nk = kQLat / KB;
+    auto wait_stage = [&](int kt) {
+        const int later = min(S - 2, nk - 1 - kt);
+        if (later >= 2) asm volatile("s_waitcnt vmcnt(16)" ::: "memory");
+        else if (later == 1) asm volatile("s_waitcnt vmcnt(8)" ::: "memory");
+        else asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
+        asm volatile("s_waitcnt lgkmcnt(0)\n\ts_barrier" ::: "memory");
+    };
+    u32x4 fa[2][SM], fb[2][SN];
+    auto read_frags = [&](int kt, int p) {
+        const uint16_t *st = qsm + (kt % S) * kQStage;
+#pragma unroll
+        for (int i = 0; i < SM; ++i)
+            fa[p][i] = *reinterpret_cast<const u32x4 *>(st + (wm * 128 + 16 * i + l16) * KB + 8 * lg);
+#pragma unroll
+        for (int j = 0; j < SN; ++j)
+            fb[p][j] = *reinterpret_cast<const u32x4 *>(st + kQBM * KB + (wn * 128 + 16 * j + l16) * KB + 8 * lg);
+    };
+    // the ring holds S stages; step k refills the slot of stage k, already in registers
+#pragma unroll
+    for (int p = 0; p < S; ++p)
+        if (p < nk) issue(p);
+    wait_stage(0);
+    read_frags(0, 0);
+    for (int kt = 0; kt < nk; kt += 2) {
+#pragma unroll
+        for (int h = 0; h < 2; ++h) {   // fragments of step kt + h in register set h
+            const int k = kt + h;
+            if (k < nk) {
+                if (k + 1 < nk) {
+                    wait_stage(k + 1);
+                    if (k + S < nk) issue(k + S);
+                    read_frags(k + 1, h ^ 1);
+                }
+#pragma unroll
+                for (int i = 0; i < SM; ++i)
+#pragma unroll
+                    for (int j = 0; j < SN; ++j) acc[i][j] = mfma16x16x32(fa[h][i], fb[h][j], acc[i][j]);
+            }
+        }
+    }
+#pragma unroll
+    for (int i = 0; i < SM; ++i)
 #pragma unroll
         for (int r = 0; r < 4; ++r) {
-            const int64_t row = m0 + wm * 64 + 16 * i + 4 * lg + r;
+            const int64_t row = m0 + wm * 128 + 16 * i + 4 * lg + r;
             if (row >= T) continue;
 #pragma unroll
-            for (int j = 0; j < Core::SN; ++j)
-                q[row * kQOut + n0 + wn * 64 + 16 * j + l16] = (uint16_t)f32_to_bf16(acc[i][j][r]);
+            for (int j = 0; j < SN; ++j)
+                q[row * kQOut + n0 + wn * 128 + 16 * j + l16] = (uint16_t)f32_to_bf16(acc[i][j][r]);
         }
 }
+
+static_assert(kQLat % (2 * kQKB) == 0 && kQOut % kQBN == 0, "q tiles");
 
 // [k | w] = x . [W_k | W_w] (N = 128 + 32), LayerNorm on the k part: 128-row tiles, each
 // of the 4 waves owns 32 full rows.  The two weight matrices are read as one [7168][160]
@@ -395,7 +496,8 @@ constexpr int kSkKWSlice = 128;   // k/w: K = 7,168 in 56 slices
 }  // namespace
 
 size_t project_workspace(int64_t T) {
-    if (T > kSkinnyT || T <= 0) return 0;
+    if (T <= 0) return 0;
+    if (T > kSkinnyT) return (size_t)kQOut * kQLat * 2;   // W_q transposed
     return 4u * (size_t)T * ((size_t)(kQLat / kSkQSlice) * kQOut + (size_t)(kHidden / kSkKWSlice) * (kDim + kHeads));
 }
 
@@ -436,7 +538,7 @@ hipError_t launch_project(const uint16_t *x, int64_t ldx, const uint16_t *c_q, i
         return hipGetLastError();
     }
     static bool attr_done = false;
-    const size_t smem_q = sizeof(GemmSmem<128, 128>);
+    const size_t smem_q = sizeof(uint16_t) * kQStage * kQStages;
     const size_t smem_kw = sizeof(GemmSmem<128, 160>);
     if (!attr_done) {
         hipError_t e = hipFuncSetAttribute(reinterpret_cast<const void *>(proj_q_kernel),
@@ -449,8 +551,11 @@ hipError_t launch_project(const uint16_t *x, int64_t ldx, const uint16_t *c_q, i
     }
     const int64_t mt = (T + 127) / 128;
     if (q) {
-        hipLaunchKernelGGL(proj_q_kernel, dim3((unsigned)(mt * (kQOut / 128))), dim3(256), smem_q,
-                           stream, c_q, ldc, T, W_q, q);
+        uint16_t *WqT = reinterpret_cast<uint16_t *>(ws);
+        hipLaunchKernelGGL(transpose_wq_kernel, dim3(kQOut / 64, kQLat / 64), dim3(256), 0, stream, W_q, WqT);
+        const int64_t qt = (T + kQBM - 1) / kQBM;
+        hipLaunchKernelGGL(proj_q_kernel, dim3((unsigned)(qt * (kQOut / kQBN))), dim3(256), smem_q, stream,
+                           c_q, ldc, T, WqT, q);
         hipError_t e = hipGetLastError();
         if (e != hipSuccess) return e;
     }

@@ -39,7 +39,8 @@ def test_version(dsa):
 
 
 def test_workspace_sizes(dsa):
-    assert dsa.workspace_size(dsa.OP_PROJECT, 100) == 0
+    # more than 64 tokens: W_q transposed (4096 x 1536 bf16)
+    assert dsa.workspace_size(dsa.OP_PROJECT, 100) == 4096 * 1536 * 2
     # a few tokens (at most 64) split K: fp32 partial sums, 6 slices of q and 56 of [k | w]
     assert dsa.workspace_size(dsa.OP_PROJECT, 64) == 4 * 64 * (6 * 4096 + 56 * 160)
     assert dsa.workspace_size(dsa.OP_PROJECT, 1) == 4 * (6 * 4096 + 56 * 160)
