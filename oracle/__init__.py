@@ -68,6 +68,17 @@ def lib():
         L.oracle_topk.argtypes = [vp, i64, i32, vp, vp, vp, vp]
         L.oracle_rows.restype = None
         L.oracle_rows.argtypes = [vp, vp, vp, vp, vp, i64, i32, i32, i32, vp, vp, vp, vp, vp, vp]
+        L.oracle_e4m3_to_f64.restype = f64
+        L.oracle_e4m3_to_f64.argtypes = [ctypes.c_uint8]
+        L.oracle_f64_to_e4m3.restype = ctypes.c_uint8
+        L.oracle_f64_to_e4m3.argtypes = [f64]
+        L.oracle_pow2_scale_exp.restype = i32
+        L.oracle_pow2_scale_exp.argtypes = [f64]
+        L.oracle_quantize_e4m3.restype = None
+        L.oracle_quantize_e4m3.argtypes = [vp, i64, i32, vp, vp]
+        L.oracle_rows_fp8.restype = None
+        L.oracle_rows_fp8.argtypes = [vp, vp, vp, vp, vp, vp, vp, i64, i32, i32, i32, vp, vp, vp, vp,
+                                      vp, vp]
         _lib = L
     return _lib
 
@@ -208,3 +219,58 @@ def prefill_rows(q, k, w, row_ids, topk=TOPK, full=False):
     """Rows of one causal sequence: q [T,H,D], k [T,D], w [T,H]."""
     row_ids = np.asarray(row_ids, dtype=np.int64)
     return rows(q[row_ids], w[row_ids], k, np.zeros_like(row_ids), row_ids, topk, full)
+
+
+# ---------------------------------------------------------------- FP8 (OCP E4M3) key cache
+def e4m3_to_f64(codes):
+    codes = np.asarray(codes, dtype=np.uint8)
+    return np.array([lib().oracle_e4m3_to_f64(int(c)) for c in codes.ravel()]).reshape(codes.shape)
+
+
+def f64_to_e4m3(x):
+    x = np.asarray(x, dtype=np.float64)
+    return np.array([lib().oracle_f64_to_e4m3(float(v)) for v in x.ravel()], np.uint8).reshape(x.shape)
+
+
+def pow2_scale_exp(amax):
+    return int(lib().oracle_pow2_scale_exp(float(amax)))
+
+
+def quantize_e4m3(x):
+    """x [n, d] bf16 patterns -> (codes [n, d] uint8, exponents [n] int32): scale 2^e per row."""
+    x = _c(x, np.uint16)
+    n, d = x.shape
+    codes = np.empty((n, d), np.uint8)
+    exps = np.empty(n, np.int32)
+    lib().oracle_quantize_e4m3(_p(x), n, d, _p(codes), _p(exps))
+    return codes, exps
+
+
+def rows_fp8(q_rows, w_rows, k_codes, k_exps, k_off, t, topk=TOPK, full=False):
+    """FP8 decode rows: q_rows [R,H,D] bf16 (quantised here per head), w_rows [R,H] bf16,
+    k_codes [*, D] uint8 with exponents k_exps; row r scores cache rows k_off[r] .. + t[r]."""
+    q_rows = _c(q_rows, np.uint16)
+    R, Hh, Dd = q_rows.shape
+    qc, qe = quantize_e4m3(q_rows.reshape(R * Hh, Dd))
+    qc = _c(qc.reshape(R, Hh, Dd), np.uint8)
+    qe = _c(qe.reshape(R, Hh), np.int32)
+    w_rows = _c(w_rows, np.uint16)
+    k_codes = _c(k_codes, np.uint8)
+    k_exps = _c(k_exps, np.int32)
+    k_off = _c(k_off, np.int64)
+    t = _c(t, np.int64)
+    idx = np.empty((R, topk), np.int32)
+    sc = np.empty((R, topk), np.float64)
+    tau = np.empty(R)
+    m = np.empty(R)
+    fbuf = foff = None
+    if full:
+        foff = np.zeros(R, dtype=np.int64)
+        foff[1:] = np.cumsum(t + 1)[:-1]
+        fbuf = np.empty(int((t + 1).sum()), dtype=np.float64)
+    lib().oracle_rows_fp8(_p(qc), _p(qe), _p(w_rows), _p(k_codes), _p(k_exps), _p(k_off), _p(t), R,
+                          Hh, Dd, topk, _p(idx), _p(sc), _p(tau), _p(m), _p(fbuf), _p(foff))
+    out = dict(idx=idx, score=sc, tau=tau, maxabs=m, full=None)
+    if full:
+        out["full"] = [fbuf[foff[j]:foff[j] + t[j] + 1] for j in range(R)]
+    return out

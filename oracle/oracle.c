@@ -30,6 +30,15 @@
  * applied to the unrounded projection, with gain and bias; w has no
  * activation and may be negative; head h of q is columns [128h, 128h+128).
  *
+ * FP8 key cache (a next step on the same pages: serving engines cache the
+ * indexer keys in FP8, "Kimi K3.1 Pro vs GLM-5" page, low-precision row; the
+ * pages give no FP8 format or scale, so the reading is stated here): OCP
+ * E4M3 codes (bias 7, no infinities, 448 the largest finite value) with one
+ * power-of-two scale per cached key (per query head for the query), the
+ * smallest 2^e with max|x| <= 448 * 2^e, so that x / 2^e is exact and the
+ * only rounding is round-to-nearest-even onto E4M3.  The score of the FP8
+ * path is the same formula on the dequantised q and k, in double.
+ *
  * Shares no code, header or table with the HIP implementation.
  */
 #include <math.h>
@@ -263,6 +272,100 @@ void oracle_rows(const uint16_t *q_rows, const uint16_t *w_rows, const uint16_t 
                       n, H, D, I);
         oracle_topk(I, n, topk, idx + r * (int64_t)topk, score + r * (int64_t)topk, tau + r,
                     maxabs + r);
+        if (!full) free(I);
+    }
+}
+
+/* ---------------- FP8 (OCP E4M3) key cache ---------------- */
+
+/* Value of an E4M3 code: sign, 4 exponent bits (bias 7), 3 mantissa bits;
+ * exponent 0 holds the subnormals m/8 * 2^-6; 0x7F and 0xFF are NaN. */
+double oracle_e4m3_to_f64(uint8_t c) {
+    const int sgn = c >> 7, e = (c >> 3) & 15, m = c & 7;
+    if (e == 15 && m == 7) return NAN;
+    const double mag = e ? ldexp(8.0 + m, e - 10) : ldexp((double)m, -9);
+    return sgn ? -mag : mag;
+}
+
+/* Nearest E4M3 code to x (ties to the even code), for |x| <= 448.  The codes
+ * of one sign are in value order, so the magnitude is located by walking the
+ * binades: in binade [2^E, 2^(E+1)), E >= -6, the 8 codes are spaced 2^(E-3);
+ * below 2^-6 the subnormals are spaced 2^-9.  x/spacing is exact in double. */
+uint8_t oracle_f64_to_e4m3(double x) {
+    const uint8_t sgn = (signbit(x) ? 0x80 : 0x00);
+    const double a = fabs(x);
+    int E = -6;                       /* binade of a, at least the subnormal one */
+    while (E < 8 && a >= ldexp(1.0, E + 1)) ++E;
+    const double unit = ldexp(1.0, E - 3);
+    const double n = a / unit;        /* in [0, 16) */
+    double r = floor(n);
+    const double frac = n - r;
+    if (frac > 0.5 || (frac == 0.5 && fmod(r, 2.0) != 0.0)) r += 1.0;
+    /* code magnitude: codes below 8 are the subnormals (n < 8 when E = -6 and
+     * a < 2^-6); in binade E the codes are 8 (E + 6) + r, r in [8, 16] */
+    int mag;
+    if (a < ldexp(1.0, -6)) mag = (int)r;              /* r in [0, 8]: 8 is 2^-6 */
+    else mag = 8 * (E + 6) + (int)r;
+    return (uint8_t)(sgn | mag);
+}
+
+/* Smallest integer e with amax <= 448 * 2^e (amax > 0; 0 for amax = 0). */
+int oracle_pow2_scale_exp(double amax) {
+    if (!(amax > 0.0)) return 0;
+    int e = 0;
+    while (amax > 448.0 * ldexp(1.0, e)) ++e;
+    while (amax <= 448.0 * ldexp(1.0, e - 1)) --e;
+    return e;
+}
+
+/* Quantise n vectors of d bf16 values: codes[i][j] = E4M3(x[i][j] / 2^e_i),
+ * e_i = oracle_pow2_scale_exp(max_j |x[i][j]|). */
+void oracle_quantize_e4m3(const uint16_t *x, int64_t n, int d, uint8_t *codes, int32_t *exps) {
+    for (int64_t i = 0; i < n; ++i) {
+        double amax = 0.0;
+        for (int j = 0; j < d; ++j) {
+            const double v = fabs(oracle_bf16_to_f64(x[i * d + j]));
+            if (v > amax) amax = v;
+        }
+        const int e = oracle_pow2_scale_exp(amax);
+        exps[i] = e;
+        for (int j = 0; j < d; ++j)
+            codes[i * d + j] = oracle_f64_to_e4m3(ldexp(oracle_bf16_to_f64(x[i * d + j]), -e));
+    }
+}
+
+/* FP8 decode rows: row r has query codes qc [H][D] with per-head exponents qe [H], bf16
+ * weights w [H], and scores the cached keys kc[(k_off[r] + s) * D ..] (exponent ke[..]) for
+ * s <= t[r]:  I[s] = 2^ke[s] * sum_h w[h] 2^qe[h] max(0, sum_d dq[h][d] dk[s][d]), with
+ * dq, dk the E4M3 values, in double.  Selection as oracle_rows. */
+void oracle_rows_fp8(const uint8_t *qc, const int32_t *qe, const uint16_t *w_rows,
+                     const uint8_t *kc, const int32_t *ke, const int64_t *k_off, const int64_t *t,
+                     int64_t nrows, int H, int D, int topk, int32_t *idx, double *score,
+                     double *tau, double *maxabs, double *full, const int64_t *full_off) {
+#pragma omp parallel for schedule(dynamic, 1)
+    for (int64_t r = 0; r < nrows; ++r) {
+        const int64_t n = t[r] + 1;
+        double *I = full ? full + full_off[r] : (double *)malloc(sizeof(double) * (size_t)n);
+        double *qd = (double *)malloc(sizeof(double) * (size_t)H * D);
+        double *kd = (double *)malloc(sizeof(double) * (size_t)D);
+        double *wq = (double *)malloc(sizeof(double) * (size_t)H);
+        for (int i = 0; i < H * D; ++i) qd[i] = oracle_e4m3_to_f64(qc[r * (int64_t)H * D + i]);
+        for (int h = 0; h < H; ++h)
+            wq[h] = oracle_bf16_to_f64(w_rows[r * (int64_t)H + h]) * ldexp(1.0, qe[r * (int64_t)H + h]);
+        for (int64_t s = 0; s < n; ++s) {
+            const int64_t row = k_off[r] + s;
+            for (int d = 0; d < D; ++d) kd[d] = oracle_e4m3_to_f64(kc[row * D + d]);
+            double acc = 0.0;
+            for (int h = 0; h < H; ++h) {
+                double dot = 0.0;
+                for (int d = 0; d < D; ++d) dot += qd[h * D + d] * kd[d];
+                acc += wq[h] * (dot > 0.0 ? dot : 0.0);
+            }
+            I[s] = ldexp(acc, ke[row]);
+        }
+        oracle_topk(I, n, topk, idx + r * (int64_t)topk, score + r * (int64_t)topk, tau + r,
+                    maxabs + r);
+        free(qd); free(kd); free(wq);
         if (!full) free(I);
     }
 }
