@@ -190,6 +190,33 @@ def bench_decode(dsa, args):
     torch.cuda.synchronize()
     proj_ms = float(np.mean([e[0].elapsed_time(e[1]) for e in evs]))
     dec_ms = float(np.mean([e[1].elapsed_time(e[2]) for e in evs]))
+
+    # FP8 key cache: the cache quantised once (not timed: it is written as the keys arrive);
+    # a step quantises the new tokens' keys into it and decodes against it
+    k8, k8s = dsa.quantize_keys(cache_d)
+    ws8 = torch.empty(dsa.workspace_size(dsa.OP_DECODE_FP8, 0, B, maxL, topk), dtype=torch.uint8,
+                      device="cuda")
+
+    def step8(ev=None):
+        if ev is not None:
+            ev[0].record(stream)
+        dsa.quantize_keys(cache_d[slots], k8, k8s, slot=slots)
+        if ev is not None:
+            ev[1].record(stream)
+        dsa.decode_fp8(q, w, k8, k8s, start_d, lens_d, maxL, topk=topk, ws=ws8, out=(idx, sc))
+        if ev is not None:
+            ev[2].record(stream)
+
+    for _ in range(max(args.warmup, 1)):
+        step8()
+    torch.cuda.synchronize()
+    evs8 = [[torch.cuda.Event(enable_timing=True) for _ in range(3)] for _ in range(n)]
+    torch.cuda._sleep(100_000_000)
+    for i in range(n):
+        step8(evs8[i])
+    torch.cuda.synchronize()
+    q8_ms = float(np.mean([e[0].elapsed_time(e[1]) for e in evs8]))
+    dec8_ms = float(np.mean([e[1].elapsed_time(e[2]) for e in evs8]))
     sumL = int(lens.sum())
     # algorithmic bytes of the decode kernels: every cached key once, q and w of the new
     # tokens, the selected indices and scores
@@ -197,9 +224,14 @@ def bench_decode(dsa, args):
     proj_bytes = 2 * (QLAT * 4096 + HIDDEN * D + HIDDEN * H + 2 * D) + B * 2 * (HIDDEN + QLAT) \
         + B * 2 * (H * D + D + H)
     gbps = dec_bytes / (dec_ms * 1e-3) / 1e9
+    # FP8: 128 code bytes and a 4-byte scale per cached key
+    dec8_bytes = 132 * sumL + B * (H * D * 2 + H * 2) + B * topk * 8
+    gbps8 = dec8_bytes / (dec8_ms * 1e-3) / 1e9
     log(f"decode: B={B} sum L={sumL}: project {proj_ms:.3f} ms, decode {dec_ms:.3f} ms "
         f"({gbps:.0f} GB/s); one step issued from Python, host-bound: {host_ms:.3f} ms")
+    log(f"decode fp8: quantise new keys {q8_ms:.3f} ms, decode {dec8_ms:.3f} ms ({gbps8:.0f} GB/s)")
     return dict(batch=B, sum_keys=sumL, project_ms=proj_ms, decode_ms=dec_ms, host_step_ms=host_ms,
+                fp8=dict(quantize_ms=q8_ms, decode_ms=dec8_ms, bytes=dec8_bytes, GBps=gbps8),
                 decode_bytes=dec_bytes, decode_GBps=gbps, decode_hbm_frac=gbps / PEAK_HBM_GBPS,
                 step_GBps=(dec_bytes + proj_bytes) / ((dec_ms + proj_ms) * 1e-3) / 1e9)
 
@@ -294,7 +326,12 @@ def main():
             "GBps": round(dec["decode_GBps"], 1), "hbm_frac": round(dec["decode_hbm_frac"], 4),
             "step_GBps_incl_project": round(dec["step_GBps"], 1),
             "host_step_ms": round(dec["host_step_ms"], 4),
-            "algorithmic_bytes": dec["decode_bytes"]},
+            "algorithmic_bytes": dec["decode_bytes"],
+            "fp8_cache": {"decode_ms": round(dec["fp8"]["decode_ms"], 4),
+                          "quantize_new_keys_ms": round(dec["fp8"]["quantize_ms"], 4),
+                          "GBps": round(dec["fp8"]["GBps"], 1),
+                          "hbm_frac": round(dec["fp8"]["GBps"] / PEAK_HBM_GBPS, 4),
+                          "algorithmic_bytes": dec["fp8"]["bytes"]}},
         "cpu_baseline": cpu,
     }
     print(json.dumps(line), flush=True)

@@ -73,6 +73,7 @@ extern "C" {
 #define DSA_IDX_OP_SCORE_TOPK 1
 #define DSA_IDX_OP_SCORE_TOPK_VARLEN 2
 #define DSA_IDX_OP_DECODE 3
+#define DSA_IDX_OP_DECODE_FP8 4
 
 typedef uint16_t dsa_idx_bf16;
 
@@ -174,6 +175,30 @@ int dsa_idx_decode(const dsa_idx_bf16 *q, const dsa_idx_bf16 *w, const dsa_idx_b
                    const int64_t *start, const int32_t *seqlens, int B, int max_seqlen,
                    int topk, int32_t *idx, float *scores, void *ws, size_t ws_bytes,
                    void *stream);
+
+/* ---- FP8 key cache ("Kimi K3.1 Pro vs GLM-5" page, low-precision row: the serving engines
+ * cache the indexer keys in FP8; the pages give no format or scale).  Format of this library:
+ * a cached key is 128 OCP E4M3 codes (bias 7, largest finite value 448, no infinities; one
+ * byte per dimension, k8 [*][128]) and one fp32 scale k_scale[*] = 2^e, the smallest power of
+ * two with max_j |k_j| <= 448 * 2^e; code_j = E4M3(k_j / 2^e) rounded to nearest even (the
+ * division is exact, so this is the only rounding).  Dequantised: k_j ~ 2^e * E4M3 value. */
+
+/* Quantises N bf16 keys k [N][ldk] (ldk >= 128, a multiple of 8; k 16-byte aligned) into cache
+ * rows slot[i] (device int64 [N]; NULL: row i) of k8 (16-byte aligned) and k_scale.
+ * Asynchronous on `stream`; no workspace. */
+int dsa_idx_quantize_keys(const dsa_idx_bf16 *k, int64_t ldk, int64_t N, const int64_t *slot,
+                          uint8_t *k8, float *k_scale, void *stream);
+
+/* Decode against an FP8 cache: as dsa_idx_decode, with the cached keys given as k8 / k_scale
+ * rows [start[b], start[b] + seqlens[b]).  The new queries are quantised the same way, one
+ * scale per head (q_h ~ 2^eq_h * E4M3 codes), and
+ *   scores[b][j] = I[s] = 2^e_s * sum_h w[b][h] 2^eq_h max(0, sum_d E4M3(q_h)[d] E4M3(k_s)[d]),
+ * the indexer formula on the dequantised vectors, in fp32 (the E4M3 products are exact).
+ * Needs dsa_idx_workspace_size(DSA_IDX_OP_DECODE_FP8, 0, B, max_seqlen, topk) bytes. */
+int dsa_idx_decode_fp8(const dsa_idx_bf16 *q, const dsa_idx_bf16 *w, const uint8_t *k8,
+                       const float *k_scale, const int64_t *start, const int32_t *seqlens, int B,
+                       int max_seqlen, int topk, int32_t *idx, float *scores, void *ws,
+                       size_t ws_bytes, void *stream);
 
 #ifdef __cplusplus
 }

@@ -321,6 +321,7 @@ int oracle_pow2_scale_exp(double amax) {
 /* Quantise n vectors of d bf16 values: codes[i][j] = E4M3(x[i][j] / 2^e_i),
  * e_i = oracle_pow2_scale_exp(max_j |x[i][j]|). */
 void oracle_quantize_e4m3(const uint16_t *x, int64_t n, int d, uint8_t *codes, int32_t *exps) {
+#pragma omp parallel for schedule(static)
     for (int64_t i = 0; i < n; ++i) {
         double amax = 0.0;
         for (int j = 0; j < d; ++j) {

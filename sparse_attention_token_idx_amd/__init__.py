@@ -14,12 +14,12 @@ import os
 import torch
 
 __all__ = ["version", "workspace_size", "project", "score_topk", "score_topk_varlen", "decode",
-           "prefill_scores", "prefill_select", "score_row",
+           "prefill_scores", "prefill_select", "score_row", "quantize_keys", "decode_fp8",
            "HEADS", "DIM", "QLAT", "QOUT", "HIDDEN", "MAX_TOPK", "OP_PROJECT", "OP_SCORE_TOPK",
-           "OP_SCORE_TOPK_VARLEN", "OP_DECODE", "DsaIdxError", "lib"]
+           "OP_SCORE_TOPK_VARLEN", "OP_DECODE", "OP_DECODE_FP8", "DsaIdxError", "lib"]
 
 HEADS, DIM, QLAT, QOUT, HIDDEN, MAX_TOPK = 32, 128, 1536, 4096, 7168, 2048
-OP_PROJECT, OP_SCORE_TOPK, OP_SCORE_TOPK_VARLEN, OP_DECODE = 0, 1, 2, 3
+OP_PROJECT, OP_SCORE_TOPK, OP_SCORE_TOPK_VARLEN, OP_DECODE, OP_DECODE_FP8 = 0, 1, 2, 3, 4
 
 _HERE = os.path.dirname(os.path.abspath(__file__))
 LIB_PATH = os.path.join(_HERE, "libdsaidx.so")
@@ -69,6 +69,10 @@ def lib():
         L.dsa_idx_prefill_select.argtypes = [vp, i32, i32, i64, i32, vp, vp, vp, sz, vp]
         L.dsa_idx_decode.restype = i32
         L.dsa_idx_decode.argtypes = [vp, vp, vp, vp, vp, i32, i32, i32, vp, vp, vp, sz, vp]
+        L.dsa_idx_quantize_keys.restype = i32
+        L.dsa_idx_quantize_keys.argtypes = [vp, i64, i64, vp, vp, vp, vp]
+        L.dsa_idx_decode_fp8.restype = i32
+        L.dsa_idx_decode_fp8.argtypes = [vp, vp, vp, vp, vp, vp, i32, i32, i32, vp, vp, vp, sz, vp]
         _lib = L
     return _lib
 
@@ -269,4 +273,52 @@ def decode(q, w, k_cache, start, seqlens, max_seqlen, topk=MAX_TOPK, with_scores
            lib().dsa_idx_decode(_ptr(q), _ptr(w), _ptr(k_cache), _ptr(start), _ptr(seqlens), B,
                                 int(max_seqlen), topk, _ptr(idx), _ptr(sc), _ptr(ws), nbytes,
                                 _stream(stream)))
+    return idx, sc
+
+
+def quantize_keys(k, k8_out=None, scale_out=None, slot=None, stream=None):
+    """FP8 cache rows of bf16 keys k [N,>=128] (unit column stride): codes uint8 [*,128] and
+    scales float32 [*] (powers of two); row slot[i] (int64) or i.  Returns (k8_out, scale_out)."""
+    N = k.shape[0]
+    _need(k, "k", torch.bfloat16, contiguous=False)
+    if k.dim() != 2 or k.stride(1) != 1 or k.shape[1] < DIM:
+        raise ValueError("k must be [N, >=128] with unit column stride")
+    if k8_out is None:
+        k8_out = torch.empty((N, DIM), dtype=torch.uint8, device=k.device)
+        scale_out = torch.empty((N,), dtype=torch.float32, device=k.device)
+    _need(k8_out, "k8_out", torch.uint8)
+    _need(scale_out, "scale_out", torch.float32)
+    if k8_out.dim() != 2 or k8_out.shape[1] != DIM or scale_out.shape[0] != k8_out.shape[0]:
+        raise ValueError("k8_out must be [rows, 128] and scale_out [rows]")
+    if slot is not None:
+        _need(slot, "slot", torch.int64, (N,))
+    elif k8_out.shape[0] < N:
+        raise ValueError("k8_out has fewer than N rows")
+    _check("dsa_idx_quantize_keys",
+           lib().dsa_idx_quantize_keys(_ptr(k), k.stride(0), N, _ptr(slot), _ptr(k8_out),
+                                       _ptr(scale_out), _stream(stream)))
+    return k8_out, scale_out
+
+
+def decode_fp8(q, w, k8_cache, k_scale, start, seqlens, max_seqlen, topk=MAX_TOPK, with_scores=True,
+               ws=None, out=None, stream=None):
+    """As decode, against an FP8 cache: k8_cache uint8 [*,128], k_scale float32 [*]."""
+    B = q.shape[0]
+    _need(q, "q", torch.bfloat16, (B, HEADS, DIM))
+    _need(w, "w", torch.bfloat16, (B, HEADS))
+    _need(k8_cache, "k8_cache", torch.uint8)
+    _need(k_scale, "k_scale", torch.float32)
+    _need(start, "start", torch.int64, (B,))
+    _need(seqlens, "seqlens", torch.int32, (B,))
+    if out is None:
+        idx = torch.empty((B, topk), dtype=torch.int32, device=q.device)
+        sc = torch.empty((B, topk), dtype=torch.float32, device=q.device) if with_scores else None
+    else:
+        idx, sc = out
+    nbytes = workspace_size(OP_DECODE_FP8, 0, B, max_seqlen, topk)
+    ws = _workspace(nbytes, q.device, ws)
+    _check("dsa_idx_decode_fp8",
+           lib().dsa_idx_decode_fp8(_ptr(q), _ptr(w), _ptr(k8_cache), _ptr(k_scale), _ptr(start),
+                                    _ptr(seqlens), B, int(max_seqlen), topk, _ptr(idx), _ptr(sc),
+                                    _ptr(ws), nbytes, _stream(stream)))
     return idx, sc

@@ -99,6 +99,13 @@ size_t ws_score_topk_varlen(int64_t total, int B, int max_seqlen) {
 size_t ws_decode(int B, int max_seqlen) {
     return ws_hdr(B) + (size_t)B * (size_t)dsaidx::decode_row_stride(max_seqlen) * 4u;
 }
+size_t ws_decode_fp8_q8(int B, int max_seqlen) { return round256(ws_decode(B, max_seqlen)); }
+size_t ws_decode_fp8_qw(int B, int max_seqlen) {
+    return ws_decode_fp8_q8(B, max_seqlen) + round256((size_t)B * DSA_IDX_QOUT);
+}
+size_t ws_decode_fp8(int B, int max_seqlen) {
+    return ws_decode_fp8_qw(B, max_seqlen) + (size_t)B * DSA_IDX_HEADS * 4u;
+}
 
 }  // namespace
 
@@ -132,11 +139,12 @@ int dsa_idx_workspace_size(int op, int64_t total_tokens, int B, int max_seqlen, 
             *bytes = ws_score_topk_varlen(total_tokens, B, max_seqlen);
             return ok();
         }
-        case DSA_IDX_OP_DECODE: {
+        case DSA_IDX_OP_DECODE:
+        case DSA_IDX_OP_DECODE_FP8: {
             if (B < 0 || max_seqlen < 0) return fail(DSA_IDX_EINVAL, "B=%d max_seqlen=%d", B, max_seqlen);
             int r = check_topk(topk);
             if (r) return r;
-            *bytes = ws_decode(B, max_seqlen);
+            *bytes = op == DSA_IDX_OP_DECODE ? ws_decode(B, max_seqlen) : ws_decode_fp8(B, max_seqlen);
             return ok();
         }
         default:
@@ -321,6 +329,51 @@ int dsa_idx_decode(const dsa_idx_bf16 *q, const dsa_idx_bf16 *w, const dsa_idx_b
                                          reinterpret_cast<float *>(wsb + ws_hdr(B)), idx, scores,
                                          reinterpret_cast<hipStream_t>(stream));
     if (e != hipSuccess) return hip_fail("decode launch", e);
+    return ok();
+}
+
+int dsa_idx_quantize_keys(const dsa_idx_bf16 *k, int64_t ldk, int64_t N, const int64_t *slot,
+                          uint8_t *k8, float *k_scale, void *stream) {
+    if (N < 0) return fail(DSA_IDX_EINVAL, "N=%lld < 0", (long long)N);
+    if (N == 0) return ok();
+    if (!k || !k8 || !k_scale) return fail(DSA_IDX_EINVAL, "a tensor pointer is NULL");
+    if (ldk < DSA_IDX_DIM || ldk % 8) return fail(DSA_IDX_EINVAL, "ldk=%lld must be >= 128 and a multiple of 8", (long long)ldk);
+    if (!aligned16(k) || !aligned16(k8)) return fail(DSA_IDX_EINVAL, "k and k8 must be 16-byte aligned");
+    if (N > (int64_t)INT32_MAX * 4) return fail(DSA_IDX_EUNSUPPORTED, "N=%lld too large", (long long)N);
+    int r = check_device();
+    if (r) return r;
+    hipError_t e = dsaidx::launch_quantize_keys(k, ldk, N, slot, k8, k_scale, reinterpret_cast<hipStream_t>(stream));
+    if (e != hipSuccess) return hip_fail("quantize_keys launch", e);
+    return ok();
+}
+
+int dsa_idx_decode_fp8(const dsa_idx_bf16 *q, const dsa_idx_bf16 *w, const uint8_t *k8,
+                       const float *k_scale, const int64_t *start, const int32_t *seqlens, int B,
+                       int max_seqlen, int topk, int32_t *idx, float *scores, void *ws,
+                       size_t ws_bytes, void *stream) {
+    if (B < 0 || max_seqlen < 0) return fail(DSA_IDX_EINVAL, "B=%d max_seqlen=%d must be >= 0", B, max_seqlen);
+    int r = check_topk(topk);
+    if (r) return r;
+    if (B == 0) return ok();
+    if (max_seqlen < 1) return fail(DSA_IDX_EINVAL, "max_seqlen must be >= 1");
+    if (!q || !w || !k8 || !k_scale || !start || !seqlens || !idx) return fail(DSA_IDX_EINVAL, "a tensor pointer is NULL");
+    if (!aligned16(q) || !aligned16(w) || !aligned16(k8))
+        return fail(DSA_IDX_EINVAL, "q, w and k8 must be 16-byte aligned");
+    if (B > 65535) return fail(DSA_IDX_EUNSUPPORTED, "B=%d above 65535", B);
+    const size_t need = ws_decode_fp8(B, max_seqlen);
+    if (!ws || ws_bytes < need)
+        return fail(DSA_IDX_EWORKSPACE, "workspace %zu bytes < %zu needed", ws ? ws_bytes : (size_t)0, need);
+    if (!aligned16(ws)) return fail(DSA_IDX_EINVAL, "workspace must be 16-byte aligned");
+    r = check_device();
+    if (r) return r;
+    char *wsb = static_cast<char *>(ws);
+    hipError_t e = dsaidx::launch_decode_fp8(q, w, k8, k_scale, start, seqlens, B, max_seqlen, topk,
+                                             reinterpret_cast<int64_t *>(wsb),
+                                             reinterpret_cast<float *>(wsb + ws_hdr(B)),
+                                             reinterpret_cast<uint8_t *>(wsb + ws_decode_fp8_q8(B, max_seqlen)),
+                                             reinterpret_cast<float *>(wsb + ws_decode_fp8_qw(B, max_seqlen)),
+                                             idx, scores, reinterpret_cast<hipStream_t>(stream));
+    if (e != hipSuccess) return hip_fail("decode_fp8 launch", e);
     return ok();
 }
 

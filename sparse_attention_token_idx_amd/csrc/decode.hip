@@ -152,13 +152,17 @@ int decode_grid() {
 
 }  // namespace
 
+hipError_t launch_decode_prefix(const int32_t *seqlens, int B, int max_seqlen, int64_t *cu, hipStream_t stream) {
+    hipLaunchKernelGGL(decode_prefix_kernel, dim3(1), dim3(1024), 0, stream, seqlens, B, max_seqlen, cu);
+    return hipGetLastError();
+}
+
 hipError_t launch_decode(const uint16_t *q, const uint16_t *w, const uint16_t *k_cache,
                          const int64_t *start, const int32_t *seqlens, int B, int max_seqlen,
                          int topk, int64_t *cu, float *score_buf, int32_t *idx, float *scores,
                          hipStream_t stream) {
     if (B == 0) return hipSuccess;
-    hipLaunchKernelGGL(decode_prefix_kernel, dim3(1), dim3(1024), 0, stream, seqlens, B, max_seqlen, cu);
-    hipError_t e = hipGetLastError();
+    hipError_t e = launch_decode_prefix(seqlens, B, max_seqlen, cu, stream);
     if (e != hipSuccess) return e;
     const int64_t ld = decode_row_stride(max_seqlen);
     DecArgs a{q, w, k_cache, start, cu, B, ld, score_buf};

@@ -49,9 +49,21 @@ hipError_t launch_row_topk_decode(const float *scores, const int32_t *seqlens, i
 __host__ __device__ inline int64_t decode_row_stride(int64_t max_seqlen) {
     return (max_seqlen + 63) / 64 * 64;
 }
+// cu[b] = sum of min(max(seqlens[i], 0), max_seqlen) over i < b, for b = 0 .. B
+hipError_t launch_decode_prefix(const int32_t *seqlens, int B, int max_seqlen, int64_t *cu, hipStream_t stream);
 hipError_t launch_decode(const uint16_t *q, const uint16_t *w, const uint16_t *k_cache,
                          const int64_t *start, const int32_t *seqlens, int B, int max_seqlen,
                          int topk, int64_t *cu, float *score_buf, int32_t *idx, float *scores,
                          hipStream_t stream);
+
+// ---- FP8 key cache (fp8.hip).  Cache rows: 128 E4M3 bytes and one fp32 power-of-two scale.
+hipError_t launch_quantize_keys(const uint16_t *k, int64_t ldk, int64_t N, const int64_t *slot, uint8_t *k8,
+                                float *kscale, hipStream_t stream);
+// Workspace: cu (B + 1 int64) and score_buf as for launch_decode, then q8 [B][32][128] bytes and
+// qw [B][32] fp32.
+hipError_t launch_decode_fp8(const uint16_t *q, const uint16_t *w, const uint8_t *k8, const float *kscale,
+                             const int64_t *start, const int32_t *seqlens, int B, int max_seqlen, int topk,
+                             int64_t *cu, float *score_buf, uint8_t *q8, float *qw, int32_t *idx,
+                             float *scores, hipStream_t stream);
 
 }  // namespace dsaidx

@@ -21,7 +21,7 @@ def dsa():
 
 def declared_functions():
     text = open(HEADER).read()
-    return sorted(set(re.findall(r"\b(dsa_idx_[a-z_]+)\s*\(", text)))
+    return sorted(set(re.findall(r"\b(dsa_idx_[a-z0-9_]+)\s*\(", text)))
 
 
 def test_exports_every_declared_symbol(dsa):
@@ -29,7 +29,8 @@ def test_exports_every_declared_symbol(dsa):
     names = declared_functions()
     assert set(names) == {"dsa_idx_version", "dsa_idx_last_error", "dsa_idx_workspace_size",
                           "dsa_idx_project", "dsa_idx_score_topk", "dsa_idx_score_topk_varlen",
-                          "dsa_idx_prefill_scores", "dsa_idx_prefill_select", "dsa_idx_decode"}
+                          "dsa_idx_prefill_scores", "dsa_idx_prefill_select", "dsa_idx_decode",
+                          "dsa_idx_quantize_keys", "dsa_idx_decode_fp8"}
     for n in names:
         assert getattr(L, n) is not None
 
@@ -59,6 +60,9 @@ def test_workspace_sizes(dsa):
     # multiple of 64 floats
     assert dsa.workspace_size(dsa.OP_DECODE, 0, 64, 131072, 2048) == 768 + 64 * 131072 * 4
     assert dsa.workspace_size(dsa.OP_DECODE, 0, 3, 100, 8) == 256 + 3 * 128 * 4
+    # FP8 decode: the decode workspace, then the quantised queries (3 x 4096 bytes, 256-aligned)
+    # and their folded head weights (3 x 32 fp32)
+    assert dsa.workspace_size(dsa.OP_DECODE_FP8, 0, 3, 100, 8) == 1792 + 12288 + 384
     with pytest.raises(dsa.DsaIdxError) as e:
         dsa.workspace_size(dsa.OP_SCORE_TOPK, 10, topk=0)
     assert e.value.code == -2
@@ -108,6 +112,17 @@ def test_rejections_before_device(dsa):
     assert L.dsa_idx_decode(_vp(A), _vp(A), _vp(A), _vp(A), _vp(A), 4, 100, 8, _vp(A), None, _vp(A),
                             16, None) == -3
     assert L.dsa_idx_decode(None, None, None, None, None, 0, 0, 8, None, None, None, 0, None) == 0
+    # FP8 cache
+    assert L.dsa_idx_quantize_keys(_vp(A), 128, -1, None, _vp(A), _vp(A), None) == -1
+    assert L.dsa_idx_quantize_keys(_vp(A), 100, 4, None, _vp(A), _vp(A), None) == -1
+    assert L.dsa_idx_quantize_keys(_vp(A + 2), 128, 4, None, _vp(A), _vp(A), None) == -1
+    assert L.dsa_idx_quantize_keys(None, 128, 0, None, None, None, None) == 0
+    assert L.dsa_idx_decode_fp8(_vp(A), _vp(A), _vp(A), _vp(A), _vp(A), _vp(A), 4, 100, 0, _vp(A), None,
+                                _vp(A), 1 << 30, None) == -2
+    assert L.dsa_idx_decode_fp8(_vp(A), _vp(A), _vp(A), None, _vp(A), _vp(A), 4, 100, 8, _vp(A), None,
+                                _vp(A), 1 << 30, None) == -1
+    assert L.dsa_idx_decode_fp8(_vp(A), _vp(A), _vp(A), _vp(A), _vp(A), _vp(A), 4, 100, 8, _vp(A), None,
+                                _vp(A), 16, None) == -3
 
 
 def test_project_rejections(dsa):
