@@ -12,6 +12,9 @@ Also reported on the same line:
     MFMA peak, its average duration measured with HIP events on the stream it runs on;
   * the decode leg: 64 sequences with cached bf16 keys of U[32768, 131072] tokens, one
     new query each (project + decode), as HBM GB/s of the decode kernels;
+  * the chunked-prefill leg: the last 4,096 queries of a 1,048,576-token window scored
+    against the whole prefix (dsa_idx_prefill_chunk: scores + select), as queries/s and
+    the scoring flop rate over the whole call;
   * cpu_baseline: the fp64 CPU oracle on a bounded sample of the same workload, with the
     extrapolation to the full layer.
 
@@ -55,6 +58,9 @@ def parse():
     p.add_argument("--no-decode", action="store_true")
     p.add_argument("--no-cpu-baseline", action="store_true")
     p.add_argument("--decode-batch", type=int, default=64)
+    p.add_argument("--no-chunk", action="store_true")
+    p.add_argument("--chunk", type=int, default=4096)
+    p.add_argument("--window", type=int, default=1048576)
     p.add_argument("--calibrate-copy", action="store_true",
                    help="also run a plain 1 GiB device copy (reference for HBM byte counters)")
     return p.parse_args()
@@ -236,6 +242,39 @@ def bench_decode(dsa, args):
                 step_GBps=(dec_bytes + proj_bytes) / ((dec_ms + proj_ms) * 1e-3) / 1e9)
 
 
+def bench_chunk(dsa, args):
+    """The last `chunk` queries of a `window`-token sequence against its whole prefix."""
+    import torch
+    from synth import workloads as wl
+    C, topk = args.chunk, args.topk
+    prefix = args.window - C
+    t0 = time.time()
+    inp = wl.chunk_inputs(prefix, C, seed=2)
+    q, k, w = dev_bf16(inp["q"]), dev_bf16(inp["k"]), dev_bf16(inp["w"])
+    del inp
+    log(f"chunk: prefix {prefix}, C {C}: inputs in {time.time() - t0:.1f}s")
+    idx = torch.empty((C, topk), dtype=torch.int32, device="cuda")
+    sc = torch.empty((C, topk), dtype=torch.float32, device="cuda")
+    ws = torch.empty(dsa.workspace_size(dsa.OP_PREFILL_CHUNK, C, 0, prefix, topk), dtype=torch.uint8,
+                     device="cuda")
+    stream = torch.cuda.current_stream()
+    dsa.prefill_chunk(q, k, w, prefix, topk=topk, ws=ws, out=(idx, sc))
+    torch.cuda.synchronize()
+    n = max(3, min(args.steps, 5))
+    evs = [torch.cuda.Event(enable_timing=True) for _ in range(n + 1)]
+    evs[0].record(stream)
+    for i in range(n):
+        dsa.prefill_chunk(q, k, w, prefix, topk=topk, ws=ws, out=(idx, sc))
+        evs[i + 1].record(stream)
+    torch.cuda.synchronize()
+    ms = float(np.mean([evs[i].elapsed_time(evs[i + 1]) for i in range(n)]))
+    pairs = C * prefix + C * (C + 1) // 2
+    tflops = pairs * SCORE_FLOP_PER_PAIR / (ms * 1e-3) / 1e12
+    log(f"chunk: {ms:.3f} ms per call, {C / (ms * 1e-3):.0f} queries/s, {tflops:.1f} TFLOP/s of scoring")
+    del ws
+    return dict(C=C, prefix=prefix, ms=ms, qps=C / (ms * 1e-3), tflops=tflops, pairs=pairs)
+
+
 def cpu_baseline(args):
     """The oracle on a bounded sample of the T-token layer, extrapolated per its cost model."""
     import oracle
@@ -286,6 +325,7 @@ def main():
         del src, dst
     pre = bench_prefill(dsa, args)
     dec = None if args.no_decode else bench_decode(dsa, args)
+    chk = None if args.no_chunk else bench_chunk(dsa, args)
     ms_step = pre["proj_ms"] + pre["score_ms"] + pre["select_ms"]
     ms_wall = pre["wall"] * 1e3 / args.steps
     qps = args.T / (ms_wall * 1e-3)
@@ -332,6 +372,13 @@ def main():
                           "GBps": round(dec["fp8"]["GBps"], 1),
                           "hbm_frac": round(dec["fp8"]["GBps"] / PEAK_HBM_GBPS, 4),
                           "algorithmic_bytes": dec["fp8"]["bytes"]}},
+        "chunked_prefill": None if chk is None else {
+            "workload": f"last {chk['C']} queries of a {chk['prefix'] + chk['C']}-token window "
+                        f"against the whole prefix, top-{args.topk}: scores + select",
+            "ms": round(chk["ms"], 3), "queries_per_s": round(chk["qps"], 1),
+            "score_tflops_over_call": round(chk["tflops"], 1),
+            "frac_of_bf16_peak": round(chk["tflops"] / PEAK_BF16_TFLOPS, 4),
+            "causal_pairs": chk["pairs"]},
         "cpu_baseline": cpu,
     }
     print(json.dumps(line), flush=True)

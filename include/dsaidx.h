@@ -74,6 +74,7 @@ extern "C" {
 #define DSA_IDX_OP_SCORE_TOPK_VARLEN 2
 #define DSA_IDX_OP_DECODE 3
 #define DSA_IDX_OP_DECODE_FP8 4
+#define DSA_IDX_OP_PREFILL_CHUNK 5
 
 typedef uint16_t dsa_idx_bf16;
 
@@ -96,9 +97,11 @@ const char *dsa_idx_last_error(void);
 
 /* Bytes of workspace an operation needs (host-only, no device access).
  *   op               one of DSA_IDX_OP_*
- *   total_tokens     T for PROJECT and SCORE_TOPK; the packed token count for VARLEN
+ *   total_tokens     T for PROJECT and SCORE_TOPK; the packed token count for VARLEN; the
+ *                    chunk's query count C for PREFILL_CHUNK
  *   B                number of sequences (VARLEN, DECODE); ignored otherwise
- *   max_seqlen       longest sequence (VARLEN, DECODE), keys of the longest cache for DECODE
+ *   max_seqlen       longest sequence (VARLEN, DECODE), keys of the longest cache for DECODE;
+ *                    the cached prefix length for PREFILL_CHUNK
  *   topk             tokens kept per query, 1..2048
  * Writes *bytes (0 is a valid answer).  Returns a status. */
 int dsa_idx_workspace_size(int op, int64_t total_tokens, int B, int max_seqlen, int topk,
@@ -160,6 +163,23 @@ int dsa_idx_prefill_scores(const dsa_idx_bf16 *q, const dsa_idx_bf16 *k, const d
 int dsa_idx_prefill_select(const int32_t *cu_seqlens, int B, int max_seqlen, int64_t total,
                            int topk, int32_t *idx, float *scores, void *ws, size_t ws_bytes,
                            void *stream);
+
+/* Chunked prefill: C new query tokens of one sequence, at positions prefix .. prefix + C - 1,
+ * against the whole causal prefix, the long-context mode in which the indexer scores every
+ * earlier token of the window ("Kimi K3.1 Pro vs Gemma 4 31B" page, long-context row: a
+ * 1,048,576-token window, all of it scored).  Query i scores keys 0 .. prefix + i:
+ *   q [C][32][128], w [C][32]      the chunk's projections
+ *   k [prefix + C][128]            keys of positions 0 .. prefix + C - 1: the cached prefix
+ *                                  followed by the chunk's own keys
+ *   idx [C][topk], scores [C][topk] (may be NULL): row i as prefill row prefix + i of
+ *                                  dsa_idx_score_topk (absolute positions, ascending,
+ *                                  -1 / -inf padded)
+ * prefix = 0 is dsa_idx_score_topk.  Limits: C <= 2,097,120, prefix + C <= 16,777,216.  The
+ * workspace (DSA_IDX_OP_PREFILL_CHUNK, total_tokens = C, max_seqlen = prefix) holds the C
+ * score rows, about 4 C (prefix + C / 2) bytes. */
+int dsa_idx_prefill_chunk(const dsa_idx_bf16 *q, const dsa_idx_bf16 *k, const dsa_idx_bf16 *w,
+                          int64_t C, int64_t prefix, int topk, int32_t *idx, float *scores,
+                          void *ws, size_t ws_bytes, void *stream);
 
 /* Decode: one new query per sequence against that sequence's cached keys.
  *   q [B][32][128], w [B][32]      the new tokens' projections (from dsa_idx_project)

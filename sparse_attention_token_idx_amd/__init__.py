@@ -15,11 +15,13 @@ import torch
 
 __all__ = ["version", "workspace_size", "project", "score_topk", "score_topk_varlen", "decode",
            "prefill_scores", "prefill_select", "score_row", "quantize_keys", "decode_fp8",
-           "HEADS", "DIM", "QLAT", "QOUT", "HIDDEN", "MAX_TOPK", "OP_PROJECT", "OP_SCORE_TOPK",
-           "OP_SCORE_TOPK_VARLEN", "OP_DECODE", "OP_DECODE_FP8", "DsaIdxError", "lib"]
+           "prefill_chunk", "HEADS", "DIM", "QLAT", "QOUT", "HIDDEN", "MAX_TOPK", "OP_PROJECT",
+           "OP_SCORE_TOPK", "OP_SCORE_TOPK_VARLEN", "OP_DECODE", "OP_DECODE_FP8",
+           "OP_PREFILL_CHUNK", "DsaIdxError", "lib"]
 
 HEADS, DIM, QLAT, QOUT, HIDDEN, MAX_TOPK = 32, 128, 1536, 4096, 7168, 2048
 OP_PROJECT, OP_SCORE_TOPK, OP_SCORE_TOPK_VARLEN, OP_DECODE, OP_DECODE_FP8 = 0, 1, 2, 3, 4
+OP_PREFILL_CHUNK = 5
 
 _HERE = os.path.dirname(os.path.abspath(__file__))
 LIB_PATH = os.path.join(_HERE, "libdsaidx.so")
@@ -67,6 +69,8 @@ def lib():
         L.dsa_idx_prefill_scores.argtypes = [vp, vp, vp, vp, i32, i32, i64, vp, sz, vp]
         L.dsa_idx_prefill_select.restype = i32
         L.dsa_idx_prefill_select.argtypes = [vp, i32, i32, i64, i32, vp, vp, vp, sz, vp]
+        L.dsa_idx_prefill_chunk.restype = i32
+        L.dsa_idx_prefill_chunk.argtypes = [vp, vp, vp, i64, i64, i32, vp, vp, vp, sz, vp]
         L.dsa_idx_decode.restype = i32
         L.dsa_idx_decode.argtypes = [vp, vp, vp, vp, vp, i32, i32, i32, vp, vp, vp, sz, vp]
         L.dsa_idx_quantize_keys.restype = i32
@@ -250,6 +254,28 @@ def score_row(ws, t, max_len, B=1, seq_base=0):
     off = seq_base + 8192 * q * (q + 1) + 128 * r * (q + 1)
     rows = ws[hdr + dummy:].view(torch.float32)
     return rows[off:off + t + 1]
+
+
+def prefill_chunk(q, k, w, prefix, topk=MAX_TOPK, with_scores=True, ws=None, out=None,
+                  stream=None):
+    """C query tokens at positions prefix .. prefix + C - 1 against the whole causal prefix:
+    q [C,32,128], w [C,32], k [prefix + C, 128] (the cached keys, then the chunk's own) ->
+    idx [C,topk] int32 (absolute positions), scores [C,topk] float32 (or None)."""
+    C = q.shape[0]
+    _need(q, "q", torch.bfloat16, (C, HEADS, DIM))
+    _need(k, "k", torch.bfloat16, (prefix + C, DIM))
+    _need(w, "w", torch.bfloat16, (C, HEADS))
+    if out is None:
+        idx = torch.empty((C, topk), dtype=torch.int32, device=q.device)
+        sc = torch.empty((C, topk), dtype=torch.float32, device=q.device) if with_scores else None
+    else:
+        idx, sc = out
+    nbytes = workspace_size(OP_PREFILL_CHUNK, C, 0, prefix, topk)
+    ws = _workspace(nbytes, q.device, ws)
+    _check("dsa_idx_prefill_chunk",
+           lib().dsa_idx_prefill_chunk(_ptr(q), _ptr(k), _ptr(w), C, int(prefix), topk, _ptr(idx),
+                                       _ptr(sc), _ptr(ws), nbytes, _stream(stream)))
+    return idx, sc
 
 
 def decode(q, w, k_cache, start, seqlens, max_seqlen, topk=MAX_TOPK, with_scores=True, ws=None,

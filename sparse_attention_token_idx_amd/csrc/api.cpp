@@ -91,6 +91,13 @@ int64_t varlen_score_floats(int64_t total, int B, int64_t max_len) {
 size_t ws_score_topk(int64_t T) {
     return ws_hdr(1) + ws_dummy(T) + 4u * (size_t)dsaidx::tri_row_offset(T);
 }
+// chunk of C query rows at positions prefix .. prefix + C - 1 of one sequence
+size_t ws_prefill_chunk(int64_t C, int64_t prefix) {
+    return ws_hdr(1) + ws_dummy(prefix + C) +
+           4u * (size_t)(dsaidx::tri_row_offset(prefix + C) - dsaidx::tri_row_offset(prefix));
+}
+// Longest sequence (prefix + chunk) a chunked prefill call accepts.
+constexpr int64_t kMaxWindow = 1LL << 24;
 size_t ws_score_topk_varlen(int64_t total, int B, int max_seqlen) {
     return ws_hdr(B) + ws_dummy(max_seqlen) + 4u * (size_t)varlen_score_floats(total, B, max_seqlen);
 }
@@ -137,6 +144,14 @@ int dsa_idx_workspace_size(int op, int64_t total_tokens, int B, int max_seqlen, 
             int r = check_topk(topk);
             if (r) return r;
             *bytes = ws_score_topk_varlen(total_tokens, B, max_seqlen);
+            return ok();
+        }
+        case DSA_IDX_OP_PREFILL_CHUNK: {
+            if (total_tokens < 0 || max_seqlen < 0)
+                return fail(DSA_IDX_EINVAL, "C=%lld prefix=%d must be >= 0", (long long)total_tokens, max_seqlen);
+            int r = check_topk(topk);
+            if (r) return r;
+            *bytes = total_tokens == 0 ? 0 : ws_prefill_chunk(total_tokens, max_seqlen);
             return ok();
         }
         case DSA_IDX_OP_DECODE:
@@ -244,7 +259,7 @@ int dsa_idx_prefill_scores(const dsa_idx_bf16 *q, const dsa_idx_bf16 *k, const d
     if (r) return r;
     const PrefillWs p = prefill_ws(cu_seqlens, B, max_seqlen, total, ws);
     hipError_t e = dsaidx::launch_scores(q, k, w, cu_seqlens, cu_seqlens ? B : 1,
-                                         prefill_max_len(cu_seqlens, max_seqlen, total), total, p.base,
+                                         prefill_max_len(cu_seqlens, max_seqlen, total), total, 0, p.base,
                                          p.rows, p.dummy, reinterpret_cast<hipStream_t>(stream));
     if (e != hipSuccess) return hip_fail("scores launch", e);
     return ok();
@@ -262,7 +277,8 @@ int dsa_idx_prefill_select(const int32_t *cu_seqlens, int B, int max_seqlen, int
     r = check_device();
     if (r) return r;
     const PrefillWs p = prefill_ws(cu_seqlens, B, max_seqlen, total, ws);
-    hipError_t e = dsaidx::launch_row_topk_prefill(p.rows, cu_seqlens, p.base, cu_seqlens ? B : 1, total,
+    hipError_t e = dsaidx::launch_row_topk_prefill(p.rows, cu_seqlens, p.base, cu_seqlens ? B : 1,
+                                                   prefill_max_len(cu_seqlens, max_seqlen, total), 0,
                                                    total, topk, idx, scores,
                                                    reinterpret_cast<hipStream_t>(stream));
     if (e != hipSuccess) return hip_fail("row top-k launch", e);
@@ -302,6 +318,39 @@ int dsa_idx_score_topk_varlen(const dsa_idx_bf16 *q, const dsa_idx_bf16 *k,
     if (r) return r;
     return dsa_idx_prefill_select(cu_seqlens, B, max_seqlen, total, topk, idx, scores, ws, ws_bytes,
                                   stream);
+}
+
+int dsa_idx_prefill_chunk(const dsa_idx_bf16 *q, const dsa_idx_bf16 *k, const dsa_idx_bf16 *w,
+                          int64_t C, int64_t prefix, int topk, int32_t *idx, float *scores,
+                          void *ws, size_t ws_bytes, void *stream) {
+    if (C < 0 || prefix < 0)
+        return fail(DSA_IDX_EINVAL, "C=%lld prefix=%lld must be >= 0", (long long)C, (long long)prefix);
+    int r = check_topk(topk);
+    if (r) return r;
+    if (C == 0) return ok();
+    if (!q || !k || !w || !idx) return fail(DSA_IDX_EINVAL, "a tensor pointer is NULL");
+    if (!aligned16(q) || !aligned16(k) || !aligned16(w))
+        return fail(DSA_IDX_EINVAL, "q, k and w must be 16-byte aligned");
+    if (C > kMaxSeq) return fail(DSA_IDX_EUNSUPPORTED, "C=%lld above %lld", (long long)C, (long long)kMaxSeq);
+    if (prefix + C > kMaxWindow)
+        return fail(DSA_IDX_EUNSUPPORTED, "prefix + C = %lld above %lld", (long long)(prefix + C),
+                    (long long)kMaxWindow);
+    const size_t need = ws_prefill_chunk(C, prefix);
+    if (!ws || ws_bytes < need)
+        return fail(DSA_IDX_EWORKSPACE, "workspace %zu bytes < %zu needed", ws ? ws_bytes : (size_t)0, need);
+    if (!aligned16(ws)) return fail(DSA_IDX_EINVAL, "workspace must be 16-byte aligned");
+    r = check_device();
+    if (r) return r;
+    char *wsb = static_cast<char *>(ws);
+    int64_t *base = reinterpret_cast<int64_t *>(wsb);
+    float *dummy = reinterpret_cast<float *>(wsb + ws_hdr(1));
+    float *rows = reinterpret_cast<float *>(wsb + ws_hdr(1) + ws_dummy(prefix + C));
+    const hipStream_t st = reinterpret_cast<hipStream_t>(stream);
+    hipError_t e = dsaidx::launch_scores(q, k, w, nullptr, 1, C, C, prefix, base, rows, dummy, st);
+    if (e != hipSuccess) return hip_fail("scores launch", e);
+    e = dsaidx::launch_row_topk_prefill(rows, nullptr, base, 1, C, prefix, C, topk, idx, scores, st);
+    if (e != hipSuccess) return hip_fail("row top-k launch", e);
+    return ok();
 }
 
 int dsa_idx_decode(const dsa_idx_bf16 *q, const dsa_idx_bf16 *w, const dsa_idx_bf16 *k_cache,

@@ -26,20 +26,24 @@ hipError_t launch_project(const uint16_t *x, int64_t ldx, const uint16_t *c_q, i
                           float eps, uint16_t *q, uint16_t *k_base, const int64_t *k_slot,
                           uint16_t *w, float *ws, hipStream_t stream);
 
-// ---- prefill scores (scores.hip).  cu_seqlens == nullptr -> one sequence of length T.
-// seq_base: B + 1 int64 (written here for varlen), out: triangular rows, dummy: a row of
-// kRowQuant * ceil(max_len / kRowQuant) floats that absorbs the stores of rows past a
-// sequence end.
+// ---- prefill scores (scores.hip).  cu_seqlens == nullptr -> one sequence of T query rows
+// at positions pos0 .. pos0 + T - 1 (keys 0 .. pos0 + T - 1 of k); ragged batches start at
+// position 0.  seq_base: B + 1 int64 (written here for varlen), out: triangular rows (row t
+// at tri_row_offset(t) - tri_row_offset(pos0)), dummy: a row of kRowQuant * ceil((pos0 +
+// max_len) / kRowQuant) floats that absorbs the stores of rows past a sequence end and past
+// a row's own last key tile.
 hipError_t launch_scores(const uint16_t *q, const uint16_t *k, const uint16_t *w,
-                         const int32_t *cu_seqlens, int B, int64_t max_len, int64_t T,
+                         const int32_t *cu_seqlens, int B, int64_t max_len, int64_t T, int64_t pos0,
                          int64_t *seq_base, float *out, float *dummy, hipStream_t stream);
 
-// ---- row top-k (topk.hip).  Prefill: rows = T (dense) or the packed total (varlen), scores
-// in the triangular layout.  Decode: B rows of stride ld (a multiple of 4), row b holding
-// seqlens[b] scores.
+// ---- row top-k (topk.hip).  Prefill: rows = T (dense, query row g at position pos0 + g)
+// or the packed total (varlen, longest sequence max_len), scores in the triangular layout of
+// launch_scores.  Decode: B rows of stride ld (a multiple of 4), row b holding seqlens[b]
+// scores.
 hipError_t launch_row_topk_prefill(const float *scores, const int32_t *cu_seqlens,
-                                   const int64_t *seq_base, int B, int64_t T, int64_t rows,
-                                   int topk, int32_t *idx, float *out_scores, hipStream_t stream);
+                                   const int64_t *seq_base, int B, int64_t max_len, int64_t pos0,
+                                   int64_t rows, int topk, int32_t *idx, float *out_scores,
+                                   hipStream_t stream);
 hipError_t launch_row_topk_decode(const float *scores, const int32_t *seqlens, int B, int64_t ld,
                                   int64_t nmax, int topk, int32_t *idx, float *out_scores,
                                   hipStream_t stream);

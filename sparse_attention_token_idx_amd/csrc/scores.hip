@@ -49,6 +49,8 @@ struct ScoreArgs {
     const int32_t *cu_seqlens;  // nullptr: one sequence of length T
     const int64_t *seq_base;    // start of each sequence's rows in `out` (varlen)
     int64_t T;
+    int64_t pos0;               // one sequence: position of its first query row; its keys are
+                                // rows 0 .. pos0 + T - 1 of k (0 for ragged batches)
     int nrb;                    // grid.y: row blocks of the longest sequence
     float *out;                 // triangular score rows
     float *dummy;               // write target of rows past a sequence end
@@ -94,7 +96,12 @@ __global__ __launch_bounds__(kThreads, 1) void score_rows_kernel(ScoreArgs a) {
     const int64_t r0 = (int64_t)rb * kBQ;
     if (r0 >= L) return;
     const int rows_here = (int)(L - r0 < kBQ ? L - r0 : kBQ);
-    const int nkt = (int)(r0 / kBK) + 1;          // every row of the block: keys < kBK * nkt
+    // rows r0 .. r0 + rows_here - 1 sit at positions p0 + r0 .. ; the block streams the key
+    // tiles of its last row, and a row whose own last tile comes earlier sends the rest of
+    // its stores to the dummy row (only when p0 is not a multiple of kBQ)
+    const int64_t p0 = a.pos0;
+    const int64_t nkeys = p0 + L;
+    const int nkt = (int)((p0 + r0 + rows_here - 1) / kBK) + 1;
 
     const int tid = threadIdx.x;
     const int wave = tid >> 6, lane = tid & 63;
@@ -135,11 +142,15 @@ __global__ __launch_bounds__(kThreads, 1) void score_rows_kernel(ScoreArgs a) {
     }
     // this lane's output row; rows past the end write to the dummy row, so that every store
     // is issued (a conditional store would make each later wait on a load wait for it too)
+    float *const drow = a.dummy + 8 * l16;
     float *orow;
+    int row_nt;                          // key tiles of this lane's row
     {
         const int row = 4 * wave + lg;
-        orow = row < rows_here ? a.out + base + tri_row_offset(r0 + row) : a.dummy;
-        orow += 8 * l16;
+        const int64_t pos = p0 + r0 + row;
+        const bool ok = row < rows_here;
+        orow = ok ? a.out + base + tri_row_offset(pos) - tri_row_offset(p0) + 8 * l16 : drow;
+        row_nt = ok ? (int)(pos / kBK) + 1 : nkt;
     }
 
     // ---- key staging: wave w stages keys 16w .. 16w + 15 of every tile, lane -> key
@@ -149,7 +160,7 @@ __global__ __launch_bounds__(kThreads, 1) void score_rows_kernel(ScoreArgs a) {
     u32x4 kv[4];
     auto load_k = [&](int kt) {
         int64_t s = (int64_t)kt * kBK + sk;
-        s = s < L ? s : L - 1;
+        s = s < nkeys ? s : nkeys - 1;
         const uint16_t *src = a.k + (seq_start + s) * kDim + sd;
 #pragma unroll
         for (int j = 0; j < 4; ++j) kv[j] = *reinterpret_cast<const u32x4 *>(src + 8 * j);
@@ -236,8 +247,9 @@ __global__ __launch_bounds__(kThreads, 1) void score_rows_kernel(ScoreArgs a) {
         signal(&sm.k_used[wave]);             // every read of key slot t % kKR is done
         // one store and one load per tile, unconditionally and in this order, so that the
         // wait for the load in the next tile never has to include a store
-        *reinterpret_cast<f32x4 *>(orow + (int64_t)t * kBK) = f32x4{sc[0], sc[1], sc[2], sc[3]};
-        *reinterpret_cast<f32x4 *>(orow + (int64_t)t * kBK + 4) = f32x4{sc[4], sc[5], sc[6], sc[7]};
+        float *const dst = (t < row_nt ? orow : drow) + (int64_t)t * kBK;
+        *reinterpret_cast<f32x4 *>(dst) = f32x4{sc[0], sc[1], sc[2], sc[3]};
+        *reinterpret_cast<f32x4 *>(dst + 4) = f32x4{sc[4], sc[5], sc[6], sc[7]};
         // stage tile t + kKR - 2 into the slot of tile t - 2 once every wave is done with it
         // (so waves may drift up to two tiles apart); its loads were issued a tile earlier
         const int u = t + kKR - 2;
@@ -277,7 +289,7 @@ __global__ __launch_bounds__(1024) void seq_base_kernel(const int32_t *cu_seqlen
 }  // namespace
 
 hipError_t launch_scores(const uint16_t *q, const uint16_t *k, const uint16_t *w,
-                         const int32_t *cu_seqlens, int B, int64_t max_len, int64_t T,
+                         const int32_t *cu_seqlens, int B, int64_t max_len, int64_t T, int64_t pos0,
                          int64_t *seq_base, float *out, float *dummy, hipStream_t stream) {
     static bool attr_done = false;
     const size_t smem = sizeof(ScoreSmem);
@@ -300,6 +312,7 @@ hipError_t launch_scores(const uint16_t *q, const uint16_t *k, const uint16_t *w
     a.cu_seqlens = cu_seqlens;
     a.seq_base = seq_base;
     a.T = T;
+    a.pos0 = cu_seqlens ? 0 : pos0;
     a.nrb = (int)((max_len + kBQ - 1) / kBQ);
     a.out = out;
     a.dummy = dummy;

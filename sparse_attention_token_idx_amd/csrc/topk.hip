@@ -38,11 +38,16 @@ namespace {
 // (the register path and the full-row passes).
 constexpr int kPer = 16;                        // keys per thread per chunk
 constexpr int kWChunk = 64 * kPer;              // 1,024: one wave's chunk in the streaming pass
-constexpr int kSample = 4096;                   // sampled keys of a long row (first 256 threads)
-constexpr int kCand = 4096;                     // candidate list capacity
-constexpr int kMaxRun = 512;                    // chunk runs: rows of up to 512K keys
+// candidate list capacity: one kPer group per thread
+template <int W> constexpr int kCand = kPer * 64 * W;
+// chunk runs: rows of up to 512K keys (W = 4) or 1M keys (W = 16)
+template <int W> constexpr int kMaxRun = W <= 4 ? 512 : 1024;
+// sample of a long row: 64 blocks of 64 scores (W = 4); W = 16 takes up to 256 blocks on
+// rows long enough for them to stay a small share of the row
+template <int W> constexpr int kSampleBlocks = W <= 4 ? 64 : 256;
 constexpr int kPrefetch = 2;                    // wave chunks in flight ahead of the current
 constexpr int kRankMax = 128;                   // keys of the threshold bin ranked directly
+constexpr int64_t kLongRow = 65536;             // longest prefill row of the 4-wave variant
 
 // Histogram bins (digits of kDigit<W> bits): 512 for the 4-wave prefill workgroups, whose
 // LDS footprint sets how many rows a CU holds, 1,024 for the 16-wave decode ones.
@@ -50,17 +55,19 @@ template <int W> constexpr int kDigit = W <= 4 ? 9 : 10;
 template <int W> constexpr int kBins = 1 << kDigit<W>;
 // bins owned by a thread in a histogram scan
 template <int W> constexpr int kBinsPer = kBins<W> / (64 * W);
-static_assert(kBinsPer<4> >= 1 && kBinsPer<16> >= 1 && kMaxRun <= 2 * 64 * 4,
-              "thread ownership of bins and runs");
+static_assert(kBinsPer<4> >= 1 && kBinsPer<16> >= 1 && kMaxRun<4> <= 2 * 64 * 4 &&
+              kMaxRun<16> <= 2 * 64 * 16, "thread ownership of bins and runs");
+static_assert(kSampleBlocks<4> * 4 <= 64 * 4 && kSampleBlocks<16> * 4 <= 64 * 16,
+              "four threads per sample block");
 
 template <int W> struct TopkSmem {
     union {
         struct {                   // a candidate: its key and its offset in its chunk
-            uint32_t key[kCand];
-            uint16_t off[kCand];
+            uint32_t key[kCand<W>];
+            uint16_t off[kCand<W>];
         } cand;
         struct {                   // emission: list prefix counts, staged output
-            uint16_t pre[kCand];
+            uint16_t pre[kCand<W>];
             int32_t out_idx[kMaxTopk];
             float out_score[kMaxTopk];
         } emit;
@@ -73,9 +80,9 @@ template <int W> struct TopkSmem {
             uint16_t slot[kRankMax];
         } bin;
     };
-    uint32_t run[kMaxRun];         // start | length << 16 of each chunk's run in the list
-    uint32_t rlog[kMaxRun];        // chunk | start << 16 of each run, in list order
-    uint32_t win[kCand / 32];      // ranked-in keys of the threshold bin, by list slot
+    uint32_t run[kMaxRun<W>];      // start | length << 16 of each chunk's run in the list
+    uint32_t rlog[kMaxRun<W>];     // chunk | start << 16 of each run, in list order
+    uint32_t win[kCand<W> / 32];   // ranked-in keys of the threshold bin, by list slot
     uint32_t count;                // candidates reserved so far | runs reserved << 16
     uint32_t nbin;                 // keys gathered from the threshold bin
     int32_t wsum[W];
@@ -84,13 +91,16 @@ template <int W> struct TopkSmem {
 };
 
 static_assert(sizeof(TopkSmem<4>) <= 32 * 1024, "five workgroups of 4 waves per CU");
-static_assert(kMaxRun <= kBins<4> && kMaxRun <= kBins<16>, "per-run emission data lives in hist");
+static_assert(kMaxRun<4> <= kBins<4> && kMaxRun<16> <= kBins<16>, "per-run emission data lives in hist");
+static_assert(kCand<16> <= 65536, "list positions are 16-bit");
 
 struct TopkArgs {
     const float *scores;
     int mode;                      // 0: prefill rows (triangular), 1: decode rows
     const int32_t *cu_seqlens;     // prefill varlen (nullptr: one sequence of length T)
     const int64_t *seq_base;
+    int64_t pos0;                  // prefill, one sequence: position of query row 0
+    int64_t g0;                    // first row of this launch
     int B;
     const int32_t *seqlens;        // decode: row b holds seqlens[b] (clamped to nmax) scores
     int64_t ld;                    // decode: row stride (a multiple of 4)
@@ -323,7 +333,7 @@ __device__ void emit_winners(const uint32_t (&key)[kPer], const int32_t (&idx)[k
 // Row g's scores and their number.
 __device__ __forceinline__ void locate_row(const TopkArgs &a, int64_t g, const float *&row, int64_t &n) {
     if (a.mode == 0) {
-        int64_t t = g, base = 0;
+        int64_t t = a.pos0 + g, base = -tri_row_offset(a.pos0);
         if (a.cu_seqlens) {
             int lo = 0, hi = a.B - 1;   // last sequence with cu_seqlens[i] <= g
             while (lo < hi) {
@@ -356,17 +366,16 @@ __device__ __forceinline__ void load16(const float *row, int64_t n, int64_t e0, 
     }
 }
 
-// The sample of a long row: 64 blocks of 64 consecutive scores spread over the row; thread t
-// reads quarter t % 4 of block t / 4.
-__device__ __forceinline__ void load_sample(const float *row, int64_t n, uint32_t (&key)[kPer]) {
+// The sample of a long row: nblk blocks of 64 consecutive scores spread over the row (n >
+// 64 nblk); thread t reads quarter t % 4 of block t / 4.
+__device__ __forceinline__ void load_sample(const float *row, int64_t n, int nblk, uint32_t (&key)[kPer]) {
     const int tid = (int)threadIdx.x;
-    if (tid >= kSample / kPer) {
+    if (tid >= 4 * nblk) {
 #pragma unroll
         for (int i = 0; i < kPer; ++i) key[i] = 0u;
         return;
     }
-    constexpr int kBlocks = kSample / 64;
-    const int64_t start = ((int64_t)(tid >> 2) * (n - 64) / (kBlocks - 1)) & ~(int64_t)3;
+    const int64_t start = ((int64_t)(tid >> 2) * (n - 64) / (nblk - 1)) & ~(int64_t)3;
     load16(row, n, start + 16 * (tid & 3), key);
 }
 
@@ -375,7 +384,7 @@ template <int W>
 __global__ __launch_bounds__(64 * W, W == 4 ? 5 : 16 / W) void row_topk_kernel(TopkArgs a) {
     constexpr int kChunk = 64 * W * kPer;   // keys of the register path / one full-row pass step
     __shared__ TopkSmem<W> sm;
-    const int64_t g = blockIdx.x;
+    const int64_t g = a.g0 + (int64_t)blockIdx.x;
     const int topk = a.topk;
     const int tid = (int)threadIdx.x;
     const int lane = tid & 63, wave = tid >> 6;
@@ -417,20 +426,29 @@ __global__ __launch_bounds__(64 * W, W == 4 ? 5 : 16 / W) void row_topk_kernel(T
     // it, so they arrive while theta0 is placed.
 #pragma unroll
     for (int j = 0; j < kBinsPer<W>; ++j) sm.hist[kBinsPer<W> * tid + j] = 0u;
-    if (tid < kCand / 32) sm.win[tid] = 0u;
+    if (tid < kCand<W> / 32) sm.win[tid] = 0u;
     if (tid == 0) {
         sm.count = 0u;
         sm.nbin = 0u;
     }
-    load_sample(row, n, key);
+    // sample blocks: 64, or on long rows of the 16-wave variant one per 4,096 scores
+    int nblk = 64;
+    if (W > 4) {
+        const int64_t b = n >> 12;
+        nblk = b < 64 ? 64 : (b > kSampleBlocks<W> ? kSampleBlocks<W> : (int)b);
+    }
+    const int ns = 64 * nblk;   // sampled scores
+    load_sample(row, n, nblk, key);
     const int64_t nwc = (n + kWChunk - 1) / kWChunk;   // wave chunks
     uint32_t buf[kPrefetch][kPer];
 #pragma unroll
     for (int p = 0; p < kPrefetch; ++p) load16(row, n, (int64_t)(wave + W * p) * kWChunk + kPer * lane, buf[p]);
 
-    // r such that about 1.4 topk keys of the row reach the r-th largest of the sample
-    int r = (int)(((int64_t)topk * 7 * kSample + (int64_t)5 * n - 1) / ((int64_t)5 * n)) + 8;
-    if (r > kSample) r = kSample;
+    // r such that about f topk keys of the row reach the r-th largest of the sample: f = 1.4
+    // with 4 waves, 2 with 16 (whose list holds 16,384 candidates)
+    constexpr int64_t kNum = W <= 4 ? 7 : 2, kDen = W <= 4 ? 5 : 1;
+    int r = (int)(((int64_t)topk * kNum * ns + kDen * n - 1) / (kDen * n)) + 8;
+    if (r > ns) r = ns;
     uint32_t theta0, top;
     {
         uint32_t m = 0;
@@ -509,7 +527,7 @@ __global__ __launch_bounds__(64 * W, W == 4 ? 5 : 16 / W) void row_topk_kernel(T
 
     // ---- streaming pass, every wave on its own: compact the keys >= theta0 of wave chunk c
     // into a run of the candidate list, in index order (no workgroup barrier until the end)
-    const bool runs_fit = nwc <= kMaxRun;
+    const bool runs_fit = nwc <= kMaxRun<W>;
     uint32_t cmax = 0;
 #pragma unroll 1
     for (int64_t c = wave; c < nwc; c += W) {
@@ -536,7 +554,7 @@ __global__ __launch_bounds__(64 * W, W == 4 ? 5 : 16 / W) void row_topk_kernel(T
         if (lane == 0) res = atomicAdd(&sm.count, (uint32_t)total | 0x10000u);
         res = (uint32_t)__builtin_amdgcn_readfirstlane((int)res);
         const uint32_t start = res & 0xFFFFu;
-        if (start + (uint32_t)total > (uint32_t)kCand || !runs_fit) break;   // wave-uniform
+        if (start + (uint32_t)total > (uint32_t)kCand<W> || !runs_fit) break;   // wave-uniform
         if (lane == 0) {
             sm.run[c] = start | ((uint32_t)total << 16);
             sm.rlog[res >> 16] = (uint32_t)c | (start << 16);
@@ -558,7 +576,7 @@ __global__ __launch_bounds__(64 * W, W == 4 ? 5 : 16 / W) void row_topk_kernel(T
     const int nres = (int)(sm.count >> 16);
 
     int need = topk;
-    if (runs_fit && count >= topk && count <= kCand) {
+    if (runs_fit && count >= topk && count <= kCand<W>) {
         // ---- select among the candidates: thread t holds list entries 16t .. 16t+15
         // the run (and so the chunk) of list entry 16t: the last run starting at or below it
         // (runs are logged in list order; an empty run starts where the next one does)
@@ -678,21 +696,41 @@ __global__ __launch_bounds__(64 * W, W == 4 ? 5 : 16 / W) void row_topk_kernel(T
 }  // namespace
 
 hipError_t launch_row_topk_prefill(const float *scores, const int32_t *cu_seqlens,
-                                   const int64_t *seq_base, int B, int64_t T, int64_t rows,
-                                   int topk, int32_t *idx, float *out_scores, hipStream_t stream) {
-    (void)T;
+                                   const int64_t *seq_base, int B, int64_t max_len, int64_t pos0,
+                                   int64_t rows, int topk, int32_t *idx, float *out_scores,
+                                   hipStream_t stream) {
     if (rows == 0) return hipSuccess;
     TopkArgs a{};
     a.scores = scores;
     a.mode = 0;
     a.cu_seqlens = cu_seqlens;
     a.seq_base = seq_base;
+    a.pos0 = cu_seqlens ? 0 : pos0;
     a.B = B;
     a.topk = topk;
     a.out_idx = idx;
     a.out_score = out_scores;
-    hipLaunchKernelGGL(row_topk_kernel<4>, dim3((unsigned)rows), dim3(256), 0, stream, a);
-    return hipGetLastError();
+    // rows of up to kLongRow scores: 4-wave workgroups; longer rows: the 16-wave variant
+    // (ragged batches take one variant for all rows, from the longest sequence)
+    int64_t g1 = rows;
+    if (cu_seqlens) {
+        g1 = max_len > kLongRow ? 0 : rows;
+    } else {
+        g1 = kLongRow - a.pos0;
+        g1 = g1 < 0 ? 0 : (g1 > rows ? rows : g1);
+    }
+    if (g1 > 0) {
+        a.g0 = 0;
+        hipLaunchKernelGGL(row_topk_kernel<4>, dim3((unsigned)g1), dim3(256), 0, stream, a);
+        hipError_t e = hipGetLastError();
+        if (e != hipSuccess) return e;
+    }
+    if (g1 < rows) {
+        a.g0 = g1;
+        hipLaunchKernelGGL(row_topk_kernel<16>, dim3((unsigned)(rows - g1)), dim3(1024), 0, stream, a);
+        return hipGetLastError();
+    }
+    return hipSuccess;
 }
 
 hipError_t launch_row_topk_decode(const float *scores, const int32_t *seqlens, int B, int64_t ld,

@@ -37,19 +37,23 @@ def lib():
         u64, i64, f64 = ctypes.c_uint64, ctypes.c_int64, ctypes.c_double
         vp = ctypes.c_void_p
         L.synth_normal_bf16.argtypes = [u64, u64, u64, f64, f64, i64, vp]
+        L.synth_normal_bf16_range.argtypes = [u64, u64, u64, f64, f64, i64, i64, vp]
         L.synth_uniform_f64.argtypes = [u64, u64, u64, i64, vp]
         L.synth_uniform_int.argtypes = [u64, u64, u64, i64, i64, i64, vp]
-        for f in (L.synth_normal_bf16, L.synth_uniform_f64, L.synth_uniform_int):
+        for f in (L.synth_normal_bf16, L.synth_normal_bf16_range, L.synth_uniform_f64,
+                  L.synth_uniform_int):
             f.restype = None
         _lib = L
     return _lib
 
 
-def normal_bf16(shape, mean, var, tensor, layer=0, seed=0):
-    """bf16 bit patterns (uint16) of N(mean, var) samples; ``var`` is the variance."""
+def normal_bf16(shape, mean, var, tensor, layer=0, seed=0, first=0):
+    """bf16 bit patterns (uint16) of N(mean, var) samples; ``var`` is the variance.  The
+    samples are elements first, first + 1, ... of the stream, so a slice of a large tensor
+    can be drawn on its own."""
     out = np.empty(shape, dtype=np.uint16)
-    lib().synth_normal_bf16(seed, tensor, layer, float(mean), float(np.sqrt(var)), out.size,
-                            out.ctypes.data)
+    lib().synth_normal_bf16_range(seed, tensor, layer, float(mean), float(np.sqrt(var)),
+                                  int(first), out.size, out.ctypes.data)
     return out
 
 

@@ -45,20 +45,29 @@ static uint16_t narrow_bf16(double v) {
     return (uint16_t)(u >> 16);
 }
 
-/* out[i] = bf16(mean + std * N_i), N_i standard normal, i in [0, n). */
-void synth_normal_bf16(uint64_t seed, uint64_t tensor, uint64_t layer, double mean, double std,
-                       int64_t n, uint16_t *out) {
+/* out[i] = bf16(mean + std * N_{first + i}), N_j standard normal, i in [0, n): elements
+ * first .. first + n - 1 of the stream (pair p of Box-Muller gives elements 2p and 2p + 1). */
+void synth_normal_bf16_range(uint64_t seed, uint64_t tensor, uint64_t layer, double mean,
+                             double std, int64_t first, int64_t n, uint16_t *out) {
     const uint64_t key = stream_key(seed, tensor, layer);
     const double two_pi = 6.283185307179586476925286766559;
+    const int64_t p0 = first / 2, p1 = (first + n + 1) / 2;
 #pragma omp parallel for schedule(static)
-    for (int64_t p = 0; p < (n + 1) / 2; ++p) {
+    for (int64_t p = p0; p < p1; ++p) {
         double u1 = unif53(key, 2 * (uint64_t)p);
         double u2 = unif53(key, 2 * (uint64_t)p + 1);
         double r = sqrt(-2.0 * log(1.0 - u1));
         double a = two_pi * u2;
-        out[2 * p] = narrow_bf16(mean + std * r * cos(a));
-        if (2 * p + 1 < n) out[2 * p + 1] = narrow_bf16(mean + std * r * sin(a));
+        const int64_t e = 2 * p - first;
+        if (e >= 0 && e < n) out[e] = narrow_bf16(mean + std * r * cos(a));
+        if (e + 1 >= 0 && e + 1 < n) out[e + 1] = narrow_bf16(mean + std * r * sin(a));
     }
+}
+
+/* out[i] = bf16(mean + std * N_i), i in [0, n). */
+void synth_normal_bf16(uint64_t seed, uint64_t tensor, uint64_t layer, double mean, double std,
+                       int64_t n, uint16_t *out) {
+    synth_normal_bf16_range(seed, tensor, layer, mean, std, 0, n, out);
 }
 
 /* out[i] uniform in [0, 1) (53-bit), i in [0, n). */

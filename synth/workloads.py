@@ -22,6 +22,15 @@ def score_inputs(T, seed=0, layer=0):
                 w=normal_bf16((T, H), 0.0, 0.1, W, layer, seed))
 
 
+def chunk_inputs(prefix, C, seed=0, layer=0):
+    """Chunked prefill: the queries and head weights of positions prefix .. prefix + C - 1
+    and the keys of positions 0 .. prefix + C - 1, the same values as
+    score_inputs(T)[...][prefix : prefix + C] (q, w) and [: prefix + C] (k) for any larger T."""
+    return dict(q=normal_bf16((C, H, D), 0.0, 1.0, Q, layer, seed, first=prefix * H * D),
+                k=normal_bf16((prefix + C, D), 0.0, 1.0, K, layer, seed),
+                w=normal_bf16((C, H), 0.0, 0.1, W, layer, seed, first=prefix * H))
+
+
 def layer_weights(layer=0, seed=0):
     """One indexer layer: W_q ~N(0,1/1536), W_k, W_w ~N(0,1/7168), gamma ~1+N(0,0.02), beta ~N(0,0.02)."""
     return dict(W_q=normal_bf16((QLAT, QOUT), 0.0, 1.0 / QLAT, WQ, layer, seed),

@@ -30,7 +30,7 @@ def test_exports_every_declared_symbol(dsa):
     assert set(names) == {"dsa_idx_version", "dsa_idx_last_error", "dsa_idx_workspace_size",
                           "dsa_idx_project", "dsa_idx_score_topk", "dsa_idx_score_topk_varlen",
                           "dsa_idx_prefill_scores", "dsa_idx_prefill_select", "dsa_idx_decode",
-                          "dsa_idx_quantize_keys", "dsa_idx_decode_fp8"}
+                          "dsa_idx_quantize_keys", "dsa_idx_decode_fp8", "dsa_idx_prefill_chunk"}
     for n in names:
         assert getattr(L, n) is not None
 
@@ -63,6 +63,13 @@ def test_workspace_sizes(dsa):
     # FP8 decode: the decode workspace, then the quantised queries (3 x 4096 bytes, 256-aligned)
     # and their folded head weights (3 x 32 fp32)
     assert dsa.workspace_size(dsa.OP_DECODE_FP8, 0, 3, 100, 8) == 1792 + 12288 + 384
+    # chunked prefill: header, a dummy row of 128*ceil((prefix + C)/128) floats, and rows
+    # prefix .. prefix + C - 1 of the triangular layout
+    assert dsa.workspace_size(dsa.OP_PREFILL_CHUNK, 300, 0, 1000, 8) == \
+        256 + r256(4 * 1408) + 4 * (tri(1300) - tri(1000))
+    assert dsa.workspace_size(dsa.OP_PREFILL_CHUNK, 1000, 0, 0, 8) == \
+        dsa.workspace_size(dsa.OP_SCORE_TOPK, 1000, topk=8)
+    assert dsa.workspace_size(dsa.OP_PREFILL_CHUNK, 0, 0, 5000, 8) == 0
     with pytest.raises(dsa.DsaIdxError) as e:
         dsa.workspace_size(dsa.OP_SCORE_TOPK, 10, topk=0)
     assert e.value.code == -2
@@ -123,6 +130,18 @@ def test_rejections_before_device(dsa):
                                 _vp(A), 1 << 30, None) == -1
     assert L.dsa_idx_decode_fp8(_vp(A), _vp(A), _vp(A), _vp(A), _vp(A), _vp(A), 4, 100, 8, _vp(A), None,
                                 _vp(A), 16, None) == -3
+    # chunked prefill
+    chunk = lambda *a: L.dsa_idx_prefill_chunk(*a)
+    assert chunk(_vp(A), _vp(A), _vp(A), 10, 100, 0, _vp(A), None, _vp(A), 1 << 30, None) == -2
+    assert chunk(_vp(A), _vp(A), _vp(A), -1, 100, 8, _vp(A), None, _vp(A), 1 << 30, None) == -1
+    assert chunk(_vp(A), _vp(A), _vp(A), 10, -1, 8, _vp(A), None, _vp(A), 1 << 30, None) == -1
+    assert chunk(_vp(A), None, _vp(A), 10, 100, 8, _vp(A), None, _vp(A), 1 << 30, None) == -1
+    assert chunk(_vp(A), _vp(A + 8), _vp(A), 10, 100, 8, _vp(A), None, _vp(A), 1 << 30, None) == -1
+    assert chunk(_vp(A), _vp(A), _vp(A), 10, 100, 8, _vp(A), None, _vp(A), 16, None) == -3
+    assert chunk(_vp(A), _vp(A), _vp(A), 4096, (1 << 24) - 4095, 8, _vp(A), None, _vp(A), 1 << 62,
+                 None) == -2
+    assert b"prefix + C" in L.dsa_idx_last_error()
+    assert chunk(None, None, None, 0, 100, 8, None, None, None, 0, None) == 0
 
 
 def test_project_rejections(dsa):

@@ -27,6 +27,18 @@ def test_prefix_property():
     assert np.array_equal(a, b[:999])
 
 
+def test_range_is_a_slice_of_the_stream():
+    full = synth.normal_bf16((5001,), 0.0, 1.0, synth.Q, 2, 3)
+    for first, n in [(0, 10), (1, 10), (2, 7), (999, 1002), (4990, 11), (5000, 1)]:
+        part = synth.normal_bf16((n,), 0.0, 1.0, synth.Q, 2, 3, first=first)
+        assert np.array_equal(part, full[first:first + n])
+    c = wl.chunk_inputs(300, 77, seed=4)
+    s = wl.score_inputs(400, seed=4)
+    assert np.array_equal(c["q"], s["q"][300:377])
+    assert np.array_equal(c["w"], s["w"][300:377])
+    assert np.array_equal(c["k"], s["k"][:377])
+
+
 def test_moments_variance_convention():
     n = 400_000
     z = _f(synth.normal_bf16((n,), 0.0, 0.1, synth.W))
