@@ -31,6 +31,8 @@ constexpr int kWaves = 8;             // 4 rows each
 constexpr int kThreads = 64 * kWaves;
 constexpr int kKR = 4;                // key tiles in the LDS ring
 constexpr int kKStride = kDim + 8;    // bf16 per key row in LDS (272 B: conflict-free reads)
+constexpr int kFillWg = 2048;         // workgroups a split launch aims for (8 per CU)
+constexpr int kMinSegTiles = 64;      // shortest key segment of a split launch (8,192 keys)
 
 struct ScoreSmem {
     // key ring; key 8n + st of a tile sits in row 16 st + n, so that the 16-key slice st
@@ -52,6 +54,8 @@ struct ScoreArgs {
     int64_t pos0;               // one sequence: position of its first query row; its keys are
                                 // rows 0 .. pos0 + T - 1 of k (0 for ragged batches)
     int nrb;                    // grid.y: row blocks of the longest sequence
+    int seg_tiles;              // one sequence: key tiles per workgroup along grid.x (0: all
+                                // of a row block's tiles in one workgroup, grid.x = sequence)
     float *out;                 // triangular score rows
     float *dummy;               // write target of rows past a sequence end
 };
@@ -85,7 +89,7 @@ __global__ __launch_bounds__(kThreads, 1) void score_rows_kernel(ScoreArgs a) {
     extern __shared__ __align__(16) unsigned char smem_raw[];
     ScoreSmem &sm = *reinterpret_cast<ScoreSmem *>(smem_raw);
 
-    const int seq = blockIdx.x;
+    const int seq = a.seg_tiles > 0 ? 0 : (int)blockIdx.x;
     const int rb = a.nrb - 1 - (int)blockIdx.y;   // longest rows first
     int64_t seq_start = 0, L = a.T, base = 0;
     if (a.cu_seqlens) {
@@ -102,6 +106,13 @@ __global__ __launch_bounds__(kThreads, 1) void score_rows_kernel(ScoreArgs a) {
     const int64_t p0 = a.pos0;
     const int64_t nkeys = p0 + L;
     const int nkt = (int)((p0 + r0 + rows_here - 1) / kBK) + 1;
+    // this workgroup's key tiles: kt0 .. kt0 + nt - 1
+    int kt0 = 0, nt = nkt;
+    if (a.seg_tiles > 0) {
+        kt0 = (int)blockIdx.x * a.seg_tiles;
+        if (kt0 >= nkt) return;
+        nt = nkt - kt0 < a.seg_tiles ? nkt - kt0 : a.seg_tiles;
+    }
 
     const int tid = threadIdx.x;
     const int wave = tid >> 6, lane = tid & 63;
@@ -158,8 +169,8 @@ __global__ __launch_bounds__(kThreads, 1) void score_rows_kernel(ScoreArgs a) {
     // its last row; their scores are never read.
     const int sk = 16 * wave + (lane >> 2), sd = 32 * (lane & 3);
     u32x4 kv[4];
-    auto load_k = [&](int kt) {
-        int64_t s = (int64_t)kt * kBK + sk;
+    auto load_k = [&](int u) {   // the u-th tile of this workgroup
+        int64_t s = (int64_t)(kt0 + u) * kBK + sk;
         s = s < nkeys ? s : nkeys - 1;
         const uint16_t *src = a.k + (seq_start + s) * kDim + sd;
 #pragma unroll
@@ -172,11 +183,11 @@ __global__ __launch_bounds__(kThreads, 1) void score_rows_kernel(ScoreArgs a) {
     };
     // the first kKR - 2 tiles go to fresh slots
     for (int u = 0; u < kKR - 2; ++u) {
-        load_k(u < nkt ? u : nkt - 1);
+        load_k(u < nt ? u : nt - 1);
         store_k(u);
         signal(&sm.k_staged[wave]);
     }
-    load_k(kKR - 2 < nkt ? kKR - 2 : nkt - 1);
+    load_k(kKR - 2 < nt ? kKR - 2 : nt - 1);
 
     // ---- the stream.  Software pipeline inside a tile: a unit is kUG products g (4 heads
     // each) of one 16-key slice, kUG independent MFMA chains over the 128 dims.  The ReLU / w
@@ -200,7 +211,7 @@ __global__ __launch_bounds__(kThreads, 1) void score_rows_kernel(ScoreArgs a) {
         return v;
     };
 #pragma unroll 1
-    for (int t = 0; t < nkt; ++t) {
+    for (int t = 0; t < nt; ++t) {
         wait_min_geq(sm.k_staged, (uint32_t)(t + 1), spin);   // tile t staged by every wave
         const uint16_t *kb = &sm.k[t % kKR][l16][8 * lg];
         u32x4 b[4];
@@ -247,18 +258,18 @@ __global__ __launch_bounds__(kThreads, 1) void score_rows_kernel(ScoreArgs a) {
         signal(&sm.k_used[wave]);             // every read of key slot t % kKR is done
         // one store and one load per tile, unconditionally and in this order, so that the
         // wait for the load in the next tile never has to include a store
-        float *const dst = (t < row_nt ? orow : drow) + (int64_t)t * kBK;
+        float *const dst = (kt0 + t < row_nt ? orow : drow) + (int64_t)(kt0 + t) * kBK;
         *reinterpret_cast<f32x4 *>(dst) = f32x4{sc[0], sc[1], sc[2], sc[3]};
         *reinterpret_cast<f32x4 *>(dst + 4) = f32x4{sc[4], sc[5], sc[6], sc[7]};
         // stage tile t + kKR - 2 into the slot of tile t - 2 once every wave is done with it
         // (so waves may drift up to two tiles apart); its loads were issued a tile earlier
         const int u = t + kKR - 2;
-        if (u < nkt) {
+        if (u < nt) {
             wait_min_geq(sm.k_used, (uint32_t)(t - 1 > 0 ? t - 1 : 0), spin);
             store_k(u % kKR);
             signal(&sm.k_staged[wave]);
         }
-        load_k(u + 1 < nkt ? u + 1 : nkt - 1);
+        load_k(u + 1 < nt ? u + 1 : nt - 1);
     }
 }
 
@@ -316,7 +327,22 @@ hipError_t launch_scores(const uint16_t *q, const uint16_t *k, const uint16_t *w
     a.nrb = (int)((max_len + kBQ - 1) / kBQ);
     a.out = out;
     a.dummy = dummy;
-    hipLaunchKernelGGL(score_rows_kernel, dim3(B, a.nrb), dim3(kThreads), smem, stream, a);
+    // One sequence with few row blocks (a chunk of queries against a long prefix): split each
+    // row block's key tiles over several workgroups, for about kFillWg workgroups of at least
+    // kMinSegTiles tiles.  A score needs no reduction across keys, so segments are independent.
+    a.seg_tiles = 0;
+    unsigned gx = (unsigned)B;
+    if (!cu_seqlens && a.nrb < kFillWg) {
+        const int64_t max_nkt = (a.pos0 + T - 1) / kBK + 1;
+        const int64_t want = (kFillWg + a.nrb - 1) / a.nrb;
+        int64_t st = (max_nkt + want - 1) / want;
+        st = st < kMinSegTiles ? kMinSegTiles : st;
+        if (st < max_nkt) {
+            a.seg_tiles = (int)st;
+            gx = (unsigned)((max_nkt + st - 1) / st);
+        }
+    }
+    hipLaunchKernelGGL(score_rows_kernel, dim3(gx, a.nrb), dim3(kThreads), smem, stream, a);
     return hipGetLastError();
 }
 
