@@ -126,4 +126,14 @@ __device__ __forceinline__ int wave_sum(int v) {
     return v;
 }
 
+// Sum over the four lane groups (lg = lane / 16) of this lane's partial scores p[u] of the
+// four slices u of a 64-key group, returned so that lane (l16, lg) holds slice lg's total:
+// the score of key 16 lg + l16 of the group.  Two exchanges across lg bit 1, one across bit 0.
+__device__ __forceinline__ float group_scores(const float (&p)[4], int lg) {
+    const bool h = (lg >> 1) & 1, e = lg & 1;
+    const float x0 = (h ? p[2] : p[0]) + __shfl_xor(h ? p[0] : p[2], 32, 64);   // slice 2h
+    const float x1 = (h ? p[3] : p[1]) + __shfl_xor(h ? p[1] : p[3], 32, 64);   // slice 2h + 1
+    return (e ? x1 : x0) + __shfl_xor(e ? x0 : x1, 16, 64);
+}
+
 }  // namespace dsaidx

@@ -83,7 +83,6 @@ __global__ __launch_bounds__(256) void quantize_queries_kernel(const uint16_t *_
 }
 
 constexpr int kDecThreads = 256;
-constexpr int kUnroll = 4;            // 16-key slices in flight per wave
 constexpr int kSplit = 64;            // a workgroup's share of keys is a multiple of this
 
 struct Fp8Args {
@@ -92,7 +91,9 @@ struct Fp8Args {
     const uint8_t *k8;
     const float *kscale;
     const int64_t *start;
-    const int64_t *cu;
+    const int64_t *cu;             // prefix sums of the cache lengths rounded up to 64
+    const int32_t *seqlens;
+    int max_seqlen;
     int B;
     int64_t ld;
     float *score_buf;
@@ -102,10 +103,12 @@ __device__ __forceinline__ f32x4 mfma_fp8(uint64_t a, uint64_t b, f32x4 c) {
     return __builtin_amdgcn_mfma_f32_16x16x32_fp8_fp8((long)a, (long)b, c, 0, 0, 0);
 }
 
-// As the bf16 decode score pass: the flat range of all cached keys split evenly over the grid;
-// lane (l16, lg) of a 16-key slice reads bytes 32 lg .. 32 lg + 31 of key l16 (two 16-byte
-// loads), k-step ks uses bytes 32 lg + 8 ks .. + 7 of the key and of the query head (rows of
-// the A operand: head 16 hh + l16).
+// As the bf16 decode score pass: the flat range of all cached keys (each sequence padded to a
+// multiple of 64) split evenly over the grid, 64-key groups per wave, one 256-byte store of
+// scores per group; lane (l16, lg) of a 16-key slice reads bytes 32 lg .. 32 lg + 31 of key
+// l16 (two 16-byte loads), k-step ks uses bytes 32 lg + 8 ks .. + 7 of the key and of the
+// query head (rows of the A operand: head 16 hh + l16).  The key scales of a group are read
+// with one 256-byte load, lane i taking key i's.
 __global__ __launch_bounds__(kDecThreads) void decode_score_fp8_kernel(Fp8Args a) {
     const int64_t total = a.cu[a.B];
     const int64_t per = ((total + gridDim.x - 1) / gridDim.x + kSplit - 1) / kSplit * kSplit;
@@ -127,7 +130,8 @@ __global__ __launch_bounds__(kDecThreads) void decode_score_fp8_kernel(Fp8Args a
     while (pos < end) {
         while (a.cu[b + 1] <= pos) ++b;
         const int64_t seg_end = min(end, a.cu[b + 1]);
-        const int s_begin = (int)(pos - a.cu[b]), s_end = (int)(seg_end - a.cu[b]);
+        const int len = max(0, min(a.seqlens[b], a.max_seqlen));
+        const int s_begin = (int)(pos - a.cu[b]), s_end = min(len, (int)(seg_end - a.cu[b]));
 
         uint64_t qa[2][4];
         float wv[2][4];
@@ -147,17 +151,25 @@ __global__ __launch_bounds__(kDecThreads) void decode_score_fp8_kernel(Fp8Args a
         const float *ks = a.kscale + a.start[b];
         float *out = a.score_buf + (int64_t)b * a.ld;
 
-        for (int s0 = s_begin + 16 * wave; s0 < s_end; s0 += 64 * kUnroll) {
-            u32x4 kb[kUnroll][2];
+        // next group's loads before this group's store; every lane stores (see the bf16 pass)
+        u32x4 kb[4][2];
+        float kscale;
+        auto load = [&](int g) {
 #pragma unroll
-            for (int u = 0; u < kUnroll; ++u) {
-                const int key = s0 + 64 * u + l16;
+            for (int u = 0; u < 4; ++u) {
+                const int key = min(g + 16 * u + l16, s_end - 1);
                 const uint32_t off = (uint32_t)key * (uint32_t)kDim + 32u * (uint32_t)lg;
-                kb[u][0] = key < s_end ? *reinterpret_cast<const u32x4 *>(kc + off) : u32x4{0u, 0u, 0u, 0u};
-                kb[u][1] = key < s_end ? *reinterpret_cast<const u32x4 *>(kc + off + 16) : u32x4{0u, 0u, 0u, 0u};
+                kb[u][0] = *reinterpret_cast<const u32x4 *>(kc + off);
+                kb[u][1] = *reinterpret_cast<const u32x4 *>(kc + off + 16);
             }
+            kscale = ks[min(g + lane, s_end - 1)];
+        };
+        int g0 = s_begin + 64 * wave;
+        if (g0 < s_end) load(g0);
+        for (; g0 < s_end; g0 += 256) {
+            float p[4];
 #pragma unroll
-            for (int u = 0; u < kUnroll; ++u) {
+            for (int u = 0; u < 4; ++u) {
                 const uint64_t b0 = (uint64_t)kb[u][0][0] | ((uint64_t)kb[u][0][1] << 32);
                 const uint64_t b1 = (uint64_t)kb[u][0][2] | ((uint64_t)kb[u][0][3] << 32);
                 const uint64_t b2 = (uint64_t)kb[u][1][0] | ((uint64_t)kb[u][1][1] << 32);
@@ -171,16 +183,16 @@ __global__ __launch_bounds__(kDecThreads) void decode_score_fp8_kernel(Fp8Args a
                 s_hi = mfma_fp8(qa[1][2], b2, s_hi);
                 s_lo = mfma_fp8(qa[0][3], b3, s_lo);
                 s_hi = mfma_fp8(qa[1][3], b3, s_hi);
-                float p = 0.f;
+                float v = 0.f;
 #pragma unroll
-                for (int r = 0; r < 4; ++r) p = fmaf(wv[0][r], relu(s_lo[r]), p);
+                for (int r = 0; r < 4; ++r) v = fmaf(wv[0][r], relu(s_lo[r]), v);
 #pragma unroll
-                for (int r = 0; r < 4; ++r) p = fmaf(wv[1][r], relu(s_hi[r]), p);
-                p += __shfl_xor(p, 16, 64);
-                p += __shfl_xor(p, 32, 64);
-                const int key = s0 + 64 * u + l16;
-                if (lg == 0 && key < s_end) out[key] = p * ks[key];
+                for (int r = 0; r < 4; ++r) v = fmaf(wv[1][r], relu(s_hi[r]), v);
+                p[u] = v;
             }
+            const float scale = kscale;
+            if (g0 + 256 < s_end) load(g0 + 256);
+            out[g0 + lane] = group_scores(p, lg) * scale;
         }
         pos = seg_end;
     }
@@ -223,8 +235,8 @@ hipError_t launch_decode_fp8(const uint16_t *q, const uint16_t *w, const uint8_t
     e = hipGetLastError();
     if (e != hipSuccess) return e;
     const int64_t ld = decode_row_stride(max_seqlen);
-    Fp8Args a{q8, qw, k8, kscale, start, cu, B, ld, score_buf};
-    const int64_t bound = ((int64_t)B * max_seqlen + kSplit - 1) / kSplit;
+    Fp8Args a{q8, qw, k8, kscale, start, cu, seqlens, max_seqlen, B, ld, score_buf};
+    const int64_t bound = (int64_t)B * ((max_seqlen + kSplit - 1) / kSplit);
     const int64_t grid = bound < decode_fp8_grid() ? bound : decode_fp8_grid();
     hipLaunchKernelGGL(decode_score_fp8_kernel, dim3((unsigned)grid), dim3(kDecThreads), 0, stream, a);
     e = hipGetLastError();
