@@ -102,17 +102,8 @@ size_t ws_score_topk_varlen(int64_t total, int B, int max_seqlen) {
     return ws_hdr(B) + ws_dummy(max_seqlen) + 4u * (size_t)varlen_score_floats(total, B, max_seqlen);
 }
 
-// decode: B + 1 cache offsets, then B score rows of decode_row_stride(max_seqlen) floats
-size_t ws_decode(int B, int max_seqlen) {
-    return ws_hdr(B) + (size_t)B * (size_t)dsaidx::decode_row_stride(max_seqlen) * 4u;
-}
-size_t ws_decode_fp8_q8(int B, int max_seqlen) { return round256(ws_decode(B, max_seqlen)); }
-size_t ws_decode_fp8_qw(int B, int max_seqlen) {
-    return ws_decode_fp8_q8(B, max_seqlen) + round256((size_t)B * DSA_IDX_QOUT);
-}
-size_t ws_decode_fp8(int B, int max_seqlen) {
-    return ws_decode_fp8_qw(B, max_seqlen) + (size_t)B * DSA_IDX_HEADS * 4u;
-}
+size_t ws_decode(int B, int max_seqlen) { return dsaidx::decode_workspace(B, max_seqlen, false); }
+size_t ws_decode_fp8(int B, int max_seqlen) { return dsaidx::decode_workspace(B, max_seqlen, true); }
 
 }  // namespace
 
@@ -372,11 +363,8 @@ int dsa_idx_decode(const dsa_idx_bf16 *q, const dsa_idx_bf16 *w, const dsa_idx_b
     if (!aligned16(ws)) return fail(DSA_IDX_EINVAL, "workspace must be 16-byte aligned");
     r = check_device();
     if (r) return r;
-    char *wsb = static_cast<char *>(ws);
-    hipError_t e = dsaidx::launch_decode(q, w, k_cache, start, seqlens, B, max_seqlen, topk,
-                                         reinterpret_cast<int64_t *>(wsb),
-                                         reinterpret_cast<float *>(wsb + ws_hdr(B)), idx, scores,
-                                         reinterpret_cast<hipStream_t>(stream));
+    hipError_t e = dsaidx::launch_decode(q, w, k_cache, start, seqlens, B, max_seqlen, topk, ws, idx,
+                                         scores, reinterpret_cast<hipStream_t>(stream));
     if (e != hipSuccess) return hip_fail("decode launch", e);
     return ok();
 }
@@ -415,12 +403,7 @@ int dsa_idx_decode_fp8(const dsa_idx_bf16 *q, const dsa_idx_bf16 *w, const uint8
     if (!aligned16(ws)) return fail(DSA_IDX_EINVAL, "workspace must be 16-byte aligned");
     r = check_device();
     if (r) return r;
-    char *wsb = static_cast<char *>(ws);
-    hipError_t e = dsaidx::launch_decode_fp8(q, w, k8, k_scale, start, seqlens, B, max_seqlen, topk,
-                                             reinterpret_cast<int64_t *>(wsb),
-                                             reinterpret_cast<float *>(wsb + ws_hdr(B)),
-                                             reinterpret_cast<uint8_t *>(wsb + ws_decode_fp8_q8(B, max_seqlen)),
-                                             reinterpret_cast<float *>(wsb + ws_decode_fp8_qw(B, max_seqlen)),
+    hipError_t e = dsaidx::launch_decode_fp8(q, w, k8, k_scale, start, seqlens, B, max_seqlen, topk, ws,
                                              idx, scores, reinterpret_cast<hipStream_t>(stream));
     if (e != hipSuccess) return hip_fail("decode_fp8 launch", e);
     return ok();

@@ -1,51 +1,604 @@
 // Decode: one new query per sequence scored against that sequence's cached indexer keys
 // (serving engines cache the indexer keys: "Kimi K3.1 Pro vs GLM-5" compare page,
-// low-precision row), then the top-k of the whole prefix (sparse/compressed-attention
-// row of the "Qwen3.5-397B-A17B vs Kimi K3.1 Pro" page; long-context row of the
-// "Kimi K3.1 Pro vs Gemma 4 31B" page).
+// low-precision row), then the top-k of the whole prefix (sparse/compressed-attention row of
+// the "Qwen3.5-397B-A17B vs Kimi K3.1 Pro" page; long-context row of the "Kimi K3.1 Pro vs
+// Gemma 4 31B" page).  The cache holds bf16 keys (256 bytes each) or FP8 keys (128 E4M3 bytes
+// and a power-of-two scale; see fp8.hip).
 //
-// Pass 1 streams the key cache once (256 bytes per key, the bandwidth-bound part), split
-// evenly over the grid across sequences: each 16-key slice is one pair of
-// v_mfma_f32_16x16x32_bf16 chains with the 32 heads as the M dimension (two halves of 16),
-// ReLU and the w-weighted head sum in registers, and one fp32 score per key written to the
-// workspace (4 bytes against 256 read).  A wave takes 64 consecutive keys (four slices) at a
-// time and writes their scores with one 256-byte store: every lane stores one score, at a
-// 256-byte aligned address (each sequence's range in the flat split starts at a multiple of
-// 64), because scattered 64-byte stores of the scores slow the read stream measurably.
-// Pass 2 is the row top-k of topk.hip, one workgroup of 16 waves per sequence: a sampled
-// threshold, one streaming pass that keeps the keys above it, an exact select among those,
-// and the winners in ascending index order.
+// Three passes.  Streaming the cache is the bandwidth-bound part; writing every score back
+// to HBM in the middle of that stream, and then a row top-k whose single workgroup per row
+// streams those scores again, each cost a sizeable fraction of the stream itself.  So:
+//  1. plan (one workgroup per sequence): the scores of a stratified sample of the sequence's
+//     keys give a threshold theta that, with overwhelming probability, between topk and a
+//     few times topk of the row's scores reach;
+//  2. filter (the flat split below): every key is scored, and only the keys whose score
+//     reaches theta are written, as (score, index) pairs, in index order;
+//  3. select (one workgroup per sequence): the exact top-k of those candidates, ties to the
+//     lower index, in ascending index order.
+// The result is exact whatever theta is: a row whose candidates turn out fewer than topk (a
+// sample that overshoots) is scored again in full by its select workgroup and selected from
+// all its scores; a row whose sample predicts too many candidates (many equal scores) has
+// all its scores written by the filter pass and is selected from those.  Rows of at most
+// kShortRow keys take every key as a candidate.
+//
+// The filter pass splits the flat range of all cached keys (each sequence padded to a
+// multiple of 64 positions) evenly over its waves, so every wave streams the same number of
+// bytes whatever the lengths.  Each 16-key slice is a pair of MFMA chains with the 32 heads
+// as the M dimension (two halves of 16); ReLU and the w-weighted head sum stay in registers;
+// a wave takes 64 consecutive keys (four slices) at a time, and issues the next group's loads
+// before any store of this one, so that waiting for loads never waits for a store.  A wave's
+// candidates go to a small LDS ring and leave it 64 at a time with full-width stores.
 #include "common.hpp"
 #include "launch.hpp"
+#include "topk_impl.hpp"
 
 namespace dsaidx {
 namespace {
+using namespace topk_impl;
 
-constexpr int kDecThreads = 256;
-constexpr int kSplit = 64;            // a workgroup's share of keys is a multiple of this
+constexpr int kFilterThreads = 256;
+constexpr int kPlanThreads = 512;
+constexpr int kSelectThreads = 1024;
+constexpr int kShortRow = kPer * kSelectThreads;   // 16,384: every key a candidate
+constexpr int kSampleMin = 1024, kSampleMax = 8192;
+constexpr int64_t kDenseCount = 12288;              // predicted candidates of a dense row
+constexpr int kPlanPrefixMax = 4096;                // batches whose prefix the plan pass computes
+static_assert(kMaxPieces<16> >= 8, "pieces per row");
 
-struct DecArgs {
-    const uint16_t *q;
-    const uint16_t *w;
-    const uint16_t *k_cache;
-    const int64_t *start;
-    const int64_t *cu;  // [B + 1] prefix sums of the clamped cache lengths rounded up to 64
-    const int32_t *seqlens;
-    int max_seqlen;
-    int B;
-    int64_t ld;         // score row stride (a multiple of 64)
-    float *score_buf;   // [B][ld]
+struct DecodePlan {
+    uint32_t theta;   // candidates: order keys >= theta (0: every key)
+    uint32_t dense;   // 1: the filter writes all scores of the row, the select takes them all
 };
 
-// cu[b] = sum over i < b of L_i = min(max(seqlens[i], 0), max_seqlen) rounded up to a
-// multiple of 64, for b = 0 .. B.
+struct DecCommon {
+    const int64_t *start;    // [B] first cache row of each sequence
+    const int32_t *seqlens;  // [B] cached keys (clamped to [0, max_seqlen])
+    int B;
+    int max_seqlen;
+    int topk;
+    int filter_grid;         // workgroups of the filter pass (its geometry is recomputed)
+    int64_t *cu;             // [B + 1] prefix sums of the padded lengths
+    DecodePlan *plan;        // [B]
+    int32_t *cnt;            // candidates of the piece starting at flat position p: cnt[p / 64]
+    uint2 *cand;             // the piece's candidates from cand[p] on: (score bits, index)
+    float *score_buf;        // [B][ld]: all scores of dense and re-scored rows
+    int64_t ld;
+    int32_t *idx;            // [B][topk]
+    float *scores;           // [B][topk] or nullptr
+};
+
+__device__ __forceinline__ int clamp_len(const DecCommon &a, int b) {
+    return max(0, min(a.seqlens[b], a.max_seqlen));
+}
+__device__ __forceinline__ int64_t pad64(int64_t n) { return (n + 63) & ~(int64_t)63; }
+
+// Keys per wave of the filter pass: an even split of the flat range over its waves, but long
+// enough that a row has at most kMaxPieces pieces; a multiple of 64.
+__device__ __forceinline__ int64_t decode_sub(int64_t total, int grid, int max_seqlen) {
+    const int64_t waves = (int64_t)grid * (kFilterThreads / 64);
+    const int64_t even = (total + waves - 1) / waves;
+    const int64_t longest = ((int64_t)max_seqlen + kMaxPieces<16> - 3) / (kMaxPieces<16> - 2);
+    return pad64(even > longest ? even : longest);
+}
+
+// Sample i of S of a row of n keys: a position in stratum [i n / S, (i + 1) n / S), picked by
+// an integer hash of (sequence, i) (the "lowbias32" mixer of C. Wellons), so that the sample
+// is spread over the whole row and follows no fixed stride.
+__device__ __forceinline__ int sample_pos(int b, int i, int n, int S) {
+    const int64_t lo = (int64_t)i * n / S, hi = (int64_t)(i + 1) * n / S;
+    uint32_t x = (uint32_t)i + 0x9E3779B9u * (uint32_t)(b + 1);
+    x ^= x >> 16;
+    x *= 0x7FEB352Du;
+    x ^= x >> 15;
+    x *= 0x846CA68Bu;
+    x ^= x >> 16;
+    return (int)(lo + x % (uint32_t)(hi - lo));
+}
+
+// ---------------------------------------------------------------- key scorers
+// A scorer holds one sequence's query (the MFMA A operand) and head weights, loads the keys
+// of one 64-key group (key[u]: this lane's key, row of the sequence, in slice u) and turns
+// them into this lane's partial scores p[u] (its 8 heads).  group_scores then gives lane
+// (l16, lg) the score of slice lg's key l16, which the scorer's scale() finishes.
+
+struct Bf16Keys {
+    const uint16_t *q, *w, *k_cache;
+};
+
+struct Bf16Scorer {
+    u32x4 qa[2][4];   // A operand: head 16 hh + l16, k-slot chunk 4 ks + lg (8 dims)
+    float wv[2][4];
+    const uint16_t *kc;
+    u32x4 kb[4][4];
+
+    __device__ __forceinline__ void init(const Bf16Keys &p, const int64_t *start, int b, int l16, int lg) {
+        const uint16_t *qb = p.q + (int64_t)b * kQOut;
+#pragma unroll
+        for (int hh = 0; hh < 2; ++hh) {
+#pragma unroll
+            for (int ks = 0; ks < 4; ++ks)
+                qa[hh][ks] = *reinterpret_cast<const u32x4 *>(qb + (16 * hh + l16) * kDim + 8 * (4 * ks + lg));
+#pragma unroll
+            for (int r = 0; r < 4; ++r) wv[hh][r] = bf16_to_f32(p.w[(int64_t)b * kHeads + 16 * hh + 4 * lg + r]);
+        }
+        kc = p.k_cache + start[b] * kDim;
+    }
+    __device__ __forceinline__ void load(const int (&key)[4], int lg) {
+#pragma unroll
+        for (int u = 0; u < 4; ++u) {
+            const uint32_t off = (uint32_t)key[u] * (uint32_t)kDim + 8u * (uint32_t)lg;   // elements
+#pragma unroll
+            for (int ks = 0; ks < 4; ++ks) kb[u][ks] = *reinterpret_cast<const u32x4 *>(kc + off + 32 * ks);
+        }
+    }
+    __device__ __forceinline__ void partial(float (&p)[4]) const {
+#pragma unroll
+        for (int u = 0; u < 4; ++u) {
+            f32x4 s_lo = {0.f, 0.f, 0.f, 0.f}, s_hi = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+            for (int ks = 0; ks < 4; ++ks) {
+                s_lo = mfma16x16x32(qa[0][ks], kb[u][ks], s_lo);
+                s_hi = mfma16x16x32(qa[1][ks], kb[u][ks], s_hi);
+            }
+            float v = 0.f;
+#pragma unroll
+            for (int r = 0; r < 4; ++r) v = fmaf(wv[0][r], relu(s_lo[r]), v);
+#pragma unroll
+            for (int r = 0; r < 4; ++r) v = fmaf(wv[1][r], relu(s_hi[r]), v);
+            p[u] = v;
+        }
+    }
+    __device__ __forceinline__ float scale() const { return 1.f; }
+    static constexpr bool kScaled = false;
+
+    // The plain (non-MFMA) score of key s, for the select's re-scoring of a row: the query
+    // (bf16 pairs) and weights of the row are in LDS.
+    static __device__ void stage(const Bf16Keys &p, int b, uint32_t *q_lds, float *w_lds) {
+        const uint32_t *src = reinterpret_cast<const uint32_t *>(p.q + (int64_t)b * kQOut);
+        for (int i = (int)threadIdx.x; i < kQOut / 2; i += (int)blockDim.x) q_lds[i] = src[i];
+        if ((int)threadIdx.x < kHeads) w_lds[threadIdx.x] = bf16_to_f32(p.w[(int64_t)b * kHeads + threadIdx.x]);
+    }
+    static __device__ float rescore(const Bf16Keys &p, const int64_t *start, int b, int s,
+                                    const uint32_t *q_lds, const float *w_lds) {
+        const uint16_t *kr = p.k_cache + (start[b] + s) * kDim;
+        float sc = 0.f;
+#pragma unroll 1
+        for (int h = 0; h < kHeads; ++h) {
+            float dot = 0.f;
+#pragma unroll 1
+            for (int c = 0; c < kDim / 8; ++c) {
+                const u32x4 kv = *reinterpret_cast<const u32x4 *>(kr + 8 * c);
+                const uint32_t *qr = q_lds + h * (kDim / 2) + 4 * c;
+#pragma unroll
+                for (int j = 0; j < 4; ++j) {
+                    dot = fmaf(bf16_to_f32(qr[j] & 0xFFFFu), bf16_to_f32(kv[j] & 0xFFFFu), dot);
+                    dot = fmaf(bf16_to_f32(qr[j] >> 16), bf16_to_f32(kv[j] >> 16), dot);
+                }
+            }
+            sc = fmaf(w_lds[h], relu(dot), sc);
+        }
+        return sc;
+    }
+};
+
+struct Fp8Keys {
+    const uint8_t *q8;     // [B][32][128] E4M3 codes of the new queries
+    const float *qw;       // [B][32] w * 2^eq
+    const uint8_t *k8;     // [*][128] E4M3 codes of the cached keys
+    const float *kscale;   // [*] 2^ek
+};
+
+__device__ __forceinline__ f32x4 mfma_fp8(uint64_t a, uint64_t b, f32x4 c) {
+    return __builtin_amdgcn_mfma_f32_16x16x32_fp8_fp8((long)a, (long)b, c, 0, 0, 0);
+}
+
+// Value of an E4M3 code (bias 7; the codes 0x7F / 0xFF, NaN, never occur in the cache).
+__device__ __forceinline__ float e4m3_value(uint32_t c) {
+    const uint32_t e = (c >> 3) & 15u, m = c & 7u;
+    const float mag = e ? __uint_as_float(((e + 120u) << 23) | (m << 20)) : (float)m * 0x1p-9f;
+    return (c & 0x80u) ? -mag : mag;
+}
+
+// Lane (l16, lg) of a 16-key slice reads bytes 32 lg .. 32 lg + 31 of key l16 (two 16-byte
+// loads); k-step ks uses bytes 32 lg + 8 ks .. + 7 of the key and of the query head.
+struct Fp8Scorer {
+    uint64_t qa[2][4];
+    float wv[2][4];
+    const uint8_t *kc;
+    const float *ks;
+    u32x4 kb[4][2];
+    float kscale;
+
+    __device__ __forceinline__ void init(const Fp8Keys &p, const int64_t *start, int b, int l16, int lg) {
+#pragma unroll
+        for (int hh = 0; hh < 2; ++hh) {
+            const uint8_t *qr = p.q8 + ((int64_t)b * kHeads + 16 * hh + l16) * kDim + 32 * lg;
+            const u32x4 v0 = *reinterpret_cast<const u32x4 *>(qr);
+            const u32x4 v1 = *reinterpret_cast<const u32x4 *>(qr + 16);
+            qa[hh][0] = (uint64_t)v0[0] | ((uint64_t)v0[1] << 32);
+            qa[hh][1] = (uint64_t)v0[2] | ((uint64_t)v0[3] << 32);
+            qa[hh][2] = (uint64_t)v1[0] | ((uint64_t)v1[1] << 32);
+            qa[hh][3] = (uint64_t)v1[2] | ((uint64_t)v1[3] << 32);
+#pragma unroll
+            for (int r = 0; r < 4; ++r) wv[hh][r] = p.qw[(int64_t)b * kHeads + 16 * hh + 4 * lg + r];
+        }
+        kc = p.k8 + start[b] * kDim;
+        ks = p.kscale + start[b];
+    }
+    __device__ __forceinline__ void load(const int (&key)[4], int lg) {
+#pragma unroll
+        for (int u = 0; u < 4; ++u) {
+            const uint32_t off = (uint32_t)key[u] * (uint32_t)kDim + 32u * (uint32_t)lg;
+            kb[u][0] = *reinterpret_cast<const u32x4 *>(kc + off);
+            kb[u][1] = *reinterpret_cast<const u32x4 *>(kc + off + 16);
+        }
+        kscale = ks[key[lg]];   // this lane's output key: slice lg, key l16
+    }
+    __device__ __forceinline__ void partial(float (&p)[4]) const {
+#pragma unroll
+        for (int u = 0; u < 4; ++u) {
+            const uint64_t b0 = (uint64_t)kb[u][0][0] | ((uint64_t)kb[u][0][1] << 32);
+            const uint64_t b1 = (uint64_t)kb[u][0][2] | ((uint64_t)kb[u][0][3] << 32);
+            const uint64_t b2 = (uint64_t)kb[u][1][0] | ((uint64_t)kb[u][1][1] << 32);
+            const uint64_t b3 = (uint64_t)kb[u][1][2] | ((uint64_t)kb[u][1][3] << 32);
+            f32x4 s_lo = {0.f, 0.f, 0.f, 0.f}, s_hi = {0.f, 0.f, 0.f, 0.f};
+            s_lo = mfma_fp8(qa[0][0], b0, s_lo);
+            s_hi = mfma_fp8(qa[1][0], b0, s_hi);
+            s_lo = mfma_fp8(qa[0][1], b1, s_lo);
+            s_hi = mfma_fp8(qa[1][1], b1, s_hi);
+            s_lo = mfma_fp8(qa[0][2], b2, s_lo);
+            s_hi = mfma_fp8(qa[1][2], b2, s_hi);
+            s_lo = mfma_fp8(qa[0][3], b3, s_lo);
+            s_hi = mfma_fp8(qa[1][3], b3, s_hi);
+            float v = 0.f;
+#pragma unroll
+            for (int r = 0; r < 4; ++r) v = fmaf(wv[0][r], relu(s_lo[r]), v);
+#pragma unroll
+            for (int r = 0; r < 4; ++r) v = fmaf(wv[1][r], relu(s_hi[r]), v);
+            p[u] = v;
+        }
+    }
+    __device__ __forceinline__ float scale() const { return kscale; }
+    static constexpr bool kScaled = true;
+
+    static __device__ void stage(const Fp8Keys &p, int b, uint32_t *q_lds, float *w_lds) {
+        const uint32_t *src = reinterpret_cast<const uint32_t *>(p.q8 + (int64_t)b * kHeads * kDim);
+        for (int i = (int)threadIdx.x; i < kHeads * kDim / 4; i += (int)blockDim.x) q_lds[i] = src[i];
+        if ((int)threadIdx.x < kHeads) w_lds[threadIdx.x] = p.qw[(int64_t)b * kHeads + threadIdx.x];
+    }
+    static __device__ float rescore(const Fp8Keys &p, const int64_t *start, int b, int s,
+                                    const uint32_t *q_lds, const float *w_lds) {
+        const uint8_t *kr = p.k8 + (start[b] + s) * kDim;
+        float sc = 0.f;
+#pragma unroll 1
+        for (int h = 0; h < kHeads; ++h) {
+            float dot = 0.f;
+#pragma unroll 1
+            for (int c = 0; c < kDim / 16; ++c) {
+                const u32x4 kv = *reinterpret_cast<const u32x4 *>(kr + 16 * c);
+                const uint32_t *qr = q_lds + h * (kDim / 4) + 4 * c;
+#pragma unroll
+                for (int j = 0; j < 16; ++j)
+                    dot = fmaf(e4m3_value((qr[j / 4] >> (8 * (j % 4))) & 0xFFu),
+                               e4m3_value((kv[j / 4] >> (8 * (j % 4))) & 0xFFu), dot);
+            }
+            sc = fmaf(w_lds[h], relu(dot), sc);
+        }
+        return sc * p.kscale[start[b] + s];
+    }
+};
+
+template <class Sc>
+__device__ __forceinline__ float finish(const Sc &sc, const float (&p)[4], float scl, int lg) {
+    const float v = group_scores(p, lg);
+    return Sc::kScaled ? v * scl : v;
+}
+
+// ---------------------------------------------------------------- pass 1: plan
+// One workgroup per sequence.  With own_prefix it also writes cu[b] (and cu[B]).
+template <class Sc, class Keys>
+__global__ __launch_bounds__(kPlanThreads) void decode_plan_kernel(DecCommon a, Keys kp, int own_prefix) {
+    __shared__ uint32_t skey[kSampleMax];
+    __shared__ uint32_t hist[256];
+    __shared__ int64_t red[kPlanThreads / 64];
+    __shared__ int bc[2];
+    const int b = blockIdx.x, tid = threadIdx.x;
+    const int lane = tid & 63, wave = tid >> 6;
+    const int l16 = lane & 15, lg = lane >> 4;
+    auto block_sum = [&](int64_t v) {
+#pragma unroll
+        for (int d = 32; d >= 1; d >>= 1) v += __shfl_xor(v, d, 64);
+        if (lane == 0) red[wave] = v;
+        __syncthreads();
+        int64_t t = 0;
+#pragma unroll
+        for (int i = 0; i < kPlanThreads / 64; ++i) t += red[i];
+        __syncthreads();
+        return t;
+    };
+    if (own_prefix) {
+        int64_t s = 0;
+        for (int i = tid; i < b; i += kPlanThreads) s += pad64(clamp_len(a, i));
+        s = block_sum(s);
+        if (tid == 0) {
+            a.cu[b] = s;
+            if (b == a.B - 1) a.cu[a.B] = s + pad64(clamp_len(a, b));
+        }
+    }
+    const int n = clamp_len(a, b);
+    if (n <= kShortRow) {
+        if (tid == 0) a.plan[b] = DecodePlan{0u, 0u};
+        return;
+    }
+    int S = (n / 128 + kSampleMin - 1) / kSampleMin * kSampleMin;
+    S = S < kSampleMin ? kSampleMin : (S > kSampleMax ? kSampleMax : S);
+    Sc sc;
+    sc.init(kp, a.start, b, l16, lg);
+    for (int j = wave; j < S / 64; j += kPlanThreads / 64) {
+        int key[4];
+#pragma unroll
+        for (int u = 0; u < 4; ++u) key[u] = sample_pos(b, 64 * j + 16 * u + l16, n, S);
+        sc.load(key, lg);
+        float p[4];
+        sc.partial(p);
+        skey[64 * j + lane] = score_key(finish(sc, p, sc.scale(), lg));
+    }
+    __syncthreads();
+    // r such that fewer than r of the S samples reach the topk-th largest score of the row
+    // only with negligible probability (their number is about binomial with mean E)
+    const float E = (float)S * (float)a.topk / (float)n;
+    int r = (int)ceilf(E + 8.f * sqrtf(E) + 8.f);
+    r = r > S ? S : r;
+    // theta = the r-th largest sample key: most significant byte first
+    uint32_t prefix = 0, pmask = 0;
+    int rr = r;
+#pragma unroll 1
+    for (int shift = 24; shift >= 0; shift -= 8) {
+        if (tid < 256) hist[tid] = 0u;
+        __syncthreads();
+        for (int i = tid; i < S; i += kPlanThreads) {
+            const uint32_t k = skey[i];
+            if ((k & pmask) == prefix) atomicAdd(&hist[(k >> shift) & 255u], 1u);
+        }
+        __syncthreads();
+        if (wave == 0) {
+            int c[4], sum = 0;
+#pragma unroll
+            for (int j = 0; j < 4; ++j) {   // lane l: digits 255 - 4l - j, from the top
+                c[j] = (int)hist[255 - 4 * lane - j];
+                sum += c[j];
+            }
+            int run = wave_inclusive_sum(sum) - sum;
+#pragma unroll
+            for (int j = 0; j < 4; ++j) {
+                if (run < rr && rr <= run + c[j]) {
+                    bc[0] = 255 - 4 * lane - j;
+                    bc[1] = run;
+                }
+                run += c[j];
+            }
+        }
+        __syncthreads();
+        prefix |= (uint32_t)bc[0] << shift;
+        pmask |= 255u << shift;
+        rr -= bc[1];
+        __syncthreads();
+    }
+    int64_t reach = 0;
+    for (int i = tid; i < S; i += kPlanThreads) reach += skey[i] >= prefix ? 1 : 0;
+    reach = block_sum(reach);
+    if (tid == 0) a.plan[b] = DecodePlan{prefix, reach * n / S > kDenseCount ? 1u : 0u};
+}
+
+// ---------------------------------------------------------------- pass 2: filter
+template <class Sc, class Keys>
+__global__ __launch_bounds__(kFilterThreads, 2) void decode_filter_kernel(DecCommon a, Keys kp) {
+    __shared__ uint2 ring[kFilterThreads / 64][128];
+    const int64_t total = a.cu[a.B];
+    const int64_t sub = decode_sub(total, gridDim.x, a.max_seqlen);
+    const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+    const int l16 = lane & 15, lg = lane >> 4;
+    int64_t pos = ((int64_t)blockIdx.x * (kFilterThreads / 64) + wave) * sub;
+    const int64_t end = min(total, pos + sub);
+    if (pos >= end) return;
+    uint2 *rw = ring[wave];
+    // the last sequence with cu[b] <= pos (cu is non-decreasing: count the entries <= pos,
+    // 64 at a time)
+    int b = -1;
+    for (int base = 0; base < a.B; base += 64) {
+        const bool le = base + lane < a.B && a.cu[base + lane] <= pos;
+        const uint64_t m = __ballot(le);
+        b += (int)__popcll(m);
+        if (m != ~0ull) break;
+    }
+    while (pos < end) {
+        while (a.cu[b + 1] <= pos) ++b;   // skips empty sequences
+        const int64_t seg_end = min(end, a.cu[b + 1]);
+        // keys s_begin .. s_end - 1 of sequence b (s_begin a multiple of 64)
+        const int s_begin = (int)(pos - a.cu[b]);
+        const int s_end = min(clamp_len(a, b), (int)(seg_end - a.cu[b]));
+        const DecodePlan pl = a.plan[b];
+        Sc sc;
+        sc.init(kp, a.start, b, l16, lg);
+        auto keys = [&](int g, int (&key)[4]) {   // rows past the end clamped to the last
+#pragma unroll
+            for (int u = 0; u < 4; ++u) key[u] = min(g + 16 * u + l16, s_end - 1);
+        };
+        int key[4];
+        int g0 = s_begin;
+        if (g0 < s_end) {
+            keys(g0, key);
+            sc.load(key, lg);
+        }
+        if (pl.dense) {
+            // every lane stores (past the end lie the row's padding positions)
+            float *out = a.score_buf + (int64_t)b * a.ld;
+            for (; g0 < s_end; g0 += 64) {
+                float p[4];
+                sc.partial(p);
+                const float scl = sc.scale();
+                if (g0 + 64 < s_end) {
+                    keys(g0 + 64, key);
+                    sc.load(key, lg);
+                }
+                out[g0 + lane] = finish(sc, p, scl, lg);
+            }
+        } else {
+            // key >= theta  <=>  score >= the score of theta (the keys order the scores)
+            const bool every = pl.theta == 0u;
+            const float th = key_score(every ? 1u : pl.theta);
+            uint2 *list = a.cand + pos;   // this piece's list (room for one entry per position)
+            int nst = 0, nfl = 0;         // candidates staged, flushed
+            for (; g0 < s_end; g0 += 64) {
+                float p[4];
+                sc.partial(p);
+                const float scl = sc.scale();
+                if (g0 + 64 < s_end) {
+                    keys(g0 + 64, key);
+                    sc.load(key, lg);
+                }
+                const float v = finish(sc, p, scl, lg);
+                const bool c = g0 + lane < s_end && (every || v >= th);
+                const uint64_t m = __ballot(c);
+                if (m) {
+                    if (c) rw[(nst + (int)bits_below(m)) & 127] = make_uint2(__float_as_uint(v), (uint32_t)(g0 + lane));
+                    nst += (int)__popcll(m);
+                    __builtin_amdgcn_wave_barrier();
+                    if (nst - nfl >= 64) {
+                        list[nfl + lane] = rw[(nfl + lane) & 127];
+                        nfl += 64;
+                    }
+                }
+            }
+            __builtin_amdgcn_wave_barrier();
+            if (lane < nst - nfl) list[nfl + lane] = rw[(nfl + lane) & 127];
+            if (lane == 0) a.cnt[pos / 64] = nst;
+        }
+        pos = seg_end;
+    }
+}
+
+// ---------------------------------------------------------------- pass 3: select
+template <class Sc, class Keys>
+__global__ __launch_bounds__(kSelectThreads) void decode_select_kernel(DecCommon a, Keys kp) {
+    __shared__ TopkSmem<16> sm;
+    const int b = blockIdx.x, tid = threadIdx.x;
+    const int topk = a.topk;
+    const int n = clamp_len(a, b);
+    int32_t *oi = a.idx + (int64_t)b * topk;
+    float *os = a.scores ? a.scores + (int64_t)b * topk : nullptr;
+    TopkArgs ta{};
+    ta.scores = a.score_buf;
+    ta.mode = 1;
+    ta.seqlens = a.seqlens;
+    ta.ld = a.ld;
+    ta.nmax = a.max_seqlen;
+    ta.B = a.B;
+    ta.topk = topk;
+    ta.out_idx = a.idx;
+    ta.out_score = a.scores;
+    const DecodePlan pl = a.plan[b];
+    // the row's pieces: one from cu[b], then one from every multiple of sub inside the row
+    const int64_t c0 = a.cu[b];
+    const int64_t sub = decode_sub(a.cu[a.B], a.filter_grid, a.max_seqlen);
+    const int np = n > 0 ? (int)((c0 + n - 1) / sub - c0 / sub) + 1 : 0;
+    const bool fits = np <= kMaxPieces<16>;
+    int c = 0;
+    if (!pl.dense && fits && np > 0) {
+        int run = 0;
+        for (int j0 = 0; j0 < np; j0 += kSelectThreads) {
+            const int j = j0 + tid;
+            int cj = 0;
+            if (j < np) {
+                const int64_t st = j == 0 ? c0 : (c0 / sub + j) * sub;
+                sm.u.pc.start[j] = st;
+                cj = a.cnt[st / 64];
+            }
+            int tot;
+            const int incl = block_inclusive_sum(cj, tot, sm);
+            if (j < np) sm.u.pc.off[j] = run + incl - cj;
+            run += tot;
+        }
+        if (tid == 0) sm.u.pc.off[np] = run;
+        c = run;
+        __syncthreads();
+    }
+    const int need_min = n < topk ? n : topk;
+    if (!pl.dense && (!fits || c < need_min || c > kCand<16>)) {
+        // the sample overshot (or the list does not fit): score the whole row again
+        Sc::stage(kp, b, sm.u.resc.q, sm.u.resc.w);
+        __syncthreads();
+        float *row = a.score_buf + (int64_t)b * a.ld;
+        for (int s = tid; s < n; s += kSelectThreads)
+            row[s] = Sc::rescore(kp, a.start, b, s, sm.u.resc.q, sm.u.resc.w);
+        __threadfence();
+        __syncthreads();
+        c = -1;
+    }
+    if (pl.dense || c < 0) {   // all the row's scores are in score_buf
+        row_topk_row<16>(ta, b, sm);
+        return;
+    }
+    // candidates to registers: list entry kPer tid + i, in index order
+    uint32_t key[kPer];
+    int32_t kidx[kPer];
+    {
+        const int e0 = kPer * tid;
+        int j = 0;
+        if (np > 0) {
+            int lo = 0, hi = np - 1;   // the last piece with off <= e0
+            while (lo < hi) {
+                const int mid = (lo + hi + 1) >> 1;
+                if (sm.u.pc.off[mid] <= e0) lo = mid;
+                else hi = mid - 1;
+            }
+            j = lo;
+        }
+#pragma unroll
+        for (int i = 0; i < kPer; ++i) {
+            const int e = e0 + i;
+            key[i] = 0u;
+            kidx[i] = 0;
+            if (e < c) {
+                while (j + 1 < np && sm.u.pc.off[j + 1] <= e) ++j;
+                const uint2 v = a.cand[sm.u.pc.start[j] + (e - sm.u.pc.off[j])];
+                key[i] = score_key(__uint_as_float(v.x));
+                kidx[i] = (int32_t)v.y;
+            }
+        }
+    }
+    __syncthreads();
+    int need = 0;
+    uint32_t theta = 0u;   // c <= topk: every candidate is kept
+    if (c > topk) {
+        uint32_t m = 0, mn = 0xFFFFFFFFu;
+#pragma unroll
+        for (int i = 0; i < kPer; ++i) {
+            m = key[i] > m ? key[i] : m;
+            mn = key[i] != 0u && key[i] < mn ? key[i] : mn;
+        }
+        const uint32_t top = block_max(m, sm);
+        const uint32_t bot = ~block_max(~mn, sm);
+        need = topk;
+        theta = select_rel(key, bot, bit_width(top - bot), need, sm);
+    }
+    int eq_base = 0;
+    const int wrote = emit_ordered_idx(key, kidx, theta, need, 0, eq_base, oi, os, sm);
+    for (int i = wrote + tid; i < topk; i += kSelectThreads) {
+        oi[i] = -1;
+        if (os) os[i] = -INFINITY;
+    }
+}
+
+// cu[b] = sum over i < b of pad64(min(max(seqlens[i], 0), max_seqlen)), b = 0 .. B (batches
+// too large for the plan pass to sum itself).
 __global__ __launch_bounds__(1024) void decode_prefix_kernel(const int32_t *seqlens, int B,
                                                               int max_seqlen, int64_t *cu) {
     __shared__ int64_t part[1024];
     const int tid = threadIdx.x;
     const int per = (B + 1023) / 1024;
     const int i0 = tid * per, i1 = min(B, i0 + per);
-    auto len = [&](int i) { return ((int64_t)max(0, min(seqlens[i], max_seqlen)) + 63) & ~(int64_t)63; };
+    auto len = [&](int i) { return pad64(max(0, min(seqlens[i], max_seqlen))); };
     int64_t s = 0;
     for (int i = i0; i < i1; ++i) s += len(i);
     part[tid] = s;
@@ -64,126 +617,110 @@ __global__ __launch_bounds__(1024) void decode_prefix_kernel(const int32_t *seql
     if (tid == 1023) cu[B] = part[1023];
 }
 
-// The cached keys of all sequences, taken as one flat range of cu[B] positions (each
-// sequence's keys padded to a multiple of 64), are split evenly over the grid, so every
-// workgroup streams the same number of bytes whatever the lengths.  A workgroup's share may
-// cross sequence boundaries; each piece uses its sequence's q and w.  Within a piece, wave w
-// takes the 64-key groups w, w + 4, ...
-__global__ __launch_bounds__(kDecThreads) void decode_score_kernel(DecArgs a) {
-    const int64_t total = a.cu[a.B];
-    const int64_t per = ((total + gridDim.x - 1) / gridDim.x + kSplit - 1) / kSplit * kSplit;
-    int64_t pos = (int64_t)blockIdx.x * per;
-    const int64_t end = min(total, pos + per);
-    if (pos >= end) return;
-    const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
-    const int l16 = lane & 15, lg = lane >> 4;
-    int b = 0;
-    {
-        int lo = 0, hi = a.B - 1;   // the last sequence with cu[b] <= pos
-        while (lo < hi) {
-            const int mid = (lo + hi + 1) >> 1;
-            if (a.cu[mid] <= pos) lo = mid;
-            else hi = mid - 1;
-        }
-        b = lo;
-    }
-    while (pos < end) {
-        while (a.cu[b + 1] <= pos) ++b;   // skips empty sequences
-        const int64_t seg_end = min(end, a.cu[b + 1]);
-        // keys s_begin .. s_end - 1 of sequence b (s_begin a multiple of 64; below max_seqlen)
-        const int len = max(0, min(a.seqlens[b], a.max_seqlen));
-        const int s_begin = (int)(pos - a.cu[b]), s_end = min(len, (int)(seg_end - a.cu[b]));
-
-        // A operand: head 16*hh + l16, k-slot chunk 4*ks + lg (8 dims)
-        u32x4 qa[2][4];
-        float wv[2][4];
-        const uint16_t *qb = a.q + (int64_t)b * kQOut;
-#pragma unroll
-        for (int hh = 0; hh < 2; ++hh) {
-#pragma unroll
-            for (int ks = 0; ks < 4; ++ks)
-                qa[hh][ks] = *reinterpret_cast<const u32x4 *>(qb + (16 * hh + l16) * kDim + 8 * (4 * ks + lg));
-#pragma unroll
-            for (int r = 0; r < 4; ++r) wv[hh][r] = bf16_to_f32(a.w[(int64_t)b * kHeads + 16 * hh + 4 * lg + r]);
-        }
-        const uint16_t *kc = a.k_cache + a.start[b] * kDim;
-        float *out = a.score_buf + (int64_t)b * a.ld;
-
-        // The next group's loads are issued before this group's store, and every lane stores
-        // (positions past the end are the row's padding), so that waiting for loads never
-        // waits for a store.  Key rows past the end are clamped to the last one.
-        u32x4 kb[4][4];
-        auto load = [&](int g) {
-#pragma unroll
-            for (int u = 0; u < 4; ++u) {
-                const int key = min(g + 16 * u + l16, s_end - 1);
-                const uint32_t off = (uint32_t)key * (uint32_t)kDim + 8u * (uint32_t)lg;   // elements
-#pragma unroll
-                for (int ks = 0; ks < 4; ++ks) kb[u][ks] = *reinterpret_cast<const u32x4 *>(kc + off + 32 * ks);
-            }
-        };
-        int g0 = s_begin + 64 * wave;
-        if (g0 < s_end) load(g0);
-        for (; g0 < s_end; g0 += 256) {
-            float p[4];
-#pragma unroll
-            for (int u = 0; u < 4; ++u) {
-                f32x4 s_lo = {0.f, 0.f, 0.f, 0.f}, s_hi = {0.f, 0.f, 0.f, 0.f};
-#pragma unroll
-                for (int ks = 0; ks < 4; ++ks) {
-                    s_lo = mfma16x16x32(qa[0][ks], kb[u][ks], s_lo);
-                    s_hi = mfma16x16x32(qa[1][ks], kb[u][ks], s_hi);
-                }
-                float v = 0.f;
-#pragma unroll
-                for (int r = 0; r < 4; ++r) v = fmaf(wv[0][r], relu(s_lo[r]), v);
-#pragma unroll
-                for (int r = 0; r < 4; ++r) v = fmaf(wv[1][r], relu(s_hi[r]), v);
-                p[u] = v;
-            }
-            if (g0 + 256 < s_end) load(g0 + 256);
-            out[g0 + lane] = group_scores(p, lg);
-        }
-        pos = seg_end;
-    }
-}
-
-int decode_grid() {
+template <class K>
+int filter_grid(K kernel) {
     static int cached[64] = {0};
     int dev = 0;
     if (hipGetDevice(&dev) != hipSuccess || dev < 0) return 2048;
     if (dev < 64 && cached[dev] > 0) return cached[dev];
     int cus = 0, per = 0;
     if (hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess || cus <= 0) cus = 256;
-    if (hipOccupancyMaxActiveBlocksPerMultiprocessor(&per, decode_score_kernel, kDecThreads, 0) != hipSuccess || per <= 0)
+    if (hipOccupancyMaxActiveBlocksPerMultiprocessor(&per, kernel, kFilterThreads, 0) != hipSuccess || per <= 0)
         per = 2;
-    const int g = 8 * per * cus;   // eight rounds of the workgroups resident at once: short shares
+    const int g = 2 * per * cus;   // two rounds of the workgroups resident at once
     if (dev < 64) cached[dev] = g;
     return g;
 }
 
+template <class Sc, class Keys>
+hipError_t run_decode(const Keys &kp, const int64_t *start, const int32_t *seqlens, int B, int max_seqlen,
+                      int topk, const DecodeWs &w, int32_t *idx, float *scores, hipStream_t stream) {
+    DecCommon a{};
+    a.start = start;
+    a.seqlens = seqlens;
+    a.B = B;
+    a.max_seqlen = max_seqlen;
+    a.topk = topk;
+    a.cu = w.cu;
+    a.plan = reinterpret_cast<DecodePlan *>(w.plan);
+    a.cnt = w.cnt;
+    a.cand = reinterpret_cast<uint2 *>(w.cand);
+    a.score_buf = w.score_buf;
+    a.ld = decode_row_stride(max_seqlen);
+    a.idx = idx;
+    a.scores = scores;
+    const int64_t bound = ((int64_t)B * (decode_row_stride(max_seqlen) / 64) + 3) / 4;   // 4 waves of 64 keys
+    const int g = filter_grid(decode_filter_kernel<Sc, Keys>);
+    a.filter_grid = (int)(bound < g ? (bound > 0 ? bound : 1) : g);
+    const int own = B <= kPlanPrefixMax ? 1 : 0;
+    if (!own) {
+        hipLaunchKernelGGL(decode_prefix_kernel, dim3(1), dim3(1024), 0, stream, seqlens, B, max_seqlen, w.cu);
+        hipError_t e = hipGetLastError();
+        if (e != hipSuccess) return e;
+    }
+    hipLaunchKernelGGL((decode_plan_kernel<Sc, Keys>), dim3(B), dim3(kPlanThreads), 0, stream, a, kp, own);
+    hipError_t e = hipGetLastError();
+    if (e != hipSuccess) return e;
+    hipLaunchKernelGGL((decode_filter_kernel<Sc, Keys>), dim3(a.filter_grid), dim3(kFilterThreads), 0, stream, a, kp);
+    e = hipGetLastError();
+    if (e != hipSuccess) return e;
+    hipLaunchKernelGGL((decode_select_kernel<Sc, Keys>), dim3(B), dim3(kSelectThreads), 0, stream, a, kp);
+    return hipGetLastError();
+}
+
+size_t r256(size_t b) { return (b + 255u) & ~(size_t)255u; }
+
 }  // namespace
 
-hipError_t launch_decode_prefix(const int32_t *seqlens, int B, int max_seqlen, int64_t *cu, hipStream_t stream) {
-    hipLaunchKernelGGL(decode_prefix_kernel, dim3(1), dim3(1024), 0, stream, seqlens, B, max_seqlen, cu);
-    return hipGetLastError();
+size_t decode_workspace(int B, int max_seqlen, bool fp8, DecodeWs *w, void *base) {
+    const size_t Bs = (size_t)(B > 0 ? B : 0);
+    const size_t flat = Bs * (size_t)decode_row_stride(max_seqlen);   // padded positions
+    size_t off = 0;
+    auto take = [&](size_t bytes) {
+        const size_t o = off;
+        off += r256(bytes);
+        return o;
+    };
+    const size_t o_cu = take(8u * (Bs + 1));
+    const size_t o_plan = take(8u * Bs);
+    const size_t o_cnt = take(4u * (flat / 64 + 1));
+    const size_t o_cand = take(8u * flat);
+    const size_t o_sb = take(4u * flat);
+    const size_t o_q8 = fp8 ? take(Bs * kQOut) : 0;
+    const size_t o_qw = fp8 ? take(4u * Bs * kHeads) : 0;
+    if (w && base) {
+        char *p = static_cast<char *>(base);
+        w->cu = reinterpret_cast<int64_t *>(p + o_cu);
+        w->plan = reinterpret_cast<uint64_t *>(p + o_plan);
+        w->cnt = reinterpret_cast<int32_t *>(p + o_cnt);
+        w->cand = reinterpret_cast<uint64_t *>(p + o_cand);
+        w->score_buf = reinterpret_cast<float *>(p + o_sb);
+        w->q8 = fp8 ? reinterpret_cast<uint8_t *>(p + o_q8) : nullptr;
+        w->qw = fp8 ? reinterpret_cast<float *>(p + o_qw) : nullptr;
+    }
+    return off;
 }
 
 hipError_t launch_decode(const uint16_t *q, const uint16_t *w, const uint16_t *k_cache,
                          const int64_t *start, const int32_t *seqlens, int B, int max_seqlen,
-                         int topk, int64_t *cu, float *score_buf, int32_t *idx, float *scores,
-                         hipStream_t stream) {
+                         int topk, void *ws, int32_t *idx, float *scores, hipStream_t stream) {
     if (B == 0) return hipSuccess;
-    hipError_t e = launch_decode_prefix(seqlens, B, max_seqlen, cu, stream);
+    DecodeWs dw{};
+    decode_workspace(B, max_seqlen, false, &dw, ws);
+    return run_decode<Bf16Scorer>(Bf16Keys{q, w, k_cache}, start, seqlens, B, max_seqlen, topk, dw, idx,
+                                  scores, stream);
+}
+
+hipError_t launch_decode_fp8(const uint16_t *q, const uint16_t *w, const uint8_t *k8, const float *kscale,
+                             const int64_t *start, const int32_t *seqlens, int B, int max_seqlen, int topk,
+                             void *ws, int32_t *idx, float *scores, hipStream_t stream) {
+    if (B == 0) return hipSuccess;
+    DecodeWs dw{};
+    decode_workspace(B, max_seqlen, true, &dw, ws);
+    hipError_t e = launch_quantize_queries(q, w, B, dw.q8, dw.qw, stream);
     if (e != hipSuccess) return e;
-    const int64_t ld = decode_row_stride(max_seqlen);
-    DecArgs a{q, w, k_cache, start, cu, seqlens, max_seqlen, B, ld, score_buf};
-    const int64_t bound = (int64_t)B * ((max_seqlen + kSplit - 1) / kSplit);   // shares of kSplit keys
-    const int64_t grid = bound < decode_grid() ? bound : decode_grid();
-    hipLaunchKernelGGL(decode_score_kernel, dim3((unsigned)grid), dim3(kDecThreads), 0, stream, a);
-    e = hipGetLastError();
-    if (e != hipSuccess) return e;
-    return launch_row_topk_decode(score_buf, seqlens, B, ld, max_seqlen, topk, idx, scores, stream);
+    return run_decode<Fp8Scorer>(Fp8Keys{dw.q8, dw.qw, k8, kscale}, start, seqlens, B, max_seqlen, topk, dw,
+                                 idx, scores, stream);
 }
 
 }  // namespace dsaidx

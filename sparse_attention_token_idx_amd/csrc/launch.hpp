@@ -48,26 +48,34 @@ hipError_t launch_row_topk_decode(const float *scores, const int32_t *seqlens, i
                                   int64_t nmax, int topk, int32_t *idx, float *out_scores,
                                   hipStream_t stream);
 
-// ---- decode (decode.hip).  Workspace: cu (B + 1 int64), then score_buf of B rows of
-// decode_row_stride(max_seqlen) floats.
+// ---- decode (decode.hip).  Score rows of decode_row_stride(max_seqlen) floats.
 __host__ __device__ inline int64_t decode_row_stride(int64_t max_seqlen) {
     return (max_seqlen + 63) / 64 * 64;
 }
-// cu[b] = sum of min(max(seqlens[i], 0), max_seqlen) over i < b, for b = 0 .. B
-hipError_t launch_decode_prefix(const int32_t *seqlens, int B, int max_seqlen, int64_t *cu, hipStream_t stream);
+// Parts of the decode workspace.
+struct DecodeWs {
+    int64_t *cu;        // [B + 1] prefix sums of the padded cache lengths
+    uint64_t *plan;     // [B] per-row threshold plan
+    int32_t *cnt;       // candidate counts per piece
+    uint64_t *cand;     // candidate lists, flat-indexed
+    float *score_buf;   // [B][decode_row_stride(max_seqlen)]
+    uint8_t *q8;        // FP8 path: [B][32][128] query codes
+    float *qw;          // FP8 path: [B][32] folded head weights
+};
+// Bytes of the decode workspace (16-byte aligned base); with w and base, also its parts.
+size_t decode_workspace(int B, int max_seqlen, bool fp8, DecodeWs *w = nullptr, void *base = nullptr);
 hipError_t launch_decode(const uint16_t *q, const uint16_t *w, const uint16_t *k_cache,
                          const int64_t *start, const int32_t *seqlens, int B, int max_seqlen,
-                         int topk, int64_t *cu, float *score_buf, int32_t *idx, float *scores,
-                         hipStream_t stream);
+                         int topk, void *ws, int32_t *idx, float *scores, hipStream_t stream);
 
 // ---- FP8 key cache (fp8.hip).  Cache rows: 128 E4M3 bytes and one fp32 power-of-two scale.
 hipError_t launch_quantize_keys(const uint16_t *k, int64_t ldk, int64_t N, const int64_t *slot, uint8_t *k8,
                                 float *kscale, hipStream_t stream);
-// Workspace: cu (B + 1 int64) and score_buf as for launch_decode, then q8 [B][32][128] bytes and
-// qw [B][32] fp32.
+// The new queries: q8 [B][32][128] codes, qw[b][h] = w[b][h] * 2^eq[b][h].
+hipError_t launch_quantize_queries(const uint16_t *q, const uint16_t *w, int B, uint8_t *q8, float *qw,
+                                   hipStream_t stream);
 hipError_t launch_decode_fp8(const uint16_t *q, const uint16_t *w, const uint8_t *k8, const float *kscale,
                              const int64_t *start, const int32_t *seqlens, int B, int max_seqlen, int topk,
-                             int64_t *cu, float *score_buf, uint8_t *q8, float *qw, int32_t *idx,
-                             float *scores, hipStream_t stream);
+                             void *ws, int32_t *idx, float *scores, hipStream_t stream);
 
 }  // namespace dsaidx

@@ -56,13 +56,18 @@ def test_workspace_sizes(dsa):
     # ragged: bound from sequences of max length (here 2 of length 8 -> (8+128)^2/2 floats each)
     vb = ((2 * 136 * 136 // 2 + 127) // 128) * 128
     assert dsa.workspace_size(dsa.OP_SCORE_TOPK_VARLEN, 16, 2, 8, topk=5) == 256 + 512 + 4 * vb
-    # decode: 256-byte-aligned header of B + 1 cache offsets, then score rows padded to a
-    # multiple of 64 floats
-    assert dsa.workspace_size(dsa.OP_DECODE, 0, 64, 131072, 2048) == 768 + 64 * 131072 * 4
-    assert dsa.workspace_size(dsa.OP_DECODE, 0, 3, 100, 8) == 256 + 3 * 128 * 4
-    # FP8 decode: the decode workspace, then the quantised queries (3 x 4096 bytes, 256-aligned)
-    # and their folded head weights (3 x 32 fp32)
-    assert dsa.workspace_size(dsa.OP_DECODE_FP8, 0, 3, 100, 8) == 1792 + 12288 + 384
+    # decode: 256-byte aligned parts over the padded positions P = B * 64 * ceil(max / 64):
+    # B + 1 cache offsets, B plans (8 bytes), P / 64 + 1 piece counts, P candidate slots of
+    # 8 bytes, P fp32 scores; FP8 adds the quantised queries (B x 4096 bytes) and their folded
+    # head weights (B x 32 fp32)
+    def dec(B, m, fp8=False):
+        P = B * 64 * ((m + 63) // 64)
+        n = r256(8 * (B + 1)) + r256(8 * B) + r256(4 * (P // 64 + 1)) + r256(8 * P) + r256(4 * P)
+        return n + (r256(B * 4096) + r256(128 * B) if fp8 else 0)
+    assert dec(64, 131072) == 101189120 and dec(3, 100) == 5376 and dec(3, 100, True) == 18176
+    assert dsa.workspace_size(dsa.OP_DECODE, 0, 64, 131072, 2048) == dec(64, 131072)
+    assert dsa.workspace_size(dsa.OP_DECODE, 0, 3, 100, 8) == dec(3, 100)
+    assert dsa.workspace_size(dsa.OP_DECODE_FP8, 0, 3, 100, 8) == dec(3, 100, True)
     # chunked prefill: header, a dummy row of 128*ceil((prefix + C)/128) floats, and rows
     # prefix .. prefix + C - 1 of the triangular layout
     assert dsa.workspace_size(dsa.OP_PREFILL_CHUNK, 300, 0, 1000, 8) == \
