@@ -44,6 +44,7 @@ constexpr int kSampleMin = 1024, kSampleMax = 8192;
 constexpr int64_t kDenseCount = 12288;              // predicted candidates of a dense row
 constexpr int kPlanPrefixMax = 4096;                // batches whose prefix the plan pass computes
 static_assert(kMaxPieces<16> >= 8, "pieces per row");
+static_assert(kSampleMin == 1024 && kSampleMax == 8192, "sample sizes 2^10 .. 2^13");
 
 struct DecodePlan {
     uint32_t theta;   // candidates: order keys >= theta (0: every key)
@@ -81,18 +82,19 @@ __device__ __forceinline__ int64_t decode_sub(int64_t total, int grid, int max_s
     return pad64(even > longest ? even : longest);
 }
 
-// Sample i of S of a row of n keys: a position in stratum [i n / S, (i + 1) n / S), picked by
-// an integer hash of (sequence, i) (the "lowbias32" mixer of C. Wellons), so that the sample
-// is spread over the whole row and follows no fixed stride.
-__device__ __forceinline__ int sample_pos(int b, int i, int n, int S) {
-    const int64_t lo = (int64_t)i * n / S, hi = (int64_t)(i + 1) * n / S;
+// Sample i of S = 2^lgS of a row of n keys: a position in stratum [i n / S, (i + 1) n / S),
+// picked by an integer hash of (sequence, i) (the "lowbias32" mixer of C. Wellons) scaled to
+// the stratum's width, so that the sample is spread over the whole row and follows no fixed
+// stride.
+__device__ __forceinline__ int sample_pos(int b, int i, int n, int lgS) {
+    const int64_t lo = ((int64_t)i * n) >> lgS, hi = ((int64_t)(i + 1) * n) >> lgS;
     uint32_t x = (uint32_t)i + 0x9E3779B9u * (uint32_t)(b + 1);
     x ^= x >> 16;
     x *= 0x7FEB352Du;
     x ^= x >> 15;
     x *= 0x846CA68Bu;
     x ^= x >> 16;
-    return (int)(lo + x % (uint32_t)(hi - lo));
+    return (int)(lo + (int64_t)(((uint64_t)x * (uint64_t)(hi - lo)) >> 32));
 }
 
 // ---------------------------------------------------------------- key scorers
@@ -299,8 +301,9 @@ __device__ __forceinline__ float finish(const Sc &sc, const float (&p)[4], float
 template <class Sc, class Keys>
 __global__ __launch_bounds__(kPlanThreads) void decode_plan_kernel(DecCommon a, Keys kp, int own_prefix) {
     __shared__ uint32_t skey[kSampleMax];
-    __shared__ uint32_t hist[256];
+    __shared__ uint32_t hist[1024];
     __shared__ int64_t red[kPlanThreads / 64];
+    __shared__ uint32_t red2[kPlanThreads / 64];
     __shared__ int bc[2];
     const int b = blockIdx.x, tid = threadIdx.x;
     const int lane = tid & 63, wave = tid >> 6;
@@ -316,6 +319,7 @@ __global__ __launch_bounds__(kPlanThreads) void decode_plan_kernel(DecCommon a, 
         __syncthreads();
         return t;
     };
+    const int n = clamp_len(a, b);
     if (own_prefix) {
         int64_t s = 0;
         for (int i = tid; i < b; i += kPlanThreads) s += pad64(clamp_len(a, i));
@@ -325,23 +329,37 @@ __global__ __launch_bounds__(kPlanThreads) void decode_plan_kernel(DecCommon a, 
             if (b == a.B - 1) a.cu[a.B] = s + pad64(clamp_len(a, b));
         }
     }
-    const int n = clamp_len(a, b);
     if (n <= kShortRow) {
         if (tid == 0) a.plan[b] = DecodePlan{0u, 0u};
         return;
     }
-    int S = (n / 128 + kSampleMin - 1) / kSampleMin * kSampleMin;
-    S = S < kSampleMin ? kSampleMin : (S > kSampleMax ? kSampleMax : S);
-    Sc sc;
-    sc.init(kp, a.start, b, l16, lg);
-    for (int j = wave; j < S / 64; j += kPlanThreads / 64) {
-        int key[4];
+    // S = 2^lgS samples, at least n / 128 (1,024 .. 8,192)
+    int lgS = 10;
+    while (lgS < 13 && (1 << lgS) < n / 128) ++lgS;
+    const int S = 1 << lgS;
+    // sample scores, two 64-key groups in flight per wave
+    constexpr int kWaves = kPlanThreads / 64;
+    Sc s0, s1;
+    s0.init(kp, a.start, b, l16, lg);
+    s1.init(kp, a.start, b, l16, lg);
+    for (int j = wave; j < S / 64; j += 2 * kWaves) {
+        const int j1 = j + kWaves;
+        const bool two = j1 < S / 64;
+        int k0[4], k1[4];
 #pragma unroll
-        for (int u = 0; u < 4; ++u) key[u] = sample_pos(b, 64 * j + 16 * u + l16, n, S);
-        sc.load(key, lg);
+        for (int u = 0; u < 4; ++u) {
+            k0[u] = sample_pos(b, 64 * j + 16 * u + l16, n, lgS);
+            k1[u] = two ? sample_pos(b, 64 * j1 + 16 * u + l16, n, lgS) : k0[u];
+        }
+        s0.load(k0, lg);
+        s1.load(k1, lg);
         float p[4];
-        sc.partial(p);
-        skey[64 * j + lane] = score_key(finish(sc, p, sc.scale(), lg));
+        s0.partial(p);
+        skey[64 * j + lane] = score_key(finish(s0, p, s0.scale(), lg));
+        if (two) {
+            s1.partial(p);
+            skey[64 * j1 + lane] = score_key(finish(s1, p, s1.scale(), lg));
+        }
     }
     __syncthreads();
     // r such that fewer than r of the S samples reach the topk-th largest score of the row
@@ -349,45 +367,76 @@ __global__ __launch_bounds__(kPlanThreads) void decode_plan_kernel(DecCommon a, 
     const float E = (float)S * (float)a.topk / (float)n;
     int r = (int)ceilf(E + 8.f * sqrtf(E) + 8.f);
     r = r > S ? S : r;
-    // theta = the r-th largest sample key: most significant byte first
-    uint32_t prefix = 0, pmask = 0;
+    // theta: the lower edge of the bin that holds the r-th largest sample key, first in 1,024
+    // bins over the sample's key range, then in 1,024 bins over that bin (exact when the bins
+    // reach single key values, otherwise at most 1/2^20 of the range lower)
+    uint32_t top = 0, bot = 0xFFFFFFFFu;
+    for (int x = tid; x < S; x += kPlanThreads) {
+        const uint32_t k = skey[x];
+        top = k > top ? k : top;
+        bot = k < bot ? k : bot;
+    }
+#pragma unroll
+    for (int d = 32; d >= 1; d >>= 1) {
+        const uint32_t o = (uint32_t)__shfl_xor((int)top, d, 64), o2 = (uint32_t)__shfl_xor((int)bot, d, 64);
+        top = o > top ? o : top;
+        bot = o2 < bot ? o2 : bot;
+    }
+    if (lane == 0) {
+        red[wave] = top;
+        red2[wave] = bot;
+    }
+    __syncthreads();
+#pragma unroll
+    for (int x = 0; x < kWaves; ++x) {
+        top = (uint32_t)red[x] > top ? (uint32_t)red[x] : top;
+        bot = red2[x] < bot ? red2[x] : bot;
+    }
+    int nb = 32 - __builtin_clz((top - bot) | 1u);
+    int sh = nb > 10 ? nb - 10 : 0;
+    uint32_t base = bot, theta = bot;
     int rr = r;
-#pragma unroll 1
-    for (int shift = 24; shift >= 0; shift -= 8) {
-        if (tid < 256) hist[tid] = 0u;
+    int span = 32;   // keys counted: base <= key < base + 2^span (pass 0: all)
+    for (int pass = 0; pass < 2; ++pass) {
+        hist[tid] = 0u;
+        if (tid + kPlanThreads < 1024) hist[tid + kPlanThreads] = 0u;
         __syncthreads();
-        for (int i = tid; i < S; i += kPlanThreads) {
-            const uint32_t k = skey[i];
-            if ((k & pmask) == prefix) atomicAdd(&hist[(k >> shift) & 255u], 1u);
+        for (int x = tid; x < S; x += kPlanThreads) {
+            const uint32_t k = skey[x];
+            const uint64_t rel = (uint64_t)k - base;
+            if (k >= base && (rel >> span) == 0) atomicAdd(&hist[rel >> sh], 1u);
         }
         __syncthreads();
         if (wave == 0) {
-            int c[4], sum = 0;
+            int c[16], sum = 0;
 #pragma unroll
-            for (int j = 0; j < 4; ++j) {   // lane l: digits 255 - 4l - j, from the top
-                c[j] = (int)hist[255 - 4 * lane - j];
-                sum += c[j];
+            for (int q = 0; q < 16; ++q) {   // lane l: bins 1023 - 16 l - q, from the top
+                c[q] = (int)hist[1023 - 16 * lane - q];
+                sum += c[q];
             }
             int run = wave_inclusive_sum(sum) - sum;
 #pragma unroll
-            for (int j = 0; j < 4; ++j) {
-                if (run < rr && rr <= run + c[j]) {
-                    bc[0] = 255 - 4 * lane - j;
+            for (int q = 0; q < 16; ++q) {
+                if (run < rr && rr <= run + c[q]) {
+                    bc[0] = 1023 - 16 * lane - q;
                     bc[1] = run;
                 }
-                run += c[j];
+                run += c[q];
             }
         }
         __syncthreads();
-        prefix |= (uint32_t)bc[0] << shift;
-        pmask |= 255u << shift;
+        base += (uint32_t)bc[0] << sh;
         rr -= bc[1];
+        theta = base;
         __syncthreads();
+        if (sh == 0) break;
+        span = sh;
+        sh = sh > 10 ? sh - 10 : 0;
     }
     int64_t reach = 0;
-    for (int i = tid; i < S; i += kPlanThreads) reach += skey[i] >= prefix ? 1 : 0;
+    for (int x = tid; x < S; x += kPlanThreads) reach += skey[x] >= theta ? 1 : 0;
     reach = block_sum(reach);
-    if (tid == 0) a.plan[b] = DecodePlan{prefix, reach * n / S > kDenseCount ? 1u : 0u};
+    if (tid == 0) a.plan[b] = DecodePlan{theta, reach * n / S > kDenseCount ? 1u : 0u};
 }
 
 // ---------------------------------------------------------------- pass 2: filter
@@ -539,37 +588,36 @@ __global__ __launch_bounds__(kSelectThreads) void decode_select_kernel(DecCommon
         row_topk_row<16>(ta, b, sm);
         return;
     }
-    // candidates to registers: list entry kPer tid + i, in index order
-    uint32_t key[kPer];
-    int32_t kidx[kPer];
-    {
-        const int e0 = kPer * tid;
-        int j = 0;
-        if (np > 0) {
-            int lo = 0, hi = np - 1;   // the last piece with off <= e0
-            while (lo < hi) {
-                const int mid = (lo + hi + 1) >> 1;
-                if (sm.u.pc.off[mid] <= e0) lo = mid;
-                else hi = mid - 1;
-            }
-            j = lo;
-        }
-#pragma unroll
-        for (int i = 0; i < kPer; ++i) {
-            const int e = e0 + i;
-            key[i] = 0u;
-            kidx[i] = 0;
-            if (e < c) {
-                while (j + 1 < np && sm.u.pc.off[j + 1] <= e) ++j;
-                const uint2 v = a.cand[sm.u.pc.start[j] + (e - sm.u.pc.off[j])];
-                key[i] = score_key(__uint_as_float(v.x));
-                kidx[i] = (int32_t)v.y;
-            }
-        }
+    // Candidates to registers, entry e = tid + 1024 i (list order is index order), so that the
+    // loads of a wave cover consecutive entries.  blk[k]: the piece of entry 64 k.
+    for (int j = tid; j < np; j += kSelectThreads) {
+        const int lo = sm.u.pc.off[j], hi = sm.u.pc.off[j + 1];
+        for (int k = (lo + 63) >> 6; (k << 6) < hi; ++k) sm.u.pc.blk[k] = j;
     }
     __syncthreads();
-    int need = 0;
-    uint32_t theta = 0u;   // c <= topk: every candidate is kept
+    uint32_t key[kPer];
+    int32_t kidx[kPer];
+#pragma unroll
+    for (int i = 0; i < kPer; ++i) {
+        const int e = tid + kSelectThreads * i;
+        key[i] = 0u;
+        kidx[i] = 0;
+        if (e < c) {
+            int j = sm.u.pc.blk[e >> 6];
+            while (sm.u.pc.off[j + 1] <= e) ++j;
+            const uint2 v = a.cand[sm.u.pc.start[j] + (e - sm.u.pc.off[j])];
+            key[i] = score_key(__uint_as_float(v.x));
+            kidx[i] = (int32_t)v.y;
+        }
+    }
+    if (tid < kCand<16> / 32) sm.win[tid] = 0u;
+    if (tid == 0) sm.nbin = 0u;
+    __syncthreads();
+    // Winners: keys above hi, plus, among keys in [lo, hi], those whose bit is set in win (the
+    // bin ranked exactly) or, for a crowded bin narrowed to one value (lo == hi == theta), the
+    // first eq_need of them in entry order.
+    uint32_t lo = 1u, hi = 0u;   // c <= topk: every candidate wins
+    int eq_need = -1;            // -1: bin members win by their bit
     if (c > topk) {
         uint32_t m = 0, mn = 0xFFFFFFFFu;
 #pragma unroll
@@ -579,11 +627,133 @@ __global__ __launch_bounds__(kSelectThreads) void decode_select_kernel(DecCommon
         }
         const uint32_t top = block_max(m, sm);
         const uint32_t bot = ~block_max(~mn, sm);
-        need = topk;
-        theta = select_rel(key, bot, bit_width(top - bot), need, sm);
+        const int nb = bit_width(top - bot);
+        const int sh = nb > kDigit<16> ? nb - kDigit<16> : 0;   // kBins bins of 2^sh from bot
+        for (int x = tid; x < kBins<16>; x += kSelectThreads) sm.hist[x] = 0u;
+        __syncthreads();
+#pragma unroll
+        for (int i = 0; i < kPer; ++i)
+            if (key[i] != 0u) atomicAdd(&sm.hist[(key[i] - bot) >> sh], 1u);
+        __syncthreads();
+        int need = topk, in_bin;
+        const uint32_t d = pick_digit(need, sm, &in_bin);   // need: winners inside bin d
+        const uint64_t lo64 = (uint64_t)bot + ((uint64_t)d << sh);
+        lo = (uint32_t)lo64;
+        hi = (uint32_t)(lo64 + (1ull << sh) - 1ull);
+        if (in_bin <= kRankMax) {
+            // rank the bin's keys exactly: by key, then lower index first; the need best win
+#pragma unroll
+            for (int i = 0; i < kPer; ++i) {
+                if (key[i] >= lo && key[i] <= hi) {
+                    const uint32_t slot = atomicAdd(&sm.nbin, 1u);
+                    sm.bin.key[slot] = key[i];
+                    sm.bin.idx[slot] = kidx[i];
+                    sm.bin.slot[slot] = (uint16_t)(tid + kSelectThreads * i);
+                }
+            }
+            __syncthreads();
+            if (tid < in_bin) {
+                const uint32_t mk = sm.bin.key[tid];
+                const int32_t mi = sm.bin.idx[tid];
+                int rank = 0;
+                for (int x = 0; x < in_bin; ++x) {
+                    const uint32_t ok = sm.bin.key[x];
+                    rank += (ok > mk || (ok == mk && sm.bin.idx[x] < mi)) ? 1 : 0;
+                }
+                if (rank < need) {
+                    const int e = sm.bin.slot[tid];
+                    atomicOr(&sm.win[e >> 5], 1u << (e & 31));
+                }
+            }
+            __syncthreads();
+        } else {
+            // a crowded bin: narrow it to one key value by an exact select over its keys
+            uint32_t kb[kPer];
+            uint32_t bmax = 0;
+#pragma unroll
+            for (int i = 0; i < kPer; ++i) {
+                kb[i] = key[i] >= lo && key[i] <= hi ? key[i] : 0u;
+                bmax = kb[i] > bmax ? kb[i] : bmax;
+            }
+            const uint32_t theta = select_rel(kb, lo, bit_width(block_max(bmax, sm) - lo), need, sm);
+            lo = hi = theta;
+            eq_need = need;
+        }
     }
-    int eq_base = 0;
-    const int wrote = emit_ordered_idx(key, kidx, theta, need, 0, eq_base, oi, os, sm);
+    // Output positions in entry order: per entry row i, the winners of the earlier rows, of
+    // the earlier waves in row i and of the lower lanes.
+    const int lane = tid & 63, wave = tid >> 6;
+    bool win[kPer];
+    if (eq_need >= 0) {
+        // ties at theta: the first eq_need in entry order win
+        uint64_t em[kPer];
+#pragma unroll
+        for (int i = 0; i < kPer; ++i) {
+            em[i] = __ballot(key[i] == lo);
+            if (lane == 0) sm.u.ecnt[i * 16 + wave] = (int)__popcll(em[i]);
+        }
+        __syncthreads();
+        if (tid < 64) {   // exclusive prefix over the 256 (row, wave) counts
+            int v[4], sum = 0;
+#pragma unroll
+            for (int x = 0; x < 4; ++x) {
+                v[x] = sm.u.ecnt[4 * tid + x];
+                sum += v[x];
+            }
+            int run = wave_inclusive_sum(sum) - sum;
+#pragma unroll
+            for (int x = 0; x < 4; ++x) {
+                sm.u.ecnt[4 * tid + x] = run;
+                run += v[x];
+            }
+        }
+        __syncthreads();
+#pragma unroll
+        for (int i = 0; i < kPer; ++i) {
+            const int r = sm.u.ecnt[i * 16 + wave] + (int)bits_below(em[i]);
+            win[i] = key[i] > hi || (key[i] == lo && r < eq_need);
+        }
+        __syncthreads();
+    } else {
+#pragma unroll
+        for (int i = 0; i < kPer; ++i) {
+            const int e = tid + kSelectThreads * i;
+            win[i] = key[i] != 0u &&
+                     (key[i] > hi || (key[i] >= lo && ((sm.win[e >> 5] >> (e & 31)) & 1u)));
+        }
+    }
+    uint64_t wm[kPer];
+#pragma unroll
+    for (int i = 0; i < kPer; ++i) {
+        wm[i] = __ballot(win[i]);
+        if (lane == 0) sm.u.ecnt[i * 16 + wave] = (int)__popcll(wm[i]);
+    }
+    __syncthreads();
+    if (tid < 64) {
+        int v[4], sum = 0;
+#pragma unroll
+        for (int x = 0; x < 4; ++x) {
+            v[x] = sm.u.ecnt[4 * tid + x];
+            sum += v[x];
+        }
+        int run = wave_inclusive_sum(sum) - sum;
+#pragma unroll
+        for (int x = 0; x < 4; ++x) {
+            sm.u.ecnt[4 * tid + x] = run;
+            run += v[x];
+        }
+        if (tid == 63) sm.bcast[0] = run;
+    }
+    __syncthreads();
+    const int wrote = sm.bcast[0];
+#pragma unroll
+    for (int i = 0; i < kPer; ++i) {
+        if (win[i]) {
+            const int pos = sm.u.ecnt[i * 16 + wave] + (int)bits_below(wm[i]);
+            oi[pos] = kidx[i];
+            if (os) os[pos] = key_score(key[i]);
+        }
+    }
     for (int i = wrote + tid; i < topk; i += kSelectThreads) {
         oi[i] = -1;
         if (os) os[i] = -INFINITY;

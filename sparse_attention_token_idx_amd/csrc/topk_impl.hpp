@@ -77,9 +77,11 @@ template <int W> struct TopkSmem {
             float out_score[kMaxTopk];
         } emit;
         struct {                   // decode select: start (flat position) and list offset of
-            int64_t start[kMaxPieces<W>];   // each piece of the row's candidate list
-            int32_t off[kMaxPieces<W> + 1];
+            int64_t start[kMaxPieces<W>];   // each piece of the row's candidate list, and the
+            int32_t off[kMaxPieces<W> + 1];   // piece of the first entry of every 64 entries
+            int32_t blk[kCand<W> / 64];
         } pc;
+        int32_t ecnt[kPer * W];    // decode select: winners per (entry row, wave), then prefixes
         struct {                   // decode select fallback: the row's query and head weights
             uint32_t q[kHeads * kDim / 2];
             float w[kHeads];

@@ -26,19 +26,23 @@ def _bf(x):
 
 
 def _sample_positions(b, n):
-    """The plan pass's sample of row b (n keys): stratum i of S, offset by an integer hash."""
-    S = min(max((n // 128 + 1023) // 1024 * 1024, 1024), 8192)
+    """The plan pass's sample of row b (n keys): S = 2^lgS >= n / 128 strata (1,024 .. 8,192);
+    in stratum i the offset is an integer hash of (b, i) scaled to the stratum width."""
+    lgS = 10
+    while lgS < 13 and (1 << lgS) < n // 128:
+        lgS += 1
+    S = 1 << lgS
     M = 0xFFFFFFFF
     pos = []
     for i in range(S):
-        lo, hi = i * n // S, (i + 1) * n // S
+        lo, hi = (i * n) >> lgS, ((i + 1) * n) >> lgS
         x = (i + 0x9E3779B9 * (b + 1)) & M
         x ^= x >> 16
         x = (x * 0x7FEB352D) & M
         x ^= x >> 15
         x = (x * 0x846CA68B) & M
         x ^= x >> 16
-        pos.append(lo + x % (hi - lo))
+        pos.append(lo + ((x * (hi - lo)) >> 32))
     return np.asarray(pos)
 
 
