@@ -37,7 +37,7 @@ PEAK_BF16_TFLOPS = 2516.6     # MI355X dense bf16 MFMA (published)
 # HBM bytes per launch of the scoring kernel at T=65536, from rocprofv3 FETCH_SIZE and
 # WRITE_SIZE scaled by a 1 GiB device-copy calibration; reported only while the kernel
 # source is the one the counters were taken on (None: not measured for this source)
-TRAFFIC_SCORE_T65536 = {"source_sha256_prefix": "ac6e30b80565b5da", "bytes": 10879542492}
+TRAFFIC_SCORE_T65536 = {"source_sha256_prefix": "497fca71c49eba94", "bytes": 10869075527}
 PEAK_HBM_GBPS = 8000.0        # MI355X HBM3E (published)
 H, D, QLAT, HIDDEN = 32, 128, 1536, 7168
 PROJ_FLOP_PER_TOKEN = 2 * (QLAT * 4096 + HIDDEN * D + HIDDEN * H)   # 14,876,672
