@@ -8,9 +8,10 @@
 // Three passes.  Streaming the cache is the bandwidth-bound part; writing every score back
 // to HBM in the middle of that stream, and then a row top-k whose single workgroup per row
 // streams those scores again, each cost a sizeable fraction of the stream itself.  So:
-//  1. plan (one workgroup per sequence): the scores of a stratified sample of the sequence's
-//     keys give a threshold theta that, with overwhelming probability, between topk and a
-//     few times topk of the row's scores reach;
+//  1. plan (four workgroups per sequence score a stratified sample of its keys, then one
+//     workgroup per sequence turns the sample into a threshold): theta is such that, with
+//     overwhelming probability, between topk and a few times topk of the row's scores
+//     reach it;
 //  2. filter (the flat split below): every key is scored, and only the keys whose score
 //     reaches theta are written, as (score, index) pairs, in index order;
 //  3. select (one workgroup per sequence): the exact top-k of those candidates, ties to the
@@ -43,6 +44,7 @@ constexpr int kShortRow = kPer * kSelectThreads;   // 16,384: every key a candid
 constexpr int kSampleMin = 1024, kSampleMax = 8192;
 constexpr int64_t kDenseCount = 12288;              // predicted candidates of a dense row
 constexpr int kPlanPrefixMax = 4096;                // batches whose prefix the plan pass computes
+constexpr int kSampleParts = 4, kSampleThreads = 256;
 static_assert(kMaxPieces<16> >= 8, "pieces per row");
 static_assert(kSampleMin == 1024 && kSampleMax == 8192, "sample sizes 2^10 .. 2^13");
 
@@ -63,6 +65,7 @@ struct DecCommon {
     int32_t *cnt;            // candidates of the piece starting at flat position p: cnt[p / 64]
     uint2 *cand;             // the piece's candidates from cand[p] on: (score bits, index)
     float *score_buf;        // [B][ld]: all scores of dense and re-scored rows
+    uint32_t *skey;          // [B][kSampleMax] order keys of the sampled scores
     int64_t ld;
     int32_t *idx;            // [B][topk]
     float *scores;           // [B][topk] or nullptr
@@ -82,19 +85,21 @@ __device__ __forceinline__ int64_t decode_sub(int64_t total, int grid, int max_s
     return pad64(even > longest ? even : longest);
 }
 
-// Sample i of S = 2^lgS of a row of n keys: a position in stratum [i n / S, (i + 1) n / S),
-// picked by an integer hash of (sequence, i) (the "lowbias32" mixer of C. Wellons) scaled to
-// the stratum's width, so that the sample is spread over the whole row and follows no fixed
-// stride.
+// Sample i of S = 2^lgS of a row of n >= S keys.  The sample is S / 8 runs of 8 consecutive
+// keys (2 KB of bf16 keys: random single keys would cost a DRAM page each): run j lies in
+// stratum [j n / (S/8), (j + 1) n / (S/8)) at an offset picked by an integer hash of
+// (sequence, j) (the "lowbias32" mixer of C. Wellons) scaled to the stratum's width less 8,
+// so that the runs are spread over the whole row and follow no fixed stride.
 __device__ __forceinline__ int sample_pos(int b, int i, int n, int lgS) {
-    const int64_t lo = ((int64_t)i * n) >> lgS, hi = ((int64_t)(i + 1) * n) >> lgS;
-    uint32_t x = (uint32_t)i + 0x9E3779B9u * (uint32_t)(b + 1);
+    const int j = i >> 3, lgR = lgS - 3;
+    const int64_t lo = ((int64_t)j * n) >> lgR, hi = ((int64_t)(j + 1) * n) >> lgR;
+    uint32_t x = (uint32_t)j + 0x9E3779B9u * (uint32_t)(b + 1);
     x ^= x >> 16;
     x *= 0x7FEB352Du;
     x ^= x >> 15;
     x *= 0x846CA68Bu;
     x ^= x >> 16;
-    return (int)(lo + (int64_t)(((uint64_t)x * (uint64_t)(hi - lo)) >> 32));
+    return (int)(lo + (int64_t)(((uint64_t)x * (uint64_t)(hi - lo - 7)) >> 32)) + (i & 7);
 }
 
 // ---------------------------------------------------------------- key scorers
@@ -297,9 +302,62 @@ __device__ __forceinline__ float finish(const Sc &sc, const float (&p)[4], float
 }
 
 // ---------------------------------------------------------------- pass 1: plan
-// One workgroup per sequence.  With own_prefix it also writes cu[b] (and cu[B]).
+// S = 2^lgS samples of a row of n keys: at least n / 128 (1,024 .. 8,192).
+__device__ __forceinline__ int sample_lg(int n) {
+    int lgS = 10;
+    while (lgS < 13 && (1 << lgS) < n / 128) ++lgS;
+    return lgS;
+}
+
+// 1a. kSampleParts workgroups per sequence score a quarter of its sample each (one CU streams
+// only some 20 GB/s, so a single workgroup per sequence took 12 us for its 256 KB sample)
+// and write the order keys to the workspace.  Part 0 also writes cu[b] (own_prefix) and the
+// plan of a short row.
 template <class Sc, class Keys>
-__global__ __launch_bounds__(kPlanThreads) void decode_plan_kernel(DecCommon a, Keys kp, int own_prefix) {
+__global__ __launch_bounds__(kSampleThreads) void decode_sample_kernel(DecCommon a, Keys kp, int own_prefix) {
+    __shared__ int64_t red[kSampleThreads / 64];
+    const int b = blockIdx.x / kSampleParts, part = blockIdx.x % kSampleParts, tid = threadIdx.x;
+    const int lane = tid & 63, wave = tid >> 6;
+    const int l16 = lane & 15, lg = lane >> 4;
+    const int n = clamp_len(a, b);
+    if (own_prefix && part == 0) {
+        int64_t s = 0;
+        for (int i = tid; i < b; i += kSampleThreads) s += pad64(clamp_len(a, i));
+#pragma unroll
+        for (int d = 32; d >= 1; d >>= 1) s += __shfl_xor(s, d, 64);
+        if (lane == 0) red[wave] = s;
+        __syncthreads();
+        if (tid == 0) {
+            int64_t t = 0;
+#pragma unroll
+            for (int i = 0; i < kSampleThreads / 64; ++i) t += red[i];
+            a.cu[b] = t;
+            if (b == a.B - 1) a.cu[a.B] = t + pad64(n);
+        }
+    }
+    if (n <= kShortRow) {
+        if (part == 0 && tid == 0) a.plan[b] = DecodePlan{0u, 0u};
+        return;
+    }
+    const int lgS = sample_lg(n);
+    const int G = (1 << lgS) / 64 / kSampleParts;   // 64-key groups of this part
+    Sc sc;
+    sc.init(kp, a.start, b, l16, lg);
+    uint32_t *out = a.skey + (int64_t)b * kSampleMax;
+    for (int g = wave; g < G; g += kSampleThreads / 64) {
+        const int j = part * G + g;
+        int key[4];
+#pragma unroll
+        for (int u = 0; u < 4; ++u) key[u] = sample_pos(b, 64 * j + 16 * u + l16, n, lgS);
+        sc.load(key, lg);
+        float p[4];
+        sc.partial(p);
+        out[64 * j + lane] = score_key(finish(sc, p, sc.scale(), lg));
+    }
+}
+
+// 1b. One workgroup per sequence: the threshold from the sample keys.
+__global__ __launch_bounds__(kPlanThreads) void decode_threshold_kernel(DecCommon a) {
     __shared__ uint32_t skey[kSampleMax];
     __shared__ uint32_t hist[1024];
     __shared__ int64_t red[kPlanThreads / 64];
@@ -307,7 +365,7 @@ __global__ __launch_bounds__(kPlanThreads) void decode_plan_kernel(DecCommon a, 
     __shared__ int bc[2];
     const int b = blockIdx.x, tid = threadIdx.x;
     const int lane = tid & 63, wave = tid >> 6;
-    const int l16 = lane & 15, lg = lane >> 4;
+    constexpr int kWaves = kPlanThreads / 64;
     auto block_sum = [&](int64_t v) {
 #pragma unroll
         for (int d = 32; d >= 1; d >>= 1) v += __shfl_xor(v, d, 64);
@@ -315,52 +373,16 @@ __global__ __launch_bounds__(kPlanThreads) void decode_plan_kernel(DecCommon a, 
         __syncthreads();
         int64_t t = 0;
 #pragma unroll
-        for (int i = 0; i < kPlanThreads / 64; ++i) t += red[i];
+        for (int i = 0; i < kWaves; ++i) t += red[i];
         __syncthreads();
         return t;
     };
     const int n = clamp_len(a, b);
-    if (own_prefix) {
-        int64_t s = 0;
-        for (int i = tid; i < b; i += kPlanThreads) s += pad64(clamp_len(a, i));
-        s = block_sum(s);
-        if (tid == 0) {
-            a.cu[b] = s;
-            if (b == a.B - 1) a.cu[a.B] = s + pad64(clamp_len(a, b));
-        }
-    }
-    if (n <= kShortRow) {
-        if (tid == 0) a.plan[b] = DecodePlan{0u, 0u};
-        return;
-    }
-    // S = 2^lgS samples, at least n / 128 (1,024 .. 8,192)
-    int lgS = 10;
-    while (lgS < 13 && (1 << lgS) < n / 128) ++lgS;
-    const int S = 1 << lgS;
-    // sample scores, two 64-key groups in flight per wave
-    constexpr int kWaves = kPlanThreads / 64;
-    Sc s0, s1;
-    s0.init(kp, a.start, b, l16, lg);
-    s1.init(kp, a.start, b, l16, lg);
-    for (int j = wave; j < S / 64; j += 2 * kWaves) {
-        const int j1 = j + kWaves;
-        const bool two = j1 < S / 64;
-        int k0[4], k1[4];
-#pragma unroll
-        for (int u = 0; u < 4; ++u) {
-            k0[u] = sample_pos(b, 64 * j + 16 * u + l16, n, lgS);
-            k1[u] = two ? sample_pos(b, 64 * j1 + 16 * u + l16, n, lgS) : k0[u];
-        }
-        s0.load(k0, lg);
-        s1.load(k1, lg);
-        float p[4];
-        s0.partial(p);
-        skey[64 * j + lane] = score_key(finish(s0, p, s0.scale(), lg));
-        if (two) {
-            s1.partial(p);
-            skey[64 * j1 + lane] = score_key(finish(s1, p, s1.scale(), lg));
-        }
-    }
+    if (n <= kShortRow) return;   // planned by the sample pass
+    const int S = 1 << sample_lg(n);
+    const uint32_t *in = a.skey + (int64_t)b * kSampleMax;
+    for (int x = 4 * tid; x < S; x += 4 * kPlanThreads)
+        *reinterpret_cast<u32x4 *>(&skey[x]) = *reinterpret_cast<const u32x4 *>(in + x);
     __syncthreads();
     // r such that fewer than r of the S samples reach the topk-th largest score of the row
     // only with negligible probability (their number is about binomial with mean E)
@@ -816,6 +838,7 @@ hipError_t run_decode(const Keys &kp, const int64_t *start, const int32_t *seqle
     a.cnt = w.cnt;
     a.cand = reinterpret_cast<uint2 *>(w.cand);
     a.score_buf = w.score_buf;
+    a.skey = w.skey;
     a.ld = decode_row_stride(max_seqlen);
     a.idx = idx;
     a.scores = scores;
@@ -828,8 +851,12 @@ hipError_t run_decode(const Keys &kp, const int64_t *start, const int32_t *seqle
         hipError_t e = hipGetLastError();
         if (e != hipSuccess) return e;
     }
-    hipLaunchKernelGGL((decode_plan_kernel<Sc, Keys>), dim3(B), dim3(kPlanThreads), 0, stream, a, kp, own);
+    hipLaunchKernelGGL((decode_sample_kernel<Sc, Keys>), dim3(B * kSampleParts), dim3(kSampleThreads), 0, stream,
+                       a, kp, own);
     hipError_t e = hipGetLastError();
+    if (e != hipSuccess) return e;
+    hipLaunchKernelGGL(decode_threshold_kernel, dim3(B), dim3(kPlanThreads), 0, stream, a);
+    e = hipGetLastError();
     if (e != hipSuccess) return e;
     hipLaunchKernelGGL((decode_filter_kernel<Sc, Keys>), dim3(a.filter_grid), dim3(kFilterThreads), 0, stream, a, kp);
     e = hipGetLastError();
@@ -856,6 +883,7 @@ size_t decode_workspace(int B, int max_seqlen, bool fp8, DecodeWs *w, void *base
     const size_t o_cnt = take(4u * (flat / 64 + 1));
     const size_t o_cand = take(8u * flat);
     const size_t o_sb = take(4u * flat);
+    const size_t o_sk = take(4u * Bs * kSampleMax);
     const size_t o_q8 = fp8 ? take(Bs * kQOut) : 0;
     const size_t o_qw = fp8 ? take(4u * Bs * kHeads) : 0;
     if (w && base) {
@@ -865,6 +893,7 @@ size_t decode_workspace(int B, int max_seqlen, bool fp8, DecodeWs *w, void *base
         w->cnt = reinterpret_cast<int32_t *>(p + o_cnt);
         w->cand = reinterpret_cast<uint64_t *>(p + o_cand);
         w->score_buf = reinterpret_cast<float *>(p + o_sb);
+        w->skey = reinterpret_cast<uint32_t *>(p + o_sk);
         w->q8 = fp8 ? reinterpret_cast<uint8_t *>(p + o_q8) : nullptr;
         w->qw = fp8 ? reinterpret_cast<float *>(p + o_qw) : nullptr;
     }

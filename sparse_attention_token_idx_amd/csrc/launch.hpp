@@ -59,6 +59,7 @@ struct DecodeWs {
     int32_t *cnt;       // candidate counts per piece
     uint64_t *cand;     // candidate lists, flat-indexed
     float *score_buf;   // [B][decode_row_stride(max_seqlen)]
+    uint32_t *skey;     // [B][8192] sampled score keys of the plan pass
     uint8_t *q8;        // FP8 path: [B][32][128] query codes
     float *qw;          // FP8 path: [B][32] folded head weights
 };

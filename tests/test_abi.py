@@ -58,13 +58,14 @@ def test_workspace_sizes(dsa):
     assert dsa.workspace_size(dsa.OP_SCORE_TOPK_VARLEN, 16, 2, 8, topk=5) == 256 + 512 + 4 * vb
     # decode: 256-byte aligned parts over the padded positions P = B * 64 * ceil(max / 64):
     # B + 1 cache offsets, B plans (8 bytes), P / 64 + 1 piece counts, P candidate slots of
-    # 8 bytes, P fp32 scores; FP8 adds the quantised queries (B x 4096 bytes) and their folded
-    # head weights (B x 32 fp32)
+    # 8 bytes, P fp32 scores, 8,192 sampled score keys per sequence; FP8 adds the quantised
+    # queries (B x 4096 bytes) and their folded head weights (B x 32 fp32)
     def dec(B, m, fp8=False):
         P = B * 64 * ((m + 63) // 64)
-        n = r256(8 * (B + 1)) + r256(8 * B) + r256(4 * (P // 64 + 1)) + r256(8 * P) + r256(4 * P)
+        n = (r256(8 * (B + 1)) + r256(8 * B) + r256(4 * (P // 64 + 1)) + r256(8 * P) + r256(4 * P)
+             + r256(4 * 8192 * B))
         return n + (r256(B * 4096) + r256(128 * B) if fp8 else 0)
-    assert dec(64, 131072) == 101189120 and dec(3, 100) == 5376 and dec(3, 100, True) == 18176
+    assert dec(64, 131072) == 101189120 + 2097152 and dec(3, 100) == 5376 + 98304
     assert dsa.workspace_size(dsa.OP_DECODE, 0, 64, 131072, 2048) == dec(64, 131072)
     assert dsa.workspace_size(dsa.OP_DECODE, 0, 3, 100, 8) == dec(3, 100)
     assert dsa.workspace_size(dsa.OP_DECODE_FP8, 0, 3, 100, 8) == dec(3, 100, True)

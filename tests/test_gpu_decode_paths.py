@@ -26,8 +26,9 @@ def _bf(x):
 
 
 def _sample_positions(b, n):
-    """The plan pass's sample of row b (n keys): S = 2^lgS >= n / 128 strata (1,024 .. 8,192);
-    in stratum i the offset is an integer hash of (b, i) scaled to the stratum width."""
+    """The plan pass's sample of row b (n keys): S = 2^lgS >= n / 128 keys (1,024 .. 8,192) in
+    S / 8 runs of 8 consecutive keys; run j lies in stratum j of S / 8 at an offset that is an
+    integer hash of (b, j) scaled to the stratum width less 8."""
     lgS = 10
     while lgS < 13 and (1 << lgS) < n // 128:
         lgS += 1
@@ -35,14 +36,15 @@ def _sample_positions(b, n):
     M = 0xFFFFFFFF
     pos = []
     for i in range(S):
-        lo, hi = (i * n) >> lgS, ((i + 1) * n) >> lgS
-        x = (i + 0x9E3779B9 * (b + 1)) & M
+        j = i >> 3
+        lo, hi = (j * n) >> (lgS - 3), ((j + 1) * n) >> (lgS - 3)
+        x = (j + 0x9E3779B9 * (b + 1)) & M
         x ^= x >> 16
         x = (x * 0x7FEB352D) & M
         x ^= x >> 15
         x = (x * 0x846CA68B) & M
         x ^= x >> 16
-        pos.append(lo + ((x * (hi - lo)) >> 32))
+        pos.append(lo + ((x * (hi - lo - 7)) >> 32) + (i & 7))
     return np.asarray(pos)
 
 
