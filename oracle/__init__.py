@@ -76,6 +76,8 @@ def lib():
         L.oracle_pow2_scale_exp.argtypes = [f64]
         L.oracle_quantize_e4m3.restype = None
         L.oracle_quantize_e4m3.argtypes = [vp, i64, i32, vp, vp]
+        L.oracle_sparse_mla.restype = None
+        L.oracle_sparse_mla.argtypes = [vp, vp, vp, vp, i64, i32, i32, f64, vp, vp]
         L.oracle_rows_fp8.restype = None
         L.oracle_rows_fp8.argtypes = [vp, vp, vp, vp, vp, vp, vp, i64, i32, i32, i32, vp, vp, vp, vp,
                                       vp, vp]
@@ -274,3 +276,24 @@ def rows_fp8(q_rows, w_rows, k_codes, k_exps, k_off, t, topk=TOPK, full=False):
     if full:
         out["full"] = [fbuf[foff[j]:foff[j] + t[j] + 1] for j in range(R)]
     return out
+
+
+# ---------------------------------------------------------------- sparse MLA consumer
+MLA_HEADS, MLA_KV, MLA_V = 96, 576, 512
+
+
+def sparse_mla(q, kv, idx, row0=None, scale=1.0 / np.sqrt(192.0)):
+    """Sparse MLA over the selected tokens (gated-MLA row of the "Qwen3.5-397B-A17B vs Kimi
+    K3.1 Pro" page, absorbed-query reading): q [T,H,576] bf16, kv [*,576] bf16, idx [T,K] int32
+    (-1 = none), row0 [T] or None.  Returns (o [T,H,512] f64, lse [T,H] f64)."""
+    q = _c(q, np.uint16)
+    T, Hh, Dk = q.shape
+    assert Dk == MLA_KV
+    kv = _c(kv, np.uint16)
+    idx = _c(idx, np.int32)
+    K = idx.shape[1]
+    r0 = None if row0 is None else _c(row0, np.int64)
+    o = np.empty((T, Hh, MLA_V), np.float64)
+    lse = np.empty((T, Hh), np.float64)
+    lib().oracle_sparse_mla(_p(q), _p(kv), _p(idx), _p(r0), T, Hh, K, float(scale), _p(o), _p(lse))
+    return o, lse

@@ -39,6 +39,18 @@
  * only rounding is round-to-nearest-even onto E4M3.  The score of the FP8
  * path is the same formula on the dequantised q and k, in double.
  *
+ * Sparse MLA over the selected tokens (the consumer of the selection, a next step on the
+ * same pages: "Qwen3.5-397B-A17B vs Kimi K3.1 Pro" page, gated-MLA row -- 96 heads, keys and
+ * values from a 512-dim latent plus a 64-dim shared key slot, 576 cached values per token,
+ * q/k head dim 192, v head dim 128, each query attending only to the 2,048 tokens its layer's
+ * indexer selects; no rotary step, RoPE row of the "Kimi K3.1 Pro vs Gemma 4 31B" page).  The
+ * reading: queries come in the absorbed latent form (the key up-projection folded into the
+ * 128 no-position dims of each head, the 64 key-slot dims as they are), so head h's logit
+ * for token s is scale * q~_h . kv[s] over the 576 cached values, the softmax runs over the
+ * selected tokens only, and the head's output is the softmax-weighted sum of the 512-dim
+ * latents (the value up-projection, the output gate and the output projection follow as
+ * dense products).
+ *
  * Shares no code, header or table with the HIP implementation.
  */
 #include <math.h>
@@ -368,5 +380,56 @@ void oracle_rows_fp8(const uint8_t *qc, const int32_t *qe, const uint16_t *w_row
                     maxabs + r);
         free(qd); free(kd); free(wq);
         if (!full) free(I);
+    }
+}
+
+/* ---- sparse MLA over the selected tokens ----
+ * q [T][H][576] bf16 (absorbed queries), kv [*][576] bf16 (cache rows: 512-dim latent, then
+ * the 64-dim key slot), idx [T][K] int32 (selected rows relative to row0[t]; -1 = no token),
+ * row0 [T] (NULL: 0).  For query t and head h, over the valid selections j:
+ *   z_j = scale * sum_d q[t][h][d] kv[r_j][d]
+ *   o[t][h][:] = sum_j exp(z_j - m) kv[r_j][0:512] / sum_j exp(z_j - m),   m = max_j z_j
+ *   lse[t][h] = m + log(sum_j exp(z_j - m))
+ * in double, j ascending.  No valid selection: o = 0, lse = -inf. */
+enum { OR_MLA_KV = 576, OR_MLA_V = 512 };
+void oracle_sparse_mla(const uint16_t *q, const uint16_t *kv, const int32_t *idx, const int64_t *row0,
+                       int64_t T, int H, int K, double scale, double *o, double *lse) {
+#pragma omp parallel for schedule(dynamic, 1)
+    for (int64_t t = 0; t < T; ++t) {
+        double *z = (double *)malloc(sizeof(double) * (size_t)K);
+        double *qd = (double *)malloc(sizeof(double) * OR_MLA_KV);
+        for (int h = 0; h < H; ++h) {
+            const uint16_t *qh = q + ((size_t)t * H + h) * OR_MLA_KV;
+            for (int d = 0; d < OR_MLA_KV; ++d) qd[d] = oracle_bf16_to_f64(qh[d]);
+            double m = -INFINITY;
+            for (int j = 0; j < K; ++j) {
+                const int32_t s = idx[t * (int64_t)K + j];
+                if (s < 0) continue;
+                const uint16_t *kr = kv + (size_t)((row0 ? row0[t] : 0) + s) * OR_MLA_KV;
+                double dot = 0.0;
+                for (int d = 0; d < OR_MLA_KV; ++d) dot += qd[d] * oracle_bf16_to_f64(kr[d]);
+                z[j] = scale * dot;
+                if (z[j] > m) m = z[j];
+            }
+            double *oh = o + ((size_t)t * H + h) * OR_MLA_V;
+            for (int d = 0; d < OR_MLA_V; ++d) oh[d] = 0.0;
+            if (m == -INFINITY) {
+                lse[t * H + h] = -INFINITY;
+                continue;
+            }
+            double l = 0.0;
+            for (int j = 0; j < K; ++j) {
+                const int32_t s = idx[t * (int64_t)K + j];
+                if (s < 0) continue;
+                const double p = exp(z[j] - m);
+                const uint16_t *kr = kv + (size_t)((row0 ? row0[t] : 0) + s) * OR_MLA_KV;
+                for (int d = 0; d < OR_MLA_V; ++d) oh[d] += p * oracle_bf16_to_f64(kr[d]);
+                l += p;
+            }
+            for (int d = 0; d < OR_MLA_V; ++d) oh[d] /= l;
+            lse[t * H + h] = m + log(l);
+        }
+        free(z);
+        free(qd);
     }
 }
