@@ -75,6 +75,7 @@ extern "C" {
 #define DSA_IDX_OP_DECODE 3
 #define DSA_IDX_OP_DECODE_FP8 4
 #define DSA_IDX_OP_PREFILL_CHUNK 5
+#define DSA_IDX_OP_SPARSE_MLA 6
 
 typedef uint16_t dsa_idx_bf16;
 
@@ -97,12 +98,12 @@ const char *dsa_idx_last_error(void);
 
 /* Bytes of workspace an operation needs (host-only, no device access).
  *   op               one of DSA_IDX_OP_*
- *   total_tokens     T for PROJECT and SCORE_TOPK; the packed token count for VARLEN; the
- *                    chunk's query count C for PREFILL_CHUNK
+ *   total_tokens     T for PROJECT, SCORE_TOPK and SPARSE_MLA; the packed token count for
+ *                    VARLEN; the chunk's query count C for PREFILL_CHUNK
  *   B                number of sequences (VARLEN, DECODE); ignored otherwise
  *   max_seqlen       longest sequence (VARLEN, DECODE), keys of the longest cache for DECODE;
  *                    the cached prefix length for PREFILL_CHUNK
- *   topk             tokens kept per query, 1..2048
+ *   topk             tokens kept (selected, for SPARSE_MLA) per query, 1..2048
  * Writes *bytes (0 is a valid answer).  Returns a status. */
 int dsa_idx_workspace_size(int op, int64_t total_tokens, int B, int max_seqlen, int topk,
                            size_t *bytes);
@@ -219,6 +220,29 @@ int dsa_idx_decode_fp8(const dsa_idx_bf16 *q, const dsa_idx_bf16 *w, const uint8
                        const float *k_scale, const int64_t *start, const int32_t *seqlens, int B,
                        int max_seqlen, int topk, int32_t *idx, float *scores, void *ws,
                        size_t ws_bytes, void *stream);
+
+/* ---- The consumer of the selection: sparse MLA over the selected tokens ("Qwen3.5-397B-A17B
+ * vs Kimi K3.1 Pro" page, gated-MLA row: 96 heads, keys and values from a 512-dim latent plus
+ * a 64-dim shared key slot -- 576 cached values per token -- q/k head dim 192, v head dim
+ * 128, each query attending only to the 2,048 tokens its layer's indexer selects; no rotary
+ * step, RoPE row of the "Kimi K3.1 Pro vs Gemma 4 31B" page).  Queries come in the absorbed
+ * latent form (the key up-projection folded into each head's 128 no-position dims, its 64
+ * key-slot dims as they are), so for query t and head h over its valid selections j:
+ *   z_j = scale * q[t][h] . kv[row0[t] + idx[t][j]]                (576 values)
+ *   o[t][h] = sum_j exp(z_j - m) kv[row_j][0:512] / sum_j exp(z_j - m),   m = max_j z_j
+ *   lse[t][h] = m + ln(sum_j exp(z_j - m))
+ * The value up-projection, the output gate and the output projection that follow are dense
+ * products and not part of this call.
+ *   q [T][96][576] bf16, kv [*][576] bf16 (16-byte aligned; row 0 must exist: it stands in
+ *   for empty slots), idx [T][topk] int32 (-1: no token), row0 (device int64 [T], or NULL for
+ *   0), scale > 0 (the pages' q/k head dim 192 gives 1/sqrt(192)),
+ *   o [T][96][512] bf16 (rounded to nearest even), lse [T][96] fp32 natural log (may be NULL).
+ * A query with no valid selection gets o = 0 and lse = -inf.  Logits and the softmax are fp32;
+ * the probabilities enter the weighted sum rounded to bf16.
+ * Needs dsa_idx_workspace_size(DSA_IDX_OP_SPARSE_MLA, T, 0, 0, topk) bytes. */
+int dsa_idx_sparse_mla(const dsa_idx_bf16 *q, const dsa_idx_bf16 *kv, const int32_t *idx,
+                       const int64_t *row0, int64_t T, int topk, float scale, dsa_idx_bf16 *o,
+                       float *lse, void *ws, size_t ws_bytes, void *stream);
 
 #ifdef __cplusplus
 }

@@ -15,13 +15,15 @@ import torch
 
 __all__ = ["version", "workspace_size", "project", "score_topk", "score_topk_varlen", "decode",
            "prefill_scores", "prefill_select", "score_row", "quantize_keys", "decode_fp8",
-           "prefill_chunk", "HEADS", "DIM", "QLAT", "QOUT", "HIDDEN", "MAX_TOPK", "OP_PROJECT",
+           "prefill_chunk", "sparse_mla", "OP_SPARSE_MLA", "HEADS", "DIM", "QLAT", "QOUT", "HIDDEN", "MAX_TOPK", "OP_PROJECT",
            "OP_SCORE_TOPK", "OP_SCORE_TOPK_VARLEN", "OP_DECODE", "OP_DECODE_FP8",
            "OP_PREFILL_CHUNK", "DsaIdxError", "lib"]
 
 HEADS, DIM, QLAT, QOUT, HIDDEN, MAX_TOPK = 32, 128, 1536, 4096, 7168, 2048
 OP_PROJECT, OP_SCORE_TOPK, OP_SCORE_TOPK_VARLEN, OP_DECODE, OP_DECODE_FP8 = 0, 1, 2, 3, 4
 OP_PREFILL_CHUNK = 5
+OP_SPARSE_MLA = 6
+MLA_HEADS, MLA_KV, MLA_V = 96, 576, 512
 
 _HERE = os.path.dirname(os.path.abspath(__file__))
 LIB_PATH = os.path.join(_HERE, "libdsaidx.so")
@@ -71,6 +73,8 @@ def lib():
         L.dsa_idx_prefill_select.argtypes = [vp, i32, i32, i64, i32, vp, vp, vp, sz, vp]
         L.dsa_idx_prefill_chunk.restype = i32
         L.dsa_idx_prefill_chunk.argtypes = [vp, vp, vp, i64, i64, i32, vp, vp, vp, sz, vp]
+        L.dsa_idx_sparse_mla.restype = i32
+        L.dsa_idx_sparse_mla.argtypes = [vp, vp, vp, vp, i64, i32, ctypes.c_float, vp, vp, vp, sz, vp]
         L.dsa_idx_decode.restype = i32
         L.dsa_idx_decode.argtypes = [vp, vp, vp, vp, vp, i32, i32, i32, vp, vp, vp, sz, vp]
         L.dsa_idx_quantize_keys.restype = i32
@@ -276,6 +280,35 @@ def prefill_chunk(q, k, w, prefix, topk=MAX_TOPK, with_scores=True, ws=None, out
            lib().dsa_idx_prefill_chunk(_ptr(q), _ptr(k), _ptr(w), C, int(prefix), topk, _ptr(idx),
                                        _ptr(sc), _ptr(ws), nbytes, _stream(stream)))
     return idx, sc
+
+
+def sparse_mla(q, kv, idx, row0=None, scale=192.0 ** -0.5, with_lse=True, ws=None, out=None,
+               stream=None):
+    """Sparse MLA over the selected tokens: q [T,96,576] bf16 (absorbed queries), kv [*,576]
+    bf16 (latent cache rows), idx [T,topk] int32 (-1: none), row0 int64 [T] or None ->
+    o [T,96,512] bf16, lse [T,96] float32 (or None)."""
+    T = q.shape[0]
+    _need(q, "q", torch.bfloat16, (T, MLA_HEADS, MLA_KV))
+    _need(kv, "kv", torch.bfloat16)
+    if kv.dim() != 2 or kv.shape[1] != MLA_KV:
+        raise ValueError("kv must be [rows, 576]")
+    _need(idx, "idx", torch.int32)
+    if idx.dim() != 2 or idx.shape[0] != T:
+        raise ValueError("idx must be [T, topk]")
+    topk = idx.shape[1]
+    if row0 is not None:
+        _need(row0, "row0", torch.int64, (T,))
+    if out is None:
+        o = torch.empty((T, MLA_HEADS, MLA_V), dtype=torch.bfloat16, device=q.device)
+        lse = torch.empty((T, MLA_HEADS), dtype=torch.float32, device=q.device) if with_lse else None
+    else:
+        o, lse = out
+    nbytes = workspace_size(OP_SPARSE_MLA, T, 0, 0, topk)
+    ws = _workspace(nbytes, q.device, ws)
+    _check("dsa_idx_sparse_mla",
+           lib().dsa_idx_sparse_mla(_ptr(q), _ptr(kv), _ptr(idx), _ptr(row0), T, topk, float(scale),
+                                    _ptr(o), _ptr(lse), _ptr(ws), nbytes, _stream(stream)))
+    return o, lse
 
 
 def decode(q, w, k_cache, start, seqlens, max_seqlen, topk=MAX_TOPK, with_scores=True, ws=None,

@@ -6,6 +6,7 @@
 
 #include <hip/hip_runtime.h>
 
+#include <cmath>
 #include <cstdarg>
 #include <cstdio>
 #include <cstring>
@@ -143,6 +144,13 @@ int dsa_idx_workspace_size(int op, int64_t total_tokens, int B, int max_seqlen, 
             int r = check_topk(topk);
             if (r) return r;
             *bytes = total_tokens == 0 ? 0 : ws_prefill_chunk(total_tokens, max_seqlen);
+            return ok();
+        }
+        case DSA_IDX_OP_SPARSE_MLA: {
+            if (total_tokens < 0) return fail(DSA_IDX_EINVAL, "T=%lld < 0", (long long)total_tokens);
+            int r = check_topk(topk);
+            if (r) return r;
+            *bytes = dsaidx::sparse_mla_workspace(total_tokens, topk);
             return ok();
         }
         case DSA_IDX_OP_DECODE:
@@ -341,6 +349,29 @@ int dsa_idx_prefill_chunk(const dsa_idx_bf16 *q, const dsa_idx_bf16 *k, const ds
     if (e != hipSuccess) return hip_fail("scores launch", e);
     e = dsaidx::launch_row_topk_prefill(rows, nullptr, base, 1, C, prefix, C, topk, idx, scores, st);
     if (e != hipSuccess) return hip_fail("row top-k launch", e);
+    return ok();
+}
+
+int dsa_idx_sparse_mla(const dsa_idx_bf16 *q, const dsa_idx_bf16 *kv, const int32_t *idx,
+                       const int64_t *row0, int64_t T, int topk, float scale, dsa_idx_bf16 *o,
+                       float *lse, void *ws, size_t ws_bytes, void *stream) {
+    if (T < 0) return fail(DSA_IDX_EINVAL, "T=%lld < 0", (long long)T);
+    int r = check_topk(topk);
+    if (r) return r;
+    if (T == 0) return ok();
+    if (!q || !kv || !idx || !o) return fail(DSA_IDX_EINVAL, "a tensor pointer is NULL");
+    if (!aligned16(q) || !aligned16(kv) || !aligned16(o)) return fail(DSA_IDX_EINVAL, "q, kv and o must be 16-byte aligned");
+    if (!(scale > 0.f) || !(scale < INFINITY)) return fail(DSA_IDX_EINVAL, "scale must be positive and finite");
+    if (T > 65535) return fail(DSA_IDX_EUNSUPPORTED, "T=%lld above 65535", (long long)T);
+    const size_t need = dsaidx::sparse_mla_workspace(T, topk);
+    if (need > 0 && (!ws || ws_bytes < need))
+        return fail(DSA_IDX_EWORKSPACE, "workspace %zu bytes < %zu needed", ws ? ws_bytes : (size_t)0, need);
+    if (need > 0 && !aligned16(ws)) return fail(DSA_IDX_EINVAL, "workspace must be 16-byte aligned");
+    r = check_device();
+    if (r) return r;
+    hipError_t e = dsaidx::launch_sparse_mla(q, kv, idx, row0, T, topk, scale, o, lse, static_cast<float *>(ws),
+                                             reinterpret_cast<hipStream_t>(stream));
+    if (e != hipSuccess) return hip_fail("sparse_mla launch", e);
     return ok();
 }
 

@@ -79,4 +79,12 @@ hipError_t launch_decode_fp8(const uint16_t *q, const uint16_t *w, const uint8_t
                              const int64_t *start, const int32_t *seqlens, int B, int max_seqlen, int topk,
                              void *ws, int32_t *idx, float *scores, hipStream_t stream);
 
+// ---- sparse MLA over the selected tokens (mla.hip).  Workspace: sparse_mla_workspace(T, topk)
+// bytes (the splits' partial outputs; 0 when one split per query).
+int sparse_mla_splits(int64_t T, int topk);
+size_t sparse_mla_workspace(int64_t T, int topk);
+hipError_t launch_sparse_mla(const uint16_t *q, const uint16_t *kv, const int32_t *idx, const int64_t *row0,
+                             int64_t T, int topk, float scale, uint16_t *o, float *lse, float *ws,
+                             hipStream_t stream);
+
 }  // namespace dsaidx

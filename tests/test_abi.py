@@ -30,7 +30,8 @@ def test_exports_every_declared_symbol(dsa):
     assert set(names) == {"dsa_idx_version", "dsa_idx_last_error", "dsa_idx_workspace_size",
                           "dsa_idx_project", "dsa_idx_score_topk", "dsa_idx_score_topk_varlen",
                           "dsa_idx_prefill_scores", "dsa_idx_prefill_select", "dsa_idx_decode",
-                          "dsa_idx_quantize_keys", "dsa_idx_decode_fp8", "dsa_idx_prefill_chunk"}
+                          "dsa_idx_quantize_keys", "dsa_idx_decode_fp8", "dsa_idx_prefill_chunk",
+                          "dsa_idx_sparse_mla"}
     for n in names:
         assert getattr(L, n) is not None
 
@@ -76,6 +77,11 @@ def test_workspace_sizes(dsa):
     assert dsa.workspace_size(dsa.OP_PREFILL_CHUNK, 1000, 0, 0, 8) == \
         dsa.workspace_size(dsa.OP_SCORE_TOPK, 1000, topk=8)
     assert dsa.workspace_size(dsa.OP_PREFILL_CHUNK, 0, 0, 5000, 8) == 0
+    # sparse MLA: the splits' fp32 partial outputs and (max, sum) per (split, query, head), only
+    # when a query's selections are split over several workgroups (few queries)
+    assert dsa.workspace_size(dsa.OP_SPARSE_MLA, 5000, 0, 0, 2048) == 0
+    n64 = dsa.workspace_size(dsa.OP_SPARSE_MLA, 64, 0, 0, 2048)
+    assert n64 > 0 and n64 % (64 * 96 * 514 * 4) == 0
     with pytest.raises(dsa.DsaIdxError) as e:
         dsa.workspace_size(dsa.OP_SCORE_TOPK, 10, topk=0)
     assert e.value.code == -2
@@ -148,6 +154,16 @@ def test_rejections_before_device(dsa):
                  None) == -2
     assert b"prefix + C" in L.dsa_idx_last_error()
     assert chunk(None, None, None, 0, 100, 8, None, None, None, 0, None) == 0
+    # sparse MLA
+    mla = lambda *a: L.dsa_idx_sparse_mla(*a)
+    f = ctypes.c_float
+    assert mla(_vp(A), _vp(A), _vp(A), None, 4, 0, f(0.1), _vp(A), None, _vp(A), 1 << 30, None) == -2
+    assert mla(_vp(A), _vp(A), _vp(A), None, -1, 8, f(0.1), _vp(A), None, _vp(A), 1 << 30, None) == -1
+    assert mla(_vp(A), None, _vp(A), None, 4, 8, f(0.1), _vp(A), None, _vp(A), 1 << 30, None) == -1
+    assert mla(_vp(A + 4), _vp(A), _vp(A), None, 4, 8, f(0.1), _vp(A), None, _vp(A), 1 << 30, None) == -1
+    assert mla(_vp(A), _vp(A), _vp(A), None, 4, 8, f(0.0), _vp(A), None, _vp(A), 1 << 30, None) == -1
+    assert mla(_vp(A), _vp(A), _vp(A), None, 64, 2048, f(0.1), _vp(A), None, _vp(A), 16, None) == -3
+    assert mla(None, None, None, None, 0, 8, f(0.1), None, None, None, 0, None) == 0
 
 
 def test_project_rejections(dsa):
