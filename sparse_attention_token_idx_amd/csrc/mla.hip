@@ -9,16 +9,19 @@
 // products).
 //
 // One workgroup takes one query and a contiguous split of its selections; its 12 waves pair up
-// on 16 heads each, one wave of a pair taking the first half of the 576 logit dims and of the
-// 512 output dims, the other the second halves, so that a wave holds its query slice (36
-// VGPRs) and its output (64) with three waves per SIMD.  The selected cache rows stream
-// through LDS 32 at a time with direct global->LDS loads (double-buffered): row-major for the
-// logits S^T = K q~^T (v_mfma_f32_16x16x32_bf16, the wave's q~ as the B operand), whose two
-// halves the pair adds through LDS, and transposed (latent dim major) for O^T += V^T P^T,
-// whose B operand is the wave's probabilities straight from the logit accumulators (the 32
-// tokens of a tile taken in the order the accumulators hold them).  The softmax is online, in
-// the log2 domain; with several splits per query, a second kernel merges the splits' (max,
-// sum, unnormalised output).
+// on 16 heads each, the two waves of a pair taking alternate 32-dim k-steps of the 576 logit
+// dims and alternate 16-dim tiles of the 512 output dims, so that a wave holds its query
+// slice (36 VGPRs) and its output (64) with three waves per SIMD.  The selected cache rows
+// stream through LDS 32 at a time with direct global->LDS loads, three tiles deep, row-major
+// (a token's 72 16-byte pieces in a row, the piece order swizzled by the token so that the
+// rows one operand read touches fall in different banks).  The logits S^T = K q~^T
+// (v_mfma_f32_16x16x32_bf16, the wave's q~ as the B operand) take K straight from those rows;
+// the pair adds its two halves through LDS.  The output O^T += V^T P^T takes V^T from the same
+// rows with the transposing LDS read of gfx950 (ds_read_b64_tr_b16: each 16-lane group loads 4
+// tokens x 16 dims and every lane receives one dim of the 4 tokens), and P^T straight from the
+// logit accumulators (the 32 tokens of a tile taken in the order the accumulators hold them).
+// The softmax is online, in the log2 domain; with several splits per query, a second kernel
+// merges the splits' (max, sum, unnormalised output).
 #include "common.hpp"
 #include "launch.hpp"
 
@@ -34,20 +37,34 @@ constexpr int kTile = 32;                // selected tokens per LDS tile
 constexpr int kPieces = kKv / 8;         // 16-byte pieces of a cache row: 72
 constexpr int kSlots = kTile * kPieces;  // of a tile: 2,304 = 36 load instructions of 64 lanes
 constexpr int kSlotsPerWave = kSlots / kMlaThreads;   // 3
-constexpr int kVRow = 36;                // bf16 per latent-dim row of the V^T area (72 bytes)
+constexpr int kBufs = 3;                 // tiles in LDS: the current one and two in flight
 constexpr int kMaxSel = 2048;            // selections per split held in LDS
-static_assert(kSlots % kMlaThreads == 0 && kPieces % 8 == 0, "tile geometry");
+constexpr int kTileBytes = kSlots * 16;
+constexpr int kHalfTileBytes = kTileBytes / 2;        // tokens 16..31 start here
+static_assert(kSlots % kMlaThreads == 0 && kPieces == 72 && kV == 512, "tile geometry");
 
 typedef __attribute__((address_space(3))) void lds_void;
+typedef __attribute__((address_space(3))) char lds_char;
+typedef short v4i16 __attribute__((ext_vector_type(4)));
+typedef __attribute__((address_space(3))) v4i16 lds_v4i16;
+typedef __attribute__((address_space(3))) u32x4 lds_u32x4;
 
 struct MlaSmem {
-    // token rows of two tiles: piece u of token tau sits in slot 72 tau + (u ^ (tau & 7)) (16
-    // bytes each), which spreads the 16 rows one MFMA operand read touches over the banks
-    uint16_t k[2][kSlots * 8];
-    uint16_t vt[kV][kVRow];      // the current tile, latent-dim major (token contiguous)
-    int32_t sel[kMaxSel];        // this split's selections (-1: none)
-    f32x4 sx[kWavesMla][2][64];  // each wave's half of the logits, for its partner
+    uint16_t k[kBufs][kSlots * 8];   // token tau's piece u sits in slot 72 tau + (u ^ swz(tau))
+    int32_t sel[kMaxSel];            // this split's selections (-1: none)
+    f32x4 sx[kWavesMla][2][64];      // each wave's half of the logits, for its partner
 };
+
+// Piece u of token tau sits at position u ^ swz(tau) among the token's 72 slots: a permutation
+// within each aligned group of 8 pieces, so that a piece's offset from the group start, and
+// hence every operand address below, is a per-lane base plus a constant.  The LDS serves 256
+// bytes (64 banks) at a time and the rows are 1,152 bytes apart, so rows of equal parity start
+// in the same bank, odd ones 128 bytes on.  swz takes all 8 values on the 8 even and on the 8
+// odd tokens of each 16 (a logit-operand read: 16 rows x 16 bytes), and 4 different even
+// values on the 4 tokens of equal parity among any 8 tokens 8 m .. 8 m + 7 (a transposing read:
+// 32 lanes, 8 tokens x 32 bytes), so that both fill the banks once.  An involution.
+__device__ __forceinline__ int swz(int tau) { return (2 * ((tau >> 1) & 3) + ((tau >> 3) & 1)) & 7; }
+constexpr float kLazy = 8.f;   // a head's reference max moves only when exceeded by 2^8
 
 struct MlaArgs {
     const uint16_t *q;       // [T][96][576]
@@ -65,23 +82,47 @@ struct MlaArgs {
     float *part_ml;          // [nsplit][T][96][2]: running max (log2 domain), sum
 };
 
-__device__ __forceinline__ uint32_t bf16_pair(float lo, float hi) { return pack_bf16x2(lo, hi); }
+typedef __bf16 bf16x2_t __attribute__((ext_vector_type(2)));
+typedef float f32x2_t __attribute__((ext_vector_type(2)));
+
+// Two floats to bf16 (round to nearest even), with gfx950's packing conversion.
+__device__ __forceinline__ uint32_t bf16_pair(float lo, float hi) {
+    return __builtin_bit_cast(uint32_t, __builtin_convertvector((f32x2_t{lo, hi}), bf16x2_t));
+}
+
+// 2^x with the hardware instruction: the arguments here are at most 8 (or -inf), and a result
+// below the normal range (a weight under 2^-126 of the largest) may flush to 0.
+__device__ __forceinline__ float exp2_hw(float x) { return __builtin_amdgcn_exp2f(x); }
 
 // Workgroup barrier over LDS traffic only: __syncthreads() would also wait for every global
-// load in flight, the next tile's included.
+// load in flight, the tiles ahead included.
 __device__ __forceinline__ void lds_barrier() { asm volatile("s_waitcnt lgkmcnt(0)\n\ts_barrier" ::: "memory"); }
 
+// One 16-byte-per-lane global->LDS load (lane i lands at lds_addr + 16 i).  Written out so that
+// the compiler, which cannot tell the tiles in flight from the one being read, does not wait for
+// them before every LDS read; the kernel counts these loads and waits for them itself.  The
+// instruction has no result registers and reads its address registers when it issues.
+__device__ __forceinline__ void dma16(const void *src, uint32_t lds_addr) {
+    asm volatile("s_mov_b32 m0, %1\n\ts_nop 0\n\tglobal_load_lds_dwordx4 %0, off" ::"v"(src), "s"(lds_addr) : "memory", "m0");
+}
+
+__device__ __forceinline__ uint2 tr_read(const lds_char *p) {
+    const v4i16 v = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_v4i16 *)p);
+    return __builtin_bit_cast(uint2, v);
+}
+
 __global__ __launch_bounds__(kMlaThreads, 1) void sparse_mla_kernel(MlaArgs a) {
-    static_assert(kV / 16 / 2 * 2 == kV / 16 && kKv / 32 % 2 == 0, "halves");
     extern __shared__ __align__(16) unsigned char smem_raw[];
     MlaSmem &sm = *reinterpret_cast<MlaSmem *>(smem_raw);
+    const lds_char *lds_k = (const lds_char *)smem_raw;   // the tile buffers start the area
     const int split = blockIdx.x;
     const int64_t t = blockIdx.y;
-    const int tid = threadIdx.x, wave = tid >> 6, lane = tid & 63;
+    const int tid = threadIdx.x, lane = tid & 63;
+    const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
     const int l16 = lane & 15, g = lane >> 4;
-    const int hg = wave >> 1, half = wave & 1;   // heads 16 hg .. + 15; dims half
-    constexpr int kKs = kKv / 32 / 2;             // logit k-steps of a half: 9
-    constexpr int kMt = kV / 16 / 2;              // 16-dim output tiles of a half: 16
+    const int hg = wave >> 1, half = wave & 1;   // heads 16 hg .. + 15; alternate k-steps / tiles
+    constexpr int kKs = kKv / 32 / 2;             // logit k-steps of a wave: 9
+    constexpr int kMt = kV / 16 / 2;              // 16-dim output tiles of a wave: 16
     const int sel0 = split * a.per;
     const int nsel = max(0, min(a.topk, sel0 + a.per) - sel0);
     const int ntile = (nsel + kTile - 1) / kTile;
@@ -90,76 +131,96 @@ __global__ __launch_bounds__(kMlaThreads, 1) void sparse_mla_kernel(MlaArgs a) {
         sm.sel[x] = x < nsel ? a.idx[t * (int64_t)a.topk + sel0 + x] : -1;
 
     // this wave's q~ as the B operand of S^T = K q~^T: lane (l16, g) holds head 16 hg + l16,
-    // dims 32 (kKs half + ks) + 8 g .. + 7
+    // dims 32 (2 ks + half) + 8 g .. + 7
     u32x4 qb[kKs];
     {
-        const uint16_t *qh = a.q + (t * kMlaHeads + 16 * hg + l16) * (int64_t)kKv + 32 * kKs * half + 8 * g;
+        const uint16_t *qh = a.q + (t * kMlaHeads + 16 * hg + l16) * (int64_t)kKv + 32 * half + 8 * g;
 #pragma unroll
-        for (int ks = 0; ks < kKs; ++ks) qb[ks] = *reinterpret_cast<const u32x4 *>(qh + 32 * ks);
+        for (int ks = 0; ks < kKs; ++ks) qb[ks] = *reinterpret_cast<const u32x4 *>(qh + 64 * ks);
+        // use them here, so that the compiler waits for these loads before the tile loop rather
+        // than inside it, where its count of loads in flight would not include the tiles'
+#pragma unroll
+        for (int ks = 0; ks < kKs; ++ks) asm volatile("" ::"v"(qb[ks]));
     }
     __syncthreads();   // sel
 
-    // A tile goes to LDS with direct global->LDS loads: slot 64 (6 wave + j) + lane of
-    // instruction j holds piece u = (slot % 72) ^ (tau & 7) of token tau = slot / 72.  A token
+    // A tile goes to LDS with direct global->LDS loads: lane i of instruction j of a wave fills
+    // slot 64 (3 wave + j) + i, i.e. piece (slot % 72) ^ swz(tau) of token tau = slot / 72.  A token
     // with no selection reads cache row 0 instead (its logit is masked, its weight is 0).
-    auto load_tile = [&](int tile, int buf) {
+    // Exactly kSlotsPerWave vector-memory instructions per tile and wave: the waits below count
+    // on it.
+    const char *kv_bytes = reinterpret_cast<const char *>(a.kv);
+    const uint32_t lds_k0 = (uint32_t)(uintptr_t)(lds_void *)sm.k[0];
+    auto load_tile = [&](int tile, int buf_off) {
+        // the slot geometry is recomputed per tile from the lane index, itself recomputed here
+        // (v_mbcnt): held across the loop it would cost registers the operands need
+        int ln;
+        asm volatile("v_mbcnt_lo_u32_b32 %0, -1, 0\n\tv_mbcnt_hi_u32_b32 %0, -1, %0" : "=v"(ln));
+        int tau[kSlotsPerWave];
+        int32_t r[kSlotsPerWave];
+#pragma unroll
+        for (int j = 0; j < kSlotsPerWave; ++j) {
+            tau[j] = (64 * (kSlotsPerWave * wave + j) + ln) / kPieces;
+            r[j] = sm.sel[tile * kTile + tau[j]];
+        }
 #pragma unroll
         for (int j = 0; j < kSlotsPerWave; ++j) {
             const int slot0 = 64 * (kSlotsPerWave * wave + j);
-            const int slot = slot0 + lane;
-            const int tau = slot / kPieces, u = (slot % kPieces) ^ (tau & 7);
-            const int32_t r = sm.sel[tile * kTile + tau];
-            const int64_t row = r >= 0 ? base + r : 0;
-            __builtin_amdgcn_global_load_lds(static_cast<const void *>(a.kv + row * kKv + 8 * u),
-                                             (lds_void *)(&sm.k[buf][8 * slot0]), 16, 0, 0);
-        }
-    };
-    // the latent part of a tile, transposed into vt: thread i < 512 takes 4 consecutive tokens
-    // 4 (i % 8) .. + 3 of piece u = i / 8 (8 dims) and writes each dim's 4 tokens as 8 bytes
-    auto transpose = [&](int buf) {
-        if (tid < (kTile / 4) * (kV / 8)) {
-            const int tq = tid & 7, u = tid >> 3;
-            u32x4 v[4];
-#pragma unroll
-            for (int x = 0; x < 4; ++x) {
-                const int tau = 4 * tq + x;
-                v[x] = *reinterpret_cast<const u32x4 *>(&sm.k[buf][8 * (kPieces * tau + (u ^ (tau & 7)))]);
-            }
-#pragma unroll
-            for (int j = 0; j < 4; ++j) {
-                // dims 8 u + 2 j (low halves) and 8 u + 2 j + 1 (high halves) of the 4 tokens
-                const uint2 lo = {(v[0][j] & 0xFFFFu) | (v[1][j] << 16), (v[2][j] & 0xFFFFu) | (v[3][j] << 16)};
-                const uint2 hi = {(v[0][j] >> 16) | (v[1][j] & 0xFFFF0000u), (v[2][j] >> 16) | (v[3][j] & 0xFFFF0000u)};
-                *reinterpret_cast<uint2 *>(&sm.vt[8 * u + 2 * j][4 * tq]) = lo;
-                *reinterpret_cast<uint2 *>(&sm.vt[8 * u + 2 * j + 1][4 * tq]) = hi;
-            }
+            const int slot = slot0 + ln;
+            const int u16 = 16 * ((slot - kPieces * tau[j]) ^ swz(tau[j]));
+            const int64_t row = r[j] >= 0 ? base + r[j] : 0;
+            dma16(kv_bytes + (row * (2 * kKv) + u16),
+                  __builtin_amdgcn_readfirstlane(lds_k0 + buf_off + 16 * slot0));
         }
     };
 
-    f32x4 acc_o[kMt];   // O^T: lane (l16, g) holds dims 256 half + 16 mt + 4 g + r of head 16 hg + l16
+    // LDS byte offsets (within a tile) of this lane's operand reads.  Logits, k-step ks: token
+    // l16 (and 16 + l16, kHalfTileBytes further: the same swizzle), piece 8 ks + 4 half + g, at
+    // qk_base + 128 ks.
+    const int qk_base = 16 * (kPieces * l16 + ((4 * half + g) ^ swz(l16)));
+    // Values, tile mt (dims 16 (2 mt + half) ..): this lane loads token 4 g + (l16 >> 2) (and
+    // 16 + that, kHalfTileBytes further), dims 4 (l16 & 3) .. + 3 of the tile, i.e. piece
+    // 4 mt + 2 half + ((l16 & 3) >> 1), bytes 8 (l16 & 1) .., at pv_base[mt & 1] + 128 (mt >> 1)
+    const int vtok = 4 * g + (l16 >> 2);
+    int pv_base[2];
+#pragma unroll
+    for (int m2 = 0; m2 < 2; ++m2)
+        pv_base[m2] = 16 * (kPieces * vtok + ((4 * m2 + 2 * half + ((l16 & 3) >> 1)) ^ swz(vtok))) + 8 * (l16 & 1);
+
+    f32x4 acc_o[kMt];   // O^T: lane (l16, g) holds dims 16 (2 mt + half) + 4 g + r of head 16 hg + l16
 #pragma unroll
     for (int mt = 0; mt < kMt; ++mt) acc_o[mt] = f32x4{0.f, 0.f, 0.f, 0.f};
     float m_run = -INFINITY;   // running max of the head's logits (log2 domain)
     float l_run = 0.f;         // this lane's part of the running sum
 
     if (ntile > 0) load_tile(0, 0);
-    __syncthreads();   // (waits for the loads)
-    if (ntile > 0) transpose(0);
-    __syncthreads();
+    if (ntile > 1) load_tile(1, kTileBytes);
+    // byte offset of the current tile's buffer, kept in a scalar register (computing it from
+    // the tile index costs vector instructions on every operand address)
+    int buf_off = 0;
 #pragma unroll 1
     for (int tile = 0; tile < ntile; ++tile) {
-        const int buf = tile & 1;
-        if (tile + 1 < ntile) load_tile(tile + 1, buf ^ 1);   // in flight during this tile
+        // this tile's loads have landed (the next tile's may still be in flight) ...
+        if (tile + 1 < ntile)
+            asm volatile("s_waitcnt vmcnt(3)" ::: "memory");
+        else
+            asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
+        // ... for every wave, and every wave is done with the previous tile, whose buffer the
+        // loads of tile + 2 now refill
+        lds_barrier();
+        const int prev_off = buf_off == 0 ? (kBufs - 1) * kTileBytes : buf_off - kTileBytes;
+        if (tile + 2 < ntile) load_tile(tile + 2, prev_off);   // tile + 2 takes the previous tile's buffer
+        const lds_char *kb = lds_k + __builtin_amdgcn_readfirstlane(buf_off);
+        buf_off = buf_off == (kBufs - 1) * kTileBytes ? 0 : buf_off + kTileBytes;
+
         // logits: S^T rows are tokens (two 16-token halves), columns the pair's 16 heads; this
-        // wave sums its half of the dims, the partner's half comes through LDS
+        // wave sums its k-steps, the partner's come through LDS
         f32x4 s0 = {0.f, 0.f, 0.f, 0.f}, s1 = {0.f, 0.f, 0.f, 0.f};
-        const uint16_t *kb = sm.k[buf];
 #pragma unroll
         for (int ks = 0; ks < kKs; ++ks) {
-            const int u = 4 * (kKs * half + ks) + g;
-            const u32x4 k0 = *reinterpret_cast<const u32x4 *>(kb + 8 * (kPieces * l16 + (u ^ (l16 & 7))));
-            const u32x4 k1 = *reinterpret_cast<const u32x4 *>(
-                kb + 8 * (kPieces * (16 + l16) + (u ^ (l16 & 7))));
+            const int off = qk_base + 128 * ks;
+            const u32x4 k0 = *(const lds_u32x4 *)(kb + off);
+            const u32x4 k1 = *(const lds_u32x4 *)(kb + off + kHalfTileBytes);
             s0 = mfma16x16x32(k0, qb[ks], s0);
             s1 = mfma16x16x32(k1, qb[ks], s1);
         }
@@ -175,54 +236,59 @@ __global__ __launch_bounds__(kMlaThreads, 1) void sparse_mla_kernel(MlaArgs a) {
             }
         }
         // lane (l16, g): head 16 hg + l16, tokens 4 g + r (s0) and 16 + 4 g + r (s1)
+        const int4 sa = *reinterpret_cast<const int4 *>(&sm.sel[tile * kTile + 4 * g]);
+        const int4 sb = *reinterpret_cast<const int4 *>(&sm.sel[tile * kTile + 16 + 4 * g]);
+        const int sv[8] = {sa.x, sa.y, sa.z, sa.w, sb.x, sb.y, sb.z, sb.w};
         float z[8];
 #pragma unroll
         for (int r = 0; r < 4; ++r) {
-            z[r] = sm.sel[tile * kTile + 4 * g + r] >= 0 ? s0[r] * a.scale_log2 : -INFINITY;
-            z[4 + r] = sm.sel[tile * kTile + 16 + 4 * g + r] >= 0 ? s1[r] * a.scale_log2 : -INFINITY;
+            z[r] = sv[r] >= 0 ? s0[r] * a.scale_log2 : -INFINITY;
+            z[4 + r] = sv[4 + r] >= 0 ? s1[r] * a.scale_log2 : -INFINITY;
         }
         float mx = z[0];
 #pragma unroll
         for (int r = 1; r < 8; ++r) mx = fmaxf(mx, z[r]);
         mx = fmaxf(mx, __shfl_xor(mx, 16, 64));
         mx = fmaxf(mx, __shfl_xor(mx, 32, 64));
-        const float m_new = fmaxf(m_run, mx);
+        // The reference max m_run only moves when the tile's max exceeds it by more than 2^8
+        // (so the weights below stay under 256): the output and sum are kept relative to m_run,
+        // and most tiles then need no rescaling at all.  Both waves of a pair hold the same
+        // logits, so they move it together.
+        const bool move = mx > m_run + kLazy;
+        const float m_new = move ? mx : m_run;
+        const float factor = move ? exp2_hw(m_run - m_new) : 1.f;   // 0 when m_run is -inf
         float p[8];
-        float factor = 1.f;
         if (m_new == -INFINITY) {
 #pragma unroll
             for (int r = 0; r < 8; ++r) p[r] = 0.f;
         } else {
-            factor = exp2f(m_run - m_new);   // 0 when m_run is -inf
 #pragma unroll
-            for (int r = 0; r < 8; ++r) p[r] = exp2f(z[r] - m_new);
+            for (int r = 0; r < 8; ++r) p[r] = exp2_hw(z[r] - m_new);
         }
         m_run = m_new;
+        const bool rescale = __ballot(move) != 0;
         float ps = 0.f;
 #pragma unroll
         for (int r = 0; r < 8; ++r) ps += p[r];
         l_run = l_run * factor + ps;
         // P^T as the B operand: k slots 8 g .. 8 g + 7 are the lane's 8 tokens, and the V^T
-        // operand reads the same tokens (4 g .. 4 g + 3 and 16 + 4 g .. + 3)
+        // operand holds the same tokens (4 g .. 4 g + 3 and 16 + 4 g .. + 3)
         const u32x4 pb = {bf16_pair(p[0], p[1]), bf16_pair(p[2], p[3]), bf16_pair(p[4], p[5]),
                           bf16_pair(p[6], p[7])};
+        if (__builtin_expect(rescale, 0)) {   // a wave-uniform branch, rarely taken after the first tiles
+#pragma unroll
+            for (int mt = 0; mt < kMt; ++mt)
+#pragma unroll
+                for (int r = 0; r < 4; ++r) acc_o[mt][r] *= factor;
+        }
 #pragma unroll
         for (int mt = 0; mt < kMt; ++mt) {
-            const uint16_t *vr = &sm.vt[256 * half + 16 * mt + l16][0];
-            const uint2 lo = *reinterpret_cast<const uint2 *>(vr + 4 * g);
-            const uint2 hi = *reinterpret_cast<const uint2 *>(vr + 16 + 4 * g);
+            const lds_char *vp = kb + pv_base[mt & 1] + 128 * (mt >> 1);
+            const uint2 lo = tr_read(vp);
+            const uint2 hi = tr_read(vp + kHalfTileBytes);
             const u32x4 va = {lo.x, lo.y, hi.x, hi.y};
-            f32x4 o = acc_o[mt];
-#pragma unroll
-            for (int r = 0; r < 4; ++r) o[r] *= factor;
-            acc_o[mt] = mfma16x16x32(va, pb, o);
+            acc_o[mt] = mfma16x16x32(va, pb, acc_o[mt]);
         }
-        // vt and k[buf] read by every wave, and (after each wave's wait) the next tile's loads
-        // have landed
-        asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
-        lds_barrier();
-        if (tile + 1 < ntile) transpose(buf ^ 1);
-        lds_barrier();
     }
 
     // the head's sum over its 4 lane groups
@@ -231,20 +297,20 @@ __global__ __launch_bounds__(kMlaThreads, 1) void sparse_mla_kernel(MlaArgs a) {
     const int head = 16 * hg + l16;
     if (a.nsplit == 1) {
         const float inv = l_tot > 0.f ? 1.f / l_tot : 0.f;
-        uint16_t *oh = a.o + (t * kMlaHeads + head) * (int64_t)kV + 256 * half;
+        uint16_t *oh = a.o + (t * kMlaHeads + head) * (int64_t)kV + 16 * half + 4 * g;
 #pragma unroll
         for (int mt = 0; mt < kMt; ++mt) {
             const f32x4 o = acc_o[mt];
             const uint2 v = {bf16_pair(o[0] * inv, o[1] * inv), bf16_pair(o[2] * inv, o[3] * inv)};
-            *reinterpret_cast<uint2 *>(oh + 16 * mt + 4 * g) = v;
+            *reinterpret_cast<uint2 *>(oh + 32 * mt) = v;
         }
         if (a.lse && g == 0 && half == 0)
             a.lse[t * kMlaHeads + head] = l_tot > 0.f ? (m_run + log2f(l_tot)) * 0.69314718055994531f : -INFINITY;
     } else {
         const int64_t ph = ((int64_t)split * a.T + t) * kMlaHeads + head;
-        float *oh = a.part_o + ph * kV + 256 * half;
+        float *oh = a.part_o + ph * kV + 16 * half + 4 * g;
 #pragma unroll
-        for (int mt = 0; mt < kMt; ++mt) *reinterpret_cast<f32x4 *>(oh + 16 * mt + 4 * g) = acc_o[mt];
+        for (int mt = 0; mt < kMt; ++mt) *reinterpret_cast<f32x4 *>(oh + 32 * mt) = acc_o[mt];
         if (g == 0 && half == 0) {
             a.part_ml[2 * ph] = m_run;
             a.part_ml[2 * ph + 1] = l_tot;
@@ -300,7 +366,7 @@ int mla_cus() {
 
 int sparse_mla_splits(int64_t T, int topk) {
     if (T <= 0 || topk <= 0) return 1;
-    const int64_t want = (2 * (int64_t)mla_cus() + T - 1) / T;           // about 2 workgroups per CU
+    const int64_t want = ((int64_t)mla_cus() + T - 1) / T;               // a workgroup per CU (LDS fits one)
     const int64_t most = ((int64_t)topk + 8 * kTile - 1) / (8 * kTile);   // at least 8 tiles a split
     const int64_t least = ((int64_t)topk + kMaxSel - 1) / kMaxSel;         // at most kMaxSel a split
     int64_t n = want < most ? want : most;
