@@ -40,6 +40,7 @@ PEAK_BF16_TFLOPS = 2516.6     # MI355X dense bf16 MFMA (published)
 TRAFFIC_SCORE_T65536 = {"source_sha256_prefix": "497fca71c49eba94", "bytes": 10869075527}
 PEAK_HBM_GBPS = 8000.0        # MI355X HBM3E (published)
 H, D, QLAT, HIDDEN = 32, 128, 1536, 7168
+MLA_HEADS, MLA_KV, MLA_V = 96, 576, 512          # the sparse MLA consumer (gated-MLA row)
 PROJ_FLOP_PER_TOKEN = 2 * (QLAT * 4096 + HIDDEN * D + HIDDEN * H)   # 14,876,672
 SCORE_FLOP_PER_PAIR = 2 * H * D                                     # 8,192
 
@@ -59,6 +60,7 @@ def parse():
     p.add_argument("--no-cpu-baseline", action="store_true")
     p.add_argument("--decode-batch", type=int, default=64)
     p.add_argument("--no-chunk", action="store_true")
+    p.add_argument("--no-mla", action="store_true")
     p.add_argument("--chunk", type=int, default=4096)
     p.add_argument("--window", type=int, default=1048576)
     p.add_argument("--calibrate-copy", action="store_true",
@@ -236,10 +238,57 @@ def bench_decode(dsa, args):
     log(f"decode: B={B} sum L={sumL}: project {proj_ms:.3f} ms, decode {dec_ms:.3f} ms "
         f"({gbps:.0f} GB/s); one step issued from Python, host-bound: {host_ms:.3f} ms")
     log(f"decode fp8: quantise new keys {q8_ms:.3f} ms, decode {dec8_ms:.3f} ms ({gbps8:.0f} GB/s)")
-    return dict(batch=B, sum_keys=sumL, project_ms=proj_ms, decode_ms=dec_ms, host_step_ms=host_ms,
+    mla = None if args.no_mla else bench_mla(dsa, args, idx, start_d, sumL, n)
+    return dict(mla=mla, batch=B, sum_keys=sumL, project_ms=proj_ms, decode_ms=dec_ms, host_step_ms=host_ms,
                 fp8=dict(quantize_ms=q8_ms, decode_ms=dec8_ms, bytes=dec8_bytes, GBps=gbps8),
                 decode_bytes=dec_bytes, decode_GBps=gbps, decode_hbm_frac=gbps / PEAK_HBM_GBPS,
                 step_GBps=(dec_bytes + proj_bytes) / ((dec_ms + proj_ms) * 1e-3) / 1e9)
+
+
+def bench_mla(dsa, args, idx, start_d, sum_keys, n):
+    """The consumer step of the decode: each sequence's new query attends, with all 96 heads,
+    to the latent-cache rows its indexer selection names (idx relative to the sequence start)."""
+    import torch
+    B, topk = idx.shape
+    g = torch.Generator(device="cuda")
+    g.manual_seed(3)
+    t0 = time.time()
+    # latent cache rows laid out like the key cache (one row per cached token), and absorbed
+    # queries; seeded, generated on the device (about 6 GB)
+    latent = torch.randn((sum_keys, MLA_KV), generator=g, device="cuda", dtype=torch.float32
+                         ).to(torch.bfloat16) if sum_keys * MLA_KV < (1 << 31) else None
+    if latent is None:
+        latent = torch.empty((sum_keys, MLA_KV), dtype=torch.bfloat16, device="cuda")
+        for r0 in range(0, sum_keys, 1 << 20):
+            r1 = min(sum_keys, r0 + (1 << 20))
+            latent[r0:r1] = torch.randn((r1 - r0, MLA_KV), generator=g, device="cuda").to(torch.bfloat16)
+    qm = (torch.randn((B, MLA_HEADS, MLA_KV), generator=g, device="cuda") * 0.5).to(torch.bfloat16)
+    torch.cuda.synchronize()
+    log(f"mla: latent cache of {sum_keys} rows generated in {time.time() - t0:.1f}s")
+    o = torch.empty((B, MLA_HEADS, MLA_V), dtype=torch.bfloat16, device="cuda")
+    lse = torch.empty((B, MLA_HEADS), dtype=torch.float32, device="cuda")
+    ws = torch.empty(max(dsa.workspace_size(dsa.OP_SPARSE_MLA, B, 0, 0, topk), 1), dtype=torch.uint8,
+                     device="cuda")
+    stream = torch.cuda.current_stream()
+    for _ in range(max(args.warmup, 1)):
+        dsa.sparse_mla(qm, latent, idx, row0=start_d, ws=ws, out=(o, lse))
+    torch.cuda.synchronize()
+    evs = [torch.cuda.Event(enable_timing=True) for _ in range(n + 1)]
+    torch.cuda._sleep(100_000_000)   # as for the decode: the calls queue up ahead of the GPU
+    evs[0].record(stream)
+    for i in range(n):
+        dsa.sparse_mla(qm, latent, idx, row0=start_d, ws=ws, out=(o, lse))
+        evs[i + 1].record(stream)
+    torch.cuda.synchronize()
+    ms = float(np.mean([evs[i].elapsed_time(evs[i + 1]) for i in range(n)]))
+    # algorithmic bytes: each selected latent row once, the queries, indices, outputs and lse
+    nbytes = B * topk * MLA_KV * 2 + B * MLA_HEADS * MLA_KV * 2 + B * topk * 4 + B * MLA_HEADS * (MLA_V * 2 + 4)
+    flop = B * MLA_HEADS * topk * (MLA_KV + MLA_V) * 2
+    gbps = nbytes / (ms * 1e-3) / 1e9
+    log(f"mla: B={B} top-{topk}: {ms * 1e3:.1f} us per call, {gbps:.0f} GB/s, "
+        f"{flop / (ms * 1e-3) / 1e12:.1f} TFLOP/s")
+    del latent, ws
+    return dict(ms=ms, bytes=nbytes, flop=flop, GBps=gbps)
 
 
 def bench_chunk(dsa, args):
@@ -371,7 +420,14 @@ def main():
                           "quantize_new_keys_ms": round(dec["fp8"]["quantize_ms"], 4),
                           "GBps": round(dec["fp8"]["GBps"], 1),
                           "hbm_frac": round(dec["fp8"]["GBps"] / PEAK_HBM_GBPS, 4),
-                          "algorithmic_bytes": dec["fp8"]["bytes"]}},
+                          "algorithmic_bytes": dec["fp8"]["bytes"]},
+            "sparse_mla": None if dec["mla"] is None else {
+                "workload": f"the decode's consumer: {dec['batch']} queries x {MLA_HEADS} heads over "
+                            f"the {args.topk} latent-cache rows (576 values) each selection names",
+                "us": round(dec["mla"]["ms"] * 1e3, 2), "GBps": round(dec["mla"]["GBps"], 1),
+                "bound": "hbm", "hbm_frac": round(dec["mla"]["GBps"] / PEAK_HBM_GBPS, 4),
+                "tflops": round(dec["mla"]["flop"] / (dec["mla"]["ms"] * 1e-3) / 1e12, 2),
+                "algorithmic_bytes": dec["mla"]["bytes"]}},
         "chunked_prefill": None if chk is None else {
             "workload": f"last {chk['C']} queries of a {chk['prefix'] + chk['C']}-token window "
                         f"against the whole prefix, top-{args.topk}: scores + select",
