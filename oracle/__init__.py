@@ -13,6 +13,8 @@ archdiff.com compare pages on Kimi K3.1 Pro (component tables):
   * QK-norm row: the LayerNorm is on the indexer key;
   * RoPE row ("Kimi K3.1 Pro vs Gemma 4 31B" page): no rotary step in the indexer;
   * long-context row (same page): the whole prefix is scored.
+The DeepSeek-V3.2-shaped indexer (64 heads, rotary step on 64 of the 128 dims) and the sparse
+MLA over the selected tokens are at the end of this module.
 """
 import ctypes
 import os
@@ -297,3 +299,56 @@ def sparse_mla(q, kv, idx, row0=None, scale=1.0 / np.sqrt(192.0)):
     lse = np.empty((T, Hh), np.float64)
     lib().oracle_sparse_mla(_p(q), _p(kv), _p(idx), _p(r0), T, Hh, K, float(scale), _p(o), _p(lse))
     return o, lse
+
+
+# ---------------------------------------------------------------- DeepSeek-V3.2-shaped indexer
+# The sparse-attention row of the "Qwen3.5-397B-A17B vs Kimi K3.1 Pro" page gives DeepSeek-
+# V3.2's indexer 64 heads, and the RoPE row of the "Kimi K3.1 Pro vs Gemma 4 31B" page says
+# it rotates 64 of its 128 dims.  Read here as the K3.1 indexer above with those two changes:
+# q = c_q W_q (1,536 -> 8,192 = 64 heads x 128), k = LayerNorm(x W_k) (7,168 -> 128),
+# w = x W_w (7,168 -> 64), I = sum over the 64 heads; the rotary step turns dims (2i, 2i+1),
+# i < 32, of every query head and of the key by the angle pos * theta^(-2i/64) (theta = 10^4),
+# on the stored bf16 projections, and its result is rounded to bf16 again.  Dims 64..127 are
+# not rotated.
+V32_H, V32_QOUT, V32_ROT, V32_THETA = 64, 8192, 64, 10000.0
+
+
+def rope_angles(pos, rot=V32_ROT, theta=V32_THETA):
+    """Angles [len(pos), rot/2] in fp64: position times theta^(-2i/rot)."""
+    i = np.arange(rot // 2, dtype=np.float64)
+    return np.asarray(pos, dtype=np.float64)[:, None] * theta ** (-2.0 * i / rot)[None, :]
+
+
+def rope_f64(v, pos, rot=V32_ROT, theta=V32_THETA):
+    """The rotary step on v [T, ..., 128] (fp64 values) at positions pos [T]: returns fp64.
+
+    Pair i of a vector, (v[2i], v[2i+1]), becomes (v[2i] c - v[2i+1] s, v[2i] s + v[2i+1] c)
+    with c, s the cosine and sine of its angle; the dims past `rot` are copied."""
+    v = np.asarray(v, dtype=np.float64)
+    a = rope_angles(pos, rot, theta)
+    shape = (v.shape[0],) + (1,) * (v.ndim - 2) + (rot // 2,)
+    c, s = np.cos(a).reshape(shape), np.sin(a).reshape(shape)
+    out = v.copy()
+    x, y = v[..., 0:rot:2], v[..., 1:rot:2]
+    out[..., 0:rot:2] = x * c - y * s
+    out[..., 1:rot:2] = x * s + y * c
+    return out
+
+
+def project_v32(x, c_q, Wt, pos0=0, theta=V32_THETA, want=("q", "k", "w")):
+    """q [T,64,128], k [T,128], w [T,64] (bf16 patterns) of the DeepSeek-V3.2-shaped indexer
+    for tokens at positions pos0 .. pos0 + T - 1: the projections rounded to bf16, then the
+    rotary step on q and k, rounded to bf16 again."""
+    T = (x if x is not None else c_q).shape[0]
+    pos = pos0 + np.arange(T, dtype=np.int64)
+    q = k = w = None
+    if "q" in want:
+        qb = f64_to_bf16(linear_f64(c_q, Wt["W_q"])).reshape(T, V32_H, D)
+        q = f64_to_bf16(rope_f64(bf16_to_f64(qb), pos, theta=theta))
+    if "k" in want:
+        lin = linear_f64(x, Wt["W_k"])
+        kb = f64_to_bf16(layernorm_f64(lin, Wt["gamma"], Wt["beta"], Wt["eps"]))
+        k = f64_to_bf16(rope_f64(bf16_to_f64(kb), pos, theta=theta))
+    if "w" in want:
+        w = f64_to_bf16(linear_f64(x, Wt["W_w"]))
+    return q, k, w

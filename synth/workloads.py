@@ -41,6 +41,20 @@ def layer_weights(layer=0, seed=0):
                 eps=LN_EPS)
 
 
+def layer_weights_v32(layer=0, seed=0):
+    """One DeepSeek-V3.2-shaped indexer layer (64 heads): W_q [1536, 8192] ~N(0,1/1536), W_k
+    [7168, 128] and W_w [7168, 64] ~N(0,1/7168), gamma and beta as above.  Drawn from the
+    streams of `layer_weights` at layer index 4096 + layer, so the two shapes never share
+    values."""
+    lv = 4096 + layer
+    return dict(W_q=normal_bf16((QLAT, 2 * QOUT), 0.0, 1.0 / QLAT, WQ, lv, seed),
+                W_k=normal_bf16((HIDDEN, D), 0.0, 1.0 / HIDDEN, WK, lv, seed),
+                W_w=normal_bf16((HIDDEN, 2 * H), 0.0, 1.0 / HIDDEN, WW, lv, seed),
+                gamma=normal_bf16((D,), 1.0, 0.02, GAMMA, lv, seed),
+                beta=normal_bf16((D,), 0.0, 0.02, BETA, lv, seed),
+                eps=LN_EPS)
+
+
 def layer_activations(T, seed=0, layer=0):
     """Hidden state x [T,7168] and query latent c_q [T,1536], both ~N(0,1)."""
     return dict(x=normal_bf16((T, HIDDEN), 0.0, 1.0, X, layer, seed),
