@@ -76,6 +76,8 @@ extern "C" {
 #define DSA_IDX_OP_DECODE_FP8 4
 #define DSA_IDX_OP_PREFILL_CHUNK 5
 #define DSA_IDX_OP_SPARSE_MLA 6
+#define DSA_IDX_OP_V32_PROJECT 7
+#define DSA_IDX_OP_V32_SCORE_TOPK 8
 
 typedef uint16_t dsa_idx_bf16;
 
@@ -243,6 +245,37 @@ int dsa_idx_decode_fp8(const dsa_idx_bf16 *q, const dsa_idx_bf16 *w, const uint8
 int dsa_idx_sparse_mla(const dsa_idx_bf16 *q, const dsa_idx_bf16 *kv, const int32_t *idx,
                        const int64_t *row0, int64_t T, int topk, float scale, dsa_idx_bf16 *o,
                        float *lse, void *ws, size_t ws_bytes, void *stream);
+
+/* ---------------------------------------------------------------- 64-head indexer
+ * The DeepSeek-V3.2-shaped indexer: 64 heads ("Qwen3.5-397B-A17B vs Kimi K3.1 Pro" page,
+ * sparse-attention row) with a rotary step on 64 of the 128 dims (RoPE row of the "Kimi K3.1
+ * Pro vs Gemma 4 31B" page), otherwise the indexer above: q from the 1,536-dim query latent
+ * (1,536 -> 8,192 = 64 heads x 128), one LayerNorm key from the hidden state, head weights
+ * 7,168 -> 64, I = sum over the 64 heads of w_h ReLU(q_h . k), top-k per query.
+ * The rotary step (this library's reading): dims (2i, 2i+1), i < 32, of every query head and
+ * of the key turn by the angle pos * rope_theta^(-2i/64), on the projections as rounded to
+ * bf16, and the result is rounded to bf16 (nearest even) again; dims 64..127 do not turn. */
+#define DSA_IDX_V32_HEADS 64
+#define DSA_IDX_V32_QOUT 8192
+
+/* Projections and rotary step of T tokens at positions pos0 .. pos0 + T - 1.
+ *   wt: W_q [1536][8192], W_k [7168][128], W_w [7168][64] (row-major), LayerNorm gamma,
+ *       beta [128], ln_eps > 0; x [T][ldx], c_q [T][ldc] as for dsa_idx_project;
+ *   pos0 >= 0, rope_theta > 0 (10000 in the oracle's reading);
+ *   q [T][64][128], k [T][128], w [T][64] bf16 out (16-byte aligned).
+ * Needs dsa_idx_workspace_size(DSA_IDX_OP_V32_PROJECT, T, ...) bytes of workspace. */
+int dsa_idx_v32_project(const dsa_idx_weights *wt, const dsa_idx_bf16 *x, int64_t ldx,
+                        const dsa_idx_bf16 *c_q, int64_t ldc, int64_t T, int64_t pos0, float rope_theta,
+                        dsa_idx_bf16 *q, dsa_idx_bf16 *k, dsa_idx_bf16 *w, void *ws, size_t ws_bytes,
+                        void *stream);
+
+/* Causal scores and top-k of one sequence for the 64-head indexer: as dsa_idx_score_topk,
+ * with q [T][64][128] and w [T][64] (the keys [T][128] as before).  The 64-head score is
+ * computed as the sum of its two 32-head halves (fp32).
+ * Needs dsa_idx_workspace_size(DSA_IDX_OP_V32_SCORE_TOPK, T, 0, 0, topk) bytes. */
+int dsa_idx_v32_score_topk(const dsa_idx_bf16 *q, const dsa_idx_bf16 *k, const dsa_idx_bf16 *w,
+                           int64_t T, int topk, int32_t *idx, float *scores, void *ws,
+                           size_t ws_bytes, void *stream);
 
 #ifdef __cplusplus
 }

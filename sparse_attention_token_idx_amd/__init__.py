@@ -23,7 +23,9 @@ HEADS, DIM, QLAT, QOUT, HIDDEN, MAX_TOPK = 32, 128, 1536, 4096, 7168, 2048
 OP_PROJECT, OP_SCORE_TOPK, OP_SCORE_TOPK_VARLEN, OP_DECODE, OP_DECODE_FP8 = 0, 1, 2, 3, 4
 OP_PREFILL_CHUNK = 5
 OP_SPARSE_MLA = 6
+OP_V32_PROJECT, OP_V32_SCORE_TOPK = 7, 8
 MLA_HEADS, MLA_KV, MLA_V = 96, 576, 512
+V32_HEADS, V32_QOUT, V32_THETA = 64, 8192, 10000.0   # the 64-head (DeepSeek-V3.2-shaped) indexer
 
 _HERE = os.path.dirname(os.path.abspath(__file__))
 LIB_PATH = os.path.join(_HERE, "libdsaidx.so")
@@ -73,6 +75,11 @@ def lib():
         L.dsa_idx_prefill_select.argtypes = [vp, i32, i32, i64, i32, vp, vp, vp, sz, vp]
         L.dsa_idx_prefill_chunk.restype = i32
         L.dsa_idx_prefill_chunk.argtypes = [vp, vp, vp, i64, i64, i32, vp, vp, vp, sz, vp]
+        L.dsa_idx_v32_project.restype = i32
+        L.dsa_idx_v32_project.argtypes = [ctypes.POINTER(_Weights), vp, i64, vp, i64, i64, i64,
+                                          ctypes.c_float, vp, vp, vp, vp, sz, vp]
+        L.dsa_idx_v32_score_topk.restype = i32
+        L.dsa_idx_v32_score_topk.argtypes = [vp, vp, vp, i64, i32, vp, vp, vp, sz, vp]
         L.dsa_idx_sparse_mla.restype = i32
         L.dsa_idx_sparse_mla.argtypes = [vp, vp, vp, vp, i64, i32, ctypes.c_float, vp, vp, vp, sz, vp]
         L.dsa_idx_decode.restype = i32
@@ -191,6 +198,59 @@ def score_topk(q, k, w, topk=MAX_TOPK, with_scores=True, ws=None, out=None, stre
     _check("dsa_idx_score_topk",
            lib().dsa_idx_score_topk(_ptr(q), _ptr(k), _ptr(w), T, topk, _ptr(idx), _ptr(sc),
                                     _ptr(ws), nbytes, _stream(stream)))
+    return idx, sc
+
+
+def v32_project(x, c_q, weights, pos0=0, theta=V32_THETA, q=None, k=None, w=None, stream=None):
+    """The 64-head indexer's projections with the rotary step, tokens at positions pos0 ..:
+    q [T,64,128], k [T,128], w [T,64]; weights = dict(W_q [1536,8192], W_k [7168,128],
+    W_w [7168,64], gamma, beta, eps)."""
+    T = x.shape[0]
+    dev = x.device
+    _need(x, "x", torch.bfloat16, contiguous=False)
+    _need(c_q, "c_q", torch.bfloat16, contiguous=False)
+    if x.stride(1) != 1 or c_q.stride(1) != 1 or c_q.shape[0] != T:
+        raise ValueError("x and c_q need unit column stride and equal row counts")
+    W = weights
+    _need(W["W_q"], "W_q", torch.bfloat16, (QLAT, V32_QOUT))
+    _need(W["W_k"], "W_k", torch.bfloat16, (HIDDEN, DIM))
+    _need(W["W_w"], "W_w", torch.bfloat16, (HIDDEN, V32_HEADS))
+    _need(W["gamma"], "gamma", torch.bfloat16, (DIM,))
+    _need(W["beta"], "beta", torch.bfloat16, (DIM,))
+    q = torch.empty((T, V32_HEADS, DIM), dtype=torch.bfloat16, device=dev) if q is None else q
+    k = torch.empty((T, DIM), dtype=torch.bfloat16, device=dev) if k is None else k
+    w = torch.empty((T, V32_HEADS), dtype=torch.bfloat16, device=dev) if w is None else w
+    _need(q, "q", torch.bfloat16, (T, V32_HEADS, DIM))
+    _need(k, "k", torch.bfloat16, (T, DIM))
+    _need(w, "w", torch.bfloat16, (T, V32_HEADS))
+    wt = _Weights(_ptr(W["W_q"]), _ptr(W["W_k"]), _ptr(W["W_w"]), _ptr(W["gamma"]),
+                  _ptr(W["beta"]), float(W["eps"]))
+    nbytes = workspace_size(OP_V32_PROJECT, T)
+    ws = _workspace(nbytes, dev, None)
+    _check("dsa_idx_v32_project",
+           lib().dsa_idx_v32_project(ctypes.byref(wt), _ptr(x), x.stride(0), _ptr(c_q), c_q.stride(0),
+                                     T, int(pos0), float(theta), _ptr(q), _ptr(k), _ptr(w), _ptr(ws),
+                                     nbytes, _stream(stream)))
+    return q, k, w
+
+
+def v32_score_topk(q, k, w, topk=MAX_TOPK, with_scores=True, ws=None, out=None, stream=None):
+    """Causal top-k of one sequence for the 64-head indexer: q [T,64,128], k [T,128],
+    w [T,64] -> idx [T,topk] int32, scores [T,topk] float32 (or None)."""
+    T = q.shape[0]
+    _need(q, "q", torch.bfloat16, (T, V32_HEADS, DIM))
+    _need(k, "k", torch.bfloat16, (T, DIM))
+    _need(w, "w", torch.bfloat16, (T, V32_HEADS))
+    if out is None:
+        idx = torch.empty((T, topk), dtype=torch.int32, device=q.device)
+        sc = torch.empty((T, topk), dtype=torch.float32, device=q.device) if with_scores else None
+    else:
+        idx, sc = out
+    nbytes = workspace_size(OP_V32_SCORE_TOPK, T, topk=topk)
+    ws = _workspace(nbytes, q.device, ws)
+    _check("dsa_idx_v32_score_topk",
+           lib().dsa_idx_v32_score_topk(_ptr(q), _ptr(k), _ptr(w), T, topk, _ptr(idx), _ptr(sc),
+                                        _ptr(ws), nbytes, _stream(stream)))
     return idx, sc
 
 

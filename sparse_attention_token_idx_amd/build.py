@@ -6,7 +6,7 @@ import sys
 HERE = os.path.dirname(os.path.abspath(__file__))
 CSRC = os.path.join(HERE, "csrc")
 SO = os.path.join(HERE, "libdsaidx.so")
-SOURCES = ["api.cpp", "project.hip", "scores.hip", "topk.hip", "decode.hip", "fp8.hip", "mla.hip"]
+SOURCES = ["api.cpp", "project.hip", "scores.hip", "topk.hip", "decode.hip", "fp8.hip", "mla.hip", "rope.hip"]
 
 # Packed fp32 arithmetic is switched off for the device code (see the design notes); the
 # host pass only warns that it does not know the feature.

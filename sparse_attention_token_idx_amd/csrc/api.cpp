@@ -146,6 +146,17 @@ int dsa_idx_workspace_size(int op, int64_t total_tokens, int B, int max_seqlen, 
             *bytes = total_tokens == 0 ? 0 : ws_prefill_chunk(total_tokens, max_seqlen);
             return ok();
         }
+        case DSA_IDX_OP_V32_PROJECT:
+            if (total_tokens < 0) return fail(DSA_IDX_EINVAL, "T=%lld < 0", (long long)total_tokens);
+            *bytes = dsaidx::project_workspace(total_tokens);   // the halves reuse it in turn
+            return ok();
+        case DSA_IDX_OP_V32_SCORE_TOPK: {
+            if (total_tokens < 0) return fail(DSA_IDX_EINVAL, "T=%lld < 0", (long long)total_tokens);
+            int r = check_topk(topk);
+            if (r) return r;
+            *bytes = ws_score_topk(total_tokens);
+            return ok();
+        }
         case DSA_IDX_OP_SPARSE_MLA: {
             if (total_tokens < 0) return fail(DSA_IDX_EINVAL, "T=%lld < 0", (long long)total_tokens);
             int r = check_topk(topk);
@@ -296,6 +307,74 @@ int dsa_idx_score_topk(const dsa_idx_bf16 *q, const dsa_idx_bf16 *k, const dsa_i
     if (r || T == 0) return r;
     r = dsa_idx_prefill_scores(q, k, w, nullptr, 1, 0, T, ws, ws_bytes, stream);
     if (r) return r;
+    return dsa_idx_prefill_select(nullptr, 1, 0, T, topk, idx, scores, ws, ws_bytes, stream);
+}
+
+int dsa_idx_v32_project(const dsa_idx_weights *wt, const dsa_idx_bf16 *x, int64_t ldx,
+                        const dsa_idx_bf16 *c_q, int64_t ldc, int64_t T, int64_t pos0, float rope_theta,
+                        dsa_idx_bf16 *q, dsa_idx_bf16 *k, dsa_idx_bf16 *w, void *ws, size_t ws_bytes,
+                        void *stream) {
+    if (!wt) return fail(DSA_IDX_EINVAL, "weights is NULL");
+    if (T < 0 || pos0 < 0) return fail(DSA_IDX_EINVAL, "T=%lld pos0=%lld must be >= 0", (long long)T, (long long)pos0);
+    if (!(rope_theta > 0.f)) return fail(DSA_IDX_EINVAL, "rope_theta must be > 0");
+    if (T == 0) return ok();
+    if (!wt->W_q || !wt->W_k || !wt->W_w || !wt->ln_gamma || !wt->ln_beta)
+        return fail(DSA_IDX_EINVAL, "a weight pointer is NULL");
+    if (!x || !c_q || !q || !k || !w) return fail(DSA_IDX_EINVAL, "a tensor pointer is NULL");
+    if (ldx < DSA_IDX_HIDDEN || ldx % 8) return fail(DSA_IDX_EINVAL, "ldx=%lld must be >= 7168 and a multiple of 8", (long long)ldx);
+    if (ldc < DSA_IDX_QLAT || ldc % 8) return fail(DSA_IDX_EINVAL, "ldc=%lld must be >= 1536 and a multiple of 8", (long long)ldc);
+    if (!(wt->ln_eps > 0.f)) return fail(DSA_IDX_EINVAL, "ln_eps must be > 0");
+    const void *ptrs[] = {x, c_q, q, k, w, wt->W_q, wt->W_k, wt->W_w};
+    for (const void *p : ptrs)
+        if (!aligned16(p)) return fail(DSA_IDX_EINVAL, "tensor pointer %p is not 16-byte aligned", p);
+    if (T > (int64_t)INT32_MAX * 128) return fail(DSA_IDX_EUNSUPPORTED, "T=%lld too large", (long long)T);
+    const size_t need = dsaidx::project_workspace(T);
+    if (need && (!ws || ws_bytes < need))
+        return fail(DSA_IDX_EWORKSPACE, "workspace %zu bytes < %zu needed", ws ? ws_bytes : (size_t)0, need);
+    if (need && !aligned16(ws)) return fail(DSA_IDX_EINVAL, "workspace must be 16-byte aligned");
+    int r = check_device();
+    if (r) return r;
+    const hipStream_t st = reinterpret_cast<hipStream_t>(stream);
+    constexpr int64_t kHalf = DSA_IDX_QOUT;   // q columns and w columns of one half: 4,096 and 32
+    // first half: q columns 0..4,095, the key, w columns 0..31; second: the rest, no key
+    hipError_t e = dsaidx::launch_project_ex(x, ldx, c_q, ldc, T, wt->W_q, DSA_IDX_V32_QOUT, wt->W_k, wt->W_w,
+                                             DSA_IDX_V32_HEADS, wt->ln_gamma, wt->ln_beta, wt->ln_eps, q,
+                                             DSA_IDX_V32_QOUT, k, nullptr, w, DSA_IDX_V32_HEADS,
+                                             static_cast<float *>(ws), st);
+    if (e != hipSuccess) return hip_fail("project launch", e);
+    e = dsaidx::launch_project_ex(x, ldx, c_q, ldc, T, wt->W_q + kHalf, DSA_IDX_V32_QOUT, wt->W_k,
+                                  wt->W_w + DSA_IDX_HEADS, DSA_IDX_V32_HEADS, wt->ln_gamma, wt->ln_beta, wt->ln_eps,
+                                  q + kHalf, DSA_IDX_V32_QOUT, nullptr, nullptr, w + DSA_IDX_HEADS,
+                                  DSA_IDX_V32_HEADS, static_cast<float *>(ws), st);
+    if (e != hipSuccess) return hip_fail("project launch", e);
+    e = dsaidx::launch_rope(q, DSA_IDX_V32_QOUT, DSA_IDX_V32_HEADS, k, DSA_IDX_DIM, T, pos0, (double)rope_theta, st);
+    if (e != hipSuccess) return hip_fail("rotary launch", e);
+    return ok();
+}
+
+int dsa_idx_v32_score_topk(const dsa_idx_bf16 *q, const dsa_idx_bf16 *k, const dsa_idx_bf16 *w,
+                           int64_t T, int topk, int32_t *idx, float *scores, void *ws,
+                           size_t ws_bytes, void *stream) {
+    if (T < 0) return fail(DSA_IDX_EINVAL, "T=%lld < 0", (long long)T);
+    int r = check_topk(topk);
+    if (r) return r;
+    if (T > 0 && (!q || !k || !w || !idx)) return fail(DSA_IDX_EINVAL, "a tensor pointer is NULL");
+    size_t need = 0;
+    r = prefill_check(nullptr, 1, 0, T, ws, ws_bytes, need);
+    if (r || T == 0) return r;
+    if (!aligned16(q) || !aligned16(k) || !aligned16(w))
+        return fail(DSA_IDX_EINVAL, "q, k and w must be 16-byte aligned");
+    r = check_device();
+    if (r) return r;
+    const PrefillWs p = prefill_ws(nullptr, 1, 0, T, ws);
+    const hipStream_t st = reinterpret_cast<hipStream_t>(stream);
+    // heads 0..31 write the score rows, heads 32..63 add to them
+    for (int half = 0; half < 2; ++half) {
+        hipError_t e = dsaidx::launch_scores_ex(q + half * DSA_IDX_QOUT, DSA_IDX_V32_QOUT, k, w + half * DSA_IDX_HEADS,
+                                                DSA_IDX_V32_HEADS, half == 1, nullptr, 1, T, T, 0, p.base, p.rows,
+                                                p.dummy, st);
+        if (e != hipSuccess) return hip_fail("scores launch", e);
+    }
     return dsa_idx_prefill_select(nullptr, 1, 0, T, topk, idx, scores, ws, ws_bytes, stream);
 }
 

@@ -32,6 +32,24 @@ hipError_t launch_project(const uint16_t *x, int64_t ldx, const uint16_t *c_q, i
 // at tri_row_offset(t) - tri_row_offset(pos0)), dummy: a row of kRowQuant * ceil((pos0 +
 // max_len) / kRowQuant) floats that absorbs the stores of rows past a sequence end and past
 // a row's own last key tile.
+// launch_project with explicit row strides: of W_q (ldwq) and q (ldq) for the 4,096 q columns
+// it computes, of W_w (ldww) and w (ldwo) for the 32 w columns; k_base may be nullptr (no key).
+hipError_t launch_project_ex(const uint16_t *x, int64_t ldx, const uint16_t *c_q, int64_t ldc,
+                             int64_t T, const uint16_t *W_q, int64_t ldwq, const uint16_t *W_k,
+                             const uint16_t *W_w, int64_t ldww, const uint16_t *gamma,
+                             const uint16_t *beta, float eps, uint16_t *q, int64_t ldq,
+                             uint16_t *k_base, const int64_t *k_slot, uint16_t *w, int64_t ldwo,
+                             float *ws, hipStream_t stream);
+// The rotary step of the 64-head indexer, in place: dims (2i, 2i+1), i < 32, of every head of q
+// (heads x 128 per row, rows ldq apart) and of k (rows ldk apart; either may be nullptr), token
+// t at position pos0 + t.
+hipError_t launch_rope(uint16_t *q, int64_t ldq, int heads, uint16_t *k, int64_t ldk, int64_t T, int64_t pos0,
+                       double theta, hipStream_t stream);
+// launch_scores with explicit row strides of q (ldq) and w (ldw) for the 32 heads it scores;
+// accumulate: add to the score rows instead of writing them.
+hipError_t launch_scores_ex(const uint16_t *q, int64_t ldq, const uint16_t *k, const uint16_t *w, int64_t ldw,
+                            bool accumulate, const int32_t *cu_seqlens, int B, int64_t max_len, int64_t T,
+                            int64_t pos0, int64_t *seq_base, float *out, float *dummy, hipStream_t stream);
 hipError_t launch_scores(const uint16_t *q, const uint16_t *k, const uint16_t *w,
                          const int32_t *cu_seqlens, int B, int64_t max_len, int64_t T, int64_t pos0,
                          int64_t *seq_base, float *out, float *dummy, hipStream_t stream);

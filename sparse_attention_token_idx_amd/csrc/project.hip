@@ -146,12 +146,13 @@ constexpr int kQBM = 256, kQBN = 256, kQKB = 32, kQStages = 3;
 constexpr int kQStage = (kQBM + kQBN) * kQKB;   // bf16 per stage
 
 // W_qT[n][k] = W_q[k][n], 64 x 64 tiles through LDS.
-__global__ __launch_bounds__(256) void transpose_wq_kernel(const uint16_t *__restrict__ Wq, uint16_t *__restrict__ WqT) {
+__global__ __launch_bounds__(256) void transpose_wq_kernel(const uint16_t *__restrict__ Wq, int64_t ldw,
+                                                           uint16_t *__restrict__ WqT) {
     __shared__ uint16_t t[64][72];
     const int n0 = 64 * blockIdx.x, k0 = 64 * blockIdx.y;
     const int r = threadIdx.x >> 2, c = 16 * (threadIdx.x & 3);
-    const u32x4 v0 = *reinterpret_cast<const u32x4 *>(Wq + (int64_t)(k0 + r) * kQOut + n0 + c);
-    const u32x4 v1 = *reinterpret_cast<const u32x4 *>(Wq + (int64_t)(k0 + r) * kQOut + n0 + c + 8);
+    const u32x4 v0 = *reinterpret_cast<const u32x4 *>(Wq + (int64_t)(k0 + r) * ldw + n0 + c);
+    const u32x4 v1 = *reinterpret_cast<const u32x4 *>(Wq + (int64_t)(k0 + r) * ldw + n0 + c + 8);
 #pragma unroll
     for (int j = 0; j < 4; ++j) {
         t[r][c + 2 * j] = (uint16_t)(v0[j] & 0xFFFFu);
@@ -172,7 +173,7 @@ __global__ __launch_bounds__(256) void transpose_wq_kernel(const uint16_t *__res
 
 __global__ __launch_bounds__(256, 1) void proj_q_kernel(const uint16_t *__restrict__ cq, int64_t ldc,
                                                         int64_t T, const uint16_t *__restrict__ WqT,
-                                                        uint16_t *__restrict__ q) {
+                                                        uint16_t *__restrict__ q, int64_t ldq) {
     constexpr int SM = 8, SN = 8, S = kQStages, KB = kQKB;
     extern __shared__ __align__(16) uint16_t qsm[];
     const int ntn = kQOut / kQBN;
@@ -255,7 +256,7 @@ __global__ __launch_bounds__(256, 1) void proj_q_kernel(const uint16_t *__restri
             if (row >= T) continue;
 #pragma unroll
             for (int j = 0; j < SN; ++j)
-                q[row * kQOut + n0 + wn * 128 + 16 * j + l16] = (uint16_t)f32_to_bf16(acc[i][j][r]);
+                q[row * ldq + n0 + wn * 128 + 16 * j + l16] = (uint16_t)f32_to_bf16(acc[i][j][r]);
         }
 }
 
@@ -273,9 +274,11 @@ struct KWArgs {
     const uint16_t *gamma;
     const uint16_t *beta;
     float eps;
-    uint16_t *k_base;
+    uint16_t *k_base;           // nullptr: compute no key
     const int64_t *k_slot;
     uint16_t *w;
+    int64_t ldww;               // row stride of W_w (elements)
+    int64_t ldwo;               // row stride of w
 };
 
 __global__ __launch_bounds__(256) void proj_kw_kernel(KWArgs a) {
@@ -310,7 +313,7 @@ __global__ __launch_bounds__(256) void proj_kw_kernel(KWArgs a) {
         }
         if (b_thread) {
             const uint16_t *src = bnb < 16 ? a.Wk + 8 * bnb : a.Ww + 8 * (bnb - 16);
-            const int ld = bnb < 16 ? kDim : kHeads;
+            const int ld = bnb < 16 ? kDim : (int)a.ldww;
 #pragma unroll
             for (int i = 0; i < 8; ++i)
                 rb[i] = *reinterpret_cast<const u32x4 *>(src + (int64_t)(k0 + 8 * bkb + i) * ld);
@@ -392,14 +395,16 @@ __global__ __launch_bounds__(256) void proj_kw_kernel(KWArgs a) {
             for (int d = 1; d < 16; d <<= 1) v += __shfl_xor(v, d, 64);
             const float inv = 1.0f / sqrtf(v * (1.0f / kDim) + a.eps);
             if (row >= a.T) continue;
-            const int64_t slot = a.k_slot ? a.k_slot[row] : row;
-            uint16_t *kr = a.k_base + slot * kDim;
+            if (a.k_base) {
+                const int64_t slot = a.k_slot ? a.k_slot[row] : row;
+                uint16_t *kr = a.k_base + slot * kDim;
 #pragma unroll
-            for (int j = 0; j < 8; ++j)
-                kr[16 * j + l16] = (uint16_t)f32_to_bf16(fmaf((acc[i][j][r] - mu) * inv, g[j], b[j]));
+                for (int j = 0; j < 8; ++j)
+                    kr[16 * j + l16] = (uint16_t)f32_to_bf16(fmaf((acc[i][j][r] - mu) * inv, g[j], b[j]));
+            }
 #pragma unroll
             for (int j = 0; j < 2; ++j)
-                a.w[row * kHeads + 16 * j + l16] = (uint16_t)f32_to_bf16(acc[i][8 + j][r]);
+                a.w[row * a.ldwo + 16 * j + l16] = (uint16_t)f32_to_bf16(acc[i][8 + j][r]);
         }
 }
 
@@ -435,9 +440,10 @@ __global__ __launch_bounds__(256) void skinny_partial_kernel(const uint16_t *__r
         }
 }
 
-// q[t][n] = bf16(sum over the S slices of part[s][t][n]); thread: 4 consecutive n.
+// q[t][n] = bf16(sum over the S slices of part[s][t][n]), q rows ldq apart; thread: 4
+// consecutive n.
 __global__ __launch_bounds__(256) void skinny_reduce_q_kernel(const float *__restrict__ part, int S, int T,
-                                                              uint16_t *__restrict__ q) {
+                                                              uint16_t *__restrict__ q, int64_t ldq) {
     const int64_t e = 4 * ((int64_t)blockIdx.x * 256 + threadIdx.x);
     if (e >= (int64_t)T * kQOut) return;
     f32x4 v = *reinterpret_cast<const f32x4 *>(part + e);
@@ -445,7 +451,8 @@ __global__ __launch_bounds__(256) void skinny_reduce_q_kernel(const float *__res
         const f32x4 p = *reinterpret_cast<const f32x4 *>(part + (int64_t)s * T * kQOut + e);
         v = f32x4{v[0] + p[0], v[1] + p[1], v[2] + p[2], v[3] + p[3]};
     }
-    *reinterpret_cast<u32x2 *>(q + e) = u32x2{pack_bf16x2(v[0], v[1]), pack_bf16x2(v[2], v[3])};
+    const int64_t t = e / kQOut, n = e % kQOut;
+    *reinterpret_cast<u32x2 *>(q + t * ldq + n) = u32x2{pack_bf16x2(v[0], v[1]), pack_bf16x2(v[2], v[3])};
 }
 
 // One workgroup per token: wave j adds the slices s = j, j + 4, ... of the 160 columns of
@@ -483,11 +490,13 @@ __global__ __launch_bounds__(256) void skinny_reduce_kw_kernel(const float *__re
 #pragma unroll
     for (int d = 1; d < 64; d <<= 1) var += __shfl_xor(var, d, 64);
     const float inv = 1.0f / sqrtf(var * (1.0f / kDim) + a.eps);
-    const int64_t slot = a.k_slot ? a.k_slot[t] : t;
-    uint16_t *kr = a.k_base + slot * kDim;
-    kr[lane] = (uint16_t)f32_to_bf16(fmaf(c0 * inv, bf16_to_f32(a.gamma[lane]), bf16_to_f32(a.beta[lane])));
-    kr[64 + lane] = (uint16_t)f32_to_bf16(fmaf(c1 * inv, bf16_to_f32(a.gamma[64 + lane]), bf16_to_f32(a.beta[64 + lane])));
-    if (lane < kHeads) a.w[t * kHeads + lane] = (uint16_t)f32_to_bf16(vw);
+    if (a.k_base) {
+        const int64_t slot = a.k_slot ? a.k_slot[t] : t;
+        uint16_t *kr = a.k_base + slot * kDim;
+        kr[lane] = (uint16_t)f32_to_bf16(fmaf(c0 * inv, bf16_to_f32(a.gamma[lane]), bf16_to_f32(a.beta[lane])));
+        kr[64 + lane] = (uint16_t)f32_to_bf16(fmaf(c1 * inv, bf16_to_f32(a.gamma[64 + lane]), bf16_to_f32(a.beta[64 + lane])));
+    }
+    if (lane < kHeads) a.w[t * a.ldwo + lane] = (uint16_t)f32_to_bf16(vw);
 }
 
 constexpr int kSkQSlice = 256;    // q: K = 1,536 in 6 slices x 32 column tiles
@@ -506,6 +515,16 @@ hipError_t launch_project(const uint16_t *x, int64_t ldx, const uint16_t *c_q, i
                           const uint16_t *W_w, const uint16_t *gamma, const uint16_t *beta,
                           float eps, uint16_t *q, uint16_t *k_base, const int64_t *k_slot,
                           uint16_t *w, float *ws, hipStream_t stream) {
+    return launch_project_ex(x, ldx, c_q, ldc, T, W_q, kQOut, W_k, W_w, kHeads, gamma, beta, eps, q, kQOut,
+                             k_base, k_slot, w, kHeads, ws, stream);
+}
+
+hipError_t launch_project_ex(const uint16_t *x, int64_t ldx, const uint16_t *c_q, int64_t ldc,
+                             int64_t T, const uint16_t *W_q, int64_t ldwq, const uint16_t *W_k,
+                             const uint16_t *W_w, int64_t ldww, const uint16_t *gamma,
+                             const uint16_t *beta, float eps, uint16_t *q, int64_t ldq,
+                             uint16_t *k_base, const int64_t *k_slot, uint16_t *w, int64_t ldwo,
+                             float *ws, hipStream_t stream) {
     if (T == 0) return hipSuccess;
     if (T <= kSkinnyT) {
         const int t = (int)T;
@@ -524,15 +543,15 @@ hipError_t launch_project(const uint16_t *x, int64_t ldx, const uint16_t *c_q, i
         }
         if (q) {
             hipLaunchKernelGGL((skinny_partial_kernel<128, 1, 4, kSkQSlice>), dim3(kQOut / 128, kQLat / kSkQSlice),
-                               dim3(256), sizeof(GemmSmem<64, 128>), stream, c_q, ldc, t, W_q, kQOut, W_q, kQOut,
-                               kQOut, kQOut, part_q);
+                               dim3(256), sizeof(GemmSmem<64, 128>), stream, c_q, ldc, t, W_q, (int)ldwq, W_q,
+                               (int)ldwq, kQOut, kQOut, part_q);
             hipLaunchKernelGGL(skinny_reduce_q_kernel, dim3((unsigned)((T * kQOut / 4 + 255) / 256)), dim3(256),
-                               0, stream, part_q, kQLat / kSkQSlice, t, q);
+                               0, stream, part_q, kQLat / kSkQSlice, t, q, ldq);
         }
         hipLaunchKernelGGL((skinny_partial_kernel<160, 2, 2, kSkKWSlice>), dim3(1, kHidden / kSkKWSlice), dim3(256),
-                           sizeof(GemmSmem<64, 160>), stream, x, ldx, t, W_k, kDim, W_w, kHeads, kDim, kDim + kHeads,
-                           part_kw);
-        KWArgs a{x, ldx, T, W_k, W_w, gamma, beta, eps, k_base, k_slot, w};
+                           sizeof(GemmSmem<64, 160>), stream, x, ldx, t, W_k, kDim, W_w, (int)ldww, kDim,
+                           kDim + kHeads, part_kw);
+        KWArgs a{x, ldx, T, W_k, W_w, gamma, beta, eps, k_base, k_slot, w, ldww, ldwo};
         hipLaunchKernelGGL(skinny_reduce_kw_kernel, dim3((unsigned)T), dim3(256), 0, stream, part_kw,
                            kHidden / kSkKWSlice, a);
         return hipGetLastError();
@@ -552,14 +571,15 @@ hipError_t launch_project(const uint16_t *x, int64_t ldx, const uint16_t *c_q, i
     const int64_t mt = (T + 127) / 128;
     if (q) {
         uint16_t *WqT = reinterpret_cast<uint16_t *>(ws);
-        hipLaunchKernelGGL(transpose_wq_kernel, dim3(kQOut / 64, kQLat / 64), dim3(256), 0, stream, W_q, WqT);
+        hipLaunchKernelGGL(transpose_wq_kernel, dim3(kQOut / 64, kQLat / 64), dim3(256), 0, stream, W_q, ldwq,
+                           WqT);
         const int64_t qt = (T + kQBM - 1) / kQBM;
         hipLaunchKernelGGL(proj_q_kernel, dim3((unsigned)(qt * (kQOut / kQBN))), dim3(256), smem_q, stream,
-                           c_q, ldc, T, WqT, q);
+                           c_q, ldc, T, WqT, q, ldq);
         hipError_t e = hipGetLastError();
         if (e != hipSuccess) return e;
     }
-    KWArgs a{x, ldx, T, W_k, W_w, gamma, beta, eps, k_base, k_slot, w};
+    KWArgs a{x, ldx, T, W_k, W_w, gamma, beta, eps, k_base, k_slot, w, ldww, ldwo};
     hipLaunchKernelGGL(proj_kw_kernel, dim3((unsigned)mt), dim3(256), smem_kw, stream, a);
     return hipGetLastError();
 }

@@ -1,0 +1,61 @@
+// The rotary step of the DeepSeek-V3.2-shaped indexer.  The pages give it 64 heads (sparse-
+// attention row of the "Qwen3.5-397B-A17B vs Kimi K3.1 Pro" compare page) and say it rotates
+// 64 of its 128 dims (RoPE row of the "Kimi K3.1 Pro vs Gemma 4 31B" page).  Read here as:
+// dims (2i, 2i+1), i < 32, of every query head and of the key turn by the angle
+// pos * theta^(-2i/64), applied to the projections as stored in bf16 and rounded to bf16
+// once more; dims 64..127 stay.
+//
+// One thread per (token, pair): it forms the angle and its sine and cosine in fp64 (positions
+// reach 2^20, where an fp32 angle would be off by tenths of a radian), turns the pair of every
+// head and of the key in fp64, and rounds each result to bf16 directly (round to odd into fp32,
+// then to nearest even into bf16, which is the correctly rounded bf16 value).  The 32 threads
+// of a token touch 128 contiguous bytes of each head.
+#include "common.hpp"
+#include "launch.hpp"
+
+namespace dsaidx {
+namespace {
+
+constexpr int kRotPairs = 32;   // pairs turned per head: 64 of the 128 dims
+
+__device__ __forceinline__ uint16_t f64_to_bf16(double x) {
+    float f = __double2float_rz(x);
+    if ((double)f != x) f = __uint_as_float(__float_as_uint(f) | 1u);   // round to odd (NaN stays NaN)
+    return (uint16_t)f32_to_bf16(f);
+}
+
+__device__ __forceinline__ void turn(uint16_t *p, double c, double s) {
+    const uint32_t v = *reinterpret_cast<const uint32_t *>(p);
+    const double x = (double)bf16_to_f32(v & 0xFFFFu), y = (double)bf16_to_f32(v >> 16);
+    const uint32_t o = (uint32_t)f64_to_bf16(x * c - y * s) | ((uint32_t)f64_to_bf16(x * s + y * c) << 16);
+    *reinterpret_cast<uint32_t *>(p) = o;
+}
+
+__global__ __launch_bounds__(256) void rope_kernel(uint16_t *q, int64_t ldq, int heads, uint16_t *k, int64_t ldk,
+                                                   int64_t T, int64_t pos0, double theta) {
+    const int64_t g = (int64_t)blockIdx.x * 256 + threadIdx.x;
+    const int64_t t = g / kRotPairs;
+    const int i = (int)(g % kRotPairs);
+    if (t >= T) return;
+    const double ang = (double)(pos0 + t) * pow(theta, -2.0 * i / (2 * kRotPairs));
+    double s, c;
+    sincos(ang, &s, &c);
+    if (q) {
+        uint16_t *qr = q + t * ldq + 2 * i;
+        for (int h = 0; h < heads; ++h) turn(qr + (int64_t)h * kDim, c, s);
+    }
+    if (k) turn(k + t * ldk + 2 * i, c, s);
+}
+
+}  // namespace
+
+hipError_t launch_rope(uint16_t *q, int64_t ldq, int heads, uint16_t *k, int64_t ldk, int64_t T, int64_t pos0,
+                       double theta, hipStream_t stream) {
+    if (T == 0) return hipSuccess;
+    const int64_t n = T * kRotPairs;
+    hipLaunchKernelGGL(rope_kernel, dim3((unsigned)((n + 255) / 256)), dim3(256), 0, stream, q, ldq, heads, k, ldk,
+                       T, pos0, theta);
+    return hipGetLastError();
+}
+
+}  // namespace dsaidx

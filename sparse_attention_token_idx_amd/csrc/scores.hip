@@ -58,6 +58,8 @@ struct ScoreArgs {
                                 // of a row block's tiles in one workgroup, grid.x = sequence)
     float *out;                 // triangular score rows
     float *dummy;               // write target of rows past a sequence end
+    int64_t ldq;                // row stride of q (elements): 4,096, or 8,192 for 64 heads
+    int64_t ldw;                // row stride of w: 32, or 64
 };
 
 // Polls `ctr` (the smallest of kWaves counters) until it reaches `target`.  Every target is
@@ -85,6 +87,9 @@ __device__ __forceinline__ void signal(uint32_t *ctr) {
     __hip_atomic_fetch_add(ctr, __lane_id() == 0 ? 1u : 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_WORKGROUP);
 }
 
+// kAccum: add the scores to the rows already there (the second half of a 64-head score,
+// whose head sum splits into two 32-head sums) instead of writing them.
+template <bool kAccum>
 __global__ __launch_bounds__(kThreads, 1) void score_rows_kernel(ScoreArgs a) {
     extern __shared__ __align__(16) unsigned char smem_raw[];
     ScoreSmem &sm = *reinterpret_cast<ScoreSmem *>(smem_raw);
@@ -132,7 +137,7 @@ __global__ __launch_bounds__(kThreads, 1) void score_rows_kernel(ScoreArgs a) {
         const int qrow = 4 * wave + (l16 >> 2);
         const bool qok = qrow < rows_here;
         const int64_t gq = seq_start + r0 + (qok ? qrow : 0);
-        const uint16_t *qp = a.q + gq * kQOut + (l16 & 3) * kDim + 8 * lg;
+        const uint16_t *qp = a.q + gq * a.ldq + (l16 & 3) * kDim + 8 * lg;
 #pragma unroll
         for (int g = 0; g < 8; ++g)
 #pragma unroll
@@ -145,7 +150,7 @@ __global__ __launch_bounds__(kThreads, 1) void score_rows_kernel(ScoreArgs a) {
         const int64_t gw = seq_start + r0 + (wok ? wrow : 0);
 #pragma unroll
         for (int g = 0; g < 8; ++g) {
-            const uint2 w4 = *reinterpret_cast<const uint2 *>(a.w + gw * kHeads + 4 * g);
+            const uint2 w4 = *reinterpret_cast<const uint2 *>(a.w + gw * a.ldw + 4 * g);
             wv[g] = wok ? f32x4{bf16_to_f32(w4.x & 0xFFFFu), bf16_to_f32(w4.x >> 16),
                                 bf16_to_f32(w4.y & 0xFFFFu), bf16_to_f32(w4.y >> 16)}
                         : f32x4{0.f, 0.f, 0.f, 0.f};
@@ -213,6 +218,12 @@ __global__ __launch_bounds__(kThreads, 1) void score_rows_kernel(ScoreArgs a) {
 #pragma unroll 1
     for (int t = 0; t < nt; ++t) {
         wait_min_geq(sm.k_staged, (uint32_t)(t + 1), spin);   // tile t staged by every wave
+        f32x4 old0, old1;   // kAccum: this tile's scores so far, loaded under the tile's products
+        if constexpr (kAccum) {
+            const float *src = (kt0 + t < row_nt ? orow : drow) + (int64_t)(kt0 + t) * kBK;
+            old0 = *reinterpret_cast<const f32x4 *>(src);
+            old1 = *reinterpret_cast<const f32x4 *>(src + 4);
+        }
         const uint16_t *kb = &sm.k[t % kKR][l16][8 * lg];
         u32x4 b[4];
 #pragma unroll
@@ -259,6 +270,13 @@ __global__ __launch_bounds__(kThreads, 1) void score_rows_kernel(ScoreArgs a) {
         // one store and one load per tile, unconditionally and in this order, so that the
         // wait for the load in the next tile never has to include a store
         float *const dst = (kt0 + t < row_nt ? orow : drow) + (int64_t)(kt0 + t) * kBK;
+        if constexpr (kAccum) {
+#pragma unroll
+            for (int r = 0; r < 4; ++r) {
+                sc[r] += old0[r];
+                sc[4 + r] += old1[r];
+            }
+        }
         *reinterpret_cast<f32x4 *>(dst) = f32x4{sc[0], sc[1], sc[2], sc[3]};
         *reinterpret_cast<f32x4 *>(dst + 4) = f32x4{sc[4], sc[5], sc[6], sc[7]};
         // stage tile t + kKR - 2 into the slot of tile t - 2 once every wave is done with it
@@ -302,11 +320,21 @@ __global__ __launch_bounds__(1024) void seq_base_kernel(const int32_t *cu_seqlen
 hipError_t launch_scores(const uint16_t *q, const uint16_t *k, const uint16_t *w,
                          const int32_t *cu_seqlens, int B, int64_t max_len, int64_t T, int64_t pos0,
                          int64_t *seq_base, float *out, float *dummy, hipStream_t stream) {
+    return launch_scores_ex(q, kQOut, k, w, kHeads, false, cu_seqlens, B, max_len, T, pos0, seq_base, out, dummy,
+                            stream);
+}
+
+hipError_t launch_scores_ex(const uint16_t *q, int64_t ldq, const uint16_t *k, const uint16_t *w, int64_t ldw,
+                            bool accumulate, const int32_t *cu_seqlens, int B, int64_t max_len, int64_t T,
+                            int64_t pos0, int64_t *seq_base, float *out, float *dummy, hipStream_t stream) {
     static bool attr_done = false;
     const size_t smem = sizeof(ScoreSmem);
     if (!attr_done) {
-        hipError_t e = hipFuncSetAttribute(reinterpret_cast<const void *>(score_rows_kernel),
+        hipError_t e = hipFuncSetAttribute(reinterpret_cast<const void *>(score_rows_kernel<false>),
                                            hipFuncAttributeMaxDynamicSharedMemorySize, (int)smem);
+        if (e != hipSuccess) return e;
+        e = hipFuncSetAttribute(reinterpret_cast<const void *>(score_rows_kernel<true>),
+                                hipFuncAttributeMaxDynamicSharedMemorySize, (int)smem);
         if (e != hipSuccess) return e;
         attr_done = true;
     }
@@ -327,6 +355,8 @@ hipError_t launch_scores(const uint16_t *q, const uint16_t *k, const uint16_t *w
     a.nrb = (int)((max_len + kBQ - 1) / kBQ);
     a.out = out;
     a.dummy = dummy;
+    a.ldq = ldq;
+    a.ldw = ldw;
     // One sequence with few row blocks (a chunk of queries against a long prefix): split each
     // row block's key tiles over several workgroups, for about kFillWg workgroups of at least
     // kMinSegTiles tiles.  A score needs no reduction across keys, so segments are independent.
@@ -342,7 +372,10 @@ hipError_t launch_scores(const uint16_t *q, const uint16_t *k, const uint16_t *w
             gx = (unsigned)((max_nkt + st - 1) / st);
         }
     }
-    hipLaunchKernelGGL(score_rows_kernel, dim3(gx, a.nrb), dim3(kThreads), smem, stream, a);
+    if (accumulate)
+        hipLaunchKernelGGL(score_rows_kernel<true>, dim3(gx, a.nrb), dim3(kThreads), smem, stream, a);
+    else
+        hipLaunchKernelGGL(score_rows_kernel<false>, dim3(gx, a.nrb), dim3(kThreads), smem, stream, a);
     return hipGetLastError();
 }
 

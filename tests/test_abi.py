@@ -31,7 +31,7 @@ def test_exports_every_declared_symbol(dsa):
                           "dsa_idx_project", "dsa_idx_score_topk", "dsa_idx_score_topk_varlen",
                           "dsa_idx_prefill_scores", "dsa_idx_prefill_select", "dsa_idx_decode",
                           "dsa_idx_quantize_keys", "dsa_idx_decode_fp8", "dsa_idx_prefill_chunk",
-                          "dsa_idx_sparse_mla"}
+                          "dsa_idx_sparse_mla", "dsa_idx_v32_project", "dsa_idx_v32_score_topk"}
     for n in names:
         assert getattr(L, n) is not None
 
@@ -164,6 +164,40 @@ def test_rejections_before_device(dsa):
     assert mla(_vp(A), _vp(A), _vp(A), None, 4, 8, f(0.0), _vp(A), None, _vp(A), 1 << 30, None) == -1
     assert mla(_vp(A), _vp(A), _vp(A), None, 64, 2048, f(0.1), _vp(A), None, _vp(A), 16, None) == -3
     assert mla(None, None, None, None, 0, 8, f(0.1), None, None, None, 0, None) == 0
+    # 64-head indexer: the score call has the one-sequence rules, its workspace the same size
+    v32 = lambda *a: L.dsa_idx_v32_score_topk(*a)
+    assert v32(_vp(A), _vp(A), _vp(A), 100, 0, _vp(A), None, _vp(A), 1 << 30, None) == -2
+    assert v32(_vp(A), _vp(A), _vp(A), -1, 8, _vp(A), None, _vp(A), 1 << 30, None) == -1
+    assert v32(_vp(A), None, _vp(A), 100, 8, _vp(A), None, _vp(A), 1 << 30, None) == -1
+    assert v32(_vp(A), _vp(A + 8), _vp(A), 100, 8, _vp(A), None, _vp(A), 1 << 30, None) == -1
+    assert v32(_vp(A), _vp(A), _vp(A), 100, 8, _vp(A), None, _vp(A), 16, None) == -3
+    assert v32(None, None, None, 0, 8, None, None, None, 0, None) == 0
+    assert dsa.workspace_size(dsa.OP_V32_SCORE_TOPK, 1000) == dsa.workspace_size(dsa.OP_SCORE_TOPK, 1000)
+    assert dsa.workspace_size(dsa.OP_V32_PROJECT, 100) == dsa.workspace_size(dsa.OP_PROJECT, 100)
+    assert dsa.workspace_size(dsa.OP_V32_PROJECT, 7) == dsa.workspace_size(dsa.OP_PROJECT, 7)
+
+
+def test_v32_project_rejections(dsa):
+    L = dsa.lib()
+    A = 0x10000
+    W = dsa._Weights(A, A, A, A, A, 1e-6)
+    f = ctypes.c_float
+
+    def call(wt=W, ldx=7168, ldc=1536, T=4, pos0=0, theta=1e4, q=_vp(A), k=_vp(A), w=_vp(A), x=_vp(A),
+             ws=_vp(A), nbytes=1 << 30):
+        return L.dsa_idx_v32_project(ctypes.byref(wt) if wt is not None else None, x, ldx, _vp(A), ldc, T,
+                                     pos0, f(theta), q, k, w, ws, nbytes, None)
+    assert call(wt=None) == -1
+    assert call(T=-1) == -1
+    assert call(pos0=-5) == -1
+    assert call(theta=0.0) == -1
+    assert call(ldx=7000) == -1
+    assert call(ldc=1537) == -1
+    assert call(k=None) == -1
+    assert call(x=_vp(A + 8)) == -1
+    assert call(wt=dsa._Weights(A, A, A, A, A, 0.0)) == -1
+    assert call(T=4, ws=None, nbytes=0) == -3
+    assert call(T=0) == 0
 
 
 def test_project_rejections(dsa):

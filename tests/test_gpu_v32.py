@@ -1,0 +1,111 @@
+"""GPU parity of the 64-head (DeepSeek-V3.2-shaped) indexer against the CPU oracle.
+
+Projections: q, k and w against the fp64 products (the fp32 accumulation bound of the existing
+projection test), with the rotary step applied to the exact values.  The GPU rounds each
+projection to bf16, turns it (fp64) and rounds again, so a pre-rotation error d per element
+(accumulation bound + one ulp) moves a rotated pair by at most sqrt(d_x^2 + d_y^2), and the last
+rounding adds one ulp.  Scores and selection: the parity rule of tests/helpers.py, with the
+oracle scoring all 64 heads (the GPU sums two 32-head halves in fp32)."""
+import numpy as np
+import pytest
+import torch
+
+import oracle
+from oracle import D, V32_H
+from synth import workloads as wl
+from tests.helpers import (U32, assert_bf16_within, bf16_ulp, check_row, projection_bounds, to_dev,
+                           to_host, weights_to_dev)
+
+pytestmark = pytest.mark.gpu
+
+
+@pytest.fixture(scope="module")
+def dsa():
+    import sparse_attention_token_idx_amd as m
+    assert torch.cuda.is_available()
+    return m
+
+
+def _rot_bound(exact, err):
+    d = err + bf16_ulp(exact)
+    out = d.copy()
+    pair = np.sqrt(d[..., 0:64:2] ** 2 + d[..., 1:64:2] ** 2)
+    out[..., 0:64:2] = pair
+    out[..., 1:64:2] = pair
+    return out
+
+
+@pytest.mark.parametrize("T,pos0", [(1, 0), (37, 5000), (300, 0), (130, 1_000_000)])
+def test_v32_project_matches_oracle(dsa, T, pos0):
+    Wt = wl.layer_weights_v32(seed=T)
+    act = wl.layer_activations(T, seed=T + 1)
+    print(f"v32 project: T={T} pos0={pos0}", flush=True)
+    q, k, w = dsa.v32_project(to_dev(act["x"]), to_dev(act["c_q"]), weights_to_dev(Wt), pos0=pos0)
+    torch.cuda.synchronize()
+    pos = pos0 + np.arange(T)
+    eq, bq = projection_bounds(act["c_q"], Wt["W_q"])
+    eq, bq = eq.reshape(T, V32_H, D), bq.reshape(T, V32_H, D)
+    assert_bf16_within(to_host(q).reshape(T, V32_H, D), oracle.rope_f64(eq, pos), _rot_bound(eq, bq), "q")
+    ew, bw = projection_bounds(act["x"], Wt["W_w"])
+    assert_bf16_within(to_host(w), ew, bw, "w")
+    ea, ba = projection_bounds(act["x"], Wt["W_k"])
+    ek = oracle.layernorm_f64(ea, Wt["gamma"], Wt["beta"], Wt["eps"])
+    sigma = np.sqrt(ea.var(axis=1, keepdims=True) + Wt["eps"])
+    gam = np.abs(oracle.bf16_to_f64(Wt["gamma"]))[None, :]
+    bk = 2 * ba.max(axis=1, keepdims=True) / sigma * gam + 16 * U32 * (np.abs(ek) + 1)
+    assert_bf16_within(to_host(k), oracle.rope_f64(ek, pos), _rot_bound(ek, bk), "k")
+    # and nearly always the oracle's own bf16 values
+    oq, ok, ow = oracle.project_v32(act["x"], act["c_q"], Wt, pos0=pos0)
+    fr = [float((to_host(g).reshape(o.shape) != o).mean()) for g, o in ((q, oq), (k, ok), (w, ow))]
+    print(f"  fraction differing from the oracle's bf16 values: q {fr[0]:.1e} k {fr[1]:.1e} w {fr[2]:.1e}")
+    assert max(fr) < 2e-2
+
+
+def _inputs(T, seed):
+    rng = np.random.default_rng(seed)
+    q = oracle.f64_to_bf16(rng.standard_normal((T, V32_H, D)))
+    k = oracle.f64_to_bf16(rng.standard_normal((T, D)))
+    w = oracle.f64_to_bf16(rng.standard_normal((T, V32_H)) * np.sqrt(0.1))
+    return q, k, w
+
+
+@pytest.mark.parametrize("T,topk", [(1, 5), (300, 2048), (2600, 2048), (2600, 100)])
+def test_v32_score_topk_matches_oracle(dsa, T, topk):
+    q, k, w = _inputs(T, T + topk)
+    print(f"v32 score_topk: T={T} topk={topk}", flush=True)
+    idx, sc = dsa.v32_score_topk(to_dev(q), to_dev(k), to_dev(w), topk=topk)
+    torch.cuda.synchronize()
+    idx, sc = idx.cpu().numpy(), sc.cpu().numpy()
+    rows = np.arange(T) if T <= 300 else np.array([0, 1, 127, 128, 129, 1000, 2047, 2048, 2049, 2599])
+    ref = oracle.prefill_rows(q, k, w, rows, topk=topk, full=True)
+    for r, t in enumerate(rows):
+        check_row(int(t), idx[t], sc[t], ref, r, topk)
+
+
+def test_v32_end_to_end(dsa):
+    T = 700
+    Wt = wl.layer_weights_v32(seed=11)
+    act = wl.layer_activations(T, seed=11)
+    print(f"v32 end to end: T={T}", flush=True)
+    q, k, w = dsa.v32_project(to_dev(act["x"]), to_dev(act["c_q"]), weights_to_dev(Wt))
+    idx, sc = dsa.v32_score_topk(q, k, w, topk=256)
+    torch.cuda.synchronize()
+    qh, kh, wh = to_host(q).reshape(T, V32_H, D), to_host(k), to_host(w)
+    rows = np.array([0, 255, 256, 257, 511, 699])
+    ref = oracle.prefill_rows(qh, kh, wh, rows, topk=256, full=True)
+    for r, t in enumerate(rows):
+        check_row(int(t), idx.cpu().numpy()[t], sc.cpu().numpy()[t], ref, r, 256)
+
+
+def test_v32_full_size_sampled_rows(dsa):
+    # the benchmark's launch: T = 65,536, top 2,048, checked on sampled rows
+    T, topk = 65536, 2048
+    q, k, w = _inputs(T, 7)
+    print(f"v32 full size: T={T}", flush=True)
+    idx, sc = dsa.v32_score_topk(to_dev(q), to_dev(k), to_dev(w), topk=topk)
+    torch.cuda.synchronize()
+    rows = np.array([0, 2047, 2048, 30000, 65535])
+    idx, sc = idx[rows].cpu().numpy(), sc[rows].cpu().numpy()
+    ref = oracle.prefill_rows(q, k, w, rows, topk=topk, full=True)
+    for r, t in enumerate(rows):
+        check_row(int(t), idx[r], sc[r], ref, r, topk)
