@@ -37,10 +37,11 @@ PEAK_BF16_TFLOPS = 2516.6     # MI355X dense bf16 MFMA (published)
 # HBM bytes per launch of the scoring kernel at T=65536, from rocprofv3 FETCH_SIZE and
 # WRITE_SIZE scaled by a 1 GiB device-copy calibration; reported only while the kernel
 # source is the one the counters were taken on (None: not measured for this source)
-TRAFFIC_SCORE_T65536 = {"source_sha256_prefix": "497fca71c49eba94", "bytes": 10869075527}
+TRAFFIC_SCORE_T65536 = {"source_sha256_prefix": "4540d23fdcbccca7", "bytes": 10781450858}
 PEAK_HBM_GBPS = 8000.0        # MI355X HBM3E (published)
 H, D, QLAT, HIDDEN = 32, 128, 1536, 7168
 MLA_HEADS, MLA_KV, MLA_V = 96, 576, 512          # the sparse MLA consumer (gated-MLA row)
+V32_H = 64                                        # the DeepSeek-V3.2-shaped indexer
 PROJ_FLOP_PER_TOKEN = 2 * (QLAT * 4096 + HIDDEN * D + HIDDEN * H)   # 14,876,672
 SCORE_FLOP_PER_PAIR = 2 * H * D                                     # 8,192
 
@@ -61,6 +62,7 @@ def parse():
     p.add_argument("--decode-batch", type=int, default=64)
     p.add_argument("--no-chunk", action="store_true")
     p.add_argument("--no-mla", action="store_true")
+    p.add_argument("--no-v32", action="store_true")
     p.add_argument("--chunk", type=int, default=4096)
     p.add_argument("--window", type=int, default=1048576)
     p.add_argument("--calibrate-copy", action="store_true",
@@ -291,6 +293,56 @@ def bench_mla(dsa, args, idx, start_d, sum_keys, n):
     return dict(ms=ms, bytes=nbytes, flop=flop, GBps=gbps)
 
 
+def bench_v32(dsa, args):
+    """The 64-head (DeepSeek-V3.2-shaped) indexer layer at the same T: projections with the
+    rotary step, then scores (two 32-head passes) and top-k."""
+    import torch
+    from synth import workloads as wl
+    T, topk = args.T, args.topk
+    t0 = time.time()
+    Wt = wl.layer_weights_v32(layer=0, seed=0)
+    act = wl.layer_activations(T, seed=0)
+    W = {k: dev_bf16(v) for k, v in Wt.items() if k != "eps"}
+    W["eps"] = Wt["eps"]
+    x, cq = dev_bf16(act["x"]), dev_bf16(act["c_q"])
+    del act
+    log(f"v32: inputs T={T} in {time.time() - t0:.1f}s")
+    q = torch.empty((T, V32_H, D), dtype=torch.bfloat16, device="cuda")
+    k = torch.empty((T, D), dtype=torch.bfloat16, device="cuda")
+    w = torch.empty((T, V32_H), dtype=torch.bfloat16, device="cuda")
+    idx = torch.empty((T, topk), dtype=torch.int32, device="cuda")
+    sc = torch.empty((T, topk), dtype=torch.float32, device="cuda")
+    ws = torch.empty(dsa.workspace_size(dsa.OP_V32_SCORE_TOPK, T, topk=topk), dtype=torch.uint8, device="cuda")
+    stream = torch.cuda.current_stream()
+
+    def step(ev=None):
+        if ev is not None:
+            ev[0].record(stream)
+        dsa.v32_project(x, cq, W, q=q, k=k, w=w)
+        if ev is not None:
+            ev[1].record(stream)
+        dsa.v32_score_topk(q, k, w, topk=topk, ws=ws, out=(idx, sc))
+        if ev is not None:
+            ev[2].record(stream)
+
+    step()
+    torch.cuda.synchronize()
+    n = max(2, min(args.steps, 5))
+    evs = [[torch.cuda.Event(enable_timing=True) for _ in range(3)] for _ in range(n)]
+    for i in range(n):
+        step(evs[i])
+    torch.cuda.synchronize()
+    proj_ms = float(np.mean([e[0].elapsed_time(e[1]) for e in evs]))
+    st_ms = float(np.mean([e[1].elapsed_time(e[2]) for e in evs]))
+    pairs = T * (T + 1) // 2
+    score_flop = pairs * 2 * V32_H * D
+    log(f"v32: project {proj_ms:.3f} ms, scores + select {st_ms:.3f} ms "
+        f"({score_flop / (st_ms * 1e-3) / 1e12:.1f} TFLOP/s of scoring over the call)")
+    del ws
+    return dict(proj_ms=proj_ms, score_topk_ms=st_ms, pairs=pairs, score_flop=score_flop,
+                qps=T / ((proj_ms + st_ms) * 1e-3))
+
+
 def bench_chunk(dsa, args):
     """The last `chunk` queries of a `window`-token sequence against its whole prefix."""
     import torch
@@ -375,6 +427,7 @@ def main():
     pre = bench_prefill(dsa, args)
     dec = None if args.no_decode else bench_decode(dsa, args)
     chk = None if args.no_chunk else bench_chunk(dsa, args)
+    v32 = None if args.no_v32 else bench_v32(dsa, args)
     ms_step = pre["proj_ms"] + pre["score_ms"] + pre["select_ms"]
     ms_wall = pre["wall"] * 1e3 / args.steps
     qps = args.T / (ms_wall * 1e-3)
@@ -435,6 +488,13 @@ def main():
             "score_tflops_over_call": round(chk["tflops"], 1),
             "frac_of_bf16_peak": round(chk["tflops"] / PEAK_BF16_TFLOPS, 4),
             "causal_pairs": chk["pairs"]},
+        "v32_indexer": None if v32 is None else {
+            "workload": f"the 64-head (DeepSeek-V3.2-shaped) indexer layer, causal prefill T={args.T}, "
+                        f"top-{args.topk}: project + rotary step, scores (two 32-head passes) + select",
+            "ms_per_step": round(v32["proj_ms"] + v32["score_topk_ms"], 3),
+            "queries_per_s": round(v32["qps"], 1), "project_ms": round(v32["proj_ms"], 3),
+            "score_topk_ms": round(v32["score_topk_ms"], 3),
+            "score_tflops_over_call": round(v32["score_flop"] / (v32["score_topk_ms"] * 1e-3) / 1e12, 1)},
         "cpu_baseline": cpu,
     }
     print(json.dumps(line), flush=True)
