@@ -193,26 +193,31 @@ __global__ __launch_bounds__(kMlaThreads, 1) void sparse_mla_kernel(MlaArgs a) {
     float m_run = -INFINITY;   // running max of the head's logits (log2 domain)
     float l_run = 0.f;         // this lane's part of the running sum
 
-    if (ntile > 0) load_tile(0, 0);
-    if (ntile > 1) load_tile(1, kTileBytes);
-    // byte offset of the current tile's buffer, kept in a scalar register (computing it from
-    // the tile index costs vector instructions on every operand address)
-    int buf_off = 0;
-#pragma unroll 1
-    for (int tile = 0; tile < ntile; ++tile) {
-        // this tile's loads have landed (the next tile's may still be in flight) ...
-        if (tile + 1 < ntile)
-            asm volatile("s_waitcnt vmcnt(3)" ::: "memory");
-        else
-            asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
-        // ... for every wave, and every wave is done with the previous tile, whose buffer the
-        // loads of tile + 2 now refill
-        lds_barrier();
-        const int prev_off = buf_off == 0 ? (kBufs - 1) * kTileBytes : buf_off - kTileBytes;
-        if (tile + 2 < ntile) load_tile(tile + 2, prev_off);   // tile + 2 takes the previous tile's buffer
-        const lds_char *kb = lds_k + __builtin_amdgcn_readfirstlane(buf_off);
-        buf_off = buf_off == (kBufs - 1) * kTileBytes ? 0 : buf_off + kTileBytes;
+    u32x4 pb = {0u, 0u, 0u, 0u};   // P^T of the tile whose values are added next (bf16 pairs)
+    float factor = 1.f;            // and the rescaling of the output that must come first
+    bool rescale = false;
 
+    // Output update with the previous tile's values: O^T += V^T P^T over one 16-dim tile mt.
+    auto pv = [&](const lds_char *vb, int mt) {
+        const lds_char *vp = vb + pv_base[mt & 1] + 128 * (mt >> 1);
+        const uint2 lo = tr_read(vp);
+        const uint2 hi = tr_read(vp + kHalfTileBytes);
+        acc_o[mt] = mfma16x16x32(u32x4{lo.x, lo.y, hi.x, hi.y}, pb, acc_o[mt]);
+    };
+    auto apply_rescale = [&] {
+        if (__builtin_expect(rescale, 0)) {   // wave-uniform, rarely taken after the first tiles
+#pragma unroll
+            for (int mt = 0; mt < kMt; ++mt)
+#pragma unroll
+                for (int r = 0; r < 4; ++r) acc_o[mt][r] *= factor;
+        }
+    };
+    // One pipeline step: the logits of tile `tile` (buffer kb); then, when with_pv, the output
+    // update with the previous tile's values (buffer vb), issued just before the barrier of the
+    // logit exchange so that the matrix cores work through it while the waves compute the
+    // softmax (a barrier does not wait for them); then the softmax, which leaves the weights
+    // for the next step's output update in pb / factor / rescale.
+    auto step = [&](int tile, const lds_char *kb, const lds_char *vb, bool with_pv) {
         // logits: S^T rows are tokens (two 16-token halves), columns the pair's 16 heads; this
         // wave sums its k-steps, the partner's come through LDS
         f32x4 s0 = {0.f, 0.f, 0.f, 0.f}, s1 = {0.f, 0.f, 0.f, 0.f};
@@ -226,6 +231,11 @@ __global__ __launch_bounds__(kMlaThreads, 1) void sparse_mla_kernel(MlaArgs a) {
         }
         sm.sx[wave][0][lane] = s0;
         sm.sx[wave][1][lane] = s1;
+        if (with_pv) {
+            apply_rescale();
+#pragma unroll
+            for (int mt = 0; mt < kMt; ++mt) pv(vb, mt);
+        }
         lds_barrier();
         {   // mine + partner's: both waves of a pair add the same two numbers, so they agree
             const f32x4 o0 = sm.sx[wave ^ 1][0][lane], o1 = sm.sx[wave ^ 1][1][lane];
@@ -256,7 +266,7 @@ __global__ __launch_bounds__(kMlaThreads, 1) void sparse_mla_kernel(MlaArgs a) {
         // logits, so they move it together.
         const bool move = mx > m_run + kLazy;
         const float m_new = move ? mx : m_run;
-        const float factor = move ? exp2_hw(m_run - m_new) : 1.f;   // 0 when m_run is -inf
+        factor = move ? exp2_hw(m_run - m_new) : 1.f;   // 0 when m_run is -inf
         float p[8];
         if (m_new == -INFINITY) {
 #pragma unroll
@@ -266,29 +276,50 @@ __global__ __launch_bounds__(kMlaThreads, 1) void sparse_mla_kernel(MlaArgs a) {
             for (int r = 0; r < 8; ++r) p[r] = exp2_hw(z[r] - m_new);
         }
         m_run = m_new;
-        const bool rescale = __ballot(move) != 0;
+        rescale = __ballot(move) != 0;
         float ps = 0.f;
 #pragma unroll
         for (int r = 0; r < 8; ++r) ps += p[r];
         l_run = l_run * factor + ps;
         // P^T as the B operand: k slots 8 g .. 8 g + 7 are the lane's 8 tokens, and the V^T
         // operand holds the same tokens (4 g .. 4 g + 3 and 16 + 4 g .. + 3)
-        const u32x4 pb = {bf16_pair(p[0], p[1]), bf16_pair(p[2], p[3]), bf16_pair(p[4], p[5]),
-                          bf16_pair(p[6], p[7])};
-        if (__builtin_expect(rescale, 0)) {   // a wave-uniform branch, rarely taken after the first tiles
-#pragma unroll
-            for (int mt = 0; mt < kMt; ++mt)
-#pragma unroll
-                for (int r = 0; r < 4; ++r) acc_o[mt][r] *= factor;
+        pb = u32x4{bf16_pair(p[0], p[1]), bf16_pair(p[2], p[3]), bf16_pair(p[4], p[5]), bf16_pair(p[6], p[7])};
+    };
+
+    // Tiles 0 and 1 are loaded ahead, tile 2 during step 0, and tile t + 1 (t >= 2) during step
+    // t, into the buffer of tile t - 2, whose values step t - 1 consumed.  So when step t
+    // begins, the loads of tile t + 1 are still in flight only for t <= 1.
+    if (ntile > 0) load_tile(0, 0);
+    if (ntile > 1) load_tile(1, kTileBytes);
+    // byte offsets of the current and previous tiles' buffers, kept in scalar registers
+    // (computing them from the tile index costs vector instructions on every operand address)
+    int cur_off = 0, prev_off = 0;
+#pragma unroll 1
+    for (int tile = 0; tile < ntile; ++tile) {
+        if (tile + 1 < ntile && tile <= 1)
+            asm volatile("s_waitcnt vmcnt(3)" ::: "memory");
+        else
+            asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
+        // every wave's loads of this tile have landed, and every wave is done with step
+        // tile - 1, i.e. with the values of tile - 2
+        lds_barrier();
+        const int next_off = cur_off == (kBufs - 1) * kTileBytes ? 0 : cur_off + kTileBytes;
+        if (tile == 0) {
+            if (ntile > 2) load_tile(2, 2 * kTileBytes);
+        } else if (tile >= 2 && tile + 1 < ntile) {
+            load_tile(tile + 1, next_off);
         }
+        const lds_char *kb = lds_k + __builtin_amdgcn_readfirstlane(cur_off);
+        const lds_char *vb = lds_k + __builtin_amdgcn_readfirstlane(prev_off);
+        step(tile, kb, vb, tile > 0);
+        prev_off = cur_off;
+        cur_off = next_off;
+    }
+    if (ntile > 0) {   // the last tile's values
+        const lds_char *vb = lds_k + __builtin_amdgcn_readfirstlane(prev_off);
+        apply_rescale();
 #pragma unroll
-        for (int mt = 0; mt < kMt; ++mt) {
-            const lds_char *vp = kb + pv_base[mt & 1] + 128 * (mt >> 1);
-            const uint2 lo = tr_read(vp);
-            const uint2 hi = tr_read(vp + kHalfTileBytes);
-            const u32x4 va = {lo.x, lo.y, hi.x, hi.y};
-            acc_o[mt] = mfma16x16x32(va, pb, acc_o[mt]);
-        }
+        for (int mt = 0; mt < kMt; ++mt) pv(vb, mt);
     }
 
     // the head's sum over its 4 lane groups
