@@ -377,32 +377,42 @@ def bench_chunk(dsa, args):
 
 
 def cpu_baseline(args):
-    """The oracle on a bounded sample of the T-token layer, extrapolated per its cost model."""
+    """The oracle on a bounded sample of the T-token layer, extrapolated per its cost model.
+
+    Keys are projected for every token the sampled rows need; then batches of sampled rows
+    (q and w projected, each row scored over its whole causal prefix and fully sorted), each
+    batch twice the last, until about 10 s of oracle work has been measured."""
     import oracle
     from synth import workloads as wl
     T, topk = args.T, args.topk
     cores = oracle.num_threads()
     rng = np.random.default_rng(0)
-    rows = np.unique(np.concatenate([[0, T - 1], rng.integers(0, T, 62)]))
     Wt = wl.layer_weights(layer=0, seed=0)
     act = wl.layer_activations(T, seed=0)
-    kmax = int(rows.max()) + 1
     t0 = time.perf_counter()
-    _, k_all, _ = oracle.project(act["x"][:kmax], None, Wt, want=("k",))   # every key needed
+    _, k_all, _ = oracle.project(act["x"], None, Wt, want=("k",))   # every key
     t_k = time.perf_counter() - t0
-    t0 = time.perf_counter()
-    q_s, _, w_s = oracle.project(act["x"][rows], act["c_q"][rows], Wt, want=("q", "w"))
-    t_qw = time.perf_counter() - t0
-    t0 = time.perf_counter()
-    oracle.rows(q_s, w_s, k_all, np.zeros(len(rows), np.int64), rows, topk=topk)
-    t_rows = time.perf_counter() - t0
-    total = (t_k * T / kmax + t_qw * T / len(rows)
-             + t_rows * (T * (T + 1) / 2) / float((rows + 1).sum()))
+    t_qw = t_rows = 0.0
+    n_rows = pairs = 0
+    batch = np.array([0, T - 1] + rng.integers(0, T, 62).tolist())
+    while True:
+        t0 = time.perf_counter()
+        q_s, _, w_s = oracle.project(act["x"][batch], act["c_q"][batch], Wt, want=("q", "w"))
+        t_qw += time.perf_counter() - t0
+        t0 = time.perf_counter()
+        oracle.rows(q_s, w_s, k_all, np.zeros(len(batch), np.int64), batch, topk=topk)
+        t_rows += time.perf_counter() - t0
+        n_rows += len(batch)
+        pairs += int((batch + 1).sum())
+        if t_k + t_qw + t_rows >= 10.0 or n_rows >= 8192:
+            break
+        batch = rng.integers(0, T, 2 * len(batch))
+    total = t_k + t_qw * T / n_rows + t_rows * (T * (T + 1) / 2) / float(pairs)
     return dict(value=round(T / total, 2), unit="queries/s", cores=cores, kind="oracle",
-                sample=(f"fp64 oracle, OpenMP over {cores} host threads: keys projected for all "
-                        f"{kmax} tokens, q and w for {len(rows)} sampled rows, those rows scored "
-                        f"over their whole causal prefix and fully sorted; extrapolated to all "
-                        f"{T} rows by tokens (projections) and causal pairs (scores)"),
+                sample=(f"fp64 oracle, OpenMP over {cores} host threads: keys projected for all {T} "
+                        f"tokens, q and w for {n_rows} sampled rows, those rows scored over their whole "
+                        f"causal prefix and fully sorted; extrapolated to all {T} rows by tokens "
+                        f"(projections) and causal pairs (scores)"),
                 measured_s=round(t_k + t_qw + t_rows, 2), extrapolated_s=round(total, 1))
 
 
