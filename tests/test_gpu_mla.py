@@ -112,3 +112,36 @@ def test_sparse_mla_on_the_decode_selection(dsa):
     torch.cuda.synchronize()
     _check(to_host(o).reshape(B, NH, MLA_V), lse.cpu().numpy(), qm, latent, idx.cpu().numpy(),
            row0=start)
+
+
+def test_sparse_mla_full_decode_size(dsa):
+    # the benchmark's launch: 64 queries, top 2,048 each, over a latent cache with one row per
+    # cached token of the decode workload (5.2M rows); sampled queries against the oracle,
+    # which gets only their selected rows
+    lens = wl.decode_lengths(64, seed=0)
+    cache, start = wl.decode_cache(lens, seed=0)
+    B = len(lens)
+    rng = np.random.default_rng(64)
+    qi = _bf(rng.standard_normal((B, 32, 128)))
+    wi = _bf(rng.standard_normal((B, 32)) * 0.3)
+    print(f"sparse mla full size: B={B}, {int(lens.sum())} cache rows", flush=True)
+    idx, _ = dsa.decode(to_dev(qi), to_dev(wi), to_dev(cache), torch.from_numpy(start).cuda(),
+                        torch.from_numpy(lens.astype(np.int32)).cuda(), int(lens.max()), topk=2048)
+    del cache
+    g = torch.Generator(device="cuda")
+    g.manual_seed(5)
+    latent = torch.empty((int(lens.sum()), MLA_KV), dtype=torch.bfloat16, device="cuda")
+    for r0 in range(0, latent.shape[0], 1 << 20):
+        r1 = min(latent.shape[0], r0 + (1 << 20))
+        latent[r0:r1] = torch.randn((r1 - r0, MLA_KV), generator=g, device="cuda").to(torch.bfloat16)
+    qm = _bf(rng.standard_normal((B, NH, MLA_KV)) * 0.5)
+    start_d = torch.from_numpy(start).cuda()
+    o, lse = dsa.sparse_mla(to_dev(qm), latent, idx, row0=start_d)
+    torch.cuda.synchronize()
+    assert dsa.workspace_size(dsa.OP_SPARSE_MLA, B, 0, 0, 2048) > 0   # the split launch
+    pick = np.array([0, 9, 17, 31, 40, 52, 60, 63])
+    idx_h = idx.cpu().numpy()[pick]
+    rows = torch.from_numpy((idx_h.astype(np.int64) + start[pick, None]).reshape(-1)).cuda()
+    kv_sel = to_host(latent[rows])                        # the sampled queries' rows, in order
+    local = np.arange(len(pick) * 2048, dtype=np.int32).reshape(len(pick), 2048)
+    _check(to_host(o).reshape(B, NH, MLA_V)[pick], lse.cpu().numpy()[pick], qm[pick], kv_sel, local)
