@@ -100,12 +100,14 @@ const char *dsa_idx_last_error(void);
 
 /* Bytes of workspace an operation needs (host-only, no device access).
  *   op               one of DSA_IDX_OP_*
- *   total_tokens     T for PROJECT, SCORE_TOPK and SPARSE_MLA; the packed token count for
- *                    VARLEN; the chunk's query count C for PREFILL_CHUNK
+ *   total_tokens     T for PROJECT, SCORE_TOPK, SPARSE_MLA, V32_PROJECT and V32_SCORE_TOPK;
+ *                    the packed token count for VARLEN; the chunk's query count C for
+ *                    PREFILL_CHUNK
  *   B                number of sequences (VARLEN, DECODE); ignored otherwise
  *   max_seqlen       longest sequence (VARLEN, DECODE), keys of the longest cache for DECODE;
  *                    the cached prefix length for PREFILL_CHUNK
- *   topk             tokens kept (selected, for SPARSE_MLA) per query, 1..2048
+ *   topk             tokens kept (selected, for SPARSE_MLA) per query, 1..2048; ignored
+ *                    for PROJECT and V32_PROJECT
  * Writes *bytes (0 is a valid answer).  Returns a status. */
 int dsa_idx_workspace_size(int op, int64_t total_tokens, int B, int max_seqlen, int topk,
                            size_t *bytes);
