@@ -279,6 +279,15 @@ int dsa_idx_v32_score_topk(const dsa_idx_bf16 *q, const dsa_idx_bf16 *k, const d
                            int64_t T, int topk, int32_t *idx, float *scores, void *ws,
                            size_t ws_bytes, void *stream);
 
+/* Ragged prefill for the 64-head indexer: as dsa_idx_score_topk_varlen, with q [total][64][128]
+ * and w [total][64].  The rotary positions are each token's position in its own sequence, so
+ * project each sequence with its own pos0 (dsa_idx_v32_project).
+ * Needs dsa_idx_workspace_size(DSA_IDX_OP_SCORE_TOPK_VARLEN, total, B, max_seqlen, topk) bytes. */
+int dsa_idx_v32_score_topk_varlen(const dsa_idx_bf16 *q, const dsa_idx_bf16 *k,
+                                  const dsa_idx_bf16 *w, const int32_t *cu_seqlens, int B,
+                                  int max_seqlen, int64_t total, int topk, int32_t *idx,
+                                  float *scores, void *ws, size_t ws_bytes, void *stream);
+
 #ifdef __cplusplus
 }
 #endif

@@ -80,6 +80,9 @@ def lib():
                                           ctypes.c_float, vp, vp, vp, vp, sz, vp]
         L.dsa_idx_v32_score_topk.restype = i32
         L.dsa_idx_v32_score_topk.argtypes = [vp, vp, vp, i64, i32, vp, vp, vp, sz, vp]
+        L.dsa_idx_v32_score_topk_varlen.restype = i32
+        L.dsa_idx_v32_score_topk_varlen.argtypes = [vp, vp, vp, vp, i32, i32, i64, i32, vp, vp, vp,
+                                                    sz, vp]
         L.dsa_idx_sparse_mla.restype = i32
         L.dsa_idx_sparse_mla.argtypes = [vp, vp, vp, vp, i64, i32, ctypes.c_float, vp, vp, vp, sz, vp]
         L.dsa_idx_decode.restype = i32
@@ -251,6 +254,30 @@ def v32_score_topk(q, k, w, topk=MAX_TOPK, with_scores=True, ws=None, out=None, 
     _check("dsa_idx_v32_score_topk",
            lib().dsa_idx_v32_score_topk(_ptr(q), _ptr(k), _ptr(w), T, topk, _ptr(idx), _ptr(sc),
                                         _ptr(ws), nbytes, _stream(stream)))
+    return idx, sc
+
+
+def v32_score_topk_varlen(q, k, w, cu_seqlens, max_seqlen, topk=MAX_TOPK, with_scores=True, ws=None,
+                          out=None, stream=None):
+    """Packed sequences for the 64-head indexer: q [total,64,128], k [total,128], w [total,64],
+    cu_seqlens int32 [B+1] on the device; indices relative to each sequence's start."""
+    total = q.shape[0]
+    _need(q, "q", torch.bfloat16, (total, V32_HEADS, DIM))
+    _need(k, "k", torch.bfloat16, (total, DIM))
+    _need(w, "w", torch.bfloat16, (total, V32_HEADS))
+    _need(cu_seqlens, "cu_seqlens", torch.int32)
+    B = cu_seqlens.numel() - 1
+    if out is None:
+        idx = torch.empty((total, topk), dtype=torch.int32, device=q.device)
+        sc = torch.empty((total, topk), dtype=torch.float32, device=q.device) if with_scores else None
+    else:
+        idx, sc = out
+    nbytes = workspace_size(OP_SCORE_TOPK_VARLEN, total, B, max_seqlen, topk)
+    ws = _workspace(nbytes, q.device, ws)
+    _check("dsa_idx_v32_score_topk_varlen",
+           lib().dsa_idx_v32_score_topk_varlen(_ptr(q), _ptr(k), _ptr(w), _ptr(cu_seqlens), B,
+                                               int(max_seqlen), total, topk, _ptr(idx), _ptr(sc),
+                                               _ptr(ws), nbytes, _stream(stream)))
     return idx, sc
 
 

@@ -378,6 +378,36 @@ int dsa_idx_v32_score_topk(const dsa_idx_bf16 *q, const dsa_idx_bf16 *k, const d
     return dsa_idx_prefill_select(nullptr, 1, 0, T, topk, idx, scores, ws, ws_bytes, stream);
 }
 
+int dsa_idx_v32_score_topk_varlen(const dsa_idx_bf16 *q, const dsa_idx_bf16 *k,
+                                  const dsa_idx_bf16 *w, const int32_t *cu_seqlens, int B,
+                                  int max_seqlen, int64_t total, int topk, int32_t *idx,
+                                  float *scores, void *ws, size_t ws_bytes, void *stream) {
+    if (B < 0 || max_seqlen < 0 || total < 0)
+        return fail(DSA_IDX_EINVAL, "B=%d max_seqlen=%d total=%lld must be >= 0", B, max_seqlen, (long long)total);
+    if (B > 0 && !cu_seqlens) return fail(DSA_IDX_EINVAL, "cu_seqlens is NULL");
+    int r = check_topk(topk);
+    if (r) return r;
+    if (total > 0 && (!q || !k || !w || !idx)) return fail(DSA_IDX_EINVAL, "a tensor pointer is NULL");
+    if (B == 0) return total == 0 ? ok() : fail(DSA_IDX_EINVAL, "total=%lld with B=0", (long long)total);
+    size_t need = 0;
+    r = prefill_check(cu_seqlens, B, max_seqlen, total, ws, ws_bytes, need);
+    if (r || prefill_empty(cu_seqlens, B, max_seqlen, total)) return r;
+    if (!aligned16(q) || !aligned16(k) || !aligned16(w))
+        return fail(DSA_IDX_EINVAL, "q, k and w must be 16-byte aligned");
+    r = check_device();
+    if (r) return r;
+    const PrefillWs p = prefill_ws(cu_seqlens, B, max_seqlen, total, ws);
+    const hipStream_t st = reinterpret_cast<hipStream_t>(stream);
+    // heads 0..31 write the score rows, heads 32..63 add to them
+    for (int half = 0; half < 2; ++half) {
+        hipError_t e = dsaidx::launch_scores_ex(q + half * DSA_IDX_QOUT, DSA_IDX_V32_QOUT, k, w + half * DSA_IDX_HEADS,
+                                                DSA_IDX_V32_HEADS, half == 1, cu_seqlens, B, max_seqlen, total, 0,
+                                                p.base, p.rows, p.dummy, st);
+        if (e != hipSuccess) return hip_fail("scores launch", e);
+    }
+    return dsa_idx_prefill_select(cu_seqlens, B, max_seqlen, total, topk, idx, scores, ws, ws_bytes, stream);
+}
+
 int dsa_idx_score_topk_varlen(const dsa_idx_bf16 *q, const dsa_idx_bf16 *k,
                               const dsa_idx_bf16 *w, const int32_t *cu_seqlens, int B,
                               int max_seqlen, int64_t total, int topk, int32_t *idx,

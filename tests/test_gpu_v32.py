@@ -109,3 +109,25 @@ def test_v32_full_size_sampled_rows(dsa):
     ref = oracle.prefill_rows(q, k, w, rows, topk=topk, full=True)
     for r, t in enumerate(rows):
         check_row(int(t), idx[r], sc[r], ref, r, topk)
+
+
+def test_v32_varlen_equals_per_sequence(dsa):
+    lens = [1, 130, 2049, 700, 2048]
+    total = sum(lens)
+    q, k, w = _inputs(total, 21)
+    cu = np.concatenate([[0], np.cumsum(lens)]).astype(np.int32)
+    print(f"v32 varlen: lens={lens}", flush=True)
+    qd, kd, wd = to_dev(q), to_dev(k), to_dev(w)
+    idx, sc = dsa.v32_score_topk_varlen(qd, kd, wd, torch.from_numpy(cu).cuda(), max(lens), topk=256)
+    torch.cuda.synchronize()
+    idx, sc = idx.cpu().numpy(), sc.cpu().numpy()
+    for b, L in enumerate(lens):
+        s0, s1 = int(cu[b]), int(cu[b + 1])
+        i1, c1 = dsa.v32_score_topk(qd[s0:s1].contiguous(), kd[s0:s1].contiguous(), wd[s0:s1].contiguous(),
+                                    topk=256)
+        assert np.array_equal(idx[s0:s1], i1.cpu().numpy()), f"sequence {b}: indices differ"
+        assert np.array_equal(sc[s0:s1].view(np.uint32), c1.cpu().numpy().view(np.uint32)), f"sequence {b}: scores differ"
+        rows = np.unique(np.array([0, L // 2, L - 1]))
+        ref = oracle.prefill_rows(q[s0:s1], k[s0:s1], w[s0:s1], rows, topk=256, full=True)
+        for r, t in enumerate(rows):
+            check_row(int(t), idx[s0 + t], sc[s0 + t], ref, r, 256)
