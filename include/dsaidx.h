@@ -288,6 +288,13 @@ int dsa_idx_v32_score_topk_varlen(const dsa_idx_bf16 *q, const dsa_idx_bf16 *k,
                                   int max_seqlen, int64_t total, int topk, int32_t *idx,
                                   float *scores, void *ws, size_t ws_bytes, void *stream);
 
+/* Chunked prefill for the 64-head indexer: as dsa_idx_prefill_chunk, with q [C][64][128] and
+ * w [C][64] (the queries' rotary positions prefix .. prefix + C - 1: project the chunk with
+ * pos0 = prefix).  Needs dsa_idx_workspace_size(DSA_IDX_OP_PREFILL_CHUNK, C, 0, prefix, topk) bytes. */
+int dsa_idx_v32_prefill_chunk(const dsa_idx_bf16 *q, const dsa_idx_bf16 *k, const dsa_idx_bf16 *w,
+                              int64_t C, int64_t prefix, int topk, int32_t *idx, float *scores,
+                              void *ws, size_t ws_bytes, void *stream);
+
 #ifdef __cplusplus
 }
 #endif

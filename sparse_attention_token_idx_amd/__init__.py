@@ -83,6 +83,8 @@ def lib():
         L.dsa_idx_v32_score_topk_varlen.restype = i32
         L.dsa_idx_v32_score_topk_varlen.argtypes = [vp, vp, vp, vp, i32, i32, i64, i32, vp, vp, vp,
                                                     sz, vp]
+        L.dsa_idx_v32_prefill_chunk.restype = i32
+        L.dsa_idx_v32_prefill_chunk.argtypes = [vp, vp, vp, i64, i64, i32, vp, vp, vp, sz, vp]
         L.dsa_idx_sparse_mla.restype = i32
         L.dsa_idx_sparse_mla.argtypes = [vp, vp, vp, vp, i64, i32, ctypes.c_float, vp, vp, vp, sz, vp]
         L.dsa_idx_decode.restype = i32
@@ -351,11 +353,13 @@ def prefill_chunk(q, k, w, prefix, topk=MAX_TOPK, with_scores=True, ws=None, out
                   stream=None):
     """C query tokens at positions prefix .. prefix + C - 1 against the whole causal prefix:
     q [C,32,128], w [C,32], k [prefix + C, 128] (the cached keys, then the chunk's own) ->
-    idx [C,topk] int32 (absolute positions), scores [C,topk] float32 (or None)."""
+    idx [C,topk] int32 (absolute positions), scores [C,topk] float32 (or None).  With
+    q [C,64,128] and w [C,64], the 64-head indexer."""
     C = q.shape[0]
-    _need(q, "q", torch.bfloat16, (C, HEADS, DIM))
+    heads = V32_HEADS if q.dim() == 3 and q.shape[1] == V32_HEADS else HEADS
+    _need(q, "q", torch.bfloat16, (C, heads, DIM))
     _need(k, "k", torch.bfloat16, (prefix + C, DIM))
-    _need(w, "w", torch.bfloat16, (C, HEADS))
+    _need(w, "w", torch.bfloat16, (C, heads))
     if out is None:
         idx = torch.empty((C, topk), dtype=torch.int32, device=q.device)
         sc = torch.empty((C, topk), dtype=torch.float32, device=q.device) if with_scores else None
@@ -363,9 +367,9 @@ def prefill_chunk(q, k, w, prefix, topk=MAX_TOPK, with_scores=True, ws=None, out
         idx, sc = out
     nbytes = workspace_size(OP_PREFILL_CHUNK, C, 0, prefix, topk)
     ws = _workspace(nbytes, q.device, ws)
-    _check("dsa_idx_prefill_chunk",
-           lib().dsa_idx_prefill_chunk(_ptr(q), _ptr(k), _ptr(w), C, int(prefix), topk, _ptr(idx),
-                                       _ptr(sc), _ptr(ws), nbytes, _stream(stream)))
+    fn = "dsa_idx_v32_prefill_chunk" if heads == V32_HEADS else "dsa_idx_prefill_chunk"
+    _check(fn, getattr(lib(), fn)(_ptr(q), _ptr(k), _ptr(w), C, int(prefix), topk, _ptr(idx),
+                                  _ptr(sc), _ptr(ws), nbytes, _stream(stream)))
     return idx, sc
 
 

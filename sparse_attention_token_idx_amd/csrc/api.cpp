@@ -428,9 +428,11 @@ int dsa_idx_score_topk_varlen(const dsa_idx_bf16 *q, const dsa_idx_bf16 *k,
                                   stream);
 }
 
-int dsa_idx_prefill_chunk(const dsa_idx_bf16 *q, const dsa_idx_bf16 *k, const dsa_idx_bf16 *w,
-                          int64_t C, int64_t prefix, int topk, int32_t *idx, float *scores,
-                          void *ws, size_t ws_bytes, void *stream) {
+// A chunk of C queries against its whole prefix, with heads/32 scoring passes of 32 heads each
+// (q rows heads x 128, w rows heads), the later ones adding to the score rows.
+static int prefill_chunk_impl(const dsa_idx_bf16 *q, const dsa_idx_bf16 *k, const dsa_idx_bf16 *w,
+                              int64_t C, int64_t prefix, int topk, int32_t *idx, float *scores,
+                              void *ws, size_t ws_bytes, void *stream, int heads) {
     if (C < 0 || prefix < 0)
         return fail(DSA_IDX_EINVAL, "C=%lld prefix=%lld must be >= 0", (long long)C, (long long)prefix);
     int r = check_topk(topk);
@@ -454,11 +456,27 @@ int dsa_idx_prefill_chunk(const dsa_idx_bf16 *q, const dsa_idx_bf16 *k, const ds
     float *dummy = reinterpret_cast<float *>(wsb + ws_hdr(1));
     float *rows = reinterpret_cast<float *>(wsb + ws_hdr(1) + ws_dummy(prefix + C));
     const hipStream_t st = reinterpret_cast<hipStream_t>(stream);
-    hipError_t e = dsaidx::launch_scores(q, k, w, nullptr, 1, C, C, prefix, base, rows, dummy, st);
-    if (e != hipSuccess) return hip_fail("scores launch", e);
+    hipError_t e = hipSuccess;
+    for (int half = 0; half < heads / DSA_IDX_HEADS; ++half) {
+        e = dsaidx::launch_scores_ex(q + half * DSA_IDX_QOUT, (int64_t)heads * DSA_IDX_DIM, k, w + half * DSA_IDX_HEADS,
+                                     heads, half > 0, nullptr, 1, C, C, prefix, base, rows, dummy, st);
+        if (e != hipSuccess) return hip_fail("scores launch", e);
+    }
     e = dsaidx::launch_row_topk_prefill(rows, nullptr, base, 1, C, prefix, C, topk, idx, scores, st);
     if (e != hipSuccess) return hip_fail("row top-k launch", e);
     return ok();
+}
+
+int dsa_idx_prefill_chunk(const dsa_idx_bf16 *q, const dsa_idx_bf16 *k, const dsa_idx_bf16 *w,
+                          int64_t C, int64_t prefix, int topk, int32_t *idx, float *scores,
+                          void *ws, size_t ws_bytes, void *stream) {
+    return prefill_chunk_impl(q, k, w, C, prefix, topk, idx, scores, ws, ws_bytes, stream, DSA_IDX_HEADS);
+}
+
+int dsa_idx_v32_prefill_chunk(const dsa_idx_bf16 *q, const dsa_idx_bf16 *k, const dsa_idx_bf16 *w,
+                              int64_t C, int64_t prefix, int topk, int32_t *idx, float *scores,
+                              void *ws, size_t ws_bytes, void *stream) {
+    return prefill_chunk_impl(q, k, w, C, prefix, topk, idx, scores, ws, ws_bytes, stream, DSA_IDX_V32_HEADS);
 }
 
 int dsa_idx_sparse_mla(const dsa_idx_bf16 *q, const dsa_idx_bf16 *kv, const int32_t *idx,

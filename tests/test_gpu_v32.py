@@ -131,3 +131,19 @@ def test_v32_varlen_equals_per_sequence(dsa):
         ref = oracle.prefill_rows(q[s0:s1], k[s0:s1], w[s0:s1], rows, topk=256, full=True)
         for r, t in enumerate(rows):
             check_row(int(t), idx[s0 + t], sc[s0 + t], ref, r, 256)
+
+
+def test_v32_chunk_equals_the_last_rows(dsa):
+    # C queries at offset prefix against the whole prefix: the last C rows of the one-sequence
+    # call, bit for bit (offsets inside and across 128-key tiles)
+    T, topk = 2600, 512
+    q, k, w = _inputs(T, 31)
+    qd, kd, wd = to_dev(q), to_dev(k), to_dev(w)
+    full_i, full_s = dsa.v32_score_topk(qd, kd, wd, topk=topk)
+    for prefix in (0, 77, 2048, 2500):
+        C = T - prefix
+        print(f"v32 chunk: prefix={prefix} C={C}", flush=True)
+        ci, cs = dsa.prefill_chunk(qd[prefix:].contiguous(), kd, wd[prefix:].contiguous(), prefix, topk=topk)
+        torch.cuda.synchronize()
+        assert torch.equal(ci, full_i[prefix:]), f"prefix {prefix}: indices differ"
+        assert torch.equal(cs.view(torch.int32), full_s[prefix:].view(torch.int32)), f"prefix {prefix}: scores differ"
