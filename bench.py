@@ -241,7 +241,28 @@ def bench_decode(dsa, args):
         f"({gbps:.0f} GB/s); one step issued from Python, host-bound: {host_ms:.3f} ms")
     log(f"decode fp8: quantise new keys {q8_ms:.3f} ms, decode {dec8_ms:.3f} ms ({gbps8:.0f} GB/s)")
     mla = None if args.no_mla else bench_mla(dsa, args, idx, start_d, sumL, n)
-    return dict(mla=mla, batch=B, sum_keys=sumL, project_ms=proj_ms, decode_ms=dec_ms, host_step_ms=host_ms,
+
+    # the 64-head indexer's decode against the same cache (its queries and weights from the
+    # 64-head projection of the same activations)
+    W64t = wl.layer_weights_v32(layer=0, seed=1)
+    W64 = {k: dev_bf16(v) for k, v in W64t.items() if k != "eps"}
+    W64["eps"] = W64t["eps"]
+    q64, _, w64 = dsa.v32_project(x, cq, W64)
+    for _ in range(max(args.warmup, 1)):
+        dsa.decode(q64, w64, cache_d, start_d, lens_d, maxL, topk=topk, ws=ws, out=(idx, sc))
+    torch.cuda.synchronize()
+    ev64 = [torch.cuda.Event(enable_timing=True) for _ in range(n + 1)]
+    torch.cuda._sleep(100_000_000)
+    ev64[0].record(stream)
+    for i in range(n):
+        dsa.decode(q64, w64, cache_d, start_d, lens_d, maxL, topk=topk, ws=ws, out=(idx, sc))
+        ev64[i + 1].record(stream)
+    torch.cuda.synchronize()
+    dec64_ms = float(np.mean([ev64[i].elapsed_time(ev64[i + 1]) for i in range(n)]))
+    dec64_bytes = 256 * sumL + B * (64 * D * 2 + 64 * 2) + B * topk * 8
+    log(f"decode, 64 heads: {dec64_ms:.3f} ms ({dec64_bytes / (dec64_ms * 1e-3) / 1e9:.0f} GB/s)")
+    return dict(mla=mla, v32=dict(decode_ms=dec64_ms, bytes=dec64_bytes,
+                                  GBps=dec64_bytes / (dec64_ms * 1e-3) / 1e9), batch=B, sum_keys=sumL, project_ms=proj_ms, decode_ms=dec_ms, host_step_ms=host_ms,
                 fp8=dict(quantize_ms=q8_ms, decode_ms=dec8_ms, bytes=dec8_bytes, GBps=gbps8),
                 decode_bytes=dec_bytes, decode_GBps=gbps, decode_hbm_frac=gbps / PEAK_HBM_GBPS,
                 step_GBps=(dec_bytes + proj_bytes) / ((dec_ms + proj_ms) * 1e-3) / 1e9)
@@ -484,6 +505,10 @@ def main():
                           "GBps": round(dec["fp8"]["GBps"], 1),
                           "hbm_frac": round(dec["fp8"]["GBps"] / PEAK_HBM_GBPS, 4),
                           "algorithmic_bytes": dec["fp8"]["bytes"]},
+            "v32_64_heads": {"decode_ms": round(dec["v32"]["decode_ms"], 4),
+                             "GBps": round(dec["v32"]["GBps"], 1),
+                             "hbm_frac": round(dec["v32"]["GBps"] / PEAK_HBM_GBPS, 4),
+                             "algorithmic_bytes": dec["v32"]["bytes"]},
             "sparse_mla": None if dec["mla"] is None else {
                 "workload": f"the decode's consumer: {dec['batch']} queries x {MLA_HEADS} heads over "
                             f"the {args.topk} latent-cache rows (576 values) each selection names",

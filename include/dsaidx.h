@@ -295,6 +295,15 @@ int dsa_idx_v32_prefill_chunk(const dsa_idx_bf16 *q, const dsa_idx_bf16 *k, cons
                               int64_t C, int64_t prefix, int topk, int32_t *idx, float *scores,
                               void *ws, size_t ws_bytes, void *stream);
 
+/* Decode for the 64-head indexer: as dsa_idx_decode, with q [B][64][128] and w [B][64] (the
+ * new tokens' projections at their positions seqlens[b] - 1, from dsa_idx_v32_project, and
+ * their rotated keys in the cache).  Needs dsa_idx_workspace_size(DSA_IDX_OP_DECODE, 0, B,
+ * max_seqlen, topk) bytes. */
+int dsa_idx_v32_decode(const dsa_idx_bf16 *q, const dsa_idx_bf16 *w, const dsa_idx_bf16 *k_cache,
+                       const int64_t *start, const int32_t *seqlens, int B, int max_seqlen,
+                       int topk, int32_t *idx, float *scores, void *ws, size_t ws_bytes,
+                       void *stream);
+
 #ifdef __cplusplus
 }
 #endif

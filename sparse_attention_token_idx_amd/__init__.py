@@ -85,6 +85,8 @@ def lib():
                                                     sz, vp]
         L.dsa_idx_v32_prefill_chunk.restype = i32
         L.dsa_idx_v32_prefill_chunk.argtypes = [vp, vp, vp, i64, i64, i32, vp, vp, vp, sz, vp]
+        L.dsa_idx_v32_decode.restype = i32
+        L.dsa_idx_v32_decode.argtypes = [vp, vp, vp, vp, vp, i32, i32, i32, vp, vp, vp, sz, vp]
         L.dsa_idx_sparse_mla.restype = i32
         L.dsa_idx_sparse_mla.argtypes = [vp, vp, vp, vp, i64, i32, ctypes.c_float, vp, vp, vp, sz, vp]
         L.dsa_idx_decode.restype = i32
@@ -405,10 +407,12 @@ def sparse_mla(q, kv, idx, row0=None, scale=192.0 ** -0.5, with_lse=True, ws=Non
 def decode(q, w, k_cache, start, seqlens, max_seqlen, topk=MAX_TOPK, with_scores=True, ws=None,
            out=None, stream=None):
     """One query per sequence against its cached keys: q [B,32,128], w [B,32],
-    k_cache [*,128], start int64 [B], seqlens int32 [B] (own key included)."""
+    k_cache [*,128], start int64 [B], seqlens int32 [B] (own key included).  With q [B,64,128]
+    and w [B,64], the 64-head indexer."""
     B = q.shape[0]
-    _need(q, "q", torch.bfloat16, (B, HEADS, DIM))
-    _need(w, "w", torch.bfloat16, (B, HEADS))
+    heads = V32_HEADS if q.dim() == 3 and q.shape[1] == V32_HEADS else HEADS
+    _need(q, "q", torch.bfloat16, (B, heads, DIM))
+    _need(w, "w", torch.bfloat16, (B, heads))
     _need(k_cache, "k_cache", torch.bfloat16)
     _need(start, "start", torch.int64, (B,))
     _need(seqlens, "seqlens", torch.int32, (B,))
@@ -419,10 +423,10 @@ def decode(q, w, k_cache, start, seqlens, max_seqlen, topk=MAX_TOPK, with_scores
         idx, sc = out
     nbytes = workspace_size(OP_DECODE, 0, B, max_seqlen, topk)
     ws = _workspace(nbytes, q.device, ws)
-    _check("dsa_idx_decode",
-           lib().dsa_idx_decode(_ptr(q), _ptr(w), _ptr(k_cache), _ptr(start), _ptr(seqlens), B,
-                                int(max_seqlen), topk, _ptr(idx), _ptr(sc), _ptr(ws), nbytes,
-                                _stream(stream)))
+    fn = "dsa_idx_v32_decode" if heads == V32_HEADS else "dsa_idx_decode"
+    _check(fn, getattr(lib(), fn)(_ptr(q), _ptr(w), _ptr(k_cache), _ptr(start), _ptr(seqlens), B,
+                                  int(max_seqlen), topk, _ptr(idx), _ptr(sc), _ptr(ws), nbytes,
+                                  _stream(stream)))
     return idx, sc
 
 

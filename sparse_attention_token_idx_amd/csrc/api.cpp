@@ -502,10 +502,11 @@ int dsa_idx_sparse_mla(const dsa_idx_bf16 *q, const dsa_idx_bf16 *kv, const int3
     return ok();
 }
 
-int dsa_idx_decode(const dsa_idx_bf16 *q, const dsa_idx_bf16 *w, const dsa_idx_bf16 *k_cache,
-                   const int64_t *start, const int32_t *seqlens, int B, int max_seqlen,
-                   int topk, int32_t *idx, float *scores, void *ws, size_t ws_bytes,
-                   void *stream) {
+// heads: 32, or 64 for the 64-head indexer
+static int decode_impl(const dsa_idx_bf16 *q, const dsa_idx_bf16 *w, const dsa_idx_bf16 *k_cache,
+                       const int64_t *start, const int32_t *seqlens, int B, int max_seqlen,
+                       int topk, int32_t *idx, float *scores, void *ws, size_t ws_bytes,
+                       void *stream, int heads) {
     if (B < 0 || max_seqlen < 0) return fail(DSA_IDX_EINVAL, "B=%d max_seqlen=%d must be >= 0", B, max_seqlen);
     int r = check_topk(topk);
     if (r) return r;
@@ -521,10 +522,29 @@ int dsa_idx_decode(const dsa_idx_bf16 *q, const dsa_idx_bf16 *w, const dsa_idx_b
     if (!aligned16(ws)) return fail(DSA_IDX_EINVAL, "workspace must be 16-byte aligned");
     r = check_device();
     if (r) return r;
-    hipError_t e = dsaidx::launch_decode(q, w, k_cache, start, seqlens, B, max_seqlen, topk, ws, idx,
-                                         scores, reinterpret_cast<hipStream_t>(stream));
+    hipError_t e = heads == DSA_IDX_V32_HEADS
+                       ? dsaidx::launch_decode_v32(q, w, k_cache, start, seqlens, B, max_seqlen, topk, ws, idx,
+                                                   scores, reinterpret_cast<hipStream_t>(stream))
+                       : dsaidx::launch_decode(q, w, k_cache, start, seqlens, B, max_seqlen, topk, ws, idx,
+                                               scores, reinterpret_cast<hipStream_t>(stream));
     if (e != hipSuccess) return hip_fail("decode launch", e);
     return ok();
+}
+
+int dsa_idx_decode(const dsa_idx_bf16 *q, const dsa_idx_bf16 *w, const dsa_idx_bf16 *k_cache,
+                   const int64_t *start, const int32_t *seqlens, int B, int max_seqlen,
+                   int topk, int32_t *idx, float *scores, void *ws, size_t ws_bytes,
+                   void *stream) {
+    return decode_impl(q, w, k_cache, start, seqlens, B, max_seqlen, topk, idx, scores, ws, ws_bytes, stream,
+                       DSA_IDX_HEADS);
+}
+
+int dsa_idx_v32_decode(const dsa_idx_bf16 *q, const dsa_idx_bf16 *w, const dsa_idx_bf16 *k_cache,
+                       const int64_t *start, const int32_t *seqlens, int B, int max_seqlen,
+                       int topk, int32_t *idx, float *scores, void *ws, size_t ws_bytes,
+                       void *stream) {
+    return decode_impl(q, w, k_cache, start, seqlens, B, max_seqlen, topk, idx, scores, ws, ws_bytes, stream,
+                       DSA_IDX_V32_HEADS);
 }
 
 int dsa_idx_quantize_keys(const dsa_idx_bf16 *k, int64_t ldk, int64_t N, const int64_t *slot,

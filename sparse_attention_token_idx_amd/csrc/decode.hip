@@ -112,21 +112,24 @@ struct Bf16Keys {
     const uint16_t *q, *w, *k_cache;
 };
 
-struct Bf16Scorer {
-    u32x4 qa[2][4];   // A operand: head 16 hh + l16, k-slot chunk 4 ks + lg (8 dims)
-    float wv[2][4];
+// HB blocks of 16 heads: 2 for the 32-head indexer, 4 for the 64-head one.
+template <int HB>
+struct Bf16ScorerT {
+    static constexpr int kH = 16 * HB;                 // heads
+    u32x4 qa[HB][4];   // A operand: head 16 hh + l16, k-slot chunk 4 ks + lg (8 dims)
+    float wv[HB][4];
     const uint16_t *kc;
     u32x4 kb[4][4];
 
     __device__ __forceinline__ void init(const Bf16Keys &p, const int64_t *start, int b, int l16, int lg) {
-        const uint16_t *qb = p.q + (int64_t)b * kQOut;
+        const uint16_t *qb = p.q + (int64_t)b * kH * kDim;
 #pragma unroll
-        for (int hh = 0; hh < 2; ++hh) {
+        for (int hh = 0; hh < HB; ++hh) {
 #pragma unroll
             for (int ks = 0; ks < 4; ++ks)
                 qa[hh][ks] = *reinterpret_cast<const u32x4 *>(qb + (16 * hh + l16) * kDim + 8 * (4 * ks + lg));
 #pragma unroll
-            for (int r = 0; r < 4; ++r) wv[hh][r] = bf16_to_f32(p.w[(int64_t)b * kHeads + 16 * hh + 4 * lg + r]);
+            for (int r = 0; r < 4; ++r) wv[hh][r] = bf16_to_f32(p.w[(int64_t)b * kH + 16 * hh + 4 * lg + r]);
         }
         kc = p.k_cache + start[b] * kDim;
     }
@@ -141,17 +144,18 @@ struct Bf16Scorer {
     __device__ __forceinline__ void partial(float (&p)[4]) const {
 #pragma unroll
         for (int u = 0; u < 4; ++u) {
-            f32x4 s_lo = {0.f, 0.f, 0.f, 0.f}, s_hi = {0.f, 0.f, 0.f, 0.f};
+            f32x4 s[HB];
 #pragma unroll
-            for (int ks = 0; ks < 4; ++ks) {
-                s_lo = mfma16x16x32(qa[0][ks], kb[u][ks], s_lo);
-                s_hi = mfma16x16x32(qa[1][ks], kb[u][ks], s_hi);
-            }
+            for (int hh = 0; hh < HB; ++hh) s[hh] = f32x4{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+            for (int ks = 0; ks < 4; ++ks)
+#pragma unroll
+                for (int hh = 0; hh < HB; ++hh) s[hh] = mfma16x16x32(qa[hh][ks], kb[u][ks], s[hh]);
             float v = 0.f;
 #pragma unroll
-            for (int r = 0; r < 4; ++r) v = fmaf(wv[0][r], relu(s_lo[r]), v);
+            for (int hh = 0; hh < HB; ++hh)
 #pragma unroll
-            for (int r = 0; r < 4; ++r) v = fmaf(wv[1][r], relu(s_hi[r]), v);
+                for (int r = 0; r < 4; ++r) v = fmaf(wv[hh][r], relu(s[hh][r]), v);
             p[u] = v;
         }
     }
@@ -161,16 +165,16 @@ struct Bf16Scorer {
     // The plain (non-MFMA) score of key s, for the select's re-scoring of a row: the query
     // (bf16 pairs) and weights of the row are in LDS.
     static __device__ void stage(const Bf16Keys &p, int b, uint32_t *q_lds, float *w_lds) {
-        const uint32_t *src = reinterpret_cast<const uint32_t *>(p.q + (int64_t)b * kQOut);
-        for (int i = (int)threadIdx.x; i < kQOut / 2; i += (int)blockDim.x) q_lds[i] = src[i];
-        if ((int)threadIdx.x < kHeads) w_lds[threadIdx.x] = bf16_to_f32(p.w[(int64_t)b * kHeads + threadIdx.x]);
+        const uint32_t *src = reinterpret_cast<const uint32_t *>(p.q + (int64_t)b * kH * kDim);
+        for (int i = (int)threadIdx.x; i < kH * kDim / 2; i += (int)blockDim.x) q_lds[i] = src[i];
+        if ((int)threadIdx.x < kH) w_lds[threadIdx.x] = bf16_to_f32(p.w[(int64_t)b * kH + threadIdx.x]);
     }
     static __device__ float rescore(const Bf16Keys &p, const int64_t *start, int b, int s,
                                     const uint32_t *q_lds, const float *w_lds) {
         const uint16_t *kr = p.k_cache + (start[b] + s) * kDim;
         float sc = 0.f;
 #pragma unroll 1
-        for (int h = 0; h < kHeads; ++h) {
+        for (int h = 0; h < kH; ++h) {
             float dot = 0.f;
 #pragma unroll 1
             for (int c = 0; c < kDim / 8; ++c) {
@@ -187,6 +191,8 @@ struct Bf16Scorer {
         return sc;
     }
 };
+using Bf16Scorer = Bf16ScorerT<2>;
+static_assert(Bf16Scorer::kH == kHeads, "the 32-head scorer");
 
 struct Fp8Keys {
     const uint8_t *q8;     // [B][32][128] E4M3 codes of the new queries
@@ -908,6 +914,16 @@ hipError_t launch_decode(const uint16_t *q, const uint16_t *w, const uint16_t *k
     decode_workspace(B, max_seqlen, false, &dw, ws);
     return run_decode<Bf16Scorer>(Bf16Keys{q, w, k_cache}, start, seqlens, B, max_seqlen, topk, dw, idx,
                                   scores, stream);
+}
+
+hipError_t launch_decode_v32(const uint16_t *q, const uint16_t *w, const uint16_t *k_cache,
+                             const int64_t *start, const int32_t *seqlens, int B, int max_seqlen,
+                             int topk, void *ws, int32_t *idx, float *scores, hipStream_t stream) {
+    if (B == 0) return hipSuccess;
+    DecodeWs dw{};
+    decode_workspace(B, max_seqlen, false, &dw, ws);
+    return run_decode<Bf16ScorerT<4>>(Bf16Keys{q, w, k_cache}, start, seqlens, B, max_seqlen, topk, dw, idx,
+                                      scores, stream);
 }
 
 hipError_t launch_decode_fp8(const uint16_t *q, const uint16_t *w, const uint8_t *k8, const float *kscale,

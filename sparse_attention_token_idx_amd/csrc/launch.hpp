@@ -83,6 +83,10 @@ struct DecodeWs {
 };
 // Bytes of the decode workspace (16-byte aligned base); with w and base, also its parts.
 size_t decode_workspace(int B, int max_seqlen, bool fp8, DecodeWs *w = nullptr, void *base = nullptr);
+// The 64-head indexer's decode: q [B][64][128], w [B][64]; the workspace as for launch_decode.
+hipError_t launch_decode_v32(const uint16_t *q, const uint16_t *w, const uint16_t *k_cache,
+                             const int64_t *start, const int32_t *seqlens, int B, int max_seqlen,
+                             int topk, void *ws, int32_t *idx, float *scores, hipStream_t stream);
 hipError_t launch_decode(const uint16_t *q, const uint16_t *w, const uint16_t *k_cache,
                          const int64_t *start, const int32_t *seqlens, int B, int max_seqlen,
                          int topk, void *ws, int32_t *idx, float *scores, hipStream_t stream);

@@ -83,8 +83,8 @@ template <int W> struct TopkSmem {
         } pc;
         int32_t ecnt[kPer * W];    // decode select: winners per (entry row, wave), then prefixes
         struct {                   // decode select fallback: the row's query and head weights
-            uint32_t q[kHeads * kDim / 2];
-            float w[kHeads];
+            uint32_t q[2 * kHeads * kDim / 2];   // room for the 64-head indexer
+            float w[2 * kHeads];
         } resc;
     } u;
     union {

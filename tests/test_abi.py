@@ -32,7 +32,8 @@ def test_exports_every_declared_symbol(dsa):
                           "dsa_idx_prefill_scores", "dsa_idx_prefill_select", "dsa_idx_decode",
                           "dsa_idx_quantize_keys", "dsa_idx_decode_fp8", "dsa_idx_prefill_chunk",
                           "dsa_idx_sparse_mla", "dsa_idx_v32_project", "dsa_idx_v32_score_topk",
-                          "dsa_idx_v32_score_topk_varlen", "dsa_idx_v32_prefill_chunk"}
+                          "dsa_idx_v32_score_topk_varlen", "dsa_idx_v32_prefill_chunk",
+                          "dsa_idx_v32_decode"}
     for n in names:
         assert getattr(L, n) is not None
 
@@ -179,6 +180,12 @@ def test_rejections_before_device(dsa):
     assert vv(_vp(A), _vp(A), _vp(A), _vp(A), 2, 100, 150, 0, _vp(A), None, _vp(A), 1 << 30, None) == -2
     assert vv(_vp(A), _vp(A), _vp(A), _vp(A), 2, 100, 150, 8, _vp(A), None, _vp(A), 16, None) == -3
     assert vv(None, None, None, None, 0, 0, 0, 8, None, None, None, 0, None) == 0
+    vd = lambda *a: L.dsa_idx_v32_decode(*a)
+    assert vd(_vp(A), _vp(A), _vp(A), _vp(A), _vp(A), 4, 100, 0, _vp(A), None, _vp(A), 1 << 30, None) == -2
+    assert vd(_vp(A), _vp(A), _vp(A), _vp(A), _vp(A), -1, 100, 8, _vp(A), None, _vp(A), 1 << 30, None) == -1
+    assert vd(_vp(A), None, _vp(A), _vp(A), _vp(A), 4, 100, 8, _vp(A), None, _vp(A), 1 << 30, None) == -1
+    assert vd(_vp(A), _vp(A), _vp(A), _vp(A), _vp(A), 4, 100, 8, _vp(A), None, _vp(A), 16, None) == -3
+    assert vd(None, None, None, None, None, 0, 0, 8, None, None, None, 0, None) == 0
     vc = lambda *a: L.dsa_idx_v32_prefill_chunk(*a)
     assert vc(_vp(A), _vp(A), _vp(A), 10, 100, 0, _vp(A), None, _vp(A), 1 << 30, None) == -2
     assert vc(_vp(A), _vp(A), _vp(A), 10, -1, 8, _vp(A), None, _vp(A), 1 << 30, None) == -1

@@ -147,3 +147,34 @@ def test_v32_chunk_equals_the_last_rows(dsa):
         torch.cuda.synchronize()
         assert torch.equal(ci, full_i[prefix:]), f"prefix {prefix}: indices differ"
         assert torch.equal(cs.view(torch.int32), full_s[prefix:].view(torch.int32)), f"prefix {prefix}: scores differ"
+
+
+@pytest.mark.parametrize("topk", [2048, 100])
+def test_v32_decode(dsa, topk):
+    # one new query per sequence against its cached keys, the new token's key written by the
+    # 64-head projection at its own position; stage-wise against the oracle on the GPU's own
+    # projections and cache, and equal to the last row of the one-sequence call
+    lens = [1, 100, 2048, 2049, 5000, 40000]
+    B = len(lens)
+    Wt = wl.layer_weights_v32(seed=41)
+    act = wl.layer_activations(B, seed=41)
+    cache, start = wl.decode_cache(np.asarray(lens), seed=41)
+    cache_d = to_dev(cache)
+    Wd = weights_to_dev(Wt)
+    print(f"v32 decode: lens={lens} topk={topk}", flush=True)
+    qs, ws_ = [], []
+    for b, L in enumerate(lens):   # each token at its own position L - 1
+        q1, k1, w1 = dsa.v32_project(to_dev(act["x"][b:b + 1]), to_dev(act["c_q"][b:b + 1]), Wd, pos0=L - 1)
+        cache_d[start[b] + L - 1] = k1[0]
+        qs.append(q1)
+        ws_.append(w1)
+    q = torch.cat(qs)
+    w = torch.cat(ws_)
+    idx, sc = dsa.decode(q, w, cache_d, torch.from_numpy(start).cuda(),
+                         torch.from_numpy(np.asarray(lens, np.int32)).cuda(), max(lens), topk=topk)
+    torch.cuda.synchronize()
+    qh, wh, ch = to_host(q).reshape(B, V32_H, D), to_host(w), to_host(cache_d)
+    ref = oracle.rows(qh, wh, ch, start, np.asarray(lens) - 1, topk=topk, full=True)
+    idx, sc = idx.cpu().numpy(), sc.cpu().numpy()
+    for b, L in enumerate(lens):
+        check_row(L - 1, idx[b], sc[b], ref, b, topk)
