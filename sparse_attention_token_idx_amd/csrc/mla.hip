@@ -20,8 +20,9 @@
 // rows with the transposing LDS read of gfx950 (ds_read_b64_tr_b16: each 16-lane group loads 4
 // tokens x 16 dims and every lane receives one dim of the 4 tokens), and P^T straight from the
 // logit accumulators (the 32 tokens of a tile taken in the order the accumulators hold them).
-// The softmax is online, in the log2 domain; with several splits per query, a second kernel
-// merges the splits' (max, sum, unnormalised output).
+// The softmax is online, in the log2 domain; with several splits per query, each split writes
+// its (max, sum) and its output normalised by its own sum, in bf16 (a convex combination of
+// latents, so in their range), and a second kernel merges them.
 #include "common.hpp"
 #include "launch.hpp"
 
@@ -78,7 +79,7 @@ struct MlaArgs {
     float scale_log2;        // scale * log2(e)
     uint16_t *o;             // [T][96][512] (nsplit == 1)
     float *lse;              // [T][96] or nullptr (nsplit == 1)
-    float *part_o;           // [nsplit][T][96][512] unnormalised (nsplit > 1)
+    uint16_t *part_o;        // [nsplit][T][96][512] bf16, normalised by the split's sum (nsplit > 1)
     float *part_ml;          // [nsplit][T][96][2]: running max (log2 domain), sum
 };
 
@@ -339,9 +340,14 @@ __global__ __launch_bounds__(kMlaThreads, 1) void sparse_mla_kernel(MlaArgs a) {
             a.lse[t * kMlaHeads + head] = l_tot > 0.f ? (m_run + log2f(l_tot)) * 0.69314718055994531f : -INFINITY;
     } else {
         const int64_t ph = ((int64_t)split * a.T + t) * kMlaHeads + head;
-        float *oh = a.part_o + ph * kV + 16 * half + 4 * g;
+        const float inv = l_tot > 0.f ? 1.f / l_tot : 0.f;
+        uint16_t *oh = a.part_o + ph * kV + 16 * half + 4 * g;
 #pragma unroll
-        for (int mt = 0; mt < kMt; ++mt) *reinterpret_cast<f32x4 *>(oh + 32 * mt) = acc_o[mt];
+        for (int mt = 0; mt < kMt; ++mt) {
+            const f32x4 o = acc_o[mt];
+            const uint2 v = {bf16_pair(o[0] * inv, o[1] * inv), bf16_pair(o[2] * inv, o[3] * inv)};
+            *reinterpret_cast<uint2 *>(oh + 32 * mt) = v;
+        }
         if (g == 0 && half == 0) {
             a.part_ml[2 * ph] = m_run;
             a.part_ml[2 * ph + 1] = l_tot;
@@ -366,12 +372,13 @@ __global__ __launch_bounds__(256) void sparse_mla_merge_kernel(MlaArgs a) {
             if (ms == -INFINITY) continue;
             const float f = exp2f(ms - M);
             L += f * a.part_ml[2 * ph + 1];
-            const f32x4 x0 = *reinterpret_cast<const f32x4 *>(a.part_o + ph * kV + 8 * lane);
-            const f32x4 x1 = *reinterpret_cast<const f32x4 *>(a.part_o + ph * kV + 8 * lane + 4);
+            // the split's normalised output weighs by its share of the sum, f * l_s
+            const float fl = f * a.part_ml[2 * ph + 1];
+            const u32x4 x = *reinterpret_cast<const u32x4 *>(a.part_o + ph * kV + 8 * lane);
 #pragma unroll
             for (int r = 0; r < 4; ++r) {
-                acc[r] = fmaf(f, x0[r], acc[r]);
-                acc[4 + r] = fmaf(f, x1[r], acc[4 + r]);
+                acc[2 * r] = fmaf(fl, bf16_to_f32(x[r] & 0xFFFFu), acc[2 * r]);
+                acc[2 * r + 1] = fmaf(fl, bf16_to_f32(x[r] >> 16), acc[2 * r + 1]);
             }
         }
     }
@@ -408,7 +415,7 @@ int sparse_mla_splits(int64_t T, int topk) {
 size_t sparse_mla_workspace(int64_t T, int topk) {
     const int ns = sparse_mla_splits(T, topk);
     if (ns <= 1) return 0;
-    return (size_t)ns * (size_t)T * kMlaHeads * (kV + 2) * 4u;
+    return (size_t)ns * (size_t)T * kMlaHeads * (kV * 2u + 2 * 4u);
 }
 
 hipError_t launch_sparse_mla(const uint16_t *q, const uint16_t *kv, const int32_t *idx, const int64_t *row0,
@@ -435,8 +442,9 @@ hipError_t launch_sparse_mla(const uint16_t *q, const uint16_t *kv, const int32_
     a.scale_log2 = scale * 1.4426950408889634f;
     a.o = o;
     a.lse = lse;
-    a.part_o = ws;
-    a.part_ml = ws ? ws + (size_t)a.nsplit * (size_t)T * kMlaHeads * kV : nullptr;
+    a.part_o = reinterpret_cast<uint16_t *>(ws);
+    a.part_ml = ws ? reinterpret_cast<float *>(reinterpret_cast<char *>(ws) + (size_t)a.nsplit * (size_t)T * kMlaHeads * kV * 2u)
+                   : nullptr;
     hipLaunchKernelGGL(sparse_mla_kernel, dim3(a.nsplit, (unsigned)T), dim3(kMlaThreads), smem, stream, a);
     hipError_t e = hipGetLastError();
     if (e != hipSuccess || a.nsplit == 1) return e;

@@ -83,7 +83,7 @@ def test_workspace_sizes(dsa):
     # when a query's selections are split over several workgroups (few queries)
     assert dsa.workspace_size(dsa.OP_SPARSE_MLA, 5000, 0, 0, 2048) == 0
     n64 = dsa.workspace_size(dsa.OP_SPARSE_MLA, 64, 0, 0, 2048)
-    assert n64 > 0 and n64 % (64 * 96 * 514 * 4) == 0
+    assert n64 > 0 and n64 % (64 * 96 * (512 * 2 + 8)) == 0
     with pytest.raises(dsa.DsaIdxError) as e:
         dsa.workspace_size(dsa.OP_SCORE_TOPK, 10, topk=0)
     assert e.value.code == -2
