@@ -133,16 +133,7 @@ __global__ __launch_bounds__(kMlaThreads, 1) void sparse_mla_kernel(MlaArgs a) {
 
     // this wave's q~ as the B operand of S^T = K q~^T: lane (l16, g) holds head 16 hg + l16,
     // dims 32 (2 ks + half) + 8 g .. + 7
-    u32x4 qb[kKs];
-    {
-        const uint16_t *qh = a.q + (t * kMlaHeads + 16 * hg + l16) * (int64_t)kKv + 32 * half + 8 * g;
-#pragma unroll
-        for (int ks = 0; ks < kKs; ++ks) qb[ks] = *reinterpret_cast<const u32x4 *>(qh + 64 * ks);
-        // use them here, so that the compiler waits for these loads before the tile loop rather
-        // than inside it, where its count of loads in flight would not include the tiles'
-#pragma unroll
-        for (int ks = 0; ks < kKs; ++ks) asm volatile("" ::"v"(qb[ks]));
-    }
+    u32x4 qb[kKs];   // loaded after the first tiles' loads are issued (below)
     __syncthreads();   // sel
 
     // A tile goes to LDS with direct global->LDS loads: lane i of instruction j of a wave fills
@@ -292,6 +283,16 @@ __global__ __launch_bounds__(kMlaThreads, 1) void sparse_mla_kernel(MlaArgs a) {
     // begins, the loads of tile t + 1 are still in flight only for t <= 1.
     if (ntile > 0) load_tile(0, 0);
     if (ntile > 1) load_tile(1, kTileBytes);
+    {   // the queries, their latency under that of the first tiles' loads
+        const uint16_t *qh = a.q + (t * kMlaHeads + 16 * hg + l16) * (int64_t)kKv + 32 * half + 8 * g;
+#pragma unroll
+        for (int ks = 0; ks < kKs; ++ks) qb[ks] = *reinterpret_cast<const u32x4 *>(qh + 64 * ks);
+        // use them here, so that the compiler waits for these loads before the tile loop rather
+        // than inside it, where its count of loads in flight would not include the tiles' (the
+        // wait drains the tiles' loads issued before them too: the first tile needs them anyway)
+#pragma unroll
+        for (int ks = 0; ks < kKs; ++ks) asm volatile("" ::"v"(qb[ks]));
+    }
     // byte offsets of the current and previous tiles' buffers, kept in scalar registers
     // (computing them from the tile index costs vector instructions on every operand address)
     int cur_off = 0, prev_off = 0;
