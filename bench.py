@@ -261,8 +261,22 @@ def bench_decode(dsa, args):
     dec64_ms = float(np.mean([ev64[i].elapsed_time(ev64[i + 1]) for i in range(n)]))
     dec64_bytes = 256 * sumL + B * (64 * D * 2 + 64 * 2) + B * topk * 8
     log(f"decode, 64 heads: {dec64_ms:.3f} ms ({dec64_bytes / (dec64_ms * 1e-3) / 1e9:.0f} GB/s)")
+    for _ in range(max(args.warmup, 1)):
+        dsa.decode_fp8(q64, w64, k8, k8s, start_d, lens_d, maxL, topk=topk, ws=ws8, out=(idx, sc))
+    torch.cuda.synchronize()
+    torch.cuda._sleep(100_000_000)
+    ev64[0].record(stream)
+    for i in range(n):
+        dsa.decode_fp8(q64, w64, k8, k8s, start_d, lens_d, maxL, topk=topk, ws=ws8, out=(idx, sc))
+        ev64[i + 1].record(stream)
+    torch.cuda.synchronize()
+    dec64f_ms = float(np.mean([ev64[i].elapsed_time(ev64[i + 1]) for i in range(n)]))
+    dec64f_bytes = 132 * sumL + B * (64 * D * 2 + 64 * 2) + B * topk * 8
+    log(f"decode fp8, 64 heads: {dec64f_ms:.3f} ms ({dec64f_bytes / (dec64f_ms * 1e-3) / 1e9:.0f} GB/s)")
     return dict(mla=mla, v32=dict(decode_ms=dec64_ms, bytes=dec64_bytes,
-                                  GBps=dec64_bytes / (dec64_ms * 1e-3) / 1e9), batch=B, sum_keys=sumL, project_ms=proj_ms, decode_ms=dec_ms, host_step_ms=host_ms,
+                                  GBps=dec64_bytes / (dec64_ms * 1e-3) / 1e9,
+                                  fp8_decode_ms=dec64f_ms, fp8_bytes=dec64f_bytes,
+                                  fp8_GBps=dec64f_bytes / (dec64f_ms * 1e-3) / 1e9), batch=B, sum_keys=sumL, project_ms=proj_ms, decode_ms=dec_ms, host_step_ms=host_ms,
                 fp8=dict(quantize_ms=q8_ms, decode_ms=dec8_ms, bytes=dec8_bytes, GBps=gbps8),
                 decode_bytes=dec_bytes, decode_GBps=gbps, decode_hbm_frac=gbps / PEAK_HBM_GBPS,
                 step_GBps=(dec_bytes + proj_bytes) / ((dec_ms + proj_ms) * 1e-3) / 1e9)
@@ -508,7 +522,11 @@ def main():
             "v32_64_heads": {"decode_ms": round(dec["v32"]["decode_ms"], 4),
                              "GBps": round(dec["v32"]["GBps"], 1),
                              "hbm_frac": round(dec["v32"]["GBps"] / PEAK_HBM_GBPS, 4),
-                             "algorithmic_bytes": dec["v32"]["bytes"]},
+                             "algorithmic_bytes": dec["v32"]["bytes"],
+                             "fp8_cache": {"decode_ms": round(dec["v32"]["fp8_decode_ms"], 4),
+                                           "GBps": round(dec["v32"]["fp8_GBps"], 1),
+                                           "hbm_frac": round(dec["v32"]["fp8_GBps"] / PEAK_HBM_GBPS, 4),
+                                           "algorithmic_bytes": dec["v32"]["fp8_bytes"]}},
             "sparse_mla": None if dec["mla"] is None else {
                 "workload": f"the decode's consumer: {dec['batch']} queries x {MLA_HEADS} heads over "
                             f"the {args.topk} latent-cache rows (576 values) each selection names",

@@ -304,6 +304,14 @@ int dsa_idx_v32_decode(const dsa_idx_bf16 *q, const dsa_idx_bf16 *w, const dsa_i
                        int topk, int32_t *idx, float *scores, void *ws, size_t ws_bytes,
                        void *stream);
 
+/* Decode for the 64-head indexer against the FP8 key cache: as dsa_idx_decode_fp8, with
+ * q [B][64][128] and w [B][64] (each head quantised with its own power-of-two scale).  Needs
+ * dsa_idx_workspace_size(DSA_IDX_OP_DECODE_FP8, 0, B, max_seqlen, topk) bytes. */
+int dsa_idx_v32_decode_fp8(const dsa_idx_bf16 *q, const dsa_idx_bf16 *w, const uint8_t *k8,
+                           const float *k_scale, const int64_t *start, const int32_t *seqlens, int B,
+                           int max_seqlen, int topk, int32_t *idx, float *scores, void *ws,
+                           size_t ws_bytes, void *stream);
+
 #ifdef __cplusplus
 }
 #endif

@@ -87,6 +87,8 @@ def lib():
         L.dsa_idx_v32_prefill_chunk.argtypes = [vp, vp, vp, i64, i64, i32, vp, vp, vp, sz, vp]
         L.dsa_idx_v32_decode.restype = i32
         L.dsa_idx_v32_decode.argtypes = [vp, vp, vp, vp, vp, i32, i32, i32, vp, vp, vp, sz, vp]
+        L.dsa_idx_v32_decode_fp8.restype = i32
+        L.dsa_idx_v32_decode_fp8.argtypes = [vp, vp, vp, vp, vp, vp, i32, i32, i32, vp, vp, vp, sz, vp]
         L.dsa_idx_sparse_mla.restype = i32
         L.dsa_idx_sparse_mla.argtypes = [vp, vp, vp, vp, i64, i32, ctypes.c_float, vp, vp, vp, sz, vp]
         L.dsa_idx_decode.restype = i32
@@ -456,10 +458,12 @@ def quantize_keys(k, k8_out=None, scale_out=None, slot=None, stream=None):
 
 def decode_fp8(q, w, k8_cache, k_scale, start, seqlens, max_seqlen, topk=MAX_TOPK, with_scores=True,
                ws=None, out=None, stream=None):
-    """As decode, against an FP8 cache: k8_cache uint8 [*,128], k_scale float32 [*]."""
+    """As decode, against an FP8 cache: k8_cache uint8 [*,128], k_scale float32 [*].  With
+    q [B,64,128] and w [B,64], the 64-head indexer."""
     B = q.shape[0]
-    _need(q, "q", torch.bfloat16, (B, HEADS, DIM))
-    _need(w, "w", torch.bfloat16, (B, HEADS))
+    heads = V32_HEADS if q.dim() == 3 and q.shape[1] == V32_HEADS else HEADS
+    _need(q, "q", torch.bfloat16, (B, heads, DIM))
+    _need(w, "w", torch.bfloat16, (B, heads))
     _need(k8_cache, "k8_cache", torch.uint8)
     _need(k_scale, "k_scale", torch.float32)
     _need(start, "start", torch.int64, (B,))
@@ -471,8 +475,8 @@ def decode_fp8(q, w, k8_cache, k_scale, start, seqlens, max_seqlen, topk=MAX_TOP
         idx, sc = out
     nbytes = workspace_size(OP_DECODE_FP8, 0, B, max_seqlen, topk)
     ws = _workspace(nbytes, q.device, ws)
-    _check("dsa_idx_decode_fp8",
-           lib().dsa_idx_decode_fp8(_ptr(q), _ptr(w), _ptr(k8_cache), _ptr(k_scale), _ptr(start),
-                                    _ptr(seqlens), B, int(max_seqlen), topk, _ptr(idx), _ptr(sc),
-                                    _ptr(ws), nbytes, _stream(stream)))
+    fn = "dsa_idx_v32_decode_fp8" if heads == V32_HEADS else "dsa_idx_decode_fp8"
+    _check(fn, getattr(lib(), fn)(_ptr(q), _ptr(w), _ptr(k8_cache), _ptr(k_scale), _ptr(start),
+                                  _ptr(seqlens), B, int(max_seqlen), topk, _ptr(idx), _ptr(sc),
+                                  _ptr(ws), nbytes, _stream(stream)))
     return idx, sc

@@ -562,10 +562,10 @@ int dsa_idx_quantize_keys(const dsa_idx_bf16 *k, int64_t ldk, int64_t N, const i
     return ok();
 }
 
-int dsa_idx_decode_fp8(const dsa_idx_bf16 *q, const dsa_idx_bf16 *w, const uint8_t *k8,
-                       const float *k_scale, const int64_t *start, const int32_t *seqlens, int B,
-                       int max_seqlen, int topk, int32_t *idx, float *scores, void *ws,
-                       size_t ws_bytes, void *stream) {
+static int decode_fp8_impl(const dsa_idx_bf16 *q, const dsa_idx_bf16 *w, const uint8_t *k8,
+                           const float *k_scale, const int64_t *start, const int32_t *seqlens, int B,
+                           int max_seqlen, int topk, int32_t *idx, float *scores, void *ws,
+                           size_t ws_bytes, void *stream, int heads) {
     if (B < 0 || max_seqlen < 0) return fail(DSA_IDX_EINVAL, "B=%d max_seqlen=%d must be >= 0", B, max_seqlen);
     int r = check_topk(topk);
     if (r) return r;
@@ -581,10 +581,30 @@ int dsa_idx_decode_fp8(const dsa_idx_bf16 *q, const dsa_idx_bf16 *w, const uint8
     if (!aligned16(ws)) return fail(DSA_IDX_EINVAL, "workspace must be 16-byte aligned");
     r = check_device();
     if (r) return r;
-    hipError_t e = dsaidx::launch_decode_fp8(q, w, k8, k_scale, start, seqlens, B, max_seqlen, topk, ws,
-                                             idx, scores, reinterpret_cast<hipStream_t>(stream));
+    const hipStream_t st = reinterpret_cast<hipStream_t>(stream);
+    hipError_t e = heads == DSA_IDX_V32_HEADS
+                       ? dsaidx::launch_decode_fp8_v32(q, w, k8, k_scale, start, seqlens, B, max_seqlen, topk, ws,
+                                                       idx, scores, st)
+                       : dsaidx::launch_decode_fp8(q, w, k8, k_scale, start, seqlens, B, max_seqlen, topk, ws, idx,
+                                                   scores, st);
     if (e != hipSuccess) return hip_fail("decode_fp8 launch", e);
     return ok();
+}
+
+int dsa_idx_decode_fp8(const dsa_idx_bf16 *q, const dsa_idx_bf16 *w, const uint8_t *k8,
+                       const float *k_scale, const int64_t *start, const int32_t *seqlens, int B,
+                       int max_seqlen, int topk, int32_t *idx, float *scores, void *ws,
+                       size_t ws_bytes, void *stream) {
+    return decode_fp8_impl(q, w, k8, k_scale, start, seqlens, B, max_seqlen, topk, idx, scores, ws, ws_bytes,
+                           stream, DSA_IDX_HEADS);
+}
+
+int dsa_idx_v32_decode_fp8(const dsa_idx_bf16 *q, const dsa_idx_bf16 *w, const uint8_t *k8,
+                           const float *k_scale, const int64_t *start, const int32_t *seqlens, int B,
+                           int max_seqlen, int topk, int32_t *idx, float *scores, void *ws,
+                           size_t ws_bytes, void *stream) {
+    return decode_fp8_impl(q, w, k8, k_scale, start, seqlens, B, max_seqlen, topk, idx, scores, ws, ws_bytes,
+                           stream, DSA_IDX_V32_HEADS);
 }
 
 }  // extern "C"

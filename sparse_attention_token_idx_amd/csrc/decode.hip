@@ -214,9 +214,11 @@ __device__ __forceinline__ float e4m3_value(uint32_t c) {
 
 // Lane (l16, lg) of a 16-key slice reads bytes 32 lg .. 32 lg + 31 of key l16 (two 16-byte
 // loads); k-step ks uses bytes 32 lg + 8 ks .. + 7 of the key and of the query head.
-struct Fp8Scorer {
-    uint64_t qa[2][4];
-    float wv[2][4];
+template <int HB>
+struct Fp8ScorerT {
+    static constexpr int kH = 16 * HB;                 // heads: 32 or 64
+    uint64_t qa[HB][4];
+    float wv[HB][4];
     const uint8_t *kc;
     const float *ks;
     u32x4 kb[4][2];
@@ -224,8 +226,8 @@ struct Fp8Scorer {
 
     __device__ __forceinline__ void init(const Fp8Keys &p, const int64_t *start, int b, int l16, int lg) {
 #pragma unroll
-        for (int hh = 0; hh < 2; ++hh) {
-            const uint8_t *qr = p.q8 + ((int64_t)b * kHeads + 16 * hh + l16) * kDim + 32 * lg;
+        for (int hh = 0; hh < HB; ++hh) {
+            const uint8_t *qr = p.q8 + ((int64_t)b * kH + 16 * hh + l16) * kDim + 32 * lg;
             const u32x4 v0 = *reinterpret_cast<const u32x4 *>(qr);
             const u32x4 v1 = *reinterpret_cast<const u32x4 *>(qr + 16);
             qa[hh][0] = (uint64_t)v0[0] | ((uint64_t)v0[1] << 32);
@@ -233,7 +235,7 @@ struct Fp8Scorer {
             qa[hh][2] = (uint64_t)v1[0] | ((uint64_t)v1[1] << 32);
             qa[hh][3] = (uint64_t)v1[2] | ((uint64_t)v1[3] << 32);
 #pragma unroll
-            for (int r = 0; r < 4; ++r) wv[hh][r] = p.qw[(int64_t)b * kHeads + 16 * hh + 4 * lg + r];
+            for (int r = 0; r < 4; ++r) wv[hh][r] = p.qw[(int64_t)b * kH + 16 * hh + 4 * lg + r];
         }
         kc = p.k8 + start[b] * kDim;
         ks = p.kscale + start[b];
@@ -254,20 +256,19 @@ struct Fp8Scorer {
             const uint64_t b1 = (uint64_t)kb[u][0][2] | ((uint64_t)kb[u][0][3] << 32);
             const uint64_t b2 = (uint64_t)kb[u][1][0] | ((uint64_t)kb[u][1][1] << 32);
             const uint64_t b3 = (uint64_t)kb[u][1][2] | ((uint64_t)kb[u][1][3] << 32);
-            f32x4 s_lo = {0.f, 0.f, 0.f, 0.f}, s_hi = {0.f, 0.f, 0.f, 0.f};
-            s_lo = mfma_fp8(qa[0][0], b0, s_lo);
-            s_hi = mfma_fp8(qa[1][0], b0, s_hi);
-            s_lo = mfma_fp8(qa[0][1], b1, s_lo);
-            s_hi = mfma_fp8(qa[1][1], b1, s_hi);
-            s_lo = mfma_fp8(qa[0][2], b2, s_lo);
-            s_hi = mfma_fp8(qa[1][2], b2, s_hi);
-            s_lo = mfma_fp8(qa[0][3], b3, s_lo);
-            s_hi = mfma_fp8(qa[1][3], b3, s_hi);
+            const uint64_t bk[4] = {b0, b1, b2, b3};
+            f32x4 s[HB];
+#pragma unroll
+            for (int hh = 0; hh < HB; ++hh) s[hh] = f32x4{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+            for (int c = 0; c < 4; ++c)
+#pragma unroll
+                for (int hh = 0; hh < HB; ++hh) s[hh] = mfma_fp8(qa[hh][c], bk[c], s[hh]);
             float v = 0.f;
 #pragma unroll
-            for (int r = 0; r < 4; ++r) v = fmaf(wv[0][r], relu(s_lo[r]), v);
+            for (int hh = 0; hh < HB; ++hh)
 #pragma unroll
-            for (int r = 0; r < 4; ++r) v = fmaf(wv[1][r], relu(s_hi[r]), v);
+                for (int r = 0; r < 4; ++r) v = fmaf(wv[hh][r], relu(s[hh][r]), v);
             p[u] = v;
         }
     }
@@ -275,16 +276,16 @@ struct Fp8Scorer {
     static constexpr bool kScaled = true;
 
     static __device__ void stage(const Fp8Keys &p, int b, uint32_t *q_lds, float *w_lds) {
-        const uint32_t *src = reinterpret_cast<const uint32_t *>(p.q8 + (int64_t)b * kHeads * kDim);
-        for (int i = (int)threadIdx.x; i < kHeads * kDim / 4; i += (int)blockDim.x) q_lds[i] = src[i];
-        if ((int)threadIdx.x < kHeads) w_lds[threadIdx.x] = p.qw[(int64_t)b * kHeads + threadIdx.x];
+        const uint32_t *src = reinterpret_cast<const uint32_t *>(p.q8 + (int64_t)b * kH * kDim);
+        for (int i = (int)threadIdx.x; i < kH * kDim / 4; i += (int)blockDim.x) q_lds[i] = src[i];
+        if ((int)threadIdx.x < kH) w_lds[threadIdx.x] = p.qw[(int64_t)b * kH + threadIdx.x];
     }
     static __device__ float rescore(const Fp8Keys &p, const int64_t *start, int b, int s,
                                     const uint32_t *q_lds, const float *w_lds) {
         const uint8_t *kr = p.k8 + (start[b] + s) * kDim;
         float sc = 0.f;
 #pragma unroll 1
-        for (int h = 0; h < kHeads; ++h) {
+        for (int h = 0; h < kH; ++h) {
             float dot = 0.f;
 #pragma unroll 1
             for (int c = 0; c < kDim / 16; ++c) {
@@ -300,6 +301,7 @@ struct Fp8Scorer {
         return sc * p.kscale[start[b] + s];
     }
 };
+using Fp8Scorer = Fp8ScorerT<2>;
 
 template <class Sc>
 __device__ __forceinline__ float finish(const Sc &sc, const float (&p)[4], float scl, int lg) {
@@ -890,8 +892,8 @@ size_t decode_workspace(int B, int max_seqlen, bool fp8, DecodeWs *w, void *base
     const size_t o_cand = take(8u * flat);
     const size_t o_sb = take(4u * flat);
     const size_t o_sk = take(4u * Bs * kSampleMax);
-    const size_t o_q8 = fp8 ? take(Bs * kQOut) : 0;
-    const size_t o_qw = fp8 ? take(4u * Bs * kHeads) : 0;
+    const size_t o_q8 = fp8 ? take(Bs * 2 * kQOut) : 0;      // room for 64 heads
+    const size_t o_qw = fp8 ? take(4u * Bs * 2 * kHeads) : 0;
     if (w && base) {
         char *p = static_cast<char *>(base);
         w->cu = reinterpret_cast<int64_t *>(p + o_cu);
@@ -932,10 +934,22 @@ hipError_t launch_decode_fp8(const uint16_t *q, const uint16_t *w, const uint8_t
     if (B == 0) return hipSuccess;
     DecodeWs dw{};
     decode_workspace(B, max_seqlen, true, &dw, ws);
-    hipError_t e = launch_quantize_queries(q, w, B, dw.q8, dw.qw, stream);
+    hipError_t e = launch_quantize_queries(q, w, B, kHeads, dw.q8, dw.qw, stream);
     if (e != hipSuccess) return e;
     return run_decode<Fp8Scorer>(Fp8Keys{dw.q8, dw.qw, k8, kscale}, start, seqlens, B, max_seqlen, topk, dw,
                                  idx, scores, stream);
+}
+
+hipError_t launch_decode_fp8_v32(const uint16_t *q, const uint16_t *w, const uint8_t *k8, const float *kscale,
+                                 const int64_t *start, const int32_t *seqlens, int B, int max_seqlen, int topk,
+                                 void *ws, int32_t *idx, float *scores, hipStream_t stream) {
+    if (B == 0) return hipSuccess;
+    DecodeWs dw{};
+    decode_workspace(B, max_seqlen, true, &dw, ws);
+    hipError_t e = launch_quantize_queries(q, w, B, 2 * kHeads, dw.q8, dw.qw, stream);
+    if (e != hipSuccess) return e;
+    return run_decode<Fp8ScorerT<4>>(Fp8Keys{dw.q8, dw.qw, k8, kscale}, start, seqlens, B, max_seqlen, topk, dw,
+                                     idx, scores, stream);
 }
 
 }  // namespace dsaidx

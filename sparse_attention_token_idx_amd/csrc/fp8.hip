@@ -72,12 +72,12 @@ __global__ __launch_bounds__(256) void quantize_keys_kernel(const uint16_t *__re
     quantize_row(k + i * ldk, k8 + r * kDim, kscale + r);
 }
 
-// The new queries: q8 [B][32][128] codes and qw[b][h] = w[b][h] * 2^eq[b][h] (exact in fp32).
+// The new queries: q8 [B][H][128] codes and qw[b][h] = w[b][h] * 2^eq[b][h] (exact in fp32).
 __global__ __launch_bounds__(256) void quantize_queries_kernel(const uint16_t *__restrict__ q,
-                                                               const uint16_t *__restrict__ w, int B,
+                                                               const uint16_t *__restrict__ w, int64_t n,
                                                                uint8_t *__restrict__ q8, float *__restrict__ qw) {
-    const int64_t i = (int64_t)blockIdx.x * 4 + (threadIdx.x >> 6);   // (b, h)
-    if (i >= (int64_t)B * kHeads) return;
+    const int64_t i = (int64_t)blockIdx.x * 4 + (threadIdx.x >> 6);   // (b, h), n = B H of them
+    if (i >= n) return;
     float sc;
     quantize_row(q + i * kDim, q8 + i * kDim, &sc);
     if (__lane_id() == 0) qw[i] = bf16_to_f32(w[i]) * sc;
@@ -93,11 +93,12 @@ hipError_t launch_quantize_keys(const uint16_t *k, int64_t ldk, int64_t N, const
     return hipGetLastError();
 }
 
-hipError_t launch_quantize_queries(const uint16_t *q, const uint16_t *w, int B, uint8_t *q8, float *qw,
-                                   hipStream_t stream) {
+hipError_t launch_quantize_queries(const uint16_t *q, const uint16_t *w, int B, int heads, uint8_t *q8,
+                                   float *qw, hipStream_t stream) {
     if (B == 0) return hipSuccess;
-    hipLaunchKernelGGL(quantize_queries_kernel, dim3((unsigned)(((int64_t)B * kHeads + 3) / 4)), dim3(256), 0,
-                       stream, q, w, B, q8, qw);
+    const int64_t n = (int64_t)B * heads;
+    hipLaunchKernelGGL(quantize_queries_kernel, dim3((unsigned)((n + 3) / 4)), dim3(256), 0, stream, q, w, n, q8,
+                       qw);
     return hipGetLastError();
 }
 

@@ -95,8 +95,12 @@ hipError_t launch_decode(const uint16_t *q, const uint16_t *w, const uint16_t *k
 hipError_t launch_quantize_keys(const uint16_t *k, int64_t ldk, int64_t N, const int64_t *slot, uint8_t *k8,
                                 float *kscale, hipStream_t stream);
 // The new queries: q8 [B][32][128] codes, qw[b][h] = w[b][h] * 2^eq[b][h].
-hipError_t launch_quantize_queries(const uint16_t *q, const uint16_t *w, int B, uint8_t *q8, float *qw,
-                                   hipStream_t stream);
+hipError_t launch_quantize_queries(const uint16_t *q, const uint16_t *w, int B, int heads, uint8_t *q8,
+                                   float *qw, hipStream_t stream);
+// The 64-head indexer's decode against the FP8 key cache (workspace as for launch_decode_fp8).
+hipError_t launch_decode_fp8_v32(const uint16_t *q, const uint16_t *w, const uint8_t *k8, const float *kscale,
+                                 const int64_t *start, const int32_t *seqlens, int B, int max_seqlen, int topk,
+                                 void *ws, int32_t *idx, float *scores, hipStream_t stream);
 hipError_t launch_decode_fp8(const uint16_t *q, const uint16_t *w, const uint8_t *k8, const float *kscale,
                              const int64_t *start, const int32_t *seqlens, int B, int max_seqlen, int topk,
                              void *ws, int32_t *idx, float *scores, hipStream_t stream);

@@ -33,7 +33,7 @@ def test_exports_every_declared_symbol(dsa):
                           "dsa_idx_quantize_keys", "dsa_idx_decode_fp8", "dsa_idx_prefill_chunk",
                           "dsa_idx_sparse_mla", "dsa_idx_v32_project", "dsa_idx_v32_score_topk",
                           "dsa_idx_v32_score_topk_varlen", "dsa_idx_v32_prefill_chunk",
-                          "dsa_idx_v32_decode"}
+                          "dsa_idx_v32_decode", "dsa_idx_v32_decode_fp8"}
     for n in names:
         assert getattr(L, n) is not None
 
@@ -67,7 +67,7 @@ def test_workspace_sizes(dsa):
         P = B * 64 * ((m + 63) // 64)
         n = (r256(8 * (B + 1)) + r256(8 * B) + r256(4 * (P // 64 + 1)) + r256(8 * P) + r256(4 * P)
              + r256(4 * 8192 * B))
-        return n + (r256(B * 4096) + r256(128 * B) if fp8 else 0)
+        return n + (r256(B * 2 * 4096) + r256(2 * 128 * B) if fp8 else 0)   # room for 64 heads
     assert dec(64, 131072) == 101189120 + 2097152 and dec(3, 100) == 5376 + 98304
     assert dsa.workspace_size(dsa.OP_DECODE, 0, 64, 131072, 2048) == dec(64, 131072)
     assert dsa.workspace_size(dsa.OP_DECODE, 0, 3, 100, 8) == dec(3, 100)

@@ -178,3 +178,33 @@ def test_v32_decode(dsa, topk):
     idx, sc = idx.cpu().numpy(), sc.cpu().numpy()
     for b, L in enumerate(lens):
         check_row(L - 1, idx[b], sc[b], ref, b, topk)
+
+
+def test_v32_decode_fp8(dsa):
+    # the 64-head decode against the FP8 key cache: stage-wise against the oracle's FP8 rows
+    # (queries quantised per head there too) on the GPU's own projections and cache codes
+    lens = [1, 300, 2049, 9000]
+    B = len(lens)
+    Wt = wl.layer_weights_v32(seed=43)
+    act = wl.layer_activations(B, seed=43)
+    cache, start = wl.decode_cache(np.asarray(lens), seed=43)
+    cache_d = to_dev(cache)
+    Wd = weights_to_dev(Wt)
+    print(f"v32 decode fp8: lens={lens}", flush=True)
+    qs, ws_ = [], []
+    for b, L in enumerate(lens):
+        q1, k1, w1 = dsa.v32_project(to_dev(act["x"][b:b + 1]), to_dev(act["c_q"][b:b + 1]), Wd, pos0=L - 1)
+        cache_d[start[b] + L - 1] = k1[0]
+        qs.append(q1)
+        ws_.append(w1)
+    q, w = torch.cat(qs), torch.cat(ws_)
+    k8, ks = dsa.quantize_keys(cache_d)
+    idx, sc = dsa.decode_fp8(q, w, k8, ks, torch.from_numpy(start).cuda(),
+                             torch.from_numpy(np.asarray(lens, np.int32)).cuda(), max(lens), topk=2048)
+    torch.cuda.synchronize()
+    ke = np.round(np.log2(ks.cpu().numpy())).astype(np.int32)
+    ref = oracle.rows_fp8(to_host(q).reshape(B, V32_H, D), to_host(w), k8.cpu().numpy(), ke, start,
+                          np.asarray(lens) - 1, topk=2048, full=True)
+    idx, sc = idx.cpu().numpy(), sc.cpu().numpy()
+    for b, L in enumerate(lens):
+        check_row(L - 1, idx[b], sc[b], ref, b, 2048)
