@@ -9,7 +9,10 @@
 // reach 2^20, where an fp32 angle would be off by tenths of a radian), turns the pair of every
 // head and of the key in fp64, and rounds each result to bf16 directly (round to odd into fp32,
 // then to nearest even into bf16, which is the correctly rounded bf16 value).  The 32 threads
-// of a token touch 128 contiguous bytes of each head.
+// of a token touch 128 contiguous bytes of each head.  A thread loads the pairs of kBatch
+// heads before it turns and stores them, so each thread waits on a few memory round trips
+// instead of one per head; the key and the first batch are in flight while it forms the
+// sine and cosine.
 #include "common.hpp"
 #include "launch.hpp"
 
@@ -24,11 +27,11 @@ __device__ __forceinline__ uint16_t f64_to_bf16(double x) {
     return (uint16_t)f32_to_bf16(f);
 }
 
-__device__ __forceinline__ void turn(uint16_t *p, double c, double s) {
-    const uint32_t v = *reinterpret_cast<const uint32_t *>(p);
+constexpr int kBatch = 16;      // head pairs loaded before the first of them is turned
+
+__device__ __forceinline__ uint32_t turn(uint32_t v, double c, double s) {
     const double x = (double)bf16_to_f32(v & 0xFFFFu), y = (double)bf16_to_f32(v >> 16);
-    const uint32_t o = (uint32_t)f64_to_bf16(x * c - y * s) | ((uint32_t)f64_to_bf16(x * s + y * c) << 16);
-    *reinterpret_cast<uint32_t *>(p) = o;
+    return (uint32_t)f64_to_bf16(x * c - y * s) | ((uint32_t)f64_to_bf16(x * s + y * c) << 16);
 }
 
 __global__ __launch_bounds__(256) void rope_kernel(uint16_t *q, int64_t ldq, int heads, uint16_t *k, int64_t ldk,
@@ -37,14 +40,31 @@ __global__ __launch_bounds__(256) void rope_kernel(uint16_t *q, int64_t ldq, int
     const int64_t t = g / kRotPairs;
     const int i = (int)(g % kRotPairs);
     if (t >= T) return;
+    uint32_t *kp = k ? reinterpret_cast<uint32_t *>(k + t * ldk + 2 * i) : nullptr;
+    uint32_t *qp = q ? reinterpret_cast<uint32_t *>(q + t * ldq + 2 * i) : nullptr;
+    constexpr int64_t kHeadStride = kDim / 2;   // uint32 pairs between heads
+    uint32_t kv = 0, v[kBatch];
+    auto load_batch = [&](int h0) {
+#pragma unroll
+        for (int j = 0; j < kBatch; ++j)
+            if (h0 + j < heads) v[j] = qp[(int64_t)(h0 + j) * kHeadStride];
+    };
+    if (kp) kv = *kp;
+    if (qp) load_batch(0);
     const double ang = (double)(pos0 + t) * pow(theta, -2.0 * i / (2 * kRotPairs));
     double s, c;
     sincos(ang, &s, &c);
-    if (q) {
-        uint16_t *qr = q + t * ldq + 2 * i;
-        for (int h = 0; h < heads; ++h) turn(qr + (int64_t)h * kDim, c, s);
+    if (qp) {
+        for (int h0 = 0;;) {
+#pragma unroll
+            for (int j = 0; j < kBatch; ++j)
+                if (h0 + j < heads) qp[(int64_t)(h0 + j) * kHeadStride] = turn(v[j], c, s);
+            h0 += kBatch;
+            if (h0 >= heads) break;
+            load_batch(h0);
+        }
     }
-    if (k) turn(k + t * ldk + 2 * i, c, s);
+    if (kp) *kp = turn(kv, c, s);
 }
 
 }  // namespace
