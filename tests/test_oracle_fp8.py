@@ -115,3 +115,31 @@ def test_fp8_scores_power_of_two_key_scaling():
     assert np.array_equal(kc2, kc) and np.array_equal(ke2, ke + j)
     scaled = oracle.rows_fp8(q, w, kc2, ke2, [0], [L - 1], topk=8, full=True)["full"][0]
     assert np.array_equal(scaled, base * 2.0 ** j)
+
+
+def test_fp8_scores_query_head_scales():
+    """Each query head carries its own power-of-two scale 2^eq[h], folded into its head
+    weight: with heads scaled by 2^j (j != 0, up and down) the FP8 row must still equal the
+    bf16 row exactly, so a dropped or inverted 2^eq factor fails here."""
+    rng = np.random.default_rng(5)
+    L = 60
+    k = _representable_row(rng, L)
+    j = np.array([(h % 7) - 3 if (h % 7) != 3 else 4 for h in range(H)])   # -3..4, never 0
+    assert (j != 0).all()
+    q0 = oracle.bf16_to_f64(_representable_row(rng, H))
+    q = oracle.f64_to_bf16(q0 * (2.0 ** j)[:, None]).reshape(1, H, D)
+    assert np.array_equal(oracle.bf16_to_f64(q).reshape(H, D), q0 * (2.0 ** j)[:, None])
+    qc, qe = oracle.quantize_e4m3(q.reshape(H, D))
+    assert np.array_equal(qe, j)                                # the scale is 2^j per head
+    w = oracle.f64_to_bf16(rng.standard_normal((1, H)))
+    f8 = oracle.rows_fp8(q, w, *oracle.quantize_e4m3(k), [0], [L - 1], topk=16, full=True)
+    b16 = oracle.rows(q, w, k, [0], [L - 1], topk=16, full=True)
+    assert np.array_equal(f8["full"][0], b16["full"][0])
+    # one head at a time: the head's contribution scales by exactly 2^j[h]
+    for h in (0, 3, 10, 31):
+        wh = np.zeros((1, H), np.uint16)
+        wh[0, h] = oracle.f64_to_bf16(np.array([1.0]))[0]
+        one = oracle.rows_fp8(q, wh, *oracle.quantize_e4m3(k), [0], [L - 1], topk=4, full=True)["full"][0]
+        q_un = oracle.f64_to_bf16(q0).reshape(1, H, D)
+        base = oracle.rows(q_un, wh, k, [0], [L - 1], topk=4, full=True)["full"][0]
+        assert np.array_equal(one, base * 2.0 ** j[h])
