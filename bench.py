@@ -3,26 +3,31 @@
 
 Default workload (the headline): one full indexer layer over one causal sequence of
 T = 65,536 tokens -- q/k/w projections from x [T,7168] and c_q [T,1536], then causal scores
-I = sum_h w_h ReLU(q_h . k) over the whole prefix and the top 2,048 keys per query.  One
-step = dsa_idx_project + dsa_idx_score_topk (run as its two halves, dsa_idx_prefill_scores
-and dsa_idx_prefill_select) on resident inputs.  `value` is queries/s.
+I = sum_h w_h ReLU(q_h . k) over the whole prefix and the top 2,048 keys per query, with no
+T x T score matrix stored.  One step = dsa_idx_project + dsa_idx_score_topk on resident
+inputs.  `value` is queries/s.
 
-Also reported on the same line:
-  * roofline of the dominant kernel (score_rows_kernel, the causal scores) against the bf16
-    MFMA peak, its average duration measured with HIP events on the stream it runs on;
-  * the decode leg: 64 sequences with cached bf16 keys of U[32768, 131072] tokens, one
-    new query each (project + decode), as HBM GB/s of the decode kernels;
-  * the chunked-prefill leg: the last 4,096 queries of a 1,048,576-token window scored
-    against the whole prefix (dsa_idx_prefill_chunk: scores + select), as queries/s and
-    the scoring flop rate over the whole call;
+Also reported on the same line (each with median and min over its timed iterations):
+  * roofline of the dominant kernel (the score-and-filter pass of dsa_idx_score_topk) against
+    the bf16 MFMA peak: its duration from HIP events the library records around it on the
+    stream it runs on (diagnostic phase timing), and the phases of the call;
+  * the other workloads: scores + top-k only at T = 2,560; the full layer at T = 8,192; 24
+    indexer layers (own weights each) over 16 ragged sequences of log-uniform length in
+    [2,048, 32,768];
+  * the decode leg: 64 sequences with cached bf16 keys of U[32768, 131072] tokens, one new
+    query each (project + decode), as HBM GB/s of the decode kernels; the FP8-cache and
+    64-head decodes and the sparse-MLA consumer beside it;
+  * the chunked-prefill leg and the 64-head (DeepSeek-V3.2-shaped) layer;
+  * a measured device-copy rate (the HBM rate a plain read+write reaches on this machine);
   * cpu_baseline: the fp64 CPU oracle on a bounded sample of the same workload, with the
     extrapolation to the full layer.
 
-Inputs are seeded synthetic tensors with the shapes and distributions of the workload
+Inputs are seeded synthetic tensors with the shapes and distributions of the workloads
 (x, c_q ~ N(0,1); W_q ~ N(0,1/1536); W_k, W_w ~ N(0,1/7168); LayerNorm gain 1 + N(0,0.02),
-bias N(0,0.02), eps 1e-6; all bf16).
+bias N(0,0.02), eps 1e-6; q, k ~ N(0,1) and w ~ N(0,0.1) for the score-only case; all bf16).
 """
 import argparse
+import hashlib
 import json
 import os
 import sys
@@ -34,10 +39,10 @@ ROOT = os.path.dirname(os.path.abspath(__file__))
 sys.path.insert(0, ROOT)
 
 PEAK_BF16_TFLOPS = 2516.6     # MI355X dense bf16 MFMA (published)
-# HBM bytes per launch of the scoring kernel at T=65536, from rocprofv3 FETCH_SIZE and
+# HBM bytes per launch of the score-and-filter pass at T=65536, from rocprofv3 FETCH_SIZE and
 # WRITE_SIZE scaled by a 1 GiB device-copy calibration; reported only while the kernel
 # source is the one the counters were taken on (None: not measured for this source)
-TRAFFIC_SCORE_T65536 = {"source_sha256_prefix": "4540d23fdcbccca7", "bytes": 10781450858}
+TRAFFIC_FILTER_T65536 = {"source_sha256_prefix": None, "bytes": None}
 PEAK_HBM_GBPS = 8000.0        # MI355X HBM3E (published)
 H, D, QLAT, HIDDEN = 32, 128, 1536, 7168
 MLA_HEADS, MLA_KV, MLA_V = 96, 576, 512          # the sparse MLA consumer (gated-MLA row)
@@ -63,6 +68,8 @@ def parse():
     p.add_argument("--no-chunk", action="store_true")
     p.add_argument("--no-mla", action="store_true")
     p.add_argument("--no-v32", action="store_true")
+    p.add_argument("--no-configs", action="store_true",
+                   help="skip the score-only T=2560, layer T=8192 and 24-layer ragged legs")
     p.add_argument("--chunk", type=int, default=4096)
     p.add_argument("--window", type=int, default=1048576)
     p.add_argument("--calibrate-copy", action="store_true",
@@ -75,23 +82,45 @@ def dev_bf16(a):
     return torch.from_numpy(a.view(np.int16)).view(torch.bfloat16).cuda()
 
 
-def score_traffic(args):
-    import hashlib
-    src = os.path.join(ROOT, "sparse_attention_token_idx_amd", "csrc", "scores.hip")
+def filter_traffic(args):
+    src = os.path.join(ROOT, "sparse_attention_token_idx_amd", "csrc", "prefill.hip")
     h = hashlib.sha256(open(src, "rb").read()).hexdigest()[:16]
-    if args.T == 65536 and args.topk == 2048 and h == TRAFFIC_SCORE_T65536["source_sha256_prefix"]:
-        return TRAFFIC_SCORE_T65536["bytes"]
+    if args.T == 65536 and args.topk == 2048 and h == TRAFFIC_FILTER_T65536["source_sha256_prefix"]:
+        return TRAFFIC_FILTER_T65536["bytes"]
     return None
 
 
-def bench_prefill(dsa, args):
+def stats(v):
+    v = np.asarray(v, np.float64)
+    return dict(median=round(float(np.median(v)), 4), min=round(float(np.min(v)), 4),
+                mean=round(float(np.mean(v)), 4))
+
+
+def timed(step, n, stream, nev):
+    """Runs step(events) n times with nev events each; returns the per-interval times [n][nev-1]."""
+    import torch
+    evs = [[torch.cuda.Event(enable_timing=True) for _ in range(nev)] for _ in range(n)]
+    for i in range(n):
+        step(evs[i])
+    torch.cuda.synchronize()
+    return [[e[j].elapsed_time(e[j + 1]) for j in range(nev - 1)] for e in evs]
+
+
+def phase_split(dsa, steps):
+    """Per-call milliseconds of the phases recorded since phase_timing(True)."""
+    t = dsa.phase_times()
+    return {k: round(ms / steps, 4) for k, (ms, n) in t.items() if n > 0}
+
+
+def bench_layer(dsa, args, T, steps, warmup, label):
+    """One indexer layer (project + score_topk) over one causal sequence of T tokens."""
     import torch
     from synth import workloads as wl
-    T, topk = args.T, args.topk
+    topk = args.topk
     t0 = time.time()
     Wt = wl.layer_weights(layer=0, seed=0)
     act = wl.layer_activations(T, seed=0)
-    log(f"prefill: generated inputs T={T} in {time.time() - t0:.1f}s")
+    log(f"{label}: generated inputs T={T} in {time.time() - t0:.1f}s")
     W = {k: dev_bf16(v) for k, v in Wt.items() if k != "eps"}
     W["eps"] = Wt["eps"]
     x, cq = dev_bf16(act["x"]), dev_bf16(act["c_q"])
@@ -101,46 +130,150 @@ def bench_prefill(dsa, args):
     w = torch.empty((T, H), dtype=torch.bfloat16, device="cuda")
     idx = torch.empty((T, topk), dtype=torch.int32, device="cuda")
     sc = torch.empty((T, topk), dtype=torch.float32, device="cuda")
-    ws = torch.empty(dsa.workspace_size(dsa.OP_SCORE_TOPK, T, topk=topk), dtype=torch.uint8,
-                     device="cuda")
+    ws = torch.empty(dsa.workspace_size(dsa.OP_SCORE_TOPK, T, topk=topk), dtype=torch.uint8, device="cuda")
     stream = torch.cuda.current_stream()
 
-    # score_topk run as its two halves (the same C-ABI calls it makes), so that the scoring
-    # kernel, the dominant one, is timed on its own stream with events
     def step(ev=None):
         if ev is not None:
             ev[0].record(stream)
         dsa.project(x, cq, W, q=q, k_out=k, w=w)
         if ev is not None:
             ev[1].record(stream)
-        dsa.prefill_scores(q, k, w, ws)
+        dsa.score_topk(q, k, w, topk=topk, ws=ws, out=(idx, sc))
         if ev is not None:
             ev[2].record(stream)
-        dsa.prefill_select(T, ws, topk=topk, out=(idx, sc))
-        if ev is not None:
-            ev[3].record(stream)
 
-    for i in range(args.warmup):
+    for i in range(warmup):
         step()
         torch.cuda.synchronize()
-        log(f"prefill: warmup step {i + 1}/{args.warmup} done")
-    evs = [[torch.cuda.Event(enable_timing=True) for _ in range(4)] for _ in range(args.steps)]
+    log(f"{label}: {warmup} warmup steps done")
+    dsa.phase_timing(True)
     torch.cuda.synchronize()
     t0 = time.perf_counter()
-    for i in range(args.steps):
-        step(evs[i])
-    torch.cuda.synchronize()
+    times = timed(step, steps, stream, 3)
     wall = time.perf_counter() - t0
-    proj_ms = [e[0].elapsed_time(e[1]) for e in evs]
-    score_ms = [e[1].elapsed_time(e[2]) for e in evs]
-    select_ms = [e[2].elapsed_time(e[3]) for e in evs]
-    log(f"prefill: {args.steps} steps in {wall:.3f}s; project {np.mean(proj_ms):.3f} ms, "
-        f"scores {np.mean(score_ms):.3f} ms, select {np.mean(select_ms):.3f} ms")
+    phases = phase_split(dsa, steps)
+    dsa.phase_timing(False)
+    dsa.workspace_status(ws)
+    proj = [t[0] for t in times]
+    st = [t[1] for t in times]
+    step_ms = [a + b for a, b in times]
     pairs = T * (T + 1) // 2
-    return dict(wall=wall, proj_ms=float(np.mean(proj_ms)), score_ms=float(np.mean(score_ms)),
-                select_ms=float(np.mean(select_ms)), score_ms_min=float(np.min(score_ms)),
-                pairs=pairs, score_flop=pairs * SCORE_FLOP_PER_PAIR,
-                proj_flop=T * PROJ_FLOP_PER_TOKEN, score_bytes=4 * pairs)
+    log(f"{label}: {steps} steps in {wall:.3f}s; project {np.median(proj):.3f} ms, "
+        f"score_topk {np.median(st):.3f} ms (median); phases {phases}")
+    del ws, x, cq
+    return dict(T=T, wall=wall, proj=stats(proj), score_topk=stats(st), step=stats(step_ms), phases=phases,
+                pairs=pairs, score_flop=pairs * SCORE_FLOP_PER_PAIR, proj_flop=T * PROJ_FLOP_PER_TOKEN)
+
+
+def bench_score_only(dsa, args, T=2560, steps=50):
+    """Scores + top-k only over one causal sequence (q, k ~ N(0,1), w ~ N(0,0.1), seed 0)."""
+    import torch
+    from synth import workloads as wl
+    topk = args.topk
+    s = wl.score_inputs(T, seed=0)
+    q, k, w = dev_bf16(s["q"]), dev_bf16(s["k"]), dev_bf16(s["w"])
+    idx = torch.empty((T, topk), dtype=torch.int32, device="cuda")
+    sc = torch.empty((T, topk), dtype=torch.float32, device="cuda")
+    ws = torch.empty(dsa.workspace_size(dsa.OP_SCORE_TOPK, T, topk=topk), dtype=torch.uint8, device="cuda")
+    stream = torch.cuda.current_stream()
+
+    def step(ev=None):
+        if ev is not None:
+            ev[0].record(stream)
+        dsa.score_topk(q, k, w, topk=topk, ws=ws, out=(idx, sc))
+        if ev is not None:
+            ev[1].record(stream)
+
+    for _ in range(5):
+        step()
+    torch.cuda.synchronize()
+    torch.cuda._sleep(50_000_000)   # the calls queue up ahead of the GPU: events time the GPU
+    times = [t[0] for t in timed(step, steps, stream, 2)]
+    pairs = T * (T + 1) // 2
+    log(f"score only T={T}: {np.median(times):.4f} ms median, {np.min(times):.4f} ms min")
+    return dict(T=T, ms=stats(times), pairs=pairs, score_flop=pairs * SCORE_FLOP_PER_PAIR)
+
+
+def bench_varlen_layers(dsa, args, layers=24, steps=3):
+    """24 indexer layers, each with its own weights, over 16 ragged sequences (lengths
+    log-uniform in [2048, 32768]): per layer project + score_topk_varlen."""
+    import torch
+    from synth import workloads as wl
+    topk = args.topk
+    B = 16
+    lens = wl.varlen_lengths(B, seed=0)
+    cu = wl.cu_seqlens(lens)
+    total = int(cu[-1])
+    t0 = time.time()
+    act = wl.layer_activations(total, seed=0)
+    x, cq = dev_bf16(act["x"]), dev_bf16(act["c_q"])
+    del act
+    Ws = []
+    for layer in range(layers):
+        Wt = wl.layer_weights(layer=layer, seed=0)
+        W = {k: dev_bf16(v) for k, v in Wt.items() if k != "eps"}
+        W["eps"] = Wt["eps"]
+        Ws.append(W)
+    log(f"varlen: {layers} layers, {B} sequences, {total} tokens: inputs in {time.time() - t0:.1f}s")
+    cu_d = torch.from_numpy(cu).cuda()
+    maxL = int(lens.max())
+    q = torch.empty((total, H, D), dtype=torch.bfloat16, device="cuda")
+    k = torch.empty((total, D), dtype=torch.bfloat16, device="cuda")
+    w = torch.empty((total, H), dtype=torch.bfloat16, device="cuda")
+    idx = torch.empty((total, topk), dtype=torch.int32, device="cuda")
+    sc = torch.empty((total, topk), dtype=torch.float32, device="cuda")
+    ws = torch.empty(dsa.workspace_size(dsa.OP_SCORE_TOPK_VARLEN, total, B, maxL, topk), dtype=torch.uint8,
+                     device="cuda")
+    stream = torch.cuda.current_stream()
+
+    def step(ev=None):
+        if ev is not None:
+            ev[0].record(stream)
+        for W in Ws:
+            dsa.project(x, cq, W, q=q, k_out=k, w=w)
+            dsa.score_topk_varlen(q, k, w, cu_d, maxL, topk=topk, ws=ws, out=(idx, sc))
+        if ev is not None:
+            ev[1].record(stream)
+
+    step()
+    torch.cuda.synchronize()
+    times = [t[0] for t in timed(step, steps, stream, 2)]
+    dsa.workspace_status(ws)
+    pairs = int(sum(L * (L + 1) // 2 for L in lens.tolist()))
+    flop = layers * (pairs * SCORE_FLOP_PER_PAIR + total * PROJ_FLOP_PER_TOKEN)
+    log(f"varlen: {layers} layers in {np.median(times):.2f} ms median "
+        f"({flop / (np.median(times) * 1e-3) / 1e12:.1f} TFLOP/s)")
+    del ws, x, cq
+    return dict(layers=layers, B=B, total=total, ms=stats(times), pairs_per_layer=pairs, flop=flop)
+
+
+def copy_rate(n_bytes=1 << 30, steps=10):
+    """GB/s of a plain device-to-device copy (bytes read + bytes written per second)."""
+    import torch
+    src = torch.empty(n_bytes, dtype=torch.uint8, device="cuda")
+    dst = torch.empty_like(src)
+    dst.copy_(src)
+    torch.cuda.synchronize()
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    e0.record()
+    for _ in range(steps):
+        dst.copy_(src)
+    e1.record()
+    torch.cuda.synchronize()
+    ms = e0.elapsed_time(e1) / steps
+    del src, dst
+    return round(2 * n_bytes / (ms * 1e-3) / 1e9, 1)
+
+
+def cpu_model():
+    try:
+        for line in open("/proc/cpuinfo"):
+            if line.startswith("model name"):
+                return line.split(":", 1)[1].strip()
+    except OSError:
+        pass
+    return None
 
 
 def bench_decode(dsa, args):
@@ -330,7 +463,7 @@ def bench_mla(dsa, args, idx, start_d, sum_keys, n):
 
 def bench_v32(dsa, args):
     """The 64-head (DeepSeek-V3.2-shaped) indexer layer at the same T: projections with the
-    rotary step, then scores (two 32-head passes) and top-k."""
+    rotary step, then scores (all 64 heads in one pass) and top-k."""
     import torch
     from synth import workloads as wl
     T, topk = args.T, args.topk
@@ -443,7 +576,7 @@ def cpu_baseline(args):
             break
         batch = rng.integers(0, T, 2 * len(batch))
     total = t_k + t_qw * T / n_rows + t_rows * (T * (T + 1) / 2) / float(pairs)
-    return dict(value=round(T / total, 2), unit="queries/s", cores=cores, kind="oracle",
+    return dict(value=round(T / total, 2), unit="queries/s", cores=cores, cpu_model=cpu_model(), kind="oracle",
                 sample=(f"fp64 oracle, OpenMP over {cores} host threads: keys projected for all {T} "
                         f"tokens, q and w for {n_rows} sampled rows, those rows scored over their whole "
                         f"causal prefix and fully sorted; extrapolated to all {T} rows by tokens "
@@ -469,20 +602,56 @@ def main():
         torch.cuda.synchronize()
         log("calibration: copied 1073741824 bytes device to device")
         del src, dst
-    pre = bench_prefill(dsa, args)
+    copy_gbps = copy_rate()
+    log(f"device copy: {copy_gbps} GB/s (read + write)")
+    pre = bench_layer(dsa, args, args.T, args.steps, args.warmup, "prefill")
+    cfg1 = cfg2 = cfg5 = None
+    if not args.no_configs:
+        cfg1 = bench_score_only(dsa, args)
+        cfg2 = bench_layer(dsa, args, 8192, 30, 3, "layer T=8192")
+        cfg5 = bench_varlen_layers(dsa, args)
     dec = None if args.no_decode else bench_decode(dsa, args)
     chk = None if args.no_chunk else bench_chunk(dsa, args)
     v32 = None if args.no_v32 else bench_v32(dsa, args)
-    ms_step = pre["proj_ms"] + pre["score_ms"] + pre["select_ms"]
     ms_wall = pre["wall"] * 1e3 / args.steps
     qps = args.T / (ms_wall * 1e-3)
     tflops = (pre["score_flop"] + pre["proj_flop"]) / (ms_wall * 1e-3) / 1e12
-    achieved = pre["score_flop"] / (pre["score_ms"] * 1e-3) / 1e12
+    filt_ms = pre["phases"].get("filter")
+    achieved = pre["score_flop"] / (filt_ms * 1e-3) / 1e12 if filt_ms else None
     cpu = None
     if not args.no_cpu_baseline:
         log("cpu baseline: running the oracle on a bounded sample")
         cpu = cpu_baseline(args)
         log(f"cpu baseline: {cpu['value']:.1f} queries/s ({cpu['measured_s']} s measured)")
+
+    def frac(flop, ms):
+        return round(flop / (ms * 1e-3) / 1e12 / PEAK_BF16_TFLOPS, 4)
+
+    configs = None
+    if cfg1 is not None:
+        configs = {
+            "score_only_T2560": {
+                "workload": "scores + top-2048 of one causal sequence, T=2560, q/k ~ N(0,1), w ~ N(0,0.1)",
+                "ms": cfg1["ms"], "queries_per_s_median": round(cfg1["T"] / (cfg1["ms"]["median"] * 1e-3), 1),
+                "score_tflops_median": round(cfg1["score_flop"] / (cfg1["ms"]["median"] * 1e-3) / 1e12, 1),
+                "frac_of_bf16_peak_median": frac(cfg1["score_flop"], cfg1["ms"]["median"]),
+                "frac_of_bf16_peak_best": frac(cfg1["score_flop"], cfg1["ms"]["min"])},
+            "layer_T8192": {
+                "workload": "one indexer layer, causal prefill T=8192: project + scores + top-2048",
+                "step_ms": cfg2["step"], "project_ms": cfg2["proj"], "score_topk_ms": cfg2["score_topk"],
+                "queries_per_s_median": round(cfg2["T"] / (cfg2["step"]["median"] * 1e-3), 1),
+                "tflops_median": round((cfg2["score_flop"] + cfg2["proj_flop"]) / (cfg2["step"]["median"] * 1e-3) / 1e12, 1),
+                "frac_of_bf16_peak_median": frac(cfg2["score_flop"] + cfg2["proj_flop"], cfg2["step"]["median"]),
+                "phases_ms": cfg2["phases"]},
+            "varlen_24_layers": {
+                "workload": f"24 indexer layers (own weights each), {cfg5['B']} ragged sequences, "
+                            f"{cfg5['total']} tokens, lengths log-uniform in [2048, 32768]: per layer "
+                            "project + scores + top-2048",
+                "ms": cfg5["ms"],
+                "queries_per_s_median": round(cfg5["layers"] * cfg5["total"] / (cfg5["ms"]["median"] * 1e-3), 1),
+                "tflops_median": round(cfg5["flop"] / (cfg5["ms"]["median"] * 1e-3) / 1e12, 1),
+                "frac_of_bf16_peak_median": frac(cfg5["flop"], cfg5["ms"]["median"])},
+        }
     line = {
         "metric": "DSA indexer queries/s + TFLOP/s (T=64K prefill, top-2048); decode HBM GB/s",
         "value": round(qps, 1),
@@ -497,20 +666,24 @@ def main():
         "dtype": "bf16",
         "data": "synthetic",
         "config": {"workload": f"one indexer layer, causal prefill T={args.T}, top-{args.topk}: "
-                               "project + scores + select", "seq_len": args.T, "topk": args.topk,
-                   "heads": H, "head_dim": D, "parallelism": "single GPU"},
+                               "project + scores + select, no T x T score matrix stored",
+                   "seq_len": args.T, "topk": args.topk, "heads": H, "head_dim": D,
+                   "parallelism": "single GPU"},
         "tflops": round(tflops, 1),
-        "split_ms": {"project": round(pre["proj_ms"], 3), "scores": round(pre["score_ms"], 3),
-                     "select": round(pre["select_ms"], 3), "sum_of_events": round(ms_step, 3)},
-        "roofline": {"kernel": "score_rows_kernel", "bound": "mfma",
-                     "achieved": round(achieved, 1), "peak": PEAK_BF16_TFLOPS, "unit": "TFLOP/s",
-                     "frac": round(achieved / PEAK_BF16_TFLOPS, 4), "traffic": score_traffic(args),
-                     "algorithmic_flop_per_launch": pre["score_flop"]},
+        "step_ms": pre["step"],
+        "split_ms": {"project": pre["proj"], "score_topk": pre["score_topk"], "phases": pre["phases"]},
+        "roofline": {"kernel": "score_kernel<32, filter> (score-and-filter pass)", "bound": "mfma",
+                     "achieved": None if achieved is None else round(achieved, 1), "peak": PEAK_BF16_TFLOPS,
+                     "unit": "TFLOP/s", "frac": None if achieved is None else round(achieved / PEAK_BF16_TFLOPS, 4),
+                     "traffic": filter_traffic(args), "algorithmic_flop_per_launch": pre["score_flop"]},
+        "device_copy_GBps": copy_gbps,
+        "configs": configs,
         "decode": None if dec is None else {
             "workload": f"{dec['batch']} sequences, one new query each, cached bf16 keys "
                         f"U[32768,131072] (sum {dec['sum_keys']}), top-{args.topk}",
             "decode_ms": round(dec["decode_ms"], 4), "project_ms": round(dec["project_ms"], 4),
             "GBps": round(dec["decode_GBps"], 1), "hbm_frac": round(dec["decode_hbm_frac"], 4),
+            "frac_of_copy_rate": round(dec["decode_GBps"] / copy_gbps, 4),
             "step_GBps_incl_project": round(dec["step_GBps"], 1),
             "host_step_ms": round(dec["host_step_ms"], 4),
             "algorithmic_bytes": dec["decode_bytes"],
@@ -536,14 +709,14 @@ def main():
                 "algorithmic_bytes": dec["mla"]["bytes"]}},
         "chunked_prefill": None if chk is None else {
             "workload": f"last {chk['C']} queries of a {chk['prefix'] + chk['C']}-token window "
-                        f"against the whole prefix, top-{args.topk}: scores + select",
+                        f"against the whole prefix, top-{args.topk}",
             "ms": round(chk["ms"], 3), "queries_per_s": round(chk["qps"], 1),
             "score_tflops_over_call": round(chk["tflops"], 1),
             "frac_of_bf16_peak": round(chk["tflops"] / PEAK_BF16_TFLOPS, 4),
             "causal_pairs": chk["pairs"]},
         "v32_indexer": None if v32 is None else {
             "workload": f"the 64-head (DeepSeek-V3.2-shaped) indexer layer, causal prefill T={args.T}, "
-                        f"top-{args.topk}: project + rotary step, scores (two 32-head passes) + select",
+                        f"top-{args.topk}: project + rotary step, scores (64 heads in one pass) + select",
             "ms_per_step": round(v32["proj_ms"] + v32["score_topk_ms"], 3),
             "queries_per_s": round(v32["qps"], 1), "project_ms": round(v32["proj_ms"], 3),
             "score_topk_ms": round(v32["score_topk_ms"], 3),

@@ -3,17 +3,16 @@
  *
  * The operation is the one fixed on the archdiff.com compare page "Qwen3.5-397B-A17B vs
  * Kimi K3.1 Pro" (component table, sparse/compressed-attention row, Kimi K3.1 Pro cell):
- * every MLA layer owns an indexer with 32 heads of 128 dims whose queries are projected
- * from the 1,536-dim query latent (1,536 -> 4,096), one 128-dim key shared by all heads
- * taken from the hidden state through a LayerNorm, and per-head weights from a
- * 7,168 -> 32 projection; the score of key token s for query token t is
+ * each MLA layer has an indexer with H = 32, D = 128: q = c_q W_q (W_q [1536][4096]),
+ * k = LayerNorm(x W_k) (W_k [7168][128], one key vector per token for all heads) and
+ * w = x W_w (W_w [7168][32]); the score of key token s for query token t is
  *
  *         I[t,s] = sum_h w[t,h] * ReLU( q[t,h,:] . k[s,:] ),
  *
  * and each query keeps the 2,048 tokens with the largest scores, which become the only
  * keys its MLA attends (gated-MLA row of the same table).  The key LayerNorm is named in
  * the QK-norm row; the indexer applies no rotary embedding ("Kimi K3.1 Pro vs Gemma 4 31B"
- * page, RoPE row) and scores the whole prefix (same page, long-context row).  Serving
+ * page, RoPE row) and every key s <= t is scored (same page, long-context row).  Serving
  * engines cache the indexer keys across decode steps ("Kimi K3.1 Pro vs GLM-5" page,
  * low-precision row); dsa_idx_decode scores against such a cache.
  *
@@ -67,6 +66,7 @@ extern "C" {
 #define DSA_IDX_EUNSUPPORTED (-2)/* topk outside [1, 2048], device not gfx950, size too large */
 #define DSA_IDX_EWORKSPACE (-3)  /* ws_bytes below dsa_idx_workspace_size() */
 #define DSA_IDX_EHIP (-4)        /* a HIP runtime call failed (message names it) */
+#define DSA_IDX_ESTALL (-5)      /* dsa_idx_workspace_status: a score kernel's ring wait gave up */
 
 /* operations for dsa_idx_workspace_size */
 #define DSA_IDX_OP_PROJECT 0
@@ -78,11 +78,15 @@ extern "C" {
 #define DSA_IDX_OP_SPARSE_MLA 6
 #define DSA_IDX_OP_V32_PROJECT 7
 #define DSA_IDX_OP_V32_SCORE_TOPK 8
+#define DSA_IDX_OP_V32_SCORE_TOPK_VARLEN 9
+#define DSA_IDX_OP_V32_PREFILL_CHUNK 10
+#define DSA_IDX_OP_PREFILL_ROWS 11   /* dsa_idx_prefill_scores / dsa_idx_prefill_select */
 
 typedef uint16_t dsa_idx_bf16;
 
-/* One layer's indexer weights (device pointers, borrowed for the call).  Each of the 24
- * MLA layers owns its own set (sparse/compressed-attention row: no index sharing). */
+/* One layer's indexer weights (device pointers, borrowed for the call).  The 24 MLA layers
+ * have 24 separate sets; no layer reuses another's selection (sparse/compressed-attention
+ * row). */
 typedef struct {
     const dsa_idx_bf16 *W_q;      /* [1536][4096] row-major: q = c_q . W_q            */
     const dsa_idx_bf16 *W_k;      /* [7168][128]  row-major: k = LN(x . W_k)           */
@@ -101,11 +105,13 @@ const char *dsa_idx_last_error(void);
 /* Bytes of workspace an operation needs (host-only, no device access).
  *   op               one of DSA_IDX_OP_*
  *   total_tokens     T for PROJECT, SCORE_TOPK, SPARSE_MLA, V32_PROJECT and V32_SCORE_TOPK;
- *                    the packed token count for VARLEN; the chunk's query count C for
- *                    PREFILL_CHUNK
- *   B                number of sequences (VARLEN, DECODE); ignored otherwise
- *   max_seqlen       longest sequence (VARLEN, DECODE), keys of the longest cache for DECODE;
- *                    the cached prefix length for PREFILL_CHUNK
+ *                    the packed token count for the VARLEN ops and PREFILL_ROWS; the chunk's
+ *                    query count C for the PREFILL_CHUNK ops
+ *   B                number of sequences (VARLEN ops, DECODE ops; PREFILL_ROWS: 0 for one
+ *                    sequence of total_tokens tokens); ignored otherwise
+ *   max_seqlen       longest sequence (VARLEN ops, PREFILL_ROWS with B > 0), keys of the
+ *                    longest cache for the DECODE ops; the cached prefix length for the
+ *                    PREFILL_CHUNK ops
  *   topk             tokens kept (selected, for SPARSE_MLA) per query, 1..2048; ignored
  *                    for PROJECT and V32_PROJECT
  * Writes *bytes (0 is a valid answer).  Returns a status. */
@@ -132,8 +138,14 @@ int dsa_idx_project(const dsa_idx_weights *weights, const dsa_idx_bf16 *x, int64
  *   q [T][32][128], k [T][128], w [T][32]   bf16, 16-byte aligned
  *   idx    [T][topk] int32  selected key positions s <= t, ascending, -1 padded
  *   scores [T][topk] fp32   I[t, idx] (may be NULL), -inf padded
- * Runs dsa_idx_prefill_scores then dsa_idx_prefill_select (below) on the same workspace, which
- * holds the causal fp32 scores of every row (about 2 T^2 bytes). */
+ * No T x T score matrix is stored: each row first scores one key per 32-key stratum to place
+ * a threshold, the full causal score stream then keeps only the (score, index) pairs at or
+ * above it, and the top-k is selected exactly from those; a row the threshold cannot decide
+ * (too few or too many kept keys) is scored again in full into a bounded scratch row.  The
+ * result equals the full sort of each row whatever the data.  The workspace
+ * (DSA_IDX_OP_SCORE_TOPK) grows linearly in T: about 3.7 GB at T = 65,536, 4.8 GB at
+ * T = 1,048,576.  Its first 32-bit word is the status that dsa_idx_workspace_status() reads.
+ * Limit: T <= 16,777,216. */
 int dsa_idx_score_topk(const dsa_idx_bf16 *q, const dsa_idx_bf16 *k, const dsa_idx_bf16 *w,
                        int64_t T, int topk, int32_t *idx, float *scores, void *ws,
                        size_t ws_bytes, void *stream);
@@ -148,20 +160,24 @@ int dsa_idx_score_topk_varlen(const dsa_idx_bf16 *q, const dsa_idx_bf16 *k,
                               int max_seqlen, int64_t total, int topk, int32_t *idx,
                               float *scores, void *ws, size_t ws_bytes, void *stream);
 
-/* The two halves of dsa_idx_score_topk (cu_seqlens == NULL: one sequence of `total` tokens,
- * B and max_seqlen ignored) and of dsa_idx_score_topk_varlen (cu_seqlens given), for callers
- * that want the causal scores themselves or time the halves separately.  Both take the
- * workspace of the matching dsa_idx_workspace_size op.
+/* The causal score rows themselves (32 heads), for callers that want the scores I[t, s] of
+ * every key, and a row top-k over them.  cu_seqlens == NULL: one sequence of `total` tokens
+ * (B and max_seqlen ignored); else a ragged batch as dsa_idx_score_topk_varlen.  These two
+ * calls DO store every causal score: their workspace (DSA_IDX_OP_PREFILL_ROWS) is about
+ * 2 total^2 bytes for one sequence (8.6 GB at 65,536 tokens), so they suit inspection and
+ * moderate lengths; dsa_idx_score_topk does not need them.
  *
- * dsa_idx_prefill_scores writes the scores I[t, s], s <= t, into ws: a header of
- * H = 256 * ceil(8 (B' + 1) / 256) bytes (B' = 1 without cu_seqlens, else B) whose first
- * B' + 1 int64 are the sequences' float offsets into the row area; a scratch row of
- * 4 * 128 * ceil(max_len / 128) bytes (rounded up to 256; max_len = total or max_seqlen);
- * then the row area: row t of sequence i starts at float offset
+ * dsa_idx_prefill_scores writes into ws: a 256-byte header whose first word is the status
+ * (see dsa_idx_workspace_status); B' + 1 int64 (B' = 1 without cu_seqlens, else B) at byte
+ * 256, the sequences' float offsets into the row area, padded to H = 256 + 256 *
+ * ceil(8 (B' + 1) / 256) bytes; a scratch row of 4 * 128 * ceil(max_len / 128) bytes (rounded
+ * up to 256; max_len = total or max_seqlen); then the row area: row t of sequence i starts at
+ * float offset
  *     base[i] + 8192 q (q + 1) + 128 r (q + 1),   q = t / 128, r = t % 128,
  * and holds 128 (q + 1) floats, of which the first t + 1 are the scores (the rest are
  * unspecified).
- * dsa_idx_prefill_select reads those rows and writes idx and scores as dsa_idx_score_topk. */
+ * dsa_idx_prefill_select reads those rows and writes idx and scores as dsa_idx_score_topk
+ * (every row index -2 and score NaN if the status word says the scoring kernel gave up). */
 int dsa_idx_prefill_scores(const dsa_idx_bf16 *q, const dsa_idx_bf16 *k, const dsa_idx_bf16 *w,
                            const int32_t *cu_seqlens, int B, int max_seqlen, int64_t total,
                            void *ws, size_t ws_bytes, void *stream);
@@ -179,9 +195,10 @@ int dsa_idx_prefill_select(const int32_t *cu_seqlens, int B, int max_seqlen, int
  *   idx [C][topk], scores [C][topk] (may be NULL): row i as prefill row prefix + i of
  *                                  dsa_idx_score_topk (absolute positions, ascending,
  *                                  -1 / -inf padded)
- * prefix = 0 is dsa_idx_score_topk.  Limits: C <= 2,097,120, prefix + C <= 16,777,216.  The
- * workspace (DSA_IDX_OP_PREFILL_CHUNK, total_tokens = C, max_seqlen = prefix) holds the C
- * score rows, about 4 C (prefix + C / 2) bytes. */
+ * prefix = 0 is dsa_idx_score_topk, and the method and workspace are that call's: the
+ * workspace (DSA_IDX_OP_PREFILL_CHUNK, total_tokens = C, max_seqlen = prefix) is linear in C
+ * and in prefix + C (4.3 GB for the last 4,096 queries of a 1,048,576-token window).
+ * Limit: prefix + C <= 16,777,216. */
 int dsa_idx_prefill_chunk(const dsa_idx_bf16 *q, const dsa_idx_bf16 *k, const dsa_idx_bf16 *w,
                           int64_t C, int64_t prefix, int topk, int32_t *idx, float *scores,
                           void *ws, size_t ws_bytes, void *stream);
@@ -192,7 +209,8 @@ int dsa_idx_prefill_chunk(const dsa_idx_bf16 *q, const dsa_idx_bf16 *k, const ds
  *                                  [start[b], start[b] + seqlens[b]), whose last row is
  *                                  the new token's own key (written by dsa_idx_project
  *                                  through k_slot)
- *   start   (device, int64 [B]), seqlens (device, int32 [B], 1 <= seqlens[b] <= max_seqlen)
+ *   start   (device, int64 [B]), seqlens (device, int32 [B], 1 <= seqlens[b] <= max_seqlen),
+ *   max_seqlen <= 16,777,216
  *   idx [B][topk], scores [B][topk] (may be NULL): as for prefill row seqlens[b] - 1,
  *   indices relative to start[b].
  * The cached keys are the per-layer indexer keys that serving engines keep across steps. */
@@ -226,10 +244,9 @@ int dsa_idx_decode_fp8(const dsa_idx_bf16 *q, const dsa_idx_bf16 *w, const uint8
                        size_t ws_bytes, void *stream);
 
 /* ---- The consumer of the selection: sparse MLA over the selected tokens ("Qwen3.5-397B-A17B
- * vs Kimi K3.1 Pro" page, gated-MLA row: 96 heads, keys and values from a 512-dim latent plus
- * a 64-dim shared key slot -- 576 cached values per token -- q/k head dim 192, v head dim
- * 128, each query attending only to the 2,048 tokens its layer's indexer selects; no rotary
- * step, RoPE row of the "Kimi K3.1 Pro vs Gemma 4 31B" page).  Queries come in the absorbed
+ * vs Kimi K3.1 Pro" page, gated-MLA row: H = 96; a cache row of 512 latent + 64 position-key
+ * values = 576 per token; q/k head dim 192, v head dim 128; query t attends to the <= 2,048
+ * rows picked for it; no rotary step, RoPE row of the "Kimi K3.1 Pro vs Gemma 4 31B" page).  Queries come in the absorbed
  * latent form (the key up-projection folded into each head's 128 no-position dims, its 64
  * key-slot dims as they are), so for query t and head h over its valid selections j:
  *   z_j = scale * q[t][h] . kv[row0[t] + idx[t][j]]                (576 values)
@@ -272,9 +289,9 @@ int dsa_idx_v32_project(const dsa_idx_weights *wt, const dsa_idx_bf16 *x, int64_
                         void *stream);
 
 /* Causal scores and top-k of one sequence for the 64-head indexer: as dsa_idx_score_topk,
- * with q [T][64][128] and w [T][64] (the keys [T][128] as before).  The 64-head score is
- * computed as the sum of its two 32-head halves (fp32).
- * Needs dsa_idx_workspace_size(DSA_IDX_OP_V32_SCORE_TOPK, T, 0, 0, topk) bytes. */
+ * with q [T][64][128] and w [T][64] (the keys [T][128] as before); all 64 heads are summed in
+ * one pass (fp32).  Needs dsa_idx_workspace_size(DSA_IDX_OP_V32_SCORE_TOPK, T, 0, 0, topk)
+ * bytes. */
 int dsa_idx_v32_score_topk(const dsa_idx_bf16 *q, const dsa_idx_bf16 *k, const dsa_idx_bf16 *w,
                            int64_t T, int topk, int32_t *idx, float *scores, void *ws,
                            size_t ws_bytes, void *stream);
@@ -282,7 +299,8 @@ int dsa_idx_v32_score_topk(const dsa_idx_bf16 *q, const dsa_idx_bf16 *k, const d
 /* Ragged prefill for the 64-head indexer: as dsa_idx_score_topk_varlen, with q [total][64][128]
  * and w [total][64].  The rotary positions are each token's position in its own sequence, so
  * project each sequence with its own pos0 (dsa_idx_v32_project).
- * Needs dsa_idx_workspace_size(DSA_IDX_OP_SCORE_TOPK_VARLEN, total, B, max_seqlen, topk) bytes. */
+ * Needs dsa_idx_workspace_size(DSA_IDX_OP_V32_SCORE_TOPK_VARLEN, total, B, max_seqlen, topk)
+ * bytes. */
 int dsa_idx_v32_score_topk_varlen(const dsa_idx_bf16 *q, const dsa_idx_bf16 *k,
                                   const dsa_idx_bf16 *w, const int32_t *cu_seqlens, int B,
                                   int max_seqlen, int64_t total, int topk, int32_t *idx,
@@ -290,7 +308,8 @@ int dsa_idx_v32_score_topk_varlen(const dsa_idx_bf16 *q, const dsa_idx_bf16 *k,
 
 /* Chunked prefill for the 64-head indexer: as dsa_idx_prefill_chunk, with q [C][64][128] and
  * w [C][64] (the queries' rotary positions prefix .. prefix + C - 1: project the chunk with
- * pos0 = prefix).  Needs dsa_idx_workspace_size(DSA_IDX_OP_PREFILL_CHUNK, C, 0, prefix, topk) bytes. */
+ * pos0 = prefix).  Needs dsa_idx_workspace_size(DSA_IDX_OP_V32_PREFILL_CHUNK, C, 0, prefix, topk)
+ * bytes. */
 int dsa_idx_v32_prefill_chunk(const dsa_idx_bf16 *q, const dsa_idx_bf16 *k, const dsa_idx_bf16 *w,
                               int64_t C, int64_t prefix, int topk, int32_t *idx, float *scores,
                               void *ws, size_t ws_bytes, void *stream);
@@ -311,6 +330,33 @@ int dsa_idx_v32_decode_fp8(const dsa_idx_bf16 *q, const dsa_idx_bf16 *w, const u
                            const float *k_scale, const int64_t *start, const int32_t *seqlens, int B,
                            int max_seqlen, int topk, int32_t *idx, float *scores, void *ws,
                            size_t ws_bytes, void *stream);
+
+/* ---------------------------------------------------------------- run-time checks
+ * The prefill score kernels order their key ring with per-wave progress counters; every wait
+ * on them is bounded (2^20 polls by default).  A wait that runs out of polls (which a correct
+ * kernel never does) lets the kernel finish, sets bit 0 of the first 32-bit word of the
+ * workspace, and the call's outputs become index -2, score NaN.
+ *
+ * dsa_idx_workspace_status reads that word after the work queued on `stream` so far: it
+ * SYNCHRONIZES the stream, then returns DSA_IDX_OK, or DSA_IDX_ESTALL with a message.  Valid
+ * on the workspaces of the prefill top-k ops (SCORE_TOPK, the VARLEN and PREFILL_CHUNK ops and
+ * their V32 forms) and of PREFILL_ROWS. */
+int dsa_idx_workspace_status(const void *ws, size_t ws_bytes, void *stream);
+
+/* Diagnostic: sets the polls allowed per ring wait of the prefill score kernels for calls
+ * launched afterwards (process-wide; values < 0 read as 0, and 0 makes every wait that is not
+ * already satisfied give up at once).  Returns the previous value.  For tests of the status
+ * report; the default needs no change. */
+int dsa_idx_set_wait_budget(int polls);
+
+/* Diagnostic phase timing of the prefill top-k calls (process-wide, off by default).  While it
+ * is on, each phase launch of a call is bracketed by two HIP events on the call's stream:
+ *   0 sample scores, 1 thresholds, 2 score and filter pass, 3 select, 4 fallback.
+ * dsa_idx_phase_timing(1) switches it on and forgets older records, (0) switches it off.
+ * dsa_idx_phase_times(ms, count, n) SYNCHRONIZES on the recorded events, writes the summed
+ * milliseconds and the number of launches of phases 0 .. n - 1, and forgets the records. */
+int dsa_idx_phase_timing(int enable);
+int dsa_idx_phase_times(double *ms, int *count, int n);
 
 #ifdef __cplusplus
 }

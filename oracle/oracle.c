@@ -6,15 +6,15 @@
  * It is a plain, slow, obviously-correct restatement of the method, written
  * from the archdiff.com compare pages for Kimi K3.1 Pro (page "Qwen3.5 vs
  * Kimi K3.1 Pro", component table):
- *   - sparse/compressed-attention row: a DSA lightning indexer per MLA layer,
- *     32 heads x 128 dims, queries projected 1,536 -> 4,096 from the query
- *     latent, one shared 128-dim key from the hidden state with a LayerNorm,
- *     per-head weights from a 7,168 -> 32 projection, scores
- *     I = sum_h w_h * ReLU(q_h . k), top 2,048 tokens kept per query;
- *   - QK-norm row: the LayerNorm sits on the indexer key;
- *   - RoPE row of the "Kimi K3.1 Pro vs Gemma 4 31B" page: the indexer uses no
- *     rotary embedding (index_rope_dim = 0);
- *   - long-context row of that page: the indexer scores the whole prefix.
+ *   - sparse/compressed-attention row: per MLA layer, H = 32, D = 128;
+ *     q = c_q W_q with W_q [1536][4096]; one key vector per token,
+ *     k = LayerNorm(x W_k) with W_k [7168][128], common to all heads;
+ *     w = x W_w with W_w [7168][32]; I = sum_h w_h * ReLU(q_h . k); each
+ *     query keeps 2,048 tokens;
+ *   - QK-norm row: the LayerNorm is applied to k;
+ *   - RoPE row of the "Kimi K3.1 Pro vs Gemma 4 31B" page: index_rope_dim = 0,
+ *     so q and k are not rotated;
+ *   - long-context row of that page: every key s <= t of the prefix is scored.
  *
  * Arithmetic: inputs are bf16 bit patterns widened exactly to double; every
  * sum runs in double in a fixed ascending order; the projected q, k, w are
@@ -40,10 +40,10 @@
  * path is the same formula on the dequantised q and k, in double.
  *
  * Sparse MLA over the selected tokens (the consumer of the selection, a next step on the
- * same pages: "Qwen3.5-397B-A17B vs Kimi K3.1 Pro" page, gated-MLA row -- 96 heads, keys and
- * values from a 512-dim latent plus a 64-dim shared key slot, 576 cached values per token,
- * q/k head dim 192, v head dim 128, each query attending only to the 2,048 tokens its layer's
- * indexer selects; no rotary step, RoPE row of the "Kimi K3.1 Pro vs Gemma 4 31B" page).  The
+ * same pages: "Qwen3.5-397B-A17B vs Kimi K3.1 Pro" page, gated-MLA row -- H = 96; cache row
+ * = 512 latent + 64 position-key values = 576 per token; q/k head dim 192, v head dim 128;
+ * query t attends to the <= 2,048 rows picked for it; no rotary step, RoPE row of the
+ * "Kimi K3.1 Pro vs Gemma 4 31B" page).  The
  * reading: queries come in the absorbed latent form (the key up-projection folded into the
  * 128 no-position dims of each head, the 64 key-slot dims as they are), so head h's logit
  * for token s is scale * q~_h . kv[s] over the 576 cached values, the softmax runs over the

@@ -17,13 +17,16 @@ __all__ = ["version", "workspace_size", "project", "score_topk", "score_topk_var
            "prefill_scores", "prefill_select", "score_row", "quantize_keys", "decode_fp8",
            "prefill_chunk", "sparse_mla", "OP_SPARSE_MLA", "HEADS", "DIM", "QLAT", "QOUT", "HIDDEN", "MAX_TOPK", "OP_PROJECT",
            "OP_SCORE_TOPK", "OP_SCORE_TOPK_VARLEN", "OP_DECODE", "OP_DECODE_FP8",
-           "OP_PREFILL_CHUNK", "DsaIdxError", "lib"]
+           "OP_PREFILL_CHUNK", "OP_PREFILL_ROWS", "OP_V32_SCORE_TOPK_VARLEN", "OP_V32_PREFILL_CHUNK",
+           "prefill_rows_workspace", "workspace_status", "set_wait_budget", "phase_timing", "phase_times", "PHASES", "ESTALL", "DsaIdxError", "lib"]
 
 HEADS, DIM, QLAT, QOUT, HIDDEN, MAX_TOPK = 32, 128, 1536, 4096, 7168, 2048
 OP_PROJECT, OP_SCORE_TOPK, OP_SCORE_TOPK_VARLEN, OP_DECODE, OP_DECODE_FP8 = 0, 1, 2, 3, 4
 OP_PREFILL_CHUNK = 5
 OP_SPARSE_MLA = 6
 OP_V32_PROJECT, OP_V32_SCORE_TOPK = 7, 8
+OP_V32_SCORE_TOPK_VARLEN, OP_V32_PREFILL_CHUNK, OP_PREFILL_ROWS = 9, 10, 11
+ESTALL = -5
 MLA_HEADS, MLA_KV, MLA_V = 96, 576, 512
 V32_HEADS, V32_QOUT, V32_THETA = 64, 8192, 10000.0   # the 64-head (DeepSeek-V3.2-shaped) indexer
 
@@ -95,6 +98,14 @@ def lib():
         L.dsa_idx_decode.argtypes = [vp, vp, vp, vp, vp, i32, i32, i32, vp, vp, vp, sz, vp]
         L.dsa_idx_quantize_keys.restype = i32
         L.dsa_idx_quantize_keys.argtypes = [vp, i64, i64, vp, vp, vp, vp]
+        L.dsa_idx_workspace_status.restype = i32
+        L.dsa_idx_workspace_status.argtypes = [vp, sz, vp]
+        L.dsa_idx_set_wait_budget.restype = i32
+        L.dsa_idx_set_wait_budget.argtypes = [i32]
+        L.dsa_idx_phase_timing.restype = i32
+        L.dsa_idx_phase_timing.argtypes = [i32]
+        L.dsa_idx_phase_times.restype = i32
+        L.dsa_idx_phase_times.argtypes = [ctypes.POINTER(ctypes.c_double), ctypes.POINTER(ctypes.c_int), i32]
         L.dsa_idx_decode_fp8.restype = i32
         L.dsa_idx_decode_fp8.argtypes = [vp, vp, vp, vp, vp, vp, i32, i32, i32, vp, vp, vp, sz, vp]
         _lib = L
@@ -278,7 +289,7 @@ def v32_score_topk_varlen(q, k, w, cu_seqlens, max_seqlen, topk=MAX_TOPK, with_s
         sc = torch.empty((total, topk), dtype=torch.float32, device=q.device) if with_scores else None
     else:
         idx, sc = out
-    nbytes = workspace_size(OP_SCORE_TOPK_VARLEN, total, B, max_seqlen, topk)
+    nbytes = workspace_size(OP_V32_SCORE_TOPK_VARLEN, total, B, max_seqlen, topk)
     ws = _workspace(nbytes, q.device, ws)
     _check("dsa_idx_v32_score_topk_varlen",
            lib().dsa_idx_v32_score_topk_varlen(_ptr(q), _ptr(k), _ptr(w), _ptr(cu_seqlens), B,
@@ -311,9 +322,47 @@ def score_topk_varlen(q, k, w, cu_seqlens, max_seqlen, topk=MAX_TOPK, with_score
     return idx, sc
 
 
+def prefill_rows_workspace(total, cu_seqlens=None, max_seqlen=0, device="cuda"):
+    """A workspace for prefill_scores / prefill_select (about 2 total^2 bytes for one
+    sequence: every causal score is stored)."""
+    B = 0 if cu_seqlens is None else cu_seqlens.numel() - 1
+    nbytes = workspace_size(OP_PROJECT if total == 0 else OP_PREFILL_ROWS, total, B, max_seqlen)
+    return torch.empty(max(nbytes, 256), dtype=torch.uint8, device=device)
+
+
+def workspace_status(ws, stream=None):
+    """Synchronizes `stream` and raises DsaIdxError (ESTALL) if a prefill call on this
+    workspace reported that a score kernel's ring wait gave up."""
+    nb = ws.numel() * ws.element_size()
+    _check("dsa_idx_workspace_status", lib().dsa_idx_workspace_status(_ptr(ws), nb, _stream(stream)))
+
+
+PHASES = ("sample", "threshold", "filter", "select", "fallback")
+
+
+def phase_timing(enable):
+    """Diagnostic: switch the event timing of the prefill top-k phases on (forgetting older
+    records) or off."""
+    _check("dsa_idx_phase_timing", lib().dsa_idx_phase_timing(1 if enable else 0))
+
+
+def phase_times():
+    """Synchronizes the recorded phase events; {phase: (total ms, launches)} since the last read."""
+    n = len(PHASES)
+    ms = (ctypes.c_double * n)()
+    cnt = (ctypes.c_int * n)()
+    _check("dsa_idx_phase_times", lib().dsa_idx_phase_times(ms, cnt, n))
+    return {PHASES[i]: (ms[i], cnt[i]) for i in range(n)}
+
+
+def set_wait_budget(polls):
+    """Diagnostic: polls per ring wait of the prefill score kernels; returns the previous value."""
+    return lib().dsa_idx_set_wait_budget(int(polls))
+
+
 def prefill_scores(q, k, w, ws, cu_seqlens=None, max_seqlen=0, stream=None):
-    """First half of score_topk / score_topk_varlen: causal fp32 scores into the workspace
-    `ws` (a uint8 tensor of workspace_size(...) bytes; see score_row for the layout)."""
+    """Every causal fp32 score I[t, s], s <= t, into the workspace `ws` (prefill_rows_workspace;
+    see score_row for the layout).  This stores the whole triangle; score_topk does not."""
     total = q.shape[0]
     _need(q, "q", torch.bfloat16, (total, HEADS, DIM))
     _need(k, "k", torch.bfloat16, (total, DIM))
@@ -327,7 +376,7 @@ def prefill_scores(q, k, w, ws, cu_seqlens=None, max_seqlen=0, stream=None):
 
 def prefill_select(total, ws, topk=MAX_TOPK, with_scores=True, cu_seqlens=None, max_seqlen=0,
                    out=None, stream=None):
-    """Second half: the top-k of the score rows that prefill_scores left in `ws`."""
+    """The row top-k of the score rows that prefill_scores left in `ws`."""
     B = 1 if cu_seqlens is None else cu_seqlens.numel() - 1
     if out is None:
         idx = torch.empty((total, topk), dtype=torch.int32, device=ws.device)
@@ -345,7 +394,7 @@ def score_row(ws, t, max_len, B=1, seq_base=0):
     """View of the t+1 causal scores of row t (of a sequence whose rows start at float offset
     seq_base of the row area) inside a prefill workspace; max_len is the T or max_seqlen of the
     call, B its sequence count (1 for the dense call)."""
-    hdr = (8 * (B + 1) + 255) // 256 * 256
+    hdr = 256 + (8 * (B + 1) + 255) // 256 * 256
     dummy = (4 * ((max_len + 127) // 128) * 128 + 255) // 256 * 256
     q, r = divmod(t, 128)
     off = seq_base + 8192 * q * (q + 1) + 128 * r * (q + 1)
@@ -369,7 +418,7 @@ def prefill_chunk(q, k, w, prefix, topk=MAX_TOPK, with_scores=True, ws=None, out
         sc = torch.empty((C, topk), dtype=torch.float32, device=q.device) if with_scores else None
     else:
         idx, sc = out
-    nbytes = workspace_size(OP_PREFILL_CHUNK, C, 0, prefix, topk)
+    nbytes = workspace_size(OP_V32_PREFILL_CHUNK if heads == V32_HEADS else OP_PREFILL_CHUNK, C, 0, prefix, topk)
     ws = _workspace(nbytes, q.device, ws)
     fn = "dsa_idx_v32_prefill_chunk" if heads == V32_HEADS else "dsa_idx_prefill_chunk"
     _check(fn, getattr(lib(), fn)(_ptr(q), _ptr(k), _ptr(w), C, int(prefix), topk, _ptr(idx),

@@ -62,14 +62,19 @@ int check_topk(int topk) {
     return ok();
 }
 
-// Longest sequence the prefill grid can address (row blocks of 32 on grid.y).
-constexpr int64_t kMaxSeq = 65535LL * 32;
+// Longest sequence (prefix + chunk, or one sequence) a prefill call accepts: key positions stay
+// below 2^24, so 32-bit element offsets within a sequence never wrap.
+constexpr int64_t kMaxWindow = 1LL << 24;
+// Longest sequence of a ragged batch (its row blocks sit on grid.y, at most 65,535; 16 rows a
+// block for 64 heads).
+constexpr int64_t kMaxVarlenSeq = 65535LL * 16;
 
-// Prefill workspace: [sequence bases: int64 x (B + 1)] [dummy row] [triangular score rows],
-// each part a multiple of 256 bytes.
 size_t round256(size_t b) { return (b + 255u) & ~(size_t)255u; }
-size_t ws_hdr(int B) { return round256(8u * (size_t)(B + 1)); }
-size_t ws_dummy(int64_t max_len) {
+
+// Raw causal score rows (dsa_idx_prefill_scores / dsa_idx_prefill_select): [status word, 256 B]
+// [sequence bases: int64 x (B + 1)] [dummy row] [triangular rows], each part 256-byte aligned.
+size_t rows_hdr(int B) { return 256u + round256(8u * (size_t)(B + 1)); }
+size_t rows_dummy(int64_t max_len) {
     const int64_t q = dsaidx::kRowQuant;
     return round256(4u * (size_t)(((max_len + q - 1) / q) * q));
 }
@@ -88,19 +93,15 @@ int64_t varlen_score_floats(int64_t total, int B, int64_t max_len) {
     if (k < B) sq += (rem + Q) * (rem + Q) + (int64_t)(B - k - 1) * Q * Q;
     return ((sq / 2 + Q - 1) / Q) * Q;
 }
+size_t ws_rows(const bool varlen, int64_t total, int B, int64_t max_seqlen) {
+    if (!varlen) return rows_hdr(1) + rows_dummy(total) + 4u * (size_t)dsaidx::tri_row_offset(total);
+    return rows_hdr(B) + rows_dummy(max_seqlen) + 4u * (size_t)varlen_score_floats(total, B, max_seqlen);
+}
 
-size_t ws_score_topk(int64_t T) {
-    return ws_hdr(1) + ws_dummy(T) + 4u * (size_t)dsaidx::tri_row_offset(T);
-}
-// chunk of C query rows at positions prefix .. prefix + C - 1 of one sequence
-size_t ws_prefill_chunk(int64_t C, int64_t prefix) {
-    return ws_hdr(1) + ws_dummy(prefix + C) +
-           4u * (size_t)(dsaidx::tri_row_offset(prefix + C) - dsaidx::tri_row_offset(prefix));
-}
-// Longest sequence (prefix + chunk) a chunked prefill call accepts.
-constexpr int64_t kMaxWindow = 1LL << 24;
-size_t ws_score_topk_varlen(int64_t total, int B, int max_seqlen) {
-    return ws_hdr(B) + ws_dummy(max_seqlen) + 4u * (size_t)varlen_score_floats(total, B, max_seqlen);
+// Top-k workspace of a prefill call (see prefill_plan): linear in the rows.
+size_t ws_topk(int heads, bool varlen, int64_t rows, int B, int64_t max_len, int64_t pos0) {
+    if (rows == 0) return 0;
+    return dsaidx::prefill_plan(heads, varlen, rows, B, max_len, pos0).bytes;
 }
 
 size_t ws_decode(int B, int max_seqlen) { return dsaidx::decode_workspace(B, max_seqlen, false); }
@@ -122,41 +123,46 @@ int dsa_idx_workspace_size(int op, int64_t total_tokens, int B, int max_seqlen, 
             if (total_tokens < 0) return fail(DSA_IDX_EINVAL, "T=%lld < 0", (long long)total_tokens);
             *bytes = dsaidx::project_workspace(total_tokens);
             return ok();
-        case DSA_IDX_OP_SCORE_TOPK: {
+        case DSA_IDX_OP_SCORE_TOPK:
+        case DSA_IDX_OP_V32_SCORE_TOPK: {
             if (total_tokens < 0) return fail(DSA_IDX_EINVAL, "T=%lld < 0", (long long)total_tokens);
             int r = check_topk(topk);
             if (r) return r;
-            *bytes = ws_score_topk(total_tokens);
+            *bytes = ws_topk(op == DSA_IDX_OP_SCORE_TOPK ? 32 : 64, false, total_tokens, 1, total_tokens, 0);
             return ok();
         }
-        case DSA_IDX_OP_SCORE_TOPK_VARLEN: {
+        case DSA_IDX_OP_SCORE_TOPK_VARLEN:
+        case DSA_IDX_OP_V32_SCORE_TOPK_VARLEN: {
             if (total_tokens < 0 || B < 0 || max_seqlen < 0)
                 return fail(DSA_IDX_EINVAL, "total=%lld B=%d max_seqlen=%d must be >= 0",
                             (long long)total_tokens, B, max_seqlen);
             int r = check_topk(topk);
             if (r) return r;
-            *bytes = ws_score_topk_varlen(total_tokens, B, max_seqlen);
+            *bytes = B == 0 || max_seqlen == 0
+                         ? 0
+                         : ws_topk(op == DSA_IDX_OP_SCORE_TOPK_VARLEN ? 32 : 64, true, total_tokens, B, max_seqlen, 0);
             return ok();
         }
-        case DSA_IDX_OP_PREFILL_CHUNK: {
+        case DSA_IDX_OP_PREFILL_CHUNK:
+        case DSA_IDX_OP_V32_PREFILL_CHUNK: {
             if (total_tokens < 0 || max_seqlen < 0)
                 return fail(DSA_IDX_EINVAL, "C=%lld prefix=%d must be >= 0", (long long)total_tokens, max_seqlen);
             int r = check_topk(topk);
             if (r) return r;
-            *bytes = total_tokens == 0 ? 0 : ws_prefill_chunk(total_tokens, max_seqlen);
+            *bytes = ws_topk(op == DSA_IDX_OP_PREFILL_CHUNK ? 32 : 64, false, total_tokens, 1, total_tokens, max_seqlen);
+            return ok();
+        }
+        case DSA_IDX_OP_PREFILL_ROWS: {
+            if (total_tokens < 0 || B < 0 || max_seqlen < 0)
+                return fail(DSA_IDX_EINVAL, "total=%lld B=%d max_seqlen=%d must be >= 0",
+                            (long long)total_tokens, B, max_seqlen);
+            *bytes = total_tokens == 0 ? 0 : ws_rows(B > 0, total_tokens, B, max_seqlen);
             return ok();
         }
         case DSA_IDX_OP_V32_PROJECT:
             if (total_tokens < 0) return fail(DSA_IDX_EINVAL, "T=%lld < 0", (long long)total_tokens);
             *bytes = dsaidx::project_workspace(total_tokens);   // the halves reuse it in turn
             return ok();
-        case DSA_IDX_OP_V32_SCORE_TOPK: {
-            if (total_tokens < 0) return fail(DSA_IDX_EINVAL, "T=%lld < 0", (long long)total_tokens);
-            int r = check_topk(topk);
-            if (r) return r;
-            *bytes = ws_score_topk(total_tokens);
-            return ok();
-        }
         case DSA_IDX_OP_SPARSE_MLA: {
             if (total_tokens < 0) return fail(DSA_IDX_EINVAL, "T=%lld < 0", (long long)total_tokens);
             int r = check_topk(topk);
@@ -208,69 +214,146 @@ int dsa_idx_project(const dsa_idx_weights *wt, const dsa_idx_bf16 *x, int64_t ld
 }
 
 
-// Workspace parts of a prefill call.  cu == nullptr: one sequence of `total` tokens.
-struct PrefillWs {
+// ---------------------------------------------------------------- prefill
+// Shape checks shared by the prefill entries.  varlen: B sequences packed back to back
+// (longest max_seqlen); else one sequence of `rows` tokens at positions pos0 ...
+static int prefill_args(bool varlen, const int32_t *cu, int B, int max_seqlen, int64_t rows, int64_t pos0) {
+    if (rows < 0 || pos0 < 0) return fail(DSA_IDX_EINVAL, "rows=%lld pos0=%lld must be >= 0", (long long)rows, (long long)pos0);
+    if (varlen) {
+        if (B < 0 || max_seqlen < 0)
+            return fail(DSA_IDX_EINVAL, "B=%d max_seqlen=%d must be >= 0", B, max_seqlen);
+        if (B > 0 && !cu) return fail(DSA_IDX_EINVAL, "cu_seqlens is NULL");
+        if (B == 0 && rows > 0) return fail(DSA_IDX_EINVAL, "total=%lld with B=0", (long long)rows);
+        if (B > 65535) return fail(DSA_IDX_EUNSUPPORTED, "B=%d above 65535", B);
+        if (max_seqlen > kMaxVarlenSeq)
+            return fail(DSA_IDX_EUNSUPPORTED, "max_seqlen=%d above %lld", max_seqlen, (long long)kMaxVarlenSeq);
+        if (rows > (int64_t)B * max_seqlen)
+            return fail(DSA_IDX_EINVAL, "total=%lld above B * max_seqlen", (long long)rows);
+    } else if (pos0 + rows > kMaxWindow) {
+        return fail(DSA_IDX_EUNSUPPORTED, "sequence of %lld keys above %lld", (long long)(pos0 + rows),
+                    (long long)kMaxWindow);
+    }
+    return ok();
+}
+
+static bool prefill_empty(bool varlen, int B, int max_seqlen, int64_t rows) {
+    return rows == 0 || (varlen && (B == 0 || max_seqlen == 0));
+}
+
+// Scores and top-k of every row, workspace linear in the rows (heads: 32, or 64).
+static int prefill_topk_impl(const dsa_idx_bf16 *q, const dsa_idx_bf16 *k, const dsa_idx_bf16 *w, bool varlen,
+                             const int32_t *cu, int B, int max_seqlen, int64_t rows, int64_t pos0, int topk,
+                             int32_t *idx, float *scores, void *ws, size_t ws_bytes, void *stream, int heads) {
+    int r = check_topk(topk);
+    if (r) return r;
+    r = prefill_args(varlen, cu, B, max_seqlen, rows, pos0);
+    if (r || prefill_empty(varlen, B, max_seqlen, rows)) return r;
+    if (!q || !k || !w || !idx) return fail(DSA_IDX_EINVAL, "a tensor pointer is NULL");
+    if (!aligned16(q) || !aligned16(k) || !aligned16(w))
+        return fail(DSA_IDX_EINVAL, "q, k and w must be 16-byte aligned");
+    const dsaidx::PrefillPlan plan =
+        dsaidx::prefill_plan(heads, varlen, rows, varlen ? B : 1, varlen ? max_seqlen : rows, pos0);
+    if (!ws || ws_bytes < plan.bytes)
+        return fail(DSA_IDX_EWORKSPACE, "workspace %zu bytes < %zu needed", ws ? ws_bytes : (size_t)0, plan.bytes);
+    if (!aligned16(ws)) return fail(DSA_IDX_EINVAL, "workspace must be 16-byte aligned");
+    r = check_device();
+    if (r) return r;
+    hipError_t e = dsaidx::launch_prefill_topk(plan, q, k, w, varlen ? cu : nullptr, topk, idx, scores, ws,
+                                               reinterpret_cast<hipStream_t>(stream));
+    if (e != hipSuccess) return hip_fail("prefill launch", e);
+    return ok();
+}
+
+int dsa_idx_score_topk(const dsa_idx_bf16 *q, const dsa_idx_bf16 *k, const dsa_idx_bf16 *w,
+                       int64_t T, int topk, int32_t *idx, float *scores, void *ws,
+                       size_t ws_bytes, void *stream) {
+    return prefill_topk_impl(q, k, w, false, nullptr, 1, 0, T, 0, topk, idx, scores, ws, ws_bytes, stream,
+                             DSA_IDX_HEADS);
+}
+
+int dsa_idx_score_topk_varlen(const dsa_idx_bf16 *q, const dsa_idx_bf16 *k,
+                              const dsa_idx_bf16 *w, const int32_t *cu_seqlens, int B,
+                              int max_seqlen, int64_t total, int topk, int32_t *idx,
+                              float *scores, void *ws, size_t ws_bytes, void *stream) {
+    return prefill_topk_impl(q, k, w, true, cu_seqlens, B, max_seqlen, total, 0, topk, idx, scores, ws, ws_bytes,
+                             stream, DSA_IDX_HEADS);
+}
+
+int dsa_idx_prefill_chunk(const dsa_idx_bf16 *q, const dsa_idx_bf16 *k, const dsa_idx_bf16 *w,
+                          int64_t C, int64_t prefix, int topk, int32_t *idx, float *scores,
+                          void *ws, size_t ws_bytes, void *stream) {
+    return prefill_topk_impl(q, k, w, false, nullptr, 1, 0, C, prefix, topk, idx, scores, ws, ws_bytes, stream,
+                             DSA_IDX_HEADS);
+}
+
+int dsa_idx_v32_score_topk(const dsa_idx_bf16 *q, const dsa_idx_bf16 *k, const dsa_idx_bf16 *w,
+                           int64_t T, int topk, int32_t *idx, float *scores, void *ws,
+                           size_t ws_bytes, void *stream) {
+    return prefill_topk_impl(q, k, w, false, nullptr, 1, 0, T, 0, topk, idx, scores, ws, ws_bytes, stream,
+                             DSA_IDX_V32_HEADS);
+}
+
+int dsa_idx_v32_score_topk_varlen(const dsa_idx_bf16 *q, const dsa_idx_bf16 *k,
+                                  const dsa_idx_bf16 *w, const int32_t *cu_seqlens, int B,
+                                  int max_seqlen, int64_t total, int topk, int32_t *idx,
+                                  float *scores, void *ws, size_t ws_bytes, void *stream) {
+    return prefill_topk_impl(q, k, w, true, cu_seqlens, B, max_seqlen, total, 0, topk, idx, scores, ws, ws_bytes,
+                             stream, DSA_IDX_V32_HEADS);
+}
+
+int dsa_idx_v32_prefill_chunk(const dsa_idx_bf16 *q, const dsa_idx_bf16 *k, const dsa_idx_bf16 *w,
+                              int64_t C, int64_t prefix, int topk, int32_t *idx, float *scores,
+                              void *ws, size_t ws_bytes, void *stream) {
+    return prefill_topk_impl(q, k, w, false, nullptr, 1, 0, C, prefix, topk, idx, scores, ws, ws_bytes, stream,
+                             DSA_IDX_V32_HEADS);
+}
+
+// ---- raw causal score rows (32 heads) and the row top-k over them
+struct RowsWs {
+    uint32_t *status;
     int64_t *base;
     float *dummy;
     float *rows;
 };
 
-static int64_t prefill_max_len(const int32_t *cu, int max_seqlen, int64_t total) {
-    return cu ? (int64_t)max_seqlen : total;
+static RowsWs rows_ws(bool varlen, int B, int max_seqlen, int64_t total, void *ws) {
+    const int Bh = varlen ? B : 1;
+    char *p = static_cast<char *>(ws);
+    RowsWs r;
+    r.status = reinterpret_cast<uint32_t *>(p);
+    r.base = reinterpret_cast<int64_t *>(p + 256);
+    r.dummy = reinterpret_cast<float *>(p + rows_hdr(Bh));
+    r.rows = reinterpret_cast<float *>(p + rows_hdr(Bh) + rows_dummy(varlen ? max_seqlen : total));
+    return r;
 }
 
-static int prefill_check(const int32_t *cu, int B, int max_seqlen, int64_t total, void *ws,
-                         size_t ws_bytes, size_t &need) {
-    if (total < 0) return fail(DSA_IDX_EINVAL, "total=%lld < 0", (long long)total);
-    if (cu) {
-        if (B < 0 || max_seqlen < 0)
-            return fail(DSA_IDX_EINVAL, "B=%d max_seqlen=%d must be >= 0", B, max_seqlen);
-        if (B > 65535) return fail(DSA_IDX_EUNSUPPORTED, "B=%d above 65535", B);
-        if (max_seqlen > kMaxSeq)
-            return fail(DSA_IDX_EUNSUPPORTED, "max_seqlen=%d above %lld", max_seqlen, (long long)kMaxSeq);
-        if (total > (int64_t)B * max_seqlen)
-            return fail(DSA_IDX_EINVAL, "total=%lld above B * max_seqlen", (long long)total);
-        need = ws_score_topk_varlen(total, B, max_seqlen);
-    } else {
-        if (total > kMaxSeq) return fail(DSA_IDX_EUNSUPPORTED, "T=%lld above %lld", (long long)total, (long long)kMaxSeq);
-        need = ws_score_topk(total);
-    }
-    if (total == 0 || (cu && (B == 0 || max_seqlen == 0))) return ok();
+static int rows_check(bool varlen, const int32_t *cu, int B, int max_seqlen, int64_t total, void *ws,
+                      size_t ws_bytes) {
+    int r = prefill_args(varlen, cu, B, max_seqlen, total, 0);
+    if (r || prefill_empty(varlen, B, max_seqlen, total)) return r;
+    if (varlen && max_seqlen > 65535LL * 32)
+        return fail(DSA_IDX_EUNSUPPORTED, "max_seqlen=%d above %lld", max_seqlen, 65535LL * 32);
+    const size_t need = ws_rows(varlen, total, B, max_seqlen);
     if (!ws || ws_bytes < need)
         return fail(DSA_IDX_EWORKSPACE, "workspace %zu bytes < %zu needed", ws ? ws_bytes : (size_t)0, need);
     if (!aligned16(ws)) return fail(DSA_IDX_EINVAL, "workspace must be 16-byte aligned");
     return ok();
 }
 
-static PrefillWs prefill_ws(const int32_t *cu, int B, int max_seqlen, int64_t total, void *ws) {
-    const int Bh = cu ? B : 1;
-    char *p = static_cast<char *>(ws);
-    PrefillWs r;
-    r.base = reinterpret_cast<int64_t *>(p);
-    r.dummy = reinterpret_cast<float *>(p + ws_hdr(Bh));
-    r.rows = reinterpret_cast<float *>(p + ws_hdr(Bh) + ws_dummy(prefill_max_len(cu, max_seqlen, total)));
-    return r;
-}
-
-static bool prefill_empty(const int32_t *cu, int B, int max_seqlen, int64_t total) {
-    return total == 0 || (cu && (B == 0 || max_seqlen == 0));
-}
-
 int dsa_idx_prefill_scores(const dsa_idx_bf16 *q, const dsa_idx_bf16 *k, const dsa_idx_bf16 *w,
                            const int32_t *cu_seqlens, int B, int max_seqlen, int64_t total,
                            void *ws, size_t ws_bytes, void *stream) {
-    size_t need = 0;
-    int r = prefill_check(cu_seqlens, B, max_seqlen, total, ws, ws_bytes, need);
-    if (r || prefill_empty(cu_seqlens, B, max_seqlen, total)) return r;
+    const bool varlen = cu_seqlens != nullptr;
+    int r = rows_check(varlen, cu_seqlens, B, max_seqlen, total, ws, ws_bytes);
+    if (r || prefill_empty(varlen, B, max_seqlen, total)) return r;
     if (!q || !k || !w) return fail(DSA_IDX_EINVAL, "a tensor pointer is NULL");
     if (!aligned16(q) || !aligned16(k) || !aligned16(w))
         return fail(DSA_IDX_EINVAL, "q, k and w must be 16-byte aligned");
     r = check_device();
     if (r) return r;
-    const PrefillWs p = prefill_ws(cu_seqlens, B, max_seqlen, total, ws);
-    hipError_t e = dsaidx::launch_scores(q, k, w, cu_seqlens, cu_seqlens ? B : 1,
-                                         prefill_max_len(cu_seqlens, max_seqlen, total), total, 0, p.base,
-                                         p.rows, p.dummy, reinterpret_cast<hipStream_t>(stream));
+    const RowsWs p = rows_ws(varlen, B, max_seqlen, total, ws);
+    hipError_t e = dsaidx::launch_scores(q, k, w, cu_seqlens, varlen ? B : 1, varlen ? max_seqlen : total, total, 0,
+                                         p.base, p.rows, p.dummy, p.status, reinterpret_cast<hipStream_t>(stream));
     if (e != hipSuccess) return hip_fail("scores launch", e);
     return ok();
 }
@@ -280,34 +363,56 @@ int dsa_idx_prefill_select(const int32_t *cu_seqlens, int B, int max_seqlen, int
                            void *stream) {
     int r = check_topk(topk);
     if (r) return r;
-    size_t need = 0;
-    r = prefill_check(cu_seqlens, B, max_seqlen, total, ws, ws_bytes, need);
-    if (r || prefill_empty(cu_seqlens, B, max_seqlen, total)) return r;
+    const bool varlen = cu_seqlens != nullptr;
+    r = rows_check(varlen, cu_seqlens, B, max_seqlen, total, ws, ws_bytes);
+    if (r || prefill_empty(varlen, B, max_seqlen, total)) return r;
     if (!idx) return fail(DSA_IDX_EINVAL, "idx is NULL");
     r = check_device();
     if (r) return r;
-    const PrefillWs p = prefill_ws(cu_seqlens, B, max_seqlen, total, ws);
-    hipError_t e = dsaidx::launch_row_topk_prefill(p.rows, cu_seqlens, p.base, cu_seqlens ? B : 1,
-                                                   prefill_max_len(cu_seqlens, max_seqlen, total), 0,
-                                                   total, topk, idx, scores,
-                                                   reinterpret_cast<hipStream_t>(stream));
+    const RowsWs p = rows_ws(varlen, B, max_seqlen, total, ws);
+    hipError_t e = dsaidx::launch_row_topk_prefill(p.rows, cu_seqlens, p.base, varlen ? B : 1,
+                                                   varlen ? max_seqlen : total, 0, total, topk, idx, scores,
+                                                   p.status, reinterpret_cast<hipStream_t>(stream));
     if (e != hipSuccess) return hip_fail("row top-k launch", e);
     return ok();
 }
 
-int dsa_idx_score_topk(const dsa_idx_bf16 *q, const dsa_idx_bf16 *k, const dsa_idx_bf16 *w,
-                       int64_t T, int topk, int32_t *idx, float *scores, void *ws,
-                       size_t ws_bytes, void *stream) {
-    if (T < 0) return fail(DSA_IDX_EINVAL, "T=%lld < 0", (long long)T);
-    int r = check_topk(topk);
-    if (r) return r;
-    if (T > 0 && (!q || !k || !w || !idx)) return fail(DSA_IDX_EINVAL, "a tensor pointer is NULL");
-    size_t need = 0;
-    r = prefill_check(nullptr, 1, 0, T, ws, ws_bytes, need);
-    if (r || T == 0) return r;
-    r = dsa_idx_prefill_scores(q, k, w, nullptr, 1, 0, T, ws, ws_bytes, stream);
-    if (r) return r;
-    return dsa_idx_prefill_select(nullptr, 1, 0, T, topk, idx, scores, ws, ws_bytes, stream);
+int dsa_idx_workspace_status(const void *ws, size_t ws_bytes, void *stream) {
+    if (!ws || ws_bytes < 4) return fail(DSA_IDX_EINVAL, "workspace is NULL or smaller than its status word");
+    uint32_t st = 0;
+    const hipStream_t s = reinterpret_cast<hipStream_t>(stream);
+    hipError_t e = hipMemcpyAsync(&st, ws, sizeof(st), hipMemcpyDeviceToHost, s);
+    if (e != hipSuccess) return hip_fail("status copy", e);
+    e = hipStreamSynchronize(s);
+    if (e != hipSuccess) return hip_fail("stream synchronize", e);
+    if (st & 1u)
+        return fail(DSA_IDX_ESTALL,
+                    "a score kernel's wait on its key ring ran out of polls; that call's outputs are invalid "
+                    "(indices -2, scores NaN)");
+    return ok();
+}
+
+int dsa_idx_phase_timing(int enable) {
+    if (enable) {
+        double ms[dsaidx::kPhases];
+        int cnt[dsaidx::kPhases];
+        (void)dsaidx::prefill_phase_times(ms, cnt, dsaidx::kPhases);   // forget older records
+    }
+    dsaidx::prefill_phase_timing(enable != 0);
+    return ok();
+}
+
+int dsa_idx_phase_times(double *ms, int *count, int n) {
+    if (!ms || !count || n < 0) return fail(DSA_IDX_EINVAL, "ms and count must be non-NULL, n >= 0");
+    hipError_t e = dsaidx::prefill_phase_times(ms, count, n);
+    if (e != hipSuccess) return hip_fail("phase events", e);
+    return ok();
+}
+
+int dsa_idx_set_wait_budget(int polls) {
+    const int prev = dsaidx::prefill_wait_budget();
+    dsaidx::prefill_set_wait_budget(polls);
+    return prev;
 }
 
 int dsa_idx_v32_project(const dsa_idx_weights *wt, const dsa_idx_bf16 *x, int64_t ldx,
@@ -352,133 +457,6 @@ int dsa_idx_v32_project(const dsa_idx_weights *wt, const dsa_idx_bf16 *x, int64_
     return ok();
 }
 
-int dsa_idx_v32_score_topk(const dsa_idx_bf16 *q, const dsa_idx_bf16 *k, const dsa_idx_bf16 *w,
-                           int64_t T, int topk, int32_t *idx, float *scores, void *ws,
-                           size_t ws_bytes, void *stream) {
-    if (T < 0) return fail(DSA_IDX_EINVAL, "T=%lld < 0", (long long)T);
-    int r = check_topk(topk);
-    if (r) return r;
-    if (T > 0 && (!q || !k || !w || !idx)) return fail(DSA_IDX_EINVAL, "a tensor pointer is NULL");
-    size_t need = 0;
-    r = prefill_check(nullptr, 1, 0, T, ws, ws_bytes, need);
-    if (r || T == 0) return r;
-    if (!aligned16(q) || !aligned16(k) || !aligned16(w))
-        return fail(DSA_IDX_EINVAL, "q, k and w must be 16-byte aligned");
-    r = check_device();
-    if (r) return r;
-    const PrefillWs p = prefill_ws(nullptr, 1, 0, T, ws);
-    const hipStream_t st = reinterpret_cast<hipStream_t>(stream);
-    // heads 0..31 write the score rows, heads 32..63 add to them
-    for (int half = 0; half < 2; ++half) {
-        hipError_t e = dsaidx::launch_scores_ex(q + half * DSA_IDX_QOUT, DSA_IDX_V32_QOUT, k, w + half * DSA_IDX_HEADS,
-                                                DSA_IDX_V32_HEADS, half == 1, nullptr, 1, T, T, 0, p.base, p.rows,
-                                                p.dummy, st);
-        if (e != hipSuccess) return hip_fail("scores launch", e);
-    }
-    return dsa_idx_prefill_select(nullptr, 1, 0, T, topk, idx, scores, ws, ws_bytes, stream);
-}
-
-int dsa_idx_v32_score_topk_varlen(const dsa_idx_bf16 *q, const dsa_idx_bf16 *k,
-                                  const dsa_idx_bf16 *w, const int32_t *cu_seqlens, int B,
-                                  int max_seqlen, int64_t total, int topk, int32_t *idx,
-                                  float *scores, void *ws, size_t ws_bytes, void *stream) {
-    if (B < 0 || max_seqlen < 0 || total < 0)
-        return fail(DSA_IDX_EINVAL, "B=%d max_seqlen=%d total=%lld must be >= 0", B, max_seqlen, (long long)total);
-    if (B > 0 && !cu_seqlens) return fail(DSA_IDX_EINVAL, "cu_seqlens is NULL");
-    int r = check_topk(topk);
-    if (r) return r;
-    if (total > 0 && (!q || !k || !w || !idx)) return fail(DSA_IDX_EINVAL, "a tensor pointer is NULL");
-    if (B == 0) return total == 0 ? ok() : fail(DSA_IDX_EINVAL, "total=%lld with B=0", (long long)total);
-    size_t need = 0;
-    r = prefill_check(cu_seqlens, B, max_seqlen, total, ws, ws_bytes, need);
-    if (r || prefill_empty(cu_seqlens, B, max_seqlen, total)) return r;
-    if (!aligned16(q) || !aligned16(k) || !aligned16(w))
-        return fail(DSA_IDX_EINVAL, "q, k and w must be 16-byte aligned");
-    r = check_device();
-    if (r) return r;
-    const PrefillWs p = prefill_ws(cu_seqlens, B, max_seqlen, total, ws);
-    const hipStream_t st = reinterpret_cast<hipStream_t>(stream);
-    // heads 0..31 write the score rows, heads 32..63 add to them
-    for (int half = 0; half < 2; ++half) {
-        hipError_t e = dsaidx::launch_scores_ex(q + half * DSA_IDX_QOUT, DSA_IDX_V32_QOUT, k, w + half * DSA_IDX_HEADS,
-                                                DSA_IDX_V32_HEADS, half == 1, cu_seqlens, B, max_seqlen, total, 0,
-                                                p.base, p.rows, p.dummy, st);
-        if (e != hipSuccess) return hip_fail("scores launch", e);
-    }
-    return dsa_idx_prefill_select(cu_seqlens, B, max_seqlen, total, topk, idx, scores, ws, ws_bytes, stream);
-}
-
-int dsa_idx_score_topk_varlen(const dsa_idx_bf16 *q, const dsa_idx_bf16 *k,
-                              const dsa_idx_bf16 *w, const int32_t *cu_seqlens, int B,
-                              int max_seqlen, int64_t total, int topk, int32_t *idx,
-                              float *scores, void *ws, size_t ws_bytes, void *stream) {
-    if (B < 0 || max_seqlen < 0 || total < 0)
-        return fail(DSA_IDX_EINVAL, "B=%d max_seqlen=%d total=%lld must be >= 0", B, max_seqlen, (long long)total);
-    if (B > 0 && !cu_seqlens) return fail(DSA_IDX_EINVAL, "cu_seqlens is NULL");
-    int r = check_topk(topk);
-    if (r) return r;
-    if (total > 0 && (!q || !k || !w || !idx)) return fail(DSA_IDX_EINVAL, "a tensor pointer is NULL");
-    if (B == 0) return total == 0 ? ok() : fail(DSA_IDX_EINVAL, "total=%lld with B=0", (long long)total);
-    size_t need = 0;
-    r = prefill_check(cu_seqlens, B, max_seqlen, total, ws, ws_bytes, need);
-    if (r || prefill_empty(cu_seqlens, B, max_seqlen, total)) return r;
-    r = dsa_idx_prefill_scores(q, k, w, cu_seqlens, B, max_seqlen, total, ws, ws_bytes, stream);
-    if (r) return r;
-    return dsa_idx_prefill_select(cu_seqlens, B, max_seqlen, total, topk, idx, scores, ws, ws_bytes,
-                                  stream);
-}
-
-// A chunk of C queries against its whole prefix, with heads/32 scoring passes of 32 heads each
-// (q rows heads x 128, w rows heads), the later ones adding to the score rows.
-static int prefill_chunk_impl(const dsa_idx_bf16 *q, const dsa_idx_bf16 *k, const dsa_idx_bf16 *w,
-                              int64_t C, int64_t prefix, int topk, int32_t *idx, float *scores,
-                              void *ws, size_t ws_bytes, void *stream, int heads) {
-    if (C < 0 || prefix < 0)
-        return fail(DSA_IDX_EINVAL, "C=%lld prefix=%lld must be >= 0", (long long)C, (long long)prefix);
-    int r = check_topk(topk);
-    if (r) return r;
-    if (C == 0) return ok();
-    if (!q || !k || !w || !idx) return fail(DSA_IDX_EINVAL, "a tensor pointer is NULL");
-    if (!aligned16(q) || !aligned16(k) || !aligned16(w))
-        return fail(DSA_IDX_EINVAL, "q, k and w must be 16-byte aligned");
-    if (C > kMaxSeq) return fail(DSA_IDX_EUNSUPPORTED, "C=%lld above %lld", (long long)C, (long long)kMaxSeq);
-    if (prefix + C > kMaxWindow)
-        return fail(DSA_IDX_EUNSUPPORTED, "prefix + C = %lld above %lld", (long long)(prefix + C),
-                    (long long)kMaxWindow);
-    const size_t need = ws_prefill_chunk(C, prefix);
-    if (!ws || ws_bytes < need)
-        return fail(DSA_IDX_EWORKSPACE, "workspace %zu bytes < %zu needed", ws ? ws_bytes : (size_t)0, need);
-    if (!aligned16(ws)) return fail(DSA_IDX_EINVAL, "workspace must be 16-byte aligned");
-    r = check_device();
-    if (r) return r;
-    char *wsb = static_cast<char *>(ws);
-    int64_t *base = reinterpret_cast<int64_t *>(wsb);
-    float *dummy = reinterpret_cast<float *>(wsb + ws_hdr(1));
-    float *rows = reinterpret_cast<float *>(wsb + ws_hdr(1) + ws_dummy(prefix + C));
-    const hipStream_t st = reinterpret_cast<hipStream_t>(stream);
-    hipError_t e = hipSuccess;
-    for (int half = 0; half < heads / DSA_IDX_HEADS; ++half) {
-        e = dsaidx::launch_scores_ex(q + half * DSA_IDX_QOUT, (int64_t)heads * DSA_IDX_DIM, k, w + half * DSA_IDX_HEADS,
-                                     heads, half > 0, nullptr, 1, C, C, prefix, base, rows, dummy, st);
-        if (e != hipSuccess) return hip_fail("scores launch", e);
-    }
-    e = dsaidx::launch_row_topk_prefill(rows, nullptr, base, 1, C, prefix, C, topk, idx, scores, st);
-    if (e != hipSuccess) return hip_fail("row top-k launch", e);
-    return ok();
-}
-
-int dsa_idx_prefill_chunk(const dsa_idx_bf16 *q, const dsa_idx_bf16 *k, const dsa_idx_bf16 *w,
-                          int64_t C, int64_t prefix, int topk, int32_t *idx, float *scores,
-                          void *ws, size_t ws_bytes, void *stream) {
-    return prefill_chunk_impl(q, k, w, C, prefix, topk, idx, scores, ws, ws_bytes, stream, DSA_IDX_HEADS);
-}
-
-int dsa_idx_v32_prefill_chunk(const dsa_idx_bf16 *q, const dsa_idx_bf16 *k, const dsa_idx_bf16 *w,
-                              int64_t C, int64_t prefix, int topk, int32_t *idx, float *scores,
-                              void *ws, size_t ws_bytes, void *stream) {
-    return prefill_chunk_impl(q, k, w, C, prefix, topk, idx, scores, ws, ws_bytes, stream, DSA_IDX_V32_HEADS);
-}
-
 int dsa_idx_sparse_mla(const dsa_idx_bf16 *q, const dsa_idx_bf16 *kv, const int32_t *idx,
                        const int64_t *row0, int64_t T, int topk, float scale, dsa_idx_bf16 *o,
                        float *lse, void *ws, size_t ws_bytes, void *stream) {
@@ -516,6 +494,8 @@ static int decode_impl(const dsa_idx_bf16 *q, const dsa_idx_bf16 *w, const dsa_i
     if (!aligned16(q) || !aligned16(w) || !aligned16(k_cache))
         return fail(DSA_IDX_EINVAL, "q, w and k_cache must be 16-byte aligned");
     if (B > 65535) return fail(DSA_IDX_EUNSUPPORTED, "B=%d above 65535", B);
+    if (max_seqlen > kMaxWindow)
+        return fail(DSA_IDX_EUNSUPPORTED, "max_seqlen=%d above %lld", max_seqlen, (long long)kMaxWindow);
     const size_t need = ws_decode(B, max_seqlen);
     if (!ws || ws_bytes < need)
         return fail(DSA_IDX_EWORKSPACE, "workspace %zu bytes < %zu needed", ws ? ws_bytes : (size_t)0, need);
@@ -575,6 +555,8 @@ static int decode_fp8_impl(const dsa_idx_bf16 *q, const dsa_idx_bf16 *w, const u
     if (!aligned16(q) || !aligned16(w) || !aligned16(k8))
         return fail(DSA_IDX_EINVAL, "q, w and k8 must be 16-byte aligned");
     if (B > 65535) return fail(DSA_IDX_EUNSUPPORTED, "B=%d above 65535", B);
+    if (max_seqlen > kMaxWindow)
+        return fail(DSA_IDX_EUNSUPPORTED, "max_seqlen=%d above %lld", max_seqlen, (long long)kMaxWindow);
     const size_t need = ws_decode_fp8(B, max_seqlen);
     if (!ws || ws_bytes < need)
         return fail(DSA_IDX_EWORKSPACE, "workspace %zu bytes < %zu needed", ws ? ws_bytes : (size_t)0, need);

@@ -13,6 +13,31 @@ constexpr int kQOut = 4096;
 constexpr int kHidden = 7168;
 constexpr int kMaxTopk = 2048;
 
+// ---------------------------------------------------------------- prefill sampling
+// A prefill row samples one key per stratum of kSampleStride consecutive keys (at an offset
+// inside the stratum picked by an integer hash of the stratum), to place its threshold; rows
+// of at most kAllKeys keys keep every key as a candidate.  The threshold is the r-th largest
+// sample score with r = E + kThetaMargin (sqrt(E) + 1), E the expected number of samples at or
+// above the row's topk-th score.
+constexpr int kSampleStride = 32;
+constexpr int64_t kAllKeys = 4096;
+constexpr double kThetaMargin = 6.0;
+
+// The "lowbias32" integer mixer (C. Wellons' hash prospector).
+__host__ __device__ inline uint32_t mix32(uint32_t x) {
+    x ^= x >> 16;
+    x *= 0x7FEB352Du;
+    x ^= x >> 15;
+    x *= 0x846CA68Bu;
+    x ^= x >> 16;
+    return x;
+}
+
+// Offset of stratum j's sampled key inside the stratum.
+__host__ __device__ inline int sample_offset(int64_t j) {
+    return (int)(mix32((uint32_t)j + 0x9E3779B9u) & (uint32_t)(kSampleStride - 1));
+}
+
 typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
 typedef float f32x4 __attribute__((ext_vector_type(4)));
 typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));

@@ -5,7 +5,45 @@
 #include <stddef.h>
 #include <stdint.h>
 
+#include <atomic>
+#include <mutex>
+
 namespace dsaidx {
+
+// Host-side set-up done once per device (kernel attributes), safe under concurrent calls from
+// several threads: a lock-free check on the fast path, the set-up itself under a mutex.
+constexpr int kMaxDevices = 64;
+struct DeviceOnce {
+    std::atomic<uint8_t> done[kMaxDevices] = {};
+    std::mutex mu;
+    template <class F> hipError_t run(F &&f) {
+        int dev = 0;
+        hipError_t e = hipGetDevice(&dev);
+        if (e != hipSuccess) return e;
+        if (dev < 0 || dev >= kMaxDevices) return hipErrorInvalidDevice;
+        if (done[dev].load(std::memory_order_acquire)) return hipSuccess;
+        std::lock_guard<std::mutex> lk(mu);
+        if (done[dev].load(std::memory_order_relaxed)) return hipSuccess;
+        e = f();
+        if (e == hipSuccess) done[dev].store(1, std::memory_order_release);
+        return e;
+    }
+};
+
+// A per-device integer computed on first use (every thread computes the same value, so a
+// race only repeats the computation).
+struct DeviceInt {
+    std::atomic<int> v[kMaxDevices] = {};
+    template <class F> int get(F &&f) {
+        int dev = 0;
+        if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= kMaxDevices) return f();
+        int x = v[dev].load(std::memory_order_relaxed);
+        if (x > 0) return x;
+        x = f();
+        v[dev].store(x, std::memory_order_relaxed);
+        return x;
+    }
+};
 
 // Offset (in floats) of score row t in a sequence's triangular block of the prefill score
 // workspace: row t holds kRowQuant * (t / kRowQuant + 1) scores (whole key tiles of the
@@ -26,12 +64,53 @@ hipError_t launch_project(const uint16_t *x, int64_t ldx, const uint16_t *c_q, i
                           float eps, uint16_t *q, uint16_t *k_base, const int64_t *k_slot,
                           uint16_t *w, float *ws, hipStream_t stream);
 
-// ---- prefill scores (scores.hip).  cu_seqlens == nullptr -> one sequence of T query rows
-// at positions pos0 .. pos0 + T - 1 (keys 0 .. pos0 + T - 1 of k); ragged batches start at
-// position 0.  seq_base: B + 1 int64 (written here for varlen), out: triangular rows (row t
-// at tri_row_offset(t) - tri_row_offset(pos0)), dummy: a row of kRowQuant * ceil((pos0 +
-// max_len) / kRowQuant) floats that absorbs the stores of rows past a sequence end and past
-// a row's own last key tile.
+// ---- prefill top-k with storage linear in the rows (prefill.hip).
+constexpr int64_t kFilterRows = 65536;        // rows of one filter pass (32 heads; 64 heads: half)
+constexpr int kListCap = 6144;                // candidates kept per (row, key segment)
+constexpr int64_t kSampleBytes = 512LL << 20; // sample rows held at once
+// Work split and workspace layout of one prefill call (host side).  rows: T (one sequence
+// at positions pos0 ..) or the packed total (ragged batch of B sequences, longest max_len).
+struct PrefillPlan {
+    int heads;
+    bool varlen;
+    int64_t rows;
+    int B;
+    int64_t max_len, pos0;
+    int64_t cf;        // rows of a filter chunk
+    int64_t lists;     // candidate lists of a filter chunk (rows x key segments)
+    int cap;           // entries per list
+    int64_t ms;        // floats per sample row
+    int64_t cs;        // rows of a sample sub-chunk
+    int64_t ld;        // floats per fallback scratch row
+    size_t off_hdr, off_theta, off_cnt, off_cand, off_srow, off_fblist, off_nbuf, off_obuf, off_scratch,
+        off_dummy, bytes;
+};
+PrefillPlan prefill_plan(int heads, bool varlen, int64_t rows, int B, int64_t max_len, int64_t pos0);
+// Scores and top-k of every row (q rows heads x 128, w rows heads); ws: plan.bytes, 256-byte
+// aligned; its first word is the status (bit 0: a ring wait of a score kernel ran out of polls).
+hipError_t launch_prefill_topk(const PrefillPlan &p, const uint16_t *q, const uint16_t *k, const uint16_t *w,
+                               const int32_t *cu_seqlens, int topk, int32_t *idx, float *scores, void *ws,
+                               hipStream_t stream);
+// Raw causal score rows, 32 heads (cu_seqlens == nullptr: one sequence of T rows at positions
+// pos0 ..; ragged batches start at 0).  seq_base: B + 1 int64 (written here for varlen), out:
+// triangular rows (row t at tri_row_offset(t) - tri_row_offset(pos0) from its sequence's base),
+// dummy: kRowQuant * ceil((pos0 + max_len) / kRowQuant) floats; status: cleared, then bit 0
+// set if a ring wait ran out of polls.
+hipError_t launch_scores(const uint16_t *q, const uint16_t *k, const uint16_t *w, const int32_t *cu_seqlens, int B,
+                         int64_t max_len, int64_t T, int64_t pos0, int64_t *seq_base, float *out, float *dummy,
+                         uint32_t *status, hipStream_t stream);
+// Diagnostic timing of the phases of prefill top-k calls (process-wide): while on, every phase
+// launch is bracketed by HIP events on its stream; prefill_phase_times synchronizes them and
+// returns the summed milliseconds and launch counts per phase (then forgets them).
+enum : int { kPhaseSample = 0, kPhaseThreshold = 1, kPhaseFilter = 2, kPhaseSelect = 3, kPhaseFallback = 4,
+             kPhases = 5 };
+void prefill_phase_timing(bool on);
+hipError_t prefill_phase_times(double *ms, int *count, int n);
+// Polls allowed per wait on a score kernel's key ring (default 2^20; 0 makes every wait that
+// is not already satisfied give up, for tests of the status report).
+void prefill_set_wait_budget(int polls);
+int prefill_wait_budget();
+
 // launch_project with explicit row strides: of W_q (ldwq) and q (ldq) for the 4,096 q columns
 // it computes, of W_w (ldww) and w (ldwo) for the 32 w columns; k_base may be nullptr (no key).
 hipError_t launch_project_ex(const uint16_t *x, int64_t ldx, const uint16_t *c_q, int64_t ldc,
@@ -45,23 +124,17 @@ hipError_t launch_project_ex(const uint16_t *x, int64_t ldx, const uint16_t *c_q
 // t at position pos0 + t.
 hipError_t launch_rope(uint16_t *q, int64_t ldq, int heads, uint16_t *k, int64_t ldk, int64_t T, int64_t pos0,
                        double theta, hipStream_t stream);
-// launch_scores with explicit row strides of q (ldq) and w (ldw) for the 32 heads it scores;
-// accumulate: add to the score rows instead of writing them.
-hipError_t launch_scores_ex(const uint16_t *q, int64_t ldq, const uint16_t *k, const uint16_t *w, int64_t ldw,
-                            bool accumulate, const int32_t *cu_seqlens, int B, int64_t max_len, int64_t T,
-                            int64_t pos0, int64_t *seq_base, float *out, float *dummy, hipStream_t stream);
-hipError_t launch_scores(const uint16_t *q, const uint16_t *k, const uint16_t *w,
-                         const int32_t *cu_seqlens, int B, int64_t max_len, int64_t T, int64_t pos0,
-                         int64_t *seq_base, float *out, float *dummy, hipStream_t stream);
 
 // ---- row top-k (topk.hip).  Prefill: rows = T (dense, query row g at position pos0 + g)
 // or the packed total (varlen, longest sequence max_len), scores in the triangular layout of
 // launch_scores.  Decode: B rows of stride ld (a multiple of 4), row b holding seqlens[b]
 // scores.
+// status (may be nullptr): when its bit 0 is set (the scoring kernel's ring wait gave up) every
+// row is written as index -2, score NaN instead of being selected.
 hipError_t launch_row_topk_prefill(const float *scores, const int32_t *cu_seqlens,
                                    const int64_t *seq_base, int B, int64_t max_len, int64_t pos0,
                                    int64_t rows, int topk, int32_t *idx, float *out_scores,
-                                   hipStream_t stream);
+                                   const uint32_t *status, hipStream_t stream);
 hipError_t launch_row_topk_decode(const float *scores, const int32_t *seqlens, int B, int64_t ld,
                                   int64_t nmax, int topk, int32_t *idx, float *out_scores,
                                   hipStream_t stream);

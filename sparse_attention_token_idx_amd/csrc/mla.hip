@@ -1,12 +1,11 @@
 // Sparse MLA over the selected tokens: the consumer of the indexer's selection ("Qwen3.5-397B-
-// A17B vs Kimi K3.1 Pro" compare page, gated-MLA row: 96 heads, keys and values from a 512-dim
-// latent plus a 64-dim shared key slot, 576 cached values per token, each query attending only
-// to the 2,048 tokens its layer's indexer selects; no rotary step, RoPE row of the "Kimi K3.1
-// Pro vs Gemma 4 31B" page).  Queries arrive in the absorbed latent form q~ [96][576], so head
-// h's logit for a selected token s is scale * q~_h . kv[s] over the 576 cached values, the
-// softmax runs over the selected tokens, and the head's output is the softmax-weighted sum of
-// the 512-dim latents (value up-projection, output gate and output projection follow as dense
-// products).
+// A17B vs Kimi K3.1 Pro" compare page, gated-MLA row).  Shapes from that row: H = 96, a cache
+// row per token of 512 + 64 = 576 bf16 values (latent, then the position key slot), and the
+// key set of query t is the <= 2,048 rows its indexer picked; MLA turns no rotary step ("Kimi
+// K3.1 Pro vs Gemma 4 31B" page, RoPE row).  Queries arrive in the absorbed latent form
+// q~ [96][576]: logit(h, s) = scale * q~_h . kv[s] over all 576 values, a softmax over the
+// picked rows, and out_h = sum_s p_h(s) kv[s][0:512] (the dense value up-projection, gate and
+// output projection come after this step).
 //
 // One workgroup takes one query and a contiguous split of its selections; its 12 waves pair up
 // on 16 heads each, the two waves of a pair taking alternate 32-dim k-steps of the 576 logit
@@ -391,14 +390,14 @@ __global__ __launch_bounds__(256) void sparse_mla_merge_kernel(MlaArgs a) {
 }
 
 int mla_cus() {
-    static int cached = 0;
-    if (cached > 0) return cached;
-    int dev = 0, cus = 0;
-    if (hipGetDevice(&dev) != hipSuccess ||
-        hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess || cus <= 0)
-        cus = 256;
-    cached = cus;
-    return cus;
+    static DeviceInt cached;
+    return cached.get([] {
+        int dev = 0, cus = 0;
+        if (hipGetDevice(&dev) != hipSuccess ||
+            hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess || cus <= 0)
+            cus = 256;
+        return cus;
+    });
 }
 
 }  // namespace
@@ -422,14 +421,13 @@ size_t sparse_mla_workspace(int64_t T, int topk) {
 hipError_t launch_sparse_mla(const uint16_t *q, const uint16_t *kv, const int32_t *idx, const int64_t *row0,
                              int64_t T, int topk, float scale, uint16_t *o, float *lse, float *ws,
                              hipStream_t stream) {
-    static bool attr_done = false;
+    static DeviceOnce attr;
     const size_t smem = sizeof(MlaSmem);
-    if (!attr_done) {
-        hipError_t e = hipFuncSetAttribute(reinterpret_cast<const void *>(sparse_mla_kernel),
-                                           hipFuncAttributeMaxDynamicSharedMemorySize, (int)smem);
-        if (e != hipSuccess) return e;
-        attr_done = true;
-    }
+    hipError_t ea = attr.run([&] {
+        return hipFuncSetAttribute(reinterpret_cast<const void *>(sparse_mla_kernel),
+                                   hipFuncAttributeMaxDynamicSharedMemorySize, (int)smem);
+    });
+    if (ea != hipSuccess) return ea;
     if (T == 0) return hipSuccess;
     MlaArgs a{};
     a.q = q;

@@ -530,17 +530,16 @@ hipError_t launch_project_ex(const uint16_t *x, int64_t ldx, const uint16_t *c_q
         const int t = (int)T;
         float *part_q = ws;
         float *part_kw = ws + (size_t)(kQLat / kSkQSlice) * T * kQOut;
-        static bool sk_attr_done = false;
-        if (!sk_attr_done) {
+        static DeviceOnce sk_attr;
+        hipError_t ea = sk_attr.run([] {
             hipError_t e = hipFuncSetAttribute(
                 reinterpret_cast<const void *>(skinny_partial_kernel<128, 1, 4, kSkQSlice>),
                 hipFuncAttributeMaxDynamicSharedMemorySize, (int)sizeof(GemmSmem<64, 128>));
             if (e != hipSuccess) return e;
-            e = hipFuncSetAttribute(reinterpret_cast<const void *>(skinny_partial_kernel<160, 2, 2, kSkKWSlice>),
-                                    hipFuncAttributeMaxDynamicSharedMemorySize, (int)sizeof(GemmSmem<64, 160>));
-            if (e != hipSuccess) return e;
-            sk_attr_done = true;
-        }
+            return hipFuncSetAttribute(reinterpret_cast<const void *>(skinny_partial_kernel<160, 2, 2, kSkKWSlice>),
+                                       hipFuncAttributeMaxDynamicSharedMemorySize, (int)sizeof(GemmSmem<64, 160>));
+        });
+        if (ea != hipSuccess) return ea;
         if (q) {
             hipLaunchKernelGGL((skinny_partial_kernel<128, 1, 4, kSkQSlice>), dim3(kQOut / 128, kQLat / kSkQSlice),
                                dim3(256), sizeof(GemmSmem<64, 128>), stream, c_q, ldc, t, W_q, (int)ldwq, W_q,
@@ -556,18 +555,17 @@ hipError_t launch_project_ex(const uint16_t *x, int64_t ldx, const uint16_t *c_q
                            kHidden / kSkKWSlice, a);
         return hipGetLastError();
     }
-    static bool attr_done = false;
+    static DeviceOnce attr;
     const size_t smem_q = sizeof(uint16_t) * kQStage * kQStages;
     const size_t smem_kw = sizeof(GemmSmem<128, 160>);
-    if (!attr_done) {
+    hipError_t ea = attr.run([&] {
         hipError_t e = hipFuncSetAttribute(reinterpret_cast<const void *>(proj_q_kernel),
                                            hipFuncAttributeMaxDynamicSharedMemorySize, (int)smem_q);
         if (e != hipSuccess) return e;
-        e = hipFuncSetAttribute(reinterpret_cast<const void *>(proj_kw_kernel),
-                                hipFuncAttributeMaxDynamicSharedMemorySize, (int)smem_kw);
-        if (e != hipSuccess) return e;
-        attr_done = true;
-    }
+        return hipFuncSetAttribute(reinterpret_cast<const void *>(proj_kw_kernel),
+                                   hipFuncAttributeMaxDynamicSharedMemorySize, (int)smem_kw);
+    });
+    if (ea != hipSuccess) return ea;
     const int64_t mt = (T + 127) / 128;
     if (q) {
         uint16_t *WqT = reinterpret_cast<uint16_t *>(ws);

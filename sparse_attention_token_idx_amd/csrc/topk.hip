@@ -9,7 +9,16 @@ using namespace topk_impl;
 template <int W>
 __global__ __launch_bounds__(64 * W, W == 4 ? 5 : 16 / W) void row_topk_kernel(TopkArgs a) {
     __shared__ TopkSmem<W> sm;
-    row_topk_row<W>(a, a.g0 + (int64_t)blockIdx.x, sm);
+    const int64_t g = a.g0 + (int64_t)blockIdx.x;
+    if (a.status && (*a.status & 1u)) {
+        // the scoring kernel's ring wait gave up: its rows are not to be trusted
+        for (int i = (int)threadIdx.x; i < a.topk; i += 64 * W) {
+            a.out_idx[g * a.topk + i] = -2;
+            if (a.out_score) a.out_score[g * a.topk + i] = __builtin_nanf("");
+        }
+        return;
+    }
+    row_topk_row<W>(a, g, sm);
 }
 
 }  // namespace
@@ -17,7 +26,7 @@ __global__ __launch_bounds__(64 * W, W == 4 ? 5 : 16 / W) void row_topk_kernel(T
 hipError_t launch_row_topk_prefill(const float *scores, const int32_t *cu_seqlens,
                                    const int64_t *seq_base, int B, int64_t max_len, int64_t pos0,
                                    int64_t rows, int topk, int32_t *idx, float *out_scores,
-                                   hipStream_t stream) {
+                                   const uint32_t *status, hipStream_t stream) {
     if (rows == 0) return hipSuccess;
     TopkArgs a{};
     a.scores = scores;
@@ -29,6 +38,7 @@ hipError_t launch_row_topk_prefill(const float *scores, const int32_t *cu_seqlen
     a.topk = topk;
     a.out_idx = idx;
     a.out_score = out_scores;
+    a.status = status;
     // rows of up to kLongRow scores: 4-wave workgroups; longer rows: the 16-wave variant
     // (ragged batches take one variant for all rows, from the longest sequence)
     int64_t g1 = rows;

@@ -44,9 +44,9 @@ constexpr int kWChunk = 64 * kPer;              // 1,024: one wave's chunk in th
 template <int W> constexpr int kCand = kPer * 64 * W;
 // chunk runs: rows of up to 512K keys (W = 4) or 1M keys (W = 16)
 template <int W> constexpr int kMaxRun = W <= 4 ? 512 : 1024;
-// sample of a long row: 64 blocks of 64 scores (W = 4); W = 16 takes up to 256 blocks on
+// sample of a long row: 64 blocks of 64 scores (W = 4); W = 8 or 16 take up to 16 W blocks on
 // rows long enough for them to stay a small share of the row
-template <int W> constexpr int kSampleBlocks = W <= 4 ? 64 : 256;
+template <int W> constexpr int kSampleBlocks = W <= 4 ? 64 : 16 * W;
 constexpr int kPrefetch = 2;                    // wave chunks in flight ahead of the current
 constexpr int kRankMax = 128;                   // keys of the threshold bin ranked directly
 constexpr int64_t kLongRow = 65536;             // longest prefill row of the 4-wave variant
@@ -66,6 +66,7 @@ static_assert(kSampleBlocks<4> * 4 <= 64 * 4 && kSampleBlocks<16> * 4 <= 64 * 16
 template <int W> constexpr int kMaxPieces = W >= 16 ? 4096 : 1;
 
 template <int W> struct TopkSmem {
+    static constexpr int kW = W;
     union {
         struct {                   // a candidate: its key and its offset in its chunk
             uint32_t key[kCand<W>];
@@ -123,12 +124,15 @@ struct TopkArgs {
     int topk;
     int32_t *out_idx;
     float *out_score;              // may be nullptr
+    const int64_t *out_row;        // output row of row g (nullptr: g)
+    const uint32_t *status;        // row_topk_kernel: bit 0 set -> rows invalid (nullptr: none)
 };
 
 
 // Inclusive sum over the workgroup of one int per thread (the sum of all in `total`).
-template <int W>
-__device__ int block_inclusive_sum(int v, int &total, TopkSmem<W> &sm) {
+template <class Sm>
+__device__ int block_inclusive_sum(int v, int &total, Sm &sm) {
+    [[maybe_unused]] constexpr int W = Sm::kW;
     const int tid = (int)threadIdx.x;
     const int lane = tid & 63, wave = tid >> 6;
     const int incl = wave_inclusive_sum(v);
@@ -161,8 +165,9 @@ __device__ __forceinline__ int wave_exclusive_sum(int v, int &total) {
 // found so far, return the digit of the need-th largest and subtract from need the keys in
 // higher digits; in_bin = the keys in the returned digit's bin.  Thread t owns bins
 // kBinsPer t .. kBinsPer t + kBinsPer - 1.
-template <int W>
-__device__ uint32_t pick_digit(int &need, TopkSmem<W> &sm, int *in_bin = nullptr) {
+template <class Sm>
+__device__ uint32_t pick_digit(int &need, Sm &sm, int *in_bin = nullptr) {
+    [[maybe_unused]] constexpr int W = Sm::kW;
     const int tid = (int)threadIdx.x;
     int cnt[kBinsPer<W>], sum = 0;
 #pragma unroll
@@ -191,8 +196,9 @@ __device__ uint32_t pick_digit(int &need, TopkSmem<W> &sm, int *in_bin = nullptr
 }
 
 // Largest of one key per thread over the workgroup.
-template <int W>
-__device__ uint32_t block_max(uint32_t v, TopkSmem<W> &sm) {
+template <class Sm>
+__device__ uint32_t block_max(uint32_t v, Sm &sm) {
+    [[maybe_unused]] constexpr int W = Sm::kW;
     const int tid = (int)threadIdx.x;
     const int lane = tid & 63, wave = tid >> 6;
 #pragma unroll
@@ -213,9 +219,10 @@ __device__ uint32_t block_max(uint32_t v, TopkSmem<W> &sm) {
 // relative key (key - base) < 2^nbits, kDigit<W> bits at a time from the top: returns theta,
 // the need-th largest key; on return need = how many keys equal to theta are among the need
 // largest.
-template <int W>
+template <class Sm>
 __device__ uint32_t select_rel(const uint32_t (&key)[kPer], uint32_t base, int nbits, int &need,
-                               TopkSmem<W> &sm) {
+                               Sm &sm) {
+    [[maybe_unused]] constexpr int W = Sm::kW;
     uint32_t prefix = 0, pmask = 0;
     int hi = nbits;
 #pragma unroll 1
@@ -245,10 +252,11 @@ __device__ __forceinline__ int bit_width(uint32_t x) { return x ? 32 - __builtin
 // this thread's kPer keys (indices idx0 + i, increasing with thread and i); out_base = outputs
 // already written and eq_base = keys equal to theta already seen (both block-uniform).
 // Returns the number written by the whole workgroup; eq_base advances by the ties seen.
-template <int W>
+template <class Sm>
 __device__ int emit_ordered(const uint32_t (&key)[kPer], int32_t idx0, uint32_t theta,
                             int need, int out_base, int &eq_base, int32_t *oi, float *os,
-                            TopkSmem<W> &sm) {
+                            Sm &sm) {
+    [[maybe_unused]] constexpr int W = Sm::kW;
     int eqc = 0;
 #pragma unroll
     for (int i = 0; i < kPer; ++i) eqc += key[i] == theta ? 1 : 0;
@@ -278,10 +286,11 @@ __device__ int emit_ordered(const uint32_t (&key)[kPer], int32_t idx0, uint32_t 
 }
 
 // emit_ordered for keys whose indices are given (kidx[i], increasing with thread and i).
-template <int W>
+template <class Sm>
 __device__ int emit_ordered_idx(const uint32_t (&key)[kPer], const int32_t (&kidx)[kPer], uint32_t theta,
                                 int need, int out_base, int &eq_base, int32_t *oi, float *os,
-                                TopkSmem<W> &sm) {
+                                Sm &sm) {
+    [[maybe_unused]] constexpr int W = Sm::kW;
     int eqc = 0;
 #pragma unroll
     for (int i = 0; i < kPer; ++i) eqc += key[i] == theta ? 1 : 0;
@@ -439,8 +448,9 @@ __device__ __forceinline__ void row_topk_row(const TopkArgs &a, int64_t g, TopkS
     const float *row;
     int64_t n;
     locate_row(a, g, row, n);
-    int32_t *oi = a.out_idx + g * topk;
-    float *os = a.out_score ? a.out_score + g * topk : nullptr;
+    const int64_t go = a.out_row ? a.out_row[g] : g;
+    int32_t *oi = a.out_idx + go * topk;
+    float *os = a.out_score ? a.out_score + go * topk : nullptr;
     if (n <= topk) {
         for (int i = tid; i < topk; i += (64 * W)) {
             const bool in = i < n;

@@ -33,7 +33,8 @@ def test_exports_every_declared_symbol(dsa):
                           "dsa_idx_quantize_keys", "dsa_idx_decode_fp8", "dsa_idx_prefill_chunk",
                           "dsa_idx_sparse_mla", "dsa_idx_v32_project", "dsa_idx_v32_score_topk",
                           "dsa_idx_v32_score_topk_varlen", "dsa_idx_v32_prefill_chunk",
-                          "dsa_idx_v32_decode", "dsa_idx_v32_decode_fp8"}
+                          "dsa_idx_v32_decode", "dsa_idx_v32_decode_fp8", "dsa_idx_workspace_status",
+                          "dsa_idx_set_wait_budget", "dsa_idx_phase_timing", "dsa_idx_phase_times"}
     for n in names:
         assert getattr(L, n) is not None
 
@@ -48,17 +49,63 @@ def test_workspace_sizes(dsa):
     # a few tokens (at most 64) split K: fp32 partial sums, 6 slices of q and 56 of [k | w]
     assert dsa.workspace_size(dsa.OP_PROJECT, 64) == 4 * 64 * (6 * 4096 + 56 * 160)
     assert dsa.workspace_size(dsa.OP_PROJECT, 1) == 4 * (6 * 4096 + 56 * 160)
-    # prefill: 256-byte header of sequence bases, a dummy row of 128*ceil(max/128) floats, and
-    # the triangular score rows (row t holds 128*(t//128 + 1) floats)
+    # raw causal score rows: a 256-byte status header, the sequence bases (256-byte aligned), a
+    # dummy row of 128*ceil(max/128) floats, and the triangular score rows (row t holds
+    # 128*(t//128 + 1) floats)
     def tri(t):
         q, r = divmod(t, 128)
         return 8192 * q * (q + 1) + 128 * r * (q + 1)
     assert tri(1000) == sum(128 * (t // 128 + 1) for t in range(1000))
     r256 = lambda b: (b + 255) // 256 * 256
-    assert dsa.workspace_size(dsa.OP_SCORE_TOPK, 1000, topk=2048) == 256 + r256(4 * 1024) + 4 * tri(1000)
+    assert dsa.workspace_size(dsa.OP_PREFILL_ROWS, 1000, 0, 0) == 256 + 256 + r256(4 * 1024) + 4 * tri(1000)
     # ragged: bound from sequences of max length (here 2 of length 8 -> (8+128)^2/2 floats each)
     vb = ((2 * 136 * 136 // 2 + 127) // 128) * 128
-    assert dsa.workspace_size(dsa.OP_SCORE_TOPK_VARLEN, 16, 2, 8, topk=5) == 256 + 512 + 4 * vb
+    assert dsa.workspace_size(dsa.OP_PREFILL_ROWS, 16, 2, 8) == 256 + 256 + 512 + 4 * vb
+    # prefill top-k: the layout of the plan (a status header; per row of a filter chunk of at most
+    # 65,536 rows a threshold, per (row, key segment) a count and a list of 6,144 (score, index)
+    # pairs followed by 64 sentinel pairs
+    # pairs; sample rows of ceil(n / 32 / 128) * 128 floats for a sub-chunk of at most 512 MB; a
+    # fallback list; and 128 fallback scratch rows of the longest row, padded to 64)
+    def plan(rows, heads=32, varlen=False, B=1, max_len=None, pos0=0):
+        bq = 16 if heads == 64 else 32
+        max_len = rows if max_len is None else max_len
+        pos0 = 0 if varlen else pos0
+        nkeys = pos0 + max_len
+        cf = min(rows, 65536 if heads == 32 else 32768)
+        lists = 0
+        for f0 in range(0, rows, cf):
+            f1 = min(rows, f0 + cf)
+            nseg = 1
+            if not varlen:
+                nrb, mt = -(-(f1 - f0) // bq), (pos0 + f1 - 1) // 128 + 1
+                if nrb < 2048 and mt > 64:
+                    want = -(-2048 // nrb)
+                    st = max(64, -(-mt // want), -(-mt // 512))
+                    if st < mt:
+                        nseg = -(-mt // st)
+            lists = max(lists, (cf if varlen else f1 - f0) * nseg)
+        ms = -(-max(nkeys // 32, 1) // 128) * 128
+        cs = max(bq, (512 * 2 ** 20 // (4 * ms)) // bq * bq)
+        cs = min(cs, cf)
+        ld = -(-max(nkeys, 1) // 64) * 64
+        parts = [256, 4 * cf, 4 * lists, 8 * lists * (6144 + 64), 4 * cs * ms, 8 * cf, 4 * 128, 8 * 128,
+                 4 * 128 * ld, 4 * max(ms, ld) + 4 * 128]
+        return sum(r256(x) for x in parts)
+    for T in (1, 300, 1000, 5000, 65536, 100000):
+        assert dsa.workspace_size(dsa.OP_SCORE_TOPK, T, topk=2048) == plan(T), T
+        assert dsa.workspace_size(dsa.OP_V32_SCORE_TOPK, T, topk=2048) == plan(T, heads=64), T
+    assert dsa.workspace_size(dsa.OP_SCORE_TOPK_VARLEN, 16, 2, 8, topk=5) == plan(16, varlen=True, B=2, max_len=8)
+    assert dsa.workspace_size(dsa.OP_V32_SCORE_TOPK_VARLEN, 177278, 16, 32768, topk=5) == \
+        plan(177278, heads=64, varlen=True, B=16, max_len=32768)
+    assert dsa.workspace_size(dsa.OP_PREFILL_CHUNK, 300, 0, 1000, 8) == plan(300, pos0=1000)
+    assert dsa.workspace_size(dsa.OP_V32_PREFILL_CHUNK, 4096, 0, 10 ** 6, 8) == plan(4096, heads=64, pos0=10 ** 6)
+    assert dsa.workspace_size(dsa.OP_PREFILL_CHUNK, 1000, 0, 0, 8) == dsa.workspace_size(dsa.OP_SCORE_TOPK, 1000, topk=8)
+    assert dsa.workspace_size(dsa.OP_PREFILL_CHUNK, 0, 0, 5000, 8) == 0
+    # no T x T matrix: the top-k workspace grows at most linearly in T, and a 1,048,576-token
+    # sequence needs a few GB where its score triangle alone would take 2.2 TB
+    big = [dsa.workspace_size(dsa.OP_SCORE_TOPK, T, topk=2048) for T in (2 ** 16, 2 ** 18, 2 ** 20, 2 ** 22)]
+    assert all(b2 <= 4 * b1 for b1, b2 in zip(big, big[1:]))
+    assert big[2] < 5 * 2 ** 30 and 4 * tri(2 ** 20) > 2 * 10 ** 12
     # decode: 256-byte aligned parts over the padded positions P = B * 64 * ceil(max / 64):
     # B + 1 cache offsets, B plans (8 bytes), P / 64 + 1 piece counts, P candidate slots of
     # 8 bytes, P fp32 scores, 8,192 sampled score keys per sequence; FP8 adds the quantised
@@ -72,13 +119,6 @@ def test_workspace_sizes(dsa):
     assert dsa.workspace_size(dsa.OP_DECODE, 0, 64, 131072, 2048) == dec(64, 131072)
     assert dsa.workspace_size(dsa.OP_DECODE, 0, 3, 100, 8) == dec(3, 100)
     assert dsa.workspace_size(dsa.OP_DECODE_FP8, 0, 3, 100, 8) == dec(3, 100, True)
-    # chunked prefill: header, a dummy row of 128*ceil((prefix + C)/128) floats, and rows
-    # prefix .. prefix + C - 1 of the triangular layout
-    assert dsa.workspace_size(dsa.OP_PREFILL_CHUNK, 300, 0, 1000, 8) == \
-        256 + r256(4 * 1408) + 4 * (tri(1300) - tri(1000))
-    assert dsa.workspace_size(dsa.OP_PREFILL_CHUNK, 1000, 0, 0, 8) == \
-        dsa.workspace_size(dsa.OP_SCORE_TOPK, 1000, topk=8)
-    assert dsa.workspace_size(dsa.OP_PREFILL_CHUNK, 0, 0, 5000, 8) == 0
     # sparse MLA: the splits' fp32 partial outputs and (max, sum) per (split, query, head), only
     # when a query's selections are split over several workgroups (few queries)
     assert dsa.workspace_size(dsa.OP_SPARSE_MLA, 5000, 0, 0, 2048) == 0
@@ -154,7 +194,7 @@ def test_rejections_before_device(dsa):
     assert chunk(_vp(A), _vp(A), _vp(A), 10, 100, 8, _vp(A), None, _vp(A), 16, None) == -3
     assert chunk(_vp(A), _vp(A), _vp(A), 4096, (1 << 24) - 4095, 8, _vp(A), None, _vp(A), 1 << 62,
                  None) == -2
-    assert b"prefix + C" in L.dsa_idx_last_error()
+    assert b"keys above 16777216" in L.dsa_idx_last_error()
     assert chunk(None, None, None, 0, 100, 8, None, None, None, 0, None) == 0
     # sparse MLA
     mla = lambda *a: L.dsa_idx_sparse_mla(*a)
@@ -191,7 +231,6 @@ def test_rejections_before_device(dsa):
     assert vc(_vp(A), _vp(A), _vp(A), 10, -1, 8, _vp(A), None, _vp(A), 1 << 30, None) == -1
     assert vc(_vp(A), _vp(A), _vp(A), 10, 100, 8, _vp(A), None, _vp(A), 16, None) == -3
     assert vc(None, None, None, 0, 100, 8, None, None, None, 0, None) == 0
-    assert dsa.workspace_size(dsa.OP_V32_SCORE_TOPK, 1000) == dsa.workspace_size(dsa.OP_SCORE_TOPK, 1000)
     assert dsa.workspace_size(dsa.OP_V32_PROJECT, 100) == dsa.workspace_size(dsa.OP_PROJECT, 100)
     assert dsa.workspace_size(dsa.OP_V32_PROJECT, 7) == dsa.workspace_size(dsa.OP_PROJECT, 7)
 

@@ -219,13 +219,13 @@ def test_negative_weights(dsa):
 
 
 def test_prefill_halves_and_score_rows(dsa):
-    """The two C-ABI halves give score_topk's result, and the workspace rows hold the causal
-    scores of the oracle (fp32 tolerance of check_row) for every key s <= t."""
+    """The raw-rows calls (every causal score stored, then the row top-k) give score_topk's
+    result bit for bit, and the stored rows hold the causal scores of the oracle (fp32
+    tolerance of check_row) for every key s <= t."""
     T = 2300
     s = wl.score_inputs(T, seed=17)
     q, k, w = to_dev(s["q"]), to_dev(s["k"]), to_dev(s["w"])
-    ws = torch.empty(dsa.workspace_size(dsa.OP_SCORE_TOPK, T, topk=2048), dtype=torch.uint8,
-                     device="cuda")
+    ws = dsa.prefill_rows_workspace(T)
     dsa.prefill_scores(q, k, w, ws)
     idx, sc = dsa.prefill_select(T, ws, topk=2048)
     torch.cuda.synchronize()
