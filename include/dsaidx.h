@@ -219,6 +219,20 @@ int dsa_idx_decode(const dsa_idx_bf16 *q, const dsa_idx_bf16 *w, const dsa_idx_b
                    int topk, int32_t *idx, float *scores, void *ws, size_t ws_bytes,
                    void *stream);
 
+/* dsa_idx_decode without a workspace argument, for callers that cannot allocate device memory
+ * (code under HIP graph capture, tight serving loops, harnesses that forbid hipMalloc).  Its
+ * scratch is a static array of DSA_IDX_DECODE_NOALLOC_SCRATCH bytes inside the library, one
+ * copy per device (held until the process ends); the call allocates nothing and otherwise
+ * behaves as dsa_idx_decode (same kernels, same results).  A (B, max_seqlen) whose decode
+ * workspace exceeds the array is rejected with DSA_IDX_EUNSUPPORTED (64 sequences of up to
+ * 131,072 cached keys fit).  Every call on one device shares that device's array: calls that
+ * may overlap on one device (several streams, several host threads) race and must be
+ * serialized by the caller. */
+#define DSA_IDX_DECODE_NOALLOC_SCRATCH (128u << 20)
+int dsa_idx_decode_noalloc(const dsa_idx_bf16 *q, const dsa_idx_bf16 *w, const dsa_idx_bf16 *k_cache,
+                           const int64_t *start, const int32_t *seqlens, int B, int max_seqlen, int topk,
+                           int32_t *idx, float *scores, void *stream);
+
 /* ---- FP8 key cache ("Kimi K3.1 Pro vs GLM-5" page, low-precision row: the serving engines
  * cache the indexer keys in FP8; the pages give no format or scale).  Format of this library:
  * a cached key is 128 OCP E4M3 codes (bias 7, largest finite value 448, no infinities; one

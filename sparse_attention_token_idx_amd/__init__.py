@@ -18,7 +18,7 @@ __all__ = ["version", "workspace_size", "project", "score_topk", "score_topk_var
            "prefill_chunk", "sparse_mla", "OP_SPARSE_MLA", "HEADS", "DIM", "QLAT", "QOUT", "HIDDEN", "MAX_TOPK", "OP_PROJECT",
            "OP_SCORE_TOPK", "OP_SCORE_TOPK_VARLEN", "OP_DECODE", "OP_DECODE_FP8",
            "OP_PREFILL_CHUNK", "OP_PREFILL_ROWS", "OP_V32_SCORE_TOPK_VARLEN", "OP_V32_PREFILL_CHUNK",
-           "prefill_rows_workspace", "workspace_status", "set_wait_budget", "phase_timing", "phase_times", "PHASES", "ESTALL", "DsaIdxError", "lib"]
+           "prefill_rows_workspace", "decode_noalloc", "workspace_status", "set_wait_budget", "phase_timing", "phase_times", "PHASES", "ESTALL", "DsaIdxError", "lib"]
 
 HEADS, DIM, QLAT, QOUT, HIDDEN, MAX_TOPK = 32, 128, 1536, 4096, 7168, 2048
 OP_PROJECT, OP_SCORE_TOPK, OP_SCORE_TOPK_VARLEN, OP_DECODE, OP_DECODE_FP8 = 0, 1, 2, 3, 4
@@ -94,6 +94,8 @@ def lib():
         L.dsa_idx_v32_decode_fp8.argtypes = [vp, vp, vp, vp, vp, vp, i32, i32, i32, vp, vp, vp, sz, vp]
         L.dsa_idx_sparse_mla.restype = i32
         L.dsa_idx_sparse_mla.argtypes = [vp, vp, vp, vp, i64, i32, ctypes.c_float, vp, vp, vp, sz, vp]
+        L.dsa_idx_decode_noalloc.restype = i32
+        L.dsa_idx_decode_noalloc.argtypes = [vp, vp, vp, vp, vp, i32, i32, i32, vp, vp, vp]
         L.dsa_idx_decode.restype = i32
         L.dsa_idx_decode.argtypes = [vp, vp, vp, vp, vp, i32, i32, i32, vp, vp, vp, sz, vp]
         L.dsa_idx_quantize_keys.restype = i32
@@ -478,6 +480,27 @@ def decode(q, w, k_cache, start, seqlens, max_seqlen, topk=MAX_TOPK, with_scores
     _check(fn, getattr(lib(), fn)(_ptr(q), _ptr(w), _ptr(k_cache), _ptr(start), _ptr(seqlens), B,
                                   int(max_seqlen), topk, _ptr(idx), _ptr(sc), _ptr(ws), nbytes,
                                   _stream(stream)))
+    return idx, sc
+
+
+def decode_noalloc(q, w, k_cache, start, seqlens, max_seqlen, topk=MAX_TOPK, with_scores=True, out=None,
+                   stream=None):
+    """decode (32 heads) through the entry point that allocates no device memory: its scratch is
+    a static array inside the library.  Pass `out` (idx, scores) to allocate nothing here either."""
+    B = q.shape[0]
+    _need(q, "q", torch.bfloat16, (B, HEADS, DIM))
+    _need(w, "w", torch.bfloat16, (B, HEADS))
+    _need(k_cache, "k_cache", torch.bfloat16)
+    _need(start, "start", torch.int64, (B,))
+    _need(seqlens, "seqlens", torch.int32, (B,))
+    if out is None:
+        idx = torch.empty((B, topk), dtype=torch.int32, device=q.device)
+        sc = torch.empty((B, topk), dtype=torch.float32, device=q.device) if with_scores else None
+    else:
+        idx, sc = out
+    _check("dsa_idx_decode_noalloc",
+           lib().dsa_idx_decode_noalloc(_ptr(q), _ptr(w), _ptr(k_cache), _ptr(start), _ptr(seqlens), B,
+                                        int(max_seqlen), topk, _ptr(idx), _ptr(sc), _stream(stream)))
     return idx, sc
 
 

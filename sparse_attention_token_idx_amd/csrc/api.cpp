@@ -519,6 +519,62 @@ int dsa_idx_decode(const dsa_idx_bf16 *q, const dsa_idx_bf16 *w, const dsa_idx_b
                        DSA_IDX_HEADS);
 }
 
+}  // extern "C"
+
+// ---- The decode entry that allocates nothing: its scratch is this array.  Each device the
+// library runs on holds its own copy until the process ends; host code never passes the array's
+// name to a kernel (on the host it is only a stand-in), but the device address that
+// hipGetSymbolAddress returns for the current device, looked up once per device.
+static __device__ __align__(256) uint8_t scratch[DSA_IDX_DECODE_NOALLOC_SCRATCH];
+
+namespace {
+std::mutex g_scratch_mu;
+void *g_scratch_ptr[dsaidx::kMaxDevices] = {};
+
+int static_scratch(void **out) {
+    int dev = 0;
+    hipError_t e = hipGetDevice(&dev);
+    if (e != hipSuccess) return hip_fail("hipGetDevice", e);
+    if (dev < 0 || dev >= dsaidx::kMaxDevices) return fail(DSA_IDX_EUNSUPPORTED, "device ordinal %d out of range", dev);
+    std::lock_guard<std::mutex> lk(g_scratch_mu);
+    if (!g_scratch_ptr[dev]) {
+        void *p = nullptr;
+        e = hipGetSymbolAddress(&p, HIP_SYMBOL(scratch));
+        if (e != hipSuccess) return hip_fail("hipGetSymbolAddress(scratch)", e);
+        if (!p) return fail(DSA_IDX_EHIP, "hipGetSymbolAddress(scratch) returned NULL");
+        g_scratch_ptr[dev] = p;
+    }
+    *out = g_scratch_ptr[dev];
+    return ok();
+}
+}  // namespace
+
+extern "C" {
+
+int dsa_idx_decode_noalloc(const dsa_idx_bf16 *q, const dsa_idx_bf16 *w, const dsa_idx_bf16 *k_cache,
+                           const int64_t *start, const int32_t *seqlens, int B, int max_seqlen, int topk,
+                           int32_t *idx, float *scores, void *stream) {
+    if (B < 0 || max_seqlen < 0) return fail(DSA_IDX_EINVAL, "B=%d max_seqlen=%d must be >= 0", B, max_seqlen);
+    int r = check_topk(topk);
+    if (r) return r;
+    if (B == 0) return ok();
+    if (max_seqlen > kMaxWindow)
+        return fail(DSA_IDX_EUNSUPPORTED, "max_seqlen=%d above %lld", max_seqlen, (long long)kMaxWindow);
+    const size_t need = ws_decode(B, max_seqlen);
+    if (need > (size_t)DSA_IDX_DECODE_NOALLOC_SCRATCH)
+        return fail(DSA_IDX_EUNSUPPORTED,
+                    "B=%d, max_seqlen=%d need %zu bytes of scratch, above the %zu bytes this entry holds; "
+                    "use dsa_idx_decode with a workspace",
+                    B, max_seqlen, need, (size_t)DSA_IDX_DECODE_NOALLOC_SCRATCH);
+    r = check_device();
+    if (r) return r;
+    void *ws = nullptr;
+    r = static_scratch(&ws);
+    if (r) return r;
+    return decode_impl(q, w, k_cache, start, seqlens, B, max_seqlen, topk, idx, scores, ws,
+                       (size_t)DSA_IDX_DECODE_NOALLOC_SCRATCH, stream, DSA_IDX_HEADS);
+}
+
 int dsa_idx_v32_decode(const dsa_idx_bf16 *q, const dsa_idx_bf16 *w, const dsa_idx_bf16 *k_cache,
                        const int64_t *start, const int32_t *seqlens, int B, int max_seqlen,
                        int topk, int32_t *idx, float *scores, void *ws, size_t ws_bytes,

@@ -34,7 +34,8 @@ def test_exports_every_declared_symbol(dsa):
                           "dsa_idx_sparse_mla", "dsa_idx_v32_project", "dsa_idx_v32_score_topk",
                           "dsa_idx_v32_score_topk_varlen", "dsa_idx_v32_prefill_chunk",
                           "dsa_idx_v32_decode", "dsa_idx_v32_decode_fp8", "dsa_idx_workspace_status",
-                          "dsa_idx_set_wait_budget", "dsa_idx_phase_timing", "dsa_idx_phase_times"}
+                          "dsa_idx_set_wait_budget", "dsa_idx_phase_timing", "dsa_idx_phase_times",
+                          "dsa_idx_decode_noalloc"}
     for n in names:
         assert getattr(L, n) is not None
 
