@@ -102,6 +102,13 @@ const char *dsa_idx_version(void);
 /* Message of the last non-OK status returned on the calling thread ("" if none). */
 const char *dsa_idx_last_error(void);
 
+/* Whether the library's kernels run on a device whose architecture name (hipDeviceProp_t::
+ * gcnArchName, e.g. "gfx950:sramecc+:xnack-") is arch_name: DSA_IDX_OK for gfx950 with any
+ * feature suffix, DSA_IDX_EUNSUPPORTED (with a message) for any other name, DSA_IDX_EINVAL for a
+ * null pointer.  Host-only; every entry point that launches work applies this check to the
+ * current device (once per device) and returns its status. */
+int dsa_idx_arch_supported(const char *arch_name);
+
 /* Bytes of workspace an operation needs (host-only, no device access).
  *   op               one of DSA_IDX_OP_*
  *   total_tokens     T for PROJECT, SCORE_TOPK, SPARSE_MLA, V32_PROJECT and V32_SCORE_TOPK;

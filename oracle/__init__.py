@@ -23,17 +23,31 @@ import subprocess
 import numpy as np
 
 _HERE = os.path.dirname(os.path.abspath(__file__))
-_SO = os.path.join(_HERE, "liboracle.so")
 _SRC = os.path.join(_HERE, "oracle.c")
+# ORACLE_LIB names another build of oracle.c (build_sanitized()); the default is liboracle.so.
+_SO_DEFAULT = os.path.join(_HERE, "liboracle.so")
+_SO = os.environ.get("ORACLE_LIB") or _SO_DEFAULT
+SO_SAN = os.path.join(_HERE, "_san", "liboracle.so")
 
 H, D, QLAT, QOUT, HIDDEN, TOPK = 32, 128, 1536, 4096, 7168, 2048
 
 
 def build(force=False):
-    if force or not os.path.exists(_SO) or os.path.getmtime(_SO) < os.path.getmtime(_SRC):
+    so = _SO_DEFAULT
+    if force or not os.path.exists(so) or os.path.getmtime(so) < os.path.getmtime(_SRC):
         subprocess.check_call(["gcc", "-O2", "-std=c11", "-ffp-contract=off", "-fopenmp",
-                               "-fPIC", "-shared", _SRC, "-o", _SO + ".tmp", "-lm"])
-        os.replace(_SO + ".tmp", _SO)
+                               "-fPIC", "-shared", _SRC, "-o", so + ".tmp", "-lm"])
+        os.replace(so + ".tmp", so)
+
+
+def build_sanitized():
+    """oracle.c with gcc's AddressSanitizer and UndefinedBehaviorSanitizer, into _san/; load it
+    with ORACLE_LIB in a process that preloads gcc's libasan and libubsan."""
+    os.makedirs(os.path.dirname(SO_SAN), exist_ok=True)
+    subprocess.check_call(["gcc", "-O1", "-g", "-std=c11", "-ffp-contract=off", "-fopenmp", "-fPIC",
+                           "-shared", "-fsanitize=address,undefined", "-fno-sanitize-recover=all",
+                           "-fno-omit-frame-pointer", _SRC, "-o", SO_SAN, "-lm"])
+    return SO_SAN
 
 
 _lib = None

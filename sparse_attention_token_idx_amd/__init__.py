@@ -18,7 +18,7 @@ __all__ = ["version", "workspace_size", "project", "score_topk", "score_topk_var
            "prefill_chunk", "sparse_mla", "OP_SPARSE_MLA", "HEADS", "DIM", "QLAT", "QOUT", "HIDDEN", "MAX_TOPK", "OP_PROJECT",
            "OP_SCORE_TOPK", "OP_SCORE_TOPK_VARLEN", "OP_DECODE", "OP_DECODE_FP8",
            "OP_PREFILL_CHUNK", "OP_PREFILL_ROWS", "OP_V32_SCORE_TOPK_VARLEN", "OP_V32_PREFILL_CHUNK",
-           "prefill_rows_workspace", "decode_noalloc", "workspace_status", "set_wait_budget", "phase_timing", "phase_times", "PHASES", "ESTALL", "DsaIdxError", "lib"]
+           "prefill_rows_workspace", "decode_noalloc", "workspace_status", "set_wait_budget", "phase_timing", "phase_times", "PHASES", "EINVAL", "EUNSUPPORTED", "ESTALL", "arch_supported", "DsaIdxError", "lib"]
 
 HEADS, DIM, QLAT, QOUT, HIDDEN, MAX_TOPK = 32, 128, 1536, 4096, 7168, 2048
 OP_PROJECT, OP_SCORE_TOPK, OP_SCORE_TOPK_VARLEN, OP_DECODE, OP_DECODE_FP8 = 0, 1, 2, 3, 4
@@ -26,12 +26,13 @@ OP_PREFILL_CHUNK = 5
 OP_SPARSE_MLA = 6
 OP_V32_PROJECT, OP_V32_SCORE_TOPK = 7, 8
 OP_V32_SCORE_TOPK_VARLEN, OP_V32_PREFILL_CHUNK, OP_PREFILL_ROWS = 9, 10, 11
-ESTALL = -5
+EINVAL, EUNSUPPORTED, ESTALL = -1, -2, -5
 MLA_HEADS, MLA_KV, MLA_V = 96, 576, 512
 V32_HEADS, V32_QOUT, V32_THETA = 64, 8192, 10000.0   # the 64-head (DeepSeek-V3.2-shaped) indexer
 
 _HERE = os.path.dirname(os.path.abspath(__file__))
-LIB_PATH = os.path.join(_HERE, "libdsaidx.so")
+# DSA_IDX_LIB names another build of the same library (e.g. the host-sanitizer build).
+LIB_PATH = os.environ.get("DSA_IDX_LIB") or os.path.join(_HERE, "libdsaidx.so")
 
 
 class DsaIdxError(RuntimeError):
@@ -108,6 +109,8 @@ def lib():
         L.dsa_idx_phase_timing.argtypes = [i32]
         L.dsa_idx_phase_times.restype = i32
         L.dsa_idx_phase_times.argtypes = [ctypes.POINTER(ctypes.c_double), ctypes.POINTER(ctypes.c_int), i32]
+        L.dsa_idx_arch_supported.restype = i32
+        L.dsa_idx_arch_supported.argtypes = [ctypes.c_char_p]
         L.dsa_idx_decode_fp8.restype = i32
         L.dsa_idx_decode_fp8.argtypes = [vp, vp, vp, vp, vp, vp, i32, i32, i32, vp, vp, vp, sz, vp]
         _lib = L
@@ -116,6 +119,11 @@ def lib():
 
 def version():
     return lib().dsa_idx_version().decode()
+
+
+def arch_supported(arch_name):
+    """Raise DsaIdxError unless the library runs on a device of this gcnArchName."""
+    _check("dsa_idx_arch_supported", lib().dsa_idx_arch_supported(arch_name.encode()))
 
 
 def _check(fn, code):

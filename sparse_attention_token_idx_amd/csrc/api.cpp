@@ -34,6 +34,12 @@ int hip_fail(const char *what, hipError_t e) {
     return fail(DSA_IDX_EHIP, "%s: %s", what, hipGetErrorString(e));
 }
 
+// The architecture part of a gcnArchName ("gfx950:sramecc+:xnack-" -> "gfx950") must be gfx950.
+bool arch_is_gfx950(const char *name) {
+    const size_t n = strcspn(name, ":");
+    return n == 6 && strncmp(name, "gfx950", 6) == 0;
+}
+
 // gfx950 check, cached per device.
 int check_device() {
     int dev = 0;
@@ -47,7 +53,7 @@ int check_device() {
         hipDeviceProp_t p;
         e = hipGetDeviceProperties(&p, dev);
         if (e != hipSuccess) return hip_fail("hipGetDeviceProperties", e);
-        state[dev] = strncmp(p.gcnArchName, "gfx950", 6) == 0 ? 1 : 2;
+        state[dev] = arch_is_gfx950(p.gcnArchName) ? 1 : 2;
         if (state[dev] == 2)
             return fail(DSA_IDX_EUNSUPPORTED, "device %d is %s; libdsaidx runs on gfx950 only", dev,
                         p.gcnArchName);
@@ -112,6 +118,13 @@ size_t ws_decode_fp8(int B, int max_seqlen) { return dsaidx::decode_workspace(B,
 extern "C" {
 
 const char *dsa_idx_version(void) { return "libdsaidx 0.1.0 (gfx950)"; }
+
+int dsa_idx_arch_supported(const char *arch_name) {
+    if (!arch_name) return fail(DSA_IDX_EINVAL, "arch_name is null");
+    if (!arch_is_gfx950(arch_name))
+        return fail(DSA_IDX_EUNSUPPORTED, "architecture %.64s; libdsaidx runs on gfx950 only", arch_name);
+    return ok();
+}
 
 const char *dsa_idx_last_error(void) { return g_err; }
 

@@ -35,13 +35,26 @@ def test_exports_every_declared_symbol(dsa):
                           "dsa_idx_v32_score_topk_varlen", "dsa_idx_v32_prefill_chunk",
                           "dsa_idx_v32_decode", "dsa_idx_v32_decode_fp8", "dsa_idx_workspace_status",
                           "dsa_idx_set_wait_budget", "dsa_idx_phase_timing", "dsa_idx_phase_times",
-                          "dsa_idx_decode_noalloc"}
+                          "dsa_idx_decode_noalloc", "dsa_idx_arch_supported"}
     for n in names:
         assert getattr(L, n) is not None
 
 
 def test_version(dsa):
     assert "gfx950" in dsa.version()
+
+
+def test_architecture_check(dsa):
+    """The device check on architecture names (no device needed): gfx950 with any feature
+    suffix runs; other gfx9 parts, near-miss names and the empty name are refused."""
+    for name in ("gfx950", "gfx950:sramecc+:xnack-", "gfx950:xnack+"):
+        dsa.arch_supported(name)
+    for name in ("gfx942", "gfx942:sramecc+:xnack-", "gfx90a", "gfx9500", "gfx95", "gfx1100", "",
+                 ":gfx950", "GFX950"):
+        with pytest.raises(dsa.DsaIdxError) as e:
+            dsa.arch_supported(name)
+        assert e.value.code == dsa.EUNSUPPORTED and "gfx950 only" in str(e.value)
+    assert dsa.lib().dsa_idx_arch_supported(None) == dsa.EINVAL
 
 
 def test_workspace_sizes(dsa):
