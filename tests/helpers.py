@@ -59,6 +59,7 @@ def check_row(t, g_idx, g_sc, ref, r, topk, exact=False):
 
 # ------------------------------------------------------------------ projection tolerance
 U32 = 2.0 ** -24   # unit roundoff of fp32
+SIGMAS = 10.0      # radius of the projection error model, in standard deviations
 
 
 def bf16_ulp(v):
@@ -67,47 +68,116 @@ def bf16_ulp(v):
     return 2.0 ** (np.floor(np.log2(a)) - 7)
 
 
-def projection_bounds(A_bits, W_bits):
-    """(exact fp64 product, deterministic fp32-summation error bound) of A @ W.
+def _rne(x):
+    from oracle import bf16_to_f64, f64_to_bf16
+    return bf16_to_f64(f64_to_bf16(x))
 
-    For a K-term sum of exact products accumulated in fp32 in any order the error is at
-    most (K - 1) * u * sum_i |a_i w_i| (u = 2^-24), to first order."""
+
+def linear_exact(A_bits, W_bits):
+    """(exact fp64 product A @ W, radius of the GPU's fp32 result around it).
+
+    The products of bf16 values are exact in fp32; only the K - 1 additions round.  With
+    rounding errors independent, of size at most u = 2^-24 relative (variance u^2/3), and
+    zero-mean terms x_i = a_i w_i, the partial sums S_j have E[S_j^2] = sum_{i<=j} x_i^2 <=
+    ||x||^2, so the accumulated error has standard deviation at most u sqrt(K/3) ||x||_2 in
+    any summation order (a blocked order makes fewer roundings and only lowers it).  The
+    radius is SIGMAS such deviations.  The deterministic worst case, (K - 1) u sum |x_i|, is
+    about 50 times larger at these shapes and would admit almost any neighbouring bf16 value."""
     from oracle import bf16_to_f64
     A = bf16_to_f64(A_bits)
     W = bf16_to_f64(W_bits)
     K = A.shape[1]
-    return A @ W, (K - 1) * U32 * (np.abs(A) @ np.abs(W))
+    return A @ W, SIGMAS * U32 * np.sqrt(K / 3.0) * np.sqrt((A * A) @ (W * W))
+
+
+def layernorm_exact(ea, ra, Wt):
+    """(LayerNorm of the exact pre-norm values ea, radius of the GPU's fp32 result).
+
+    To first order a pre-norm error d moves k_i by gamma_i / sigma (d_i - mean(d) -
+    khat_i mean(khat d)), khat = (ea - mean) / sigma; |d_j| <= ra_j bounds that term.  The
+    LayerNorm's own fp32 arithmetic adds a few u relative: 16 u (|k| + 1)."""
+    import oracle
+    ek = oracle.layernorm_f64(ea, Wt["gamma"], Wt["beta"], Wt["eps"])
+    mu = ea.mean(axis=1, keepdims=True)
+    sigma = np.sqrt(ea.var(axis=1, keepdims=True) + Wt["eps"])
+    kh = np.abs(ea - mu) / sigma
+    gam = np.abs(oracle.bf16_to_f64(Wt["gamma"]))[None, :]
+    rk = gam / sigma * (ra + ra.mean(axis=1, keepdims=True)
+                        + kh * (kh * ra).mean(axis=1, keepdims=True))
+    return ek, rk + 16 * U32 * (np.abs(ek) + 1)
+
+
+def key_exact(x_bits, Wt, chunk=8192):
+    """linear_exact + layernorm_exact of the key projection, in row chunks."""
+    e = np.empty((x_bits.shape[0], Wt["W_k"].shape[1]))
+    r = np.empty_like(e)
+    for a in range(0, x_bits.shape[0], chunk):
+        ea, ra = linear_exact(x_bits[a:a + chunk], Wt["W_k"])
+        e[a:a + chunk], r[a:a + chunk] = layernorm_exact(ea, ra, Wt)
+    return e, r
 
 
 def assert_bf16_within(g_bits, exact, err, name):
-    """GPU bf16 result within err + one bf16 ulp of the exact value; returns the fraction of
-    elements that differ from the correctly rounded value."""
-    from oracle import bf16_to_f64, f64_to_bf16
+    """GPU bf16 result within err of the exact value (for values rounded twice, where err
+    already carries the roundings)."""
+    from oracle import bf16_to_f64
     g = bf16_to_f64(g_bits).reshape(exact.shape)
-    bound = err + bf16_ulp(exact)
-    bad = np.abs(g - exact) > bound
-    assert not bad.any(), f"{name}: {bad.sum()} elements outside the fp32 accumulation bound"
-    return float((f64_to_bf16(exact) != g_bits.reshape(exact.shape)).mean())
+    bad = np.abs(g - exact) > err
+    assert not bad.any(), f"{name}: {bad.sum()} elements outside the error bound"
 
 
-def check_row_e2e(t, g_idx, g_sc, ref_e2e, r, ref_sw, r_sw, topk):
+def check_projection(g_bits, e, r, name):
+    """The GPU's bf16 value of each element is the bf16 rounding of some fp32 value within r of
+    the exact value e (so it lies in [rne(e - r), rne(e + r)]).  Returns the fraction of
+    elements that differ from the correctly rounded rne(e)."""
+    from oracle import bf16_to_f64
+    g = bf16_to_f64(g_bits).reshape(e.shape)
+    lo, hi = _rne(e - r), _rne(e + r)
+    bad = ~((g >= lo) & (g <= hi))
+    if bad.any():
+        j = np.argwhere(bad)[0]
+        raise AssertionError(f"{name}: {int(bad.sum())} elements outside the rounding radius, first "
+                             f"at {tuple(j)}: gpu {g[tuple(j)]!r}, exact {e[tuple(j)]!r}, radius {r[tuple(j)]!r}")
+    return float((g != _rne(e)).mean())
+
+
+def flip_slack(o_bits, e, r):
+    """How far the GPU's value of each element may lie from the oracle's bf16 value o_bits
+    (the rounding of e): the largest |rne(f) - o| over |f - e| <= r; zero for every element not
+    within r of a rounding boundary."""
+    from oracle import bf16_to_f64
+    o = bf16_to_f64(o_bits).reshape(e.shape)
+    return np.maximum(_rne(e + r) - o, o - _rne(e - r))
+
+
+def score_slack(q, dq, w, dw, k, dk):
+    """Bound on the change of I[s] = sum_h w_h ReLU(q_h . k_s) when each element of q [H,D],
+    w [H] and k [n,D] (fp64 values) moves by at most dq, dw, dk: with e_h = sum_i dq|k| + |q|dk
+    + dq dk (ReLU is 1-Lipschitz), |dI| <= sum_h dw_h (ReLU(q_h . k) + e_h) + |w_h| e_h."""
+    E = dq @ np.abs(k).T + np.abs(q) @ dk.T + dq @ dk.T
+    d = np.maximum(q @ k.T, 0.0)
+    return (dw[:, None] * (d + E) + np.abs(w)[:, None] * E).sum(axis=0)
+
+
+def check_row_e2e(t, g_idx, g_sc, ref, r, topk, slack):
     """End-to-end row check: GPU result against the oracle run on its own projections.
 
-    The GPU's bf16 projections may differ from the oracle's by one ulp where the exact
-    product lies within the fp32 accumulation error of a rounding boundary.  Those input
-    differences move each score by exactly |I_sw - I_e2e| (both fp64 oracle scores: on the
-    GPU's projections and on the oracle's), which is added to the per-key tolerance."""
+    slack[s] (from score_slack on the oracle's projections and their flip_slack) bounds how
+    far I[s] can move when the GPU's projections differ from the oracle's within their rounding
+    radius, which check_projection verifies for every element this row reads.  Per key the
+    tolerance is the parity rule's plus slack[s]; an index may differ between the two
+    selections only if |I[s] - tau| is within its own tolerance plus the largest tolerance
+    among the differing indices (the other side of the swap)."""
     n = min(topk, t + 1)
     g = np.asarray(g_idx)[:n]
-    I = ref_e2e["full"][r]
-    shift = np.abs(ref_sw["full"][r_sw] - I)
-    tol = 1e-3 * ref_e2e["maxabs"][r] + 1e-5 + shift
+    I = ref["full"][r]
+    tol = 1e-3 * (ref["maxabs"][r] + slack.max(initial=0.0)) + 1e-5 + slack
     if g_sc is not None:
         err = np.abs(np.asarray(g_sc)[:n].astype(np.float64) - I[g])
         bad = err > tol[g]
         assert not bad.any(), f"row {t}: end-to-end score error {err[bad].max()} beyond tolerance"
-    o = ref_e2e["idx"][r][:n]
-    tau = ref_e2e["tau"][r]
-    for s in set(g.tolist()) ^ set(o.tolist()):
-        assert abs(I[s] - tau) <= tol[s] + shift.max(), \
-            f"row {t}: index {s} differs with |I - tau| = {abs(I[s] - tau)}"
+    o = ref["idx"][r][:n]
+    diff = np.array(sorted(set(g.tolist()) ^ set(o.tolist())), dtype=np.int64)
+    if len(diff):
+        far = np.abs(I[diff] - ref["tau"][r]) > tol[diff] + tol[diff].max()
+        assert not far.any(), f"row {t}: index {diff[far][0]} differs beyond the band"

@@ -1,13 +1,17 @@
 """GPU parity at the full workload sizes, on outputs the oracle can compute one by one.
 
 * one indexer layer at T = 8,192 and at T = 65,536 (project + score_topk, the launch the
-  benchmark times): projections checked on sampled tokens against the fp32 summation
-  bound; sampled rows checked end to end (oracle projections, scores and sort) and
-  stage-wise (oracle scores and sort on the GPU's own q, k, w);
-* decode with 64 sequences of U[32768, 131072] cached keys: sampled sequences;
+  benchmark times): every element of q, k and w checked against its exact value and rounding
+  radius, with at most 1e-3 of them off the correctly rounded value; at T = 8,192 every row
+  stage-wise (oracle scores and sort on the GPU's own q, k, w), at T = 65,536 sampled rows;
+  sampled rows end to end (oracle projections, scores and sort, with the tolerance widened
+  only by what the oracle's own rounding radii allow);
+* decode with 64 sequences of U[32768, 131072] cached keys: every sequence, stage-wise and
+  end to end;
 * ragged prefill through 24 independent layers, 16 sequences of log-uniform length in
-  [2048, 32768]: every layer stage-wise on sampled rows, projections on sampled tokens, and
-  two layers end to end on the shortest sequence.
+  [2048, 32768]: every layer, every sequence stage-wise on its last row and two more,
+  projections on sampled tokens, and two layers end to end on the shortest sequence with every
+  key of it checked.
 """
 import numpy as np
 import pytest
@@ -15,10 +19,12 @@ import torch
 
 import oracle
 from synth import workloads as wl
-from tests.helpers import (U32, assert_bf16_within, check_row, check_row_e2e, projection_bounds,
-                           to_dev, to_host, weights_to_dev)
+from tests.helpers import (check_projection, check_row, check_row_e2e, flip_slack, key_exact,
+                           linear_exact, score_slack, to_dev, to_host, weights_to_dev)
 
 pytestmark = pytest.mark.gpu
+MISROUND = 1e-3    # largest fraction of projected elements off the correctly rounded value
+CHUNK = 8192
 
 
 @pytest.fixture(scope="module")
@@ -28,21 +34,38 @@ def dsa():
     return m
 
 
-def _check_projection_rows(q, k, w, act, Wt, rows):
-    """GPU q, k, w rows against the exact products (fp32 summation bound + one ulp)."""
-    eq, bq = projection_bounds(act["c_q"][rows], Wt["W_q"])
-    ew, bw = projection_bounds(act["x"][rows], Wt["W_w"])
-    ea, ba = projection_bounds(act["x"][rows], Wt["W_k"])
-    ek = oracle.layernorm_f64(ea, Wt["gamma"], Wt["beta"], Wt["eps"])
-    sigma = np.sqrt(ea.var(axis=1, keepdims=True) + Wt["eps"])
-    gam = np.abs(oracle.bf16_to_f64(Wt["gamma"]))[None, :]
-    bk = 2 * ba.max(axis=1, keepdims=True) / sigma * gam + 16 * U32 * (np.abs(ek) + 1)
-    assert_bf16_within(q[rows].reshape(len(rows), -1), eq, bq, "q")
-    assert_bf16_within(w[rows], ew, bw, "w")
-    assert_bf16_within(k[rows], ek, bk, "k")
+def _f(bits):
+    return oracle.bf16_to_f64(bits)
 
 
-def _full_layer(dsa, T, n_rows, seed):
+def _check_q(gq, c_q, Wt, keep):
+    """Every q row against its exact value (in row chunks); returns the mis-rounding fraction
+    and (exact, radius) of the rows in keep."""
+    T = c_q.shape[0]
+    bad, e_keep, r_keep = 0.0, {}, {}
+    for a in range(0, T, CHUNK):
+        e, r = linear_exact(c_q[a:a + CHUNK], Wt["W_q"])
+        bad += check_projection(gq[a:a + CHUNK].reshape(e.shape[0], -1), e, r, "q") * e.size
+        for t in keep[(keep >= a) & (keep < a + CHUNK)]:
+            e_keep[int(t)], r_keep[int(t)] = e[t - a], r[t - a]
+    return bad / (T * gq[0].size), e_keep, r_keep
+
+
+def _slack_rows(rows, oq, ow, ok, qe, qr, we, wr, ke, kr, k_off=None):
+    """score_slack of each checked row against the keys it reads (oracle bf16 values)."""
+    dk = flip_slack(ok, ke, kr)
+    kf = _f(ok)
+    out = []
+    for r, t in enumerate(rows):
+        a = 0 if k_off is None else int(k_off[r])
+        q = _f(oq[r]).reshape(32, 128)
+        dq = flip_slack(oq[r].reshape(-1), qe[r], qr[r]).reshape(32, 128)
+        dw = flip_slack(ow[r], we[r], wr[r])
+        out.append(score_slack(q, dq, _f(ow[r]), dw, kf[a:a + t + 1], dk[a:a + t + 1]))
+    return out
+
+
+def _full_layer(dsa, T, n_rows, seed, every_row):
     Wt = wl.layer_weights(layer=0, seed=seed)
     act = wl.layer_activations(T, seed=seed)
     x, cq = to_dev(act["x"]), to_dev(act["c_q"])
@@ -53,31 +76,48 @@ def _full_layer(dsa, T, n_rows, seed):
     del x, cq
     gq, gk, gw = to_host(q), to_host(k), to_host(w)
     gi, gs = idx.cpu().numpy(), sc.cpu().numpy()
+    del q, k, w, idx, sc
     rng = np.random.default_rng(T)
-    rows = np.unique(np.concatenate([[0, 1, 2046, 2047, 2048, 2049, T // 2, T - 1],
-                                     rng.integers(0, T, n_rows)]))
-    rows = rows[rows < T]
-    _check_projection_rows(gq, gk, gw, act, Wt, rows)
+    e2e_rows = np.unique(np.concatenate([[0, 1, 2046, 2047, 2048, 2049, T // 2, T - 1],
+                                         rng.integers(0, T, n_rows)]))
+    e2e_rows = e2e_rows[e2e_rows < T]
+    # projections: every element
+    print(f"layer T={T}: every projected element against its exact value", flush=True)
+    fq, qe, qr = _check_q(gq, act["c_q"], Wt, e2e_rows)
+    ke, kr = key_exact(act["x"], Wt, CHUNK)
+    fk = check_projection(gk, ke, kr, "k")
+    we, wr = linear_exact(act["x"], Wt["W_w"])
+    fw = check_projection(gw, we, wr, "w")
+    print(f"layer T={T}: mis-rounded fraction q {fq:.2e} k {fk:.2e} w {fw:.2e}", flush=True)
+    assert max(fq, fk, fw) <= MISROUND, (fq, fk, fw)
     # stage-wise: oracle scores + sort on the GPU's own q, k, w
-    ref = oracle.prefill_rows(gq, gk, gw, rows, topk=2048, full=True)
-    for r, t in enumerate(rows):
-        check_row(t, gi[t], gs[t], ref, r, 2048)
+    rows = np.arange(T) if every_row else e2e_rows
+    print(f"layer T={T}: stage-wise on {len(rows)} rows", flush=True)
+    for a in range(0, len(rows), 2048):
+        part = rows[a:a + 2048]
+        ref = oracle.prefill_rows(gq, gk, gw, part, topk=2048, full=True)
+        for r, t in enumerate(part):
+            check_row(int(t), gi[t], gs[t], ref, r, 2048)
+        del ref
     # end to end: the oracle's own projections (keys of the whole prefix of the last row)
-    kmax = int(rows.max()) + 1
-    print(f"layer T={T}: oracle keys for {kmax} tokens", flush=True)
+    kmax = int(e2e_rows.max()) + 1
+    print(f"layer T={T}: end to end on {len(e2e_rows)} rows (oracle keys for {kmax} tokens)", flush=True)
     _, ok, _ = oracle.project(act["x"][:kmax], None, Wt, want=("k",))
-    oq, _, ow = oracle.project(act["x"][rows], act["c_q"][rows], Wt, want=("q", "w"))
-    ref2 = oracle.rows(oq, ow, ok, np.zeros(len(rows), np.int64), rows, topk=2048, full=True)
-    for r, t in enumerate(rows):
-        check_row_e2e(t, gi[t], gs[t], ref2, r, ref, r, 2048)
+    oq, _, ow = oracle.project(act["x"][e2e_rows], act["c_q"][e2e_rows], Wt, want=("q", "w"))
+    ref2 = oracle.rows(oq, ow, ok, np.zeros(len(e2e_rows), np.int64), e2e_rows, topk=2048, full=True)
+    slack = _slack_rows(e2e_rows, oq, ow, ok, [qe[int(t)] for t in e2e_rows],
+                        [qr[int(t)] for t in e2e_rows], we[e2e_rows], wr[e2e_rows],
+                        ke[:kmax], kr[:kmax])
+    for r, t in enumerate(e2e_rows):
+        check_row_e2e(int(t), gi[t], gs[t], ref2, r, 2048, slack[r])
 
 
 def test_full_layer_T8192(dsa):
-    _full_layer(dsa, 8192, 56, seed=0)
+    _full_layer(dsa, 8192, 56, seed=0, every_row=True)
 
 
 def test_full_layer_T65536(dsa):
-    _full_layer(dsa, 65536, 24, seed=0)
+    _full_layer(dsa, 65536, 24, seed=0, every_row=False)
 
 
 def test_decode_64_sequences(dsa):
@@ -98,19 +138,36 @@ def test_decode_64_sequences(dsa):
     gi, gs = idx.cpu().numpy(), sc.cpu().numpy()
     new_keys = to_host(cache_d[torch.from_numpy(slots).cuda()])
     del cache_d
-    sample = np.array([0, 1, int(np.argmax(lens)), int(np.argmin(lens)), 31, 63])
-    cache[slots[sample]] = new_keys[sample]
-    # stage-wise on the GPU's q, w and the cache (with the GPU's new keys)
-    ref = oracle.rows(gq[sample], gw[sample], cache, start[sample], lens[sample] - 1, topk=2048,
-                      full=True)
-    for r, b in enumerate(sample):
-        check_row(int(lens[b]) - 1, gi[b], gs[b], ref, r, 2048)
-    # end to end: oracle projections of the new tokens
-    oq, ok, ow = oracle.project(act["x"][sample], act["c_q"][sample], Wt)
-    cache[slots[sample]] = ok
-    ref2 = oracle.rows(oq, ow, cache, start[sample], lens[sample] - 1, topk=2048, full=True)
-    for r, b in enumerate(sample):
-        check_row_e2e(int(lens[b]) - 1, gi[b], gs[b], ref2, r, ref, r, 2048)
+    # projections of the 64 new tokens
+    qe, qr = linear_exact(act["c_q"], Wt["W_q"])
+    we, wr = linear_exact(act["x"], Wt["W_w"])
+    ke, kr = key_exact(act["x"], Wt)
+    check_projection(gq.reshape(B, -1), qe, qr, "q")
+    check_projection(gw, we, wr, "w")
+    check_projection(new_keys, ke, kr, "new keys")
+    t = lens - 1
+    # stage-wise, every sequence: the GPU's q, w and the cache with the GPU's new keys
+    cache[slots] = new_keys
+    print("decode: stage-wise, 64 sequences", flush=True)
+    ref = oracle.rows(gq, gw, cache, start, t, topk=2048, full=True)
+    for b in range(B):
+        check_row(int(t[b]), gi[b], gs[b], ref, b, 2048)
+    del ref
+    # end to end, every sequence: oracle projections of the new tokens; the other cached keys
+    # are inputs (no slack)
+    oq, ok, ow = oracle.project(act["x"], act["c_q"], Wt)
+    cache[slots] = ok
+    print("decode: end to end, 64 sequences", flush=True)
+    ref2 = oracle.rows(oq, ow, cache, start, t, topk=2048, full=True)
+    dnew = flip_slack(ok, ke, kr)
+    for b in range(B):
+        kf = _f(cache[start[b]:start[b] + lens[b]])
+        dk = np.zeros_like(kf)
+        dk[-1] = dnew[b]
+        slack = score_slack(_f(oq[b]).reshape(32, 128),
+                            flip_slack(oq[b].reshape(-1), qe[b], qr[b]).reshape(32, 128),
+                            _f(ow[b]), flip_slack(ow[b], we[b], wr[b]), kf, dk)
+        check_row_e2e(int(t[b]), gi[b], gs[b], ref2, b, 2048, slack)
 
 
 def test_varlen_24_layers(dsa):
@@ -130,34 +187,42 @@ def test_varlen_24_layers(dsa):
         idx, sc = dsa.score_topk_varlen(q, k, w, cu_d, int(lens.max()), topk=2048)
         torch.cuda.synchronize()
 
-        def rows_of(t, r):
-            return to_host(t[torch.from_numpy(np.asarray(r, np.int64)).cuda()])
+        def rows_of(tns, r):
+            return to_host(tns[torch.from_numpy(np.asarray(r, np.int64)).cuda()])
         # projections on sampled tokens
         toks = np.unique(rng.integers(0, total, 16))
-        _check_projection_rows(rows_of(q, toks), rows_of(k, toks), rows_of(w, toks),
-                               {"x": act["x"][toks], "c_q": act["c_q"][toks]}, Wt,
-                               np.arange(len(toks)))
-        # stage-wise rows of two sequences
-        for b in (shortest, int(rng.integers(0, B))):
+        check_projection(rows_of(q, toks).reshape(len(toks), -1),
+                         *linear_exact(act["c_q"][toks], Wt["W_q"]), "q")
+        check_projection(rows_of(w, toks), *linear_exact(act["x"][toks], Wt["W_w"]), "w")
+        check_projection(rows_of(k, toks), *key_exact(act["x"][toks], Wt), "k")
+        # stage-wise: every sequence, its last row and two more
+        gk = to_host(k)
+        srows, soff, grows = [], [], []
+        for b in range(B):
             a0, L = int(cu[b]), int(lens[b])
-            rows = np.unique(np.concatenate([[0, 2047, L - 1], rng.integers(0, L, 5)]))
-            rows = rows[rows < L]
-            gk = to_host(k[a0:a0 + L])
-            gi = idx[a0 + rows].cpu().numpy()
-            gs = sc[a0 + rows].cpu().numpy()
-            ref = oracle.rows(rows_of(q, a0 + rows), rows_of(w, a0 + rows), gk,
-                              np.zeros(len(rows), np.int64), rows, topk=2048, full=True)
-            for r, t in enumerate(rows):
-                check_row(int(t), gi[r], gs[r], ref, r, 2048)
+            for tt in sorted({L - 1, int(rng.integers(0, L)), int(rng.integers(0, L))}):
+                srows.append(tt)
+                soff.append(a0)
+                grows.append(a0 + tt)
+        srows, soff, grows = (np.asarray(v, np.int64) for v in (srows, soff, grows))
+        gi = idx[torch.from_numpy(grows).cuda()].cpu().numpy()
+        gs = sc[torch.from_numpy(grows).cuda()].cpu().numpy()
+        ref = oracle.rows(rows_of(q, grows), rows_of(w, grows), gk, soff, srows, topk=2048, full=True)
+        for r, tt in enumerate(srows):
+            check_row(int(tt), gi[r], gs[r], ref, r, 2048)
+        del ref
         if layer in (0, layers - 1):
-            # end to end on the shortest sequence: oracle projections of all its tokens
+            # end to end on the shortest sequence, with every key of it checked
             a0, L = int(cu[shortest]), int(lens[shortest])
+            ke, kr = key_exact(act["x"][a0:a0 + L], Wt)
+            check_projection(gk[a0:a0 + L], ke, kr, "k")
             oq, ok, ow = oracle.project(act["x"][a0:a0 + L], act["c_q"][a0:a0 + L], Wt)
-            rows = np.array(sorted(set([0, 1, 2047, L // 2, L - 1]) & set(range(L))))
+            rows = np.array(sorted({0, 1, 2047, L // 2, L - 1} & set(range(L))))
             gi = idx[a0 + rows].cpu().numpy()
             gs = sc[a0 + rows].cpu().numpy()
             ref2 = oracle.prefill_rows(oq, ok, ow, rows, topk=2048, full=True)
-            ref_sw = oracle.rows(rows_of(q, a0 + rows), rows_of(w, a0 + rows), to_host(k[a0:a0 + L]),
-                                 np.zeros(len(rows), np.int64), rows, topk=2048, full=True)
-            for r, t in enumerate(rows):
-                check_row_e2e(int(t), gi[r], gs[r], ref2, r, ref_sw, r, 2048)
+            qe, qr = linear_exact(act["c_q"][a0 + rows], Wt["W_q"])
+            we, wr = linear_exact(act["x"][a0 + rows], Wt["W_w"])
+            slack = _slack_rows(rows, oq[rows], ow[rows], ok, qe, qr, we, wr, ke, kr)
+            for r, tt in enumerate(rows):
+                check_row_e2e(int(tt), gi[r], gs[r], ref2, r, 2048, slack[r])

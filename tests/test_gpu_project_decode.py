@@ -5,7 +5,7 @@ import torch
 
 import oracle
 from synth import workloads as wl
-from tests.helpers import (U32, assert_bf16_within, check_row, projection_bounds, to_dev, to_host,
+from tests.helpers import (check_projection, check_row, key_exact, linear_exact, to_dev, to_host,
                            weights_to_dev)
 
 pytestmark = pytest.mark.gpu
@@ -24,19 +24,11 @@ def test_project_matches_oracle(dsa, T):
     act = wl.layer_activations(T, seed=T)
     q, k, w = dsa.project(to_dev(act["x"]), to_dev(act["c_q"]), weights_to_dev(Wt))
     torch.cuda.synchronize()
-    # q and w: the fp64 product and the fp32 accumulation bound
-    eq, bq = projection_bounds(act["c_q"], Wt["W_q"])
-    ew, bw = projection_bounds(act["x"], Wt["W_w"])
-    fq = assert_bf16_within(to_host(q).reshape(T, -1), eq, bq, "q")
-    fw = assert_bf16_within(to_host(w), ew, bw, "w")
-    # k: LayerNorm of the fp64 product (the oracle's own LayerNorm); the pre-norm error e
-    # moves (a - mean) by at most 2 max(e) and is scaled by |gamma| / sigma
-    ea, ba = projection_bounds(act["x"], Wt["W_k"])
-    ek = oracle.layernorm_f64(ea, Wt["gamma"], Wt["beta"], Wt["eps"])
-    sigma = np.sqrt(ea.var(axis=1, keepdims=True) + Wt["eps"])
-    gam = np.abs(oracle.bf16_to_f64(Wt["gamma"]))[None, :]
-    bk = 2 * ba.max(axis=1, keepdims=True) / sigma * gam + 16 * U32 * (np.abs(ek) + 1)
-    fk = assert_bf16_within(to_host(k), ek, bk, "k")
+    # each element: the bf16 rounding of an fp32 value within the accumulation radius of the
+    # exact fp64 product (k: of its exact LayerNorm)
+    fq = check_projection(to_host(q).reshape(T, -1), *linear_exact(act["c_q"], Wt["W_q"]), "q")
+    fw = check_projection(to_host(w), *linear_exact(act["x"], Wt["W_w"]), "w")
+    fk = check_projection(to_host(k), *key_exact(act["x"], Wt), "k")
     print(f"T={T}: fraction not correctly rounded q {fq:.1e} k {fk:.1e} w {fw:.1e}", flush=True)
     assert max(fq, fk, fw) < 1e-2
 
@@ -87,13 +79,10 @@ def test_decode_small(dsa):
                       full=True)
     for b, L in enumerate(lens):
         check_row(L - 1, r["idx"][b], r["sc"][b], ref, b, 2048)
-    # the new token's key in the cache is the oracle's projection of it (within one ulp)
-    ea, ba = projection_bounds(r["act"]["x"], r["Wt"]["W_k"])
-    ek = oracle.layernorm_f64(ea, r["Wt"]["gamma"], r["Wt"]["beta"], r["Wt"]["eps"])
-    sigma = np.sqrt(ea.var(axis=1, keepdims=True) + r["Wt"]["eps"])
-    gam = np.abs(oracle.bf16_to_f64(r["Wt"]["gamma"]))[None, :]
-    bk = 2 * ba.max(axis=1, keepdims=True) / sigma * gam + 16 * U32 * (np.abs(ek) + 1)
-    assert_bf16_within(r["cache"][r["start"] + np.asarray(lens) - 1], ek, bk, "new keys")
+    # the new token's key in the cache: the rounding of a value within the accumulation
+    # radius of the exact projection
+    check_projection(r["cache"][r["start"] + np.asarray(lens) - 1], *key_exact(r["act"]["x"], r["Wt"]),
+                     "new keys")
 
 
 def test_decode_equals_prefill_last_row(dsa):
