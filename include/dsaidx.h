@@ -150,7 +150,7 @@ int dsa_idx_project(const dsa_idx_weights *weights, const dsa_idx_bf16 *x, int64
  * above it, and the top-k is selected exactly from those; a row the threshold cannot decide
  * (too few or too many kept keys) is scored again in full into a bounded scratch row.  The
  * result equals the full sort of each row whatever the data.  The workspace
- * (DSA_IDX_OP_SCORE_TOPK) grows linearly in T: about 3.7 GB at T = 65,536, 4.8 GB at
+ * (DSA_IDX_OP_SCORE_TOPK) grows linearly in T: about 3.8 GB at T = 65,536, 4.3 GB at
  * T = 1,048,576.  Its first 32-bit word is the status that dsa_idx_workspace_status() reads.
  * Limit: T <= 16,777,216. */
 int dsa_idx_score_topk(const dsa_idx_bf16 *q, const dsa_idx_bf16 *k, const dsa_idx_bf16 *w,
@@ -293,8 +293,9 @@ int dsa_idx_sparse_mla(const dsa_idx_bf16 *q, const dsa_idx_bf16 *kv, const int3
  * (1,536 -> 8,192 = 64 heads x 128), one LayerNorm key from the hidden state, head weights
  * 7,168 -> 64, I = sum over the 64 heads of w_h ReLU(q_h . k), top-k per query.
  * The rotary step (this library's reading): dims (2i, 2i+1), i < 32, of every query head and
- * of the key turn by the angle pos * rope_theta^(-2i/64), on the projections as rounded to
- * bf16, and the result is rounded to bf16 (nearest even) again; dims 64..127 do not turn. */
+ * of the key (after its LayerNorm) turn by the angle pos * rope_theta^(-2i/64), applied to the
+ * fp32 projections, and each result is rounded to bf16 (nearest even) once; dims 64..127 do
+ * not turn. */
 #define DSA_IDX_V32_HEADS 64
 #define DSA_IDX_V32_QOUT 8192
 
@@ -303,7 +304,11 @@ int dsa_idx_sparse_mla(const dsa_idx_bf16 *q, const dsa_idx_bf16 *kv, const int3
  *       beta [128], ln_eps > 0; x [T][ldx], c_q [T][ldc] as for dsa_idx_project;
  *   pos0 >= 0, rope_theta > 0 (10000 in the oracle's reading);
  *   q [T][64][128], k [T][128], w [T][64] bf16 out (16-byte aligned).
- * Needs dsa_idx_workspace_size(DSA_IDX_OP_V32_PROJECT, T, ...) bytes of workspace. */
+ * One pass: x is read once for the key and all 64 head weights, and the rotary step runs in
+ * the projection epilogues from a (cos, sin) table the call forms first in the workspace.
+ * Needs dsa_idx_workspace_size(DSA_IDX_OP_V32_PROJECT, T, ...) bytes of workspace: W_q
+ * transposed (25.2 MB) for T > 64, fp32 split-K partial sums for T <= 64, then 256 B per token
+ * for the table. */
 int dsa_idx_v32_project(const dsa_idx_weights *wt, const dsa_idx_bf16 *x, int64_t ldx,
                         const dsa_idx_bf16 *c_q, int64_t ldc, int64_t T, int64_t pos0, float rope_theta,
                         dsa_idx_bf16 *q, dsa_idx_bf16 *k, dsa_idx_bf16 *w, void *ws, size_t ws_bytes,

@@ -322,8 +322,8 @@ def sparse_mla(q, kv, idx, row0=None, scale=1.0 / np.sqrt(192.0)):
 # q = c_q W_q (1,536 -> 8,192 = 64 heads x 128), k = LayerNorm(x W_k) (7,168 -> 128),
 # w = x W_w (7,168 -> 64), I = sum over the 64 heads; the rotary step turns dims (2i, 2i+1),
 # i < 32, of every query head and of the key by the angle pos * theta^(-2i/64) (theta = 10^4),
-# on the stored bf16 projections, and its result is rounded to bf16 again.  Dims 64..127 are
-# not rotated.
+# applied to the exact projection (for k after its LayerNorm), and the rotated vector is rounded
+# to bf16 once, as the K3.1 projections are.  Dims 64..127 are not rotated.
 V32_H, V32_QOUT, V32_ROT, V32_THETA = 64, 8192, 64, 10000.0
 
 
@@ -351,18 +351,16 @@ def rope_f64(v, pos, rot=V32_ROT, theta=V32_THETA):
 
 def project_v32(x, c_q, Wt, pos0=0, theta=V32_THETA, want=("q", "k", "w")):
     """q [T,64,128], k [T,128], w [T,64] (bf16 patterns) of the DeepSeek-V3.2-shaped indexer
-    for tokens at positions pos0 .. pos0 + T - 1: the projections rounded to bf16, then the
-    rotary step on q and k, rounded to bf16 again."""
+    for tokens at positions pos0 .. pos0 + T - 1: the rotary step on the exact fp64 q and on the
+    exact LayerNorm of the key, each result rounded to bf16 once."""
     T = (x if x is not None else c_q).shape[0]
     pos = pos0 + np.arange(T, dtype=np.int64)
     q = k = w = None
     if "q" in want:
-        qb = f64_to_bf16(linear_f64(c_q, Wt["W_q"])).reshape(T, V32_H, D)
-        q = f64_to_bf16(rope_f64(bf16_to_f64(qb), pos, theta=theta))
+        q = f64_to_bf16(rope_f64(linear_f64(c_q, Wt["W_q"]).reshape(T, V32_H, D), pos, theta=theta))
     if "k" in want:
         lin = linear_f64(x, Wt["W_k"])
-        kb = f64_to_bf16(layernorm_f64(lin, Wt["gamma"], Wt["beta"], Wt["eps"]))
-        k = f64_to_bf16(rope_f64(bf16_to_f64(kb), pos, theta=theta))
+        k = f64_to_bf16(rope_f64(layernorm_f64(lin, Wt["gamma"], Wt["beta"], Wt["eps"]), pos, theta=theta))
     if "w" in want:
         w = f64_to_bf16(linear_f64(x, Wt["W_w"]))
     return q, k, w

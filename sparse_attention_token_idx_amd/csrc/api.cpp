@@ -174,7 +174,7 @@ int dsa_idx_workspace_size(int op, int64_t total_tokens, int B, int max_seqlen, 
         }
         case DSA_IDX_OP_V32_PROJECT:
             if (total_tokens < 0) return fail(DSA_IDX_EINVAL, "T=%lld < 0", (long long)total_tokens);
-            *bytes = dsaidx::project_workspace(total_tokens);   // the halves reuse it in turn
+            *bytes = dsaidx::project_workspace(total_tokens, DSA_IDX_V32_QOUT, DSA_IDX_V32_HEADS, true);
             return ok();
         case DSA_IDX_OP_SPARSE_MLA: {
             if (total_tokens < 0) return fail(DSA_IDX_EINVAL, "T=%lld < 0", (long long)total_tokens);
@@ -446,27 +446,19 @@ int dsa_idx_v32_project(const dsa_idx_weights *wt, const dsa_idx_bf16 *x, int64_
     for (const void *p : ptrs)
         if (!aligned16(p)) return fail(DSA_IDX_EINVAL, "tensor pointer %p is not 16-byte aligned", p);
     if (T > (int64_t)INT32_MAX * 128) return fail(DSA_IDX_EUNSUPPORTED, "T=%lld too large", (long long)T);
-    const size_t need = dsaidx::project_workspace(T);
-    if (need && (!ws || ws_bytes < need))
+    const size_t need = dsaidx::project_workspace(T, DSA_IDX_V32_QOUT, DSA_IDX_V32_HEADS, true);
+    if (!ws || ws_bytes < need)
         return fail(DSA_IDX_EWORKSPACE, "workspace %zu bytes < %zu needed", ws ? ws_bytes : (size_t)0, need);
-    if (need && !aligned16(ws)) return fail(DSA_IDX_EINVAL, "workspace must be 16-byte aligned");
+    if (!aligned16(ws)) return fail(DSA_IDX_EINVAL, "workspace must be 16-byte aligned");
     int r = check_device();
     if (r) return r;
     const hipStream_t st = reinterpret_cast<hipStream_t>(stream);
-    constexpr int64_t kHalf = DSA_IDX_QOUT;   // q columns and w columns of one half: 4,096 and 32
-    // first half: q columns 0..4,095, the key, w columns 0..31; second: the rest, no key
-    hipError_t e = dsaidx::launch_project_ex(x, ldx, c_q, ldc, T, wt->W_q, DSA_IDX_V32_QOUT, wt->W_k, wt->W_w,
-                                             DSA_IDX_V32_HEADS, wt->ln_gamma, wt->ln_beta, wt->ln_eps, q,
-                                             DSA_IDX_V32_QOUT, k, nullptr, w, DSA_IDX_V32_HEADS,
-                                             static_cast<float *>(ws), st);
+    // one pass: all 8,192 q columns, the key and all 64 w columns, the rotary step in the epilogues
+    hipError_t e = dsaidx::launch_project_ex(x, ldx, c_q, ldc, T, wt->W_q, DSA_IDX_V32_QOUT, DSA_IDX_V32_QOUT,
+                                             wt->W_k, wt->W_w, DSA_IDX_V32_HEADS, DSA_IDX_V32_HEADS, wt->ln_gamma,
+                                             wt->ln_beta, wt->ln_eps, q, DSA_IDX_V32_QOUT, k, nullptr, w,
+                                             DSA_IDX_V32_HEADS, pos0, (double)rope_theta, static_cast<float *>(ws), st);
     if (e != hipSuccess) return hip_fail("project launch", e);
-    e = dsaidx::launch_project_ex(x, ldx, c_q, ldc, T, wt->W_q + kHalf, DSA_IDX_V32_QOUT, wt->W_k,
-                                  wt->W_w + DSA_IDX_HEADS, DSA_IDX_V32_HEADS, wt->ln_gamma, wt->ln_beta, wt->ln_eps,
-                                  q + kHalf, DSA_IDX_V32_QOUT, nullptr, nullptr, w + DSA_IDX_HEADS,
-                                  DSA_IDX_V32_HEADS, static_cast<float *>(ws), st);
-    if (e != hipSuccess) return hip_fail("project launch", e);
-    e = dsaidx::launch_rope(q, DSA_IDX_V32_QOUT, DSA_IDX_V32_HEADS, k, DSA_IDX_DIM, T, pos0, (double)rope_theta, st);
-    if (e != hipSuccess) return hip_fail("rotary launch", e);
     return ok();
 }
 

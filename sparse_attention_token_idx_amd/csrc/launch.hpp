@@ -111,19 +111,17 @@ hipError_t prefill_phase_times(double *ms, int *count, int n);
 void prefill_set_wait_budget(int polls);
 int prefill_wait_budget();
 
-// launch_project with explicit row strides: of W_q (ldwq) and q (ldq) for the 4,096 q columns
-// it computes, of W_w (ldww) and w (ldwo) for the 32 w columns; k_base may be nullptr (no key).
+// launch_project generalised: nq q columns (4,096 or 8,192) and hw w columns (32 or 64), with the
+// row strides of W_q (ldwq), q (ldq), W_w (ldww) and w (ldwo); k_base may be nullptr (no key).
+// theta > 0 applies the rotary step to dims 0..63 of every q head and of the key, token t at
+// position pos0 + t, in the epilogues (the workspace then also holds the (cos, sin) table).
+size_t project_workspace(int64_t T, int nq, int hw, bool rope);
 hipError_t launch_project_ex(const uint16_t *x, int64_t ldx, const uint16_t *c_q, int64_t ldc,
-                             int64_t T, const uint16_t *W_q, int64_t ldwq, const uint16_t *W_k,
-                             const uint16_t *W_w, int64_t ldww, const uint16_t *gamma,
+                             int64_t T, const uint16_t *W_q, int64_t ldwq, int nq, const uint16_t *W_k,
+                             const uint16_t *W_w, int64_t ldww, int hw, const uint16_t *gamma,
                              const uint16_t *beta, float eps, uint16_t *q, int64_t ldq,
                              uint16_t *k_base, const int64_t *k_slot, uint16_t *w, int64_t ldwo,
-                             float *ws, hipStream_t stream);
-// The rotary step of the 64-head indexer, in place: dims (2i, 2i+1), i < 32, of every head of q
-// (heads x 128 per row, rows ldq apart) and of k (rows ldk apart; either may be nullptr), token
-// t at position pos0 + t.
-hipError_t launch_rope(uint16_t *q, int64_t ldq, int heads, uint16_t *k, int64_t ldk, int64_t T, int64_t pos0,
-                       double theta, hipStream_t stream);
+                             int64_t pos0, double theta, float *ws, hipStream_t stream);
 
 // ---- row top-k (topk.hip).  Prefill: rows = T (dense, query row g at position pos0 + g)
 // or the packed total (varlen, longest sequence max_len), scores in the triangular layout of

@@ -13,12 +13,21 @@
 // The k/w product (N = 160) keeps whole rows in one wave, so the LayerNorm over the 128
 // key columns runs in the epilogue on the fp32 accumulators before rounding.
 //
+// The DeepSeek-V3.2-shaped indexer (64 heads: 8,192 q columns and 64 w columns; a rotary step
+// on dims 0..63 of every q head and of the key, "Kimi K3.1 Pro vs Gemma 4 31B" page, RoPE row)
+// runs through the same kernels in one pass: the rotation is applied in the epilogues to the
+// fp32 results (for k after the LayerNorm), with (cos, sin) of every (token, pair) taken from a
+// table formed once per call in fp64, and each element is rounded to bf16 once.  Pair (2i, 2i+1)
+// sits in two neighbouring lanes of an MFMA result tile, which swap values with one exchange.
+//
 // A handful of tokens (a decode step: T <= kSkinnyT) would give the tiled GEMM a handful
 // of workgroups, each streaming whole weight matrices.  There the work is tiny and the
 // weights are the bytes that matter, so K is split over many workgroups instead: each one
 // runs the same tiled core on one 64-row tile and its K-slice and writes fp32 partial sums
 // to the workspace; a second kernel adds the slices in order (deterministic), then
 // rounds, with the LayerNorm for k.
+#include <utility>
+
 #include "common.hpp"
 #include "launch.hpp"
 
@@ -28,6 +37,26 @@ namespace {
 constexpr int kBK = 64;  // k per LDS tile (8 chunks of 8)
 
 __device__ __forceinline__ int swz(int row, int chunk) { return row * 64 + 8 * (chunk ^ (row & 7)); }
+
+constexpr int kRotPairs = 32;   // rotated pairs per head (dims 0..63)
+
+// The rotation of pair (x, y) by (c, s), for the element this lane holds: x' = x c - y s (even
+// dim), y' = x s + y c (odd dim); `other` is the pair's other element.
+__device__ __forceinline__ float rotate(float v, float other, float2 cs, bool odd) {
+    return odd ? fmaf(other, cs.y, v * cs.x) : fmaf(v, cs.x, -(other * cs.y));
+}
+
+// (cos, sin) of angle (pos0 + t) theta^(-2i/64), t < T, i < 32: the angle and its sine and cosine in
+// fp64 (positions reach 2^20, where an fp32 angle would be off by tenths of a radian), stored in fp32.
+__global__ __launch_bounds__(256) void rope_table_kernel(float2 *tab, int64_t T, int64_t pos0, double theta) {
+    const int64_t g = (int64_t)blockIdx.x * 256 + threadIdx.x;
+    if (g >= T * kRotPairs) return;
+    const int i = (int)(g % kRotPairs);
+    const double ang = (double)(pos0 + g / kRotPairs) * pow(theta, -2.0 * i / (2 * kRotPairs));
+    double sn, cs;
+    sincos(ang, &sn, &cs);
+    tab[g] = make_float2((float)cs, (float)sn);
+}
 
 template <int BM, int BN>
 struct GemmSmem {
@@ -133,14 +162,15 @@ struct GemmCore {
 };
 
 // ---------------------------------------------------------------- q for many tokens
-// q = bf16(c_q . W_q) with W_q first transposed into the workspace (W_qT [4096][1536], a
-// few microseconds), so that both operands are k-contiguous and every tile can be copied
-// from global memory into LDS by the direct global->LDS loads (16 bytes per lane, no
-// registers, no VALU transpose).  256 x 256 block tiles, 4 waves of 128 x 128 (the 64
-// accumulator tiles live in AGPRs), K-steps of 32 through a ring of kQStages LDS stages
-// refilled kQStages steps ahead; the next step's MFMA fragments are read while the current
-// step's MFMAs run.  One wave instruction fills 1 KB = 16 rows of 64 bytes, so each MFMA
-// fragment read is one contiguous 1 KB (no bank conflicts, no swizzle).
+// q = bf16(c_q . W_q) with W_q first transposed into the workspace (W_qT [N][1536], a few
+// microseconds), so that both operands are k-contiguous and every tile can be copied from
+// global memory into LDS by the direct global->LDS loads (16 bytes per lane, no registers, no
+// VALU transpose).  256 x 256 block tiles over 8 waves, two per SIMD, each a 128 x 64 quadrant
+// (32 accumulator tiles), so that one wave's MFMAs run while the other waits at a barrier or
+// for LDS; K-steps of 32 through a ring of kQStages LDS stages refilled kQStages steps ahead;
+// the next step's MFMA fragments are read while the current step's MFMAs run.  One wave
+// instruction fills 1 KB = 16 rows of 64 bytes, so each MFMA fragment read is one contiguous
+// 1 KB (no bank conflicts, no swizzle).
 typedef __attribute__((address_space(3))) void lds_void;
 constexpr int kQBM = 256, kQBN = 256, kQKB = 32, kQStages = 3;
 constexpr int kQStage = (kQBM + kQBN) * kQKB;   // bf16 per stage
@@ -171,47 +201,64 @@ __global__ __launch_bounds__(256) void transpose_wq_kernel(const uint16_t *__res
     *reinterpret_cast<u32x4 *>(WqT + (int64_t)(n0 + r) * kQLat + k0 + c + 8) = o1;
 }
 
-__global__ __launch_bounds__(256, 1) void proj_q_kernel(const uint16_t *__restrict__ cq, int64_t ldc,
-                                                        int64_t T, const uint16_t *__restrict__ WqT,
-                                                        uint16_t *__restrict__ q, int64_t ldq) {
-    constexpr int SM = 8, SN = 8, S = kQStages, KB = kQKB;
+struct QArgs {
+    const uint16_t *cq;
+    int64_t ldc, T;
+    const uint16_t *WqT;        // [N][1536]
+    int N;                      // q columns: 4,096 or 8,192
+    uint16_t *q;
+    int64_t ldq;
+    const float2 *rope;         // [T][32] (cos, sin), or nullptr: no rotary step
+};
+
+// Tile of workgroup `bid`: m-block bid / ntn, n-block bid % ntn.  Workgroup i runs on XCD i mod 8,
+// so each XCD only ever needs the ntn / 8 W_qT blocks n = x, x + 8, ... (1.5 or 3 MB, resident in
+// its L2 for the whole launch), and the tiles of one m-block that share an XCD run together.
+__device__ __forceinline__ bool q_tile(int bid, int64_t qt, int ntn, int64_t &mb, int &nb) {
+    mb = bid / ntn;
+    nb = bid % ntn;
+    return mb < qt;
+}
+
+__global__ __launch_bounds__(512, 1) void proj_q_kernel(QArgs a) {
+    constexpr int SM = 8, SN = 4, S = kQStages, KB = kQKB;
     extern __shared__ __align__(16) uint16_t qsm[];
-    const int ntn = kQOut / kQBN;
-    const int64_t m0 = (int64_t)(blockIdx.x / ntn) * kQBM;
-    const int n0 = (blockIdx.x % ntn) * kQBN;
+    const int ntn = a.N / kQBN;
+    int64_t mb;
+    int nb;
+    if (!q_tile(blockIdx.x, (a.T + kQBM - 1) / kQBM, ntn, mb, nb)) return;
+    const int64_t m0 = mb * kQBM, T = a.T;
+    const int n0 = nb * kQBN;
+    const uint16_t *__restrict__ cq = a.cq;
+    const uint16_t *__restrict__ WqT = a.WqT;
+    const int64_t ldc = a.ldc;
     const int tid = threadIdx.x, wave = tid >> 6, lane = tid & 63;
-    const int wm = wave >> 1, wn = wave & 1, l16 = lane & 15, lg = lane >> 4;
+    const int wm = wave >> 2, wn = wave & 3, l16 = lane & 15, lg = lane >> 4;
     f32x4 acc[SM][SN];
 #pragma unroll
     for (int i = 0; i < SM; ++i)
 #pragma unroll
         for (int j = 0; j < SN; ++j) acc[i][j] = f32x4{0.f, 0.f, 0.f, 0.f};
-
-    // stage of K-step kt: A rows 0..255 then B rows 0..255, 32 bf16 each; wave w fills rows
-    // 64w .. 64w+63 of both, 8 load instructions per wave (rows past T repeat row T - 1)
     auto issue = [&](int kt) {
         uint16_t *st = qsm + (kt % S) * kQStage;
         const int k0 = kt * KB;
 #pragma unroll
-        for (int i = 0; i < 4; ++i) {
-            const int row = 64 * wave + 16 * i + (lane >> 2);
+        for (int i = 0; i < 2; ++i) {
+            const int row = 32 * wave + 16 * i + (lane >> 2);
             const int kc = 8 * (lane & 3);
             const int64_t ga = m0 + row < T ? m0 + row : T - 1;
             __builtin_amdgcn_global_load_lds(static_cast<const void *>(cq + ga * ldc + k0 + kc),
-                                             (lds_void *)(st + (64 * wave + 16 * i) * KB), 16, 0, 0);
+                                             (lds_void *)(st + (32 * wave + 16 * i) * KB), 16, 0, 0);
             __builtin_amdgcn_global_load_lds(static_cast<const void *>(WqT + (int64_t)(n0 + row) * kQLat + k0 + kc),
-                                             (lds_void *)(st + kQBM * KB + (64 * wave + 16 * i) * KB),
+                                             (lds_void *)(st + kQBM * KB + (32 * wave + 16 * i) * KB),
                                              16, 0, 0);
         }
     };
-    // Until this wave's loads of stage kt are done (8 per later stage may stay in flight),
-    // then this wave's fragment reads of older stages (before anyone refills them), then a
-    // barrier without the fence of __syncthreads (which would wait for every load in flight).
     const int nk = kQLat / KB;
     auto wait_stage = [&](int kt) {
         const int later = min(S - 2, nk - 1 - kt);
-        if (later >= 2) asm volatile("s_waitcnt vmcnt(16)" ::: "memory");
-        else if (later == 1) asm volatile("s_waitcnt vmcnt(8)" ::: "memory");
+        if (later >= 2) asm volatile("s_waitcnt vmcnt(8)" ::: "memory");
+        else if (later == 1) asm volatile("s_waitcnt vmcnt(4)" ::: "memory");
         else asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
         asm volatile("s_waitcnt lgkmcnt(0)\n\ts_barrier" ::: "memory");
     };
@@ -223,9 +270,8 @@ __global__ __launch_bounds__(256, 1) void proj_q_kernel(const uint16_t *__restri
             fa[p][i] = *reinterpret_cast<const u32x4 *>(st + (wm * 128 + 16 * i + l16) * KB + 8 * lg);
 #pragma unroll
         for (int j = 0; j < SN; ++j)
-            fb[p][j] = *reinterpret_cast<const u32x4 *>(st + kQBM * KB + (wn * 128 + 16 * j + l16) * KB + 8 * lg);
+            fb[p][j] = *reinterpret_cast<const u32x4 *>(st + kQBM * KB + (wn * 64 + 16 * j + l16) * KB + 8 * lg);
     };
-    // the ring holds S stages; step k refills the slot of stage k, already in registers
 #pragma unroll
     for (int p = 0; p < S; ++p)
         if (p < nk) issue(p);
@@ -233,7 +279,7 @@ __global__ __launch_bounds__(256, 1) void proj_q_kernel(const uint16_t *__restri
     read_frags(0, 0);
     for (int kt = 0; kt < nk; kt += 2) {
 #pragma unroll
-        for (int h = 0; h < 2; ++h) {   // fragments of step kt + h in register set h
+        for (int h = 0; h < 2; ++h) {
             const int k = kt + h;
             if (k < nk) {
                 if (k + 1 < nk) {
@@ -248,23 +294,36 @@ __global__ __launch_bounds__(256, 1) void proj_q_kernel(const uint16_t *__restri
             }
         }
     }
+    const bool odd = l16 & 1;
+    const bool rot = a.rope && (wn & 1) == 0;   // this wave's 64 columns are dims 0..63 of a head
 #pragma unroll
     for (int i = 0; i < SM; ++i)
 #pragma unroll
         for (int r = 0; r < 4; ++r) {
             const int64_t row = m0 + wm * 128 + 16 * i + 4 * lg + r;
+            const int64_t rr = row < T ? row : T - 1;
+            float v[SN];
+#pragma unroll
+            for (int j = 0; j < SN; ++j) v[j] = acc[i][j][r];
+            if (rot) {
+#pragma unroll
+                for (int j = 0; j < SN; ++j) {
+                    const float other = __shfl_xor(v[j], 1, 64);
+                    v[j] = rotate(v[j], other, a.rope[rr * kRotPairs + 8 * j + (l16 >> 1)], odd);
+                }
+            }
             if (row >= T) continue;
 #pragma unroll
             for (int j = 0; j < SN; ++j)
-                q[row * ldq + n0 + wn * 128 + 16 * j + l16] = (uint16_t)f32_to_bf16(acc[i][j][r]);
+                a.q[row * a.ldq + n0 + wn * 64 + 16 * j + l16] = (uint16_t)f32_to_bf16(v[j]);
         }
 }
 
-static_assert(kQLat % (2 * kQKB) == 0 && kQOut % kQBN == 0, "q tiles");
+static_assert(kQLat % (2 * kQKB) == 0 && kQOut % kQBN == 0 && kQBN % kDim == 0, "q tiles");
 
-// [k | w] = x . [W_k | W_w] (N = 128 + 32), LayerNorm on the k part: 128-row tiles, each
-// of the 4 waves owns 32 full rows.  The two weight matrices are read as one [7168][160]
-// operand whose first 16 column-chunks come from W_k and the last 4 from W_w.
+// [k | w] = x . [W_k | W_w] (N = 128 + HW, HW = 32 or 64 w columns), LayerNorm on the k part:
+// 128-row tiles, each of the 4 waves owns 32 full rows.  The two weight matrices are read as one
+// [7168][128 + HW] operand whose first 16 column-chunks come from W_k and the rest from W_w.
 struct KWArgs {
     const uint16_t *x;
     int64_t ldx;
@@ -279,10 +338,12 @@ struct KWArgs {
     uint16_t *w;
     int64_t ldww;               // row stride of W_w (elements)
     int64_t ldwo;               // row stride of w
+    const float2 *rope;         // [T][32] (cos, sin) for the key, or nullptr: no rotary step
 };
 
-__global__ __launch_bounds__(256) void proj_kw_kernel(KWArgs a) {
-    constexpr int BM = 128, BN = 160, SM = 2, SN = 10;
+template <int HW>
+__global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2, 2))) void proj_kw_kernel(KWArgs a) {
+    constexpr int BM = 128, BN = kDim + HW, SM = 2, SN = BN / 16;
     extern __shared__ __align__(16) unsigned char smem_raw[];
     auto &sm = *reinterpret_cast<GemmSmem<BM, BN> *>(smem_raw);
     const int64_t m0 = (int64_t)blockIdx.x * BM;
@@ -300,7 +361,7 @@ __global__ __launch_bounds__(256) void proj_kw_kernel(KWArgs a) {
     u32x4 ra[A_CHUNKS];
     u32x4 rb[8];
     const bool b_thread = tid < BN;
-    const int bkb = tid & 7, bnb = tid >> 3;   // bnb in 0..19: 0..15 -> W_k, 16..19 -> W_w
+    const int bkb = tid & 7, bnb = tid >> 3;   // bnb < 16 -> W_k, the rest -> W_w
     auto load = [&](int kt) {
         const int k0 = kt * kBK;
 #pragma unroll
@@ -379,6 +440,7 @@ __global__ __launch_bounds__(256) void proj_kw_kernel(KWArgs a) {
 #pragma unroll
         for (int r = 0; r < 4; ++r) {
             const int64_t row = m0 + wave * 32 + 16 * i + 4 * lg + r;
+            const int64_t rr = row < a.T ? row : a.T - 1;
             float s = 0.f;
 #pragma unroll
             for (int j = 0; j < 8; ++j) s += acc[i][j][r];
@@ -394,16 +456,25 @@ __global__ __launch_bounds__(256) void proj_kw_kernel(KWArgs a) {
 #pragma unroll
             for (int d = 1; d < 16; d <<= 1) v += __shfl_xor(v, d, 64);
             const float inv = 1.0f / sqrtf(v * (1.0f / kDim) + a.eps);
+            float kv[8];
+#pragma unroll
+            for (int j = 0; j < 8; ++j) kv[j] = fmaf((acc[i][j][r] - mu) * inv, g[j], b[j]);
+            if (a.rope) {   // key dims 0..63 (j < 4) turn with the neighbouring lane's value
+#pragma unroll
+                for (int j = 0; j < 4; ++j) {
+                    const float other = __shfl_xor(kv[j], 1, 64);
+                    kv[j] = rotate(kv[j], other, a.rope[rr * kRotPairs + 8 * j + (l16 >> 1)], l16 & 1);
+                }
+            }
             if (row >= a.T) continue;
             if (a.k_base) {
                 const int64_t slot = a.k_slot ? a.k_slot[row] : row;
                 uint16_t *kr = a.k_base + slot * kDim;
 #pragma unroll
-                for (int j = 0; j < 8; ++j)
-                    kr[16 * j + l16] = (uint16_t)f32_to_bf16(fmaf((acc[i][j][r] - mu) * inv, g[j], b[j]));
+                for (int j = 0; j < 8; ++j) kr[16 * j + l16] = (uint16_t)f32_to_bf16(kv[j]);
             }
 #pragma unroll
-            for (int j = 0; j < 2; ++j)
+            for (int j = 0; j < HW / 16; ++j)
                 a.w[row * a.ldwo + 16 * j + l16] = (uint16_t)f32_to_bf16(acc[i][8 + j][r]);
         }
 }
@@ -440,27 +511,36 @@ __global__ __launch_bounds__(256) void skinny_partial_kernel(const uint16_t *__r
         }
 }
 
-// q[t][n] = bf16(sum over the S slices of part[s][t][n]), q rows ldq apart; thread: 4
-// consecutive n.
-__global__ __launch_bounds__(256) void skinny_reduce_q_kernel(const float *__restrict__ part, int S, int T,
-                                                              uint16_t *__restrict__ q, int64_t ldq) {
+// q[t][n] = bf16(sum over the S slices of part[s][t][n]), N columns, q rows ldq apart; thread:
+// 4 consecutive n (two rotary pairs when n mod 128 < 64 and rope is given).
+__global__ __launch_bounds__(256) void skinny_reduce_q_kernel(const float *__restrict__ part, int S, int T, int N,
+                                                              uint16_t *__restrict__ q, int64_t ldq,
+                                                              const float2 *__restrict__ rope) {
     const int64_t e = 4 * ((int64_t)blockIdx.x * 256 + threadIdx.x);
-    if (e >= (int64_t)T * kQOut) return;
+    if (e >= (int64_t)T * N) return;
     f32x4 v = *reinterpret_cast<const f32x4 *>(part + e);
     for (int s = 1; s < S; ++s) {
-        const f32x4 p = *reinterpret_cast<const f32x4 *>(part + (int64_t)s * T * kQOut + e);
+        const f32x4 p = *reinterpret_cast<const f32x4 *>(part + (int64_t)s * T * N + e);
         v = f32x4{v[0] + p[0], v[1] + p[1], v[2] + p[2], v[3] + p[3]};
     }
-    const int64_t t = e / kQOut, n = e % kQOut;
+    const int64_t t = e / N, n = e % N;
+    if (rope && (n % kDim) < 2 * kRotPairs) {
+        const int i = (int)(n % kDim) / 2;
+        const float2 c0 = rope[t * kRotPairs + i], c1 = rope[t * kRotPairs + i + 1];
+        v = f32x4{rotate(v[0], v[1], c0, false), rotate(v[1], v[0], c0, true), rotate(v[2], v[3], c1, false),
+                  rotate(v[3], v[2], c1, true)};
+    }
     *reinterpret_cast<u32x2 *>(q + t * ldq + n) = u32x2{pack_bf16x2(v[0], v[1]), pack_bf16x2(v[2], v[3])};
 }
 
-// One workgroup per token: wave j adds the slices s = j, j + 4, ... of the 160 columns of
-// [k | w] (lane: columns lane, 64 + lane, and 128 + lane for lane < 32); the four wave sums
+// One workgroup per token: wave j adds the slices s = j, j + 4, ... of the 128 + HW columns of
+// [k | w] (lane: columns lane, 64 + lane, and 128 + lane for lane < HW); the four wave sums
 // are added in a fixed order, then wave 0 applies the LayerNorm over the 128 key columns
-// (as in the tiled kernel's epilogue), rounds to bf16 and writes k to its slot.
+// (as in the tiled kernel's epilogue) and the rotary step on dims 0..63 if rope is given,
+// rounds to bf16 and writes k to its slot.
+template <int HW>
 __global__ __launch_bounds__(256) void skinny_reduce_kw_kernel(const float *__restrict__ part, int S, KWArgs a) {
-    constexpr int N = kDim + kHeads;
+    constexpr int N = kDim + HW;
     __shared__ float red[4][3][64];
     const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
     const int64_t t = blockIdx.x;
@@ -471,7 +551,7 @@ __global__ __launch_bounds__(256) void skinny_reduce_kw_kernel(const float *__re
     for (int s = wave; s < S; s += 4) {
         v0 += p[s * ss + lane];
         v1 += p[s * ss + 64 + lane];
-        vw += lane < kHeads ? p[s * ss + kDim + lane] : 0.f;
+        vw += lane < HW ? p[s * ss + kDim + lane] : 0.f;
     }
     red[wave][0][lane] = v0;
     red[wave][1][lane] = v1;
@@ -490,96 +570,125 @@ __global__ __launch_bounds__(256) void skinny_reduce_kw_kernel(const float *__re
 #pragma unroll
     for (int d = 1; d < 64; d <<= 1) var += __shfl_xor(var, d, 64);
     const float inv = 1.0f / sqrtf(var * (1.0f / kDim) + a.eps);
+    float k0 = fmaf(c0 * inv, bf16_to_f32(a.gamma[lane]), bf16_to_f32(a.beta[lane]));
+    const float k1 = fmaf(c1 * inv, bf16_to_f32(a.gamma[64 + lane]), bf16_to_f32(a.beta[64 + lane]));
+    if (a.rope) {
+        const float other = __shfl_xor(k0, 1, 64);
+        k0 = rotate(k0, other, a.rope[t * kRotPairs + (lane >> 1)], lane & 1);
+    }
     if (a.k_base) {
         const int64_t slot = a.k_slot ? a.k_slot[t] : t;
         uint16_t *kr = a.k_base + slot * kDim;
-        kr[lane] = (uint16_t)f32_to_bf16(fmaf(c0 * inv, bf16_to_f32(a.gamma[lane]), bf16_to_f32(a.beta[lane])));
-        kr[64 + lane] = (uint16_t)f32_to_bf16(fmaf(c1 * inv, bf16_to_f32(a.gamma[64 + lane]), bf16_to_f32(a.beta[64 + lane])));
+        kr[lane] = (uint16_t)f32_to_bf16(k0);
+        kr[64 + lane] = (uint16_t)f32_to_bf16(k1);
     }
-    if (lane < kHeads) a.w[t * a.ldwo + lane] = (uint16_t)f32_to_bf16(vw);
+    if (lane < HW) a.w[t * a.ldwo + lane] = (uint16_t)f32_to_bf16(vw);
 }
 
-constexpr int kSkQSlice = 256;    // q: K = 1,536 in 6 slices x 32 column tiles
+constexpr int kSkQSlice = 256;    // q: K = 1,536 in 6 slices x (N / 128) column tiles
 constexpr int kSkKWSlice = 128;   // k/w: K = 7,168 in 56 slices
+
+size_t r256(size_t b) { return (b + 255u) & ~(size_t)255u; }
+
+size_t main_workspace(int64_t T, int nq, int hw) {
+    if (T > kSkinnyT) return (size_t)nq * kQLat * 2;   // W_q transposed
+    return 4u * (size_t)T * ((size_t)(kQLat / kSkQSlice) * nq + (size_t)(kHidden / kSkKWSlice) * (kDim + hw));
+}
+
+template <int HW>
+hipError_t launch_kw(const KWArgs &a, float *part_kw, size_t smem_kw, hipStream_t stream) {
+    if (a.T <= kSkinnyT) {
+        hipLaunchKernelGGL((skinny_partial_kernel<kDim + HW, 2, 2, kSkKWSlice>), dim3(1, kHidden / kSkKWSlice),
+                           dim3(256), sizeof(GemmSmem<64, kDim + HW>), stream, a.x, a.ldx, (int)a.T, a.Wk, kDim,
+                           a.Ww, (int)a.ldww, kDim, kDim + HW, part_kw);
+        hipLaunchKernelGGL(skinny_reduce_kw_kernel<HW>, dim3((unsigned)a.T), dim3(256), 0, stream, part_kw,
+                           kHidden / kSkKWSlice, a);
+    } else {
+        hipLaunchKernelGGL(proj_kw_kernel<HW>, dim3((unsigned)((a.T + 127) / 128)), dim3(256), smem_kw, stream, a);
+    }
+    return hipGetLastError();
+}
 
 }  // namespace
 
-size_t project_workspace(int64_t T) {
+size_t project_workspace(int64_t T, int nq, int hw, bool rope) {
     if (T <= 0) return 0;
-    if (T > kSkinnyT) return (size_t)kQOut * kQLat * 2;   // W_q transposed
-    return 4u * (size_t)T * ((size_t)(kQLat / kSkQSlice) * kQOut + (size_t)(kHidden / kSkKWSlice) * (kDim + kHeads));
+    const size_t m = main_workspace(T, nq, hw);
+    return rope ? r256(m) + 8u * (size_t)T * kRotPairs : m;
 }
+
+size_t project_workspace(int64_t T) { return project_workspace(T, kQOut, kHeads, false); }
 
 hipError_t launch_project(const uint16_t *x, int64_t ldx, const uint16_t *c_q, int64_t ldc,
                           int64_t T, const uint16_t *W_q, const uint16_t *W_k,
                           const uint16_t *W_w, const uint16_t *gamma, const uint16_t *beta,
                           float eps, uint16_t *q, uint16_t *k_base, const int64_t *k_slot,
                           uint16_t *w, float *ws, hipStream_t stream) {
-    return launch_project_ex(x, ldx, c_q, ldc, T, W_q, kQOut, W_k, W_w, kHeads, gamma, beta, eps, q, kQOut,
-                             k_base, k_slot, w, kHeads, ws, stream);
+    return launch_project_ex(x, ldx, c_q, ldc, T, W_q, kQOut, kQOut, W_k, W_w, kHeads, kHeads, gamma, beta, eps,
+                             q, kQOut, k_base, k_slot, w, kHeads, 0, 0.0, ws, stream);
 }
 
 hipError_t launch_project_ex(const uint16_t *x, int64_t ldx, const uint16_t *c_q, int64_t ldc,
-                             int64_t T, const uint16_t *W_q, int64_t ldwq, const uint16_t *W_k,
-                             const uint16_t *W_w, int64_t ldww, const uint16_t *gamma,
+                             int64_t T, const uint16_t *W_q, int64_t ldwq, int nq, const uint16_t *W_k,
+                             const uint16_t *W_w, int64_t ldww, int hw, const uint16_t *gamma,
                              const uint16_t *beta, float eps, uint16_t *q, int64_t ldq,
                              uint16_t *k_base, const int64_t *k_slot, uint16_t *w, int64_t ldwo,
-                             float *ws, hipStream_t stream) {
+                             int64_t pos0, double theta, float *ws, hipStream_t stream) {
     if (T == 0) return hipSuccess;
+    if ((nq != kQOut && nq != 2 * kQOut) || (hw != kHeads && hw != 2 * kHeads)) return hipErrorInvalidValue;
+    static DeviceOnce attr;
+    const size_t smem_q = sizeof(uint16_t) * kQStage * kQStages;
+    hipError_t ea = attr.run([&] {
+        const std::pair<const void *, size_t> fs[] = {
+            {reinterpret_cast<const void *>(proj_q_kernel), smem_q},
+            {reinterpret_cast<const void *>(proj_kw_kernel<kHeads>), sizeof(GemmSmem<128, kDim + kHeads>)},
+            {reinterpret_cast<const void *>(proj_kw_kernel<2 * kHeads>), sizeof(GemmSmem<128, kDim + 2 * kHeads>)},
+            {reinterpret_cast<const void *>(skinny_partial_kernel<128, 1, 4, kSkQSlice>), sizeof(GemmSmem<64, 128>)},
+            {reinterpret_cast<const void *>(skinny_partial_kernel<kDim + kHeads, 2, 2, kSkKWSlice>),
+             sizeof(GemmSmem<64, kDim + kHeads>)},
+            {reinterpret_cast<const void *>(skinny_partial_kernel<kDim + 2 * kHeads, 2, 2, kSkKWSlice>),
+             sizeof(GemmSmem<64, kDim + 2 * kHeads>)}};
+        for (const auto &f : fs) {
+            hipError_t e = hipFuncSetAttribute(f.first, hipFuncAttributeMaxDynamicSharedMemorySize, (int)f.second);
+            if (e != hipSuccess) return e;
+        }
+        return hipSuccess;
+    });
+    if (ea != hipSuccess) return ea;
+    const bool rot = theta > 0.0;
+    float2 *rope = nullptr;
+    if (rot) {
+        rope = reinterpret_cast<float2 *>(reinterpret_cast<char *>(ws) + r256(main_workspace(T, nq, hw)));
+        hipLaunchKernelGGL(rope_table_kernel, dim3((unsigned)((T * kRotPairs + 255) / 256)), dim3(256), 0, stream,
+                           rope, T, pos0, theta);
+    }
+    KWArgs a{x, ldx, T, W_k, W_w, gamma, beta, eps, k_base, k_slot, w, ldww, ldwo, rope};
     if (T <= kSkinnyT) {
         const int t = (int)T;
         float *part_q = ws;
-        float *part_kw = ws + (size_t)(kQLat / kSkQSlice) * T * kQOut;
-        static DeviceOnce sk_attr;
-        hipError_t ea = sk_attr.run([] {
-            hipError_t e = hipFuncSetAttribute(
-                reinterpret_cast<const void *>(skinny_partial_kernel<128, 1, 4, kSkQSlice>),
-                hipFuncAttributeMaxDynamicSharedMemorySize, (int)sizeof(GemmSmem<64, 128>));
-            if (e != hipSuccess) return e;
-            return hipFuncSetAttribute(reinterpret_cast<const void *>(skinny_partial_kernel<160, 2, 2, kSkKWSlice>),
-                                       hipFuncAttributeMaxDynamicSharedMemorySize, (int)sizeof(GemmSmem<64, 160>));
-        });
-        if (ea != hipSuccess) return ea;
+        float *part_kw = ws + (size_t)(kQLat / kSkQSlice) * T * nq;
         if (q) {
-            hipLaunchKernelGGL((skinny_partial_kernel<128, 1, 4, kSkQSlice>), dim3(kQOut / 128, kQLat / kSkQSlice),
+            hipLaunchKernelGGL((skinny_partial_kernel<128, 1, 4, kSkQSlice>), dim3(nq / 128, kQLat / kSkQSlice),
                                dim3(256), sizeof(GemmSmem<64, 128>), stream, c_q, ldc, t, W_q, (int)ldwq, W_q,
-                               (int)ldwq, kQOut, kQOut, part_q);
-            hipLaunchKernelGGL(skinny_reduce_q_kernel, dim3((unsigned)((T * kQOut / 4 + 255) / 256)), dim3(256),
-                               0, stream, part_q, kQLat / kSkQSlice, t, q, ldq);
+                               (int)ldwq, nq, nq, part_q);
+            hipLaunchKernelGGL(skinny_reduce_q_kernel, dim3((unsigned)((T * nq / 4 + 255) / 256)), dim3(256), 0,
+                               stream, part_q, kQLat / kSkQSlice, t, nq, q, ldq, (const float2 *)rope);
         }
-        hipLaunchKernelGGL((skinny_partial_kernel<160, 2, 2, kSkKWSlice>), dim3(1, kHidden / kSkKWSlice), dim3(256),
-                           sizeof(GemmSmem<64, 160>), stream, x, ldx, t, W_k, kDim, W_w, (int)ldww, kDim,
-                           kDim + kHeads, part_kw);
-        KWArgs a{x, ldx, T, W_k, W_w, gamma, beta, eps, k_base, k_slot, w, ldww, ldwo};
-        hipLaunchKernelGGL(skinny_reduce_kw_kernel, dim3((unsigned)T), dim3(256), 0, stream, part_kw,
-                           kHidden / kSkKWSlice, a);
-        return hipGetLastError();
-    }
-    static DeviceOnce attr;
-    const size_t smem_q = sizeof(uint16_t) * kQStage * kQStages;
-    const size_t smem_kw = sizeof(GemmSmem<128, 160>);
-    hipError_t ea = attr.run([&] {
-        hipError_t e = hipFuncSetAttribute(reinterpret_cast<const void *>(proj_q_kernel),
-                                           hipFuncAttributeMaxDynamicSharedMemorySize, (int)smem_q);
-        if (e != hipSuccess) return e;
-        return hipFuncSetAttribute(reinterpret_cast<const void *>(proj_kw_kernel),
-                                   hipFuncAttributeMaxDynamicSharedMemorySize, (int)smem_kw);
-    });
-    if (ea != hipSuccess) return ea;
-    const int64_t mt = (T + 127) / 128;
-    if (q) {
+    } else if (q) {
         uint16_t *WqT = reinterpret_cast<uint16_t *>(ws);
-        hipLaunchKernelGGL(transpose_wq_kernel, dim3(kQOut / 64, kQLat / 64), dim3(256), 0, stream, W_q, ldwq,
-                           WqT);
-        const int64_t qt = (T + kQBM - 1) / kQBM;
-        hipLaunchKernelGGL(proj_q_kernel, dim3((unsigned)(qt * (kQOut / kQBN))), dim3(256), smem_q, stream,
-                           c_q, ldc, T, WqT, q, ldq);
+        hipLaunchKernelGGL(transpose_wq_kernel, dim3(nq / 64, kQLat / 64), dim3(256), 0, stream, W_q, ldwq, WqT);
+        const int64_t tiles = (T + kQBM - 1) / kQBM * (nq / kQBN);
+        QArgs qa{c_q, ldc, T, WqT, nq, q, ldq, rope};
+        hipLaunchKernelGGL(proj_q_kernel, dim3((unsigned)tiles), dim3(512), smem_q, stream, qa);
         hipError_t e = hipGetLastError();
         if (e != hipSuccess) return e;
     }
-    KWArgs a{x, ldx, T, W_k, W_w, gamma, beta, eps, k_base, k_slot, w, ldww, ldwo};
-    hipLaunchKernelGGL(proj_kw_kernel, dim3((unsigned)mt), dim3(256), smem_kw, stream, a);
-    return hipGetLastError();
+    hipError_t e = hipGetLastError();
+    if (e != hipSuccess) return e;
+    const size_t smem_kw = hw == kHeads ? sizeof(GemmSmem<128, kDim + kHeads>) : sizeof(GemmSmem<128, kDim + 2 * kHeads>);
+    float *part_kw = ws + (size_t)(kQLat / kSkQSlice) * T * nq;
+    return hw == kHeads ? launch_kw<kHeads>(a, part_kw, smem_kw, stream)
+                        : launch_kw<2 * kHeads>(a, part_kw, smem_kw, stream);
 }
 
 }  // namespace dsaidx

@@ -245,8 +245,12 @@ def test_rejections_before_device(dsa):
     assert vc(_vp(A), _vp(A), _vp(A), 10, -1, 8, _vp(A), None, _vp(A), 1 << 30, None) == -1
     assert vc(_vp(A), _vp(A), _vp(A), 10, 100, 8, _vp(A), None, _vp(A), 16, None) == -3
     assert vc(None, None, None, 0, 100, 8, None, None, None, 0, None) == 0
-    assert dsa.workspace_size(dsa.OP_V32_PROJECT, 100) == dsa.workspace_size(dsa.OP_PROJECT, 100)
-    assert dsa.workspace_size(dsa.OP_V32_PROJECT, 7) == dsa.workspace_size(dsa.OP_PROJECT, 7)
+    # the 64-head projection in one pass: W_q transposed (8,192 x 1,536 bf16) above 64 tokens, the
+    # split-K partial sums of 8,192 + 192 columns at most 64 tokens, then (256-byte aligned) the
+    # rotary table, (cos, sin) in fp32 for 32 pairs of every token
+    r256 = lambda b: (b + 255) // 256 * 256
+    assert dsa.workspace_size(dsa.OP_V32_PROJECT, 100) == r256(8192 * 1536 * 2) + 100 * 32 * 8
+    assert dsa.workspace_size(dsa.OP_V32_PROJECT, 7) == r256(4 * 7 * (6 * 8192 + 56 * 192)) + 7 * 32 * 8
 
 
 def test_v32_project_rejections(dsa):
