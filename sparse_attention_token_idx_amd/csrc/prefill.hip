@@ -928,13 +928,17 @@ __global__ __launch_bounds__(64 * kFbW, 1) void fallback_kernel(FbArgs a) {
     }
 }
 
-// Clears the status word (first call of a run) and the fallback counters.
-__global__ void prefill_reset_kernel(uint32_t *fb, int clear_status) {
-    if (threadIdx.x == 0) {
+// Clears the fallback counters (and the status word on a call's first chunk) and sets the first
+// n_zero thresholds to 0 (every key), for chunks that need no sample.
+__global__ __launch_bounds__(256) void prefill_reset_kernel(uint32_t *fb, int clear_status, uint32_t *theta,
+                                                            int64_t n_zero) {
+    const int64_t i = (int64_t)blockIdx.x * 256 + threadIdx.x;
+    if (i == 0) {
         if (clear_status) fb[0] = 0u;
         fb[1] = 0u;
         fb[2] = 0u;
     }
+    if (i < n_zero) theta[i] = 0u;
 }
 
 // seq_base[i] = sum over sequences j < i of tri_row_offset(L_j), i = 0 .. B (one workgroup).
@@ -1155,9 +1159,14 @@ hipError_t launch_prefill_topk(const PrefillPlan &p, const uint16_t *q, const ui
 
     for (int64_t f0 = 0; f0 < p.rows; f0 += p.cf) {
         const int64_t f1 = f0 + p.cf < p.rows ? f0 + p.cf : p.rows;
-        hipLaunchKernelGGL(prefill_reset_kernel, dim3(1), dim3(64), 0, st, fb, f0 == 0 ? 1 : 0);
+        // rows of at most kAllKeys keys keep every key: when the chunk's longest row is one of
+        // them, no sample is needed and every threshold is 0
+        const bool all_keys = p.varlen ? p.max_len <= kAllKeys : p.pos0 + f1 <= kAllKeys;
+        const int64_t nz = all_keys ? f1 - f0 : 0;
+        hipLaunchKernelGGL(prefill_reset_kernel, dim3((unsigned)(nz > 0 ? cdiv(nz, 256) : 1)), dim3(256), 0, st, fb,
+                           f0 == 0 ? 1 : 0, theta, nz);
         // 1 + 2. sample scores and thresholds, in sub-chunks of the sample buffer
-        for (int64_t s0 = f0; s0 < f1; s0 += p.cs) {
+        for (int64_t s0 = f0; s0 < f1 && !all_keys; s0 += p.cs) {
             const int64_t s1 = s0 + p.cs < f1 ? s0 + p.cs : f1;
             ScoreArgs a{};
             a.k = k;
@@ -1278,7 +1287,7 @@ hipError_t launch_scores(const uint16_t *q, const uint16_t *k, const uint16_t *w
     hipError_t e = ensure_attrs();
     if (e != hipSuccess) return e;
     if (B == 0 || max_len == 0) return hipSuccess;
-    hipLaunchKernelGGL(prefill_reset_kernel, dim3(1), dim3(64), 0, stream, status, 1);
+    hipLaunchKernelGGL(prefill_reset_kernel, dim3(1), dim3(64), 0, stream, status, 1, (uint32_t *)nullptr, (int64_t)0);
     if (cu_seqlens) hipLaunchKernelGGL(seq_base_kernel, dim3(1), dim3(1024), 0, stream, cu_seqlens, B, seq_base);
     e = hipGetLastError();
     if (e != hipSuccess) return e;
