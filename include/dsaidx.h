@@ -307,8 +307,8 @@ int dsa_idx_sparse_mla(const dsa_idx_bf16 *q, const dsa_idx_bf16 *kv, const int3
  * One pass: x is read once for the key and all 64 head weights, and the rotary step runs in
  * the projection epilogues from a (cos, sin) table the call forms first in the workspace.
  * Needs dsa_idx_workspace_size(DSA_IDX_OP_V32_PROJECT, T, ...) bytes of workspace: W_q
- * transposed (25.2 MB) for T > 64, fp32 split-K partial sums for T <= 64, then 256 B per token
- * for the table. */
+ * transposed (25.2 MB) for T > 64 (fp32 split-K partial sums of q for T <= 64), the key /
+ * head-weight split-K partial sums for T <= 32,768, then 256 B per token for the table. */
 int dsa_idx_v32_project(const dsa_idx_weights *wt, const dsa_idx_bf16 *x, int64_t ldx,
                         const dsa_idx_bf16 *c_q, int64_t ldc, int64_t T, int64_t pos0, float rope_theta,
                         dsa_idx_bf16 *q, dsa_idx_bf16 *k, dsa_idx_bf16 *w, void *ws, size_t ws_bytes,

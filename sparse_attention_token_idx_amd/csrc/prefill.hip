@@ -58,6 +58,8 @@ constexpr int kKR = 4;                 // key tiles in the LDS ring
 constexpr int kSignalSlice = 2;        // slice of a tile after which the next tile's DMA is awaited
 constexpr int kFillWg = 2048;          // workgroups a split launch aims for (8 per CU)
 constexpr int kMinSegTiles = 64;       // shortest key segment of a split launch (8,192 keys)
+constexpr int kFewRowBlocks = 128;     // at most this many row blocks (half the CUs or fewer) ...
+constexpr int kMinSegTilesFew = 8;     // ... may split their keys into segments this short
 constexpr int kMaxSeg = 512;           // most key segments of a split launch
 static_assert(kBK == kRowQuant, "a tile is one row quantum of the triangular layout");
 
@@ -1023,10 +1025,14 @@ hipError_t ensure_attrs() {
 // Key tiles per workgroup of a launch over nrb row blocks of one sequence whose longest row
 // streams max_nkt tiles (0: no split).
 int split_tiles(int64_t nrb, int64_t max_nkt) {
-    if (nrb >= kFillWg || max_nkt <= kMinSegTiles) return 0;
+    // a launch of a few row blocks leaves most CUs idle and waits on its longest row block, so
+    // it takes short segments; otherwise a segment is long enough for its workgroup to pay for
+    // loading its queries and filling the key ring
+    const int64_t min_seg = nrb <= kFewRowBlocks ? kMinSegTilesFew : kMinSegTiles;
+    if (nrb >= kFillWg || max_nkt <= min_seg) return 0;
     const int64_t want = (kFillWg + nrb - 1) / nrb;
     int64_t st = (max_nkt + want - 1) / want;
-    st = st < kMinSegTiles ? kMinSegTiles : st;
+    st = st < min_seg ? min_seg : st;
     const int64_t few = (max_nkt + kMaxSeg - 1) / kMaxSeg;   // at most kMaxSeg segments
     st = st < few ? few : st;
     return st < max_nkt ? (int)st : 0;

@@ -25,7 +25,9 @@
 // weights are the bytes that matter, so K is split over many workgroups instead: each one
 // runs the same tiled core on one 64-row tile and its K-slice and writes fp32 partial sums
 // to the workspace; a second kernel adds the slices in order (deterministic), then
-// rounds, with the LayerNorm for k.
+// rounds, with the LayerNorm for k.  The [k | w] product does the same up to kKwSplitT
+// tokens (its 128-row tiles would fill only part of the chip: 64 workgroups at T = 8,192),
+// with as many K slices as bring the workgroups to about 1,024.
 #include <utility>
 
 #include "common.hpp"
@@ -479,22 +481,25 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2, 2))) voi
         }
 }
 
-// ---------------------------------------------------------------- small T (split K)
-// part[s][t][n] for one 64-row tile (all T <= 64 rows) and one BN-column tile n0 = BN x:
-// the product of A[:, k0:k0+KS] and B[k0:k0+KS, n0:n0+BN], k0 = KS s, on the tiled core.
-template <int BN, int WM, int WN, int KS>
+// ---------------------------------------------------------------- split K
+// part[s][t][n] for the 64-row tile m0 = 64 blockIdx.z and the BN-column tile n0 = BN blockIdx.x:
+// the product of A[m0 : m0 + 64, k0 : k0 + ks] and B[k0 : k0 + ks, n0 : n0 + BN], k0 = ks
+// blockIdx.y, on the tiled core.  Used where the tiled kernels would leave most CUs idle: q and
+// [k | w] of a decode step (T <= kSkinnyT), and [k | w] up to kKwSplitT tokens.
+template <int BN, int WM, int WN>
 __global__ __launch_bounds__(256) void skinny_partial_kernel(const uint16_t *__restrict__ A, int64_t lda,
                                                              int T, const uint16_t *__restrict__ B0, int ld0,
                                                              const uint16_t *__restrict__ B1, int ld1,
-                                                             int nsplit, int N, float *__restrict__ part) {
+                                                             int nsplit, int N, int ks, float *__restrict__ part) {
     using Core = GemmCore<64, BN, WM, WN>;
     extern __shared__ __align__(16) unsigned char smem_raw[];
     auto &sm = *reinterpret_cast<GemmSmem<64, BN> *>(smem_raw);
     const int n0 = BN * blockIdx.x;
     const int s = blockIdx.y;
-    const int k0 = KS * s;
+    const int m0 = 64 * blockIdx.z;
+    const int k0 = ks * s;
     f32x4 acc[Core::SM][Core::SN];
-    Core::run(A + k0, lda, T, 0, B0 + (int64_t)k0 * ld0, ld0, B1 + (int64_t)k0 * ld1, ld1, nsplit, n0, KS,
+    Core::run(A + k0, lda, T, m0, B0 + (int64_t)k0 * ld0, ld0, B1 + (int64_t)k0 * ld1, ld1, nsplit, n0, ks,
               sm, acc);
     const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63;
     const int wm = wave / WN, wn = wave % WN;
@@ -503,7 +508,7 @@ __global__ __launch_bounds__(256) void skinny_partial_kernel(const uint16_t *__r
     for (int i = 0; i < Core::SM; ++i)
 #pragma unroll
         for (int r = 0; r < 4; ++r) {
-            const int row = wm * (64 / WM) + 16 * i + 4 * lg + r;
+            const int row = m0 + wm * (64 / WM) + 16 * i + 4 * lg + r;
             if (row >= T) continue;
             float *pr = part + ((int64_t)s * T + row) * N + n0 + wn * (BN / WN) + l16;
 #pragma unroll
@@ -585,24 +590,42 @@ __global__ __launch_bounds__(256) void skinny_reduce_kw_kernel(const float *__re
     if (lane < HW) a.w[t * a.ldwo + lane] = (uint16_t)f32_to_bf16(vw);
 }
 
-constexpr int kSkQSlice = 256;    // q: K = 1,536 in 6 slices x (N / 128) column tiles
-constexpr int kSkKWSlice = 128;   // k/w: K = 7,168 in 56 slices
+constexpr int kSkQSlice = 256;    // q of a decode step: K = 1,536 in 6 slices x (N / 128) column tiles
+constexpr int64_t kKwSplitT = 32768;   // [k | w] up to this many tokens: split K
 
 size_t r256(size_t b) { return (b + 255u) & ~(size_t)255u; }
 
+// K slices of the [k | w] product for T tokens (0: the tiled kernel): enough 64-row-tile x slice
+// workgroups to fill the chip (about 1,024), each slice a whole number of 64-wide K blocks.
+int kw_slices(int64_t T) {
+    if (T > kKwSplitT) return 0;
+    const int64_t tiles = (T + 63) / 64;
+    static const int kDivs[] = {1, 2, 4, 7, 8, 14, 16, 28, 56};   // divisors of 7,168 / 64 = 112
+    for (int d : kDivs)
+        if (tiles * d >= 1024) return d;
+    return 56;
+}
+
+size_t kw_part_bytes(int64_t T, int hw) {
+    const int S = kw_slices(T);
+    return S ? 4u * (size_t)S * (size_t)T * (size_t)(kDim + hw) : 0;
+}
+
 size_t main_workspace(int64_t T, int nq, int hw) {
-    if (T > kSkinnyT) return (size_t)nq * kQLat * 2;   // W_q transposed
-    return 4u * (size_t)T * ((size_t)(kQLat / kSkQSlice) * nq + (size_t)(kHidden / kSkKWSlice) * (kDim + hw));
+    const size_t q = T > kSkinnyT ? (size_t)nq * kQLat * 2           // W_q transposed
+                                  : 4u * (size_t)T * (size_t)(kQLat / kSkQSlice) * nq;   // q partial sums
+    return r256(q) + kw_part_bytes(T, hw);
 }
 
 template <int HW>
 hipError_t launch_kw(const KWArgs &a, float *part_kw, size_t smem_kw, hipStream_t stream) {
-    if (a.T <= kSkinnyT) {
-        hipLaunchKernelGGL((skinny_partial_kernel<kDim + HW, 2, 2, kSkKWSlice>), dim3(1, kHidden / kSkKWSlice),
-                           dim3(256), sizeof(GemmSmem<64, kDim + HW>), stream, a.x, a.ldx, (int)a.T, a.Wk, kDim,
-                           a.Ww, (int)a.ldww, kDim, kDim + HW, part_kw);
-        hipLaunchKernelGGL(skinny_reduce_kw_kernel<HW>, dim3((unsigned)a.T), dim3(256), 0, stream, part_kw,
-                           kHidden / kSkKWSlice, a);
+    const int S = kw_slices(a.T);
+    if (S) {
+        const unsigned tiles = (unsigned)((a.T + 63) / 64);
+        hipLaunchKernelGGL((skinny_partial_kernel<kDim + HW, 2, 2>), dim3(1, S, tiles), dim3(256),
+                           sizeof(GemmSmem<64, kDim + HW>), stream, a.x, a.ldx, (int)a.T, a.Wk, kDim, a.Ww,
+                           (int)a.ldww, kDim, kDim + HW, kHidden / S, part_kw);
+        hipLaunchKernelGGL(skinny_reduce_kw_kernel<HW>, dim3((unsigned)a.T), dim3(256), 0, stream, part_kw, S, a);
     } else {
         hipLaunchKernelGGL(proj_kw_kernel<HW>, dim3((unsigned)((a.T + 127) / 128)), dim3(256), smem_kw, stream, a);
     }
@@ -643,10 +666,10 @@ hipError_t launch_project_ex(const uint16_t *x, int64_t ldx, const uint16_t *c_q
             {reinterpret_cast<const void *>(proj_q_kernel), smem_q},
             {reinterpret_cast<const void *>(proj_kw_kernel<kHeads>), sizeof(GemmSmem<128, kDim + kHeads>)},
             {reinterpret_cast<const void *>(proj_kw_kernel<2 * kHeads>), sizeof(GemmSmem<128, kDim + 2 * kHeads>)},
-            {reinterpret_cast<const void *>(skinny_partial_kernel<128, 1, 4, kSkQSlice>), sizeof(GemmSmem<64, 128>)},
-            {reinterpret_cast<const void *>(skinny_partial_kernel<kDim + kHeads, 2, 2, kSkKWSlice>),
+            {reinterpret_cast<const void *>(skinny_partial_kernel<128, 1, 4>), sizeof(GemmSmem<64, 128>)},
+            {reinterpret_cast<const void *>(skinny_partial_kernel<kDim + kHeads, 2, 2>),
              sizeof(GemmSmem<64, kDim + kHeads>)},
-            {reinterpret_cast<const void *>(skinny_partial_kernel<kDim + 2 * kHeads, 2, 2, kSkKWSlice>),
+            {reinterpret_cast<const void *>(skinny_partial_kernel<kDim + 2 * kHeads, 2, 2>),
              sizeof(GemmSmem<64, kDim + 2 * kHeads>)}};
         for (const auto &f : fs) {
             hipError_t e = hipFuncSetAttribute(f.first, hipFuncAttributeMaxDynamicSharedMemorySize, (int)f.second);
@@ -663,14 +686,16 @@ hipError_t launch_project_ex(const uint16_t *x, int64_t ldx, const uint16_t *c_q
                            rope, T, pos0, theta);
     }
     KWArgs a{x, ldx, T, W_k, W_w, gamma, beta, eps, k_base, k_slot, w, ldww, ldwo, rope};
+    // the [k | w] partial sums (split K) follow the q part of the workspace
+    float *part_kw = reinterpret_cast<float *>(reinterpret_cast<char *>(ws) +
+                                               (main_workspace(T, nq, hw) - kw_part_bytes(T, hw)));
     if (T <= kSkinnyT) {
         const int t = (int)T;
         float *part_q = ws;
-        float *part_kw = ws + (size_t)(kQLat / kSkQSlice) * T * nq;
         if (q) {
-            hipLaunchKernelGGL((skinny_partial_kernel<128, 1, 4, kSkQSlice>), dim3(nq / 128, kQLat / kSkQSlice),
+            hipLaunchKernelGGL((skinny_partial_kernel<128, 1, 4>), dim3(nq / 128, kQLat / kSkQSlice, 1),
                                dim3(256), sizeof(GemmSmem<64, 128>), stream, c_q, ldc, t, W_q, (int)ldwq, W_q,
-                               (int)ldwq, nq, nq, part_q);
+                               (int)ldwq, nq, nq, kSkQSlice, part_q);
             hipLaunchKernelGGL(skinny_reduce_q_kernel, dim3((unsigned)((T * nq / 4 + 255) / 256)), dim3(256), 0,
                                stream, part_q, kQLat / kSkQSlice, t, nq, q, ldq, (const float2 *)rope);
         }
@@ -686,7 +711,6 @@ hipError_t launch_project_ex(const uint16_t *x, int64_t ldx, const uint16_t *c_q
     hipError_t e = hipGetLastError();
     if (e != hipSuccess) return e;
     const size_t smem_kw = hw == kHeads ? sizeof(GemmSmem<128, kDim + kHeads>) : sizeof(GemmSmem<128, kDim + 2 * kHeads>);
-    float *part_kw = ws + (size_t)(kQLat / kSkQSlice) * T * nq;
     return hw == kHeads ? launch_kw<kHeads>(a, part_kw, smem_kw, stream)
                         : launch_kw<2 * kHeads>(a, part_kw, smem_kw, stream);
 }

@@ -59,7 +59,15 @@ def test_architecture_check(dsa):
 
 def test_workspace_sizes(dsa):
     # more than 64 tokens: W_q transposed (4096 x 1536 bf16)
-    assert dsa.workspace_size(dsa.OP_PROJECT, 100) == 4096 * 1536 * 2
+    # more than 64 tokens, at most 32,768: then the [k | w] partial sums of its K slices (enough
+    # slices that 64-row tiles x slices reach 1,024 workgroups, at most 56)
+    def kw_slices(T):
+        tiles = (T + 63) // 64
+        return next((d for d in (1, 2, 4, 7, 8, 14, 16, 28, 56) if tiles * d >= 1024), 56)
+    assert kw_slices(8192) == 8 and kw_slices(100) == 56 and kw_slices(32768) == 2
+    for T in (100, 8192, 20000, 32768):
+        assert dsa.workspace_size(dsa.OP_PROJECT, T) == 4096 * 1536 * 2 + 4 * kw_slices(T) * T * 160
+    assert dsa.workspace_size(dsa.OP_PROJECT, 32769) == 4096 * 1536 * 2
     # a few tokens (at most 64) split K: fp32 partial sums, 6 slices of q and 56 of [k | w]
     assert dsa.workspace_size(dsa.OP_PROJECT, 64) == 4 * 64 * (6 * 4096 + 56 * 160)
     assert dsa.workspace_size(dsa.OP_PROJECT, 1) == 4 * (6 * 4096 + 56 * 160)
@@ -92,9 +100,10 @@ def test_workspace_sizes(dsa):
             nseg = 1
             if not varlen:
                 nrb, mt = -(-(f1 - f0) // bq), (pos0 + f1 - 1) // 128 + 1
-                if nrb < 2048 and mt > 64:
+                min_seg = 8 if nrb <= 128 else 64      # launches of few row blocks: short segments
+                if nrb < 2048 and mt > min_seg:
                     want = -(-2048 // nrb)
-                    st = max(64, -(-mt // want), -(-mt // 512))
+                    st = max(min_seg, -(-mt // want), -(-mt // 512))
                     if st < mt:
                         nseg = -(-mt // st)
             lists = max(lists, (cf if varlen else f1 - f0) * nseg)
@@ -105,7 +114,7 @@ def test_workspace_sizes(dsa):
         parts = [256, 4 * cf, 4 * lists, 8 * lists * (6144 + 64), 4 * cs * ms, 8 * cf, 4 * 128, 8 * 128,
                  4 * 128 * ld, 4 * max(ms, ld) + 4 * 128]
         return sum(r256(x) for x in parts)
-    for T in (1, 300, 1000, 5000, 65536, 100000):
+    for T in (1, 300, 1000, 2560, 4096, 5000, 65536, 100000):
         assert dsa.workspace_size(dsa.OP_SCORE_TOPK, T, topk=2048) == plan(T), T
         assert dsa.workspace_size(dsa.OP_V32_SCORE_TOPK, T, topk=2048) == plan(T, heads=64), T
     assert dsa.workspace_size(dsa.OP_SCORE_TOPK_VARLEN, 16, 2, 8, topk=5) == plan(16, varlen=True, B=2, max_len=8)
@@ -249,7 +258,7 @@ def test_rejections_before_device(dsa):
     # split-K partial sums of 8,192 + 192 columns at most 64 tokens, then (256-byte aligned) the
     # rotary table, (cos, sin) in fp32 for 32 pairs of every token
     r256 = lambda b: (b + 255) // 256 * 256
-    assert dsa.workspace_size(dsa.OP_V32_PROJECT, 100) == r256(8192 * 1536 * 2) + 100 * 32 * 8
+    assert dsa.workspace_size(dsa.OP_V32_PROJECT, 100) == r256(8192 * 1536 * 2 + 4 * 56 * 100 * 192) + 100 * 32 * 8
     assert dsa.workspace_size(dsa.OP_V32_PROJECT, 7) == r256(4 * 7 * (6 * 8192 + 56 * 192)) + 7 * 32 * 8
 
 
