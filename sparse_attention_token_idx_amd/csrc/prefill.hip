@@ -568,16 +568,20 @@ __global__ __launch_bounds__(256) void threshold_kernel(ThrArgs a) {
 }
 
 // ---------------------------------------------------------------- exact select of the lists
-// A row whose kept keys are one list: a workgroup of two waves, wave h holding a contiguous half
-// of the list (entry h * half + 64 i + lane in key[i]).  An MSD radix select over the order
-// keys relative to their minimum, 8 bits at a time with a shared 256-bin LDS histogram, finds
-// theta = the need-th largest key and how many keys equal to theta win (the lowest-index
-// ones); the winners are written in list order, which is index order, from ballots, each wave
-// starting after the first wave's winners.
-constexpr int kSelKeys = kListCap / 128;          // keys per lane (two waves per row)
-constexpr int kSelCap = kSelKeys * 128;           // kept keys a row may have
+// A row whose kept keys are one list: a workgroup of kSelW waves, wave h holding a contiguous
+// quarter of the list's 64-entry groups (entry 64 (g0 + i) + lane in key[i] and pos[i]), the
+// order key and the key position of every entry in registers, so the list is read once.  An MSD
+// radix select over the order keys relative to their minimum, 8 bits at a time with a shared
+// 256-bin LDS histogram, finds theta = the need-th largest key and how many keys equal to
+// theta win (the lowest-index ones).  Each wave then counts its keys above and equal to theta;
+// from the counts of the waves before it, it knows where its winners start and how many of its
+// keys equal to theta still win, and writes its winners in list order, which is index order,
+// from ballots.
+constexpr int kSelW = 4;                               // waves per row
+constexpr int kSelKeys = kListCap / (64 * kSelW);      // entries per lane: 24
+constexpr int kSelCap = kSelKeys * 64 * kSelW;         // kept keys a row may have
 static_assert(kSelCap == kListCap, "a row's list fits the select");
-constexpr int kSelBlk = 8;                         // loads in flight per lane
+constexpr int kSelBlk = 8;                             // loads in flight per lane
 static_assert(kSelKeys % kSelBlk == 0, "whole load blocks");
 
 struct SelArgs {
@@ -595,40 +599,46 @@ struct SelArgs {
     int32_t *dummy_i;          // store target of the lanes that write nothing (2 words a wave)
 };
 
-// List entry i of this wave's part for lane `lane`: its own entry for i < nit, else the first
+// List entry of this wave's group i for lane `lane`: its own entry for i < nit, else the first
 // sentinel pair after the list (key 0), so that no load sits behind a branch.
 __device__ __forceinline__ int sel_entry(int i, int nit, int lane, int first, int total) {
     return i < nit ? first + 64 * i + lane : total;
 }
 
-// This wave's keys: entries first + 64 i + lane (i < nit; past the list's end its sentinel run
-// reads as key 0), kSelBlk loads in flight at a time.
-__device__ __forceinline__ void sel_load(uint32_t (&key)[kSelKeys], const uint2 *list, int nit, int lane,
-                                         int first, int total) {
+// This wave's order keys and key positions: entries first + 64 i + lane (i < nit; past the
+// list's end its sentinel run reads as key 0), kSelBlk loads in flight at a time.
+__device__ __forceinline__ void sel_load(uint32_t (&key)[kSelKeys], int32_t (&pos)[kSelKeys], const uint2 *list,
+                                         int nit, int lane, int first, int total) {
 #pragma unroll
     for (int blk = 0; blk < kSelKeys / kSelBlk; ++blk) {
         if (kSelBlk * blk < nit) {
+            uint2 e[kSelBlk];
+#pragma unroll
+            for (int j = 0; j < kSelBlk; ++j) e[j] = list[sel_entry(kSelBlk * blk + j, nit, lane, first, total)];
 #pragma unroll
             for (int j = 0; j < kSelBlk; ++j) {
-                const int i = kSelBlk * blk + j;
-                key[i] = score_key(__uint_as_float(list[sel_entry(i, nit, lane, first, total)].x));
+                key[kSelBlk * blk + j] = score_key(__uint_as_float(e[j].x));
+                pos[kSelBlk * blk + j] = (int32_t)e[j].y;
             }
         } else {
 #pragma unroll
-            for (int j = 0; j < kSelBlk; ++j) key[kSelBlk * blk + j] = 0u;
+            for (int j = 0; j < kSelBlk; ++j) {
+                key[kSelBlk * blk + j] = 0u;
+                pos[kSelBlk * blk + j] = 0;
+            }
         }
     }
 }
 
-__global__ __launch_bounds__(128) __attribute__((amdgpu_waves_per_eu(4, 4))) void select_kernel(SelArgs a) {
+__global__ __launch_bounds__(64 * kSelW) void select_kernel(SelArgs a) {
     __shared__ uint32_t hist[256];
-    __shared__ uint32_t xch[4];
+    __shared__ uint32_t xch[2 * kSelW];
     const int tid = (int)threadIdx.x;
     const int h = tid >> 6, lane = tid & 63;
     const int64_t g = a.f0 + (int64_t)blockIdx.x;
-    int64_t pos, ss;
-    locate(a.map, g, pos, ss);
-    const int64_t n = pos + 1;
+    int64_t pos_t, ss;
+    locate(a.map, g, pos_t, ss);
+    const int64_t n = pos_t + 1;
     const int topk = a.topk;
     const int need = n < topk ? (int)n : topk;
     int32_t *oi = a.idx + g * topk;
@@ -636,7 +646,7 @@ __global__ __launch_bounds__(128) __attribute__((amdgpu_waves_per_eu(4, 4))) voi
     if (*a.status & 1u) {
         // a wait of the scoring kernel ran out of polls: its scores are not to be trusted,
         // so the row is marked invalid (index -2, NaN) instead of returning a wrong selection
-        for (int i = tid; i < topk; i += 128) {
+        for (int i = tid; i < topk; i += 64 * kSelW) {
             oi[i] = -2;
             if (os) os[i] = __builtin_nanf("");
         }
@@ -652,12 +662,14 @@ __global__ __launch_bounds__(128) __attribute__((amdgpu_waves_per_eu(4, 4))) voi
         return;
     }
     const int nit_all = (total + 63) >> 6;
-    const int nit0 = (nit_all + 1) >> 1;
-    const int nit = h == 0 ? nit0 : nit_all - nit0;
+    const int per = (nit_all + kSelW - 1) / kSelW;
+    const int g0 = min(h * per, nit_all);
+    const int nit = min(per, nit_all - g0);
     const uint2 *list = a.cand + lrow * (int64_t)(a.cap + 64);
-    const int first = h ? 64 * nit0 : 0;
+    const int first = 64 * g0;
     uint32_t key[kSelKeys];
-    sel_load(key, list, nit, lane, first, total);
+    int32_t pos[kSelKeys];
+    sel_load(key, pos, list, nit, lane, first, total);
     uint32_t lo = 0xFFFFFFFFu, hi = 0u;
 #pragma unroll
     for (int i = 0; i < kSelKeys; ++i)
@@ -676,8 +688,11 @@ __global__ __launch_bounds__(128) __attribute__((amdgpu_waves_per_eu(4, 4))) voi
         xch[2 * h + 1] = hi;
     }
     __syncthreads();
-    lo = xch[0] < xch[2] ? xch[0] : xch[2];
-    hi = xch[1] > xch[3] ? xch[1] : xch[3];
+#pragma unroll
+    for (int v = 0; v < kSelW; ++v) {
+        lo = xch[2 * v] < lo ? xch[2 * v] : lo;
+        hi = xch[2 * v + 1] > hi ? xch[2 * v + 1] : hi;
+    }
     // radix select over rel = key - lo, 8 bits at a time from the top
     int left = need;          // winners still to place among the keys matching the prefix
     uint32_t prefix = 0, pmask = 0;
@@ -687,10 +702,7 @@ __global__ __launch_bounds__(128) __attribute__((amdgpu_waves_per_eu(4, 4))) voi
         const int wd = hb < 8 ? hb : 8;
         const int shift = hb - wd;
         const uint32_t dmask = (1u << wd) - 1u;
-        if (h == 0) {
-#pragma unroll
-            for (int i = 0; i < 4; ++i) hist[4 * lane + i] = 0u;
-        }
+        hist[tid] = 0u;       // 256 threads, 256 bins
         __syncthreads();
 #pragma unroll
         for (int i = 0; i < kSelKeys; ++i) {
@@ -707,52 +719,52 @@ __global__ __launch_bounds__(128) __attribute__((amdgpu_waves_per_eu(4, 4))) voi
         __syncthreads();   // every read of this pass's histogram is done
     }
     const uint32_t theta = lo + prefix;   // the need-th largest key; `left` keys equal to it win
-    const uint64_t below = (1ull << lane) - 1ull;
-    // the first wave's winners and keys equal to theta, for the second wave's starting point
-    int out = 0, eq_seen = 0;
-    if (h == 0) {
+    // this wave's keys above theta and equal to it; from those of the waves before it, where
+    // its winners start and how many keys equal to theta were seen before it
+    int gt = 0, eq = 0;
 #pragma unroll
-        for (int i = 0; i < kSelKeys; ++i) {
-            const bool eq = (key[i] == theta) & (key[i] != 0u);
-            const uint64_t em = __ballot(eq);
-            const bool keep = (key[i] > theta) | (eq & (eq_seen + (int)__popcll(em & below) < left));
-            eq_seen += (int)__popcll(em);
-            out += (int)__popcll(__ballot(keep));
-        }
-        if (lane == 0) {
-            xch[0] = (uint32_t)out;
-            xch[1] = (uint32_t)eq_seen;
-        }
+    for (int i = 0; i < kSelKeys; ++i) {
+        gt += (int)__popcll(__ballot((key[i] > theta) & (key[i] != 0u)));
+        eq += (int)__popcll(__ballot((key[i] == theta) & (key[i] != 0u)));
+    }
+    if (lane == 0) {
+        xch[2 * h] = (uint32_t)gt;
+        xch[2 * h + 1] = (uint32_t)eq;
     }
     __syncthreads();
-    out = h ? (int)xch[0] : 0;
-    eq_seen = h ? (int)xch[1] : 0;
+    int out = 0, eq_seen = 0;
+#pragma unroll
+    for (int v = 0; v < kSelW; ++v) {
+        if (v < h) {
+            const int gv = (int)xch[2 * v], ev = (int)xch[2 * v + 1];
+            const int ek = left - eq_seen;   // keys equal to theta that still win
+            out += gv + (ek <= 0 ? 0 : (ek < ev ? ek : ev));
+            eq_seen += ev;
+        }
+    }
     // the winners, in list order; the lanes that keep nothing store to a dummy word
-    int32_t *const dummy_i = a.dummy_i + 2 * (tid >> 6);
+    const uint64_t below = (1ull << lane) - 1ull;
+    int32_t *const dummy_i = a.dummy_i + 2 * h;
     float *const dummy_s = reinterpret_cast<float *>(dummy_i + 1);
 #pragma unroll
     for (int blk = 0; blk < kSelKeys / kSelBlk; ++blk) {
         if (kSelBlk * blk < nit) {
-            int32_t ix[kSelBlk];   // all of the block's loads in flight before any store
-#pragma unroll
-            for (int j = 0; j < kSelBlk; ++j)
-                ix[j] = (int32_t)list[sel_entry(kSelBlk * blk + j, nit, lane, first, total)].y;
 #pragma unroll
             for (int j = 0; j < kSelBlk; ++j) {
                 const int i = kSelBlk * blk + j;
-                const bool eq = (key[i] == theta) & (key[i] != 0u);
-                const uint64_t em = __ballot(eq);
-                const bool keep = (key[i] > theta) | (eq & (eq_seen + (int)__popcll(em & below) < left));
+                const bool e = (key[i] == theta) & (key[i] != 0u);
+                const uint64_t em = __ballot(e);
+                const bool keep = (key[i] > theta) | (e & (eq_seen + (int)__popcll(em & below) < left));
                 eq_seen += (int)__popcll(em);
                 const uint64_t km = __ballot(keep);
                 const int p = out + (int)__popcll(km & below);
                 out += (int)__popcll(km);
-                *(keep ? oi + p : dummy_i) = ix[j];
+                *(keep ? oi + p : dummy_i) = pos[i];
                 if (os) *(keep ? os + p : dummy_s) = key_score(key[i]);
             }
         }
     }
-    for (int i = need + tid; i < topk; i += 128) {
+    for (int i = need + tid; i < topk; i += 64 * kSelW) {
         oi[i] = -1;
         if (os) os[i] = -INFINITY;
     }
@@ -1267,7 +1279,7 @@ hipError_t launch_prefill_topk(const PrefillPlan &p, const uint16_t *q, const ui
             if (a.seg_tiles > 0)
                 hipLaunchKernelGGL(select_multi_kernel, dim3((unsigned)(f1 - f0)), dim3(64 * kSelMW), 0, st, s);
             else
-                hipLaunchKernelGGL(select_kernel, dim3((unsigned)(f1 - f0)), dim3(128), 0, st, s);
+                hipLaunchKernelGGL(select_kernel, dim3((unsigned)(f1 - f0)), dim3(64 * kSelW), 0, st, s);
             e = hipGetLastError();
         }
         if (e != hipSuccess) return e;
