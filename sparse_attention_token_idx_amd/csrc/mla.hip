@@ -7,21 +7,23 @@
 // picked rows, and out_h = sum_s p_h(s) kv[s][0:512] (the dense value up-projection, gate and
 // output projection come after this step).
 //
-// One workgroup takes one query and a contiguous split of its selections; its 12 waves pair up
-// on 16 heads each, the two waves of a pair taking alternate 32-dim k-steps of the 576 logit
-// dims and alternate 16-dim tiles of the 512 output dims, so that a wave holds its query
-// slice (36 VGPRs) and its output (64) with three waves per SIMD.  The selected cache rows
-// stream through LDS 32 at a time with direct global->LDS loads, three tiles deep, row-major
-// (a token's 72 16-byte pieces in a row, the piece order swizzled by the token so that the
-// rows one operand read touches fall in different banks).  The logits S^T = K q~^T
-// (v_mfma_f32_16x16x32_bf16, the wave's q~ as the B operand) take K straight from those rows;
-// the pair adds its two halves through LDS.  The output O^T += V^T P^T takes V^T from the same
-// rows with the transposing LDS read of gfx950 (ds_read_b64_tr_b16: each 16-lane group loads 4
-// tokens x 16 dims and every lane receives one dim of the 4 tokens), and P^T straight from the
-// logit accumulators (the 32 tokens of a tile taken in the order the accumulators hold them).
-// The softmax is online, in the log2 domain; with several splits per query, each split writes
-// its (max, sum) and its output normalised by its own sum, in bf16 (a convex combination of
-// latents, so in their range), and a second kernel merges them.
+// One workgroup takes one query and a contiguous split of its selections; its 3 waves, one per
+// SIMD, take 32 heads each (two 16-head MFMA groups) over all 576 logit dims and all 512 output
+// dims, so that every tile is read from LDS once per 32 heads: the wave's query slice stays in
+// 144 VGPRs and its output in the 256 accumulation registers.  The selected cache rows stream
+// through LDS 32 at a time with direct global->LDS loads, four tiles deep, row-major (a
+// token's 72 16-byte pieces in a row, the piece order swizzled by the token so that the rows
+// one operand read touches fall in different banks).  The logits S^T = K q~^T
+// (v_mfma_f32_16x16x32_bf16, the wave's q~ as the B operand) take K straight from those rows.
+// The output O^T += V^T P^T takes V^T from the same rows with the transposing LDS read of
+// gfx950 (ds_read_b64_tr_b16: each 16-lane group loads 4 tokens x 16 dims and every lane
+// receives one dim of the 4 tokens), and P^T straight from the logit accumulators (the 32
+// tokens of a tile taken in the order the accumulators hold them).  The softmax is in the log2
+// domain against a fixed reference per head (the first tile's maximum), so the accumulated
+// output is never rescaled; a split whose logits outrun the reference by more than 2^64 is run
+// again against the true maxima.  With several splits per query, each split writes its (max,
+// sum) and its output normalised by its own sum, in bf16 (a convex combination of latents, so
+// in their range), and a second kernel merges them.
 #include "common.hpp"
 #include "launch.hpp"
 
@@ -31,13 +33,14 @@ namespace {
 constexpr int kMlaHeads = 96;
 constexpr int kKv = 576;                 // cached values per token
 constexpr int kV = 512;                  // latent (value) dims
-constexpr int kWavesMla = 2 * (kMlaHeads / 16);   // a pair per 16 heads
+constexpr int kHeadsPerWave = 32;        // two 16-head MFMA groups, every logit and output dim
+constexpr int kWavesMla = kMlaHeads / kHeadsPerWave;   // 3, one per SIMD
 constexpr int kMlaThreads = 64 * kWavesMla;
 constexpr int kTile = 32;                // selected tokens per LDS tile
 constexpr int kPieces = kKv / 8;         // 16-byte pieces of a cache row: 72
 constexpr int kSlots = kTile * kPieces;  // of a tile: 2,304 = 36 load instructions of 64 lanes
-constexpr int kSlotsPerWave = kSlots / kMlaThreads;   // 3
-constexpr int kBufs = 3;                 // tiles in LDS: the current one and two in flight
+constexpr int kSlotsPerWave = kSlots / kMlaThreads;   // 12
+constexpr int kBufs = 4;                 // tiles in LDS: being read, being added, two in flight
 constexpr int kMaxSel = 2048;            // selections per split held in LDS
 constexpr int kTileBytes = kSlots * 16;
 constexpr int kHalfTileBytes = kTileBytes / 2;        // tokens 16..31 start here
@@ -51,8 +54,8 @@ typedef __attribute__((address_space(3))) u32x4 lds_u32x4;
 
 struct MlaSmem {
     uint16_t k[kBufs][kSlots * 8];   // token tau's piece u sits in slot 72 tau + (u ^ swz(tau))
-    int32_t sel[kMaxSel];            // this split's selections (-1: none)
-    f32x4 sx[kWavesMla][2][64];      // each wave's half of the logits, for its partner
+    int32_t sel[kMaxSel];            // this split's cache rows (INT_MIN: none)
+    uint32_t slot_pk[kWavesMla][kSlotsPerWave / 2][64];   // each lane's tile-load constants
 };
 
 // Piece u of token tau sits at position u ^ swz(tau) among the token's 72 slots: a permutation
@@ -64,7 +67,11 @@ struct MlaSmem {
 // values on the 4 tokens of equal parity among any 8 tokens 8 m .. 8 m + 7 (a transposing read:
 // 32 lanes, 8 tokens x 32 bytes), so that both fill the banks once.  An involution.
 __device__ __forceinline__ int swz(int tau) { return (2 * ((tau >> 1) & 3) + ((tau >> 3) & 1)) & 7; }
-constexpr float kLazy = 8.f;   // a head's reference max moves only when exceeded by 2^8
+template <bool B> struct Flag {
+    static constexpr bool value = B;
+};
+
+constexpr float kRefRange = 64.f;   // logits may exceed a head's reference by this much (log2 units)
 
 struct MlaArgs {
     const uint16_t *q;       // [T][96][576]
@@ -90,8 +97,8 @@ __device__ __forceinline__ uint32_t bf16_pair(float lo, float hi) {
     return __builtin_bit_cast(uint32_t, __builtin_convertvector((f32x2_t{lo, hi}), bf16x2_t));
 }
 
-// 2^x with the hardware instruction: the arguments here are at most 8 (or -inf), and a result
-// below the normal range (a weight under 2^-126 of the largest) may flush to 0.
+// 2^x with the hardware instruction: the arguments here are at most kRefRange = 64 (or -inf),
+// and a result below the normal range (a weight under 2^-126 of the reference) may flush to 0.
 __device__ __forceinline__ float exp2_hw(float x) { return __builtin_amdgcn_exp2f(x); }
 
 // Workgroup barrier over LDS traffic only: __syncthreads() would also wait for every global
@@ -111,246 +118,320 @@ __device__ __forceinline__ uint2 tr_read(const lds_char *p) {
     return __builtin_bit_cast(uint2, v);
 }
 
-__global__ __launch_bounds__(kMlaThreads, 1) void sparse_mla_kernel(MlaArgs a) {
+__global__ __launch_bounds__(kMlaThreads, 1) __attribute__((amdgpu_waves_per_eu(1, 1)))
+void sparse_mla_kernel(MlaArgs a) {
     extern __shared__ __align__(16) unsigned char smem_raw[];
     MlaSmem &sm = *reinterpret_cast<MlaSmem *>(smem_raw);
     const lds_char *lds_k = (const lds_char *)smem_raw;   // the tile buffers start the area
-    const int split = blockIdx.x;
-    const int64_t t = blockIdx.y;
+    // The splits of a query run on one XCD (workgroup i runs on XCD i mod 8), so its q~ comes from
+    // HBM once and from that XCD's L2 for the other splits: query t sits on XCD t mod 8, and
+    // workgroups past the last query end at once.
+    const int xcd = blockIdx.x & 7, chunk = blockIdx.x >> 3;
+    const int split = chunk % a.nsplit;
+    const int64_t t = 8 * (int64_t)(chunk / a.nsplit) + xcd;
+    if (t >= a.T) return;
     const int tid = threadIdx.x, lane = tid & 63;
     const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
     const int l16 = lane & 15, g = lane >> 4;
-    const int hg = wave >> 1, half = wave & 1;   // heads 16 hg .. + 15; alternate k-steps / tiles
-    constexpr int kKs = kKv / 32 / 2;             // logit k-steps of a wave: 9
-    constexpr int kMt = kV / 16 / 2;              // 16-dim output tiles of a wave: 16
+    constexpr int kKs = kKv / 32;                 // logit k-steps: 18
+    constexpr int kMt = kV / 16;                  // 16-dim output tiles: 32
+    constexpr int kG = kHeadsPerWave / 16;        // head groups of a wave: 2
     const int sel0 = split * a.per;
     const int nsel = max(0, min(a.topk, sel0 + a.per) - sel0);
     const int ntile = (nsel + kTile - 1) / kTile;
     const int64_t base = a.row0 ? a.row0[t] : 0;
-    for (int x = tid; x < ntile * kTile; x += kMlaThreads)
-        sm.sel[x] = x < nsel ? a.idx[t * (int64_t)a.topk + sel0 + x] : -1;
+    for (int x = tid; x < ntile * kTile; x += kMlaThreads) {
+        // the cache row of each selection (below 2^31), or INT_MIN for none
+        const int32_t r = x < nsel ? a.idx[t * (int64_t)a.topk + sel0 + x] : -1;
+        sm.sel[x] = r >= 0 ? (int32_t)(base + r) : INT_MIN;
+    }
 
-    // this wave's q~ as the B operand of S^T = K q~^T: lane (l16, g) holds head 16 hg + l16,
-    // dims 32 (2 ks + half) + 8 g .. + 7
-    u32x4 qb[kKs];   // loaded after the first tiles' loads are issued (below)
+    // this wave's q~ as the B operand of S^T = K q~^T: lane (l16, g) holds head
+    // 32 wave + 16 e + l16, dims 32 ks + 8 g .. + 7
+    u32x4 qb[kG][kKs];   // loaded after tile 0's loads are issued (below)
     __syncthreads();   // sel
 
     // A tile goes to LDS with direct global->LDS loads: lane i of instruction j of a wave fills
-    // slot 64 (3 wave + j) + i, i.e. piece (slot % 72) ^ swz(tau) of token tau = slot / 72.  A token
-    // with no selection reads cache row 0 instead (its logit is masked, its weight is 0).
-    // Exactly kSlotsPerWave vector-memory instructions per tile and wave: the waits below count
-    // on it.
+    // slot 64 (12 wave + j) + i, i.e. piece (slot - 72 tau) ^ swz(tau) of token tau = slot / 72.
+    // A token with no selection reads cache row 0 instead (its logit is masked, its weight is
+    // 0).  Exactly kSlotsPerWave vector-memory instructions per tile and wave: the waits below
+    // count on it.  tau and the piece are the same for every tile, so they are worked out once
+    // into LDS, 16 bits per instruction (tau in bits 0-4, the piece in bits 5-11), two
+    // instructions per word: in registers they would crowd out the loop's.
     const char *kv_bytes = reinterpret_cast<const char *>(a.kv);
     const uint32_t lds_k0 = (uint32_t)(uintptr_t)(lds_void *)sm.k[0];
+#pragma unroll
+    for (int j = 0; j < kSlotsPerWave; j += 2) {
+        uint32_t v = 0;
+#pragma unroll
+        for (int h = 0; h < 2; ++h) {
+            const int slot = 64 * (kSlotsPerWave * wave + j + h) + lane;
+            const int tau = slot / kPieces;
+            const int piece = (slot - kPieces * tau) ^ swz(tau);
+            v |= (uint32_t)(tau | piece << 5) << (16 * h);
+        }
+        sm.slot_pk[wave][j / 2][lane] = v;   // read back by this lane only
+    }
     auto load_tile = [&](int tile, int buf_off) {
-        // the slot geometry is recomputed per tile from the lane index, itself recomputed here
-        // (v_mbcnt): held across the loop it would cost registers the operands need
-        int ln;
-        asm volatile("v_mbcnt_lo_u32_b32 %0, -1, 0\n\tv_mbcnt_hi_u32_b32 %0, -1, %0" : "=v"(ln));
-        int tau[kSlotsPerWave];
-        int32_t r[kSlotsPerWave];
+        // every row first: the loads are opaque to the compiler, which would otherwise wait for
+        // each LDS read in turn
+        uint32_t pk[kSlotsPerWave / 2], rw[kSlotsPerWave];
+#pragma unroll
+        for (int i = 0; i < kSlotsPerWave / 2; ++i) pk[i] = sm.slot_pk[wave][i][lane];
 #pragma unroll
         for (int j = 0; j < kSlotsPerWave; ++j) {
-            tau[j] = (64 * (kSlotsPerWave * wave + j) + ln) / kPieces;
-            r[j] = sm.sel[tile * kTile + tau[j]];
+            const uint32_t tau = (pk[j / 2] >> (16 * (j & 1))) & 31u;
+            rw[j] = (uint32_t)sm.sel[tile * kTile + tau];
         }
 #pragma unroll
         for (int j = 0; j < kSlotsPerWave; ++j) {
-            const int slot0 = 64 * (kSlotsPerWave * wave + j);
-            const int slot = slot0 + ln;
-            const int u16 = 16 * ((slot - kPieces * tau[j]) ^ swz(tau[j]));
-            const int64_t row = r[j] >= 0 ? base + r[j] : 0;
-            dma16(kv_bytes + (row * (2 * kKv) + u16),
-                  __builtin_amdgcn_readfirstlane(lds_k0 + buf_off + 16 * slot0));
+            const uint32_t u16 = ((pk[j / 2] >> (16 * (j & 1))) >> 1) & 0x7f0u;
+            // a token with no selection reads cache row 0 (its logit is masked, its weight is 0)
+            const uint64_t row = rw[j] & 0x7fffffffu;
+            dma16(kv_bytes + u16 + row * (2 * kKv),
+                  __builtin_amdgcn_readfirstlane(lds_k0 + buf_off + 16 * 64 * (kSlotsPerWave * wave + j)));
         }
     };
 
     // LDS byte offsets (within a tile) of this lane's operand reads.  Logits, k-step ks: token
-    // l16 (and 16 + l16, kHalfTileBytes further: the same swizzle), piece 8 ks + 4 half + g, at
-    // qk_base + 128 ks.
-    const int qk_base = 16 * (kPieces * l16 + ((4 * half + g) ^ swz(l16)));
-    // Values, tile mt (dims 16 (2 mt + half) ..): this lane loads token 4 g + (l16 >> 2) (and
-    // 16 + that, kHalfTileBytes further), dims 4 (l16 & 3) .. + 3 of the tile, i.e. piece
-    // 4 mt + 2 half + ((l16 & 3) >> 1), bytes 8 (l16 & 1) .., at pv_base[mt & 1] + 128 (mt >> 1)
+    // l16 (and 16 + l16, kHalfTileBytes further: the same swizzle), piece 4 ks + g, at
+    // qk_base[ks & 1] + 128 (ks >> 1).
+    int qk_base[2];
+#pragma unroll
+    for (int h = 0; h < 2; ++h) qk_base[h] = 16 * (kPieces * l16 + ((4 * h + g) ^ swz(l16)));
+    // Values, tile mt (dims 16 mt ..): this lane loads token 4 g + (l16 >> 2) (and 16 + that,
+    // kHalfTileBytes further), dims 4 (l16 & 3) .. + 3 of the tile, i.e. piece
+    // 2 mt + ((l16 & 3) >> 1), bytes 8 (l16 & 1) .., at pv_base[mt & 3] + 128 (mt >> 2)
     const int vtok = 4 * g + (l16 >> 2);
-    int pv_base[2];
+    int pv_base[4];
 #pragma unroll
-    for (int m2 = 0; m2 < 2; ++m2)
-        pv_base[m2] = 16 * (kPieces * vtok + ((4 * m2 + 2 * half + ((l16 & 3) >> 1)) ^ swz(vtok))) + 8 * (l16 & 1);
+    for (int m4 = 0; m4 < 4; ++m4)
+        pv_base[m4] = 16 * (kPieces * vtok + ((2 * m4 + ((l16 & 3) >> 1)) ^ swz(vtok))) + 8 * (l16 & 1);
 
-    f32x4 acc_o[kMt];   // O^T: lane (l16, g) holds dims 16 (2 mt + half) + 4 g + r of head 16 hg + l16
+    f32x4 acc_o[kG][kMt];   // O^T: lane (l16, g) holds dims 16 mt + 4 g + r of head 32 wave + 16 e + l16
 #pragma unroll
-    for (int mt = 0; mt < kMt; ++mt) acc_o[mt] = f32x4{0.f, 0.f, 0.f, 0.f};
-    float m_run = -INFINITY;   // running max of the head's logits (log2 domain)
-    float l_run = 0.f;         // this lane's part of the running sum
+    for (int e = 0; e < kG; ++e)
+#pragma unroll
+        for (int mt = 0; mt < kMt; ++mt) acc_o[e][mt] = f32x4{0.f, 0.f, 0.f, 0.f};
+    // The weights are exp2(logit - m_ref), m_ref a reference per head: the first finite tile max,
+    // so that no accumulated output ever needs rescaling (the accumulators stay in the matrix
+    // cores' registers).  A later tile may exceed it by up to kRefRange (weights up to 2^64,
+    // well inside fp32 and bf16); if any head's logits go further, the split is run again with
+    // each head's true maximum as its reference, which the first run has found by then.
+    float m_ref[kG], m_all[kG], l_run[kG];
+    u32x4 pb[kG];                 // P^T of the tile whose values are added next (bf16 pairs)
+    bool over = false;            // this lane's heads went past their reference range
 
-    u32x4 pb = {0u, 0u, 0u, 0u};   // P^T of the tile whose values are added next (bf16 pairs)
-    float factor = 1.f;            // and the rescaling of the output that must come first
-    bool rescale = false;
-
-    // Output update with the previous tile's values: O^T += V^T P^T over one 16-dim tile mt.
-    auto pv = [&](const lds_char *vb, int mt) {
-        const lds_char *vp = vb + pv_base[mt & 1] + 128 * (mt >> 1);
+    auto head_max = [](float x) {   // over the 4 lane groups that hold one head's tokens
+        x = fmaxf(x, __shfl_xor(x, 16, 64));
+        return fmaxf(x, __shfl_xor(x, 32, 64));
+    };
+    auto vread = [&](const lds_char *vb, int mt) {
+        const lds_char *vp = vb + pv_base[mt & 3] + 128 * (mt >> 2);
         const uint2 lo = tr_read(vp);
         const uint2 hi = tr_read(vp + kHalfTileBytes);
-        acc_o[mt] = mfma16x16x32(u32x4{lo.x, lo.y, hi.x, hi.y}, pb, acc_o[mt]);
+        return u32x4{lo.x, lo.y, hi.x, hi.y};
     };
-    auto apply_rescale = [&] {
-        if (__builtin_expect(rescale, 0)) {   // wave-uniform, rarely taken after the first tiles
+    // One pipeline step over tile `tile` (buffer kb):
+    //  A. its logits (matrix instructions only, the K operands read two k-steps ahead);
+    //  B. its weights (vector instructions), under the output update of the previous tile's
+    //     values (buffer vb, O^T += V^T P^T, both head groups from one read of V^T) when pv_tag
+    //     says so; the next step's update takes the new weights from pb.
+    auto step = [&](auto pv_tag, int tile, const lds_char *kb, const lds_char *vb) {
+        constexpr bool kPv = decltype(pv_tag)::value;
+        // A. S^T rows are tokens (two 16-token halves), columns the group's 16 heads
+        f32x4 s[kG][2];
 #pragma unroll
-            for (int mt = 0; mt < kMt; ++mt)
-#pragma unroll
-                for (int r = 0; r < 4; ++r) acc_o[mt][r] *= factor;
-        }
-    };
-    // One pipeline step: the logits of tile `tile` (buffer kb); then, when with_pv, the output
-    // update with the previous tile's values (buffer vb), issued just before the barrier of the
-    // logit exchange so that the matrix cores work through it while the waves compute the
-    // softmax (a barrier does not wait for them); then the softmax, which leaves the weights
-    // for the next step's output update in pb / factor / rescale.
-    auto step = [&](int tile, const lds_char *kb, const lds_char *vb, bool with_pv) {
-        // logits: S^T rows are tokens (two 16-token halves), columns the pair's 16 heads; this
-        // wave sums its k-steps, the partner's come through LDS
-        f32x4 s0 = {0.f, 0.f, 0.f, 0.f}, s1 = {0.f, 0.f, 0.f, 0.f};
+        for (int e = 0; e < kG; ++e) s[e][0] = s[e][1] = f32x4{0.f, 0.f, 0.f, 0.f};
+        auto kread = [&](int ks, u32x4 &k0, u32x4 &k1) {
+            const int off = qk_base[ks & 1] + 128 * (ks >> 1);
+            k0 = *(const lds_u32x4 *)(kb + off);
+            k1 = *(const lds_u32x4 *)(kb + off + kHalfTileBytes);
+        };
+        // K operands read two k-steps ahead of the matrix instructions that take them
+        u32x4 k0, k1, m0, m1;
+        kread(0, k0, k1);
+        kread(1, m0, m1);
 #pragma unroll
         for (int ks = 0; ks < kKs; ++ks) {
-            const int off = qk_base + 128 * ks;
-            const u32x4 k0 = *(const lds_u32x4 *)(kb + off);
-            const u32x4 k1 = *(const lds_u32x4 *)(kb + off + kHalfTileBytes);
-            s0 = mfma16x16x32(k0, qb[ks], s0);
-            s1 = mfma16x16x32(k1, qb[ks], s1);
-        }
-        sm.sx[wave][0][lane] = s0;
-        sm.sx[wave][1][lane] = s1;
-        if (with_pv) {
-            apply_rescale();
+            u32x4 n0, n1;
+            if (ks + 2 < kKs) kread(ks + 2, n0, n1);
 #pragma unroll
-            for (int mt = 0; mt < kMt; ++mt) pv(vb, mt);
-        }
-        lds_barrier();
-        {   // mine + partner's: both waves of a pair add the same two numbers, so they agree
-            const f32x4 o0 = sm.sx[wave ^ 1][0][lane], o1 = sm.sx[wave ^ 1][1][lane];
-#pragma unroll
-            for (int r = 0; r < 4; ++r) {
-                s0[r] += o0[r];
-                s1[r] += o1[r];
+            for (int e = 0; e < kG; ++e) {
+                s[e][0] = mfma16x16x32(k0, qb[e][ks], s[e][0]);
+                s[e][1] = mfma16x16x32(k1, qb[e][ks], s[e][1]);
             }
+            k0 = m0;
+            k1 = m1;
+            m0 = n0;
+            m1 = n1;
+            // keep each k-step's four accumulation chains in order: a chain's next product then
+            // comes four matrix instructions (64 cycles) after its last
+            __builtin_amdgcn_sched_barrier(0);
         }
-        // lane (l16, g): head 16 hg + l16, tokens 4 g + r (s0) and 16 + 4 g + r (s1)
+        // B. lane (l16, g): head 16 e + l16 of the wave's 32, tokens 4 g + r (s[e][0]) and
+        // 16 + 4 g + r (s[e][1])
         const int4 sa = *reinterpret_cast<const int4 *>(&sm.sel[tile * kTile + 4 * g]);
         const int4 sb = *reinterpret_cast<const int4 *>(&sm.sel[tile * kTile + 16 + 4 * g]);
         const int sv[8] = {sa.x, sa.y, sa.z, sa.w, sb.x, sb.y, sb.z, sb.w};
-        float z[8];
+        float z[kG][8], mx[kG];
 #pragma unroll
-        for (int r = 0; r < 4; ++r) {
-            z[r] = sv[r] >= 0 ? s0[r] * a.scale_log2 : -INFINITY;
-            z[4 + r] = sv[4 + r] >= 0 ? s1[r] * a.scale_log2 : -INFINITY;
+        for (int e = 0; e < kG; ++e) {
+#pragma unroll
+            for (int r = 0; r < 4; ++r) {
+                z[e][r] = sv[r] >= 0 ? s[e][0][r] * a.scale_log2 : -INFINITY;
+                z[e][4 + r] = sv[4 + r] >= 0 ? s[e][1][r] * a.scale_log2 : -INFINITY;
+            }
+            mx[e] = z[e][0];
+#pragma unroll
+            for (int r = 1; r < 8; ++r) mx[e] = fmaxf(mx[e], z[e][r]);
+            m_all[e] = fmaxf(m_all[e], mx[e]);
         }
-        float mx = z[0];
+        // a head without a reference yet (nothing weighed so far) takes this tile's maximum;
+        // the wave agrees on it (a branch the whole wave takes, on the first tiles only)
+        bool unset = false;
 #pragma unroll
-        for (int r = 1; r < 8; ++r) mx = fmaxf(mx, z[r]);
-        mx = fmaxf(mx, __shfl_xor(mx, 16, 64));
-        mx = fmaxf(mx, __shfl_xor(mx, 32, 64));
-        // The reference max m_run only moves when the tile's max exceeds it by more than 2^8
-        // (so the weights below stay under 256): the output and sum are kept relative to m_run,
-        // and most tiles then need no rescaling at all.  Both waves of a pair hold the same
-        // logits, so they move it together.
-        const bool move = mx > m_run + kLazy;
-        const float m_new = move ? mx : m_run;
-        factor = move ? exp2_hw(m_run - m_new) : 1.f;   // 0 when m_run is -inf
-        float p[8];
-        if (m_new == -INFINITY) {
+        for (int e = 0; e < kG; ++e) unset |= m_ref[e] == -INFINITY;
+        if (__builtin_amdgcn_ballot_w64(unset)) {
 #pragma unroll
-            for (int r = 0; r < 8; ++r) p[r] = 0.f;
+            for (int e = 0; e < kG; ++e) {
+                const float hm = head_max(mx[e]);
+                m_ref[e] = m_ref[e] == -INFINITY ? hm : m_ref[e];
+            }
+        }
+        // the new weights of head group e, their vector instructions placed between the output
+        // update's matrix instructions
+        u32x4 pn[kG];
+        auto weights = [&](int e) {
+            over |= mx[e] > m_ref[e] + kRefRange;
+            const bool none = m_ref[e] == -INFINITY;
+            float p[8], ps = 0.f;
+#pragma unroll
+            for (int r = 0; r < 8; ++r) {
+                p[r] = none ? 0.f : exp2_hw(z[e][r] - m_ref[e]);
+                ps += p[r];
+            }
+            l_run[e] += ps;
+            // P^T as the B operand: k slots 8 g .. 8 g + 7 are the lane's 8 tokens, and the V^T
+            // operand holds the same tokens (4 g .. 4 g + 3 and 16 + 4 g .. + 3)
+            pn[e] = u32x4{bf16_pair(p[0], p[1]), bf16_pair(p[2], p[3]), bf16_pair(p[4], p[5]), bf16_pair(p[6], p[7])};
+        };
+        if (kPv) {
+            u32x4 v = vread(vb, 0);
+#pragma unroll
+            for (int mt = 0; mt < kMt; ++mt) {
+                u32x4 vn;
+                if (mt + 1 < kMt) vn = vread(vb, mt + 1);
+#pragma unroll
+                for (int e = 0; e < kG; ++e) acc_o[e][mt] = mfma16x16x32(v, pb[e], acc_o[e][mt]);
+                if (mt == 2) weights(0);
+                if (mt == 10) weights(1);
+                if (mt == 2 || mt == 10) __builtin_amdgcn_sched_barrier(0);
+                v = vn;
+            }
         } else {
-#pragma unroll
-            for (int r = 0; r < 8; ++r) p[r] = exp2_hw(z[r] - m_new);
+            weights(0);
+            weights(1);
         }
-        m_run = m_new;
-        rescale = __ballot(move) != 0;
-        float ps = 0.f;
 #pragma unroll
-        for (int r = 0; r < 8; ++r) ps += p[r];
-        l_run = l_run * factor + ps;
-        // P^T as the B operand: k slots 8 g .. 8 g + 7 are the lane's 8 tokens, and the V^T
-        // operand holds the same tokens (4 g .. 4 g + 3 and 16 + 4 g .. + 3)
-        pb = u32x4{bf16_pair(p[0], p[1]), bf16_pair(p[2], p[3]), bf16_pair(p[4], p[5]), bf16_pair(p[6], p[7])};
+        for (int e = 0; e < kG; ++e) pb[e] = pn[e];
     };
 
-    // Tiles 0 and 1 are loaded ahead, tile 2 during step 0, and tile t + 1 (t >= 2) during step
-    // t, into the buffer of tile t - 2, whose values step t - 1 consumed.  So when step t
-    // begins, the loads of tile t + 1 are still in flight only for t <= 1.
-    if (ntile > 0) load_tile(0, 0);
-    if (ntile > 1) load_tile(1, kTileBytes);
-    {   // the queries, their latency under that of the first tiles' loads
-        const uint16_t *qh = a.q + (t * kMlaHeads + 16 * hg + l16) * (int64_t)kKv + 32 * half + 8 * g;
+    // the queries, their latency under that of tile 0's loads
+    auto load_queries = [&] {
 #pragma unroll
-        for (int ks = 0; ks < kKs; ++ks) qb[ks] = *reinterpret_cast<const u32x4 *>(qh + 64 * ks);
+        for (int e = 0; e < kG; ++e) {
+            const uint16_t *qh = a.q + (t * kMlaHeads + kHeadsPerWave * wave + 16 * e + l16) * (int64_t)kKv + 8 * g;
+#pragma unroll
+            for (int ks = 0; ks < kKs; ++ks) qb[e][ks] = *reinterpret_cast<const u32x4 *>(qh + 32 * ks);
+        }
         // use them here, so that the compiler waits for these loads before the tile loop rather
         // than inside it, where its count of loads in flight would not include the tiles' (the
         // wait drains the tiles' loads issued before them too: the first tile needs them anyway)
 #pragma unroll
-        for (int ks = 0; ks < kKs; ++ks) asm volatile("" ::"v"(qb[ks]));
-    }
-    // byte offsets of the current and previous tiles' buffers, kept in scalar registers
-    // (computing them from the tile index costs vector instructions on every operand address)
-    int cur_off = 0, prev_off = 0;
-#pragma unroll 1
-    for (int tile = 0; tile < ntile; ++tile) {
-        if (tile + 1 < ntile && tile <= 1)
-            asm volatile("s_waitcnt vmcnt(3)" ::: "memory");
-        else
-            asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
-        // every wave's loads of this tile have landed, and every wave is done with step
-        // tile - 1, i.e. with the values of tile - 2
-        lds_barrier();
-        const int next_off = cur_off == (kBufs - 1) * kTileBytes ? 0 : cur_off + kTileBytes;
-        if (tile == 0) {
-            if (ntile > 2) load_tile(2, 2 * kTileBytes);
-        } else if (tile >= 2 && tile + 1 < ntile) {
-            load_tile(tile + 1, next_off);
-        }
-        const lds_char *kb = lds_k + __builtin_amdgcn_readfirstlane(cur_off);
-        const lds_char *vb = lds_k + __builtin_amdgcn_readfirstlane(prev_off);
-        step(tile, kb, vb, tile > 0);
-        prev_off = cur_off;
-        cur_off = next_off;
-    }
-    if (ntile > 0) {   // the last tile's values
-        const lds_char *vb = lds_k + __builtin_amdgcn_readfirstlane(prev_off);
-        apply_rescale();
+        for (int e = 0; e < kG; ++e)
 #pragma unroll
-        for (int mt = 0; mt < kMt; ++mt) pv(vb, mt);
+            for (int ks = 0; ks < kKs; ++ks) asm volatile("" ::"v"(qb[e][ks]));
+    };
+    // Tiles 0 and 1 are loaded ahead and tile t + 2 during step t, into buffer (t + 2) % 4, whose
+    // tile t - 2 step t - 1 consumed.  So when step t begins, only tile t + 1's loads may still be
+    // in flight beside tile t's.
+#pragma unroll 1
+    for (int run = 0; run < 2; ++run) {
+#pragma unroll
+        for (int e = 0; e < kG; ++e) {
+#pragma unroll
+            for (int mt = 0; mt < kMt; ++mt) acc_o[e][mt] = f32x4{0.f, 0.f, 0.f, 0.f};
+            m_ref[e] = run ? head_max(m_all[e]) : -INFINITY;   // a run again: the true maxima
+            m_all[e] = -INFINITY;
+            l_run[e] = 0.f;
+            pb[e] = u32x4{0u, 0u, 0u, 0u};
+        }
+        over = false;
+        // tile 0 and the queries first; the wait for the queries (which drains tile 0's loads,
+        // issued before them) then leaves tile 1's loads in flight into step 0
+        if (ntile > 0) load_tile(0, 0);
+        if (run == 0) load_queries();
+        if (ntile > 1) load_tile(1, kTileBytes);
+        auto body = [&](auto pv_tag, int tile) {
+            if (tile + 1 < ntile)
+                asm volatile("s_waitcnt vmcnt(12)" ::: "memory");
+            else
+                asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
+            // every wave's loads of this tile have landed, and every wave is done with step
+            // tile - 1, i.e. with the values of tile - 2 (whose buffer tile + 2 takes)
+            lds_barrier();
+            if (tile + 2 < ntile) load_tile(tile + 2, ((tile + 2) & (kBufs - 1)) * kTileBytes);
+            const lds_char *kb = lds_k + (tile & (kBufs - 1)) * kTileBytes;
+            const lds_char *vb = lds_k + ((tile - 1) & (kBufs - 1)) * kTileBytes;
+            step(pv_tag, tile, kb, vb);
+        };
+        if (ntile > 0) body(Flag<false>{}, 0);
+#pragma unroll 1
+        for (int tile = 1; tile < ntile; ++tile) body(Flag<true>{}, tile);
+        if (ntile > 0) {   // the last tile's values
+            const lds_char *vb = lds_k + ((ntile - 1) & (kBufs - 1)) * kTileBytes;
+#pragma unroll
+            for (int mt = 0; mt < kMt; ++mt) {
+                const u32x4 va = vread(vb, mt);
+#pragma unroll
+                for (int e = 0; e < kG; ++e) acc_o[e][mt] = mfma16x16x32(va, pb[e], acc_o[e][mt]);
+            }
+        }
+        // run again (every wave: they share the tile ring) if any head left its range
+        if (!__syncthreads_or(over)) break;
     }
 
-    // the head's sum over its 4 lane groups
-    float l_tot = l_run + __shfl_xor(l_run, 16, 64);
-    l_tot += __shfl_xor(l_tot, 32, 64);
-    const int head = 16 * hg + l16;
-    if (a.nsplit == 1) {
-        const float inv = l_tot > 0.f ? 1.f / l_tot : 0.f;
-        uint16_t *oh = a.o + (t * kMlaHeads + head) * (int64_t)kV + 16 * half + 4 * g;
 #pragma unroll
-        for (int mt = 0; mt < kMt; ++mt) {
-            const f32x4 o = acc_o[mt];
-            const uint2 v = {bf16_pair(o[0] * inv, o[1] * inv), bf16_pair(o[2] * inv, o[3] * inv)};
-            *reinterpret_cast<uint2 *>(oh + 32 * mt) = v;
-        }
-        if (a.lse && g == 0 && half == 0)
-            a.lse[t * kMlaHeads + head] = l_tot > 0.f ? (m_run + log2f(l_tot)) * 0.69314718055994531f : -INFINITY;
-    } else {
-        const int64_t ph = ((int64_t)split * a.T + t) * kMlaHeads + head;
+    for (int e = 0; e < kG; ++e) {
+        // the head's sum over its 4 lane groups
+        float l_tot = l_run[e] + __shfl_xor(l_run[e], 16, 64);
+        l_tot += __shfl_xor(l_tot, 32, 64);
+        const int head = kHeadsPerWave * wave + 16 * e + l16;
         const float inv = l_tot > 0.f ? 1.f / l_tot : 0.f;
-        uint16_t *oh = a.part_o + ph * kV + 16 * half + 4 * g;
+        if (a.nsplit == 1) {
+            uint16_t *oh = a.o + (t * kMlaHeads + head) * (int64_t)kV + 4 * g;
 #pragma unroll
-        for (int mt = 0; mt < kMt; ++mt) {
-            const f32x4 o = acc_o[mt];
-            const uint2 v = {bf16_pair(o[0] * inv, o[1] * inv), bf16_pair(o[2] * inv, o[3] * inv)};
-            *reinterpret_cast<uint2 *>(oh + 32 * mt) = v;
-        }
-        if (g == 0 && half == 0) {
-            a.part_ml[2 * ph] = m_run;
-            a.part_ml[2 * ph + 1] = l_tot;
+            for (int mt = 0; mt < kMt; ++mt) {
+                const f32x4 o = acc_o[e][mt];
+                const uint2 v = {bf16_pair(o[0] * inv, o[1] * inv), bf16_pair(o[2] * inv, o[3] * inv)};
+                *reinterpret_cast<uint2 *>(oh + 16 * mt) = v;
+            }
+            if (a.lse && g == 0)
+                a.lse[t * kMlaHeads + head] = l_tot > 0.f ? (m_ref[e] + log2f(l_tot)) * 0.69314718055994531f : -INFINITY;
+        } else {
+            const int64_t ph = ((int64_t)split * a.T + t) * kMlaHeads + head;
+            uint16_t *oh = a.part_o + ph * kV + 4 * g;
+#pragma unroll
+            for (int mt = 0; mt < kMt; ++mt) {
+                const f32x4 o = acc_o[e][mt];
+                const uint2 v = {bf16_pair(o[0] * inv, o[1] * inv), bf16_pair(o[2] * inv, o[3] * inv)};
+                *reinterpret_cast<uint2 *>(oh + 16 * mt) = v;
+            }
+            if (g == 0) {
+                a.part_ml[2 * ph] = m_ref[e];
+                a.part_ml[2 * ph + 1] = l_tot;
+            }
         }
     }
 }
@@ -444,7 +525,8 @@ hipError_t launch_sparse_mla(const uint16_t *q, const uint16_t *kv, const int32_
     a.part_o = reinterpret_cast<uint16_t *>(ws);
     a.part_ml = ws ? reinterpret_cast<float *>(reinterpret_cast<char *>(ws) + (size_t)a.nsplit * (size_t)T * kMlaHeads * kV * 2u)
                    : nullptr;
-    hipLaunchKernelGGL(sparse_mla_kernel, dim3(a.nsplit, (unsigned)T), dim3(kMlaThreads), smem, stream, a);
+    const int64_t groups = (T + 7) / 8;   // of 8 queries, one per XCD
+    hipLaunchKernelGGL(sparse_mla_kernel, dim3((unsigned)(groups * 8 * a.nsplit)), dim3(kMlaThreads), smem, stream, a);
     hipError_t e = hipGetLastError();
     if (e != hipSuccess || a.nsplit == 1) return e;
     hipLaunchKernelGGL(sparse_mla_merge_kernel, dim3((unsigned)((T * kMlaHeads + 3) / 4)), dim3(256), 0, stream, a);

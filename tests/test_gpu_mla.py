@@ -114,6 +114,31 @@ def test_sparse_mla_peaked_softmax(dsa, qs):
     _check(dsa, to_host(o).reshape(T, NH, MLA_V), lse.cpu().numpy(), q, kv, idx)
 
 
+def test_sparse_mla_logit_far_above_the_first_tiles(dsa):
+    """The kernel weighs each head against a reference taken from its first tile and runs a split
+    again when a later logit lies more than 64 (log2 units) above it.  Planted rows give single
+    heads a logit about 100 log2 units above the rest: later in a split (the rerun), and in a
+    split's first tile (later weights then underflow to 0 against the high reference)."""
+    rng = np.random.default_rng(12)
+    T, N, topk = 4, 6000, 2048
+    q, kv, idx = _case(rng, T, N, topk)
+    S, per = _splits(dsa, T, topk)
+    assert S > 1
+    qf = oracle.bf16_to_f64(q)
+    alpha = 100.0 / (np.log2(np.e) * 192.0 ** -0.5)       # scale * alpha * log2(e) = 100
+    planted = []
+    for t in range(T):
+        for i, h in enumerate([0, 17, 50, 95]):
+            s = (t + 3 * i) % S
+            pos = s * per + (160 + h % 32 if i % 2 == 0 else 3)   # a later tile, or the first
+            idx[t, pos] = N + len(planted)                         # a row of its own
+            planted.append(alpha * qf[t, h] / (qf[t, h] @ qf[t, h]))
+    kv = np.concatenate([kv, _bf(np.asarray(planted))])
+    o, lse = dsa.sparse_mla(to_dev(q), to_dev(kv), torch.from_numpy(idx).cuda())
+    torch.cuda.synchronize()
+    _check(dsa, to_host(o).reshape(T, NH, MLA_V), lse.cpu().numpy(), q, kv, idx)
+
+
 def test_sparse_mla_empty_slots_offsets_and_empty_queries(dsa):
     rng = np.random.default_rng(3)
     T, N, topk = 6, 5000, 300
