@@ -439,22 +439,28 @@ void sparse_mla_kernel(MlaArgs a) {
 // Merge of the splits of one (query, head): one wave per (query, head), lane i owns dims
 // 8 i .. 8 i + 7.
 __global__ __launch_bounds__(256) void sparse_mla_merge_kernel(MlaArgs a) {
-    const int64_t qh = (int64_t)blockIdx.x * 4 + (threadIdx.x >> 6);   // t * 96 + head
-    if (qh >= a.T * kMlaHeads) return;
+    // Query t's partials were written on XCD t mod 8 (the main kernel's order) and are still in
+    // that XCD's L2: its heads are merged there too, 4 per workgroup.
+    const int xcd = blockIdx.x & 7, chunk = blockIdx.x >> 3;
+    const int64_t t = 8 * (int64_t)(chunk / (kMlaHeads / 4)) + xcd;
+    if (t >= a.T) return;
+    const int64_t qh = t * kMlaHeads + 4 * (chunk % (kMlaHeads / 4)) + (threadIdx.x >> 6);   // t * 96 + head
     const int lane = threadIdx.x & 63;
+    const int64_t stride = a.T * kMlaHeads;   // between splits
     float M = -INFINITY;
-    for (int s = 0; s < a.nsplit; ++s) M = fmaxf(M, a.part_ml[2 * ((int64_t)s * a.T * kMlaHeads + qh)]);
+#pragma unroll 4
+    for (int s = 0; s < a.nsplit; ++s) M = fmaxf(M, a.part_ml[2 * (s * stride + qh)]);
     float L = 0.f;
     float acc[8] = {0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f};
     if (M != -INFINITY) {
+#pragma unroll 4
         for (int s = 0; s < a.nsplit; ++s) {
-            const int64_t ph = (int64_t)s * a.T * kMlaHeads + qh;
+            const int64_t ph = s * stride + qh;
             const float ms = a.part_ml[2 * ph];
-            if (ms == -INFINITY) continue;
-            const float f = exp2f(ms - M);
-            L += f * a.part_ml[2 * ph + 1];
-            // the split's normalised output weighs by its share of the sum, f * l_s
-            const float fl = f * a.part_ml[2 * ph + 1];
+            // the split's normalised output weighs by its share of the sum, f * l_s (0 for a
+            // split with nothing selected)
+            const float fl = ms == -INFINITY ? 0.f : exp2f(ms - M) * a.part_ml[2 * ph + 1];
+            L += fl;
             const u32x4 x = *reinterpret_cast<const u32x4 *>(a.part_o + ph * kV + 8 * lane);
 #pragma unroll
             for (int r = 0; r < 4; ++r) {
@@ -529,7 +535,7 @@ hipError_t launch_sparse_mla(const uint16_t *q, const uint16_t *kv, const int32_
     hipLaunchKernelGGL(sparse_mla_kernel, dim3((unsigned)(groups * 8 * a.nsplit)), dim3(kMlaThreads), smem, stream, a);
     hipError_t e = hipGetLastError();
     if (e != hipSuccess || a.nsplit == 1) return e;
-    hipLaunchKernelGGL(sparse_mla_merge_kernel, dim3((unsigned)((T * kMlaHeads + 3) / 4)), dim3(256), 0, stream, a);
+    hipLaunchKernelGGL(sparse_mla_merge_kernel, dim3((unsigned)(groups * 8 * (kMlaHeads / 4))), dim3(256), 0, stream, a);
     return hipGetLastError();
 }
 
