@@ -266,6 +266,28 @@ def copy_rate(n_bytes=1 << 30, steps=10):
     return round(2 * n_bytes / (ms * 1e-3) / 1e9, 1)
 
 
+def mfma_rate(dsa, iters=6000, steps=5):
+    """Sustained bf16 MFMA rate of this device (TFLOP/s): the library's calibration kernel, 16
+    independent products per wave on register operands, zero and random bf16 operands (the
+    matrix cores' power, hence the clock, depends on the data); median of `steps` launches."""
+    import torch
+    out = {}
+    stream = torch.cuda.current_stream()
+    for name, rnd in (("random_operands", True), ("zero_operands", False)):
+        flop, sink = dsa.mfma_calibrate(iters, random_operands=rnd)
+        torch.cuda.synchronize()
+        t = []
+        for _ in range(steps):
+            e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+            e0.record(stream)
+            dsa.mfma_calibrate(iters, random_operands=rnd, sink=sink)
+            e1.record(stream)
+            torch.cuda.synchronize()
+            t.append(e0.elapsed_time(e1))
+        out[name] = round(flop / (float(np.median(t)) * 1e-3) / 1e12, 1)
+    return out
+
+
 def cpu_model():
     try:
         for line in open("/proc/cpuinfo"):
@@ -613,6 +635,9 @@ def main():
     dec = None if args.no_decode else bench_decode(dsa, args)
     chk = None if args.no_chunk else bench_chunk(dsa, args)
     v32 = None if args.no_v32 else bench_v32(dsa, args)
+    # last, so that its full matrix-core load (and the heat) comes after every timed leg
+    mfma_meas = mfma_rate(dsa)
+    log(f"sustained bf16 MFMA (calibration kernel): {mfma_meas} TFLOP/s")
     ms_wall = pre["wall"] * 1e3 / args.steps
     qps = args.T / (ms_wall * 1e-3)
     tflops = (pre["score_flop"] + pre["proj_flop"]) / (ms_wall * 1e-3) / 1e12
@@ -675,8 +700,12 @@ def main():
         "roofline": {"kernel": "score_kernel<32, filter> (score-and-filter pass)", "bound": "mfma",
                      "achieved": None if achieved is None else round(achieved, 1), "peak": PEAK_BF16_TFLOPS,
                      "unit": "TFLOP/s", "frac": None if achieved is None else round(achieved / PEAK_BF16_TFLOPS, 4),
-                     "traffic": filter_traffic(args), "algorithmic_flop_per_launch": pre["score_flop"]},
+                     "traffic": filter_traffic(args), "algorithmic_flop_per_launch": pre["score_flop"],
+                     "measured_peak": mfma_meas["random_operands"],
+                     "frac_of_measured_peak": None if achieved is None
+                     else round(achieved / mfma_meas["random_operands"], 4)},
         "device_copy_GBps": copy_gbps,
+        "mfma_sustained_TFLOPs": mfma_meas,
         "configs": configs,
         "decode": None if dec is None else {
             "workload": f"{dec['batch']} sequences, one new query each, cached bf16 keys "

@@ -384,6 +384,21 @@ int dsa_idx_set_wait_budget(int polls);
 int dsa_idx_phase_timing(int enable);
 int dsa_idx_phase_times(double *ms, int *count, int n);
 
+/* Calibration (not part of the indexer; for measurement only): the sustained bf16 matrix-core
+ * rate of the device, against which the score pass and the projections are measured beside the
+ * published peak of 2,516.6 TFLOP/s (which assumes the top clock).  Launches, on `stream`, 1,024
+ * workgroups of 4 waves; each wave runs `iters` rounds of 16 independent v_mfma_f32_16x16x32_bf16
+ * products on register operands (no memory traffic): zero operands (random_operands = 0) or
+ * bf16 values with random signs and mantissas in [0.5, 2) in magnitude (1), since the matrix
+ * cores' power, and hence the clock, depends on the data.  Each thread writes the sum of its
+ * accumulators to sink[thread] (device memory, at least DSA_IDX_CALIB_SINK floats; its values
+ * have no meaning beyond keeping the work).  *flop (host) receives the bf16 flop the launch
+ * executes: 1,024 x 4 x iters x 16 x 16,384.  Asynchronous; the caller times it with events.
+ * iters in [1, 2^32]. */
+#define DSA_IDX_CALIB_SINK 262144
+int dsa_idx_mfma_calibrate(int64_t iters, int random_operands, float *sink, size_t sink_floats, int64_t *flop,
+                           void *stream);
+
 #ifdef __cplusplus
 }
 #endif

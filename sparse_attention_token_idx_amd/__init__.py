@@ -113,6 +113,8 @@ def lib():
         L.dsa_idx_arch_supported.argtypes = [ctypes.c_char_p]
         L.dsa_idx_decode_fp8.restype = i32
         L.dsa_idx_decode_fp8.argtypes = [vp, vp, vp, vp, vp, vp, i32, i32, i32, vp, vp, vp, sz, vp]
+        L.dsa_idx_mfma_calibrate.restype = i32
+        L.dsa_idx_mfma_calibrate.argtypes = [i64, i32, vp, sz, ctypes.POINTER(i64), vp]
         _lib = L
     return _lib
 
@@ -368,6 +370,23 @@ def phase_times():
 def set_wait_budget(polls):
     """Diagnostic: polls per ring wait of the prefill score kernels; returns the previous value."""
     return lib().dsa_idx_set_wait_budget(int(polls))
+
+
+CALIB_SINK = 262144
+
+
+def mfma_calibrate(iters, random_operands=True, sink=None, stream=None):
+    """Calibration, not part of the indexer: launches the library's sustained-MFMA kernel
+    (iters rounds of 16 independent bf16 products per wave, on register operands) on `stream`
+    and returns (bf16 flop executed, sink).  Asynchronous; time it with events."""
+    if sink is None:
+        sink = torch.empty(CALIB_SINK, dtype=torch.float32, device="cuda")
+    _need(sink, "sink", torch.float32)
+    flop = ctypes.c_int64(0)
+    _check("dsa_idx_mfma_calibrate", lib().dsa_idx_mfma_calibrate(int(iters), 1 if random_operands else 0,
+                                                                  _ptr(sink), sink.numel(), ctypes.byref(flop),
+                                                                  _stream(stream)))
+    return flop.value, sink
 
 
 def prefill_scores(q, k, w, ws, cu_seqlens=None, max_seqlen=0, stream=None):

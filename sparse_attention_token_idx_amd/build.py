@@ -19,7 +19,7 @@ OBJ = os.path.join(HERE, "_build")
 SO = os.path.join(HERE, "libdsaidx.so")
 OBJ_SAN = os.path.join(HERE, "_build_san")
 SO_SAN = os.path.join(OBJ_SAN, "libdsaidx.so")
-SOURCES = ["api.cpp", "project.hip", "topk.hip", "decode.hip", "fp8.hip", "mla.hip", "prefill.hip"]
+SOURCES = ["api.cpp", "project.hip", "topk.hip", "decode.hip", "fp8.hip", "mla.hip", "prefill.hip", "calib.hip"]
 
 # Packed fp32 arithmetic is switched off for the device code (see the design notes); the
 # host pass only warns that it does not know the feature.

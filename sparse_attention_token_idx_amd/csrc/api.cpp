@@ -422,6 +422,22 @@ int dsa_idx_phase_times(double *ms, int *count, int n) {
     return ok();
 }
 
+static_assert(DSA_IDX_CALIB_SINK == dsaidx::kCalibBlocks * 256, "calibration sink size");
+
+int dsa_idx_mfma_calibrate(int64_t iters, int random_operands, float *sink, size_t sink_floats, int64_t *flop,
+                           void *stream) {
+    if (iters < 1 || iters > (int64_t)1 << 32) return fail(DSA_IDX_EINVAL, "iters=%lld must be in [1, 2^32]", (long long)iters);
+    if (!sink || !flop) return fail(DSA_IDX_EINVAL, "sink and flop must be non-NULL");
+    if (sink_floats < (size_t)DSA_IDX_CALIB_SINK) return fail(DSA_IDX_EINVAL, "sink_floats=%zu below %d", sink_floats, DSA_IDX_CALIB_SINK);
+    const int r = check_device();
+    if (r != DSA_IDX_OK) return r;
+    *flop = dsaidx::mfma_calibrate_flop(iters);
+    const hipError_t e = dsaidx::launch_mfma_calibrate(iters, random_operands ? 1 : 0, sink,
+                                                       reinterpret_cast<hipStream_t>(stream));
+    if (e != hipSuccess) return hip_fail("mfma_calibrate_kernel launch", e);
+    return ok();
+}
+
 int dsa_idx_set_wait_budget(int polls) {
     const int prev = dsaidx::prefill_wait_budget();
     dsaidx::prefill_set_wait_budget(polls);

@@ -184,4 +184,10 @@ hipError_t launch_sparse_mla(const uint16_t *q, const uint16_t *kv, const int32_
                              int64_t T, int topk, float scale, uint16_t *o, float *lse, float *ws,
                              hipStream_t stream);
 
+// ---- calibration of the sustained bf16 MFMA rate (calib.hip): kCalibBlocks workgroups of 256
+// threads, one float of `sink` per thread.
+constexpr int kCalibBlocks = 1024;
+int64_t mfma_calibrate_flop(int64_t iters);
+hipError_t launch_mfma_calibrate(int64_t iters, int random_operands, float *sink, hipStream_t stream);
+
 }  // namespace dsaidx

@@ -35,7 +35,7 @@ def test_exports_every_declared_symbol(dsa):
                           "dsa_idx_v32_score_topk_varlen", "dsa_idx_v32_prefill_chunk",
                           "dsa_idx_v32_decode", "dsa_idx_v32_decode_fp8", "dsa_idx_workspace_status",
                           "dsa_idx_set_wait_budget", "dsa_idx_phase_timing", "dsa_idx_phase_times",
-                          "dsa_idx_decode_noalloc", "dsa_idx_arch_supported"}
+                          "dsa_idx_decode_noalloc", "dsa_idx_arch_supported", "dsa_idx_mfma_calibrate"}
     for n in names:
         assert getattr(L, n) is not None
 
@@ -188,6 +188,14 @@ def test_rejections_before_device(dsa):
     assert L.dsa_idx_prefill_select(_vp(A), 2, 4, 10, 8, _vp(A), None, _vp(A), 1 << 30, None) == -1
     assert b"B * max_seqlen" in L.dsa_idx_last_error()
     assert L.dsa_idx_prefill_select(None, 1, 0, 0, 8, None, None, None, 0, None) == 0
+    # the MFMA calibration kernel: iteration count, sink size, null pointers
+    import ctypes
+    flop = ctypes.c_int64(0)
+    assert L.dsa_idx_mfma_calibrate(0, 1, _vp(A), dsa.CALIB_SINK, ctypes.byref(flop), None) == -1
+    assert L.dsa_idx_mfma_calibrate(10, 1, _vp(A), dsa.CALIB_SINK - 1, ctypes.byref(flop), None) == -1
+    assert b"sink_floats" in L.dsa_idx_last_error()
+    assert L.dsa_idx_mfma_calibrate(10, 1, None, dsa.CALIB_SINK, ctypes.byref(flop), None) == -1
+    assert L.dsa_idx_mfma_calibrate(10, 1, _vp(A), dsa.CALIB_SINK, None, None) == -1
     # decode
     assert L.dsa_idx_decode(_vp(A), _vp(A), _vp(A), _vp(A), _vp(A), 4, 100, 0, _vp(A), None, _vp(A),
                             1 << 30, None) == -2
