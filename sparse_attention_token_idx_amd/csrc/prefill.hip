@@ -599,25 +599,30 @@ struct SelArgs {
     int32_t *dummy_i;          // store target of the lanes that write nothing (2 words a wave)
 };
 
-// List entry of this wave's group i for lane `lane`: its own entry for i < nit, else the first
-// sentinel pair after the list (key 0), so that no load sits behind a branch.
-__device__ __forceinline__ int sel_entry(int i, int nit, int lane, int first, int total) {
-    return i < nit ? first + 64 * i + lane : total;
-}
-
-// This wave's order keys and key positions: entries first + 64 i + lane (i < nit; past the
-// list's end its sentinel run reads as key 0), kSelBlk loads in flight at a time.
-__device__ __forceinline__ void sel_load(uint32_t (&key)[kSelKeys], int32_t (&pos)[kSelKeys], const uint2 *list,
-                                         int nit, int lane, int first, int total) {
+// This wave's order keys and key positions: entry 64 i + lane of the wave's part of the list
+// (wb = its first entry) in key[i], pos[i], kSelBlk loads in flight at a time.
+// Blocks past the wave's nit groups are not read; inside a block, a group i >= nit reads the
+// wave's last group again (a uniform index, so no branch) and its keys are zeroed; entries past
+// the list's end inside its last group read the sentinel run, whose key is 0.
+// The scores are never -0 (each is a sum from +0 of products and ReLUs), so the cheaper key
+// serves; the sentinels (all bits set) get key 0.
+__device__ __forceinline__ void sel_load(uint32_t (&key)[kSelKeys], int32_t (&pos)[kSelKeys], const uint2 *wb,
+                                         int lane, int nit) {
+    nit = __builtin_amdgcn_readfirstlane(nit);
+    const char *const base = reinterpret_cast<const char *>(wb);   // the wave's first entry
 #pragma unroll
     for (int blk = 0; blk < kSelKeys / kSelBlk; ++blk) {
         if (kSelBlk * blk < nit) {
             uint2 e[kSelBlk];
 #pragma unroll
-            for (int j = 0; j < kSelBlk; ++j) e[j] = list[sel_entry(kSelBlk * blk + j, nit, lane, first, total)];
+            for (int j = 0; j < kSelBlk; ++j) {
+                const uint32_t gi = (uint32_t)min(kSelBlk * blk + j, nit - 1);
+                e[j] = *reinterpret_cast<const uint2 *>(base + (8u * (uint32_t)lane + 512u * gi));
+            }
 #pragma unroll
             for (int j = 0; j < kSelBlk; ++j) {
-                key[kSelBlk * blk + j] = score_key(__uint_as_float(e[j].x));
+                const uint32_t k = score_key_nz(__uint_as_float(e[j].x));
+                key[kSelBlk * blk + j] = kSelBlk * blk + j < nit ? k : 0u;
                 pos[kSelBlk * blk + j] = (int32_t)e[j].y;
             }
         } else {
@@ -666,17 +671,18 @@ __global__ __launch_bounds__(64 * kSelW) void select_kernel(SelArgs a) {
     const int g0 = min(h * per, nit_all);
     const int nit = min(per, nit_all - g0);
     const uint2 *list = a.cand + lrow * (int64_t)(a.cap + 64);
-    const int first = 64 * g0;
     uint32_t key[kSelKeys];
     int32_t pos[kSelKeys];
-    sel_load(key, pos, list, nit, lane, first, total);
+    sel_load(key, pos, list + 64 * g0, lane, nit);
+    // the smallest and largest keys present (key - 1 wraps 0, no key, to the top)
     uint32_t lo = 0xFFFFFFFFu, hi = 0u;
 #pragma unroll
-    for (int i = 0; i < kSelKeys; ++i)
-        if (key[i]) {
-            lo = key[i] < lo ? key[i] : lo;
-            hi = key[i] > hi ? key[i] : hi;
-        }
+    for (int i = 0; i < kSelKeys; i += 2) {
+        lo = min(lo, min(key[i] - 1u, key[i + 1] - 1u));
+        hi = max(hi, max(key[i], key[i + 1]));
+    }
+    lo += 1u;
+    if (lo == 0u) lo = 0xFFFFFFFFu;   // no key in this lane
 #pragma unroll
     for (int d = 32; d >= 1; d >>= 1) {
         const uint32_t olo = (uint32_t)__shfl_xor((int)lo, d, 64), ohi = (uint32_t)__shfl_xor((int)hi, d, 64);
@@ -721,11 +727,12 @@ __global__ __launch_bounds__(64 * kSelW) void select_kernel(SelArgs a) {
     const uint32_t theta = lo + prefix;   // the need-th largest key; `left` keys equal to it win
     // this wave's keys above theta and equal to it; from those of the waves before it, where
     // its winners start and how many keys equal to theta were seen before it
+    // (theta is a key present, so neither test holds for 0, no key)
     int gt = 0, eq = 0;
 #pragma unroll
     for (int i = 0; i < kSelKeys; ++i) {
-        gt += (int)__popcll(__ballot((key[i] > theta) & (key[i] != 0u)));
-        eq += (int)__popcll(__ballot((key[i] == theta) & (key[i] != 0u)));
+        gt += (int)__popcll(__ballot(key[i] > theta));
+        eq += (int)__popcll(__ballot(key[i] == theta));
     }
     if (lane == 0) {
         xch[2 * h] = (uint32_t)gt;
@@ -742,25 +749,26 @@ __global__ __launch_bounds__(64 * kSelW) void select_kernel(SelArgs a) {
             eq_seen += ev;
         }
     }
-    // the winners, in list order; the lanes that keep nothing store to a dummy word
-    const uint64_t below = (1ull << lane) - 1ull;
-    int32_t *const dummy_i = a.dummy_i + 2 * h;
-    float *const dummy_s = reinterpret_cast<float *>(dummy_i + 1);
+    // the winners, in list order
 #pragma unroll
     for (int blk = 0; blk < kSelKeys / kSelBlk; ++blk) {
         if (kSelBlk * blk < nit) {
 #pragma unroll
             for (int j = 0; j < kSelBlk; ++j) {
                 const int i = kSelBlk * blk + j;
-                const bool e = (key[i] == theta) & (key[i] != 0u);
-                const uint64_t em = __ballot(e);
-                const bool keep = (key[i] > theta) | (e & (eq_seen + (int)__popcll(em & below) < left));
-                eq_seen += (int)__popcll(em);
+                bool keep = key[i] > theta;
+                const uint64_t em = __ballot(key[i] == theta);
+                if (em) {   // the group holds keys equal to theta (a uniform branch, rarely taken)
+                    keep |= (key[i] == theta) & (eq_seen + (int)bits_below(em) < left);
+                    eq_seen += (int)__popcll(em);
+                }
                 const uint64_t km = __ballot(keep);
-                const int p = out + (int)__popcll(km & below);
+                if (keep) {
+                    const uint32_t p4 = 4u * ((uint32_t)out + bits_below(km));   // byte offset of the slot
+                    *reinterpret_cast<int32_t *>(reinterpret_cast<char *>(oi) + p4) = pos[i];
+                    if (os) *reinterpret_cast<float *>(reinterpret_cast<char *>(os) + p4) = key_score(key[i]);
+                }
                 out += (int)__popcll(km);
-                *(keep ? oi + p : dummy_i) = pos[i];
-                if (os) *(keep ? os + p : dummy_s) = key_score(key[i]);
             }
         }
     }
