@@ -699,10 +699,15 @@ __global__ __launch_bounds__(64 * kSelW) void select_kernel(SelArgs a) {
         lo = xch[2 * v] < lo ? xch[2 * v] : lo;
         hi = xch[2 * v + 1] > hi ? xch[2 * v + 1] : hi;
     }
-    // radix select over rel = key - lo, 8 bits at a time from the top
+    // Radix select over r = key - (lo - 1), in [1, hi - lo + 1] for the keys present, 8 bits at a
+    // time from the top; the empty slots keep r = 0 and stay out of the histograms (counted,
+    // their crowd in one bin would serialise the LDS atomics).
+    const uint32_t base = lo - 1u;
+#pragma unroll
+    for (int i = 0; i < kSelKeys; ++i) key[i] = key[i] ? key[i] - base : 0u;
     int left = need;          // winners still to place among the keys matching the prefix
     uint32_t prefix = 0, pmask = 0;
-    int hb = bit_width(hi - lo);
+    int hb = bit_width(hi - base);
 #pragma unroll 1
     while (hb > 0) {
         const int wd = hb < 8 ? hb : 8;
@@ -711,10 +716,9 @@ __global__ __launch_bounds__(64 * kSelW) void select_kernel(SelArgs a) {
         hist[tid] = 0u;       // 256 threads, 256 bins
         __syncthreads();
 #pragma unroll
-        for (int i = 0; i < kSelKeys; ++i) {
-            const uint32_t rel = key[i] - lo;
-            if (key[i] && (rel & pmask) == prefix) atomicAdd(&hist[(rel >> shift) & dmask], 1u);
-        }
+        for (int i = 0; i < kSelKeys; ++i)
+            if (key[i] && (key[i] & pmask) == prefix)
+                atomicAdd(&hist[__builtin_amdgcn_ubfe(key[i], (uint32_t)shift, (uint32_t)wd)], 1u);
         __syncthreads();
         int above = 0;
         const int d = find_bin_from_top(hist, left, above);
@@ -724,10 +728,10 @@ __global__ __launch_bounds__(64 * kSelW) void select_kernel(SelArgs a) {
         hb = shift;
         __syncthreads();   // every read of this pass's histogram is done
     }
-    const uint32_t theta = lo + prefix;   // the need-th largest key; `left` keys equal to it win
+    const uint32_t theta = prefix;   // r of the need-th largest key; `left` keys equal to it win
     // this wave's keys above theta and equal to it; from those of the waves before it, where
     // its winners start and how many keys equal to theta were seen before it
-    // (theta is a key present, so neither test holds for 0, no key)
+    // (theta >= 1, so neither test holds for an empty slot)
     int gt = 0, eq = 0;
 #pragma unroll
     for (int i = 0; i < kSelKeys; ++i) {
@@ -766,7 +770,7 @@ __global__ __launch_bounds__(64 * kSelW) void select_kernel(SelArgs a) {
                 if (keep) {
                     const uint32_t p4 = 4u * ((uint32_t)out + bits_below(km));   // byte offset of the slot
                     *reinterpret_cast<int32_t *>(reinterpret_cast<char *>(oi) + p4) = pos[i];
-                    if (os) *reinterpret_cast<float *>(reinterpret_cast<char *>(os) + p4) = key_score(key[i]);
+                    if (os) *reinterpret_cast<float *>(reinterpret_cast<char *>(os) + p4) = key_score(key[i] + base);
                 }
                 out += (int)__popcll(km);
             }
