@@ -674,59 +674,65 @@ __global__ __launch_bounds__(64 * kSelW) void select_kernel(SelArgs a) {
     uint32_t key[kSelKeys];
     int32_t pos[kSelKeys];
     sel_load(key, pos, list + 64 * g0, lane, nit);
-    // the smallest and largest keys present (key - 1 wraps 0, no key, to the top)
-    uint32_t lo = 0xFFFFFFFFu, hi = 0u;
+    // Every candidate wins when there are only `need` of them (a row of at most topk keys): theta
+    // 0 and no key to place by ties keep every key present and no empty slot.
+    uint32_t base = 0u, prefix = 0u;
+    int left = 0;             // winners still to place among the keys matching the prefix
+    if (total > need) {
+        // the smallest and largest keys present (key - 1 wraps 0, no key, to the top)
+        uint32_t lo = 0xFFFFFFFFu, hi = 0u;
 #pragma unroll
-    for (int i = 0; i < kSelKeys; i += 2) {
-        lo = min(lo, min(key[i] - 1u, key[i + 1] - 1u));
-        hi = max(hi, max(key[i], key[i + 1]));
-    }
-    lo += 1u;
-    if (lo == 0u) lo = 0xFFFFFFFFu;   // no key in this lane
+        for (int i = 0; i < kSelKeys; i += 2) {
+            lo = min(lo, min(key[i] - 1u, key[i + 1] - 1u));
+            hi = max(hi, max(key[i], key[i + 1]));
+        }
+        lo += 1u;
+        if (lo == 0u) lo = 0xFFFFFFFFu;   // no key in this lane
 #pragma unroll
-    for (int d = 32; d >= 1; d >>= 1) {
-        const uint32_t olo = (uint32_t)__shfl_xor((int)lo, d, 64), ohi = (uint32_t)__shfl_xor((int)hi, d, 64);
-        lo = olo < lo ? olo : lo;
-        hi = ohi > hi ? ohi : hi;
-    }
-    if (lane == 0) {
-        xch[2 * h] = lo;
-        xch[2 * h + 1] = hi;
-    }
-    __syncthreads();
+        for (int d = 32; d >= 1; d >>= 1) {
+            const uint32_t olo = (uint32_t)__shfl_xor((int)lo, d, 64), ohi = (uint32_t)__shfl_xor((int)hi, d, 64);
+            lo = olo < lo ? olo : lo;
+            hi = ohi > hi ? ohi : hi;
+        }
+        if (lane == 0) {
+            xch[2 * h] = lo;
+            xch[2 * h + 1] = hi;
+        }
+        __syncthreads();
 #pragma unroll
-    for (int v = 0; v < kSelW; ++v) {
-        lo = xch[2 * v] < lo ? xch[2 * v] : lo;
-        hi = xch[2 * v + 1] > hi ? xch[2 * v + 1] : hi;
-    }
-    // Radix select over r = key - (lo - 1), in [1, hi - lo + 1] for the keys present, 8 bits at a
-    // time from the top; the empty slots keep r = 0 and stay out of the histograms (counted,
-    // their crowd in one bin would serialise the LDS atomics).
-    const uint32_t base = lo - 1u;
+        for (int v = 0; v < kSelW; ++v) {
+            lo = xch[2 * v] < lo ? xch[2 * v] : lo;
+            hi = xch[2 * v + 1] > hi ? xch[2 * v + 1] : hi;
+        }
+        // Radix select over r = key - (lo - 1), in [1, hi - lo + 1] for the keys present, 8 bits
+        // at a time from the top; the empty slots keep r = 0 and stay out of the histograms
+        // (counted, their crowd in one bin would serialise the LDS atomics).
+        base = lo - 1u;
 #pragma unroll
-    for (int i = 0; i < kSelKeys; ++i) key[i] = key[i] ? key[i] - base : 0u;
-    int left = need;          // winners still to place among the keys matching the prefix
-    uint32_t prefix = 0, pmask = 0;
-    int hb = bit_width(hi - base);
+        for (int i = 0; i < kSelKeys; ++i) key[i] = key[i] ? key[i] - base : 0u;
+        left = need;
+        uint32_t pmask = 0;
+        int hb = bit_width(hi - base);
 #pragma unroll 1
-    while (hb > 0) {
-        const int wd = hb < 8 ? hb : 8;
-        const int shift = hb - wd;
-        const uint32_t dmask = (1u << wd) - 1u;
-        hist[tid] = 0u;       // 256 threads, 256 bins
-        __syncthreads();
+        while (hb > 0) {
+            const int wd = hb < 8 ? hb : 8;
+            const int shift = hb - wd;
+            const uint32_t dmask = (1u << wd) - 1u;
+            hist[tid] = 0u;       // 256 threads, 256 bins
+            __syncthreads();
 #pragma unroll
-        for (int i = 0; i < kSelKeys; ++i)
-            if (key[i] && (key[i] & pmask) == prefix)
-                atomicAdd(&hist[__builtin_amdgcn_ubfe(key[i], (uint32_t)shift, (uint32_t)wd)], 1u);
-        __syncthreads();
-        int above = 0;
-        const int d = find_bin_from_top(hist, left, above);
-        left -= above;
-        prefix |= (uint32_t)d << shift;
-        pmask |= dmask << shift;
-        hb = shift;
-        __syncthreads();   // every read of this pass's histogram is done
+            for (int i = 0; i < kSelKeys; ++i)
+                if (key[i] && (key[i] & pmask) == prefix)
+                    atomicAdd(&hist[__builtin_amdgcn_ubfe(key[i], (uint32_t)shift, (uint32_t)wd)], 1u);
+            __syncthreads();
+            int above = 0;
+            const int d = find_bin_from_top(hist, left, above);
+            left -= above;
+            prefix |= (uint32_t)d << shift;
+            pmask |= dmask << shift;
+            hb = shift;
+            __syncthreads();   // every read of this pass's histogram is done
+        }
     }
     const uint32_t theta = prefix;   // r of the need-th largest key; `left` keys equal to it win
     // this wave's keys above theta and equal to it; from those of the waves before it, where
@@ -858,16 +864,22 @@ __global__ __launch_bounds__(64 * kSelMW) void select_multi_kernel(SelArgs a) {
             }
         }
     }
-    uint32_t m = 0, mn = 0xFFFFFFFFu;
+    // every candidate wins when there are only `need` of them (a row of at most topk keys):
+    // theta 0 keeps every key present (and no empty slot)
+    uint32_t theta = 0u;
+    int keep = 0;
+    if (total > need) {
+        uint32_t m = 0, mn = 0xFFFFFFFFu;
 #pragma unroll
-    for (int i = 0; i < kPer; ++i) {
-        m = key[i] > m ? key[i] : m;
-        mn = key[i] != 0u && key[i] < mn ? key[i] : mn;
+        for (int i = 0; i < kPer; ++i) {
+            m = key[i] > m ? key[i] : m;
+            mn = key[i] != 0u && key[i] < mn ? key[i] : mn;
+        }
+        const uint32_t top = block_max(m, sm);
+        const uint32_t bot = ~block_max(~mn, sm);
+        keep = need;
+        theta = select_rel(key, bot, bit_width(top - bot), keep, sm);
     }
-    const uint32_t top = block_max(m, sm);
-    const uint32_t bot = ~block_max(~mn, sm);
-    int keep = need;
-    const uint32_t theta = select_rel(key, bot, bit_width(top - bot), keep, sm);
     int eq_base = 0;
     emit_ordered_idx(key, kidx, theta, keep, 0, eq_base, oi, os, sm);
     for (int i = need + tid; i < topk; i += 64 * kSelMW) {
