@@ -288,6 +288,29 @@ def mfma_rate(dsa, iters=6000, steps=5):
     return out
 
 
+def vendor_q_gemm(T, steps=10):
+    """A yardstick, not part of the path: torch.matmul (the vendor BLAS) on the q projection's
+    shape, [T, 1536] x [1536, 4096] bf16 with the weights K-contiguous as the library keeps
+    them, random normal operands; median and min of `steps` calls, ms."""
+    import torch
+    g = torch.Generator(device="cuda").manual_seed(0)
+    a = torch.randn(T, QLAT, device="cuda", generator=g).to(torch.bfloat16)
+    bt = (torch.randn(4096, QLAT, device="cuda", generator=g) / QLAT ** 0.5).to(torch.bfloat16)
+    for _ in range(3):
+        a @ bt.t()
+    torch.cuda.synchronize()
+    t = []
+    for _ in range(steps):
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        e0.record()
+        a @ bt.t()
+        e1.record()
+        torch.cuda.synchronize()
+        t.append(e0.elapsed_time(e1))
+    del a, bt
+    return stats(t)
+
+
 def cpu_model():
     try:
         for line in open("/proc/cpuinfo"):
@@ -635,6 +658,8 @@ def main():
     dec = None if args.no_decode else bench_decode(dsa, args)
     chk = None if args.no_chunk else bench_chunk(dsa, args)
     v32 = None if args.no_v32 else bench_v32(dsa, args)
+    vgemm = vendor_q_gemm(args.T)
+    log(f"yardstick: torch.matmul on the q projection's shape {vgemm} ms")
     # last, so that its full matrix-core load (and the heat) comes after every timed leg
     mfma_meas = mfma_rate(dsa)
     log(f"sustained bf16 MFMA (calibration kernel): {mfma_meas} TFLOP/s")
@@ -697,6 +722,10 @@ def main():
         "tflops": round(tflops, 1),
         "step_ms": pre["step"],
         "split_ms": {"project": pre["proj"], "score_topk": pre["score_topk"], "phases": pre["phases"]},
+        "yardstick": {"what": f"torch.matmul (vendor BLAS) on the q projection's shape [{args.T},1536] x "
+                              f"[1536,4096] bf16, not part of the path",
+                      "ms": vgemm,
+                      "frac_of_bf16_peak_median": frac(2 * args.T * QLAT * 4096, vgemm["median"])},
         "roofline": {"kernel": "score_kernel<32, filter> (score-and-filter pass)", "bound": "mfma",
                      "achieved": None if achieved is None else round(achieved, 1), "peak": PEAK_BF16_TFLOPS,
                      "unit": "TFLOP/s", "frac": None if achieved is None else round(achieved / PEAK_BF16_TFLOPS, 4),
