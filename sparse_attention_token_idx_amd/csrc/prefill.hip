@@ -35,6 +35,8 @@
 // 16-key slices give each lane the scores of eight consecutive keys.  Keys stream through a
 // ring of LDS tiles that every wave stages one eighth of; progress counters in LDS, not
 // workgroup barriers, order the ring, so the waves may drift two tiles apart.
+#include <algorithm>
+#include <functional>
 #include <mutex>
 #include <type_traits>
 #include <vector>
@@ -86,7 +88,8 @@ struct ScoreArgs {
     int64_t pos0;               // one sequence: position of row 0 (its keys: rows 0 .. pos0 + T - 1)
     int64_t g_lo, g_hi;         // only packed rows g_lo <= g < g_hi produce output
     int nrb;                    // grid.y: row blocks of the longest sequence
-    int seg_tiles;              // one sequence: key tiles per workgroup along grid.x (0: none)
+    int seg_tiles;              // one sequence: key tiles per workgroup (0: none)
+    int seg_y;                  // one sequence: segments on grid.y, row blocks on grid.x
     int spin;                   // polls allowed per wait on the key ring
     uint32_t *status;           // bit 0 set when a wait ran out of polls
     float *dummy;               // store target of rows with no output
@@ -154,12 +157,14 @@ __global__ __launch_bounds__(kThreads, 1) void score_kernel(ScoreArgs a) {
     extern __shared__ __align__(16) unsigned char smem_raw[];
     ScoreSmem &sm = *reinterpret_cast<ScoreSmem *>(smem_raw);
 
-    // One sequence: grid (key segments, row blocks).  Ragged batches: grid (row blocks,
-    // sequences), so that consecutive workgroups -- which the dispatcher deals to the 8 XCDs in
-    // turn -- are row blocks of one sequence rather than one row block of every sequence
-    // (which would pin each sequence to one XCD).  Longest rows first either way.
+    // One sequence: grid (key segments, row blocks), or (row blocks, key segments) with seg_y.
+    // Ragged batches: grid (row blocks, sequences), so that consecutive workgroups -- which the
+    // dispatcher deals to the 8 XCDs in turn -- are row blocks of one sequence rather than one
+    // row block of every sequence (which would pin each sequence to one XCD).  Longest rows
+    // first either way.
+    const bool rb_x = a.cu_seqlens || a.seg_y;
     const int seq = a.cu_seqlens ? (int)blockIdx.y : 0;
-    const int rb = a.nrb - 1 - (int)(a.cu_seqlens ? blockIdx.x : blockIdx.y);
+    const int rb = a.nrb - 1 - (int)(rb_x ? blockIdx.x : blockIdx.y);
     int64_t seq_start = 0, L = a.T;
     if (a.cu_seqlens) {
         seq_start = a.cu_seqlens[seq];
@@ -185,7 +190,7 @@ __global__ __launch_bounds__(kThreads, 1) void score_kernel(ScoreArgs a) {
     }
     int kt0 = 0, nt = nkt, seg = 0;
     if (a.seg_tiles > 0) {
-        seg = (int)blockIdx.x;
+        seg = (int)(a.seg_y ? blockIdx.y : blockIdx.x);
         kt0 = seg * a.seg_tiles;
         if (kt0 >= nkt) return;
         nt = nkt - kt0 < a.seg_tiles ? nkt - kt0 : a.seg_tiles;
@@ -599,25 +604,28 @@ struct SelArgs {
     int32_t *dummy_i;          // store target of the lanes that write nothing (2 words a wave)
 };
 
-// This wave's order keys and key positions: entry 64 i + lane of the wave's part of the list
-// (wb = its first entry) in key[i], pos[i], kSelBlk loads in flight at a time.
+// This wave's order keys and key positions: entry e0 + 64 i + lane of the row's list in key[i],
+// pos[i], kSelBlk loads in flight at a time.  The list is the c0 entries at l0 followed by the
+// entries at l1 (the keys of a row whose key tiles were split over two workgroups: the second
+// segment's keys all follow the first's); entry e is l0[e] below c0, else l1[e - c0].
 // Blocks past the wave's nit groups are not read; inside a block, a group i >= nit reads the
 // wave's last group again (a uniform index, so no branch) and its keys are zeroed; entries past
-// the list's end inside its last group read the sentinel run, whose key is 0.
+// the list's end inside its last group read the sentinel run after l1's entries (l1 = l0 + c0
+// for a list in one piece), whose key is 0.
 // The scores are never -0 (each is a sum from +0 of products and ReLUs), so the cheaper key
 // serves; the sentinels (all bits set) get key 0.
-__device__ __forceinline__ void sel_load(uint32_t (&key)[kSelKeys], int32_t (&pos)[kSelKeys], const uint2 *wb,
-                                         int lane, int nit) {
+__device__ __forceinline__ void sel_load(uint32_t (&key)[kSelKeys], int32_t (&pos)[kSelKeys], const uint2 *l0,
+                                         int c0, const uint2 *l1, int e0, int lane, int nit) {
     nit = __builtin_amdgcn_readfirstlane(nit);
-    const char *const base = reinterpret_cast<const char *>(wb);   // the wave's first entry
 #pragma unroll
     for (int blk = 0; blk < kSelKeys / kSelBlk; ++blk) {
         if (kSelBlk * blk < nit) {
             uint2 e[kSelBlk];
 #pragma unroll
             for (int j = 0; j < kSelBlk; ++j) {
-                const uint32_t gi = (uint32_t)min(kSelBlk * blk + j, nit - 1);
-                e[j] = *reinterpret_cast<const uint2 *>(base + (8u * (uint32_t)lane + 512u * gi));
+                const int gi = min(kSelBlk * blk + j, nit - 1);
+                const int en = e0 + 64 * gi + lane;
+                e[j] = en < c0 ? l0[en] : l1[en - c0];
             }
 #pragma unroll
             for (int j = 0; j < kSelBlk; ++j) {
@@ -657,9 +665,14 @@ __global__ __launch_bounds__(64 * kSelW) void select_kernel(SelArgs a) {
         }
         return;
     }
+    // the row's list: one piece, or (key tiles split in two) its two segments' pieces
     const int64_t lrow = g - a.f0;
-    const int total = a.cnt[lrow];
-    if (total > a.cap || total < need) {
+    const int nsr = a.seg_tiles > 0 ? (int)((pos_t / kBK) / a.seg_tiles) + 1 : 1;
+    const int64_t l0i = lrow * a.nseg;
+    const int c0 = a.cnt[l0i];
+    const int c1 = nsr > 1 ? a.cnt[l0i + 1] : 0;
+    const int total = c0 + c1;
+    if (c0 > a.cap || c1 > a.cap || total > kSelCap || total < need) {
         if (tid == 0) {
             const uint32_t i = atomicAdd(&a.fb[1], 1u);
             a.fb_list[i] = g;
@@ -670,10 +683,11 @@ __global__ __launch_bounds__(64 * kSelW) void select_kernel(SelArgs a) {
     const int per = (nit_all + kSelW - 1) / kSelW;
     const int g0 = min(h * per, nit_all);
     const int nit = min(per, nit_all - g0);
-    const uint2 *list = a.cand + lrow * (int64_t)(a.cap + 64);
+    const uint2 *l0 = a.cand + l0i * (int64_t)(a.cap + 64);
+    const uint2 *l1 = nsr > 1 ? l0 + (a.cap + 64) : l0 + c0;
     uint32_t key[kSelKeys];
     int32_t pos[kSelKeys];
-    sel_load(key, pos, list + 64 * g0, lane, nit);
+    sel_load(key, pos, l0, c0, l1, 64 * g0, lane, nit);
     // Every candidate wins when there are only `need` of them (a row of at most topk keys): theta
     // 0 and no key to place by ties keep every key present and no empty slot.
     uint32_t base = 0u, prefix = 0u;
@@ -1076,11 +1090,82 @@ int split_tiles(int64_t nrb, int64_t max_nkt) {
 
 int64_t cdiv(int64_t a, int64_t b) { return (a + b - 1) / b; }
 
+constexpr int kCUs = 256;              // compute units of a gfx950 device
+constexpr int kSimOverhead = 2;        // a filter workgroup's query load and ring fill, in key tiles
+
+// How a one-sequence filter launch splits its key tiles: seg key tiles per workgroup (0: no
+// split), with the segments on grid.y (seg_y) or grid.x.
+struct FilterSplit {
+    int seg;
+    bool seg_y;
+};
+
+// The split of a filter launch over the rows rows at positions pos0 .. of one sequence, in row
+// blocks of bq.  With between a few row blocks and one and a half per CU, starting at most their
+// own count into the sequence, the launch is one or two rounds of workgroups whose time is that
+// of the busiest CU, set by the longest row blocks (at T = 8,192 the last one streams 64 key tiles
+// against 33 on average).  There the choice is between no split and the longest row block in two
+// segments (a row's two lists are then merged by the select), with the row blocks on grid.x:
+// the dispatcher deals consecutive workgroups to the 8 XCDs in turn and each XCD gives its next
+// workgroup to the CU that frees first, so the whole first segments go out longest first over
+// every XCD and the second segments follow on the CUs that the short ones free.  (With the
+// segments on grid.x instead, a row block's two halves alternate between even and odd XCDs and
+// the even ones get every long half.)  The choice with the least busy CU in that deal is kept,
+// and remembered per shape.  Otherwise split_tiles decides.
+int filter_span(int64_t rows, int bq, int64_t pos0, int64_t nrb, int seg) {
+    constexpr int kXcds = 8, kXcdCUs = kCUs / kXcds;
+    std::vector<int64_t> busy(kCUs, 0);   // XCD x's CUs at [kXcdCUs x, kXcdCUs x + kXcdCUs)
+    const int64_t nseg = seg ? cdiv((pos0 + rows - 1) / kBK + 1, seg) : 1;
+    int64_t span = 0, id = 0;
+    for (int64_t y = 0; y < nseg; ++y)
+        for (int64_t x = 0; x < nrb; ++x, ++id) {
+            const int64_t r0 = (nrb - 1 - x) * bq;
+            const int64_t nrows = rows - r0 < bq ? rows - r0 : bq;
+            const int64_t nkt = (pos0 + r0 + nrows - 1) / kBK + 1;
+            const int64_t kt0 = y * seg;
+            if (kt0 >= nkt) continue;   // exits at once
+            const int64_t len = seg && nkt - kt0 > seg ? seg : nkt - kt0;
+            int64_t *cu = &busy[(size_t)(id % kXcds) * kXcdCUs];
+            int64_t *m = std::min_element(cu, cu + kXcdCUs);
+            *m += len + kSimOverhead;
+            span = *m > span ? *m : span;
+        }
+    return (int)span;
+}
+
+FilterSplit filter_split(int64_t rows, int bq, int64_t pos0) {
+    const int64_t nrb = cdiv(rows, bq);
+    const int64_t max_nkt = (pos0 + rows - 1) / kBK + 1;
+    // the rows' key counts differ by less than 2x when the prefix is longer than the rows
+    if (nrb <= kFewRowBlocks || 2 * nrb > 3 * kCUs || pos0 >= rows)
+        return FilterSplit{split_tiles(nrb, max_nkt), false};
+    struct Shape {
+        int64_t rows, pos0;
+        int bq, seg;
+    };
+    static std::mutex mu;
+    static std::vector<Shape> seen;   // at most kSeenShapes shapes, first come
+    constexpr size_t kSeenShapes = 64;
+    {
+        std::lock_guard<std::mutex> lk(mu);
+        for (const Shape &sh : seen)
+            if (sh.rows == rows && sh.pos0 == pos0 && sh.bq == bq) return FilterSplit{sh.seg, sh.seg > 0};
+    }
+    const int half = (int)cdiv(max_nkt, 2);
+    const int seg = half >= kMinSegTilesFew && filter_span(rows, bq, pos0, nrb, half) < filter_span(rows, bq, pos0, nrb, 0)
+                        ? half
+                        : 0;
+    std::lock_guard<std::mutex> lk(mu);
+    if (seen.size() < kSeenShapes) seen.push_back(Shape{rows, pos0, bq, seg});
+    return FilterSplit{seg, seg > 0};
+}
+
 template <int kH>
 hipError_t launch_score(int mode, const ScoreArgs &a, unsigned gx, hipStream_t st) {
     const size_t smem = sizeof(ScoreSmem);
-    // ragged batches: grid (row blocks, sequences), gx = the sequence count
-    const dim3 grid = a.cu_seqlens ? dim3((unsigned)a.nrb, gx) : dim3(gx, (unsigned)a.nrb);
+    // ragged batches: grid (row blocks, sequences), gx = the sequence count; one sequence: gx
+    // key segments, on grid.y with seg_y
+    const dim3 grid = a.cu_seqlens || a.seg_y ? dim3((unsigned)a.nrb, gx) : dim3(gx, (unsigned)a.nrb);
     if constexpr (kH == 32) {
         if (mode == kModeRows) {
             hipLaunchKernelGGL((score_kernel<32, kModeRows>), grid, dim3(kThreads), smem, st, a);
@@ -1137,15 +1222,16 @@ PrefillPlan prefill_plan(int heads, bool varlen, int64_t rows, int B, int64_t ma
     p.pos0 = varlen ? 0 : pos0;
     const int bq = heads == 64 ? Geo<64>::kBQ : Geo<32>::kBQ;
     const int64_t nkeys = p.pos0 + p.max_len;     // keys of the longest row
-    p.cf = rows < kFilterRows ? rows : kFilterRows;
-    if (heads == 64 && p.cf > kFilterRows / 2) p.cf = kFilterRows / 2;
+    // filter chunks of equal size: a short last chunk would be a launch of few row blocks
+    const int64_t cmax = heads == 64 ? kFilterRows / 2 : kFilterRows;
+    p.cf = rows > 0 ? cdiv(rows, cdiv(rows, cmax)) : 0;
     // lists of a filter chunk: rows x segments (dense chunks may split their key tiles)
     p.lists = 0;
     for (int64_t f0 = 0; f0 < rows; f0 += p.cf) {
         const int64_t f1 = f0 + p.cf < rows ? f0 + p.cf : rows;
         int64_t nseg = 1;
         if (!varlen) {
-            const int st = split_tiles(cdiv(f1 - f0, bq), (p.pos0 + f1 - 1) / kBK + 1);
+            const int st = filter_split(f1 - f0, bq, p.pos0 + f0).seg;
             if (st) nseg = cdiv((p.pos0 + f1 - 1) / kBK + 1, st);
         }
         const int64_t l = (varlen ? p.cf : (f1 - f0)) * nseg;
@@ -1272,7 +1358,9 @@ hipError_t launch_prefill_topk(const PrefillPlan &p, const uint16_t *q, const ui
             a.T = f1 - f0; a.pos0 = p.pos0 + f0; a.g_lo = 0; a.g_hi = f1 - f0;
             a.nrb = (int)cdiv(f1 - f0, bq);
             const int64_t mt = (p.pos0 + f1 - 1) / kBK + 1;
-            a.seg_tiles = split_tiles(a.nrb, mt);
+            const FilterSplit fs = filter_split(f1 - f0, bq, p.pos0 + f0);
+            a.seg_tiles = fs.seg;
+            a.seg_y = fs.seg_y ? 1 : 0;
             a.nseg = a.seg_tiles ? (int)cdiv(mt, a.seg_tiles) : 1;
             gx = (unsigned)a.nseg;
         }
@@ -1300,7 +1388,7 @@ hipError_t launch_prefill_topk(const PrefillPlan &p, const uint16_t *q, const ui
         s.dummy_i = reinterpret_cast<int32_t *>(dummy);
         {
             PhaseMark pm(kPhaseSelect, st);
-            if (a.seg_tiles > 0)
+            if (a.nseg > 2)
                 hipLaunchKernelGGL(select_multi_kernel, dim3((unsigned)(f1 - f0)), dim3(64 * kSelMW), 0, st, s);
             else
                 hipLaunchKernelGGL(select_kernel, dim3((unsigned)(f1 - f0)), dim3(64 * kSelW), 0, st, s);

@@ -93,19 +93,47 @@ def test_workspace_sizes(dsa):
         max_len = rows if max_len is None else max_len
         pos0 = 0 if varlen else pos0
         nkeys = pos0 + max_len
-        cf = min(rows, 65536 if heads == 32 else 32768)
+        cmax = 65536 if heads == 32 else 32768
+        cf = -(-rows // -(-rows // cmax)) if rows else 0     # equal filter chunks
         lists = 0
+
+        def dealt(n, p0, seg):
+            # the busiest CU when the workgroups, row blocks (longest first) fastest and key
+            # segments second, go to the 8 XCDs in turn and, in each, to the one of its 32 CUs
+            # that frees first (each costing its key tiles + 2)
+            busy = [[0] * 32 for _ in range(8)]
+            nrb, mt = -(-n // bq), (p0 + n - 1) // 128 + 1
+            i = 0
+            for y in range(-(-mt // seg) if seg else 1):
+                for x in range(nrb):
+                    r0 = (nrb - 1 - x) * bq
+                    nkt = (p0 + r0 + min(bq, n - r0) - 1) // 128 + 1
+                    if y * seg < nkt:
+                        cu = busy[i % 8]
+                        cu[cu.index(min(cu))] += min(seg or nkt, nkt - y * seg) + 2
+                    i += 1
+            return max(max(cu) for cu in busy)
+
         for f0 in range(0, rows, cf):
             f1 = min(rows, f0 + cf)
             nseg = 1
             if not varlen:
-                nrb, mt = -(-(f1 - f0) // bq), (pos0 + f1 - 1) // 128 + 1
-                min_seg = 8 if nrb <= 128 else 64      # launches of few row blocks: short segments
-                if nrb < 2048 and mt > min_seg:
-                    want = -(-2048 // nrb)
-                    st = max(min_seg, -(-mt // want), -(-mt // 512))
-                    if st < mt:
-                        nseg = -(-mt // st)
+                n, p0 = f1 - f0, pos0 + f0
+                nrb, mt = -(-n // bq), (p0 + n - 1) // 128 + 1
+                st = 0
+                if 128 < nrb and 2 * nrb <= 3 * 256 and p0 < n:
+                    # one or two rounds of workgroups: the longest row block in two segments (of
+                    # at least 8 tiles) when that leaves the busiest CU less busy
+                    half = -(-mt // 2)
+                    st = half if half >= 8 and dealt(n, p0, half) < dealt(n, p0, 0) else 0
+                else:
+                    min_seg = 8 if nrb <= 128 else 64      # launches of few row blocks: short segments
+                    if nrb < 2048 and mt > min_seg:
+                        want = -(-2048 // nrb)
+                        st = max(min_seg, -(-mt // want), -(-mt // 512))
+                        st = st if st < mt else 0
+                if st:
+                    nseg = -(-mt // st)
             lists = max(lists, (cf if varlen else f1 - f0) * nseg)
         ms = -(-max(nkeys // 32, 1) // 128) * 128
         cs = max(bq, (512 * 2 ** 20 // (4 * ms)) // bq * bq)
@@ -114,7 +142,7 @@ def test_workspace_sizes(dsa):
         parts = [256, 4 * cf, 4 * lists, 8 * lists * (6144 + 64), 4 * cs * ms, 8 * cf, 4 * 128, 8 * 128,
                  4 * 128 * ld, 4 * max(ms, ld) + 4 * 128]
         return sum(r256(x) for x in parts)
-    for T in (1, 300, 1000, 2560, 4096, 5000, 65536, 100000):
+    for T in (1, 300, 1000, 2560, 4096, 5000, 8192, 12000, 65536, 100000, 131073):
         assert dsa.workspace_size(dsa.OP_SCORE_TOPK, T, topk=2048) == plan(T), T
         assert dsa.workspace_size(dsa.OP_V32_SCORE_TOPK, T, topk=2048) == plan(T, heads=64), T
     assert dsa.workspace_size(dsa.OP_SCORE_TOPK_VARLEN, 16, 2, 8, topk=5) == plan(16, varlen=True, B=2, max_len=8)
