@@ -604,18 +604,27 @@ struct SelArgs {
     int32_t *dummy_i;          // store target of the lanes that write nothing (2 words a wave)
 };
 
+// A row's list: the entries of up to kSelSegs pieces, one per key segment of the row (a row
+// whose key tiles were split over workgroups), the keys of each piece all above those of the
+// pieces before it.  Entry e is in the last piece j with off[j] <= e, at l[j] + (e - off[j]);
+// pieces the row does not have start at INT32_MAX.
+constexpr int kSelSegs = 4;
+struct SelList {
+    const uint2 *l[kSelSegs];
+    int off[kSelSegs];
+};
+
 // This wave's order keys and key positions: entry e0 + 64 i + lane of the row's list in key[i],
-// pos[i], kSelBlk loads in flight at a time.  The list is the c0 entries at l0 followed by the
-// entries at l1 (the keys of a row whose key tiles were split over two workgroups: the second
-// segment's keys all follow the first's); entry e is l0[e] below c0, else l1[e - c0].
+// pos[i], kSelBlk loads in flight at a time.
 // Blocks past the wave's nit groups are not read; inside a block, a group i >= nit reads the
 // wave's last group again (a uniform index, so no branch) and its keys are zeroed; entries past
-// the list's end inside its last group read the sentinel run after l1's entries (l1 = l0 + c0
-// for a list in one piece), whose key is 0.
+// the list's end inside its last group read the sentinel run that follows its last piece,
+// whose key is 0.
 // The scores are never -0 (each is a sum from +0 of products and ReLUs), so the cheaper key
 // serves; the sentinels (all bits set) get key 0.
-__device__ __forceinline__ void sel_load(uint32_t (&key)[kSelKeys], int32_t (&pos)[kSelKeys], const uint2 *l0,
-                                         int c0, const uint2 *l1, int e0, int lane, int nit) {
+template <int NS>
+__device__ __forceinline__ void sel_load(uint32_t (&key)[kSelKeys], int32_t (&pos)[kSelKeys], const SelList &sl,
+                                         int e0, int lane, int nit) {
     nit = __builtin_amdgcn_readfirstlane(nit);
 #pragma unroll
     for (int blk = 0; blk < kSelKeys / kSelBlk; ++blk) {
@@ -625,7 +634,10 @@ __device__ __forceinline__ void sel_load(uint32_t (&key)[kSelKeys], int32_t (&po
             for (int j = 0; j < kSelBlk; ++j) {
                 const int gi = min(kSelBlk * blk + j, nit - 1);
                 const int en = e0 + 64 * gi + lane;
-                e[j] = en < c0 ? l0[en] : l1[en - c0];
+                const uint2 *src = sl.l[0] + en;
+#pragma unroll
+                for (int q = 1; q < NS; ++q) src = en >= sl.off[q] ? sl.l[q] + (en - sl.off[q]) : src;
+                e[j] = *src;
             }
 #pragma unroll
             for (int j = 0; j < kSelBlk; ++j) {
@@ -643,6 +655,8 @@ __device__ __forceinline__ void sel_load(uint32_t (&key)[kSelKeys], int32_t (&po
     }
 }
 
+// NS: most pieces a row's list has (1: the key tiles of a row were not split)
+template <int NS>
 __global__ __launch_bounds__(64 * kSelW) void select_kernel(SelArgs a) {
     __shared__ uint32_t hist[256];
     __shared__ uint32_t xch[2 * kSelW];
@@ -665,14 +679,22 @@ __global__ __launch_bounds__(64 * kSelW) void select_kernel(SelArgs a) {
         }
         return;
     }
-    // the row's list: one piece, or (key tiles split in two) its two segments' pieces
+    // the row's list: one piece per key segment of the row (one, or up to NS when its key tiles
+    // were split over workgroups)
     const int64_t lrow = g - a.f0;
-    const int nsr = a.seg_tiles > 0 ? (int)((pos_t / kBK) / a.seg_tiles) + 1 : 1;
-    const int64_t l0i = lrow * a.nseg;
-    const int c0 = a.cnt[l0i];
-    const int c1 = nsr > 1 ? a.cnt[l0i + 1] : 0;
-    const int total = c0 + c1;
-    if (c0 > a.cap || c1 > a.cap || total > kSelCap || total < need) {
+    const int nsr = NS > 1 && a.seg_tiles > 0 ? (int)((pos_t / kBK) / a.seg_tiles) + 1 : 1;
+    SelList sl;
+    int total = 0;
+    bool over = false;
+#pragma unroll
+    for (int j = 0; j < NS; ++j) {
+        const int c = j < nsr ? a.cnt[lrow * a.nseg + j] : 0;
+        over |= c > a.cap;
+        sl.l[j] = a.cand + (lrow * a.nseg + (j < nsr ? j : 0)) * (int64_t)(a.cap + 64);
+        sl.off[j] = j == 0 ? 0 : j < nsr ? total : INT32_MAX;
+        total += c > a.cap ? a.cap : c;
+    }
+    if (over || total > kSelCap || total < need) {
         if (tid == 0) {
             const uint32_t i = atomicAdd(&a.fb[1], 1u);
             a.fb_list[i] = g;
@@ -683,11 +705,9 @@ __global__ __launch_bounds__(64 * kSelW) void select_kernel(SelArgs a) {
     const int per = (nit_all + kSelW - 1) / kSelW;
     const int g0 = min(h * per, nit_all);
     const int nit = min(per, nit_all - g0);
-    const uint2 *l0 = a.cand + l0i * (int64_t)(a.cap + 64);
-    const uint2 *l1 = nsr > 1 ? l0 + (a.cap + 64) : l0 + c0;
     uint32_t key[kSelKeys];
     int32_t pos[kSelKeys];
-    sel_load(key, pos, l0, c0, l1, 64 * g0, lane, nit);
+    sel_load<NS>(key, pos, sl, 64 * g0, lane, nit);
     // Every candidate wins when there are only `need` of them (a row of at most topk keys): theta
     // 0 and no key to place by ties keep every key present and no empty slot.
     uint32_t base = 0u, prefix = 0u;
@@ -1388,10 +1408,12 @@ hipError_t launch_prefill_topk(const PrefillPlan &p, const uint16_t *q, const ui
         s.dummy_i = reinterpret_cast<int32_t *>(dummy);
         {
             PhaseMark pm(kPhaseSelect, st);
-            if (a.nseg > 2)
+            if (a.nseg > kSelSegs)
                 hipLaunchKernelGGL(select_multi_kernel, dim3((unsigned)(f1 - f0)), dim3(64 * kSelMW), 0, st, s);
+            else if (a.nseg > 1)
+                hipLaunchKernelGGL(select_kernel<kSelSegs>, dim3((unsigned)(f1 - f0)), dim3(64 * kSelW), 0, st, s);
             else
-                hipLaunchKernelGGL(select_kernel, dim3((unsigned)(f1 - f0)), dim3(64 * kSelW), 0, st, s);
+                hipLaunchKernelGGL(select_kernel<1>, dim3((unsigned)(f1 - f0)), dim3(64 * kSelW), 0, st, s);
             e = hipGetLastError();
         }
         if (e != hipSuccess) return e;
