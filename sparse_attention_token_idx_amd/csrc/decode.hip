@@ -264,9 +264,16 @@ __global__ __launch_bounds__(kPlanThreads) void decode_threshold_kernel(DecCommo
 }
 
 // ---------------------------------------------------------------- pass 2: filter
+// Keys stream through LDS: each wave copies its next 64-key group into its own slot with
+// non-temporal whole-line loads (Sc::stage), reads the fragments of that group back (Sc::
+// load_staged) and, before scoring them, already requests the group after it into the slot.
+template <class Sc>
+constexpr size_t filter_smem() { return (size_t)(kFilterThreads / 64) * Sc::kSlotBytes; }
+
 template <class Sc, class Keys>
 __global__ __launch_bounds__(kFilterThreads, 2) void decode_filter_kernel(DecCommon a, Keys kp) {
     __shared__ uint2 ring[kFilterThreads / 64][128];
+    extern __shared__ __align__(16) unsigned char slots[];
     const int64_t total = a.cu[a.B];
     const int64_t sub = decode_sub(total, gridDim.x, a.max_seqlen);
     const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
@@ -293,27 +300,26 @@ __global__ __launch_bounds__(kFilterThreads, 2) void decode_filter_kernel(DecCom
         const DecodePlan pl = a.plan[b];
         Sc sc;
         sc.init(kp, a.start, b, l16, lg);
-        auto keys = [&](int g, int (&key)[4]) {   // rows past the end clamped to the last
-#pragma unroll
-            for (int u = 0; u < 4; ++u) key[u] = min(g + 16 * u + l16, s_end - 1);
-        };
-        int key[4];
+        unsigned char *const slot = slots + (size_t)wave * Sc::kSlotBytes;
+        // keys past the end are the last key again
         int g0 = s_begin;
-        if (g0 < s_end) {
-            keys(g0, key);
-            sc.load(key, lg);
-        }
+        if (g0 < s_end) sc.stage(slot, g0, s_end - 1, lane);
+        // group g (staged) into registers, its scale kept, and group g + 64 requested into the slot
+        auto next = [&](int g) {
+            asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
+            sc.load_staged(slot, l16, lg);
+            const float scl = sc.scale();
+            asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory");
+            if (g + 64 < s_end) sc.stage(slot, g + 64, s_end - 1, lane);
+            return scl;
+        };
         if (pl.dense) {
             // every lane stores (past the end lie the row's padding positions)
             float *out = a.score_buf + (int64_t)b * a.ld;
             for (; g0 < s_end; g0 += 64) {
+                const float scl = next(g0);
                 float p[4];
                 sc.partial(p);
-                const float scl = sc.scale();
-                if (g0 + 64 < s_end) {
-                    keys(g0 + 64, key);
-                    sc.load(key, lg);
-                }
                 out[g0 + lane] = finish(sc, p, scl, lg);
             }
         } else {
@@ -323,13 +329,9 @@ __global__ __launch_bounds__(kFilterThreads, 2) void decode_filter_kernel(DecCom
             uint2 *list = a.cand + pos;   // this piece's list (room for one entry per position)
             int nst = 0, nfl = 0;         // candidates staged, flushed
             for (; g0 < s_end; g0 += 64) {
+                const float scl = next(g0);
                 float p[4];
                 sc.partial(p);
-                const float scl = sc.scale();
-                if (g0 + 64 < s_end) {
-                    keys(g0 + 64, key);
-                    sc.load(key, lg);
-                }
                 const float v = finish(sc, p, scl, lg);
                 const bool c = g0 + lane < s_end && (every || v >= th);
                 const uint64_t m = __ballot(c);
@@ -612,16 +614,26 @@ __global__ __launch_bounds__(1024) void decode_prefix_kernel(const int32_t *seql
 }
 
 template <class K>
-int filter_grid(K kernel) {
+int filter_grid(K kernel, size_t smem) {
     static DeviceInt cached;
     return cached.get([&] {
         int dev = 0, cus = 0, per = 0;
         if (hipGetDevice(&dev) != hipSuccess ||
             hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess || cus <= 0)
             cus = 256;
-        if (hipOccupancyMaxActiveBlocksPerMultiprocessor(&per, kernel, kFilterThreads, 0) != hipSuccess || per <= 0)
+        if (hipOccupancyMaxActiveBlocksPerMultiprocessor(&per, kernel, kFilterThreads, smem) != hipSuccess || per <= 0)
             per = 2;
         return 2 * per * cus;   // two rounds of the workgroups resident at once
+    });
+}
+
+// The filter's dynamic LDS (the key slots) may exceed the default limit: raised once per device.
+template <class Sc, class Keys>
+hipError_t filter_attr() {
+    static DeviceOnce once;
+    return once.run([] {
+        return hipFuncSetAttribute(reinterpret_cast<const void *>(decode_filter_kernel<Sc, Keys>),
+                                   hipFuncAttributeMaxDynamicSharedMemorySize, (int)filter_smem<Sc>());
     });
 }
 
@@ -644,22 +656,25 @@ hipError_t run_decode(const Keys &kp, const int64_t *start, const int32_t *seqle
     a.idx = idx;
     a.scores = scores;
     const int64_t bound = ((int64_t)B * (decode_row_stride(max_seqlen) / 64) + 3) / 4;   // 4 waves of 64 keys
-    const int g = filter_grid(decode_filter_kernel<Sc, Keys>);
+    hipError_t e = filter_attr<Sc, Keys>();
+    if (e != hipSuccess) return e;
+    const int g = filter_grid(decode_filter_kernel<Sc, Keys>, filter_smem<Sc>());
     a.filter_grid = (int)(bound < g ? (bound > 0 ? bound : 1) : g);
     const int own = B <= kPlanPrefixMax ? 1 : 0;
     if (!own) {
         hipLaunchKernelGGL(decode_prefix_kernel, dim3(1), dim3(1024), 0, stream, seqlens, B, max_seqlen, w.cu);
-        hipError_t e = hipGetLastError();
+        e = hipGetLastError();
         if (e != hipSuccess) return e;
     }
     hipLaunchKernelGGL((decode_sample_kernel<Sc, Keys>), dim3(B * kSampleParts), dim3(kSampleThreads), 0, stream,
                        a, kp, own);
-    hipError_t e = hipGetLastError();
+    e = hipGetLastError();
     if (e != hipSuccess) return e;
     hipLaunchKernelGGL(decode_threshold_kernel, dim3(B), dim3(kPlanThreads), 0, stream, a);
     e = hipGetLastError();
     if (e != hipSuccess) return e;
-    hipLaunchKernelGGL((decode_filter_kernel<Sc, Keys>), dim3(a.filter_grid), dim3(kFilterThreads), 0, stream, a, kp);
+    hipLaunchKernelGGL((decode_filter_kernel<Sc, Keys>), dim3(a.filter_grid), dim3(kFilterThreads), filter_smem<Sc>(),
+                       stream, a, kp);
     e = hipGetLastError();
     if (e != hipSuccess) return e;
     hipLaunchKernelGGL((decode_select_kernel<Sc, Keys>), dim3(B), dim3(kSelectThreads), 0, stream, a, kp);

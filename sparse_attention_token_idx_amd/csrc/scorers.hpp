@@ -51,6 +51,28 @@ struct Bf16ScorerT {
             for (int ks = 0; ks < 4; ++ks) kb[u][ks] = *reinterpret_cast<const u32x4 *>(kc + off + 32 * ks);
         }
     }
+    // The streamed form of load (the decode filter): stage() copies keys g .. g + 63 of the row
+    // (clamped to `last`) into a 16 KB LDS slot, 4 keys of 256 bytes per instruction, row r of
+    // the slot keeping its 16-byte chunk c at position c ^ (r % 16) (the 16 rows that one
+    // fragment read touches then hit 16 different bank groups); once the loads have landed
+    // (vmcnt), load_staged() reads the fragments load() would have read.
+    static constexpr int kSlotBytes = 64 * kDim * 2;
+    __device__ __forceinline__ void stage(unsigned char *slot, int g, int last, int lane) const {
+        const uint32_t base = lds_addr(slot);
+#pragma unroll
+        for (int i = 0; i < 16; ++i) {
+            const int r = 4 * i + (lane >> 4);
+            const int key = g + r < last ? g + r : last;
+            stream_to_lds(kc + (uint32_t)key * (uint32_t)kDim + 8 * ((lane & 15) ^ (r & 15)), base + 1024u * i);
+        }
+    }
+    __device__ __forceinline__ void load_staged(const unsigned char *slot, int l16, int lg) {
+#pragma unroll
+        for (int u = 0; u < 4; ++u)
+#pragma unroll
+            for (int ks = 0; ks < 4; ++ks)
+                kb[u][ks] = *reinterpret_cast<const u32x4 *>(slot + (16 * u + l16) * (2 * kDim) + 16 * ((lg + 4 * ks) ^ l16));
+    }
     __device__ __forceinline__ void partial(float (&p)[4]) const {
 #pragma unroll
         for (int u = 0; u < 4; ++u) {
@@ -158,6 +180,28 @@ struct Fp8ScorerT {
             kb[u][1] = *reinterpret_cast<const u32x4 *>(kc + off + 16);
         }
         kscale = ks[key[lg]];   // this lane's output key: slice lg, key l16
+    }
+    // Streamed form (the decode filter), as for bf16 keys: an 8 KB slot, 8 keys of 128 bytes per
+    // instruction, row r keeping its chunk c at position c ^ (r % 8); the scales are loaded
+    // directly.
+    static constexpr int kSlotBytes = 64 * kDim;
+    __device__ __forceinline__ void stage(unsigned char *slot, int g, int last, int lane) {
+        const uint32_t base = lds_addr(slot);
+#pragma unroll
+        for (int i = 0; i < 8; ++i) {
+            const int r = 8 * i + (lane >> 3);
+            const int key = g + r < last ? g + r : last;
+            stream_to_lds(kc + (uint32_t)key * (uint32_t)kDim + 16 * ((lane & 7) ^ (r & 7)), base + 1024u * i);
+        }
+        const int own = g + 16 * (lane >> 4) + (lane & 15);   // this lane's output key: slice lg, key l16
+        kscale = __builtin_nontemporal_load(ks + (own < last ? own : last));
+    }
+    __device__ __forceinline__ void load_staged(const unsigned char *slot, int l16, int lg) {
+#pragma unroll
+        for (int u = 0; u < 4; ++u)
+#pragma unroll
+            for (int j = 0; j < 2; ++j)
+                kb[u][j] = *reinterpret_cast<const u32x4 *>(slot + (16 * u + l16) * kDim + 16 * ((2 * lg + j) ^ (l16 & 7)));
     }
     __device__ __forceinline__ void partial(float (&p)[4]) const {
 #pragma unroll
