@@ -42,7 +42,7 @@ PEAK_BF16_TFLOPS = 2516.6     # MI355X dense bf16 MFMA (published)
 # HBM bytes per launch of the score-and-filter pass at T=65536, from rocprofv3 FETCH_SIZE and
 # WRITE_SIZE scaled by a 1 GiB device-copy calibration; reported only while the kernel
 # source is the one the counters were taken on (None: not measured for this source)
-TRAFFIC_FILTER_T65536 = {"source_sha256_prefix": "941573a660f08b3b", "bytes": 3238659990}
+TRAFFIC_FILTER_T65536 = {"source_sha256_prefix": "bb1dc1f08911e03b", "bytes": 3229462775}
 PEAK_HBM_GBPS = 8000.0        # MI355X HBM3E (published)
 H, D, QLAT, HIDDEN = 32, 128, 1536, 7168
 MLA_HEADS, MLA_KV, MLA_V = 96, 576, 512          # the sparse MLA consumer (gated-MLA row)
