@@ -161,7 +161,11 @@ int dsa_idx_score_topk(const dsa_idx_bf16 *q, const dsa_idx_bf16 *k, const dsa_i
  * [B+1], non-decreasing, cu_seqlens[0] = 0, cu_seqlens[B] = total) delimits them;
  * max_seqlen bounds every length.  Scoring is causal inside each sequence and never
  * crosses sequences; returned indices are relative to the sequence start.  q, k, w,
- * idx and scores are the packed [total][...] arrays of dsa_idx_score_topk. */
+ * idx and scores are the packed [total][...] arrays of dsa_idx_score_topk.
+ * A ragged prefill batch runs this call once per MLA layer: each of the 24 MLA layers has an
+ * indexer of its own, with its own weights, and no layer reuses another's selection
+ * ("Qwen3.5-397B-A17B vs Kimi K3.1 Pro" compare page, component table, sparse/compressed-
+ * attention and gated-MLA rows). */
 int dsa_idx_score_topk_varlen(const dsa_idx_bf16 *q, const dsa_idx_bf16 *k,
                               const dsa_idx_bf16 *w, const int32_t *cu_seqlens, int B,
                               int max_seqlen, int64_t total, int topk, int32_t *idx,
