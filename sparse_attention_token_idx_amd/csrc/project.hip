@@ -257,12 +257,17 @@ __global__ __launch_bounds__(512, 1) void proj_q_kernel(QArgs a) {
         }
     };
     const int nk = kQLat / KB;
+    // The waits are the compiler's own s_waitcnt (not inline assembly), so that it knows every
+    // LDS read issued so far has completed at the barrier: otherwise it waits for the next
+    // stage's fragment reads as well before the products of this one (their latency then
+    // adds to every k-step).  Encoding (gfx9): vmcnt in bits 3:0 and 15:14, expcnt 6:4,
+    // lgkmcnt 11:8; expcnt stays at its maximum.
     auto wait_stage = [&](int kt) {
         const int later = min(S - 2, nk - 1 - kt);
-        if (later >= 2) asm volatile("s_waitcnt vmcnt(8)" ::: "memory");
-        else if (later == 1) asm volatile("s_waitcnt vmcnt(4)" ::: "memory");
-        else asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
-        asm volatile("s_waitcnt lgkmcnt(0)\n\ts_barrier" ::: "memory");
+        if (later >= 2) __builtin_amdgcn_s_waitcnt(0x0078);        // vmcnt(8) lgkmcnt(0)
+        else if (later == 1) __builtin_amdgcn_s_waitcnt(0x0074);   // vmcnt(4) lgkmcnt(0)
+        else __builtin_amdgcn_s_waitcnt(0x0070);                   // vmcnt(0) lgkmcnt(0)
+        __builtin_amdgcn_s_barrier();
     };
     u32x4 fa[2][SM], fb[2][SN];
     auto read_frags = [&](int kt, int p) {
@@ -283,17 +288,23 @@ __global__ __launch_bounds__(512, 1) void proj_q_kernel(QArgs a) {
 #pragma unroll
         for (int h = 0; h < 2; ++h) {
             const int k = kt + h;
-            if (k < nk) {
-                if (k + 1 < nk) {
-                    wait_stage(k + 1);
-                    if (k + S < nk) issue(k + S);
-                    read_frags(k + 1, h ^ 1);
-                }
-#pragma unroll
-                for (int i = 0; i < SM; ++i)
-#pragma unroll
-                    for (int j = 0; j < SN; ++j) acc[i][j] = mfma16x16x32(fa[h][i], fb[h][j], acc[i][j]);
+            if (k + 1 < nk) {
+                wait_stage(k + 1);
+                if (k + S < nk) issue(k + S);
             }
+            // the next step's fragments (after the last step: a stage read again, unused) are
+            // read between this step's products, one read after each of the first 12
+            read_frags(k + 1 < nk ? k + 1 : k, h ^ 1);
+#pragma unroll
+            for (int i = 0; i < SM; ++i)
+#pragma unroll
+                for (int j = 0; j < SN; ++j) acc[i][j] = mfma16x16x32(fa[h][i], fb[h][j], acc[i][j]);
+#pragma unroll
+            for (int x = 0; x < SM + SN; ++x) {
+                __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);   // MFMA
+                __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);   // LDS read
+            }
+            __builtin_amdgcn_sched_group_barrier(0x008, SM * SN - SM - SN, 0);
         }
     }
     const bool odd = l16 & 1;
