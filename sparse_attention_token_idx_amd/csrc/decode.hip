@@ -189,7 +189,7 @@ __global__ __launch_bounds__(kPlanThreads) void decode_threshold_kernel(DecCommo
     // r such that fewer than r of the S samples reach the topk-th largest score of the row
     // only with negligible probability (their number is about binomial with mean E)
     const float E = (float)S * (float)a.topk / (float)n;
-    int r = (int)ceilf(E + 8.f * sqrtf(E) + 8.f);
+    int r = (int)ceilf(E + 6.f * sqrtf(E) + 6.f);
     r = r > S ? S : r;
     // theta: the lower edge of the bin that holds the r-th largest sample key, first in 1,024
     // bins over the sample's key range, then in 1,024 bins over that bin (exact when the bins
